@@ -1,0 +1,360 @@
+"""CPU oracle for the MoE layer forward and backward pass.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the package smoke check and
+the CPU-baseline leg of the benchmark may import this module.  It shares no
+code with the HIP path and must never be used to produce the product's
+results.
+
+What it computes (the plain definition of the layer):
+
+    y_t = s(x_t) + sum_e m[t,e] * g[t,e] * FFN_e(x_t)
+    FFN_e(z) = (silu(z W_g[e]^T) * (z W_u[e]^T)) W_d[e]^T
+
+* The router picks, for each token, k of the E experts; only the picked
+  experts run on that token, and their outputs are weighted by the gates and
+  summed (Ultimate MoE Training Handbook, section 2.5 "First training of
+  MoE": the router selects 8 of 64 smaller experts per token; tokens are sent
+  to the selected experts and their outputs returned).
+* Each expert is a SwiGLU feed-forward block without bias, i.e. three weight
+  matrices (Handbook 2.5, "Calculation of activated parameters and total
+  parameters").
+* Router logits are computed in fp32 (Handbook 2.5, the fp32 router dtype
+  flag).  Scores are either a softmax over the experts (top-k softmax router)
+  or a per-expert sigmoid (DeepSeek-V3 style router); shared experts run on
+  every token and are added ungated (KempnerForge README, "Features /
+  Architecture" and "Sparse architecture research").
+* Sigmoid routing adds a per-expert bias to the scores only to decide which
+  experts are picked; the gate values use the unbiased scores (Apex-3 code
+  page, "What's inside", row "Fine-grained MoE": the bias balances load
+  without a loss term).
+* Dropless: every assignment is computed (no capacity factor appears for the
+  pages' MoE runs).
+
+Readings taken where the pages are silent (each is a single switch here):
+  - softmax gates are the full-softmax probabilities of the picked experts,
+    renormalised over the top k only when ``renorm`` is set;
+  - sigmoid gates are the picked scores divided by their sum;
+  - ties in the selection key go to the lower expert index; slot j holds the
+    j-th best expert;
+  - inside an expert's segment, rows keep assignment order a = t*k + j;
+  - no routed scaling factor (it is 1).
+
+Precision: the router is fp32 as the pages state.  Logits are the fp64 product
+rounded once to fp32; the sigmoid / softmax scores are evaluated in fp64 from
+those fp32 logits and rounded once to fp32; a sigmoid selection key is the
+fp32 sum of the fp32 score and the fp32 bias.  Gates are fp32.  Everything in
+the expert path (GEMMs, activation, combine, backward) is fp64, computed from
+the exact values of the stored inputs.
+
+Parity pins (tests/test_oracle_pins.py): dense-masked brute force, torch fp64
+autograd, central finite differences, single-expert == dense, granularity
+identity, permutation invariants, gate renormalisation, bias-selects-only,
+brute-force top-k, the softmax Jacobian special case and the Handbook's
+parameter count.  Every function below is covered by at least one pin.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+F32 = np.float32
+F64 = np.float64
+
+
+# ----------------------------------------------------------------------------- router
+def router_logits(x, w_router):
+    """logits = x W_r^T, fp64 product rounded once to fp32 (fp32 router).
+
+    x: [T, d] (any float dtype, taken exactly); w_router: [E, d] fp32."""
+    return (np.asarray(x, F64) @ np.asarray(w_router, F64).T).astype(F32)
+
+
+def router_scores(logits32, score):
+    """Per-expert scores from fp32 logits, evaluated in fp64, rounded to fp32.
+
+    softmax: p = exp(l - max l) / sum exp(l - max l) over the E experts.
+    sigmoid: s = 1 / (1 + exp(-l)), independently per expert."""
+    l = np.asarray(logits32, F32).astype(F64)
+    if score == "softmax":
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+        return (z / z.sum(axis=1, keepdims=True)).astype(F32)
+    if score == "sigmoid":
+        return (1.0 / (1.0 + np.exp(-l))).astype(F32)
+    raise ValueError(score)
+
+
+def selection_keys(logits32, scores32, bias32, score):
+    """The value experts are ranked by.
+
+    softmax: the logit itself (same order as the probability, no exp rounding).
+    sigmoid: score + bias, one fp32 addition; a missing bias means zero."""
+    if score == "softmax":
+        return np.asarray(logits32, F32).copy()
+    s = np.asarray(scores32, F32)
+    if bias32 is None:
+        return s.copy()
+    return (s + np.asarray(bias32, F32)[None, :]).astype(F32)
+
+
+def select_topk(keys32, k):
+    """Pick k experts per token: key descending, ties to the lower index.
+
+    Returns idx [T, k] int32 (slot j = j-th best) and the selection margin
+    key_(k) - key_(k+1) per token (inf when k == E)."""
+    keys = np.asarray(keys32, F32)
+    T, E = keys.shape
+    # a stable sort of the negated key keeps equal keys in index order
+    order = np.argsort(-keys, axis=1, kind="stable")
+    idx = order[:, :k].astype(np.int32)
+    if k < E:
+        kth = np.take_along_axis(keys, order[:, k - 1:k], axis=1)[:, 0].astype(F64)
+        nxt = np.take_along_axis(keys, order[:, k:k + 1], axis=1)[:, 0].astype(F64)
+        margin = kth - nxt
+    else:
+        margin = np.full(T, np.inf)
+    return idx, margin
+
+
+def gates_from_scores(scores32, idx, score, renorm):
+    """Gate values of the picked experts (fp32).
+
+    softmax: the picked probabilities, divided by their sum if ``renorm``.
+    sigmoid: the picked (unbiased) scores divided by their sum."""
+    picked = np.take_along_axis(np.asarray(scores32, F32), idx, axis=1).astype(F64)
+    if score == "softmax" and not renorm:
+        return picked.astype(F32)
+    return (picked / picked.sum(axis=1, keepdims=True)).astype(F32)
+
+
+# ----------------------------------------------------------------------------- permutation
+def permute_indices(idx, E):
+    """Expert-contiguous order of the T*k assignments a = t*k + j.
+
+    counts[e]: assignments routed to e; offsets: exclusive prefix sum
+    (offsets[E] = T*k); src[p]: the assignment stored at permuted row p, rows
+    of one expert in increasing a; pos[a]: the row that assignment a went to
+    (pos and src are inverse permutations)."""
+    expert_of_a = np.asarray(idx, np.int64).reshape(-1)
+    A = expert_of_a.size
+    counts = np.bincount(expert_of_a, minlength=E).astype(np.int32)
+    offsets = np.zeros(E + 1, np.int64)
+    offsets[1:] = np.cumsum(counts)
+    src = np.argsort(expert_of_a, kind="stable").astype(np.int32)
+    pos = np.empty(A, np.int32)
+    pos[src] = np.arange(A, dtype=np.int32)
+    return counts, offsets.astype(np.int32), pos, src
+
+
+# ----------------------------------------------------------------------------- experts
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu_ffn(z, w_gate, w_up, w_down):
+    """One SwiGLU FFN on rows z: returns (G, U, H, Y) with
+    G = z W_g^T, U = z W_u^T, H = silu(G) * U, Y = H W_d^T (fp64)."""
+    G = z @ w_gate.T
+    U = z @ w_up.T
+    H = silu(G) * U
+    return G, U, H, H @ w_down.T
+
+
+def swiglu_ffn_backward(z, w_gate, w_up, w_down, G, U, H, dY):
+    """Reverse of ``swiglu_ffn`` for upstream dY: returns
+    (dz, dW_g, dW_u, dW_d) with dH = dY W_d, dG = dH * U * silu'(G),
+    dU = dH * silu(G), silu'(g) = sig(g) (1 + g (1 - sig(g)))."""
+    dH = dY @ w_down
+    sg = 1.0 / (1.0 + np.exp(-G))
+    dG = dH * U * sg * (1.0 + G * (1.0 - sg))
+    dU = dH * (G * sg)
+    dW_d = dY.T @ H
+    dW_g = dG.T @ z
+    dW_u = dU.T @ z
+    dz = dG @ w_gate + dU @ w_up
+    return dz, dW_g, dW_u, dW_d, dG, dU
+
+
+def _split_gateup(w_gateup):
+    f = w_gateup.shape[-2] // 2
+    return w_gateup[..., :f, :], w_gateup[..., f:, :]
+
+
+# ----------------------------------------------------------------------------- layer
+def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
+            top_k, score, renorm=False, forced_idx=None):
+    """Forward pass of the MoE layer on the tokens of ``x``.
+
+    x: [T, d]; w_router: [E, d] fp32; bias: [E] fp32 or None (sigmoid only);
+    w_gateup: [E, 2f, d] (gate rows, then up rows); w_down: [E, d, f];
+    s_gateup: [2F, d], s_down: [d, F] for the shared experts (concatenated
+    along their hidden width) or None.  Weights are taken exactly in fp64.
+
+    ``forced_idx`` replaces the selection (used to follow another
+    implementation's choice on near-tied tokens); gates are then recomputed
+    from this oracle's own scores for the forced experts.
+
+    Returns a dict with every intermediate of the layer."""
+    x = np.asarray(x, F64)
+    T, d = x.shape
+    E = w_router.shape[0]
+    k = int(top_k)
+    logits = router_logits(x, w_router)
+    scores = router_scores(logits, score)
+    keys = selection_keys(logits, scores, bias if score == "sigmoid" else None, score)
+    idx, margin = select_topk(keys, k)
+    if forced_idx is not None:
+        idx = np.asarray(forced_idx, np.int32).reshape(T, k)
+    gate = gates_from_scores(scores, idx, score, renorm)
+    counts, offsets, pos, src = permute_indices(idx, E)
+
+    A = T * k
+    f = w_gateup.shape[1] // 2
+    tok_of_row = src // k
+    x_perm = x[tok_of_row]
+    preact = np.empty((A, 2 * f), F64)
+    h = np.empty((A, f), F64)
+    y_perm = np.empty((A, d), F64)
+    wg_all, wu_all = _split_gateup(np.asarray(w_gateup))
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        G, U, H, Y = swiglu_ffn(x_perm[r0:r1], np.asarray(wg_all[e], F64),
+                                np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64))
+        preact[r0:r1, :f] = G
+        preact[r0:r1, f:] = U
+        h[r0:r1] = H
+        y_perm[r0:r1] = Y
+
+    out = dict(logits=logits, scores=scores, keys=keys, idx=idx, margin=margin, gate=gate,
+               counts=counts, offsets=offsets, pos=pos, src=src, x_perm=x_perm,
+               preact=preact, h=h, y_perm=y_perm)
+
+    if s_gateup is not None:
+        sg, su = _split_gateup(np.asarray(s_gateup, F64))
+        Gs, Us, Hs, ys = swiglu_ffn(x, sg, su, np.asarray(s_down, F64))
+        out.update(s_preact=np.concatenate([Gs, Us], axis=1), s_h=Hs, ys=ys)
+    else:
+        ys = np.zeros((T, d), F64)
+        out.update(s_preact=None, s_h=None, ys=None)
+
+    # weighted combine: slot order, shared output last
+    y = np.zeros((T, d), F64)
+    g64 = gate.astype(F64)
+    rows = pos.reshape(T, k)
+    for j in range(k):
+        y += g64[:, j:j + 1] * y_perm[rows[:, j]]
+    y += ys
+    out["y"] = y
+    return out
+
+
+def router_backward(dgate, scores32, idx, score, renorm):
+    """Gradient of the loss w.r.t. the fp32 logits, given dL/dgate [T, k].
+
+    The selection is piecewise constant, so gradient reaches the router only
+    through the gate values; the bias receives none.
+      sigmoid:  g_i = s_i / S, S = sum of picked s  ->  ds_i = (dg_i - <g, dg>) / S
+                on picked experts, dl = ds * s * (1 - s), zero elsewhere.
+      softmax:  dp = dgate scattered onto the picked experts (through the
+                renormalisation when it is on), then the softmax Jacobian
+                dl = p * (dp - <p, dp>) over all experts."""
+    s = np.asarray(scores32, F32).astype(F64)
+    T, E = s.shape
+    dg = np.asarray(dgate, F64)
+    picked = np.take_along_axis(s, idx, axis=1)
+    if score == "sigmoid" or renorm:
+        S = picked.sum(axis=1, keepdims=True)
+        g = picked / S
+        dpicked = (dg - (g * dg).sum(axis=1, keepdims=True)) / S
+    else:
+        dpicked = dg
+    dscore = np.zeros((T, E), F64)
+    np.put_along_axis(dscore, idx.astype(np.int64), dpicked, axis=1)
+    if score == "sigmoid":
+        return dscore * s * (1.0 - s)
+    return s * (dscore - (s * dscore).sum(axis=1, keepdims=True))
+
+
+def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False):
+    """Backward pass for upstream gradient dy [T, d], reusing ``forward``'s dict.
+
+    Returns dict: dx [T,d], d_w_gateup [E,2f,d], d_w_down [E,d,f],
+    d_s_gateup / d_s_down (or None), d_w_router [E,d], d_logits [T,E],
+    dgate [T,k], plus the permuted intermediates dy_perm, dgu, dx_perm."""
+    x = np.asarray(x, F64)
+    dy = np.asarray(dy, F64)
+    T, d = x.shape
+    E = w_router.shape[0]
+    idx, gate, pos, src, offsets = fwd["idx"], fwd["gate"], fwd["pos"], fwd["src"], fwd["offsets"]
+    k = idx.shape[1]
+    A = T * k
+    f = w_gateup.shape[1] // 2
+    tok_of_row = src // k
+    slot_of_row = src % k
+
+    # combine backward: d(y_perm row p) = gate * dy[token]; dgate = <dy, y_perm row>
+    g64 = gate.astype(F64)
+    dy_perm = g64[tok_of_row, slot_of_row][:, None] * dy[tok_of_row]
+    rows = pos.reshape(T, k)
+    dgate = np.stack([(dy * fwd["y_perm"][rows[:, j]]).sum(axis=1) for j in range(k)], axis=1)
+
+    wg_all, wu_all = _split_gateup(np.asarray(w_gateup))
+    d_w_gateup = np.zeros((E, 2 * f, d), F64)
+    d_w_down = np.zeros((E, d, f), F64)
+    dgu = np.zeros((A, 2 * f), F64)
+    dx_perm = np.zeros((A, d), F64)
+    for e in range(E):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        if r1 == r0:
+            continue
+        G = fwd["preact"][r0:r1, :f]
+        U = fwd["preact"][r0:r1, f:]
+        dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward(
+            fwd["x_perm"][r0:r1], np.asarray(wg_all[e], F64), np.asarray(wu_all[e], F64),
+            np.asarray(w_down[e], F64), G, U, fwd["h"][r0:r1], dy_perm[r0:r1])
+        d_w_gateup[e, :f] = dWg
+        d_w_gateup[e, f:] = dWu
+        d_w_down[e] = dWd
+        dgu[r0:r1, :f] = dG
+        dgu[r0:r1, f:] = dU
+        dx_perm[r0:r1] = dz
+
+    out = dict(dgate=dgate, dy_perm=dy_perm, dgu=dgu, dx_perm=dx_perm,
+               d_w_gateup=d_w_gateup, d_w_down=d_w_down)
+
+    if s_gateup is not None:
+        sg, su = _split_gateup(np.asarray(s_gateup, F64))
+        Fs = sg.shape[0]
+        Gs = fwd["s_preact"][:, :Fs]
+        Us = fwd["s_preact"][:, Fs:]
+        dxs, dSg, dSu, dSd, _, _ = swiglu_ffn_backward(x, sg, su, np.asarray(s_down, F64),
+                                                       Gs, Us, fwd["s_h"], dy)
+        out["d_s_gateup"] = np.concatenate([dSg, dSu], axis=0)
+        out["d_s_down"] = dSd
+        out["dx_shared"] = dxs
+    else:
+        out["d_s_gateup"] = None
+        out["d_s_down"] = None
+        dxs = np.zeros((T, d), F64)
+        out["dx_shared"] = None
+
+    dlogits = router_backward(dgate, fwd["scores"], idx, score, renorm)
+    wr = np.asarray(w_router, F32).astype(F64)
+    out["d_logits"] = dlogits
+    out["d_w_router"] = dlogits.T @ x
+    dx_router = dlogits @ wr
+    out["dx_router"] = dx_router
+
+    # unpermute-sum: slot order, then shared, then router contribution
+    dx = np.zeros((T, d), F64)
+    for j in range(k):
+        dx += dx_perm[rows[:, j]]
+    dx += dxs
+    dx += dx_router
+    out["dx"] = dx
+    return out
+
+
+def expert_parameter_count(d_model, d_ff):
+    """Weights in one SwiGLU expert without bias: three d_model x d_ff matrices."""
+    return 3 * int(d_model) * int(d_ff)

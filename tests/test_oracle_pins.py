@@ -1,0 +1,327 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test checks the oracle against torch fp64 autograd, a brute force written
+differently, a closed form, a special case that reduces to a textbook routine,
+or numbers printed on the pages (tests/golden).  None of these tests needs a
+GPU."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+F64 = np.float64
+
+
+def _rand_layer(seed, T, d, E, k, f, Fs, score, renorm, bias=True, wr_std=0.5):
+    g = np.random.default_rng(seed)
+    x = g.standard_normal((T, d))
+    wr = (g.standard_normal((E, d)) * wr_std).astype(np.float32)
+    b = (g.uniform(-0.3, 0.3, E).astype(np.float32) if (bias and score == "sigmoid") else None)
+    wgu = g.standard_normal((E, 2 * f, d)) / np.sqrt(d)
+    wd = g.standard_normal((E, d, f)) / np.sqrt(f)
+    if Fs:
+        sgu = g.standard_normal((2 * Fs, d)) / np.sqrt(d)
+        sd = g.standard_normal((d, Fs)) / np.sqrt(Fs)
+    else:
+        sgu = sd = None
+    dy = g.standard_normal((T, d))
+    return dict(x=x, w_router=wr, bias=b, w_gateup=wgu, w_down=wd, s_gateup=sgu, s_down=sd, dy=dy,
+                k=k, score=score, renorm=renorm)
+
+
+def _fwd(L, **kw):
+    return O.forward(L["x"], L["w_router"], L["bias"], L["w_gateup"], L["w_down"], L["s_gateup"],
+                     L["s_down"], top_k=L["k"], score=L["score"], renorm=L["renorm"], **kw)
+
+
+def _bwd(L, fwd):
+    return O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                      fwd, L["dy"], score=L["score"], renorm=L["renorm"])
+
+
+def _rel(a, b):
+    a = np.asarray(a, F64)
+    b = np.asarray(b, F64)
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+# --------------------------------------------------------------------------- independent reference
+def _brute_select(keys32, k):
+    """Top-k by an explicit python sort of (-key, index) tuples."""
+    out = []
+    for row in np.asarray(keys32, np.float32):
+        order = sorted(range(len(row)), key=lambda e: (-float(row[e]), e))
+        out.append(order[:k])
+    return np.array(out, np.int32)
+
+
+def _torch_keys(L):
+    """Selection keys recomputed with torch (fp64 math, rounded like an fp32 router)."""
+    x = torch.tensor(L["x"], dtype=torch.float64)
+    wr = torch.tensor(L["w_router"], dtype=torch.float64)
+    logits32 = (x @ wr.T).to(torch.float32)
+    if L["score"] == "softmax":
+        return logits32.numpy()
+    s32 = torch.sigmoid(logits32.to(torch.float64)).to(torch.float32)
+    if L["bias"] is not None:
+        s32 = s32 + torch.tensor(L["bias"])
+    return s32.numpy()
+
+
+def _dense_masked_torch(L, mask_idx):
+    """All E experts on all T tokens in torch fp64, masked by the selection and
+    weighted by gates recomputed from the logits; returns y and a closure for
+    autograd.  The selection is fixed (it is piecewise constant)."""
+    T, d = L["x"].shape
+    E = L["w_router"].shape[0]
+    f = L["w_gateup"].shape[1] // 2
+    t = {n: torch.tensor(np.asarray(L[n], F64), dtype=torch.float64, requires_grad=True)
+         for n in ("x", "w_router", "w_gateup", "w_down")}
+    if L["s_gateup"] is not None:
+        for n in ("s_gateup", "s_down"):
+            t[n] = torch.tensor(L[n], dtype=torch.float64, requires_grad=True)
+    M = torch.zeros(T, E, dtype=torch.float64)
+    M[torch.arange(T)[:, None], torch.tensor(mask_idx, dtype=torch.long)] = 1.0
+    logits = t["x"] @ t["w_router"].T
+    if L["score"] == "softmax":
+        p = torch.softmax(logits, dim=1)
+        g = M * p
+        if L["renorm"]:
+            g = g / g.sum(dim=1, keepdim=True)
+    else:
+        s = torch.sigmoid(logits)
+        g = M * s
+        g = g / g.sum(dim=1, keepdim=True)
+    y = torch.zeros(T, d, dtype=torch.float64)
+    for e in range(E):
+        G = t["x"] @ t["w_gateup"][e, :f].T
+        U = t["x"] @ t["w_gateup"][e, f:].T
+        Y = (torch.nn.functional.silu(G) * U) @ t["w_down"][e].T
+        y = y + g[:, e:e + 1] * Y
+    if "s_gateup" in t:
+        Fs = t["s_gateup"].shape[0] // 2
+        Gs = t["x"] @ t["s_gateup"][:Fs].T
+        Us = t["x"] @ t["s_gateup"][Fs:].T
+        y = y + (torch.nn.functional.silu(Gs) * Us) @ t["s_down"].T
+    return y, t
+
+
+CASES = [
+    # seed, T, d, E, k, f, Fs, score, renorm
+    (1, 24, 16, 8, 2, 12, 0, "softmax", False),
+    (2, 20, 16, 8, 3, 8, 0, "softmax", True),
+    (3, 32, 16, 8, 4, 8, 8, "sigmoid", True),
+    (4, 16, 8, 6, 6, 4, 4, "sigmoid", True),      # k == E
+    (5, 17, 12, 5, 1, 8, 0, "sigmoid", True),     # k == 1
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_p1_dense_masked_brute_force_forward(case):
+    """Sparse oracle forward == all-experts dense compute masked by the selection."""
+    L = _rand_layer(*case)
+    fw = _fwd(L)
+    sel = _brute_select(_torch_keys(L), L["k"])
+    assert np.array_equal(fw["idx"], sel)
+    y, _ = _dense_masked_torch(L, sel)
+    assert _rel(fw["y"], y.detach().numpy()) < 1e-6
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_p2_backward_matches_torch_autograd(case):
+    """Hand-written oracle backward == torch fp64 autograd of the dense-masked layer."""
+    L = _rand_layer(*case)
+    fw = _fwd(L)
+    bw = _bwd(L, fw)
+    y, t = _dense_masked_torch(L, fw["idx"])
+    (y * torch.tensor(L["dy"])).sum().backward()
+    assert _rel(bw["dx"], t["x"].grad.numpy()) < 1e-6
+    assert _rel(bw["d_w_gateup"], t["w_gateup"].grad.numpy()) < 1e-6
+    assert _rel(bw["d_w_down"], t["w_down"].grad.numpy()) < 1e-6
+    ref = t["w_router"].grad.numpy()
+    # top-1 sigmoid: the exact gradient is zero and autograd leaves ~1e-16 noise
+    assert np.linalg.norm(bw["d_w_router"] - ref) <= 1e-5 * np.linalg.norm(ref) + 1e-12
+    if L["s_gateup"] is not None:
+        assert _rel(bw["d_s_gateup"], t["s_gateup"].grad.numpy()) < 1e-6
+        assert _rel(bw["d_s_down"], t["s_down"].grad.numpy()) < 1e-6
+
+
+def test_p2_finite_differences_expert_weights():
+    """Central differences of L = <dy, y> w.r.t. expert and shared weights.
+    These perturbations leave the router untouched, so y is smooth in fp64."""
+    L = _rand_layer(7, 12, 8, 4, 2, 6, 4, "sigmoid", True)
+    fw = _fwd(L)
+    bw = _bwd(L, fw)
+    g = np.random.default_rng(0)
+    h = 1e-6
+    for name, grad in (("w_gateup", bw["d_w_gateup"]), ("w_down", bw["d_w_down"]),
+                       ("s_gateup", bw["d_s_gateup"]), ("s_down", bw["d_s_down"])):
+        for _ in range(6):
+            i = tuple(int(g.integers(0, s)) for s in L[name].shape)
+            Lp = dict(L); Lp[name] = L[name].copy(); Lp[name][i] += h
+            Lm = dict(L); Lm[name] = L[name].copy(); Lm[name][i] -= h
+            num = ((_fwd(Lp)["y"] - _fwd(Lm)["y"]) * L["dy"]).sum() / (2 * h)
+            assert abs(num - grad[i]) <= 1e-6 * max(1.0, abs(num)), (name, i, num, grad[i])
+
+
+def test_p3_single_expert_top1_equals_dense():
+    """One expert with top-1 routing is the dense FFN it came from (Handbook 2.5)."""
+    for score in ("softmax", "sigmoid"):
+        L = _rand_layer(11, 16, 8, 1, 1, 12, 0, score, score == "sigmoid")
+        fw = _fwd(L)
+        assert np.all(fw["gate"] == 1.0)
+        x = torch.tensor(L["x"])
+        f = L["w_gateup"].shape[1] // 2
+        W = torch.tensor(L["w_gateup"][0])
+        dense = (torch.nn.functional.silu(x @ W[:f].T) * (x @ W[f:].T)) @ torch.tensor(L["w_down"][0]).T
+        assert _rel(fw["y"], dense.numpy()) < 1e-13
+
+
+def test_p4_single_expert_router_gets_no_gradient():
+    """With one expert the router weight receives exactly zero gradient
+    (Handbook 2.5: the ~32,770 zero-gradient parameters are the router)."""
+    gold = json.load(open(os.path.join(GOLDEN, "handbook_param_count.json")))
+    for score in ("softmax", "sigmoid"):
+        L = _rand_layer(12, 16, 8, 1, 1, 12, 0, score, score == "sigmoid")
+        fw = _fwd(L)
+        bw = _bwd(L, fw)
+        assert np.all(bw["d_logits"] == 0.0)
+        assert np.all(bw["d_w_router"] == 0.0)
+        # 16 layers x (1 expert x hidden 2048) router weights, all zero-gradient
+        zero_router = gold["layers"] * 1 * gold["hidden_size"]
+        assert zero_router <= gold["single_expert_zero_grad_params"] <= zero_router + gold["dense_zero_grad_params_max"]
+    # sigmoid top-1 with many experts: the renormalised gate is exactly 1
+    L = _rand_layer(13, 16, 8, 6, 1, 4, 0, "sigmoid", True)
+    bw = _bwd(L, _fwd(L))
+    assert np.all(bw["d_logits"] == 0.0)
+
+
+def test_p5_granularity_identity():
+    """A dense SwiGLU of width F cut into E experts of width F/E: routing every
+    token to every expert and summing the expert outputs gives the dense FFN
+    (Handbook 2.5: eight 1024-wide experts == the 8192-wide dense layer)."""
+    g = np.random.default_rng(5)
+    T, d, E, fe = 20, 16, 4, 6
+    F = E * fe
+    Wg = g.standard_normal((F, d)); Wu = g.standard_normal((F, d)); Wd = g.standard_normal((d, F))
+    wgu = np.stack([np.concatenate([Wg[e * fe:(e + 1) * fe], Wu[e * fe:(e + 1) * fe]]) for e in range(E)])
+    wd = np.stack([Wd[:, e * fe:(e + 1) * fe] for e in range(E)])
+    x = g.standard_normal((T, d))
+    wr = g.standard_normal((E, d)).astype(np.float32)
+    fw = O.forward(x, wr, None, wgu, wd, top_k=E, score="softmax", renorm=False)
+    summed = fw["y_perm"][fw["pos"].reshape(T, E)].sum(axis=1)
+    xt = torch.tensor(x)
+    dense = (torch.nn.functional.silu(xt @ torch.tensor(Wg).T) * (xt @ torch.tensor(Wu).T)) @ torch.tensor(Wd).T
+    assert _rel(summed, dense.numpy()) < 1e-13
+
+
+def test_p5_handbook_parameter_accounting():
+    """Parameter counts printed in the Handbook (sections 2.4 and 2.5)."""
+    gold = json.load(open(os.path.join(GOLDEN, "handbook_param_count.json")))
+    d, fe, F, k, E, Lyr = (gold[n] for n in ("hidden_size", "moe_ffn_hidden_size", "dense_ffn_hidden_size",
+                                             "router_topk", "num_experts", "layers"))
+    per_expert = O.expert_parameter_count(d, fe)
+    assert per_expert == 6_291_456
+    assert k * per_expert == O.expert_parameter_count(d, F) == 50_331_648
+    dense_ffn = Lyr * O.expert_parameter_count(d, F)
+    router = Lyr * E * d
+    rest = gold["dense_total_params_B"] * 1e9 - dense_ffn
+    active = rest + Lyr * k * per_expert + router
+    total = rest + Lyr * E * per_expert + router
+    assert abs(active / 1e9 - gold["moe_active_params_B"]) < 0.0015
+    assert abs(total / 1e9 - gold["moe_total_params_B"]) < 0.006
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_p6_p7_p11_permutation_invariants(case):
+    L = _rand_layer(*case)
+    fw = _fwd(L)
+    T, k, E = L["x"].shape[0], L["k"], L["w_router"].shape[0]
+    A = T * k
+    assert fw["counts"].sum() == A and fw["offsets"][-1] == A and fw["offsets"][0] == 0
+    assert np.array_equal(fw["src"][fw["pos"]], np.arange(A))
+    # brute-force stable grouping: per expert, assignments in increasing order
+    flat = fw["idx"].reshape(-1)
+    expect = [a for e in range(E) for a in range(A) if flat[a] == e]
+    assert np.array_equal(fw["src"], np.array(expect))
+    for e in range(E):
+        assert fw["counts"][e] == fw["offsets"][e + 1] - fw["offsets"][e] == int((flat == e).sum())
+    # permuted rows are copies of the token rows; unpermute-combine with
+    # renormalised weights gives x back
+    xp = fw["x_perm"]
+    assert np.array_equal(xp[fw["pos"]], np.repeat(L["x"], k, axis=0))
+    w = np.full((T, k), 1.0 / k)
+    back = sum(w[:, j:j + 1] * xp[fw["pos"].reshape(T, k)[:, j]] for j in range(k))
+    assert _rel(back, L["x"]) < 1e-15
+
+
+def test_p8_sigmoid_gates_renormalise():
+    L = _rand_layer(21, 64, 16, 16, 4, 4, 0, "sigmoid", True)
+    g = _fwd(L)["gate"].astype(F64)
+    assert np.all(np.abs(g.sum(axis=1) - 1.0) < 4 * 2.0 ** -24 * 4)
+
+
+def test_p9_bias_selects_but_does_not_scale():
+    L = _rand_layer(22, 64, 16, 12, 3, 4, 0, "sigmoid", True)
+    fw = _fwd(L)
+    s = torch.sigmoid(torch.tensor(fw["logits"], dtype=torch.float64)).to(torch.float32).numpy().astype(F64)
+    picked = np.take_along_axis(s, fw["idx"], axis=1)
+    assert np.array_equal(fw["gate"], (picked / picked.sum(axis=1, keepdims=True)).astype(np.float32))
+    # a +10 bias on a fixed set S of size k forces I_t = S for every token
+    S = [7, 2, 9]
+    L2 = dict(L); L2["bias"] = L["bias"].copy(); L2["bias"][S] += 10.0
+    fw2 = _fwd(L2)
+    assert all(set(r) == set(S) for r in fw2["idx"].tolist())
+    s_S = s[:, S]
+    for t in range(s.shape[0]):
+        for j, e in enumerate(fw2["idx"][t]):
+            assert fw2["gate"][t, j] == np.float32(s[t, e] / s_S[t].sum())
+    # the bias changes the selection on the unbiased layer
+    assert not np.array_equal(fw["idx"], fw2["idx"])
+
+
+def test_p10_topk_brute_force_with_ties():
+    g = np.random.default_rng(3)
+    keys = g.integers(-3, 4, size=(200, 9)).astype(np.float32)   # many exact ties
+    keys[0, :] = 0.0
+    keys[1, :] = -0.0
+    keys[1, 4] = 0.0
+    for k in (1, 2, 5, 9):
+        idx, margin = O.select_topk(keys, k)
+        assert np.array_equal(idx, _brute_select(keys, k))
+        if k == 9:
+            assert np.all(np.isinf(margin))
+            assert all(sorted(r) == list(range(9)) for r in idx.tolist())
+    # the sigmoid scores agree with an independent library evaluation
+    l = g.standard_normal((50, 7)).astype(np.float32) * 4
+    s = O.router_scores(l, "sigmoid")
+    ref = torch.sigmoid(torch.tensor(l, dtype=torch.float64)).to(torch.float32).numpy()
+    assert np.array_equal(s, ref)
+    p = O.router_scores(l, "softmax")
+    refp = torch.softmax(torch.tensor(l, dtype=torch.float64), dim=1).to(torch.float32).numpy()
+    assert np.max(np.abs(p.astype(F64) - refp)) <= 2.0 ** -24
+
+
+def test_p13_softmax_backward_is_the_softmax_jacobian():
+    """k = E, no renormalisation: dl = p * (dp - <p, dp>), checked against torch autograd."""
+    g = np.random.default_rng(8)
+    l = g.standard_normal((10, 6)).astype(np.float32)
+    p32 = O.router_scores(l, "softmax")
+    idx, _ = O.select_topk(l, 6)
+    dg = g.standard_normal((10, 6))
+    dl = O.router_backward(dg, p32, idx, "softmax", False)
+    pt = torch.tensor(p32.astype(F64), requires_grad=True)
+    # the Jacobian of softmax at p: d p_i / d l_j = p_i (delta_ij - p_j)
+    J = torch.diag_embed(pt) - pt[:, :, None] * pt[:, None, :]
+    dp = np.zeros((10, 6)); np.put_along_axis(dp, idx.astype(np.int64), dg, axis=1)
+    ref = torch.einsum("ti,tij->tj", torch.tensor(dp), J).detach().numpy()
+    assert _rel(dl, ref) < 1e-14
+    # and against autograd through torch.softmax at fp64 logits
+    lt = torch.tensor(l.astype(F64), requires_grad=True)
+    (torch.softmax(lt, 1) * torch.tensor(dp)).sum().backward()
+    assert _rel(dl, lt.grad.numpy()) < 1e-6
