@@ -1,0 +1,247 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) mixture-of-experts layer library.
+ *
+ * The library computes one MoE layer, forward and backward, on one GPU:
+ *
+ *     y_t = s(x_t) + sum_{j<k} g[t,j] * FFN_{idx[t,j]}(x_t)
+ *     FFN_e(z) = (silu(z W_g[e]^T) * (z W_u[e]^T)) W_d[e]^T        (SwiGLU, no bias)
+ *
+ * where a router picks k of E experts per token from fp32 logits x W_r^T,
+ * the picked experts' outputs are weighted by the gates and summed, and the
+ * optional shared experts s(.) run on every token, ungated.
+ *
+ * Sources of the definition (the web pages this library follows):
+ *  - The Ultimate MoE Training Handbook (Hugging Face), section 1
+ *    "Introduction" (the three new concerns of a MoE layer: router, load
+ *    balancing, token exchange) and section 2.5 "First training of MoE"
+ *    (router picks 8 of 64 experts; tokens are sent to the selected experts
+ *    and the outputs returned; experts are SwiGLU without bias; router logits
+ *    in fp32; grouped GEMM for the local experts).
+ *  - Apex-3 code page, "What's inside", row "Fine-grained MoE" (sigmoid
+ *    router, per-expert bias that balances load and only steers selection,
+ *    experts as grouped GEMMs).
+ *  - KempnerForge README, "Features / Architecture" (softmax top-k and
+ *    DeepSeek-V3 sigmoid routers, shared experts, fine-grained experts).
+ *  - "Train Large Model from Scratch" README, "Configuration / Model
+ *    Configuration" (num_experts, num_experts_per_tok, moe_intermediate_size).
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are DEVICE pointers to row-major, contiguous data,
+ *    16-byte aligned (else MOE_ERR_ALIGN).  The caller owns every buffer;
+ *    the library allocates nothing, frees nothing and keeps no state between
+ *    calls.  Workspaces are caller-provided, sized by the query functions.
+ *  - bf16 means IEEE bfloat16 bit patterns (uint16 storage).
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No call synchronises or copies device->host: counts
+ *    and offsets stay on the device.
+ *  - Arguments are validated on the host before anything is launched; an
+ *    invalid call returns a non-zero status and launches nothing.  Launch
+ *    failures return MOE_ERR_HIP.  Nothing aborts or throws across the ABI.
+ *  - Results are bitwise deterministic for fixed inputs (no float atomics).
+ *  - Every output element is written (empty experts get zero weight grads).
+ *  - The library is stateless; concurrent calls on different streams with
+ *    disjoint outputs are safe.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* ---------------------------------------------------------------- status */
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,      /* bad shape, null required pointer, bad enum   */
+  MOE_ERR_ALIGN = 2,        /* a pointer is not 16-byte aligned              */
+  MOE_ERR_UNSUPPORTED = 3,  /* valid request this build does not implement   */
+  MOE_ERR_WORKSPACE = 4,    /* workspace smaller than the query's answer     */
+  MOE_ERR_HIP = 5           /* the HIP runtime reported an error             */
+};
+
+/* element type of activations, expert weights and their gradients */
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
+
+/* router score function (KempnerForge README, "Features / Architecture") */
+enum {
+  MOE_SOFTMAX = 0,  /* p = softmax(l) over experts; selection by l; gate = p
+                       (or p / sum of picked p when renorm != 0)            */
+  MOE_SIGMOID = 1   /* s = sigmoid(l); selection by fp32(s + bias); gate =
+                       s / sum of picked s (bias never enters the gate)     */
+};
+
+/* Layer description.  Limits: 1 <= E <= 256, 1 <= k <= min(E, 16);
+ * d_model, d_ff and d_ff_shared multiples of 64; T >= 0 (T = 0 is a no-op). */
+typedef struct moe_desc {
+  int64_t num_tokens;   /* T                                              */
+  int64_t d_model;      /* d                                              */
+  int64_t num_experts;  /* E (routed experts)                             */
+  int64_t top_k;        /* k (experts per token)                          */
+  int64_t d_ff;         /* f, hidden width of one routed expert           */
+  int64_t num_shared;   /* number of shared experts (0 = none)            */
+  int64_t d_ff_shared;  /* hidden width of one shared expert              */
+  int32_t score;        /* MOE_SOFTMAX or MOE_SIGMOID                     */
+  int32_t renorm;       /* softmax only: renormalise picked probabilities */
+  int32_t dtype;        /* MOE_F32 or MOE_BF16                            */
+  int32_t reserved;     /* must be 0                                      */
+} moe_desc_t;
+
+/* Parameters.  F = num_shared * d_ff_shared: the shared experts are stored
+ * concatenated along their hidden width, which is the same function as their
+ * sum.  Router weight and bias are always fp32 (Handbook 2.5: fp32 router). */
+typedef struct moe_weights {
+  const float *w_router;  /* [E, d] fp32                                      */
+  const float *bias;      /* [E] fp32, sigmoid selection only; NULL = zero    */
+  const void *w_gateup;   /* [E, 2f, d]: rows 0..f-1 gate W_g, f..2f-1 up W_u */
+  const void *w_down;     /* [E, d, f]                                        */
+  const void *s_gateup;   /* [2F, d] (gate rows, then up rows); NULL if F = 0 */
+  const void *s_down;     /* [d, F]; NULL if F = 0                            */
+} moe_weights_t;
+
+/* Forward intermediates kept for the backward pass (A = T*k rows).
+ * Caller-allocated; moe_forward fills them, moe_backward reads them. */
+typedef struct moe_saved {
+  float *logits;     /* [T, E] fp32 router logits                             */
+  int32_t *idx;      /* [T, k] picked experts, slot j = j-th best             */
+  float *gate;       /* [T, k] fp32 gates                                     */
+  int32_t *counts;   /* [E] rows per expert                                   */
+  int32_t *offsets;  /* [E+1] exclusive prefix of counts                      */
+  int32_t *pos;      /* [A] permuted row of assignment a = t*k + j            */
+  int32_t *src;      /* [A] assignment held by permuted row p (inverse of pos) */
+  void *x_perm;      /* [A, d] token rows in expert-contiguous order          */
+  void *preact;      /* [A, 2f] gate|up pre-activations; may be NULL in an
+                        inference-only forward (then backward is invalid)     */
+  void *h;           /* [A, f] silu(G) * U                                    */
+  void *y_perm;      /* [A, d] expert outputs, permuted order                 */
+  void *s_preact;    /* [T, 2F] shared pre-activations, or NULL if F = 0      */
+  void *s_h;         /* [T, F] shared hidden, or NULL if F = 0                */
+} moe_saved_t;
+
+/* Gradients written by moe_backward (overwritten, not accumulated). */
+typedef struct moe_grads {
+  float *d_w_router;  /* [E, d] fp32                      */
+  void *d_w_gateup;   /* [E, 2f, d]                       */
+  void *d_w_down;     /* [E, d, f]                        */
+  void *d_s_gateup;   /* [2F, d], NULL if F = 0           */
+  void *d_s_down;     /* [d, F], NULL if F = 0            */
+} moe_grads_t;
+
+/* grouped GEMM layouts and epilogues (see moe_grouped_gemm) */
+enum { MOE_GEMM_NT = 0, MOE_GEMM_NN = 1, MOE_GEMM_TN = 2 };
+enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
+
+/* workspace kinds for moe_workspace_bytes */
+enum { MOE_WS_PERMUTE = 0, MOE_WS_FORWARD = 1, MOE_WS_BACKWARD = 2 };
+
+/* ---------------------------------------------------------------- queries */
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char *moe_status_str(int status);
+
+/* MOE_ABI_VERSION of the built library. */
+int moe_abi_version(void);
+
+/* Number of int32 elements of the per-block expert histogram that moe_route
+ * writes and moe_permute reads: E * ceil(T / MOE_ROUTE_BLOCK).  0 if desc is
+ * invalid. */
+size_t moe_route_hist_elems(const moe_desc_t *desc);
+
+/* Bytes of device workspace the named call needs (0 if desc is invalid). */
+size_t moe_workspace_bytes(const moe_desc_t *desc, int which);
+
+/* Bytes of device workspace moe_grouped_gemm needs for this problem. */
+size_t moe_grouped_gemm_workspace_bytes(int layout, int dtype, int64_t G, int64_t M_total,
+                                        int64_t N, int64_t K);
+
+/* ---------------------------------------------------------------- calls */
+
+/* Router: scores, top-k selection and gates from fp32 logits.
+ * (Apex-3 "Fine-grained MoE"; KempnerForge "Features / Architecture".)
+ *   logits     [T, E] fp32 (in)
+ *   bias       [E] fp32 or NULL (sigmoid only; ignored for softmax)
+ *   idx        [T, k] int32 (out): experts by key descending, ties to the
+ *              lower expert index.  Softmax key: the logit.  Sigmoid key:
+ *              fp32(s + bias) with s = sigmoid(l) evaluated in fp64 and
+ *              rounded once to fp32.
+ *   gate       [T, k] fp32 (out)
+ *   block_hist [moe_route_hist_elems] int32 (out): per block of
+ *              MOE_ROUTE_BLOCK tokens, how many of its assignments went to
+ *              each expert (layout [E][blocks]); consumed by moe_permute. */
+int moe_route(const moe_desc_t *desc, const float *logits, const float *bias, int32_t *idx,
+              float *gate, int32_t *block_hist, void *stream);
+
+/* Token permutation into expert-contiguous order ("tokens must be sent to the
+ * selected experts", Handbook 2.5): histogram (from moe_route), prefix scan
+ * over experts and blocks, stable scatter.
+ *   x       [T, d] (in, desc dtype);  idx [T, k], block_hist (in)
+ *   counts  [E], offsets [E+1] (out): offsets[E] = T*k
+ *   pos     [T*k] (out): row of assignment a = t*k + j; rows of one expert
+ *           are ordered by increasing a (stable)
+ *   src     [T*k] (out): src[pos[a]] = a
+ *   x_perm  [T*k, d] (out): x_perm[pos[t*k+j]] = x[t]
+ *   ws      >= moe_workspace_bytes(desc, MOE_WS_PERMUTE) bytes of scratch */
+int moe_permute(const moe_desc_t *desc, const void *x, const int32_t *idx,
+                const int32_t *block_hist, int32_t *counts, int32_t *offsets, int32_t *pos,
+                int32_t *src, void *x_perm, void *ws, size_t ws_bytes, void *stream);
+
+/* Grouped GEMM over G groups of rows ("experts run as grouped GEMMs", Apex-3
+ * "Fine-grained MoE"; Handbook 2.5 grouped GEMM for the local experts).
+ * group_offsets: device int32 [G+1], non-decreasing, offsets[0] = 0,
+ * offsets[G] = M_total; group g owns rows [offsets[g], offsets[g+1]).
+ * Accumulation is fp32; C is rounded once to `dtype`.
+ *   MOE_GEMM_NT (forward):  C[m,n] = sum_k A[m,k] B[g,n,k]
+ *        A [M_total,K], B [G,N,K], C [M_total,N]
+ *        MOE_EPI_SWIGLU: N = 2F, B rows 0..F-1 are gate, F..2F-1 up;
+ *        C [M_total,F] = silu(gate) * up; aux [M_total,2F] receives the
+ *        pre-activations gate|up (aux may be NULL).
+ *   MOE_GEMM_NN (data gradient): C[m,k] = sum_n A[m,n] B[g,n,k]
+ *        A [M_total,N], B [G,N,K], C [M_total,K]
+ *        MOE_EPI_DSWIGLU: the product is dH [M_total,K]; aux [M_total,2K]
+ *        holds the forward pre-activations G|U; C [M_total,2K] receives
+ *        dG = dH*U*silu'(G) | dU = dH*silu(G).
+ *   MOE_GEMM_TN (weight gradient): C[g,n,k] = sum_{m in g} A[m,n] B[m,k]
+ *        A [M_total,N], B [M_total,K], C [G,N,K]; empty groups give zeros.
+ * N and K multiples of 64.  ws >= moe_grouped_gemm_workspace_bytes(...). */
+int moe_grouped_gemm(int layout, int epilogue, int dtype, int64_t G, int64_t M_total, int64_t N,
+                     int64_t K, const int32_t *group_offsets, const void *A, const void *B, void *C,
+                     void *aux, void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted combine / unpermute ("the experts' output must be returned",
+ * Handbook 2.5):  y[t] = sum_{j<k} gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t])
+ * accumulated in fp32 in slot order, shared last, rounded once.
+ *   y_perm [T*k, d], gate [T, k] fp32, pos [T*k], shared_y [T, d] or NULL,
+ *   y [T, d] (out; may alias shared_y). */
+int moe_combine(const moe_desc_t *desc, const void *y_perm, const float *gate,
+                const int32_t *pos, const void *shared_y, void *y, void *stream);
+
+/* Whole forward pass: router GEMM (fp32) -> route -> permute -> gate/up
+ * grouped GEMM with SwiGLU -> down grouped GEMM -> shared experts -> combine.
+ *   x [T, d] (in), y [T, d] (out), saved (out, all buffers caller-allocated)
+ *   ws >= moe_workspace_bytes(desc, MOE_WS_FORWARD) */
+int moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *x, void *y,
+                const moe_saved_t *saved, void *ws, size_t ws_bytes, void *stream);
+
+/* Whole backward pass for upstream gradient dy [T, d]: combine backward
+ * (gate gradient), router backward (through the gates only; the bias gets no
+ * gradient), down and gate/up data and weight gradients, shared experts,
+ * unpermute-sum of the input gradient.
+ *   x [T, d] (the forward input), saved (from moe_forward), dy [T, d] (in),
+ *   dx [T, d] (out), grads (out)
+ *   ws >= moe_workspace_bytes(desc, MOE_WS_BACKWARD) */
+int moe_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *x,
+                 const moe_saved_t *saved, const void *dy, void *dx, const moe_grads_t *grads,
+                 void *ws, size_t ws_bytes, void *stream);
+
+/* tokens per histogram block of moe_route / moe_permute */
+#define MOE_ROUTE_BLOCK 32
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

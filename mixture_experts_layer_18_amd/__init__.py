@@ -1,0 +1,10 @@
+"""MI355X (gfx950) mixture-of-experts layer: forward and backward in HIP.
+
+The compute lives in the HIP library libmoe_mi355x.so (C ABI: include/moe.h);
+this package is its thin Python binding.  Importing the package does not load
+the library; the first call does, and fails loudly if it is not built."""
+from .api import (  # noqa: F401
+    MoeError, make_desc, desc_from_config, route_hist_elems, workspace_bytes, grouped_gemm_workspace_bytes,
+    moe_route, moe_permute, moe_grouped_gemm, moe_combine, moe_forward, moe_backward,
+    alloc_saved, alloc_grads, alloc_workspace,
+)

@@ -1,0 +1,86 @@
+"""ctypes view of the C ABI in include/moe.h (structs, enums, signatures).
+
+Loading fails loudly if the built library is missing: there is no fallback."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libmoe_mi355x.so")
+HEADER = os.path.join(os.path.dirname(PKG), "include", "moe.h")
+
+c_i32, c_i64, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p
+
+MOE_OK, MOE_ERR_INVALID, MOE_ERR_ALIGN, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = range(6)
+MOE_F32, MOE_BF16 = 0, 1
+MOE_SOFTMAX, MOE_SIGMOID = 0, 1
+MOE_GEMM_NT, MOE_GEMM_NN, MOE_GEMM_TN = 0, 1, 2
+MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
+MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
+MOE_ROUTE_BLOCK = 32
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("num_tokens", c_i64), ("d_model", c_i64), ("num_experts", c_i64), ("top_k", c_i64),
+                ("d_ff", c_i64), ("num_shared", c_i64), ("d_ff_shared", c_i64), ("score", c_i32),
+                ("renorm", c_i32), ("dtype", c_i32), ("reserved", c_i32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("w_router", c_vp), ("bias", c_vp), ("w_gateup", c_vp), ("w_down", c_vp),
+                ("s_gateup", c_vp), ("s_down", c_vp)]
+
+
+class MoeSaved(ctypes.Structure):
+    _fields_ = [("logits", c_vp), ("idx", c_vp), ("gate", c_vp), ("counts", c_vp), ("offsets", c_vp),
+                ("pos", c_vp), ("src", c_vp), ("x_perm", c_vp), ("preact", c_vp), ("h", c_vp),
+                ("y_perm", c_vp), ("s_preact", c_vp), ("s_h", c_vp)]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [("d_w_router", c_vp), ("d_w_gateup", c_vp), ("d_w_down", c_vp), ("d_s_gateup", c_vp),
+                ("d_s_down", c_vp)]
+
+
+_P = ctypes.POINTER
+SIGNATURES = {
+    "moe_status_str": (ctypes.c_char_p, [c_i32]),
+    "moe_abi_version": (c_i32, []),
+    "moe_route_hist_elems": (c_sz, [_P(MoeDesc)]),
+    "moe_workspace_bytes": (c_sz, [_P(MoeDesc), c_i32]),
+    "moe_grouped_gemm_workspace_bytes": (c_sz, [c_i32, c_i32, c_i64, c_i64, c_i64, c_i64]),
+    "moe_route": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_permute": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_grouped_gemm": (c_i32, [c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                 c_vp, c_vp, c_sz, c_vp]),
+    "moe_combine": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
+    "moe_forward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, c_vp, _P(MoeSaved), c_vp, c_sz, c_vp]),
+    "moe_backward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, _P(MoeSaved), c_vp, c_vp, _P(MoeGrads),
+                             c_vp, c_sz, c_vp]),
+}
+
+_lib = None
+
+
+def header_functions():
+    """Names of the functions declared in include/moe.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", text, re.M)))
+
+
+def load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"HIP library not built: {LIB_PATH} is missing "
+                           "(run python -m mixture_experts_layer_18_amd.build)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib

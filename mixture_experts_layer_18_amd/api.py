@@ -1,0 +1,155 @@
+"""Python binding of the C ABI (include/moe.h), same call names.
+
+Argument marshalling only: torch tensors are passed as device pointers and
+the current torch stream as the HIP stream; every step of the layer runs in
+the HIP library.  Buffer allocation helpers use torch for device memory.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+DTYPES = {"f32": L.MOE_F32, "bf16": L.MOE_BF16}
+TORCH_DTYPE = {L.MOE_F32: torch.float32, L.MOE_BF16: torch.bfloat16}
+SCORES = {"softmax": L.MOE_SOFTMAX, "sigmoid": L.MOE_SIGMOID}
+LAYOUTS = {"NT": L.MOE_GEMM_NT, "NN": L.MOE_GEMM_NN, "TN": L.MOE_GEMM_TN}
+EPILOGUES = {"none": L.MOE_EPI_NONE, "swiglu": L.MOE_EPI_SWIGLU, "dswiglu": L.MOE_EPI_DSWIGLU}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = L.load().moe_status_str(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _check(status: int, where: str):
+    if status != L.MOE_OK:
+        raise MoeError(status, where)
+
+
+def _p(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live in GPU memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_desc(T, d, E, k, f, n_shared=0, f_shared=0, score="sigmoid", renorm=False, dtype="bf16"):
+    return L.MoeDesc(num_tokens=T, d_model=d, num_experts=E, top_k=k, d_ff=f, num_shared=n_shared,
+                     d_ff_shared=f_shared if n_shared else 0, score=SCORES[score], renorm=int(bool(renorm)),
+                     dtype=DTYPES[dtype], reserved=0)
+
+
+def desc_from_config(cfg, T=None):
+    return make_desc(cfg.T if T is None else T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.n_shared, cfg.f_shared,
+                     cfg.score, cfg.renorm, cfg.dtype)
+
+
+# ------------------------------------------------------------------ queries
+def route_hist_elems(desc) -> int:
+    return int(L.load().moe_route_hist_elems(ctypes.byref(desc)))
+
+
+def workspace_bytes(desc, which: str) -> int:
+    w = {"permute": L.MOE_WS_PERMUTE, "forward": L.MOE_WS_FORWARD, "backward": L.MOE_WS_BACKWARD}[which]
+    return int(L.load().moe_workspace_bytes(ctypes.byref(desc), w))
+
+
+def grouped_gemm_workspace_bytes(layout, dtype, G, M_total, N, K) -> int:
+    return int(L.load().moe_grouped_gemm_workspace_bytes(LAYOUTS[layout], DTYPES[dtype], G, M_total, N, K))
+
+
+# ------------------------------------------------------------------ calls
+def moe_route(desc, logits, bias, idx, gate, block_hist, stream=None):
+    _check(L.load().moe_route(ctypes.byref(desc), _p(logits), _p(bias), _p(idx), _p(gate), _p(block_hist),
+                              _stream(stream)), "moe_route")
+
+
+def moe_permute(desc, x, idx, block_hist, counts, offsets, pos, src, x_perm, ws, stream=None):
+    _check(L.load().moe_permute(ctypes.byref(desc), _p(x), _p(idx), _p(block_hist), _p(counts), _p(offsets),
+                                _p(pos), _p(src), _p(x_perm), _p(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "moe_permute")
+
+
+def moe_grouped_gemm(layout, epilogue, dtype, G, M_total, N, K, group_offsets, A, B, C, aux=None, ws=None,
+                     stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(L.load().moe_grouped_gemm(LAYOUTS[layout], EPILOGUES[epilogue], DTYPES[dtype], G, M_total, N, K,
+                                     _p(group_offsets), _p(A), _p(B), _p(C), _p(aux), _p(ws), nbytes,
+                                     _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_combine(desc, y_perm, gate, pos, shared_y, y, stream=None):
+    _check(L.load().moe_combine(ctypes.byref(desc), _p(y_perm), _p(gate), _p(pos), _p(shared_y), _p(y),
+                                _stream(stream)), "moe_combine")
+
+
+def _weights(w: dict) -> L.MoeWeights:
+    return L.MoeWeights(*(_p(w.get(n)) for n in ("w_router", "bias", "w_gateup", "w_down", "s_gateup",
+                                                  "s_down")))
+
+
+SAVED_FIELDS = ("logits", "idx", "gate", "counts", "offsets", "pos", "src", "x_perm", "preact", "h", "y_perm",
+                "s_preact", "s_h")
+GRAD_FIELDS = ("d_w_router", "d_w_gateup", "d_w_down", "d_s_gateup", "d_s_down")
+
+
+def moe_forward(desc, weights: dict, x, y, saved: dict, ws, stream=None):
+    w = _weights(weights)
+    s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
+    _check(L.load().moe_forward(ctypes.byref(desc), ctypes.byref(w), _p(x), _p(y), ctypes.byref(s), _p(ws),
+                                ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
+
+
+def moe_backward(desc, weights: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None):
+    w = _weights(weights)
+    s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
+    g = L.MoeGrads(*(_p(grads.get(n)) for n in GRAD_FIELDS))
+    _check(L.load().moe_backward(ctypes.byref(desc), ctypes.byref(w), _p(x), ctypes.byref(s), _p(dy), _p(dx),
+                                 ctypes.byref(g), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_backward")
+
+
+# ------------------------------------------------------------------ buffers (torch device memory)
+def alloc_saved(desc, device="cuda", training=True) -> dict:
+    T, d, E, k, f = desc.num_tokens, desc.d_model, desc.num_experts, desc.top_k, desc.d_ff
+    F = desc.num_shared * desc.d_ff_shared
+    A = T * k
+    dt = TORCH_DTYPE[desc.dtype]
+    e = lambda *s, dtype=dt: torch.empty(*s, dtype=dtype, device=device)  # noqa: E731
+    out = dict(logits=e(T, E, dtype=torch.float32), idx=e(T, k, dtype=torch.int32),
+               gate=e(T, k, dtype=torch.float32), counts=e(E, dtype=torch.int32),
+               offsets=e(E + 1, dtype=torch.int32), pos=e(A, dtype=torch.int32), src=e(A, dtype=torch.int32),
+               x_perm=e(A, d), preact=e(A, 2 * f) if training else None, h=e(A, f), y_perm=e(A, d),
+               s_preact=e(T, 2 * F) if (F and training) else None, s_h=e(T, F) if F else None)
+    return out
+
+
+def alloc_grads(desc, device="cuda") -> dict:
+    d, E, f = desc.d_model, desc.num_experts, desc.d_ff
+    F = desc.num_shared * desc.d_ff_shared
+    dt = TORCH_DTYPE[desc.dtype]
+    return dict(d_w_router=torch.empty(E, d, dtype=torch.float32, device=device),
+                d_w_gateup=torch.empty(E, 2 * f, d, dtype=dt, device=device),
+                d_w_down=torch.empty(E, d, f, dtype=dt, device=device),
+                d_s_gateup=torch.empty(2 * F, d, dtype=dt, device=device) if F else None,
+                d_s_down=torch.empty(d, F, dtype=dt, device=device) if F else None)
+
+
+def alloc_workspace(desc, which: str, device="cuda") -> torch.Tensor:
+    n = max(workspace_bytes(desc, which), 256)
+    return torch.empty(n, dtype=torch.uint8, device=device)

@@ -1,0 +1,399 @@
+// C ABI of the MoE layer library: argument validation, workspace layout and
+// the launch sequence of the forward and backward passes.  Every check runs
+// on the host before anything is launched; the library allocates nothing.
+#include "kernels.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+inline size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline size_t esize(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+int check_desc(const moe_desc_t* d) {
+  if (!d) return MOE_ERR_INVALID;
+  if (d->num_tokens < 0 || d->d_model <= 0 || d->num_experts < 1 || d->num_experts > 256)
+    return MOE_ERR_INVALID;
+  if (d->top_k < 1 || d->top_k > 16 || d->top_k > d->num_experts) return MOE_ERR_INVALID;
+  if (d->d_ff <= 0 || d->d_model % 64 || d->d_ff % 64) return MOE_ERR_INVALID;
+  if (d->num_shared < 0) return MOE_ERR_INVALID;
+  if (d->num_shared > 0 && (d->d_ff_shared <= 0 || d->d_ff_shared % 64)) return MOE_ERR_INVALID;
+  if (d->score != MOE_SOFTMAX && d->score != MOE_SIGMOID) return MOE_ERR_INVALID;
+  if (d->renorm != 0 && d->renorm != 1) return MOE_ERR_INVALID;
+  if (d->dtype != MOE_F32 && d->dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (d->reserved != 0) return MOE_ERR_INVALID;
+  // row indices are int32: every permuted row index must fit
+  if (d->num_tokens * d->top_k >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (d->d_model > 65536 || d->d_ff > 65536 || d->num_shared * d->d_ff_shared > 65536)
+    return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+inline int64_t shared_width(const moe_desc_t* d) { return d->num_shared * d->d_ff_shared; }
+inline int64_t nblocks(const moe_desc_t* d) { return cdiv64(d->num_tokens, MOE_ROUTE_BLOCK); }
+
+// A bump allocator over the caller's workspace (sizes only when base is null).
+struct Carve {
+  char* base;
+  size_t off = 0;
+  explicit Carve(void* b) : base((char*)b) {}
+  void* take(size_t n) {
+    void* p = base ? base + off : nullptr;
+    off += align_up(n);
+    return p;
+  }
+};
+
+GemmProblem gp(int layout, int epi, int ta, int tb, int tc, int64_t G, int64_t M, int64_t N,
+               int64_t K, const int32_t* off, const void* A, const void* B, void* C, void* aux) {
+  GemmProblem p;
+  p.layout = layout;
+  p.epilogue = epi;
+  p.ta = ta;
+  p.tb = tb;
+  p.tc = tc;
+  p.G = G;
+  p.M_total = M;
+  p.N = N;
+  p.K = K;
+  p.offsets = off;
+  p.A = A;
+  p.B = B;
+  p.C = C;
+  p.aux = aux;
+  return p;
+}
+
+// The backward pass's weight-gradient products that may need split partials.
+size_t backward_gemm_ws(const moe_desc_t* d) {
+  const int dt = d->dtype;
+  const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, f = d->d_ff;
+  const int64_t A = T * d->top_k, F = shared_width(d);
+  size_t m = 0;
+  auto upd = [&](const GemmProblem& p) {
+    const size_t b = gemm_workspace_bytes(p);
+    if (b > m) m = b;
+  };
+  upd(gp(MOE_GEMM_TN, 0, MOE_F32, dt, MOE_F32, 1, T, E, D, 0, 0, 0, 0, 0));
+  upd(gp(MOE_GEMM_TN, 0, dt, dt, dt, E, A, D, f, 0, 0, 0, 0, 0));
+  upd(gp(MOE_GEMM_TN, 0, dt, dt, dt, E, A, 2 * f, D, 0, 0, 0, 0, 0));
+  if (F > 0) {
+    upd(gp(MOE_GEMM_TN, 0, dt, dt, dt, 1, T, D, F, 0, 0, 0, 0, 0));
+    upd(gp(MOE_GEMM_TN, 0, dt, dt, dt, 1, T, 2 * F, D, 0, 0, 0, 0, 0));
+  }
+  return m;
+}
+
+struct FwdWs {
+  int32_t* hist;
+  int32_t* base;
+  int32_t* one_group;  // [0, T]
+};
+size_t fwd_ws(const moe_desc_t* d, void* ws, FwdWs* out) {
+  Carve c(ws);
+  const size_t nb = (size_t)d->num_experts * nblocks(d) * sizeof(int32_t);
+  FwdWs w;
+  w.hist = (int32_t*)c.take(nb);
+  w.base = (int32_t*)c.take(nb);
+  w.one_group = (int32_t*)c.take(2 * sizeof(int32_t));
+  if (out) *out = w;
+  return c.off;
+}
+
+struct BwdWs {
+  void* dy_perm;   // [A, d]; reused for dx_perm once the down gradients are done
+  void* dgu;       // [A, 2f]
+  float* dlogits;  // [T, E]
+  void* s_dgu;     // [T, 2F]
+  void* dx_shared; // [T, d]
+  int32_t* one_group;
+  void* gemm;      // split partials
+  size_t gemm_bytes;
+};
+size_t bwd_ws(const moe_desc_t* d, void* ws, BwdWs* out) {
+  Carve c(ws);
+  const int64_t T = d->num_tokens, D = d->d_model, f = d->d_ff, A = T * d->top_k;
+  const int64_t F = shared_width(d);
+  const size_t es = esize(d->dtype);
+  BwdWs w;
+  w.dy_perm = c.take((size_t)A * D * es);
+  w.dgu = c.take((size_t)A * 2 * f * es);
+  w.dlogits = (float*)c.take((size_t)T * d->num_experts * sizeof(float));
+  w.s_dgu = F > 0 ? c.take((size_t)T * 2 * F * es) : nullptr;
+  w.dx_shared = F > 0 ? c.take((size_t)T * D * es) : nullptr;
+  w.one_group = (int32_t*)c.take(2 * sizeof(int32_t));
+  w.gemm_bytes = backward_gemm_ws(d);
+  w.gemm = c.take(w.gemm_bytes);
+  if (out) *out = w;
+  return c.off;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+#define MOE_TRY(expr)                         \
+  do {                                        \
+    hipError_t _e = (expr);                   \
+    if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(int s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID: invalid argument";
+    case MOE_ERR_ALIGN: return "MOE_ERR_ALIGN: pointer not 16-byte aligned";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape not supported by this build";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace too small";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+size_t moe_route_hist_elems(const moe_desc_t* d) {
+  if (check_desc(d) != MOE_OK) return 0;
+  return (size_t)d->num_experts * (size_t)nblocks(d);
+}
+
+size_t moe_workspace_bytes(const moe_desc_t* d, int which) {
+  if (check_desc(d) != MOE_OK) return 0;
+  switch (which) {
+    case MOE_WS_PERMUTE: return align_up((size_t)d->num_experts * nblocks(d) * sizeof(int32_t));
+    case MOE_WS_FORWARD: return fwd_ws(d, nullptr, nullptr);
+    case MOE_WS_BACKWARD: return bwd_ws(d, nullptr, nullptr);
+    default: return 0;
+  }
+}
+
+static int check_gemm(int layout, int epi, int dtype, int64_t G, int64_t M, int64_t N, int64_t K) {
+  if (layout < MOE_GEMM_NT || layout > MOE_GEMM_TN) return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_SWIGLU && layout != MOE_GEMM_NT) return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_DSWIGLU && layout != MOE_GEMM_NN) return MOE_ERR_INVALID;
+  if (epi < MOE_EPI_NONE || epi > MOE_EPI_DSWIGLU) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (G < 1 || G > 256 || M < 0 || N <= 0 || K <= 0) return MOE_ERR_INVALID;
+  if (N % 64 || K % 64) return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_SWIGLU && (N % 128)) return MOE_ERR_INVALID;
+  if (M >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_grouped_gemm_workspace_bytes(int layout, int dtype, int64_t G, int64_t M, int64_t N,
+                                        int64_t K) {
+  if (check_gemm(layout, MOE_EPI_NONE, dtype, G, M, N, K) != MOE_OK) return 0;
+  return gemm_workspace_bytes(gp(layout, 0, dtype, dtype, dtype, G, M, N, K, 0, 0, 0, 0, 0));
+}
+
+int moe_route(const moe_desc_t* d, const float* logits, const float* bias, int32_t* idx,
+              float* gate, int32_t* block_hist, void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (d->num_tokens > 0 && (!logits || !idx || !gate || !block_hist)) return MOE_ERR_INVALID;
+  if (!aligned16(logits) || !aligned16(idx) || !aligned16(gate) || !aligned16(block_hist) ||
+      !aligned16(bias))
+    return MOE_ERR_ALIGN;
+  return hip_status(launch_route(logits, d->score == MOE_SIGMOID ? bias : nullptr,
+                                 (int)d->num_tokens, (int)d->num_experts, (int)d->top_k,
+                                 d->score, d->renorm, idx, gate, block_hist,
+                                 (hipStream_t)stream));
+}
+
+int moe_permute(const moe_desc_t* d, const void* x, const int32_t* idx,
+                const int32_t* block_hist, int32_t* counts, int32_t* offsets, int32_t* pos,
+                int32_t* src, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (!counts || !offsets) return MOE_ERR_INVALID;
+  if (d->num_tokens > 0 && (!x || !idx || !block_hist || !pos || !src || !x_perm || !ws))
+    return MOE_ERR_INVALID;
+  const void* ptrs[] = {x, idx, block_hist, counts, offsets, pos, src, x_perm, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe_workspace_bytes(d, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
+  return hip_status(launch_permute(x, d->dtype, idx, block_hist, (int)d->num_tokens,
+                                   (int)d->d_model, (int)d->num_experts, (int)d->top_k,
+                                   (int32_t*)ws, counts, offsets, pos, src, x_perm,
+                                   (hipStream_t)stream));
+}
+
+int moe_grouped_gemm(int layout, int epi, int dtype, int64_t G, int64_t M, int64_t N, int64_t K,
+                     const int32_t* off, const void* A, const void* B, void* C, void* aux,
+                     void* ws, size_t ws_bytes, void* stream) {
+  int s = check_gemm(layout, epi, dtype, G, M, N, K);
+  if (s) return s;
+  if (!off || !B || !C) return MOE_ERR_INVALID;
+  if (M > 0 && !A) return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_DSWIGLU && !aux) return MOE_ERR_INVALID;
+  const void* ptrs[] = {off, A, B, C, aux, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  GemmProblem p = gp(layout, epi, dtype, dtype, dtype, G, M, N, K, off, A, B, C, aux);
+  if (ws_bytes < gemm_workspace_bytes(p) || (gemm_workspace_bytes(p) && !ws))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(launch_grouped_gemm(p, ws, ws_bytes, (hipStream_t)stream));
+}
+
+int moe_combine(const moe_desc_t* d, const void* y_perm, const float* gate, const int32_t* pos,
+                const void* shared_y, void* y, void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (d->num_tokens > 0 && (!y_perm || !gate || !pos || !y)) return MOE_ERR_INVALID;
+  const void* ptrs[] = {y_perm, gate, pos, shared_y, y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  return hip_status(launch_combine(d->dtype, y_perm, gate, pos, shared_y, y,
+                                   (int)d->num_tokens, (int)d->d_model, (int)d->top_k,
+                                   (hipStream_t)stream));
+}
+
+int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
+                const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (!w || !sv) return MOE_ERR_INVALID;
+  const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
+  const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
+  const int dt = d->dtype;
+  if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
+  if (F > 0 && (!w->s_gateup || !w->s_down || !sv->s_h)) return MOE_ERR_INVALID;
+  if (!sv->counts || !sv->offsets) return MOE_ERR_INVALID;
+  if (T > 0 && (!x || !y || !sv->logits || !sv->idx || !sv->gate || !sv->pos || !sv->src ||
+                !sv->x_perm || !sv->h || !sv->y_perm || !ws))
+    return MOE_ERR_INVALID;
+  const void* ptrs[] = {x, y, w->w_router, w->bias, w->w_gateup, w->w_down, w->s_gateup,
+                        w->s_down, sv->logits, sv->idx, sv->gate, sv->counts, sv->offsets,
+                        sv->pos, sv->src, sv->x_perm, sv->preact, sv->h, sv->y_perm,
+                        sv->s_preact, sv->s_h, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe_workspace_bytes(d, MOE_WS_FORWARD)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  if (T == 0) {
+    MOE_TRY(launch_fill_i32(sv->counts, E, 0, st));
+    MOE_TRY(launch_fill_i32(sv->offsets, E + 1, 0, st));
+    return MOE_OK;
+  }
+  FwdWs fw;
+  fwd_ws(d, ws, &fw);
+  MOE_TRY(launch_group_offsets_1(fw.one_group, (int32_t)T, st));
+  // 1. router logits in fp32
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, MOE_F32, MOE_F32, 1, T, E, D,
+                                 fw.one_group, x, w->w_router, sv->logits, nullptr),
+                              nullptr, 0, st));
+  // 2. scores, top-k, gates, per-block histogram
+  MOE_TRY(launch_route(sv->logits, d->score == MOE_SIGMOID ? w->bias : nullptr, (int)T, (int)E,
+                       (int)k, d->score, d->renorm, sv->idx, sv->gate, fw.hist, st));
+  // 3. permutation into expert-contiguous rows
+  MOE_TRY(launch_permute(x, dt, sv->idx, fw.hist, (int)T, (int)D, (int)E, (int)k, fw.base,
+                         sv->counts, sv->offsets, sv->pos, sv->src, sv->x_perm, st));
+  // 4. gate/up grouped GEMM with the SwiGLU activation
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D,
+                                 sv->offsets, sv->x_perm, w->w_gateup, sv->h, sv->preact),
+                              nullptr, 0, st));
+  // 5. down grouped GEMM
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
+                                 sv->h, w->w_down, sv->y_perm, nullptr),
+                              nullptr, 0, st));
+  // 6. shared experts on every token; their output lands in y
+  if (F > 0) {
+    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, 1, T, 2 * F, D,
+                                   fw.one_group, x, w->s_gateup, sv->s_h, sv->s_preact),
+                                nullptr, 0, st));
+    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
+                                   fw.one_group, sv->s_h, w->s_down, y, nullptr),
+                                nullptr, 0, st));
+  }
+  // 7. weighted combine (+ shared output)
+  MOE_TRY(launch_combine(dt, sv->y_perm, sv->gate, sv->pos, F > 0 ? y : nullptr, y, (int)T,
+                         (int)D, (int)k, st));
+  return MOE_OK;
+}
+
+int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
+                 const moe_saved_t* sv, const void* dy, void* dx, const moe_grads_t* g,
+                 void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (!w || !sv || !g) return MOE_ERR_INVALID;
+  const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
+  const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
+  const int dt = d->dtype;
+  if (d->dtype == MOE_BF16 ? D > 4096 : D > 2048) return MOE_ERR_UNSUPPORTED;
+  if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
+  if (!g->d_w_router || !g->d_w_gateup || !g->d_w_down) return MOE_ERR_INVALID;
+  if (F > 0 && (!w->s_gateup || !w->s_down || !sv->s_h || !sv->s_preact || !g->d_s_gateup ||
+                !g->d_s_down))
+    return MOE_ERR_INVALID;
+  if (!sv->offsets) return MOE_ERR_INVALID;
+  if (T > 0 && (!x || !dy || !dx || !sv->logits || !sv->idx || !sv->gate || !sv->pos ||
+                !sv->x_perm || !sv->preact || !sv->h || !sv->y_perm || !ws))
+    return MOE_ERR_INVALID;
+  const void* ptrs[] = {x, dy, dx, w->w_router, w->w_gateup, w->w_down, w->s_gateup, w->s_down,
+                        sv->logits, sv->idx, sv->gate, sv->offsets, sv->pos, sv->x_perm,
+                        sv->preact, sv->h, sv->y_perm, sv->s_preact, sv->s_h, g->d_w_router,
+                        g->d_w_gateup, g->d_w_down, g->d_s_gateup, g->d_s_down, ws};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (ws_bytes < moe_workspace_bytes(d, MOE_WS_BACKWARD)) return MOE_ERR_WORKSPACE;
+  hipStream_t st = (hipStream_t)stream;
+  BwdWs bw;
+  bwd_ws(d, ws, &bw);
+  MOE_TRY(launch_group_offsets_1(bw.one_group, (int32_t)T, st));
+  // 1. combine backward + router backward (dlogits)
+  MOE_TRY(launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
+                             d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
+                             bw.dlogits, st));
+  // 2. down data gradient fused with the SwiGLU derivative -> dG | dU
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
+                                 sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
+                              nullptr, 0, st));
+  // 3. down weight gradient
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
+                                 bw.dy_perm, sv->h, g->d_w_down, nullptr),
+                              bw.gemm, bw.gemm_bytes, st));
+  // 4. gate/up weight gradient
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
+                                 sv->offsets, bw.dgu, sv->x_perm, g->d_w_gateup, nullptr),
+                              bw.gemm, bw.gemm_bytes, st));
+  // 5. gate/up data gradient (written over dy_perm, which is no longer needed)
+  void* dx_perm = bw.dy_perm;
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
+                                 sv->offsets, bw.dgu, w->w_gateup, dx_perm, nullptr),
+                              nullptr, 0, st));
+  // 6. shared experts
+  if (F > 0) {
+    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
+                                   bw.one_group, dy, w->s_down, bw.s_dgu, sv->s_preact),
+                                nullptr, 0, st));
+    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
+                                   bw.one_group, dy, sv->s_h, g->d_s_down, nullptr),
+                                bw.gemm, bw.gemm_bytes, st));
+    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
+                                   bw.one_group, bw.s_dgu, x, g->d_s_gateup, nullptr),
+                                bw.gemm, bw.gemm_bytes, st));
+    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
+                                   bw.one_group, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
+                                nullptr, 0, st));
+  }
+  // 7. router weight gradient (fp32)
+  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, MOE_F32, dt, MOE_F32, 1, T, E, D,
+                                 bw.one_group, bw.dlogits, x, g->d_w_router, nullptr),
+                              bw.gemm, bw.gemm_bytes, st));
+  // 8. input gradient: permuted rows + shared + router terms
+  const int dense_router = (d->score == MOE_SOFTMAX && !d->renorm) ? 1 : 0;
+  MOE_TRY(launch_unpermute_sum(dt, dx_perm, sv->pos, F > 0 ? bw.dx_shared : nullptr, bw.dlogits,
+                               sv->idx, w->w_router, dense_router, (int)T, (int)D, (int)E, (int)k,
+                               dx, st));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,314 @@
+// Combine (unpermute + gate-weighted sum), its backward with the router
+// gradient, and the unpermute-sum of the input gradient (gfx950).
+//
+// The combine returns each expert's output to its token and weights it by the
+// gate (Ultimate MoE Training Handbook, section 2.5: the experts' outputs must
+// be returned to where they are needed); shared experts are added ungated
+// (KempnerForge README, "Features / Architecture").  The router only receives
+// gradient through the gate values, never through the selection, and the
+// selection bias receives none (Apex-3 code page, "Fine-grained MoE"; the
+// Handbook's single-expert check in 2.5, where the router gets zero gradient).
+//
+// All three kernels are HBM-bound row gathers: one wavefront per token, rows
+// moved as 16-byte vectors, fp32 accumulation in a fixed order, one rounding.
+#include "kernels.h"
+
+namespace moe {
+
+// 16-byte vector <-> floats for both storage types
+template <typename T> struct Vec;
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;
+  static MOE_DEV void load(const bf16_t* p, float* f) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  }
+  static MOE_DEV void store(bf16_t* p, const float* f) {
+    u32x4 v;
+    v.x = pack_bf16x2(f[0], f[1]); v.y = pack_bf16x2(f[2], f[3]);
+    v.z = pack_bf16x2(f[4], f[5]); v.w = pack_bf16x2(f[6], f[7]);
+    *reinterpret_cast<u32x4*>(p) = v;
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  static MOE_DEV void load(const float* p, float* f) {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  }
+  static MOE_DEV void store(float* p, const float* f) {
+    *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
+  }
+};
+
+// y[t] = sum_j gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t]), fp32, one rounding
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm,
+                                                      const float* __restrict__ gate,
+                                                      const int32_t* __restrict__ pos,
+                                                      const T* shared_y, T* y, int Tn, int d,
+                                                      int k) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int nvec = d / VN;
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[VN];
+#pragma unroll
+    for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const float g = gate[(int64_t)t * k + j];
+      const int64_t p = pos[(int64_t)t * k + j];
+      float v[VN];
+      Vec<T>::load(y_perm + p * d + (int64_t)c * VN, v);
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] = fmaf(g, v[u], acc[u]);
+    }
+    if (shared_y) {
+      float v[VN];
+      Vec<T>::load(shared_y + (int64_t)t * d + (int64_t)c * VN, v);
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] += v[u];
+    }
+    Vec<T>::store(y + (int64_t)t * d + (int64_t)c * VN, acc);
+  }
+}
+
+MOE_DEV float sigmoid_rounded_f(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
+
+// Combine backward and router backward for one token per wavefront:
+//   dy_perm[pos[t,j]] = gate[t,j] * dy[t]
+//   dgate[t,j]        = <dy[t], y_perm[pos[t,j]]>          (fp32)
+//   dlogits[t,:]      from dgate through the gate function (selection fixed)
+// Up to 8 vectors per lane of dy are kept in registers (d <= 4096 bf16).
+template <typename T, int MAXV>
+__global__ __launch_bounds__(256) void combine_bwd_kernel(
+    const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ gate,
+    const int32_t* __restrict__ pos, const int32_t* __restrict__ idx,
+    const float* __restrict__ logits, int score, int renorm, int Tn, int d, int E, int k,
+    T* __restrict__ dy_perm, float* __restrict__ dlogits) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int nvec = d / VN;
+  float dyv[MAXV][VN];
+#pragma unroll
+  for (int q = 0; q < MAXV; ++q) {
+    const int c = lane + q * 64;
+    if (c < nvec) Vec<T>::load(dy + (int64_t)t * d + (int64_t)c * VN, dyv[q]);
+  }
+  float my_dg = 0.0f;  // lane j keeps dgate[t, j]
+  for (int j = 0; j < k; ++j) {
+    const float g = gate[(int64_t)t * k + j];
+    const int64_t p = pos[(int64_t)t * k + j];
+    float dot = 0.0f;
+#pragma unroll
+    for (int q = 0; q < MAXV; ++q) {
+      const int c = lane + q * 64;
+      if (c < nvec) {
+        float v[VN], o[VN];
+        Vec<T>::load(y_perm + p * d + (int64_t)c * VN, v);
+#pragma unroll
+        for (int u = 0; u < VN; ++u) {
+          dot = fmaf(dyv[q][u], v[u], dot);
+          o[u] = g * dyv[q][u];
+        }
+        Vec<T>::store(dy_perm + p * d + (int64_t)c * VN, o);
+      }
+    }
+    dot = wave_sum(dot);
+    if (lane == j) my_dg = dot;
+  }
+
+  // ---- router backward
+  const float* lrow = logits + (int64_t)t * E;
+  float* drow = dlogits + (int64_t)t * E;
+  const int my_e = (lane < k) ? idx[(int64_t)t * k + lane] : -1;
+  if (score == MOE_SIGMOID || renorm) {
+    // picked scores (sigmoid) or probabilities (softmax, renormalised)
+    double sv = 0.0;
+    if (score == MOE_SIGMOID) {
+      if (lane < k) sv = (double)sigmoid_rounded_f(lrow[my_e]);
+    } else {
+      float m = -INFINITY;
+      for (int e = lane; e < E; e += 64) m = fmaxf(m, lrow[e]);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+      double zs = 0.0;
+      for (int e = lane; e < E; e += 64) zs += exp((double)lrow[e] - (double)m);
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o, 64);
+      if (lane < k) sv = (double)(float)(exp((double)lrow[my_e] - (double)m) / zs);
+    }
+    double S = sv;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) S += __shfl_xor(S, o, 64);
+    const double gj = (lane < k) ? sv / S : 0.0;
+    double gdg = gj * (double)my_dg;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) gdg += __shfl_xor(gdg, o, 64);
+    double dl = 0.0;
+    if (lane < k) {
+      if (score == MOE_SIGMOID) {
+        const double ds = ((double)my_dg - gdg) / S;
+        dl = ds * sv * (1.0 - sv);
+      } else {
+        dl = gj * ((double)my_dg - gdg);
+      }
+    }
+    const float dlf = (float)dl;
+    for (int e = lane; e < E; e += 64) {
+      float v = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int ej = __shfl(my_e, j, 64);
+        const float dj = __shfl(dlf, j, 64);
+        if (ej == e) v = dj;
+      }
+      drow[e] = v;
+    }
+  } else {
+    // softmax without renormalisation: dl = p * (dp - <p, dp>), dp = dgate on picked
+    float m = -INFINITY;
+    for (int e = lane; e < E; e += 64) m = fmaxf(m, lrow[e]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    double zs = 0.0;
+    for (int e = lane; e < E; e += 64) zs += exp((double)lrow[e] - (double)m);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) zs += __shfl_xor(zs, o, 64);
+    double pdp = 0.0;
+    if (lane < k) pdp = (double)(float)(exp((double)lrow[my_e] - (double)m) / zs) * (double)my_dg;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) pdp += __shfl_xor(pdp, o, 64);
+    for (int e = lane; e < E; e += 64) {
+      const double p = (double)(float)(exp((double)lrow[e] - (double)m) / zs);
+      double dp = 0.0;
+      for (int j = 0; j < k; ++j) {
+        const int ej = __shfl(my_e, j, 64);
+        const float dj = __shfl(my_dg, j, 64);
+        if (ej == e) dp = (double)dj;
+      }
+      drow[e] = (float)(p * (dp - pdp));
+    }
+  }
+}
+
+// dx[t] = sum_j dx_perm[pos[t,j]] + dx_shared[t] + sum_e dlogits[t,e] W_r[e]
+// (fp32, slot order, then shared, then router; one rounding).  For sigmoid
+// and renormalised softmax routers dlogits is zero off the picked experts, so
+// only those k rows of W_r are read.
+template <typename T>
+__global__ __launch_bounds__(256) void unpermute_sum_kernel(
+    const T* __restrict__ dx_perm, const int32_t* __restrict__ pos, const T* dx_shared,
+    const float* __restrict__ dlogits, const int32_t* __restrict__ idx,
+    const float* __restrict__ w_router, int dense_router, int Tn, int d, int E, int k,
+    T* __restrict__ dx) {
+  constexpr int VN = Vec<T>::N;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= Tn) return;
+  const int nvec = d / VN;
+  const int nr = dense_router ? E : k;
+  for (int c = lane; c < nvec; c += 64) {
+    float acc[VN];
+#pragma unroll
+    for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      const int64_t p = pos[(int64_t)t * k + j];
+      float v[VN];
+      Vec<T>::load(dx_perm + p * d + (int64_t)c * VN, v);
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] += v[u];
+    }
+    if (dx_shared) {
+      float v[VN];
+      Vec<T>::load(dx_shared + (int64_t)t * d + (int64_t)c * VN, v);
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] += v[u];
+    }
+    for (int j = 0; j < nr; ++j) {
+      const int e = dense_router ? j : idx[(int64_t)t * k + j];
+      const float dl = dlogits[(int64_t)t * E + e];
+      const float* wr = w_router + (int64_t)e * d + (int64_t)c * VN;
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] = fmaf(dl, wr[u], acc[u]);
+    }
+    Vec<T>::store(dx + (int64_t)t * d + (int64_t)c * VN, acc);
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void group_offsets_1_kernel(int32_t* o, int32_t M) {
+  if (threadIdx.x == 0) {
+    o[0] = 0;
+    o[1] = M;
+  }
+}
+
+hipError_t launch_combine(int dtype, const void* y_perm, const float* gate, const int32_t* pos,
+                          const void* shared_y, void* y, int T, int d, int k, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv64(T, 4)), block(256);
+  if (dtype == MOE_BF16)
+    combine_kernel<bf16_t><<<grid, block, 0, st>>>((const bf16_t*)y_perm, gate, pos,
+                                                   (const bf16_t*)shared_y, (bf16_t*)y, T, d, k);
+  else
+    combine_kernel<float><<<grid, block, 0, st>>>((const float*)y_perm, gate, pos,
+                                                  (const float*)shared_y, (float*)y, T, d, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, const float* gate,
+                              const int32_t* pos, const int32_t* idx, const float* logits,
+                              int score, int renorm, int T, int d, int E, int k, void* dy_perm,
+                              float* dlogits, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv64(T, 4)), block(256);
+  const int nvec = d / (dtype == MOE_BF16 ? 8 : 4);
+  if (nvec > 8 * 64) return hipErrorInvalidValue;
+  if (dtype == MOE_BF16)
+    combine_bwd_kernel<bf16_t, 8><<<grid, block, 0, st>>>(
+        (const bf16_t*)dy, (const bf16_t*)y_perm, gate, pos, idx, logits, score, renorm, T, d, E,
+        k, (bf16_t*)dy_perm, dlogits);
+  else
+    combine_bwd_kernel<float, 8><<<grid, block, 0, st>>>(
+        (const float*)dy, (const float*)y_perm, gate, pos, idx, logits, score, renorm, T, d, E, k,
+        (float*)dy_perm, dlogits);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* pos,
+                                const void* dx_shared, const float* dlogits, const int32_t* idx,
+                                const float* w_router, int dense_router, int T, int d, int E,
+                                int k, void* dx, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv64(T, 4)), block(256);
+  if (dtype == MOE_BF16)
+    unpermute_sum_kernel<bf16_t><<<grid, block, 0, st>>>(
+        (const bf16_t*)dx_perm, pos, (const bf16_t*)dx_shared, dlogits, idx, w_router,
+        dense_router, T, d, E, k, (bf16_t*)dx);
+  else
+    unpermute_sum_kernel<float><<<grid, block, 0, st>>>(
+        (const float*)dx_perm, pos, (const float*)dx_shared, dlogits, idx, w_router, dense_router,
+        T, d, E, k, (float*)dx);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  fill_i32_kernel<<<dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_offsets_1(int32_t* offsets, int32_t M, hipStream_t st) {
+  group_offsets_1_kernel<<<dim3(1), dim3(64), 0, st>>>(offsets, M);
+  return hipGetLastError();
+}
+
+}  // namespace moe

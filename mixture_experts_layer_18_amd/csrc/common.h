@@ -1,0 +1,85 @@
+// Shared device helpers for the gfx950 MoE kernels (bf16 conversion, vector
+// types, wave reductions).  Nothing here is specific to one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef uint16_t bf16_t;                                     // bf16 bit pattern
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));  // MFMA operand
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+struct alignas(16) u32x4 { uint32_t x, y, z, w; };
+struct alignas(8) u32x2 { uint32_t x, y; };
+
+MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+MOE_DEV bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+MOE_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+MOE_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element access for the two storage types the library supports.
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  static MOE_DEV float load(const float* p, int64_t i) { return p[i]; }
+  static MOE_DEV void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Elem<bf16_t> {
+  static MOE_DEV float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static MOE_DEV void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+MOE_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
+MOE_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+
+// Sum over the 64 lanes of a wavefront, identical result in every lane.
+// The butterfly order is fixed, so the result is deterministic.
+MOE_DEV float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Number of blocks of `b` covering `a` (host and device).
+__host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Block-wide exclusive prefix sum over 256 threads (4 wavefronts).  Every
+// thread must call it.  Returns the exclusive prefix of `v`; *total receives
+// the sum of all 256 inputs.  `scratch` is 4 ints of LDS.
+MOE_DEV int block_exclusive_scan256(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    int s = scratch[w];
+    if (w < wave) wbase += s;
+    tot += s;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}

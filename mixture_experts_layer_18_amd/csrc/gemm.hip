@@ -1,0 +1,618 @@
+// Grouped GEMM kernels for the expert FFNs (gfx950).
+//
+// The experts run as grouped GEMMs (Apex-3 code page, "What's inside", row
+// "Fine-grained MoE"; Ultimate MoE Training Handbook, section 2.5, grouped
+// GEMM over the local experts).  Each expert is a SwiGLU block without bias
+// (Handbook 2.5, parameter accounting): the gate/up product is fused with the
+// SwiGLU activation, and the data-gradient of the down product is fused with
+// the SwiGLU derivative.
+//
+// Two kernel families share one tile scheduler:
+//  * bf16 operands: 128x128x64 tiles on v_mfma_f32_32x32x16_bf16, 4 waves of
+//    64x64, operands staged through LDS in a K-contiguous padded layout;
+//    operands whose reduction dimension is strided in memory are transposed
+//    in registers on their way into LDS;
+//  * fp32 operands (and the fp32 router GEMMs): 64x64x16 FMA tiles.
+//
+// Rows of a group form a ragged M dimension: M-tiles are enumerated group
+// after group from the device-side offsets, so nothing is copied to the host
+// and empty groups cost nothing (weight gradients of empty groups are zero).
+#include "kernels.h"
+
+namespace moe {
+
+struct KArgs {
+  int G;
+  int nsplit;
+  int64_t M_total, N, K;
+  const int32_t* offsets;
+  const void* A;
+  const void* B;
+  void* C;
+  void* aux;
+  float* part;  // split partial sums [nsplit][G][N][K] (TN only)
+};
+
+struct RowTile {
+  int g, m_lo, m_hi;
+  bool valid;
+};
+
+// Tile tm of the concatenation of every group's ceil(rows/BMt) row tiles.
+// Block-wide (all 256 threads call it); G <= 256.
+template <int BMt>
+MOE_DEV RowTile find_row_tile(const int32_t* __restrict__ offsets, int G, int tm, int* s_pref,
+                              int* scratch) {
+  const int tid = threadIdx.x;
+  int n = 0;
+  if (tid < G) n = (offsets[tid + 1] - offsets[tid] + BMt - 1) / BMt;
+  int tot;
+  const int ex = block_exclusive_scan256(n, scratch, &tot);
+  if (tid < G) s_pref[tid] = ex;
+  __syncthreads();
+  RowTile r;
+  r.valid = tm < tot;
+  r.g = 0;
+  r.m_lo = r.m_hi = 0;
+  if (!r.valid) return r;
+  int lo = 0, hi = G;  // last g with s_pref[g] <= tm (never an empty group)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_pref[mid] <= tm)
+      lo = mid;
+    else
+      hi = mid;
+  }
+  r.g = lo;
+  r.m_lo = offsets[lo] + (tm - s_pref[lo]) * BMt;
+  r.m_hi = min(r.m_lo + BMt, offsets[lo + 1]);
+  return r;
+}
+
+// Rows [lo, hi) of a group's reduction range assigned to split s of n.
+MOE_DEV void split_range(int lo, int hi, int s, int n, int quantum, int* a, int* b) {
+  const int len = hi - lo;
+  int chunk = (len + n - 1) / n;
+  chunk = (chunk + quantum - 1) / quantum * quantum;
+  *a = min(hi, lo + s * chunk);
+  *b = min(hi, *a + chunk);
+}
+
+// ============================================================================ fp32 / mixed FMA path
+namespace simt {
+constexpr int BM = 64, BN = 64, BR = 16;
+
+template <int LAYOUT, int EPI, typename TA, typename TB, typename TC>
+__global__ __launch_bounds__(256) void gemm_kernel(KArgs a) {
+  __shared__ float sP[BR][BM + 4];
+  __shared__ float sQ[BR][BN + 4];
+  __shared__ float sQ2[EPI == MOE_EPI_SWIGLU ? BR : 1][BN + 4];
+  __shared__ int s_pref[256];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x;
+  const TA* A = (const TA*)a.A;
+  const TB* B = (const TB*)a.B;
+  const int64_t N = a.N, K = a.K;
+
+  int g, split = 0;
+  int64_t i_lo, i_hi, j0 = (int64_t)blockIdx.x * BN, r_lo, r_hi, ncols;
+  if (LAYOUT == MOE_GEMM_TN) {
+    g = blockIdx.z / a.nsplit;
+    split = blockIdx.z % a.nsplit;
+    int rl, rh;
+    split_range(a.offsets[g], a.offsets[g + 1], split, a.nsplit, BR, &rl, &rh);
+    r_lo = rl;
+    r_hi = rh;
+    i_lo = (int64_t)blockIdx.y * BM;
+    i_hi = min(i_lo + BM, N);
+    ncols = K;
+  } else {
+    const RowTile rt = find_row_tile<BM>(a.offsets, a.G, blockIdx.y, s_pref, scratch);
+    if (!rt.valid) return;
+    g = rt.g;
+    i_lo = rt.m_lo;
+    i_hi = rt.m_hi;
+    r_lo = 0;
+    r_hi = (LAYOUT == MOE_GEMM_NT) ? K : N;
+    ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? N / 2 : N) : K;
+  }
+  if (j0 >= ncols) return;
+  const int64_t F = N / 2;
+
+  const int tx = tid % 16, ty = tid / 16;
+  float acc[4][4] = {};
+  float acc2[4][4] = {};
+
+  for (int64_t r0 = r_lo; r0 < r_hi; r0 += BR) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + q * 256;
+      int ii, rr;
+      if (LAYOUT == MOE_GEMM_TN) {
+        ii = e % BM;
+        rr = e / BM;
+      } else {
+        ii = e / BR;
+        rr = e % BR;
+      }
+      const int64_t i = i_lo + ii, r = r0 + rr;
+      float v = 0.0f;
+      if (i < i_hi && r < r_hi) {
+        if (LAYOUT == MOE_GEMM_NT) v = Elem<TA>::load(A, i * K + r);
+        else if (LAYOUT == MOE_GEMM_NN) v = Elem<TA>::load(A, i * N + r);
+        else v = Elem<TA>::load(A, r * N + i);
+      }
+      sP[rr][ii] = v;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = tid + q * 256;
+      int jj, rr;
+      if (LAYOUT == MOE_GEMM_NT) {
+        jj = e / BR;
+        rr = e % BR;
+      } else {
+        jj = e % BN;
+        rr = e / BN;
+      }
+      const int64_t j = j0 + jj, r = r0 + rr;
+      float v = 0.0f, v2 = 0.0f;
+      if (j < ncols && r < r_hi) {
+        if (LAYOUT == MOE_GEMM_NT) {
+          const int64_t base = (int64_t)g * N * K;
+          v = Elem<TB>::load(B, base + j * K + r);
+          if (EPI == MOE_EPI_SWIGLU) v2 = Elem<TB>::load(B, base + (F + j) * K + r);
+        } else if (LAYOUT == MOE_GEMM_NN) {
+          v = Elem<TB>::load(B, (int64_t)g * N * K + r * K + j);
+        } else {
+          v = Elem<TB>::load(B, r * K + j);
+        }
+      }
+      sQ[rr][jj] = v;
+      if (EPI == MOE_EPI_SWIGLU) sQ2[rr][jj] = v2;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int rr = 0; rr < BR; ++rr) {
+      float p[4], q[4], q2[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        p[u] = sP[rr][ty * 4 + u];
+        q[u] = sQ[rr][tx * 4 + u];
+        if (EPI == MOE_EPI_SWIGLU) q2[u] = sQ2[rr][tx * 4 + u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          acc[u][w] = fmaf(p[u], q[w], acc[u][w]);
+          if (EPI == MOE_EPI_SWIGLU) acc2[u][w] = fmaf(p[u], q2[w], acc2[u][w]);
+        }
+    }
+    __syncthreads();
+  }
+
+  TC* C = (TC*)a.C;
+  TC* X = (TC*)a.aux;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t i = i_lo + ty * 4 + u;
+    if (i >= i_hi) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const int64_t j = j0 + tx * 4 + w;
+      if (j >= ncols) continue;
+      const float v = acc[u][w];
+      if (LAYOUT == MOE_GEMM_TN) {
+        if (a.nsplit > 1)
+          a.part[(((int64_t)split * a.G + g) * N + i) * K + j] = v;
+        else
+          Elem<TC>::store(C, ((int64_t)g * N + i) * K + j, v);
+      } else if (EPI == MOE_EPI_SWIGLU) {
+        const float u2 = acc2[u][w];
+        Elem<TC>::store(C, i * F + j, silu_f(v) * u2);
+        if (X) {
+          Elem<TC>::store(X, i * N + j, v);
+          Elem<TC>::store(X, i * N + F + j, u2);
+        }
+      } else if (EPI == MOE_EPI_DSWIGLU) {
+        const float G = Elem<TC>::load(X, i * 2 * K + j);
+        const float U = Elem<TC>::load(X, i * 2 * K + K + j);
+        const float sg = sigmoid_f(G);
+        Elem<TC>::store(C, i * 2 * K + j, v * U * sg * (1.0f + G * (1.0f - sg)));
+        Elem<TC>::store(C, i * 2 * K + K + j, v * G * sg);
+      } else {
+        Elem<TC>::store(C, i * ncols + j, v);
+      }
+    }
+  }
+}
+}  // namespace simt
+
+// Sum of split partials in split order, rounded once to TC.
+template <typename TC>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ part,
+                                                           int nsplit, int64_t n,
+                                                           TC* __restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.0f;
+  for (int p = 0; p < nsplit; ++p) s += part[(int64_t)p * n + i];
+  Elem<TC>::store(C, i, s);
+}
+
+// ============================================================================ bf16 MFMA path
+namespace mf {
+constexpr int BM = 128, BN = 128, BK = 64, PITCH = BK + 8;
+
+// Direct operand: a [rows x BK] tile whose reduction dimension is contiguous.
+// Thread t moves row (pass*32 + t/8), 16-byte chunk t%8, for pass 0..3.
+struct DirectLoader {
+  const bf16_t* row[4];
+  u32x4 v[4];
+  MOE_DEV void load(int64_t k0) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) v[p] = *reinterpret_cast<const u32x4*>(row[p] + k0);
+  }
+  MOE_DEV void store(bf16_t* s) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+      *reinterpret_cast<u32x4*>(s + (p * 32 + t / 8) * PITCH + (t % 8) * 8) = v[p];
+  }
+};
+
+// Transposed operand: a [BK x 128] block of a matrix whose tile columns are
+// contiguous (reduction dimension strided by `ld`).  Thread t reads rows
+// r = (t%16)*4 + q (q < 4) at columns (t/16)*8 .. +7, then writes 8 columns
+// x 4 reduction values into the K-contiguous LDS layout.  Rows at or past
+// r_end read as zero.
+struct TransLoader {
+  const bf16_t* col;  // points at column chunk start, row 0 of the range
+  int64_t ld;
+  int64_t r_end;      // rows >= r_end are zero (relative to the same origin)
+  u32x4 v[4];
+  MOE_DEV void load(int64_t r0) {
+    const int rq = threadIdx.x % 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t r = r0 + rq * 4 + q;
+      if (r < r_end)
+        v[q] = *reinterpret_cast<const u32x4*>(col + r * ld);
+      else
+        v[q] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  MOE_DEV void store(bf16_t* s) const {
+    const int rq = threadIdx.x % 16, ic = threadIdx.x / 16;
+    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
+    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
+    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
+    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int wi = c >> 1;
+      u32x2 o;
+      if (c & 1) {
+        o.x = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
+        o.y = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
+      } else {
+        o.x = (w0[wi] & 0xffffu) | (w1[wi] << 16);
+        o.y = (w2[wi] & 0xffffu) | (w3[wi] << 16);
+      }
+      *reinterpret_cast<u32x2*>(s + (ic * 8 + c) * PITCH + rq * 4) = o;
+    }
+  }
+};
+
+MOE_DEV void store4_bf16(bf16_t* p, const float* v) {
+  u32x2 o;
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(p) = o;
+}
+MOE_DEV void load4_bf16(const bf16_t* p, float* v) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  v[0] = bf16_lo(w.x);
+  v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y);
+  v[3] = bf16_hi(w.y);
+}
+
+template <int LAYOUT, int EPI>
+__global__ __launch_bounds__(256) void gemm_kernel(KArgs a) {
+  __shared__ __attribute__((aligned(16))) bf16_t sP[BM * PITCH];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[BN * PITCH];
+  __shared__ int s_pref[256];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bf16_t* A = (const bf16_t*)a.A;
+  const bf16_t* B = (const bf16_t*)a.B;
+  const int64_t N = a.N, K = a.K;
+
+  int g;
+  int64_t i_lo, i_hi, j0, r_lo = 0, r_hi, ncols;
+  if (LAYOUT == MOE_GEMM_TN) {
+    g = blockIdx.z;
+    r_lo = a.offsets[g];
+    r_hi = a.offsets[g + 1];
+    i_lo = (int64_t)blockIdx.y * BM;
+    i_hi = min(i_lo + BM, N);
+    j0 = (int64_t)blockIdx.x * BN;
+    ncols = K;
+  } else {
+    const RowTile rt = find_row_tile<BM>(a.offsets, a.G, blockIdx.y, s_pref, scratch);
+    if (!rt.valid) return;
+    g = rt.g;
+    i_lo = rt.m_lo;
+    i_hi = rt.m_hi;
+    r_hi = (LAYOUT == MOE_GEMM_NT) ? K : N;
+    // SwiGLU tiles cover 64 gate columns and the matching 64 up columns
+    j0 = (int64_t)blockIdx.x * ((EPI == MOE_EPI_SWIGLU) ? BN / 2 : BN);
+    ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? N / 2 : N) : K;
+  }
+  const int64_t F = N / 2;
+
+  // ---- operand loaders
+  DirectLoader dP, dQ;
+  TransLoader tP, tQ;
+  if (LAYOUT != MOE_GEMM_TN) {
+    const int64_t ldA = (LAYOUT == MOE_GEMM_NT) ? K : N;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      int64_t i = i_lo + p * 32 + tid / 8;
+      i = i < i_hi ? i : i_hi - 1;
+      dP.row[p] = A + i * ldA + (tid % 8) * 8;
+    }
+  } else {
+    int64_t c = i_lo + (tid / 16) * 8;
+    c = c < N - 8 ? c : N - 8;
+    tP.col = A + c;
+    tP.ld = N;
+    tP.r_end = r_hi;
+  }
+  if (LAYOUT == MOE_GEMM_NT) {
+    const bf16_t* Bg = B + (int64_t)g * N * K;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int qr = p * 32 + tid / 8;
+      int64_t row;
+      if (EPI == MOE_EPI_SWIGLU) {
+        const int wq = qr >> 6, jt = (qr >> 5) & 1, jj = qr & 31;
+        row = jt * F + j0 + wq * 32 + jj;
+      } else {
+        row = j0 + qr;
+        row = row < N ? row : N - 1;
+      }
+      dQ.row[p] = Bg + row * K + (tid % 8) * 8;
+    }
+  } else if (LAYOUT == MOE_GEMM_NN) {
+    int64_t c = j0 + (tid / 16) * 8;
+    c = c < K - 8 ? c : K - 8;
+    tQ.col = B + (int64_t)g * N * K + c;
+    tQ.ld = K;
+    tQ.r_end = N;
+  } else {
+    int64_t c = j0 + (tid / 16) * 8;
+    c = c < K - 8 ? c : K - 8;
+    tQ.col = B + c;
+    tQ.ld = K;
+    tQ.r_end = r_hi;
+  }
+
+  auto gload = [&](int64_t r0) {
+    if (LAYOUT == MOE_GEMM_TN) tP.load(r0); else dP.load(r0);
+    if (LAYOUT == MOE_GEMM_NT) dQ.load(r0); else tQ.load(r0);
+  };
+  auto lstore = [&]() {
+    if (LAYOUT == MOE_GEMM_TN) tP.store(sP); else dP.store(sP);
+    if (LAYOUT == MOE_GEMM_NT) dQ.store(sQ); else tQ.store(sQ);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it)
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
+
+  const int wp = wave >> 1, wq = wave & 1;
+  const int r32 = lane & 31, kh = lane >> 5;
+  const int64_t nk = (r_hi - r_lo + BK - 1) / BK;
+  if (nk > 0) gload(r_lo);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    lstore();
+    __syncthreads();
+    if (kt + 1 < nk) gload(r_lo + (kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t pa[2], qb[2];
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+        pa[it] = *reinterpret_cast<const bf16x8_t*>(sP + (wp * 64 + it * 32 + r32) * PITCH +
+                                                    ks * 16 + kh * 8);
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+        qb[jt] = *reinterpret_cast<const bf16x8_t*>(sQ + (wq * 64 + jt * 32 + r32) * PITCH +
+                                                    ks * 16 + kh * 8);
+#pragma unroll
+      for (int it = 0; it < 2; ++it)
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[jt], pa[it], acc[it][jt], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: lane holds row (.. + r32) and 4 groups of 4 consecutive columns
+  bf16_t* C = (bf16_t*)a.C;
+  bf16_t* X = (bf16_t*)a.aux;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int64_t i = i_lo + wp * 64 + it * 32 + r32;
+    if (i >= i_hi) continue;
+    if (EPI == MOE_EPI_SWIGLU) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int64_t c = j0 + wq * 32 + gq * 8 + kh * 4;
+        float Gv[4], Uv[4], H[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          Gv[u] = acc[it][0][gq * 4 + u];
+          Uv[u] = acc[it][1][gq * 4 + u];
+          H[u] = silu_f(Gv[u]) * Uv[u];
+        }
+        store4_bf16(C + i * F + c, H);
+        if (X) {
+          store4_bf16(X + i * N + c, Gv);
+          store4_bf16(X + i * N + F + c, Uv);
+        }
+      }
+      continue;
+    }
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int64_t j = j0 + wq * 64 + jt * 32 + gq * 8 + kh * 4;
+        if (j >= ncols) continue;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = acc[it][jt][gq * 4 + u];
+        if (LAYOUT == MOE_GEMM_TN) {
+          store4_bf16(C + ((int64_t)g * N + i) * K + j, v);
+        } else if (EPI == MOE_EPI_DSWIGLU) {
+          float Gv[4], Uv[4], dG[4], dU[4];
+          load4_bf16(X + i * 2 * K + j, Gv);
+          load4_bf16(X + i * 2 * K + K + j, Uv);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float sg = sigmoid_f(Gv[u]);
+            dG[u] = v[u] * Uv[u] * sg * (1.0f + Gv[u] * (1.0f - sg));
+            dU[u] = v[u] * Gv[u] * sg;
+          }
+          store4_bf16(C + i * 2 * K + j, dG);
+          store4_bf16(C + i * 2 * K + K + j, dU);
+        } else {
+          store4_bf16(C + i * ncols + j, v);
+        }
+      }
+    }
+  }
+}
+}  // namespace mf
+
+// ============================================================================ dispatch
+static int simt_splits(const GemmProblem& p) {
+  // fp32 weight gradients reduce over all rows of a group: split long
+  // reductions so that enough workgroups run; partials are summed in a fixed
+  // order afterwards.
+  if (p.layout != MOE_GEMM_TN) return 1;
+  const int64_t tiles = p.G * cdiv64(p.N, simt::BM) * cdiv64(p.K, simt::BN);
+  const int64_t rows_per_group = cdiv64(p.M_total, p.G);
+  int s = 1;
+  while (tiles * s < 1024 && rows_per_group / (s * 2) >= 256 && s < 64) s *= 2;
+  return s;
+}
+
+static bool use_mfma(const GemmProblem& p) {
+  return p.ta == MOE_BF16 && p.tb == MOE_BF16 && p.tc == MOE_BF16;
+}
+
+size_t gemm_workspace_bytes(const GemmProblem& p) {
+  if (use_mfma(p)) return 0;
+  const int s = simt_splits(p);
+  if (s <= 1) return 0;
+  return (size_t)s * p.G * p.N * p.K * sizeof(float);
+}
+
+template <int LAYOUT, int EPI, typename TA, typename TB, typename TC>
+static hipError_t run_simt(const KArgs& ka, const GemmProblem& p, hipStream_t st) {
+  dim3 grid;
+  if (LAYOUT == MOE_GEMM_TN) {
+    grid = dim3((unsigned)cdiv64(p.K, simt::BN), (unsigned)cdiv64(p.N, simt::BM),
+                (unsigned)(p.G * ka.nsplit));
+  } else {
+    const int64_t ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? p.N / 2 : p.N) : p.K;
+    grid = dim3((unsigned)cdiv64(ncols, simt::BN),
+                (unsigned)(cdiv64(p.M_total, simt::BM) + p.G), 1);
+  }
+  simt::gemm_kernel<LAYOUT, EPI, TA, TB, TC><<<grid, dim3(256), 0, st>>>(ka);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (LAYOUT == MOE_GEMM_TN && ka.nsplit > 1) {
+    const int64_t n = p.G * p.N * p.K;
+    split_reduce_kernel<TC><<<dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st>>>(
+        ka.part, ka.nsplit, n, (TC*)p.C);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+template <int LAYOUT, int EPI>
+static hipError_t run_mfma(const KArgs& ka, const GemmProblem& p, hipStream_t st) {
+  dim3 grid;
+  if (LAYOUT == MOE_GEMM_TN) {
+    grid = dim3((unsigned)cdiv64(p.K, mf::BN), (unsigned)cdiv64(p.N, mf::BM), (unsigned)p.G);
+  } else {
+    const int64_t ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? p.N / 2 : p.N) : p.K;
+    const int64_t ntile = (EPI == MOE_EPI_SWIGLU) ? ncols / (mf::BN / 2) : cdiv64(ncols, mf::BN);
+    grid = dim3((unsigned)ntile, (unsigned)(cdiv64(p.M_total, mf::BM) + p.G), 1);
+  }
+  mf::gemm_kernel<LAYOUT, EPI><<<grid, dim3(256), 0, st>>>(ka);
+  return hipGetLastError();
+}
+
+template <typename TA, typename TB, typename TC>
+static hipError_t dispatch_simt(const KArgs& ka, const GemmProblem& p, hipStream_t st) {
+  if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE)
+    return run_simt<MOE_GEMM_NT, MOE_EPI_NONE, TA, TB, TC>(ka, p, st);
+  if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU)
+    return run_simt<MOE_GEMM_NT, MOE_EPI_SWIGLU, TA, TB, TC>(ka, p, st);
+  if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE)
+    return run_simt<MOE_GEMM_NN, MOE_EPI_NONE, TA, TB, TC>(ka, p, st);
+  if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_DSWIGLU)
+    return run_simt<MOE_GEMM_NN, MOE_EPI_DSWIGLU, TA, TB, TC>(ka, p, st);
+  if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE)
+    return run_simt<MOE_GEMM_TN, MOE_EPI_NONE, TA, TB, TC>(ka, p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st) {
+  if (p.M_total == 0 && p.layout != MOE_GEMM_TN) return hipSuccess;
+  KArgs ka;
+  ka.G = (int)p.G;
+  ka.M_total = p.M_total;
+  ka.N = p.N;
+  ka.K = p.K;
+  ka.offsets = p.offsets;
+  ka.A = p.A;
+  ka.B = p.B;
+  ka.C = p.C;
+  ka.aux = p.aux;
+  ka.part = (float*)ws;
+  ka.nsplit = 1;
+  if (use_mfma(p)) {
+    if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE)
+      return run_mfma<MOE_GEMM_NT, MOE_EPI_NONE>(ka, p, st);
+    if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU)
+      return run_mfma<MOE_GEMM_NT, MOE_EPI_SWIGLU>(ka, p, st);
+    if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE)
+      return run_mfma<MOE_GEMM_NN, MOE_EPI_NONE>(ka, p, st);
+    if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_DSWIGLU)
+      return run_mfma<MOE_GEMM_NN, MOE_EPI_DSWIGLU>(ka, p, st);
+    if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE)
+      return run_mfma<MOE_GEMM_TN, MOE_EPI_NONE>(ka, p, st);
+    return hipErrorInvalidValue;
+  }
+  ka.nsplit = simt_splits(p);
+  if (ka.nsplit > 1 && ws_bytes < gemm_workspace_bytes(p)) return hipErrorInvalidValue;
+  // fp32 layers and the fp32 router products (A and/or B may be bf16 there)
+  if (p.ta == MOE_F32 && p.tb == MOE_F32 && p.tc == MOE_F32) return dispatch_simt<float, float, float>(ka, p, st);
+  if (p.ta == MOE_BF16 && p.tb == MOE_F32 && p.tc == MOE_F32) return dispatch_simt<bf16_t, float, float>(ka, p, st);
+  if (p.ta == MOE_F32 && p.tb == MOE_BF16 && p.tc == MOE_F32) return dispatch_simt<float, bf16_t, float>(ka, p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

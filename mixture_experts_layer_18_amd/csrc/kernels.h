@@ -1,0 +1,45 @@
+// Private declarations shared by the kernel sources and the ABI layer.
+#pragma once
+
+#include "../../include/moe.h"
+#include "common.h"
+
+namespace moe {
+
+// ---- route / permute
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k, int score,
+                        int renorm, int32_t* idx, float* gate, int32_t* hist, hipStream_t st);
+hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const int32_t* hist, int T,
+                          int d, int E, int k, int32_t* base, int32_t* counts, int32_t* offsets,
+                          int32_t* pos, int32_t* src, void* x_perm, hipStream_t st);
+
+// ---- grouped GEMM
+// Element types of the operands: A, B and C each f32 or bf16 (MOE_F32 / MOE_BF16).
+struct GemmProblem {
+  int layout, epilogue;
+  int ta, tb, tc;        // element type of A, B, C (and aux = tc)
+  int64_t G, M_total, N, K;
+  const int32_t* offsets;  // device [G+1]
+  const void* A;
+  const void* B;
+  void* C;
+  void* aux;
+};
+size_t gemm_workspace_bytes(const GemmProblem& p);
+hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);
+
+// ---- combine and backward helpers
+hipError_t launch_combine(int dtype, const void* y_perm, const float* gate, const int32_t* pos,
+                          const void* shared_y, void* y, int T, int d, int k, hipStream_t st);
+hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, const float* gate,
+                              const int32_t* pos, const int32_t* idx, const float* logits,
+                              int score, int renorm, int T, int d, int E, int k, void* dy_perm,
+                              float* dlogits, hipStream_t st);
+hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* pos,
+                                const void* dx_shared, const float* dlogits, const int32_t* idx,
+                                const float* w_router, int dense_router, int T, int d, int E,
+                                int k, void* dx, hipStream_t st);
+hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
+hipError_t launch_group_offsets_1(int32_t* offsets, int32_t M, hipStream_t st);
+
+}  // namespace moe

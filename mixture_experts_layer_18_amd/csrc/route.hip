@@ -1,0 +1,279 @@
+// Router top-k and token permutation kernels (gfx950).
+//
+// Routing follows the pages' description of the layer: a sigmoid router with a
+// per-expert bias that only steers selection (Apex-3 code page, "What's
+// inside", row "Fine-grained MoE"), or a softmax top-k router (KempnerForge
+// README, "Features / Architecture"), on fp32 logits (Ultimate MoE Training
+// Handbook, section 2.5, fp32 router dtype).  Permutation sends each token's
+// row to its selected experts in expert-contiguous order (Handbook 2.5:
+// tokens are sent to the selected experts).
+#include "kernels.h"
+
+namespace moe {
+
+// Map an fp32 key to an unsigned integer with the same order.  -0 is folded
+// onto +0 and NaN onto the very bottom, so NaN keys are picked last.
+MOE_DEV uint32_t ordered_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN
+  if (u == 0x80000000u) u = 0u;                     // -0 -> +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Candidate code: key in the high word, (0xffffffff - expert) in the low word,
+// so the maximum is the best key and, among equal keys, the lowest expert.
+MOE_DEV uint64_t cand_code(float key, int e) {
+  return ((uint64_t)ordered_bits(key) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+template <int L>
+MOE_DEV uint64_t group_max_u64(uint64_t v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) {
+    uint64_t o = __shfl_xor(v, m, L);
+    v = o > v ? o : v;
+  }
+  return v;
+}
+template <int L>
+MOE_DEV double group_sum_f64(double v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, L);
+  return v;
+}
+template <int L>
+MOE_DEV float group_max_f32(float v) {
+#pragma unroll
+  for (int m = L / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, L));
+  return v;
+}
+
+// sigmoid evaluated in fp64 and rounded once to fp32
+MOE_DEV float sigmoid_rounded(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
+
+// One group of L lanes handles one token; lane i holds experts i, i+L, ...
+// (V = ceil(E / L) values).  A workgroup of 256 threads handles one block of
+// MOE_ROUTE_BLOCK tokens and writes that block's expert histogram.
+template <int L, int V>
+__global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ logits,
+                                                    const float* __restrict__ bias, int T, int E,
+                                                    int k, int score, int renorm,
+                                                    int32_t* __restrict__ idx,
+                                                    float* __restrict__ gate,
+                                                    int32_t* __restrict__ hist, int nblk) {
+  __shared__ int s_hist[256];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += 256) s_hist[e] = 0;
+  __syncthreads();
+  const int blk = blockIdx.x;
+  const int li = tid % L;
+  constexpr int GROUPS = 256 / L;
+  for (int tl = tid / L; tl < MOE_ROUTE_BLOCK; tl += GROUPS) {
+    const int t = blk * MOE_ROUTE_BLOCK + tl;
+    if (t >= T) break;  // uniform within the group
+    const float* lrow = logits + (int64_t)t * E;
+    float lv[V];
+    float sc[V];
+    uint64_t cand[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = li + v * L;
+      lv[v] = (e < E) ? lrow[e] : -INFINITY;
+    }
+    if (score == MOE_SIGMOID) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = li + v * L;
+        sc[v] = sigmoid_rounded(lv[v]);
+        const float key = bias ? (sc[v] + (e < E ? bias[e] : 0.0f)) : sc[v];
+        cand[v] = (e < E) ? cand_code(key, e) : 0ull;
+      }
+    } else {
+      float m = lv[0];
+#pragma unroll
+      for (int v = 1; v < V; ++v) m = fmaxf(m, lv[v]);
+      m = group_max_f32<L>(m);
+      double z[V], zs = 0.0;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = li + v * L;
+        z[v] = (e < E) ? exp((double)lv[v] - (double)m) : 0.0;
+        zs += z[v];
+      }
+      zs = group_sum_f64<L>(zs);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int e = li + v * L;
+        sc[v] = (float)(z[v] / zs);
+        cand[v] = (e < E) ? cand_code(lv[v], e) : 0ull;
+      }
+    }
+    // k rounds of group arg-max; slot j's expert and score land in lane j
+    int my_e = 0;
+    float my_s = 0.0f;
+    for (int j = 0; j < k; ++j) {
+      uint64_t b = cand[0];
+#pragma unroll
+      for (int v = 1; v < V; ++v) b = cand[v] > b ? cand[v] : b;
+      b = group_max_u64<L>(b);
+      const int e = (int)(0xffffffffu - (uint32_t)(b & 0xffffffffu));
+      const int owner = e % L, ov = e / L;
+      float s_own = 0.0f;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (v == ov) s_own = sc[v];
+      if (li == owner) {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+          if (v == ov) cand[v] = 0ull;
+      }
+      const float s_e = __shfl(s_own, owner, L);
+      if (li == j) {
+        my_e = e;
+        my_s = s_e;
+      }
+    }
+    double gsum = (li < k) ? (double)my_s : 0.0;
+    gsum = group_sum_f64<L>(gsum);
+    if (li < k) {
+      float g;
+      if (score == MOE_SOFTMAX && !renorm)
+        g = my_s;
+      else
+        g = (float)((double)my_s / gsum);
+      idx[(int64_t)t * k + li] = my_e;
+      gate[(int64_t)t * k + li] = g;
+      atomicAdd(&s_hist[my_e], 1);
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) hist[(int64_t)e * nblk + blk] = s_hist[e];
+}
+
+// Per expert: exclusive prefix of its per-block counts (-> base) and total.
+__global__ __launch_bounds__(256) void hist_scan_kernel(const int32_t* __restrict__ hist,
+                                                        int nblk, int32_t* __restrict__ base,
+                                                        int32_t* __restrict__ counts) {
+  __shared__ int scratch[4];
+  const int e = blockIdx.x;
+  const int32_t* h = hist + (int64_t)e * nblk;
+  int32_t* b = base + (int64_t)e * nblk;
+  int carry = 0;
+  for (int c0 = 0; c0 < nblk; c0 += 256) {
+    const int i = c0 + threadIdx.x;
+    const int v = (i < nblk) ? h[i] : 0;
+    int tot;
+    const int ex = block_exclusive_scan256(v, scratch, &tot);
+    if (i < nblk) b[i] = carry + ex;
+    carry += tot;
+  }
+  if (threadIdx.x == 0) counts[e] = carry;
+}
+
+// Stable scatter: within a block of MOE_ROUTE_BLOCK (= 32) tokens, the rank of
+// assignment (t, j) among the block's assignments to the same expert is the
+// number of earlier tokens of the block that picked that expert (each token
+// picks an expert at most once), read off a 32-bit token mask per expert.
+template <typename TX>
+__global__ __launch_bounds__(256) void permute_kernel(
+    const TX* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
+    const int32_t* __restrict__ base, int T, int d, int E, int k, int nblk,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
+    TX* __restrict__ x_perm) {
+  static_assert(MOE_ROUTE_BLOCK == 32, "one mask word per expert");
+  __shared__ int s_off[256];
+  __shared__ uint32_t s_mask[256];
+  __shared__ int s_pos[MOE_ROUTE_BLOCK * 16];
+  __shared__ int scratch[4];
+  const int tid = threadIdx.x;
+  const int blk = blockIdx.x;
+  const int t0 = blk * MOE_ROUTE_BLOCK;
+  const int nt = min(MOE_ROUTE_BLOCK, T - t0);
+  {
+    const int c = (tid < E) ? counts[tid] : 0;
+    int tot;
+    const int ex = block_exclusive_scan256(c, scratch, &tot);
+    s_off[tid] = ex;
+    s_mask[tid] = 0u;
+    if (blk == 0) {
+      if (tid < E) offsets[tid] = ex;
+      if (tid == 0) offsets[E] = tot;
+    }
+  }
+  __syncthreads();
+  const int na = nt * k;
+  const int32_t* bidx = idx + (int64_t)t0 * k;
+  // ids outside [0, E) (never written by moe_route) are skipped, not followed
+  for (int i = tid; i < na; i += 256) {
+    const int e = bidx[i];
+    if ((unsigned)e < (unsigned)E) atomicOr(&s_mask[e], 1u << (i / k));
+  }
+  __syncthreads();
+  for (int i = tid; i < na; i += 256) {
+    const int tl = i / k;
+    const int e = bidx[i];
+    if ((unsigned)e >= (unsigned)E) {
+      s_pos[i] = -1;
+      continue;
+    }
+    const int rank = __popc(s_mask[e] & ((1u << tl) - 1u));
+    const int p = s_off[e] + base[(int64_t)e * nblk + blk] + rank;
+    const int a = t0 * k + i;
+    pos[a] = p;
+    src[p] = a;
+    s_pos[i] = p;
+  }
+  __syncthreads();
+  // row copies: one wavefront per token, 16-byte vectors
+  const int lane = tid & 63, wave = tid >> 6;
+  const int nvec = d * (int)sizeof(TX) / 16;
+  for (int tl = wave; tl < nt; tl += 4) {
+    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (int64_t)(t0 + tl) * d);
+    for (int c = lane; c < nvec; c += 64) {
+      const u32x4 v = xr[c];
+      for (int j = 0; j < k; ++j) {
+        const int p = s_pos[tl * k + j];
+        if (p < 0) continue;
+        u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (int64_t)p * d);
+        dst[c] = v;
+      }
+    }
+  }
+}
+
+hipError_t launch_route(const float* logits, const float* bias, int T, int E, int k, int score,
+                        int renorm, int32_t* idx, float* gate, int32_t* hist, hipStream_t st) {
+  const int nblk = (int)cdiv64(T, MOE_ROUTE_BLOCK);
+  if (nblk == 0) return hipSuccess;
+  dim3 grid(nblk), block(256);
+  if (E <= 64)
+    route_kernel<16, 4><<<grid, block, 0, st>>>(logits, bias, T, E, k, score, renorm, idx, gate,
+                                                 hist, nblk);
+  else if (E <= 128)
+    route_kernel<32, 4><<<grid, block, 0, st>>>(logits, bias, T, E, k, score, renorm, idx, gate,
+                                                 hist, nblk);
+  else
+    route_kernel<64, 4><<<grid, block, 0, st>>>(logits, bias, T, E, k, score, renorm, idx, gate,
+                                                 hist, nblk);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const int32_t* hist, int T,
+                          int d, int E, int k, int32_t* base, int32_t* counts, int32_t* offsets,
+                          int32_t* pos, int32_t* src, void* x_perm, hipStream_t st) {
+  const int nblk = (int)cdiv64(T, MOE_ROUTE_BLOCK);
+  hist_scan_kernel<<<dim3(E), dim3(256), 0, st>>>(hist, nblk, base, counts);
+  if (nblk == 0) {
+    // no tokens: offsets are all zero (a fill kernel, not a memset node)
+    return launch_fill_i32(offsets, E + 1, 0, st);
+  }
+  if (dtype == MOE_BF16)
+    permute_kernel<bf16_t><<<dim3(nblk), dim3(256), 0, st>>>(
+        (const bf16_t*)x, idx, counts, base, T, d, E, k, nblk, offsets, pos, src, (bf16_t*)x_perm);
+  else
+    permute_kernel<float><<<dim3(nblk), dim3(256), 0, st>>>(
+        (const float*)x, idx, counts, base, T, d, E, k, nblk, offsets, pos, src, (float*)x_perm);
+  return hipGetLastError();
+}
+
+}  // namespace moe

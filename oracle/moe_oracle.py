@@ -237,15 +237,52 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
         ys = np.zeros((T, d), F64)
         out.update(s_preact=None, s_h=None, ys=None)
 
-    # weighted combine: slot order, shared output last
-    y = np.zeros((T, d), F64)
-    g64 = gate.astype(F64)
-    rows = pos.reshape(T, k)
-    for j in range(k):
-        y += g64[:, j:j + 1] * y_perm[rows[:, j]]
-    y += ys
-    out["y"] = y
+    out["y"] = combine(y_perm, gate, pos, ys)
     return out
+
+
+def combine(y_perm, gate, pos, shared_y=None):
+    """y[t] = sum_j gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t]): slot order,
+    shared output last (fp64)."""
+    T, k = gate.shape
+    y = np.zeros((T, y_perm.shape[1]), F64)
+    g64 = np.asarray(gate, F32).astype(F64)
+    rows = np.asarray(pos).reshape(T, k)
+    for j in range(k):
+        y += g64[:, j:j + 1] * np.asarray(y_perm, F64)[rows[:, j]]
+    if shared_y is not None:
+        y += shared_y
+    return y
+
+
+def combine_backward(dy, y_perm, gate, pos, src):
+    """Reverse of ``combine``: d(y_perm)[p] = gate * dy[token of p] and
+    dgate[t,j] = <dy[t], y_perm[pos[t*k+j]]>."""
+    dy = np.asarray(dy, F64)
+    T, k = gate.shape
+    tok_of_row = np.asarray(src) // k
+    slot_of_row = np.asarray(src) % k
+    g64 = np.asarray(gate, F32).astype(F64)
+    dy_perm = g64[tok_of_row, slot_of_row][:, None] * dy[tok_of_row]
+    rows = np.asarray(pos).reshape(T, k)
+    yp = np.asarray(y_perm, F64)
+    dgate = np.stack([(dy * yp[rows[:, j]]).sum(axis=1) for j in range(k)], axis=1)
+    return dy_perm, dgate
+
+
+def unpermute_sum(dx_perm, pos, k, dx_shared=None, dx_router=None):
+    """dx[t] = sum_j dx_perm[pos[t*k+j]] (+ dx_shared[t]) (+ dx_router[t])."""
+    rows = np.asarray(pos).reshape(-1, k)
+    T = rows.shape[0]
+    dxp = np.asarray(dx_perm, F64)
+    dx = np.zeros((T, dxp.shape[1]), F64)
+    for j in range(k):
+        dx += dxp[rows[:, j]]
+    if dx_shared is not None:
+        dx += dx_shared
+    if dx_router is not None:
+        dx += dx_router
+    return dx
 
 
 def router_backward(dgate, scores32, idx, score, renorm):
@@ -289,14 +326,7 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
     k = idx.shape[1]
     A = T * k
     f = w_gateup.shape[1] // 2
-    tok_of_row = src // k
-    slot_of_row = src % k
-
-    # combine backward: d(y_perm row p) = gate * dy[token]; dgate = <dy, y_perm row>
-    g64 = gate.astype(F64)
-    dy_perm = g64[tok_of_row, slot_of_row][:, None] * dy[tok_of_row]
-    rows = pos.reshape(T, k)
-    dgate = np.stack([(dy * fwd["y_perm"][rows[:, j]]).sum(axis=1) for j in range(k)], axis=1)
+    dy_perm, dgate = combine_backward(dy, fwd["y_perm"], gate, pos, src)
 
     wg_all, wu_all = _split_gateup(np.asarray(w_gateup))
     d_w_gateup = np.zeros((E, 2 * f, d), F64)
@@ -346,12 +376,7 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
     out["dx_router"] = dx_router
 
     # unpermute-sum: slot order, then shared, then router contribution
-    dx = np.zeros((T, d), F64)
-    for j in range(k):
-        dx += dx_perm[rows[:, j]]
-    dx += dxs
-    dx += dx_router
-    out["dx"] = dx
+    out["dx"] = unpermute_sum(dx_perm, pos, k, dxs, dx_router)
     return out
 
 

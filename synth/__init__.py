@@ -141,32 +141,58 @@ def skew_bias(cfg: LayerConfig, alpha: Optional[float] = None) -> np.ndarray:
     return b
 
 
-def make_inputs(cfg: LayerConfig, with_dy: Optional[bool] = None, skew_alpha: Optional[float] = None):
+ALL_PARTS = ("x", "router", "experts", "shared", "dy")
+
+
+def make_inputs(cfg: LayerConfig, with_dy: Optional[bool] = None, skew_alpha: Optional[float] = None,
+                parts=None):
     """Return a dict of host arrays for one layer.
 
     Keys: x [T,d]; w_router [E,d] f32; bias [E] f32 or None; w_gateup [E,2f,d]
     (gate rows first, then up rows); w_down [E,d,f]; s_gateup [2F_s,d] and
     s_down [d,F_s] (None without shared experts); dy [T,d] when requested.
-    bf16 tensors are uint16 bit patterns."""
+    bf16 tensors are uint16 bit patterns.  ``parts`` limits what is drawn
+    (any of "x", "router", "experts", "shared", "dy"); every tensor has its
+    own stream, so a subset is identical to the same keys of the full set."""
     if with_dy is None:
         with_dy = cfg.backward
+    parts = set(ALL_PARTS if parts is None else parts)
+    if not with_dy:
+        parts.discard("dy")
     T, d, E, f, Fs = cfg.T, cfg.d, cfg.E, cfg.f, cfg.F_shared
     out = {}
-    out["x"] = _normal(cfg, "x", (T, d), 1.0)
-    out["w_router"] = rng(cfg, "w_router").standard_normal((E, d), dtype=np.float32) * np.float32(0.02)
-    if cfg.bias is None:
-        out["bias"] = None
-    elif cfg.bias == "uniform":
-        out["bias"] = rng(cfg, "bias").uniform(-0.1, 0.1, size=E).astype(np.float32)
-    elif cfg.bias == "zipf":
-        out["bias"] = skew_bias(cfg, skew_alpha)
-    else:
-        raise ValueError(cfg.bias)
+    if "x" in parts:
+        out["x"] = _normal(cfg, "x", (T, d), 1.0)
+    if "router" in parts:
+        out["w_router"] = rng(cfg, "w_router").standard_normal((E, d), dtype=np.float32) * np.float32(0.02)
+        if cfg.bias is None:
+            out["bias"] = None
+        elif cfg.bias == "uniform":
+            out["bias"] = rng(cfg, "bias").uniform(-0.1, 0.1, size=E).astype(np.float32)
+        elif cfg.bias == "zipf":
+            out["bias"] = skew_bias(cfg, skew_alpha)
+        else:
+            raise ValueError(cfg.bias)
+    if "experts" in parts:
+        _experts(cfg, out)
+    if "shared" in parts:
+        _shared(cfg, out)
+    if "dy" in parts:
+        out["dy"] = _normal(cfg, "dy", (T, d), 1.0)
+    return out
+
+
+def _experts(cfg, out):
+    T, d, E, f = cfg.T, cfg.d, cfg.E, cfg.f
     wg = _normal(cfg, "w_gate", (E * f, d), 1.0 / np.sqrt(d)).reshape(E, f, d)
     wu = _normal(cfg, "w_up", (E * f, d), 1.0 / np.sqrt(d)).reshape(E, f, d)
     out["w_gateup"] = np.concatenate([wg, wu], axis=1)
     del wg, wu
     out["w_down"] = _normal(cfg, "w_down", (E * d, f), 1.0 / np.sqrt(f)).reshape(E, d, f)
+
+
+def _shared(cfg, out):
+    d, Fs = cfg.d, cfg.F_shared
     if Fs > 0:
         sg = _normal(cfg, "s_gate", (Fs, d), 1.0 / np.sqrt(d))
         su = _normal(cfg, "s_up", (Fs, d), 1.0 / np.sqrt(d))
@@ -175,9 +201,6 @@ def make_inputs(cfg: LayerConfig, with_dy: Optional[bool] = None, skew_alpha: Op
     else:
         out["s_gateup"] = None
         out["s_down"] = None
-    if with_dy:
-        out["dy"] = _normal(cfg, "dy", (T, d), 1.0)
-    return out
 
 
 def as_f64(a: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:

@@ -1,0 +1,58 @@
+"""Helpers for GPU parity tests: host <-> device transfer of synth arrays and
+the comparison metrics the tolerances are stated in."""
+import numpy as np
+import torch
+
+import synth
+
+
+def dev(a, dtype=None):
+    """Host array -> CUDA tensor.  uint16 arrays are bf16 bit patterns."""
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+    t = torch.from_numpy(a)
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    """CUDA tensor -> numpy (bf16 -> float64 exactly; others keep their dtype)."""
+    if t.dtype == torch.bfloat16:
+        bits = t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return synth.bf16_bits_to_f32(bits).astype(np.float64)
+    return t.cpu().numpy()
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def max_abs_over_rms(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    rms = np.sqrt(np.mean(b * b))
+    return float(np.max(np.abs(a - b)) / max(rms, 1e-300))
+
+
+# tolerances: fp32 layer rel-L2 <= 1e-5; bf16 layers rel-L2 <= 1e-2 and
+# max-abs <= 5e-2 * RMS(reference)
+def assert_close(gpu, ref, dtype, what=""):
+    r = rel_l2(gpu, ref)
+    if dtype == "f32":
+        assert r <= 1e-5, f"{what}: rel-L2 {r:.3e} > 1e-5"
+    else:
+        m = max_abs_over_rms(gpu, ref)
+        assert r <= 1e-2, f"{what}: rel-L2 {r:.3e} > 1e-2"
+        assert m <= 5e-2, f"{what}: max-abs/RMS {m:.3e} > 5e-2"
+    return r
+
+
+def ulp_f32(x):
+    x = np.abs(np.asarray(x, np.float32))
+    return np.spacing(x).astype(np.float64)

@@ -1,0 +1,74 @@
+"""Whole-layer GPU parity (moe_forward / moe_backward) against the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    from tests import layer_runner as R
+
+
+def test_forward_tiny_fp32():
+    cfg = synth.CONFIG_BY_NAME["tiny_fp32"]
+    print(f"[layer] {cfg.name} fwd", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=False)
+
+
+def test_backward_tiny_fp32():
+    cfg = synth.CONFIG_BY_NAME["tiny_fp32"].replace(backward=True)
+    print(f"[layer] {cfg.name} fwd+bwd", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=True)
+
+
+@pytest.mark.parametrize("score,renorm", [("softmax", True), ("sigmoid", True)])
+def test_backward_fp32_other_routers(score, renorm):
+    cfg = synth.CONFIG_BY_NAME["tiny_fp32"].replace(score=score, renorm=renorm, backward=True, n_shared=1,
+                                                   f_shared=128, T=200, bias="uniform" if score == "sigmoid"
+                                                   else None)
+    print(f"[layer] fp32 {score} renorm={renorm} shared", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=True)
+
+
+def test_forward_finegrained_bf16():
+    cfg = synth.CONFIG_BY_NAME["finegrained_bf16"]
+    print(f"[layer] {cfg.name} fwd", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=False)
+
+
+SMALL_BF16 = synth.CONFIG_BY_NAME["moe7b_bf16"].replace(name="small_bf16", T=1000, d=256, E=16, k=4, f=192,
+                                                         n_shared=2, f_shared=128)
+
+
+def test_backward_small_bf16():
+    print("[layer] small_bf16 fwd+bwd", flush=True)
+    R.compare_full(SMALL_BF16, synth.make_inputs(SMALL_BF16), backward=True)
+
+
+def test_backward_small_bf16_skewed():
+    cfg = SMALL_BF16.replace(name="small_skew", bias="zipf")
+    print("[layer] small skew fwd+bwd", flush=True)
+    inp = synth.make_inputs(cfg, skew_alpha=0.3)
+    g, fw, bw, same = R.compare_full(cfg, inp, backward=True)
+    assert (g["counts"] == 0).sum() >= 4          # the pinned-down experts stay empty
+    empty = np.where(g["counts"] == 0)[0]
+    assert np.all(g["d_w_gateup"][empty] == 0) and np.all(g["d_w_down"][empty] == 0)
+
+
+def test_forward_backward_deterministic():
+    cfg = SMALL_BF16
+    inp = synth.make_inputs(cfg)
+    a = R.run_gpu(cfg, inp, backward=True)
+    b = R.run_gpu(cfg, inp, backward=True)
+    for n in a:
+        assert np.array_equal(a[n], b[n], equal_nan=True), n
+
+
+def test_zero_tokens_is_a_noop():
+    cfg = SMALL_BF16.replace(T=0)
+    inp = synth.make_inputs(cfg)
+    g = R.run_gpu(cfg, inp, backward=True)
+    assert np.all(g["counts"] == 0) and np.all(g["offsets"] == 0)
+    assert np.all(g["d_w_gateup"] == 0) and np.all(g["d_w_router"] == 0)
