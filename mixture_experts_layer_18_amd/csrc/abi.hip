@@ -264,10 +264,10 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
   const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
   const int dt = d->dtype;
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
-  if (F > 0 && (!w->s_gateup || !w->s_down || !sv->s_h)) return MOE_ERR_INVALID;
+  if (F > 0 && (!w->s_gateup || !w->s_down)) return MOE_ERR_INVALID;
   if (!sv->counts || !sv->offsets) return MOE_ERR_INVALID;
   if (T > 0 && (!x || !y || !sv->logits || !sv->idx || !sv->gate || !sv->pos || !sv->src ||
-                !sv->x_perm || !sv->h || !sv->y_perm || !ws))
+                !sv->x_perm || !sv->h || !sv->y_perm || !ws || (F > 0 && !sv->s_h)))
     return MOE_ERR_INVALID;
   const void* ptrs[] = {x, y, w->w_router, w->bias, w->w_gateup, w->w_down, w->s_gateup,
                         w->s_down, sv->logits, sv->idx, sv->gate, sv->counts, sv->offsets,
@@ -330,9 +330,9 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   if (d->dtype == MOE_BF16 ? D > 4096 : D > 2048) return MOE_ERR_UNSUPPORTED;
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
   if (!g->d_w_router || !g->d_w_gateup || !g->d_w_down) return MOE_ERR_INVALID;
-  if (F > 0 && (!w->s_gateup || !w->s_down || !sv->s_h || !sv->s_preact || !g->d_s_gateup ||
-                !g->d_s_down))
+  if (F > 0 && (!w->s_gateup || !w->s_down || !g->d_s_gateup || !g->d_s_down))
     return MOE_ERR_INVALID;
+  if (F > 0 && T > 0 && (!sv->s_h || !sv->s_preact)) return MOE_ERR_INVALID;
   if (!sv->offsets) return MOE_ERR_INVALID;
   if (T > 0 && (!x || !dy || !dx || !sv->logits || !sv->idx || !sv->gate || !sv->pos ||
                 !sv->x_perm || !sv->preact || !sv->h || !sv->y_perm || !ws))

@@ -8,11 +8,8 @@
 // the SwiGLU derivative.
 //
 // Two kernel families share one tile scheduler:
-//  * bf16 operands: 128x128x64 tiles on v_mfma_f32_32x32x16_bf16, 4 waves of
-//    64x64, operands staged through LDS in a K-contiguous padded layout;
-//    operands whose reduction dimension is strided in memory are transposed
-//    in registers on their way into LDS;
-//  * fp32 operands (and the fp32 router GEMMs): 64x64x16 FMA tiles.
+//  * bf16 operands: matrix-core kernels (gemm_mfma.hip);
+//  * fp32 operands (and the fp32 router GEMMs): 64x64x16 FMA tiles (here).
 //
 // Rows of a group form a ragged M dimension: M-tiles are enumerated group
 // after group from the device-side offsets, so nothing is copied to the host
@@ -241,268 +238,6 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
   Elem<TC>::store(C, i, s);
 }
 
-// ============================================================================ bf16 MFMA path
-namespace mf {
-constexpr int BM = 128, BN = 128, BK = 64, PITCH = BK + 8;
-
-// Direct operand: a [rows x BK] tile whose reduction dimension is contiguous.
-// Thread t moves row (pass*32 + t/8), 16-byte chunk t%8, for pass 0..3.
-struct DirectLoader {
-  const bf16_t* row[4];
-  u32x4 v[4];
-  MOE_DEV void load(int64_t k0) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) v[p] = *reinterpret_cast<const u32x4*>(row[p] + k0);
-  }
-  MOE_DEV void store(bf16_t* s) const {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
-      *reinterpret_cast<u32x4*>(s + (p * 32 + t / 8) * PITCH + (t % 8) * 8) = v[p];
-  }
-};
-
-// Transposed operand: a [BK x 128] block of a matrix whose tile columns are
-// contiguous (reduction dimension strided by `ld`).  Thread t reads rows
-// r = (t%16)*4 + q (q < 4) at columns (t/16)*8 .. +7, then writes 8 columns
-// x 4 reduction values into the K-contiguous LDS layout.  Rows at or past
-// r_end read as zero.
-struct TransLoader {
-  const bf16_t* col;  // points at column chunk start, row 0 of the range
-  int64_t ld;
-  int64_t r_end;      // rows >= r_end are zero (relative to the same origin)
-  u32x4 v[4];
-  MOE_DEV void load(int64_t r0) {
-    const int rq = threadIdx.x % 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t r = r0 + rq * 4 + q;
-      if (r < r_end)
-        v[q] = *reinterpret_cast<const u32x4*>(col + r * ld);
-      else
-        v[q] = u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-  MOE_DEV void store(bf16_t* s) const {
-    const int rq = threadIdx.x % 16, ic = threadIdx.x / 16;
-    const uint32_t w0[4] = {v[0].x, v[0].y, v[0].z, v[0].w};
-    const uint32_t w1[4] = {v[1].x, v[1].y, v[1].z, v[1].w};
-    const uint32_t w2[4] = {v[2].x, v[2].y, v[2].z, v[2].w};
-    const uint32_t w3[4] = {v[3].x, v[3].y, v[3].z, v[3].w};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int wi = c >> 1;
-      u32x2 o;
-      if (c & 1) {
-        o.x = (w0[wi] >> 16) | (w1[wi] & 0xffff0000u);
-        o.y = (w2[wi] >> 16) | (w3[wi] & 0xffff0000u);
-      } else {
-        o.x = (w0[wi] & 0xffffu) | (w1[wi] << 16);
-        o.y = (w2[wi] & 0xffffu) | (w3[wi] << 16);
-      }
-      *reinterpret_cast<u32x2*>(s + (ic * 8 + c) * PITCH + rq * 4) = o;
-    }
-  }
-};
-
-MOE_DEV void store4_bf16(bf16_t* p, const float* v) {
-  u32x2 o;
-  o.x = pack_bf16x2(v[0], v[1]);
-  o.y = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<u32x2*>(p) = o;
-}
-MOE_DEV void load4_bf16(const bf16_t* p, float* v) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  v[0] = bf16_lo(w.x);
-  v[1] = bf16_hi(w.x);
-  v[2] = bf16_lo(w.y);
-  v[3] = bf16_hi(w.y);
-}
-
-template <int LAYOUT, int EPI>
-__global__ __launch_bounds__(256) void gemm_kernel(KArgs a) {
-  __shared__ __attribute__((aligned(16))) bf16_t sP[BM * PITCH];
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[BN * PITCH];
-  __shared__ int s_pref[256];
-  __shared__ int scratch[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bf16_t* A = (const bf16_t*)a.A;
-  const bf16_t* B = (const bf16_t*)a.B;
-  const int64_t N = a.N, K = a.K;
-
-  int g;
-  int64_t i_lo, i_hi, j0, r_lo = 0, r_hi, ncols;
-  if (LAYOUT == MOE_GEMM_TN) {
-    g = blockIdx.z;
-    r_lo = a.offsets[g];
-    r_hi = a.offsets[g + 1];
-    i_lo = (int64_t)blockIdx.y * BM;
-    i_hi = min(i_lo + BM, N);
-    j0 = (int64_t)blockIdx.x * BN;
-    ncols = K;
-  } else {
-    const RowTile rt = find_row_tile<BM>(a.offsets, a.G, blockIdx.y, s_pref, scratch);
-    if (!rt.valid) return;
-    g = rt.g;
-    i_lo = rt.m_lo;
-    i_hi = rt.m_hi;
-    r_hi = (LAYOUT == MOE_GEMM_NT) ? K : N;
-    // SwiGLU tiles cover 64 gate columns and the matching 64 up columns
-    j0 = (int64_t)blockIdx.x * ((EPI == MOE_EPI_SWIGLU) ? BN / 2 : BN);
-    ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? N / 2 : N) : K;
-  }
-  const int64_t F = N / 2;
-
-  // ---- operand loaders
-  DirectLoader dP, dQ;
-  TransLoader tP, tQ;
-  if (LAYOUT != MOE_GEMM_TN) {
-    const int64_t ldA = (LAYOUT == MOE_GEMM_NT) ? K : N;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      int64_t i = i_lo + p * 32 + tid / 8;
-      i = i < i_hi ? i : i_hi - 1;
-      dP.row[p] = A + i * ldA + (tid % 8) * 8;
-    }
-  } else {
-    int64_t c = i_lo + (tid / 16) * 8;
-    c = c < N - 8 ? c : N - 8;
-    tP.col = A + c;
-    tP.ld = N;
-    tP.r_end = r_hi;
-  }
-  if (LAYOUT == MOE_GEMM_NT) {
-    const bf16_t* Bg = B + (int64_t)g * N * K;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int qr = p * 32 + tid / 8;
-      int64_t row;
-      if (EPI == MOE_EPI_SWIGLU) {
-        const int wq = qr >> 6, jt = (qr >> 5) & 1, jj = qr & 31;
-        row = jt * F + j0 + wq * 32 + jj;
-      } else {
-        row = j0 + qr;
-        row = row < N ? row : N - 1;
-      }
-      dQ.row[p] = Bg + row * K + (tid % 8) * 8;
-    }
-  } else if (LAYOUT == MOE_GEMM_NN) {
-    int64_t c = j0 + (tid / 16) * 8;
-    c = c < K - 8 ? c : K - 8;
-    tQ.col = B + (int64_t)g * N * K + c;
-    tQ.ld = K;
-    tQ.r_end = N;
-  } else {
-    int64_t c = j0 + (tid / 16) * 8;
-    c = c < K - 8 ? c : K - 8;
-    tQ.col = B + c;
-    tQ.ld = K;
-    tQ.r_end = r_hi;
-  }
-
-  auto gload = [&](int64_t r0) {
-    if (LAYOUT == MOE_GEMM_TN) tP.load(r0); else dP.load(r0);
-    if (LAYOUT == MOE_GEMM_NT) dQ.load(r0); else tQ.load(r0);
-  };
-  auto lstore = [&]() {
-    if (LAYOUT == MOE_GEMM_TN) tP.store(sP); else dP.store(sP);
-    if (LAYOUT == MOE_GEMM_NT) dQ.store(sQ); else tQ.store(sQ);
-  };
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int it = 0; it < 2; ++it)
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
-
-  const int wp = wave >> 1, wq = wave & 1;
-  const int r32 = lane & 31, kh = lane >> 5;
-  const int64_t nk = (r_hi - r_lo + BK - 1) / BK;
-  if (nk > 0) gload(r_lo);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    lstore();
-    __syncthreads();
-    if (kt + 1 < nk) gload(r_lo + (kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8_t pa[2], qb[2];
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-        pa[it] = *reinterpret_cast<const bf16x8_t*>(sP + (wp * 64 + it * 32 + r32) * PITCH +
-                                                    ks * 16 + kh * 8);
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-        qb[jt] = *reinterpret_cast<const bf16x8_t*>(sQ + (wq * 64 + jt * 32 + r32) * PITCH +
-                                                    ks * 16 + kh * 8);
-#pragma unroll
-      for (int it = 0; it < 2; ++it)
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[jt], pa[it], acc[it][jt], 0, 0, 0);
-    }
-    __syncthreads();
-  }
-
-  // ---- epilogue: lane holds row (.. + r32) and 4 groups of 4 consecutive columns
-  bf16_t* C = (bf16_t*)a.C;
-  bf16_t* X = (bf16_t*)a.aux;
-#pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int64_t i = i_lo + wp * 64 + it * 32 + r32;
-    if (i >= i_hi) continue;
-    if (EPI == MOE_EPI_SWIGLU) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int64_t c = j0 + wq * 32 + gq * 8 + kh * 4;
-        float Gv[4], Uv[4], H[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          Gv[u] = acc[it][0][gq * 4 + u];
-          Uv[u] = acc[it][1][gq * 4 + u];
-          H[u] = silu_f(Gv[u]) * Uv[u];
-        }
-        store4_bf16(C + i * F + c, H);
-        if (X) {
-          store4_bf16(X + i * N + c, Gv);
-          store4_bf16(X + i * N + F + c, Uv);
-        }
-      }
-      continue;
-    }
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt) {
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int64_t j = j0 + wq * 64 + jt * 32 + gq * 8 + kh * 4;
-        if (j >= ncols) continue;
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[it][jt][gq * 4 + u];
-        if (LAYOUT == MOE_GEMM_TN) {
-          store4_bf16(C + ((int64_t)g * N + i) * K + j, v);
-        } else if (EPI == MOE_EPI_DSWIGLU) {
-          float Gv[4], Uv[4], dG[4], dU[4];
-          load4_bf16(X + i * 2 * K + j, Gv);
-          load4_bf16(X + i * 2 * K + K + j, Uv);
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float sg = sigmoid_f(Gv[u]);
-            dG[u] = v[u] * Uv[u] * sg * (1.0f + Gv[u] * (1.0f - sg));
-            dU[u] = v[u] * Gv[u] * sg;
-          }
-          store4_bf16(C + i * 2 * K + j, dG);
-          store4_bf16(C + i * 2 * K + K + j, dU);
-        } else {
-          store4_bf16(C + i * ncols + j, v);
-        }
-      }
-    }
-  }
-}
-}  // namespace mf
-
 // ============================================================================ dispatch
 static int simt_splits(const GemmProblem& p) {
   // fp32 weight gradients reduce over all rows of a group: split long
@@ -550,20 +285,6 @@ static hipError_t run_simt(const KArgs& ka, const GemmProblem& p, hipStream_t st
   return e;
 }
 
-template <int LAYOUT, int EPI>
-static hipError_t run_mfma(const KArgs& ka, const GemmProblem& p, hipStream_t st) {
-  dim3 grid;
-  if (LAYOUT == MOE_GEMM_TN) {
-    grid = dim3((unsigned)cdiv64(p.K, mf::BN), (unsigned)cdiv64(p.N, mf::BM), (unsigned)p.G);
-  } else {
-    const int64_t ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? p.N / 2 : p.N) : p.K;
-    const int64_t ntile = (EPI == MOE_EPI_SWIGLU) ? ncols / (mf::BN / 2) : cdiv64(ncols, mf::BN);
-    grid = dim3((unsigned)ntile, (unsigned)(cdiv64(p.M_total, mf::BM) + p.G), 1);
-  }
-  mf::gemm_kernel<LAYOUT, EPI><<<grid, dim3(256), 0, st>>>(ka);
-  return hipGetLastError();
-}
-
 template <typename TA, typename TB, typename TC>
 static hipError_t dispatch_simt(const KArgs& ka, const GemmProblem& p, hipStream_t st) {
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE)
@@ -593,19 +314,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, 
   ka.aux = p.aux;
   ka.part = (float*)ws;
   ka.nsplit = 1;
-  if (use_mfma(p)) {
-    if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE)
-      return run_mfma<MOE_GEMM_NT, MOE_EPI_NONE>(ka, p, st);
-    if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU)
-      return run_mfma<MOE_GEMM_NT, MOE_EPI_SWIGLU>(ka, p, st);
-    if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE)
-      return run_mfma<MOE_GEMM_NN, MOE_EPI_NONE>(ka, p, st);
-    if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_DSWIGLU)
-      return run_mfma<MOE_GEMM_NN, MOE_EPI_DSWIGLU>(ka, p, st);
-    if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE)
-      return run_mfma<MOE_GEMM_TN, MOE_EPI_NONE>(ka, p, st);
-    return hipErrorInvalidValue;
-  }
+  if (use_mfma(p)) return launch_gemm_mfma(p, st);
   ka.nsplit = simt_splits(p);
   if (ka.nsplit > 1 && ws_bytes < gemm_workspace_bytes(p)) return hipErrorInvalidValue;
   // fp32 layers and the fp32 router products (A and/or B may be bf16 there)

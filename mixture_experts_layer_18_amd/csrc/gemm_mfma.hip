@@ -1,0 +1,426 @@
+// bf16 grouped GEMM on gfx950 matrix cores (v_mfma_f32_32x32x16_bf16).
+//
+// Experts run as grouped GEMMs (Apex-3 code page, "What's inside", row
+// "Fine-grained MoE"; Ultimate MoE Training Handbook, section 2.5).  One
+// kernel template covers the three products of a SwiGLU expert:
+//   NT  C[m,n]   = sum_k A[m,k] B[g,n,k]        forward (+ SwiGLU epilogue)
+//   NN  C[m,k]   = sum_n A[m,n] B[g,n,k]        data gradient (+ dSwiGLU)
+//   TN  C[g,n,k] = sum_{m in g} A[m,n] B[m,k]   weight gradient
+//
+// Design (CDNA4-first):
+//  * operands move HBM -> LDS with global_load_lds_dwordx4 (no staging
+//    registers), STAGES k-steps of 64 in flight, one barrier per k-step;
+//  * an operand whose reduction dimension is contiguous is stored as rows of
+//    128 bytes with its 16-byte chunks XOR-swizzled by (row % 8), so that the
+//    ds_read_b128 fragment reads of 8 consecutive rows hit distinct banks;
+//  * an operand whose reduction dimension is strided (NN's B, both TN
+//    operands) is stored in its natural [k][column] layout, chunks swizzled
+//    by 2*(k % 4), and fed to the matrix cores through pairs of
+//    ds_read_b64_tr_b16 transpose reads (each turns a 4 x 16 block held by
+//    16 lanes into per-lane columns);
+//  * each of the 4 wavefronts owns a (TM/2) x (TN/2) block of 32x32 MFMA
+//    tiles with fp32 accumulators in AGPRs;
+//  * ragged groups: row tiles are enumerated group after group from the
+//    device-side offsets (no host copy); surplus workgroups of the
+//    upper-bound grid exit at once;
+//  * tile order is XCD-aware: the hardware deals workgroups to the 8 XCDs
+//    round-robin, so linear tile ids are remapped to give every XCD a
+//    contiguous range, keeping the tiles of one expert inside one L2.
+#include "kernels.h"
+
+namespace moe {
+namespace mf {
+
+constexpr int BK = 64;  // reduction depth per k-step (128 bytes of bf16)
+
+struct Args {
+  int G;
+  int64_t M_total, N, K;
+  const int32_t* offsets;
+  const bf16_t* A;
+  const bf16_t* B;
+  bf16_t* C;
+  bf16_t* aux;
+};
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) char lds_char;
+
+// One 16-byte-per-lane DMA from global memory into LDS at m0 + 16*lane.
+MOE_DEV void dma16(const void* g, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
+               : "memory", "m0");
+}
+
+// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left unconstrained)
+template <int n>
+MOE_DEV void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+MOE_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_char*)p; }
+
+// Consecutive workgroup ids go to XCD 0,1,..,7,0,..; return the logical tile
+// so that XCD x owns a contiguous block of the nb tiles.
+MOE_DEV int xcd_remap(int bid, int nb) {
+  const int q = nb >> 3, r = nb & 7;
+  const int x = bid & 7, local = bid >> 3;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+MOE_DEV void store4_bf16(bf16_t* p, const float* v) {
+  u32x2 o;
+  o.x = pack_bf16x2(v[0], v[1]);
+  o.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<u32x2*>(p) = o;
+}
+MOE_DEV void load4_bf16(const bf16_t* p, float* v) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  v[0] = bf16_lo(w.x);
+  v[1] = bf16_hi(w.x);
+  v[2] = bf16_lo(w.y);
+  v[3] = bf16_hi(w.y);
+}
+
+// ---- fragment reads (lane l: tile row l%32, reduction values (l/32)*8 .. +7)
+// reduction-contiguous tile: rows of 128 bytes, chunk c stored at c ^ (row%8)
+MOE_DEV bf16x8_t frag_kc(const char* region, int row, int ks, int lane) {
+  const int r = row + (lane & 31);
+  const int c = ks * 2 + (lane >> 5);
+  return *reinterpret_cast<const bf16x8_t*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+}
+// reduction-strided tile [64][R] (row bytes RB), chunk c of k-row stored at
+// c ^ 2*(k%4); two transpose reads give k = base+0..3 and base+4..7
+template <int RB>
+MOE_DEV bf16x8_t frag_tr(const char* region, int row, int ks, int lane) {
+  const int L = lane & 15, grp = lane >> 4;
+  const int n = row + (grp & 1) * 16 + (L & 3) * 4;
+  const int k1 = ks * 16 + (grp >> 1) * 8 + (L >> 2);
+  const int k2 = k1 + 4;
+  const int o1 = k1 * RB + ((((n >> 3) ^ ((k1 & 3) << 1))) << 4) + (n & 7) * 2;
+  const int o2 = k2 * RB + ((((n >> 3) ^ ((k2 & 3) << 1))) << 4) + (n & 7) * 2;
+  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(region + o1));
+  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(region + o2));
+  typedef short s16x8_t __attribute__((ext_vector_type(8)));
+  const s16x8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+template <int LAYOUT, int EPI, int TM, int TN, int STAGES>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
+  constexpr int WM = TM / 2, WN = TN / 2;  // wave tile
+  constexpr int FI = WM / 32, FJ = WN / 32;
+  constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);  // P reduction-contiguous
+  constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
+  constexpr int PB = TM * BK * 2, QB = TN * BK * 2, SB = PB + QB;
+  constexpr int LP = PB / 4096, LQ = QB / 4096;  // DMA instructions per wave per k-step
+  constexpr int LT = LP + LQ;
+  constexpr int PRB = TM * 2, QRB = TN * 2;       // row bytes of strided layouts
+
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
+  __shared__ int s_pref[256];
+  __shared__ int scratch[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t N = a.N, K = a.K;
+
+  // ---------------------------------------------------------------- tile
+  int g;
+  int64_t i_lo, i_hi, j0, r_lo = 0, r_hi, ncols;
+  if (LAYOUT == MOE_GEMM_TN) {
+    const int ti_n = (int)cdiv64(N, TM), tj_n = (int)cdiv64(K, TN);
+    const int per_g = ti_n * tj_n;
+    const int L = xcd_remap(blockIdx.x, a.G * per_g);
+    g = L / per_g;
+    const int rem = L - g * per_g;
+    const int ti = rem / tj_n, tj = rem - ti * tj_n;
+    r_lo = a.offsets[g];
+    r_hi = a.offsets[g + 1];
+    i_lo = (int64_t)ti * TM;
+    i_hi = i_lo + TM < N ? i_lo + TM : N;
+    j0 = (int64_t)tj * TN;
+    ncols = K;
+  } else {
+    int n = 0;
+    if (tid < a.G) n = (a.offsets[tid + 1] - a.offsets[tid] + TM - 1) / TM;
+    int mt_total;
+    const int ex = block_exclusive_scan256(n, scratch, &mt_total);
+    if (tid < a.G) s_pref[tid] = ex;
+    __syncthreads();
+    ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? N / 2 : N) : K;
+    const int colw = (EPI == MOE_EPI_SWIGLU) ? TN / 2 : TN;
+    const int tn_n = (int)cdiv64(ncols, colw);
+    const int total = mt_total * tn_n;
+    if ((int)blockIdx.x >= total) return;
+    const int L = xcd_remap(blockIdx.x, total);
+    const int tm = L / tn_n, tn = L - tm * tn_n;
+    int lo = 0, hi = a.G;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_pref[mid] <= tm) lo = mid; else hi = mid;
+    }
+    g = lo;
+    i_lo = a.offsets[g] + (int64_t)(tm - s_pref[g]) * TM;
+    const int64_t gend = a.offsets[g + 1];
+    i_hi = i_lo + TM < gend ? i_lo + TM : gend;
+    j0 = (int64_t)tn * colw;
+    r_hi = (LAYOUT == MOE_GEMM_NT) ? K : N;
+  }
+  const int64_t F = N / 2;
+  const int64_t nk = (r_hi - r_lo + BK - 1) / BK;
+
+  // ---------------------------------------------------------------- DMA plan
+  // Instruction i of wave w fills LDS bytes [(i*4+w)*1024, +1024) of a region.
+  // Reduction-contiguous region: 8 rows of 128 B; lane l -> row (i*4+w)*8 + l/8,
+  // LDS slot l%8 <- source chunk (l%8) ^ (l/8).
+  // Strided region [64][R]: k-row (i*4+w)*(1024/RB) + l/(RB/16), slot l%(RB/16)
+  // <- source chunk slot ^ 2*(krow%4).
+  const char* psrc[LP];   // per instruction: this lane's source at reduction offset 0
+  const char* qsrc[LQ];
+  int pkr[P_KC ? 1 : LP];  // strided: k-row of each instruction (for zero fill)
+  int qkr[Q_KC ? 1 : LQ];
+  {
+    const char* Ab = (const char*)a.A;
+    const char* Bb = (const char*)a.B;
+#pragma unroll
+    for (int i = 0; i < LP; ++i) {
+      const int blk = i * 4 + wave;
+      if (P_KC) {
+        const int row = blk * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        int64_t m = i_lo + row;
+        m = m < i_hi ? m : i_hi - 1;
+        const int64_t ld = (LAYOUT == MOE_GEMM_NT) ? K : N;
+        psrc[i] = Ab + (m * ld + chunk * 8) * 2;
+      } else {
+        constexpr int CPR = PRB / 16;
+        const int kr = blk * (1024 / PRB) + lane / CPR;
+        const int chunk = (lane % CPR) ^ ((kr & 3) << 1);
+        int64_t col = i_lo + chunk * 8;
+        col = col < N - 8 ? col : N - 8;
+        pkr[i] = kr;
+        psrc[i] = Ab + ((r_lo + kr) * N + col) * 2;  // row clamped at issue time
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int blk = i * 4 + wave;
+      if (Q_KC) {
+        const int qr = blk * 8 + (lane >> 3);
+        const int chunk = (lane & 7) ^ (lane >> 3);
+        int64_t row;
+        if (EPI == MOE_EPI_SWIGLU) {
+          const int wq = qr / WN, jt = (qr % WN) / 32, jj = qr % 32;
+          const int up = jt >= FJ / 2 ? 1 : 0;
+          row = up * F + j0 + wq * (WN / 2) + (jt % (FJ / 2)) * 32 + jj;
+        } else {
+          row = j0 + qr;
+          row = row < N ? row : N - 1;
+        }
+        qsrc[i] = Bb + (((int64_t)g * N + row) * K + chunk * 8) * 2;
+      } else {
+        constexpr int CPR = QRB / 16;
+        const int kr = blk * (1024 / QRB) + lane / CPR;
+        const int chunk = (lane % CPR) ^ ((kr & 3) << 1);
+        int64_t col = j0 + chunk * 8;
+        col = col < K - 8 ? col : K - 8;
+        qkr[i] = kr;
+        const int64_t base_row = (LAYOUT == MOE_GEMM_NN) ? (int64_t)g * N : r_lo;
+        qsrc[i] = Bb + ((base_row + kr) * K + col) * 2;
+      }
+    }
+  }
+  const uint32_t smem_base = lds_addr(smem);
+  const int64_t p_rstride = P_KC ? 2 : N * 2;  // bytes per reduction step of 1
+  const int64_t q_rstride = Q_KC ? 2 : K * 2;
+  // strided operands: rows past the group end are clamped to its last row at
+  // issue time and zeroed in LDS before use
+  const int64_t rows_left0 = r_hi - r_lo;
+
+  auto issue = [&](int64_t kt) __attribute__((always_inline)) {
+    const int st = (int)(kt % STAGES);
+    const int64_t r0 = kt * BK;
+#pragma unroll
+    for (int i = 0; i < LP; ++i) {
+      int64_t off = r0 * p_rstride;
+      if (!P_KC) {
+        const int64_t kr = r0 + pkr[i];
+        if (kr >= rows_left0) off = (rows_left0 - 1 - pkr[i]) * p_rstride;
+      }
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_base + st * SB + (i * 4 + wave) * 1024);
+      dma16(psrc[i] + off, dst);
+    }
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      int64_t off = r0 * q_rstride;
+      if (!Q_KC && LAYOUT == MOE_GEMM_TN) {
+        const int64_t kr = r0 + qkr[i];
+        if (kr >= rows_left0) off = (rows_left0 - 1 - qkr[i]) * q_rstride;
+      }
+      const uint32_t dst =
+          __builtin_amdgcn_readfirstlane(smem_base + st * SB + PB + (i * 4 + wave) * 1024);
+      dma16(qsrc[i] + off, dst);
+    }
+  };
+
+  // ---------------------------------------------------------------- main loop
+  f32x16_t acc[FI][FJ];
+#pragma unroll
+  for (int it = 0; it < FI; ++it)
+#pragma unroll
+    for (int jt = 0; jt < FJ; ++jt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
+
+  const int wp = wave >> 1, wq = wave & 1;
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    // the k-steps issued after this one may stay in flight
+    const int64_t later = (nk - 1 - kt) < (STAGES - 2) ? (nk - 1 - kt) : (STAGES - 2);
+    if (later >= 2) wait_vmcnt<2 * LT>();
+    else if (later == 1) wait_vmcnt<LT>();
+    else wait_vmcnt<0>();
+    char* stage = smem + (kt % STAGES) * SB;
+    if (LAYOUT == MOE_GEMM_TN && (kt + 1) * BK > rows_left0) {
+      // zero the reduction rows past the group end that this lane loaded
+      const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+      for (int i = 0; i < LP; ++i)
+        if (kt * BK + pkr[i] >= rows_left0)
+          *reinterpret_cast<uint4*>(stage + (i * 4 + wave) * 1024 + lane * 16) = z;
+#pragma unroll
+      for (int i = 0; i < LQ; ++i)
+        if (kt * BK + qkr[i] >= rows_left0)
+          *reinterpret_cast<uint4*>(stage + PB + (i * 4 + wave) * 1024 + lane * 16) = z;
+    }
+    __syncthreads();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+    const char* sP = stage;
+    const char* sQ = stage + PB;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8_t pa[FI], qb[FJ];
+#pragma unroll
+      for (int it = 0; it < FI; ++it)
+        pa[it] = P_KC ? frag_kc(sP, wp * WM + it * 32, ks, lane)
+                      : frag_tr<PRB>(sP, wp * WM + it * 32, ks, lane);
+#pragma unroll
+      for (int jt = 0; jt < FJ; ++jt)
+        qb[jt] = Q_KC ? frag_kc(sQ, wq * WN + jt * 32, ks, lane)
+                      : frag_tr<QRB>(sQ, wq * WN + jt * 32, ks, lane);
+#pragma unroll
+      for (int it = 0; it < FI; ++it)
+#pragma unroll
+        for (int jt = 0; jt < FJ; ++jt)
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb[jt], pa[it], acc[it][jt], 0, 0, 0);
+    }
+  }
+
+  // ---------------------------------------------------------------- epilogue
+  // lane holds output row (.. + lane%32) and, per 32-wide tile, 4 groups of 4
+  // consecutive columns: (v/4)*8 + (lane/32)*4 + v%4
+  const int r32 = lane & 31, kh = lane >> 5;
+  bf16_t* C = a.C;
+  bf16_t* X = a.aux;
+#pragma unroll
+  for (int it = 0; it < FI; ++it) {
+    const int64_t i = i_lo + wp * WM + it * 32 + r32;
+    if (i >= i_hi) continue;
+    if (EPI == MOE_EPI_SWIGLU) {
+#pragma unroll
+      for (int jt = 0; jt < FJ / 2; ++jt)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int64_t c = j0 + wq * (WN / 2) + jt * 32 + gq * 8 + kh * 4;
+          float Gv[4], Uv[4], H[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            Gv[u] = acc[it][jt][gq * 4 + u];
+            Uv[u] = acc[it][jt + FJ / 2][gq * 4 + u];
+            H[u] = silu_f(Gv[u]) * Uv[u];
+          }
+          store4_bf16(C + i * F + c, H);
+          if (X) {
+            store4_bf16(X + i * N + c, Gv);
+            store4_bf16(X + i * N + F + c, Uv);
+          }
+        }
+      continue;
+    }
+#pragma unroll
+    for (int jt = 0; jt < FJ; ++jt)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int64_t j = j0 + wq * WN + jt * 32 + gq * 8 + kh * 4;
+        if (j >= ncols) continue;
+        float v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = acc[it][jt][gq * 4 + u];
+        if (LAYOUT == MOE_GEMM_TN) {
+          store4_bf16(C + ((int64_t)g * N + i) * K + j, v);
+        } else if (EPI == MOE_EPI_DSWIGLU) {
+          float Gv[4], Uv[4], dG[4], dU[4];
+          load4_bf16(X + i * 2 * K + j, Gv);
+          load4_bf16(X + i * 2 * K + K + j, Uv);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float sg = sigmoid_f(Gv[u]);
+            dG[u] = v[u] * Uv[u] * sg * (1.0f + Gv[u] * (1.0f - sg));
+            dU[u] = v[u] * Gv[u] * sg;
+          }
+          store4_bf16(C + i * 2 * K + j, dG);
+          store4_bf16(C + i * 2 * K + K + j, dU);
+        } else {
+          store4_bf16(C + i * ncols + j, v);
+        }
+      }
+  }
+}
+
+template <int LAYOUT, int EPI, int TM, int TN, int STAGES>
+static hipError_t run(const Args& a, hipStream_t st) {
+  int64_t nb;
+  if (LAYOUT == MOE_GEMM_TN) {
+    nb = a.G * cdiv64(a.N, TM) * cdiv64(a.K, TN);
+  } else {
+    const int64_t ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? a.N / 2 : a.N) : a.K;
+    const int64_t colw = (EPI == MOE_EPI_SWIGLU) ? TN / 2 : TN;
+    nb = (cdiv64(a.M_total, TM) + a.G) * cdiv64(ncols, colw);
+  }
+  if (nb == 0) return hipSuccess;
+  gemm_kernel<LAYOUT, EPI, TM, TN, STAGES><<<dim3((unsigned)nb), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+// 256 x 128 tiles, 3 k-steps in flight (144 KB of LDS): each wave holds
+// 4 x 2 MFMA tiles (128 fp32 accumulators per lane).
+template <int LAYOUT, int EPI>
+static hipError_t pick(const Args& a, hipStream_t st) {
+  return run<LAYOUT, EPI, 256, 128, 3>(a, st);
+}
+
+}  // namespace mf
+
+hipError_t launch_gemm_mfma(const GemmProblem& p, hipStream_t st) {
+  mf::Args a;
+  a.G = (int)p.G;
+  a.M_total = p.M_total;
+  a.N = p.N;
+  a.K = p.K;
+  a.offsets = p.offsets;
+  a.A = (const bf16_t*)p.A;
+  a.B = (const bf16_t*)p.B;
+  a.C = (bf16_t*)p.C;
+  a.aux = (bf16_t*)p.aux;
+  if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE) return mf::pick<MOE_GEMM_NT, MOE_EPI_NONE>(a, st);
+  if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU) return mf::pick<MOE_GEMM_NT, MOE_EPI_SWIGLU>(a, st);
+  if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE) return mf::pick<MOE_GEMM_NN, MOE_EPI_NONE>(a, st);
+  if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_DSWIGLU) return mf::pick<MOE_GEMM_NN, MOE_EPI_DSWIGLU>(a, st);
+  if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE) return mf::pick<MOE_GEMM_TN, MOE_EPI_NONE>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

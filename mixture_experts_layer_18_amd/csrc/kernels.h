@@ -27,6 +27,7 @@ struct GemmProblem {
 };
 size_t gemm_workspace_bytes(const GemmProblem& p);
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);
+hipError_t launch_gemm_mfma(const GemmProblem& p, hipStream_t st);  // bf16 operands only
 
 // ---- combine and backward helpers
 hipError_t launch_combine(int dtype, const void* y_perm, const float* gate, const int32_t* pos,

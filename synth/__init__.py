@@ -5,8 +5,10 @@ layer's arithmetic (no routing, no GEMM, no activation).  The HIP path and the
 oracle both consume exactly the arrays produced here.
 
 Recipe (stands in for the workloads the pages describe; no dataset is used):
-  * every tensor comes from ``np.random.default_rng([seed, tensor_id])``,
-    seed 0, with the tensor ids listed in ``TENSOR_ID``;
+  * every normal tensor is filled in row-major chunks of 2^20 elements,
+    chunk c from ``np.random.default_rng([seed, tensor_id, c])``, seed 0,
+    with the tensor ids listed in ``TENSOR_ID`` (the bias and the skew
+    permutation use ``default_rng([seed, tensor_id])``);
   * x ~ N(0, 1) (the normalised hidden state entering the MoE block);
   * expert / shared weights ~ N(0, 1/fan_in) (variance 1/fan_in);
   * router weight ~ N(0, 0.02^2) (standard deviation 0.02), fp32 always;
@@ -98,22 +100,53 @@ def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     return (np.ascontiguousarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
 
 
-def _normal(cfg, tensor, shape, std, chunk_rows=4096):
-    """Draw N(0, std^2) in fp32 and store in the layer's dtype.
+CHUNK = 1 << 20   # elements per independently seeded chunk
 
-    Returned as fp32 (f32 layers) or as raw bf16 bits in uint16 (bf16 layers).
-    Drawn in row chunks so that very large tensors never hold a float64 copy."""
-    g = rng(cfg, tensor)
+
+def _fill_chunk(args):
+    seed, tid, c, std, flat, bf16 = args
+    g = np.random.default_rng([seed, tid, c])
+    v = g.standard_normal(flat.size, dtype=np.float32)
+    if std != 1.0:
+        v *= np.float32(std)
+    if bf16:
+        u = v.view(np.uint32)
+        r = (u >> np.uint32(16)) & np.uint32(1)
+        r += np.uint32(0x7FFF)
+        r += u
+        r >>= np.uint32(16)
+        flat[...] = r
+    else:
+        flat[...] = v
+
+
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        n = min(16, len(os.sched_getaffinity(0)))
+        _POOL = ThreadPoolExecutor(max(1, n))
+    return _POOL
+
+
+def _normal(cfg, tensor, shape, std):
+    """N(0, std^2) values, stored in the layer's dtype.
+
+    The tensor is filled in row-major order, in chunks of CHUNK elements;
+    chunk c is drawn as standard normal fp32 from
+    default_rng([seed, tensor_id, c]), multiplied by std in fp32 and, for bf16
+    layers, rounded to bf16 (nearest even).  Returned as fp32, or as raw bf16
+    bits in uint16."""
     shape = tuple(int(s) for s in shape)
-    rows = shape[0]
-    inner = int(np.prod(shape[1:])) if len(shape) > 1 else 1
-    out = np.empty((rows, inner), dtype=np.float32 if cfg.dtype == "f32" else np.uint16)
-    for r0 in range(0, rows, chunk_rows):
-        r1 = min(rows, r0 + chunk_rows)
-        v = g.standard_normal((r1 - r0, inner), dtype=np.float32)
-        if std != 1.0:
-            v *= np.float32(std)
-        out[r0:r1] = v if cfg.dtype == "f32" else f32_to_bf16_bits(v)
+    n = int(np.prod(shape))
+    bf16 = cfg.dtype != "f32"
+    out = np.empty(n, dtype=np.uint16 if bf16 else np.float32)
+    jobs = [(cfg.seed, TENSOR_ID[tensor], c, float(std), out[c * CHUNK:(c + 1) * CHUNK], bf16)
+            for c in range((n + CHUNK - 1) // CHUNK)]
+    list(_pool().map(_fill_chunk, jobs))
     return out.reshape(shape)
 
 
@@ -164,7 +197,7 @@ def make_inputs(cfg: LayerConfig, with_dy: Optional[bool] = None, skew_alpha: Op
     if "x" in parts:
         out["x"] = _normal(cfg, "x", (T, d), 1.0)
     if "router" in parts:
-        out["w_router"] = rng(cfg, "w_router").standard_normal((E, d), dtype=np.float32) * np.float32(0.02)
+        out["w_router"] = _normal(cfg.replace(dtype="f32"), "w_router", (E, d), 0.02)
         if cfg.bias is None:
             out["bias"] = None
         elif cfg.bias == "uniform":

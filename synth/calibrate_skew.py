@@ -32,7 +32,7 @@ def main():
     for cfg in synth.CONFIGS:
         if cfg.bias != "zipf":
             continue
-        inp = synth.make_inputs(cfg.replace(), with_dy=False, skew_alpha=0.0)
+        inp = synth.make_inputs(cfg, with_dy=False, skew_alpha=0.0, parts=("x", "router"))
         x = synth.as_f64(inp["x"], cfg.dtype)
         logits = O.router_logits(x, inp["w_router"])
         scores = O.router_scores(logits, cfg.score)

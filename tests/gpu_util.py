@@ -53,6 +53,24 @@ def assert_close(gpu, ref, dtype, what=""):
     return r
 
 
+def assert_rounded(gpu, ref, dtype, what=""):
+    """Outputs stored once in `dtype` after fp32 accumulation: each element
+    may differ from the exact value by one rounding (half an ulp: 2^-8
+    relative for bf16, 2^-24 for fp32) plus fp32 accumulation noise."""
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    r = rel_l2(gpu, ref)
+    if dtype == "f32":
+        assert r <= 1e-5, f"{what}: rel-L2 {r:.3e} > 1e-5"
+        return r
+    assert r <= 1e-2, f"{what}: rel-L2 {r:.3e} > 1e-2"
+    bound = 2.0 ** -8 * np.abs(ref) * (1 + 1e-3) + 1e-4 * rms
+    bad = np.abs(gpu - ref) > bound
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 rounding"
+    return r
+
+
 def ulp_f32(x):
     x = np.abs(np.asarray(x, np.float32))
     return np.spacing(x).astype(np.float64)

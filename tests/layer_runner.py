@@ -59,9 +59,12 @@ def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False
 
 
 def oracle_inputs(cfg, inp):
+    """Exact values of the stored inputs.  Expert weights stay fp32 (exact for
+    bf16 values); the oracle widens each expert to fp64 when it uses it."""
     f = lambda a: synth.as_f64(a, cfg.dtype)  # noqa: E731
-    return dict(x=f(inp["x"]), w_router=inp["w_router"], bias=inp["bias"], w_gateup=f(inp["w_gateup"]),
-                w_down=f(inp["w_down"]), s_gateup=f(inp.get("s_gateup")), s_down=f(inp.get("s_down")),
+    w32 = lambda a: synth.bf16_bits_to_f32(a) if a.dtype == np.uint16 else a  # noqa: E731
+    return dict(x=f(inp["x"]), w_router=inp["w_router"], bias=inp["bias"], w_gateup=w32(inp["w_gateup"]),
+                w_down=w32(inp["w_down"]), s_gateup=f(inp.get("s_gateup")), s_down=f(inp.get("s_down")),
                 dy=f(inp.get("dy")) if inp.get("dy") is not None else None)
 
 
@@ -78,24 +81,42 @@ def oracle_run(cfg, oi, backward, tokens=None):
 
 
 def check_routing(cfg, g_logits, g_idx, fw, tokens=None):
-    """Returns the mask of tokens whose GPU routing equals the oracle's."""
+    """Check the GPU routing against the oracle's; returns the mask of tokens
+    whose GPU expert set equals the oracle's (their outputs are comparable).
+
+    Tokens whose boundary margin (k-th minus (k+1)-th key) is >= 1e-3 must
+    pick the same expert set; if in addition every gap between consecutive
+    keys inside the top k is >= 1e-3, the slots must match in order too.
+    Every other token must make a valid choice: k distinct experts, each
+    with key >= the oracle's k-th key - 1e-3, listed in non-increasing key
+    order up to 1e-3."""
     ol = fw["logits"]
     gl = g_logits if tokens is None else g_logits[tokens]
     gi = g_idx if tokens is None else g_idx[tokens]
     r = rel_l2(gl, ol)
     assert r <= 1e-5, f"logits rel-L2 {r:.3e}"
-    clear = fw["margin"] >= MARGIN
-    same = np.all(gi == fw["idx"], axis=1)
-    bad = clear & ~same
-    assert not bad.any(), f"{bad.sum()} tokens with margin >= {MARGIN} routed differently"
-    # near-tie tokens: the GPU's picks must be valid
     keys = fw["keys"].astype(np.float64)
-    kth = np.sort(keys, axis=1)[:, -cfg.k]
+    srt = -np.sort(-keys, axis=1)
+    k = cfg.k
+    inner_gap = (srt[:, :k - 1] - srt[:, 1:k]).min(axis=1) if k > 1 else np.full(len(srt), np.inf)
+    clear_set = fw["margin"] >= MARGIN
+    clear_order = clear_set & (inner_gap >= MARGIN)
+    same_set = np.all(np.sort(gi, axis=1) == np.sort(fw["idx"], axis=1), axis=1)
+    same_order = np.all(gi == fw["idx"], axis=1)
+    for name, bad in (("expert set", clear_set & ~same_set), ("slot order", clear_order & ~same_order)):
+        if bad.any():
+            for t in np.where(bad)[0][:5]:
+                d = np.abs(gl[t].astype(np.float64) - ol[t])
+                print(f"token {t}: margin {fw['margin'][t]:.3e} inner gap {inner_gap[t]:.3e} oracle "
+                      f"{fw['idx'][t].tolist()} gpu {gi[t].tolist()} max|dlogit| {d.max():.3e}", flush=True)
+        assert not bad.any(), f"{bad.sum()} clear tokens differ in {name}"
+    # near-tie tokens: the GPU's picks must be a valid top-k
+    kth = srt[:, k - 1]
     picked = np.take_along_axis(keys, gi.astype(np.int64), axis=1)
     assert np.all(picked >= kth[:, None] - MARGIN)
-    for row in gi:
-        assert len(set(row.tolist())) == cfg.k
-    return same
+    assert np.all(picked[:, :-1] >= picked[:, 1:] - MARGIN)
+    assert np.all(np.diff(np.sort(gi, axis=1), axis=1) > 0), "repeated expert"
+    return same_set
 
 
 def compare_full(cfg, inp, backward):

@@ -11,7 +11,7 @@ import torch
 
 import synth
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_close, dev, host, rel_l2, ulp_f32
+from tests.gpu_util import assert_rounded, dev, host, ulp_f32
 
 pytestmark = pytest.mark.gpu
 
@@ -155,6 +155,8 @@ GEMM_CASES = [
 @pytest.mark.parametrize("layout,epi", [("NT", "none"), ("NT", "swiglu"), ("NN", "none"),
                                         ("NN", "dswiglu"), ("TN", "none")])
 def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
+    if epi == "swiglu" and N % 128:
+        N += 64      # SwiGLU tiles pair 64 gate columns with 64 up columns
     print(f"[gemm] {layout}/{epi} {dtype} G={G} N={N} K={K}", flush=True)
     g = np.random.default_rng(zlib.crc32(f"{layout}{epi}{dtype}{G}".encode()))
     off = _groups(G * 7 + N, G, mean, empty=(1,), big=G - 1)
@@ -180,9 +182,9 @@ def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
                 refaux[a0:a1, F:] = U
             else:
                 ref[a0:a1] = f64(A[a0:a1]) @ f64(B[e]).T
-        assert_close(host(C), ref, dtype, "C")
+        assert_rounded(host(C), ref, dtype, "C")
         if epi == "swiglu":
-            assert_close(host(aux), refaux, dtype, "aux")
+            assert_rounded(host(aux), refaux, dtype, "aux")
     elif layout == "NN":
         A = _rand(g, (Mt, N), dtype)
         B = _rand(g, (G, N, K), dtype, 1 / np.sqrt(N))
@@ -202,7 +204,7 @@ def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
                 ref[a0:a1, K:] = dU
             else:
                 ref[a0:a1] = f64(A[a0:a1]) @ f64(B[e])
-        assert_close(host(C), ref, dtype, "C")
+        assert_rounded(host(C), ref, dtype, "C")
     else:
         A = _rand(g, (Mt, N), dtype)
         B = _rand(g, (Mt, K), dtype)
@@ -218,7 +220,7 @@ def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
             ref[e] = f64(A[a0:a1]).T @ f64(B[a0:a1])
         out = host(C)
         assert np.all(out[1] == 0.0), "empty group must give zero"
-        assert_close(out, ref, dtype, "C")
+        assert_rounded(out, ref, dtype, "C")
 
 
 def _dswiglu_ref(dY, Wd_e, Gm, U):
@@ -248,4 +250,4 @@ def test_combine_against_oracle(dtype):
         M.moe_combine(desc, dev(y_perm), dev(gate), dev(pos), dev(sh), y)
         torch.cuda.synchronize()
         ref = O.combine(synth.as_f64(y_perm, dtype), gate, pos, None if sh is None else synth.as_f64(sh, dtype))
-        assert_close(host(y), ref, dtype, "y")
+        assert_rounded(host(y), ref, dtype, "y")
