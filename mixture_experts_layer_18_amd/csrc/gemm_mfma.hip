@@ -9,13 +9,16 @@
 //
 // Design (CDNA4-first):
 //  * operands move HBM -> LDS with global_load_lds_dwordx4 (no staging
-//    registers), STAGES k-steps of 64 in flight, one barrier per k-step;
+//    registers), STAGES k-steps of BK in flight, one barrier per k-step;
+//  * two workgroups share a CU (72 KB of LDS and 256 registers per lane
+//    each), so one workgroup's barriers, DMA issue and epilogue stores
+//    overlap the other's matrix-core work;
 //  * an operand whose reduction dimension is contiguous is stored as rows of
-//    128 bytes with its 16-byte chunks XOR-swizzled by (row % 8), so that the
-//    ds_read_b128 fragment reads of 8 consecutive rows hit distinct banks;
+//    2*BK bytes whose 16-byte chunks are XOR-swizzled so that the 16 rows a
+//    ds_read_b128 services together land in distinct banks (64 banks);
 //  * an operand whose reduction dimension is strided (NN's B, both TN
 //    operands) is stored in its natural [k][column] layout, chunks swizzled
-//    by 2*(k % 4), and fed to the matrix cores through pairs of
+//    by 4*(k % 4), and fed to the matrix cores through pairs of
 //    ds_read_b64_tr_b16 transpose reads (each turns a 4 x 16 block held by
 //    16 lanes into per-lane columns);
 //  * each of the 4 wavefronts owns a (TM/2) x (TN/2) block of 32x32 MFMA
@@ -31,7 +34,6 @@
 namespace moe {
 namespace mf {
 
-constexpr int BK = 64;  // reduction depth per k-step (128 bytes of bf16)
 
 struct Args {
   int G;
@@ -84,22 +86,30 @@ MOE_DEV void load4_bf16(const bf16_t* p, float* v) {
 }
 
 // ---- fragment reads (lane l: tile row l%32, reduction values (l/32)*8 .. +7)
-// reduction-contiguous tile: rows of 128 bytes, chunk c stored at c ^ (row%8)
+// Swizzle of a reduction-contiguous tile with rows of 2*BK bytes: the 16-byte
+// chunk c of row r sits at slot c ^ kc_swz(r).  16 consecutive rows read at
+// the same chunk then cover all 16 bank groups of 256 bytes.
+template <int BK>
+MOE_DEV int kc_swz(int r) {
+  return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
+}
+template <int BK>
 MOE_DEV bf16x8_t frag_kc(const char* region, int row, int ks, int lane) {
   const int r = row + (lane & 31);
   const int c = ks * 2 + (lane >> 5);
-  return *reinterpret_cast<const bf16x8_t*>(region + r * 128 + ((c ^ (r & 7)) << 4));
+  return *reinterpret_cast<const bf16x8_t*>(region + r * (2 * BK) + ((c ^ kc_swz<BK>(r)) << 4));
 }
-// reduction-strided tile [64][R] (row bytes RB), chunk c of k-row stored at
-// c ^ 2*(k%4); two transpose reads give k = base+0..3 and base+4..7
+// Reduction-strided tile [BK][R] (row bytes RB): chunk c of k-row k sits at
+// slot c ^ 4*(k%4); two transpose reads give k = base+0..3 and base+4..7.
+MOE_DEV int tr_swz(int k) { return (k & 3) << 2; }
 template <int RB>
 MOE_DEV bf16x8_t frag_tr(const char* region, int row, int ks, int lane) {
   const int L = lane & 15, grp = lane >> 4;
   const int n = row + (grp & 1) * 16 + (L & 3) * 4;
   const int k1 = ks * 16 + (grp >> 1) * 8 + (L >> 2);
   const int k2 = k1 + 4;
-  const int o1 = k1 * RB + ((((n >> 3) ^ ((k1 & 3) << 1))) << 4) + (n & 7) * 2;
-  const int o2 = k2 * RB + ((((n >> 3) ^ ((k2 & 3) << 1))) << 4) + (n & 7) * 2;
+  const int o1 = k1 * RB + (((n >> 3) ^ tr_swz(k1)) << 4) + (n & 7) * 2;
+  const int o2 = k2 * RB + (((n >> 3) ^ tr_swz(k2)) << 4) + (n & 7) * 2;
   const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(region + o1));
   const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(region + o2));
   typedef short s16x8_t __attribute__((ext_vector_type(8)));
@@ -107,8 +117,8 @@ MOE_DEV bf16x8_t frag_tr(const char* region, int row, int ks, int lane) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int LAYOUT, int EPI, int TM, int TN, int STAGES>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
+template <int LAYOUT, int EPI, int TM, int TN, int BK, int STAGES, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
   constexpr int WM = TM / 2, WN = TN / 2;  // wave tile
   constexpr int FI = WM / 32, FJ = WN / 32;
   constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);  // P reduction-contiguous
@@ -117,6 +127,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   constexpr int LP = PB / 4096, LQ = QB / 4096;  // DMA instructions per wave per k-step
   constexpr int LT = LP + LQ;
   constexpr int PRB = TM * 2, QRB = TN * 2;       // row bytes of strided layouts
+  constexpr int KRB = BK * 2;                     // row bytes of contiguous layouts
+  constexpr int KCPR = KRB / 16;                  // 16-byte chunks per contiguous row
 
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB];
   __shared__ int s_pref[256];
@@ -172,95 +184,80 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
 
   // ---------------------------------------------------------------- DMA plan
   // Instruction i of wave w fills LDS bytes [(i*4+w)*1024, +1024) of a region.
-  // Reduction-contiguous region: 8 rows of 128 B; lane l -> row (i*4+w)*8 + l/8,
-  // LDS slot l%8 <- source chunk (l%8) ^ (l/8).
+  // Reduction-contiguous region: 1024/KRB rows of KRB bytes; lane l -> row
+  // (i*4+w)*(1024/KRB) + l/KCPR, LDS slot l%KCPR <- chunk slot ^ kc_swz(row).
   // Strided region [64][R]: k-row (i*4+w)*(1024/RB) + l/(RB/16), slot l%(RB/16)
-  // <- source chunk slot ^ 2*(krow%4).
-  const char* psrc[LP];   // per instruction: this lane's source at reduction offset 0
-  const char* qsrc[LQ];
-  int pkr[P_KC ? 1 : LP];  // strided: k-row of each instruction (for zero fill)
-  int qkr[Q_KC ? 1 : LQ];
-  {
-    const char* Ab = (const char*)a.A;
-    const char* Bb = (const char*)a.B;
+  // <- source chunk slot ^ 4*(k-row % 4).  Source addresses are recomputed at
+  // every issue from a few per-lane values, which keeps the register budget
+  // for the accumulators.
+  const char* Ab = (const char*)a.A;
+  const char* Bb = (const char*)a.B;
+  const int kc_row = lane / KCPR;                    // row within a 1 KB block
+  constexpr int P_CPR = PRB / 16, Q_CPR = QRB / 16;
+  const int p_kr = lane / P_CPR;                     // strided: k-row within a block
+  const int q_kr = lane / Q_CPR;
+  const int64_t pld = (LAYOUT == MOE_GEMM_NT) ? K : N;
+  const int64_t rows_left0 = r_hi - r_lo;  // strided operands: valid reduction rows
+  const uint32_t smem_base = lds_addr(smem);
+
+  // k-row (within the k-step) that instruction i of this lane fills, strided layouts
+  auto p_krow = [&](int i) __attribute__((always_inline)) { return (i * 4 + wave) * (1024 / PRB) + p_kr; };
+  auto q_krow = [&](int i) __attribute__((always_inline)) { return (i * 4 + wave) * (1024 / QRB) + q_kr; };
+
+  auto issue = [&](int64_t kt) __attribute__((always_inline)) {
+    const uint32_t st = smem_base + (uint32_t)(kt % STAGES) * SB;
+    const int64_t r0 = kt * BK;
 #pragma unroll
     for (int i = 0; i < LP; ++i) {
-      const int blk = i * 4 + wave;
+      const char* src;
       if (P_KC) {
-        const int row = blk * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ (lane >> 3);
+        const int row = (i * 4 + wave) * (1024 / KRB) + kc_row;
+        const int chunk = (lane % KCPR) ^ kc_swz<BK>(row);
         int64_t m = i_lo + row;
         m = m < i_hi ? m : i_hi - 1;
-        const int64_t ld = (LAYOUT == MOE_GEMM_NT) ? K : N;
-        psrc[i] = Ab + (m * ld + chunk * 8) * 2;
+        src = Ab + (m * pld + r0 + chunk * 8) * 2;
       } else {
-        constexpr int CPR = PRB / 16;
-        const int kr = blk * (1024 / PRB) + lane / CPR;
-        const int chunk = (lane % CPR) ^ ((kr & 3) << 1);
+        const int kr = p_krow(i);
+        const int chunk = (lane % P_CPR) ^ tr_swz(kr);
         int64_t col = i_lo + chunk * 8;
         col = col < N - 8 ? col : N - 8;
-        pkr[i] = kr;
-        psrc[i] = Ab + ((r_lo + kr) * N + col) * 2;  // row clamped at issue time
+        int64_t row = r0 + kr;
+        row = r_lo + (row < rows_left0 ? row : rows_left0 - 1);
+        src = Ab + (row * N + col) * 2;
       }
+      dma16(src, __builtin_amdgcn_readfirstlane(st + (i * 4 + wave) * 1024));
     }
 #pragma unroll
     for (int i = 0; i < LQ; ++i) {
-      const int blk = i * 4 + wave;
+      const char* src;
       if (Q_KC) {
-        const int qr = blk * 8 + (lane >> 3);
-        const int chunk = (lane & 7) ^ (lane >> 3);
+        const int qr = (i * 4 + wave) * (1024 / KRB) + kc_row;
+        const int chunk = (lane % KCPR) ^ kc_swz<BK>(qr);
         int64_t row;
         if (EPI == MOE_EPI_SWIGLU) {
-          const int wq = qr / WN, jt = (qr % WN) / 32, jj = qr % 32;
+          const int wq_ = qr / WN, jt = (qr % WN) / 32, jj = qr % 32;
           const int up = jt >= FJ / 2 ? 1 : 0;
-          row = up * F + j0 + wq * (WN / 2) + (jt % (FJ / 2)) * 32 + jj;
+          row = up * F + j0 + wq_ * (WN / 2) + (jt % (FJ / 2)) * 32 + jj;
         } else {
           row = j0 + qr;
           row = row < N ? row : N - 1;
         }
-        qsrc[i] = Bb + (((int64_t)g * N + row) * K + chunk * 8) * 2;
+        src = Bb + (((int64_t)g * N + row) * K + r0 + chunk * 8) * 2;
       } else {
-        constexpr int CPR = QRB / 16;
-        const int kr = blk * (1024 / QRB) + lane / CPR;
-        const int chunk = (lane % CPR) ^ ((kr & 3) << 1);
+        const int kr = q_krow(i);
+        const int chunk = (lane % Q_CPR) ^ tr_swz(kr);
         int64_t col = j0 + chunk * 8;
         col = col < K - 8 ? col : K - 8;
-        qkr[i] = kr;
-        const int64_t base_row = (LAYOUT == MOE_GEMM_NN) ? (int64_t)g * N : r_lo;
-        qsrc[i] = Bb + ((base_row + kr) * K + col) * 2;
+        int64_t row;
+        if (LAYOUT == MOE_GEMM_NN) {
+          row = (int64_t)g * N + r0 + kr;
+        } else {
+          row = r0 + kr;
+          row = r_lo + (row < rows_left0 ? row : rows_left0 - 1);
+        }
+        src = Bb + (row * K + col) * 2;
       }
-    }
-  }
-  const uint32_t smem_base = lds_addr(smem);
-  const int64_t p_rstride = P_KC ? 2 : N * 2;  // bytes per reduction step of 1
-  const int64_t q_rstride = Q_KC ? 2 : K * 2;
-  // strided operands: rows past the group end are clamped to its last row at
-  // issue time and zeroed in LDS before use
-  const int64_t rows_left0 = r_hi - r_lo;
-
-  auto issue = [&](int64_t kt) __attribute__((always_inline)) {
-    const int st = (int)(kt % STAGES);
-    const int64_t r0 = kt * BK;
-#pragma unroll
-    for (int i = 0; i < LP; ++i) {
-      int64_t off = r0 * p_rstride;
-      if (!P_KC) {
-        const int64_t kr = r0 + pkr[i];
-        if (kr >= rows_left0) off = (rows_left0 - 1 - pkr[i]) * p_rstride;
-      }
-      const uint32_t dst = __builtin_amdgcn_readfirstlane(smem_base + st * SB + (i * 4 + wave) * 1024);
-      dma16(psrc[i] + off, dst);
-    }
-#pragma unroll
-    for (int i = 0; i < LQ; ++i) {
-      int64_t off = r0 * q_rstride;
-      if (!Q_KC && LAYOUT == MOE_GEMM_TN) {
-        const int64_t kr = r0 + qkr[i];
-        if (kr >= rows_left0) off = (rows_left0 - 1 - qkr[i]) * q_rstride;
-      }
-      const uint32_t dst =
-          __builtin_amdgcn_readfirstlane(smem_base + st * SB + PB + (i * 4 + wave) * 1024);
-      dma16(qsrc[i] + off, dst);
+      dma16(src, __builtin_amdgcn_readfirstlane(st + PB + (i * 4 + wave) * 1024));
     }
   };
 
@@ -289,11 +286,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
       const uint4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
       for (int i = 0; i < LP; ++i)
-        if (kt * BK + pkr[i] >= rows_left0)
+        if (kt * BK + p_krow(i) >= rows_left0)
           *reinterpret_cast<uint4*>(stage + (i * 4 + wave) * 1024 + lane * 16) = z;
 #pragma unroll
       for (int i = 0; i < LQ; ++i)
-        if (kt * BK + qkr[i] >= rows_left0)
+        if (kt * BK + q_krow(i) >= rows_left0)
           *reinterpret_cast<uint4*>(stage + PB + (i * 4 + wave) * 1024 + lane * 16) = z;
     }
     __syncthreads();
@@ -305,11 +302,11 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
       bf16x8_t pa[FI], qb[FJ];
 #pragma unroll
       for (int it = 0; it < FI; ++it)
-        pa[it] = P_KC ? frag_kc(sP, wp * WM + it * 32, ks, lane)
+        pa[it] = P_KC ? frag_kc<BK>(sP, wp * WM + it * 32, ks, lane)
                       : frag_tr<PRB>(sP, wp * WM + it * 32, ks, lane);
 #pragma unroll
       for (int jt = 0; jt < FJ; ++jt)
-        qb[jt] = Q_KC ? frag_kc(sQ, wq * WN + jt * 32, ks, lane)
+        qb[jt] = Q_KC ? frag_kc<BK>(sQ, wq * WN + jt * 32, ks, lane)
                       : frag_tr<QRB>(sQ, wq * WN + jt * 32, ks, lane);
 #pragma unroll
       for (int it = 0; it < FI; ++it)
@@ -380,7 +377,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   }
 }
 
-template <int LAYOUT, int EPI, int TM, int TN, int STAGES>
+template <int LAYOUT, int EPI, int TM, int TN, int BK, int STAGES, int OCC>
 static hipError_t run(const Args& a, hipStream_t st) {
   int64_t nb;
   if (LAYOUT == MOE_GEMM_TN) {
@@ -391,15 +388,16 @@ static hipError_t run(const Args& a, hipStream_t st) {
     nb = (cdiv64(a.M_total, TM) + a.G) * cdiv64(ncols, colw);
   }
   if (nb == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI, TM, TN, STAGES><<<dim3((unsigned)nb), dim3(256), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, TM, TN, BK, STAGES, OCC><<<dim3((unsigned)nb), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
-// 256 x 128 tiles, 3 k-steps in flight (144 KB of LDS): each wave holds
-// 4 x 2 MFMA tiles (128 fp32 accumulators per lane).
+// 256 x 128 tiles, 32-deep k-steps, 3 in flight: 72 KB of LDS and at most
+// 256 registers per lane (128 fp32 accumulators), so two workgroups run on
+// each CU and hide each other's barriers, DMA issue and epilogues.
 template <int LAYOUT, int EPI>
 static hipError_t pick(const Args& a, hipStream_t st) {
-  return run<LAYOUT, EPI, 256, 128, 3>(a, st);
+  return run<LAYOUT, EPI, 256, 128, 32, 3, 2>(a, st);
 }
 
 }  // namespace mf
