@@ -77,6 +77,35 @@ MOE_DEV void store4_bf16(bf16_t* p, const float* v) {
   o.y = pack_bf16x2(v[2], v[3]);
   *reinterpret_cast<u32x2*>(p) = o;
 }
+// Store one 32-column MFMA tile row from its fp32 accumulator layout as
+// 16-byte chunks.  Lane l (kh = l/32) holds columns gq*8 + kh*4 + 0..3 of
+// groups gq = 0..3 (v[gq*4..+3]); lanes l and l+32 share the row.  For each
+// pair of groups (2p, 2p+1) the two lanes swap halves (v_permlane32_swap) so
+// that lane kh ends with the 8 consecutive columns of group 2p+kh.
+// `row` points at the tile's column 0 in the output row; columns at or past
+// `lim` (relative to that point) are not written.
+MOE_DEV void store_tile_row(bf16_t* row, const float* v, int kh, int64_t lim) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float* lo = v + 8 * p;
+    const float* hi = v + 8 * p + 4;
+    const uint32_t lo0 = pack_bf16x2(lo[0], lo[1]), lo1 = pack_bf16x2(lo[2], lo[3]);
+    const uint32_t hi0 = pack_bf16x2(hi[0], hi[1]), hi1 = pack_bf16x2(hi[2], hi[3]);
+    const uint32_t s0 = kh ? lo0 : hi0, s1 = kh ? lo1 : hi1;
+    const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
+    const uint32_t q0 = kh ? r0[0] : r0[1], q1 = kh ? r1[0] : r1[1];
+    u32x4 o;
+    if (kh == 0) {
+      o.x = lo0; o.y = lo1; o.z = q0; o.w = q1;
+    } else {
+      o.x = q0; o.y = q1; o.z = hi0; o.w = hi1;
+    }
+    const int c = (2 * p + kh) * 8;
+    if (c < lim) *reinterpret_cast<u32x4*>(row + c) = o;
+  }
+}
+
 MOE_DEV void load4_bf16(const bf16_t* p, float* v) {
   const u32x2 w = *reinterpret_cast<const u32x2*>(p);
   v[0] = bf16_lo(w.x);
@@ -116,6 +145,9 @@ MOE_DEV bf16x8_t frag_tr(const char* region, int row, int ks, int lane) {
   const s16x8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
+
+// workgroups resident on one XCD at a time (32 CUs x 2)
+constexpr int kResident = 64;
 
 template <int LAYOUT, int EPI, int TM, int TN, int BK, int STAGES, int OCC>
 __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
@@ -166,14 +198,27 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
     const int total = mt_total * tn_n;
     if ((int)blockIdx.x >= total) return;
     const int L = xcd_remap(blockIdx.x, total);
-    const int tm = L / tn_n, tn = L - tm * tn_n;
+    // group of tile L: its tiles are [s_pref[g]*tn_n, s_pref[g+1]*tn_n)
+    const int tguess = L / tn_n;
     int lo = 0, hi = a.G;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_pref[mid] <= tm) lo = mid; else hi = mid;
+      if (s_pref[mid] <= tguess) lo = mid; else hi = mid;
     }
     g = lo;
-    i_lo = a.offsets[g] + (int64_t)(tm - s_pref[g]) * TM;
+    // Inside a group, tiles run in blocks of NB column tiles x all row tiles,
+    // so the workgroups resident on one XCD at a time share both the group's
+    // rows and its weight columns in L2.
+    const int mt = (g + 1 < a.G ? s_pref[g + 1] : mt_total) - s_pref[g];
+    const int l = L - s_pref[g] * tn_n;
+    int NB = kResident / mt;
+    NB = NB < 1 ? 1 : (NB > tn_n ? tn_n : NB);
+    const int blk = l / (mt * NB);
+    const int nbw = (tn_n - blk * NB) < NB ? (tn_n - blk * NB) : NB;
+    const int rem = l - blk * mt * NB;
+    const int tm_local = rem / nbw;
+    const int tn = blk * NB + (rem - tm_local * nbw);
+    i_lo = a.offsets[g] + (int64_t)tm_local * TM;
     const int64_t gend = a.offsets[g + 1];
     i_hi = i_lo + TM < gend ? i_lo + TM : gend;
     j0 = (int64_t)tn * colw;
@@ -328,52 +373,56 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
     if (i >= i_hi) continue;
     if (EPI == MOE_EPI_SWIGLU) {
 #pragma unroll
-      for (int jt = 0; jt < FJ / 2; ++jt)
+      for (int jt = 0; jt < FJ / 2; ++jt) {
+        const int64_t c = j0 + wq * (WN / 2) + jt * 32;
+        float Gv[16], Uv[16], H[16];
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int64_t c = j0 + wq * (WN / 2) + jt * 32 + gq * 8 + kh * 4;
-          float Gv[4], Uv[4], H[4];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            Gv[u] = acc[it][jt][gq * 4 + u];
-            Uv[u] = acc[it][jt + FJ / 2][gq * 4 + u];
-            H[u] = silu_f(Gv[u]) * Uv[u];
-          }
-          store4_bf16(C + i * F + c, H);
-          if (X) {
-            store4_bf16(X + i * N + c, Gv);
-            store4_bf16(X + i * N + F + c, Uv);
-          }
+        for (int u = 0; u < 16; ++u) {
+          Gv[u] = acc[it][jt][u];
+          Uv[u] = acc[it][jt + FJ / 2][u];
+          H[u] = silu_f(Gv[u]) * Uv[u];
         }
+        store_tile_row(C + i * F + c, H, kh, 32);
+        if (X) {
+          store_tile_row(X + i * N + c, Gv, kh, 32);
+          store_tile_row(X + i * N + F + c, Uv, kh, 32);
+        }
+      }
       continue;
     }
 #pragma unroll
-    for (int jt = 0; jt < FJ; ++jt)
+    for (int jt = 0; jt < FJ; ++jt) {
+      const int64_t c = j0 + wq * WN + jt * 32;
+      const int64_t lim = ncols - c;  // columns left in the output row
+      float v[16];
 #pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int64_t j = j0 + wq * WN + jt * 32 + gq * 8 + kh * 4;
-        if (j >= ncols) continue;
-        float v[4];
+      for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
+      if (LAYOUT == MOE_GEMM_TN) {
+        store_tile_row(C + ((int64_t)g * N + i) * K + c, v, kh, lim);
+      } else if (EPI == MOE_EPI_DSWIGLU) {
+        float dG[16], dU[16];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = acc[it][jt][gq * 4 + u];
-        if (LAYOUT == MOE_GEMM_TN) {
-          store4_bf16(C + ((int64_t)g * N + i) * K + j, v);
-        } else if (EPI == MOE_EPI_DSWIGLU) {
-          float Gv[4], Uv[4], dG[4], dU[4];
-          load4_bf16(X + i * 2 * K + j, Gv);
-          load4_bf16(X + i * 2 * K + K + j, Uv);
+        for (int gq = 0; gq < 4; ++gq) {
+          const int64_t j = c + gq * 8 + kh * 4;
+          float Gv[4] = {0.f, 0.f, 0.f, 0.f}, Uv[4] = {0.f, 0.f, 0.f, 0.f};
+          if (j < ncols) {
+            load4_bf16(X + i * 2 * K + j, Gv);
+            load4_bf16(X + i * 2 * K + K + j, Uv);
+          }
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             const float sg = sigmoid_f(Gv[u]);
-            dG[u] = v[u] * Uv[u] * sg * (1.0f + Gv[u] * (1.0f - sg));
-            dU[u] = v[u] * Gv[u] * sg;
+            const float dh = v[gq * 4 + u];
+            dG[gq * 4 + u] = dh * Uv[u] * sg * (1.0f + Gv[u] * (1.0f - sg));
+            dU[gq * 4 + u] = dh * Gv[u] * sg;
           }
-          store4_bf16(C + i * 2 * K + j, dG);
-          store4_bf16(C + i * 2 * K + K + j, dU);
-        } else {
-          store4_bf16(C + i * ncols + j, v);
         }
+        store_tile_row(C + i * 2 * K + c, dG, kh, lim);
+        store_tile_row(C + i * 2 * K + K + c, dU, kh, lim);
+      } else {
+        store_tile_row(C + i * ncols + c, v, kh, lim);
       }
+    }
   }
 }
 
@@ -392,11 +441,21 @@ static hipError_t run(const Args& a, hipStream_t st) {
   return hipGetLastError();
 }
 
-// 256 x 128 tiles, 32-deep k-steps, 3 in flight: 72 KB of LDS and at most
-// 256 registers per lane (128 fp32 accumulators), so two workgroups run on
-// each CU and hide each other's barriers, DMA issue and epilogues.
+// 32-deep k-steps, 3 in flight: 72 KB of LDS and at most 256 registers per
+// lane (128 fp32 accumulators), so two workgroups run on each CU and hide
+// each other's barriers, DMA issue and epilogues.  Row tiles of the ragged
+// dimension are 128 high (half the padding of 256) when the output width is a
+// multiple of 256 (SwiGLU: the hidden width a multiple of 128); otherwise, and
+// for weight gradients, 256 x 128.
 template <int LAYOUT, int EPI>
 static hipError_t pick(const Args& a, hipStream_t st) {
+  if constexpr (LAYOUT != MOE_GEMM_TN) {
+    bool wide;
+    if (EPI == MOE_EPI_SWIGLU) wide = (a.N / 2) % 128 == 0;
+    else if (LAYOUT == MOE_GEMM_NT) wide = a.N % 256 == 0;
+    else wide = a.K % 256 == 0;
+    if (wide) return run<LAYOUT, EPI, 128, 256, 32, 3, 2>(a, st);
+  }
   return run<LAYOUT, EPI, 256, 128, 32, 3, 2>(a, st);
 }
 
