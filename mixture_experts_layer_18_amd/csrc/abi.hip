@@ -79,7 +79,8 @@ size_t backward_gemm_ws(const moe_desc_t* d) {
     const size_t b = gemm_workspace_bytes(p);
     if (b > m) m = b;
   };
-  upd(gp(MOE_GEMM_TN, 0, MOE_F32, dt, MOE_F32, 1, T, E, D, 0, 0, 0, 0, 0));
+  const int rs = router_wgrad_splits((int)T, (int)D, (int)E);
+  if (rs > 1 && (size_t)rs * E * D * sizeof(float) > m) m = (size_t)rs * E * D * sizeof(float);
   upd(gp(MOE_GEMM_TN, 0, dt, dt, dt, E, A, D, f, 0, 0, 0, 0, 0));
   upd(gp(MOE_GEMM_TN, 0, dt, dt, dt, E, A, 2 * f, D, 0, 0, 0, 0, 0));
   if (F > 0) {
@@ -286,9 +287,7 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
   fwd_ws(d, ws, &fw);
   MOE_TRY(launch_group_offsets_1(fw.one_group, (int32_t)T, st));
   // 1. router logits in fp32
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, MOE_F32, MOE_F32, 1, T, E, D,
-                                 fw.one_group, x, w->w_router, sv->logits, nullptr),
-                              nullptr, 0, st));
+  MOE_TRY(launch_router_logits(x, dt, w->w_router, (int)T, (int)D, (int)E, sv->logits, st));
   // 2. scores, top-k, gates, per-block histogram
   MOE_TRY(launch_route(sv->logits, d->score == MOE_SIGMOID ? w->bias : nullptr, (int)T, (int)E,
                        (int)k, d->score, d->renorm, sv->idx, sv->gate, fw.hist, st));
@@ -327,7 +326,6 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
   const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
   const int dt = d->dtype;
-  if (d->dtype == MOE_BF16 ? D > 4096 : D > 2048) return MOE_ERR_UNSUPPORTED;
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
   if (!g->d_w_router || !g->d_w_gateup || !g->d_w_down) return MOE_ERR_INVALID;
   if (F > 0 && (!w->s_gateup || !w->s_down || !g->d_s_gateup || !g->d_s_down))
@@ -385,9 +383,8 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
                                 nullptr, 0, st));
   }
   // 7. router weight gradient (fp32)
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, MOE_F32, dt, MOE_F32, 1, T, E, D,
-                                 bw.one_group, bw.dlogits, x, g->d_w_router, nullptr),
-                              bw.gemm, bw.gemm_bytes, st));
+  MOE_TRY(launch_router_wgrad(bw.dlogits, x, dt, (int)T, (int)D, (int)E, (float*)bw.gemm,
+                              g->d_w_router, st));
   // 8. input gradient: permuted rows + shared + router terms
   const int dense_router = (d->score == MOE_SOFTMAX && !d->renorm) ? 1 : 0;
   MOE_TRY(launch_unpermute_sum(dt, dx_perm, sv->pos, F > 0 ? bw.dx_shared : nullptr, bw.dlogits,

@@ -42,8 +42,11 @@ template <> struct Vec<float> {
   }
 };
 
-// y[t] = sum_j gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t]), fp32, one rounding
-template <typename T>
+// y[t] = sum_j gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t]), fp32, one rounding.
+// One wavefront per token.  KK > 0 fixes the number of slots at compile time,
+// so the KK row loads of a chunk (and of two chunks per step) are all in flight
+// before any is consumed; KK == 0 is the generic runtime-k loop.
+template <typename T, int KK>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_perm,
                                                       const float* __restrict__ gate,
                                                       const int32_t* __restrict__ pos,
@@ -54,25 +57,56 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nvec = d / VN;
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[VN];
+  const int64_t tk = (int64_t)t * k;
+  if constexpr (KK > 0) {
+    int64_t row[KK];
+    float g[KK];
 #pragma unroll
-    for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const float g = gate[(int64_t)t * k + j];
-      const int64_t p = pos[(int64_t)t * k + j];
-      float v[VN];
-      Vec<T>::load(y_perm + p * d + (int64_t)c * VN, v);
-#pragma unroll
-      for (int u = 0; u < VN; ++u) acc[u] = fmaf(g, v[u], acc[u]);
+    for (int j = 0; j < KK; ++j) {
+      row[j] = (int64_t)pos[tk + j] * d;
+      g[j] = gate[tk + j];
     }
-    if (shared_y) {
-      float v[VN];
-      Vec<T>::load(shared_y + (int64_t)t * d + (int64_t)c * VN, v);
+#pragma unroll 2
+    for (int c = lane; c < nvec; c += 64) {
+      float v[KK][VN];
 #pragma unroll
-      for (int u = 0; u < VN; ++u) acc[u] += v[u];
+      for (int j = 0; j < KK; ++j) Vec<T>::load(y_perm + row[j] + (int64_t)c * VN, v[j]);
+      float sh[VN];
+      if (shared_y) Vec<T>::load(shared_y + (int64_t)t * d + (int64_t)c * VN, sh);
+      float acc[VN];
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KK; ++j)
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] = fmaf(g[j], v[j][u], acc[u]);
+      if (shared_y) {
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] += sh[u];
+      }
+      Vec<T>::store(y + (int64_t)t * d + (int64_t)c * VN, acc);
     }
-    Vec<T>::store(y + (int64_t)t * d + (int64_t)c * VN, acc);
+  } else {
+    for (int c = lane; c < nvec; c += 64) {
+      float acc[VN];
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const float g = gate[tk + j];
+        const int64_t p = pos[tk + j];
+        float v[VN];
+        Vec<T>::load(y_perm + p * d + (int64_t)c * VN, v);
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] = fmaf(g, v[u], acc[u]);
+      }
+      if (shared_y) {
+        float v[VN];
+        Vec<T>::load(shared_y + (int64_t)t * d + (int64_t)c * VN, v);
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] += v[u];
+      }
+      Vec<T>::store(y + (int64_t)t * d + (int64_t)c * VN, acc);
+    }
   }
 }
 
@@ -82,8 +116,9 @@ MOE_DEV float sigmoid_rounded_f(float l) { return (float)(1.0 / (1.0 + exp(-(dou
 //   dy_perm[pos[t,j]] = gate[t,j] * dy[t]
 //   dgate[t,j]        = <dy[t], y_perm[pos[t,j]]>          (fp32)
 //   dlogits[t,:]      from dgate through the gate function (selection fixed)
-// Up to 8 vectors per lane of dy are kept in registers (d <= 4096 bf16).
-template <typename T, int MAXV>
+// The row data is streamed chunk by chunk; with KK > 0 the KK slot rows of a
+// chunk are loaded together and the per-slot dot products kept in registers.
+template <typename T, int KK>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ gate,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ idx,
@@ -94,33 +129,59 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nvec = d / VN;
-  float dyv[MAXV][VN];
-#pragma unroll
-  for (int q = 0; q < MAXV; ++q) {
-    const int c = lane + q * 64;
-    if (c < nvec) Vec<T>::load(dy + (int64_t)t * d + (int64_t)c * VN, dyv[q]);
-  }
+  const int64_t tk = (int64_t)t * k;
   float my_dg = 0.0f;  // lane j keeps dgate[t, j]
-  for (int j = 0; j < k; ++j) {
-    const float g = gate[(int64_t)t * k + j];
-    const int64_t p = pos[(int64_t)t * k + j];
-    float dot = 0.0f;
+  if constexpr (KK > 0) {
+    int64_t row[KK];
+    float g[KK], dot[KK];
 #pragma unroll
-    for (int q = 0; q < MAXV; ++q) {
-      const int c = lane + q * 64;
-      if (c < nvec) {
-        float v[VN], o[VN];
+    for (int j = 0; j < KK; ++j) {
+      row[j] = (int64_t)pos[tk + j] * d;
+      g[j] = gate[tk + j];
+      dot[j] = 0.0f;
+    }
+#pragma unroll 2
+    for (int c = lane; c < nvec; c += 64) {
+      float dv[VN];
+      Vec<T>::load(dy + (int64_t)t * d + (int64_t)c * VN, dv);
+      float v[KK][VN];
+#pragma unroll
+      for (int j = 0; j < KK; ++j) Vec<T>::load(y_perm + row[j] + (int64_t)c * VN, v[j]);
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        float o[VN];
+#pragma unroll
+        for (int u = 0; u < VN; ++u) {
+          dot[j] = fmaf(dv[u], v[j][u], dot[j]);
+          o[u] = g[j] * dv[u];
+        }
+        Vec<T>::store(dy_perm + row[j] + (int64_t)c * VN, o);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KK; ++j) {
+      const float s = wave_sum(dot[j]);
+      if (lane == j) my_dg = s;
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      const float g = gate[tk + j];
+      const int64_t p = pos[tk + j];
+      float dot = 0.0f;
+      for (int c = lane; c < nvec; c += 64) {
+        float dv[VN], v[VN], o[VN];
+        Vec<T>::load(dy + (int64_t)t * d + (int64_t)c * VN, dv);
         Vec<T>::load(y_perm + p * d + (int64_t)c * VN, v);
 #pragma unroll
         for (int u = 0; u < VN; ++u) {
-          dot = fmaf(dyv[q][u], v[u], dot);
-          o[u] = g * dyv[q][u];
+          dot = fmaf(dv[u], v[u], dot);
+          o[u] = g * dv[u];
         }
         Vec<T>::store(dy_perm + p * d + (int64_t)c * VN, o);
       }
+      dot = wave_sum(dot);
+      if (lane == j) my_dg = dot;
     }
-    dot = wave_sum(dot);
-    if (lane == j) my_dg = dot;
   }
 
   // ---- router backward
@@ -199,8 +260,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
 // dx[t] = sum_j dx_perm[pos[t,j]] + dx_shared[t] + sum_e dlogits[t,e] W_r[e]
 // (fp32, slot order, then shared, then router; one rounding).  For sigmoid
 // and renormalised softmax routers dlogits is zero off the picked experts, so
-// only those k rows of W_r are read.
-template <typename T>
+// only those k rows of W_r are read.  KK > 0: compile-time slot count, all
+// slot rows of a chunk in flight together.
+template <typename T, int KK>
 __global__ __launch_bounds__(256) void unpermute_sum_kernel(
     const T* __restrict__ dx_perm, const int32_t* __restrict__ pos, const T* dx_shared,
     const float* __restrict__ dlogits, const int32_t* __restrict__ idx,
@@ -211,32 +273,66 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= Tn) return;
   const int nvec = d / VN;
+  const int64_t tk = (int64_t)t * k;
   const int nr = dense_router ? E : k;
-  for (int c = lane; c < nvec; c += 64) {
-    float acc[VN];
+  if constexpr (KK > 0) {
+    int64_t row[KK];
 #pragma unroll
-    for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      const int64_t p = pos[(int64_t)t * k + j];
-      float v[VN];
-      Vec<T>::load(dx_perm + p * d + (int64_t)c * VN, v);
+    for (int j = 0; j < KK; ++j) row[j] = (int64_t)pos[tk + j] * d;
+#pragma unroll 2
+    for (int c = lane; c < nvec; c += 64) {
+      float v[KK][VN];
 #pragma unroll
-      for (int u = 0; u < VN; ++u) acc[u] += v[u];
+      for (int j = 0; j < KK; ++j) Vec<T>::load(dx_perm + row[j] + (int64_t)c * VN, v[j]);
+      float sh[VN];
+      if (dx_shared) Vec<T>::load(dx_shared + (int64_t)t * d + (int64_t)c * VN, sh);
+      float acc[VN];
+#pragma unroll
+      for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < KK; ++j)
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] += v[j][u];
+      if (dx_shared) {
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] += sh[u];
+      }
+      for (int j = 0; j < nr; ++j) {
+        const int e = dense_router ? j : idx[tk + j];
+        const float dl = dlogits[(int64_t)t * E + e];
+        const float* wr = w_router + (int64_t)e * d + (int64_t)c * VN;
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] = fmaf(dl, wr[u], acc[u]);
+      }
+      Vec<T>::store(dx + (int64_t)t * d + (int64_t)c * VN, acc);
     }
-    if (dx_shared) {
-      float v[VN];
-      Vec<T>::load(dx_shared + (int64_t)t * d + (int64_t)c * VN, v);
+  } else {
+    for (int c = lane; c < nvec; c += 64) {
+      float acc[VN];
 #pragma unroll
-      for (int u = 0; u < VN; ++u) acc[u] += v[u];
-    }
-    for (int j = 0; j < nr; ++j) {
-      const int e = dense_router ? j : idx[(int64_t)t * k + j];
-      const float dl = dlogits[(int64_t)t * E + e];
-      const float* wr = w_router + (int64_t)e * d + (int64_t)c * VN;
+      for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        const int64_t p = pos[tk + j];
+        float v[VN];
+        Vec<T>::load(dx_perm + p * d + (int64_t)c * VN, v);
 #pragma unroll
-      for (int u = 0; u < VN; ++u) acc[u] = fmaf(dl, wr[u], acc[u]);
+        for (int u = 0; u < VN; ++u) acc[u] += v[u];
+      }
+      if (dx_shared) {
+        float v[VN];
+        Vec<T>::load(dx_shared + (int64_t)t * d + (int64_t)c * VN, v);
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] += v[u];
+      }
+      for (int j = 0; j < nr; ++j) {
+        const int e = dense_router ? j : idx[tk + j];
+        const float dl = dlogits[(int64_t)t * E + e];
+        const float* wr = w_router + (int64_t)e * d + (int64_t)c * VN;
+#pragma unroll
+        for (int u = 0; u < VN; ++u) acc[u] = fmaf(dl, wr[u], acc[u]);
+      }
+      Vec<T>::store(dx + (int64_t)t * d + (int64_t)c * VN, acc);
     }
-    Vec<T>::store(dx + (int64_t)t * d + (int64_t)c * VN, acc);
   }
 }
 
@@ -251,16 +347,32 @@ __global__ void group_offsets_1_kernel(int32_t* o, int32_t M) {
   }
 }
 
+// Dispatch a kernel template on the slot count: 1..8 at compile time, other
+// counts through the generic loop (KK = 0).
+#define MOE_K_DISPATCH(KERNEL, T, ...)                                      \
+  switch (k) {                                                              \
+    case 1: KERNEL<T, 1><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 2: KERNEL<T, 2><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 3: KERNEL<T, 3><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 4: KERNEL<T, 4><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 5: KERNEL<T, 5><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 6: KERNEL<T, 6><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 7: KERNEL<T, 7><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    case 8: KERNEL<T, 8><<<grid, block, 0, st>>>(__VA_ARGS__); break;       \
+    default: KERNEL<T, 0><<<grid, block, 0, st>>>(__VA_ARGS__); break;      \
+  }
+
 hipError_t launch_combine(int dtype, const void* y_perm, const float* gate, const int32_t* pos,
                           const void* shared_y, void* y, int T, int d, int k, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv64(T, 4)), block(256);
-  if (dtype == MOE_BF16)
-    combine_kernel<bf16_t><<<grid, block, 0, st>>>((const bf16_t*)y_perm, gate, pos,
-                                                   (const bf16_t*)shared_y, (bf16_t*)y, T, d, k);
-  else
-    combine_kernel<float><<<grid, block, 0, st>>>((const float*)y_perm, gate, pos,
-                                                  (const float*)shared_y, (float*)y, T, d, k);
+  if (dtype == MOE_BF16) {
+    MOE_K_DISPATCH(combine_kernel, bf16_t, (const bf16_t*)y_perm, gate, pos, (const bf16_t*)shared_y,
+                   (bf16_t*)y, T, d, k)
+  } else {
+    MOE_K_DISPATCH(combine_kernel, float, (const float*)y_perm, gate, pos, (const float*)shared_y,
+                   (float*)y, T, d, k)
+  }
   return hipGetLastError();
 }
 
@@ -270,16 +382,13 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, con
                               float* dlogits, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv64(T, 4)), block(256);
-  const int nvec = d / (dtype == MOE_BF16 ? 8 : 4);
-  if (nvec > 8 * 64) return hipErrorInvalidValue;
-  if (dtype == MOE_BF16)
-    combine_bwd_kernel<bf16_t, 8><<<grid, block, 0, st>>>(
-        (const bf16_t*)dy, (const bf16_t*)y_perm, gate, pos, idx, logits, score, renorm, T, d, E,
-        k, (bf16_t*)dy_perm, dlogits);
-  else
-    combine_bwd_kernel<float, 8><<<grid, block, 0, st>>>(
-        (const float*)dy, (const float*)y_perm, gate, pos, idx, logits, score, renorm, T, d, E, k,
-        (float*)dy_perm, dlogits);
+  if (dtype == MOE_BF16) {
+    MOE_K_DISPATCH(combine_bwd_kernel, bf16_t, (const bf16_t*)dy, (const bf16_t*)y_perm, gate, pos, idx,
+                   logits, score, renorm, T, d, E, k, (bf16_t*)dy_perm, dlogits)
+  } else {
+    MOE_K_DISPATCH(combine_bwd_kernel, float, (const float*)dy, (const float*)y_perm, gate, pos, idx,
+                   logits, score, renorm, T, d, E, k, (float*)dy_perm, dlogits)
+  }
   return hipGetLastError();
 }
 
@@ -289,14 +398,13 @@ hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* p
                                 int k, void* dx, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv64(T, 4)), block(256);
-  if (dtype == MOE_BF16)
-    unpermute_sum_kernel<bf16_t><<<grid, block, 0, st>>>(
-        (const bf16_t*)dx_perm, pos, (const bf16_t*)dx_shared, dlogits, idx, w_router,
-        dense_router, T, d, E, k, (bf16_t*)dx);
-  else
-    unpermute_sum_kernel<float><<<grid, block, 0, st>>>(
-        (const float*)dx_perm, pos, (const float*)dx_shared, dlogits, idx, w_router, dense_router,
-        T, d, E, k, (float*)dx);
+  if (dtype == MOE_BF16) {
+    MOE_K_DISPATCH(unpermute_sum_kernel, bf16_t, (const bf16_t*)dx_perm, pos, (const bf16_t*)dx_shared,
+                   dlogits, idx, w_router, dense_router, T, d, E, k, (bf16_t*)dx)
+  } else {
+    MOE_K_DISPATCH(unpermute_sum_kernel, float, (const float*)dx_perm, pos, (const float*)dx_shared,
+                   dlogits, idx, w_router, dense_router, T, d, E, k, (float*)dx)
+  }
   return hipGetLastError();
 }
 

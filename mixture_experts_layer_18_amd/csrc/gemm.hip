@@ -262,6 +262,13 @@ size_t gemm_workspace_bytes(const GemmProblem& p) {
   return (size_t)s * p.G * p.N * p.K * sizeof(float);
 }
 
+hipError_t launch_split_reduce_f32(const float* part, int nsplit, int64_t n, float* out,
+                                  hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  split_reduce_kernel<float><<<dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st>>>(part, nsplit, n, out);
+  return hipGetLastError();
+}
+
 template <int LAYOUT, int EPI, typename TA, typename TB, typename TC>
 static hipError_t run_simt(const KArgs& ka, const GemmProblem& p, hipStream_t st) {
   dim3 grid;

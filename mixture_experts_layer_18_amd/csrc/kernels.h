@@ -29,6 +29,17 @@ size_t gemm_workspace_bytes(const GemmProblem& p);
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);
 hipError_t launch_gemm_mfma(const GemmProblem& p, hipStream_t st);  // bf16 operands only
 
+hipError_t launch_split_reduce_f32(const float* part, int nsplit, int64_t n, float* out,
+                                  hipStream_t st);
+
+// ---- fp32 router products (matrix cores)
+hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int d, int E,
+                                float* logits, hipStream_t st);
+int router_wgrad_splits(int T, int d, int E);
+// dw[E, d] = dl[T, E]^T x[T, d]; `part` holds router_wgrad_splits(..) * E * d floats
+hipError_t launch_router_wgrad(const float* dl, const void* x, int dtype, int T, int d, int E,
+                               float* part, float* dw, hipStream_t st);
+
 // ---- combine and backward helpers
 hipError_t launch_combine(int dtype, const void* y_perm, const float* gate, const int32_t* pos,
                           const void* shared_y, void* y, int T, int d, int k, hipStream_t st);

@@ -224,18 +224,29 @@ __global__ __launch_bounds__(256) void permute_kernel(
     s_pos[i] = p;
   }
   __syncthreads();
-  // row copies: one wavefront per token, 16-byte vectors
-  const int lane = tid & 63, wave = tid >> 6;
+  // row copies: the workgroup walks (token, 16-byte chunk) pairs with
+  // consecutive threads on consecutive chunks, four pairs per thread in
+  // flight; each loaded chunk is stored to the token's k permuted rows
   const int nvec = d * (int)sizeof(TX) / 16;
-  for (int tl = wave; tl < nt; tl += 4) {
-    const u32x4* xr = reinterpret_cast<const u32x4*>(x + (int64_t)(t0 + tl) * d);
-    for (int c = lane; c < nvec; c += 64) {
-      const u32x4 v = xr[c];
+  const int total = nt * nvec;
+  for (int i0 = tid; i0 < total; i0 += 4 * 256) {
+    u32x4 v[4];
+    int tl[4], c[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      int i = i0 + u * 256;
+      i = i < total ? i : total - 1;  // past the end: reload the last chunk, not stored
+      tl[u] = i / nvec;
+      c[u] = i - tl[u] * nvec;
+      v[u] = reinterpret_cast<const u32x4*>(x + (int64_t)(t0 + tl[u]) * d)[c[u]];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (i0 + u * 256 >= total) continue;
       for (int j = 0; j < k; ++j) {
-        const int p = s_pos[tl * k + j];
+        const int p = s_pos[tl[u] * k + j];
         if (p < 0) continue;
-        u32x4* dst = reinterpret_cast<u32x4*>(x_perm + (int64_t)p * d);
-        dst[c] = v;
+        reinterpret_cast<u32x4*>(x_perm + (int64_t)p * d)[c[u]] = v[u];
       }
     }
   }

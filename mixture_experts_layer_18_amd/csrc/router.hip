@@ -1,0 +1,174 @@
+// Router products in fp32 on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32).
+//
+// The router runs in fp32 (Ultimate MoE Training Handbook, section 2.5, the
+// fp32 router dtype): the logits l = x W_r^T and the weight gradient
+// dW_r = dl^T x are fp32 products with fp32 accumulation of a bf16 or fp32 x
+// against the fp32 router weight.  E <= 256 experts makes these thin GEMMs:
+//  * forward: a workgroup (4 waves) computes 64 tokens x 64 experts; each wave
+//    one 32 x 32 tile, the reduction over d staged through LDS in 32-deep
+//    steps (x widened to fp32 on its way in), next step prefetched into
+//    registers;
+//  * weight gradient: a workgroup computes 64 experts x 64 columns of d over
+//    a slice of the tokens; slices are summed afterwards in a fixed order, so
+//    the result is deterministic.
+#include "kernels.h"
+
+namespace moe {
+namespace rt {
+
+constexpr int BK = 32;         // reduction step
+constexpr int LP = BK + 1;     // LDS row pitch in floats (conflict-free column reads)
+
+template <typename TX>
+MOE_DEV void load8(const TX* p, float* f);
+template <>
+MOE_DEV void load8<bf16_t>(const bf16_t* p, float* f) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+template <>
+MOE_DEV void load8<float>(const float* p, float* f) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0];
+  const float4 b = reinterpret_cast<const float4*>(p)[1];
+  f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+}
+
+// logits[T, E] = x[T, d] . W_r[E, d]^T
+template <typename TX>
+__global__ __launch_bounds__(256) void router_logits_kernel(const TX* __restrict__ x,
+                                                            const float* __restrict__ w, int T,
+                                                            int d, int E,
+                                                            float* __restrict__ logits) {
+  __shared__ float xs[64 * LP];
+  __shared__ float ws[64 * LP];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  // loader: thread -> row tid/4 (0..63), 8 consecutive k at (tid%4)*8
+  const int lr = tid >> 2, lk = (tid & 3) * 8;
+  const int tr = min(t0 + lr, T - 1), er = min(e0 + lr, E - 1);
+  const TX* xp = x + (int64_t)tr * d + lk;
+  const float* wp = w + (int64_t)er * d + lk;
+  float xv[8], wv[8];
+  load8<TX>(xp, xv);
+  load8<float>(wp, wv);
+  const int wt = wave >> 1, we = wave & 1;  // this wave's 32-token x 32-expert tile
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int k0 = 0; k0 < d; k0 += BK) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      xs[lr * LP + lk + u] = xv[u];
+      ws[lr * LP + lk + u] = wv[u];
+    }
+    __syncthreads();
+    if (k0 + BK < d) {
+      load8<TX>(xp + k0 + BK, xv);
+      load8<float>(wp + k0 + BK, wv);
+    }
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      const float a = xs[(wt * 32 + (lane & 31)) * LP + kk + (lane >> 5)];
+      const float b = ws[(we * 32 + (lane & 31)) * LP + kk + (lane >> 5)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane: expert (lane%32) of the wave tile, tokens (v/4)*8 + (lane/32)*4 + v%4
+  const int e = e0 + we * 32 + (lane & 31);
+  if (e >= E) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int t = t0 + wt * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    if (t < T) logits[(int64_t)t * E + e] = acc[v];
+  }
+}
+
+// part[s][E][d] = sum over tokens of slice s of dl[t, e] x[t, :]
+template <typename TX>
+__global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dl,
+                                                           const TX* __restrict__ x, int T,
+                                                           int d, int E, int tok_per_split,
+                                                           float* __restrict__ part) {
+  __shared__ float ds[BK * 65];  // [token][expert]
+  __shared__ float xs[BK * 65];  // [token][column]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64, s = blockIdx.z;
+  const int tlo = s * tok_per_split, thi = min(T, tlo + tok_per_split);
+  // loader: thread -> token tid/8 (0..31), 8 consecutive columns at (tid%8)*8
+  const int lt = tid >> 3, lc = (tid & 7) * 8;
+  const int we = wave >> 1, wc = wave & 1;
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int tb = tlo; tb < thi; tb += BK) {
+    const int t = tb + lt;
+    float dv[8], xv[8];
+    if (t < thi) {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dv[u] = (e0 + lc + u < E) ? dl[(int64_t)t * E + e0 + lc + u] : 0.0f;
+      load8<TX>(x + (int64_t)t * d + c0 + lc, xv);
+    } else {
+#pragma unroll
+      for (int u = 0; u < 8; ++u) dv[u] = xv[u] = 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      ds[lt * 65 + lc + u] = dv[u];
+      xs[lt * 65 + lc + u] = xv[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; kk += 2) {
+      const float a = ds[(kk + (lane >> 5)) * 65 + we * 32 + (lane & 31)];
+      const float b = xs[(kk + (lane >> 5)) * 65 + wc * 32 + (lane & 31)];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, acc, 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // lane: column (lane%32) of the wave tile, experts (v/4)*8 + (lane/32)*4 + v%4
+  const int col = c0 + wc * 32 + (lane & 31);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int e = e0 + we * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    if (e < E) part[((int64_t)s * E + e) * d + col] = acc[v];
+  }
+}
+
+}  // namespace rt
+
+int router_wgrad_splits(int T, int d, int E) {
+  const int tiles = (int)(cdiv64(d, 64) * cdiv64(E, 64));
+  int s = 1;
+  while (tiles * s < 1024 && T / (s * 2) >= 256 && s < 64) s *= 2;
+  return s;
+}
+
+hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int d, int E,
+                                float* logits, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  dim3 grid((unsigned)cdiv64(T, 64), (unsigned)cdiv64(E, 64)), block(256);
+  if (dtype == MOE_BF16)
+    rt::router_logits_kernel<bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, w, T, d, E, logits);
+  else
+    rt::router_logits_kernel<float><<<grid, block, 0, st>>>((const float*)x, w, T, d, E, logits);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wgrad(const float* dl, const void* x, int dtype, int T, int d, int E,
+                               float* part, float* dw, hipStream_t st) {
+  const int S = router_wgrad_splits(T, d, E);
+  const int per = (int)cdiv64(T > 0 ? T : 1, S);
+  dim3 grid((unsigned)cdiv64(d, 64), (unsigned)cdiv64(E, 64), (unsigned)S), block(256);
+  float* out = S > 1 ? part : dw;
+  if (dtype == MOE_BF16)
+    rt::router_wgrad_kernel<bf16_t><<<grid, block, 0, st>>>(dl, (const bf16_t*)x, T, d, E, per, out);
+  else
+    rt::router_wgrad_kernel<float><<<grid, block, 0, st>>>(dl, (const float*)x, T, d, E, per, out);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return e;
+  return launch_split_reduce_f32(part, S, (int64_t)E * d, dw, st);
+}
+
+}  // namespace moe
