@@ -237,6 +237,45 @@ int moe_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *x,
                  const moe_saved_t *saved, const void *dy, void *dx, const moe_grads_t *grads,
                  void *ws, size_t ws_bytes, void *stream);
 
+/* ---------------------------------------------------------------- timing */
+
+/* Stages of moe_forward / moe_backward, for the per-stage timing below. */
+enum {
+  MOE_STAGE_ROUTER = 0,            /* fp32 router logits */
+  MOE_STAGE_ROUTE,                 /* scores, top-k, gates, block histogram */
+  MOE_STAGE_PERMUTE,               /* scan + stable scatter of the rows */
+  MOE_STAGE_GATE_UP,               /* routed gate/up GEMM + SwiGLU */
+  MOE_STAGE_DOWN,                  /* routed down GEMM */
+  MOE_STAGE_SHARED_GATE_UP,
+  MOE_STAGE_SHARED_DOWN,
+  MOE_STAGE_COMBINE,
+  MOE_STAGE_COMBINE_BWD,           /* + router backward to dlogits */
+  MOE_STAGE_DOWN_DGRAD,            /* + SwiGLU derivative */
+  MOE_STAGE_DOWN_WGRAD,
+  MOE_STAGE_GATE_UP_WGRAD,
+  MOE_STAGE_GATE_UP_DGRAD,
+  MOE_STAGE_SHARED_DOWN_DGRAD,
+  MOE_STAGE_SHARED_DOWN_WGRAD,
+  MOE_STAGE_SHARED_GATE_UP_WGRAD,
+  MOE_STAGE_SHARED_GATE_UP_DGRAD,
+  MOE_STAGE_ROUTER_WGRAD,
+  MOE_STAGE_UNPERMUTE_SUM,
+  MOE_NUM_STAGES
+};
+
+/* Per-stage timing, a measurement aid.  While enabled, moe_forward and
+ * moe_backward record a pair of HIP events around each stage's launches on
+ * the caller's stream (at most 65536 pairs are kept; later stages go
+ * untimed).  Process-wide state guarded by a lock; do not enable it while
+ * the stream is being captured into a graph.  moe_stage_timing(1) clears
+ * what was recorded; moe_stage_timing(0) stops recording. */
+int moe_stage_timing(int enable);
+
+/* Waits for every recorded stage, adds its elapsed milliseconds to
+ * ms[stage] and 1 to launches[stage] (both arrays of MOE_NUM_STAGES, written
+ * in full), and clears the records.  MOE_ERR_HIP if an event query fails. */
+int moe_stage_times(double *ms, int64_t *launches);
+
 /* tokens per histogram block of moe_route / moe_permute */
 #define MOE_ROUTE_BLOCK 32
 

@@ -20,6 +20,11 @@ MOE_GEMM_NT, MOE_GEMM_NN, MOE_GEMM_TN = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
 MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
 MOE_ROUTE_BLOCK = 32
+STAGES = ["router", "route", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine",
+          "combine_bwd", "down_dgrad", "down_wgrad", "gate_up_wgrad", "gate_up_dgrad", "shared_down_dgrad",
+          "shared_down_wgrad", "shared_gate_up_wgrad", "shared_gate_up_dgrad", "router_wgrad",
+          "unpermute_sum"]
+MOE_NUM_STAGES = len(STAGES)
 
 
 class MoeDesc(ctypes.Structure):
@@ -59,6 +64,8 @@ SIGNATURES = {
     "moe_forward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, c_vp, _P(MoeSaved), c_vp, c_sz, c_vp]),
     "moe_backward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, _P(MoeSaved), c_vp, c_vp, _P(MoeGrads),
                              c_vp, c_sz, c_vp]),
+    "moe_stage_timing": (c_i32, [c_i32]),
+    "moe_stage_times": (c_i32, [_P(ctypes.c_double), _P(c_i64)]),
 }
 
 _lib = None

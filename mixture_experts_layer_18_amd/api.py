@@ -153,3 +153,18 @@ def alloc_grads(desc, device="cuda") -> dict:
 def alloc_workspace(desc, which: str, device="cuda") -> torch.Tensor:
     n = max(workspace_bytes(desc, which), 256)
     return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def stage_timing(enable: bool):
+    """Start (clearing earlier records) or stop per-stage event timing of
+    moe_forward / moe_backward."""
+    _check(L.load().moe_stage_timing(int(bool(enable))), "moe_stage_timing")
+
+
+def stage_times() -> dict:
+    """{stage: (total ms, launches)} of everything recorded since timing was
+    enabled or last read; waits for the recorded events."""
+    ms = (ctypes.c_double * L.MOE_NUM_STAGES)()
+    n = (ctypes.c_int64 * L.MOE_NUM_STAGES)()
+    _check(L.load().moe_stage_times(ms, n), "moe_stage_times")
+    return {name: (ms[i], n[i]) for i, name in enumerate(L.STAGES)}

@@ -1,6 +1,9 @@
 // C ABI of the MoE layer library: argument validation, workspace layout and
 // the launch sequence of the forward and backward passes.  Every check runs
 // on the host before anything is launched; the library allocates nothing.
+#include <mutex>
+#include <vector>
+
 #include "kernels.h"
 
 using namespace moe;
@@ -140,6 +143,56 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
   do {                                        \
     hipError_t _e = (expr);                   \
     if (_e != hipSuccess) return MOE_ERR_HIP; \
+  } while (0)
+
+// ---- per-stage event timing (off unless the caller enables it)
+struct StageRec {
+  int stage;
+  hipEvent_t a, b;
+};
+constexpr size_t kMaxStageRecs = size_t(1) << 16;
+std::mutex g_timing_mu;
+bool g_timing = false;
+std::vector<StageRec> g_recs;   // recorded, not yet read
+std::vector<StageRec> g_spare;  // event pairs ready for reuse
+
+// Returns an event pair already recorded on `st`, or {-1} when not timing.
+StageRec stage_begin(int stage, hipStream_t st) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  StageRec r{-1, nullptr, nullptr};
+  if (!g_timing || g_recs.size() >= kMaxStageRecs) return r;
+  if (!g_spare.empty()) {
+    r = g_spare.back();
+    g_spare.pop_back();
+  } else if (hipEventCreate(&r.a) != hipSuccess) {
+    return StageRec{-1, nullptr, nullptr};
+  } else if (hipEventCreate(&r.b) != hipSuccess) {
+    (void)hipEventDestroy(r.a);
+    return StageRec{-1, nullptr, nullptr};
+  }
+  r.stage = stage;
+  if (hipEventRecord(r.a, st) != hipSuccess) {
+    g_spare.push_back(r);
+    r.stage = -1;
+  }
+  return r;
+}
+
+void stage_end(StageRec r, hipStream_t st) {
+  if (r.stage < 0) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  if (hipEventRecord(r.b, st) == hipSuccess)
+    g_recs.push_back(r);
+  else
+    g_spare.push_back(r);
+}
+
+// Runs the launches of one stage between its two events.
+#define MOE_STAGE(stage, expr)                    \
+  do {                                            \
+    const StageRec _r = stage_begin((stage), st); \
+    MOE_TRY(expr);                                \
+    stage_end(_r, st);                            \
   } while (0)
 
 }  // namespace
@@ -287,32 +340,32 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
   fwd_ws(d, ws, &fw);
   MOE_TRY(launch_group_offsets_1(fw.one_group, (int32_t)T, st));
   // 1. router logits in fp32
-  MOE_TRY(launch_router_logits(x, dt, w->w_router, (int)T, (int)D, (int)E, sv->logits, st));
+  MOE_STAGE(MOE_STAGE_ROUTER, launch_router_logits(x, dt, w->w_router, (int)T, (int)D, (int)E, sv->logits, st));
   // 2. scores, top-k, gates, per-block histogram
-  MOE_TRY(launch_route(sv->logits, d->score == MOE_SIGMOID ? w->bias : nullptr, (int)T, (int)E,
+  MOE_STAGE(MOE_STAGE_ROUTE, launch_route(sv->logits, d->score == MOE_SIGMOID ? w->bias : nullptr, (int)T, (int)E,
                        (int)k, d->score, d->renorm, sv->idx, sv->gate, fw.hist, st));
   // 3. permutation into expert-contiguous rows
-  MOE_TRY(launch_permute(x, dt, sv->idx, fw.hist, (int)T, (int)D, (int)E, (int)k, fw.base,
+  MOE_STAGE(MOE_STAGE_PERMUTE, launch_permute(x, dt, sv->idx, fw.hist, (int)T, (int)D, (int)E, (int)k, fw.base,
                          sv->counts, sv->offsets, sv->pos, sv->src, sv->x_perm, st));
   // 4. gate/up grouped GEMM with the SwiGLU activation
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D,
+  MOE_STAGE(MOE_STAGE_GATE_UP, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D,
                                  sv->offsets, sv->x_perm, w->w_gateup, sv->h, sv->preact),
                               nullptr, 0, st));
   // 5. down grouped GEMM
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
+  MOE_STAGE(MOE_STAGE_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
                                  sv->h, w->w_down, sv->y_perm, nullptr),
                               nullptr, 0, st));
   // 6. shared experts on every token; their output lands in y
   if (F > 0) {
-    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, 1, T, 2 * F, D,
+    MOE_STAGE(MOE_STAGE_SHARED_GATE_UP, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, 1, T, 2 * F, D,
                                    fw.one_group, x, w->s_gateup, sv->s_h, sv->s_preact),
                                 nullptr, 0, st));
-    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
+    MOE_STAGE(MOE_STAGE_SHARED_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
                                    fw.one_group, sv->s_h, w->s_down, y, nullptr),
                                 nullptr, 0, st));
   }
   // 7. weighted combine (+ shared output)
-  MOE_TRY(launch_combine(dt, sv->y_perm, sv->gate, sv->pos, F > 0 ? y : nullptr, y, (int)T,
+  MOE_STAGE(MOE_STAGE_COMBINE, launch_combine(dt, sv->y_perm, sv->gate, sv->pos, F > 0 ? y : nullptr, y, (int)T,
                          (int)D, (int)k, st));
   return MOE_OK;
 }
@@ -347,50 +400,80 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   bwd_ws(d, ws, &bw);
   MOE_TRY(launch_group_offsets_1(bw.one_group, (int32_t)T, st));
   // 1. combine backward + router backward (dlogits)
-  MOE_TRY(launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
+  MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
                              d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
                              bw.dlogits, st));
   // 2. down data gradient fused with the SwiGLU derivative -> dG | dU
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
+  MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
                                  sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
                               nullptr, 0, st));
   // 3. down weight gradient
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
+  MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
                                  bw.dy_perm, sv->h, g->d_w_down, nullptr),
                               bw.gemm, bw.gemm_bytes, st));
   // 4. gate/up weight gradient
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
+  MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
                                  sv->offsets, bw.dgu, sv->x_perm, g->d_w_gateup, nullptr),
                               bw.gemm, bw.gemm_bytes, st));
   // 5. gate/up data gradient (written over dy_perm, which is no longer needed)
   void* dx_perm = bw.dy_perm;
-  MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
+  MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
                                  sv->offsets, bw.dgu, w->w_gateup, dx_perm, nullptr),
                               nullptr, 0, st));
   // 6. shared experts
   if (F > 0) {
-    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
+    MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
                                    bw.one_group, dy, w->s_down, bw.s_dgu, sv->s_preact),
                                 nullptr, 0, st));
-    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
+    MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
                                    bw.one_group, dy, sv->s_h, g->d_s_down, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
-    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
+    MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
                                    bw.one_group, bw.s_dgu, x, g->d_s_gateup, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
-    MOE_TRY(launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
+    MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
                                    bw.one_group, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
                                 nullptr, 0, st));
   }
   // 7. router weight gradient (fp32)
-  MOE_TRY(launch_router_wgrad(bw.dlogits, x, dt, (int)T, (int)D, (int)E, (float*)bw.gemm,
+  MOE_STAGE(MOE_STAGE_ROUTER_WGRAD, launch_router_wgrad(bw.dlogits, x, dt, (int)T, (int)D, (int)E, (float*)bw.gemm,
                               g->d_w_router, st));
   // 8. input gradient: permuted rows + shared + router terms
   const int dense_router = (d->score == MOE_SOFTMAX && !d->renorm) ? 1 : 0;
-  MOE_TRY(launch_unpermute_sum(dt, dx_perm, sv->pos, F > 0 ? bw.dx_shared : nullptr, bw.dlogits,
+  MOE_STAGE(MOE_STAGE_UNPERMUTE_SUM, launch_unpermute_sum(dt, dx_perm, sv->pos, F > 0 ? bw.dx_shared : nullptr, bw.dlogits,
                                sv->idx, w->w_router, dense_router, (int)T, (int)D, (int)E, (int)k,
                                dx, st));
   return MOE_OK;
+}
+
+int moe_stage_timing(int enable) {
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  for (const StageRec& r : g_recs) g_spare.push_back(r);
+  g_recs.clear();
+  g_timing = enable != 0;
+  return MOE_OK;
+}
+
+int moe_stage_times(double* ms, int64_t* launches) {
+  if (!ms || !launches) return MOE_ERR_INVALID;
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+    ms[i] = 0.0;
+    launches[i] = 0;
+  }
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  int status = MOE_OK;
+  for (const StageRec& r : g_recs) {
+    float t = 0.0f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&t, r.a, r.b) != hipSuccess) {
+      status = MOE_ERR_HIP;
+    } else {
+      ms[r.stage] += t;
+      launches[r.stage] += 1;
+    }
+    g_spare.push_back(r);
+  }
+  g_recs.clear();
+  return status;
 }
 
 }  // extern "C"

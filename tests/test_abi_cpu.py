@@ -2,6 +2,7 @@
 answers its size queries and rejects invalid arguments on the host, before
 any GPU work (these calls never reach the HIP runtime)."""
 import ctypes
+import re
 
 import pytest
 
@@ -117,3 +118,21 @@ def test_grouped_gemm_argument_checks(lib):
     assert call(K=96) == L.MOE_ERR_INVALID
     assert call(epi=L.MOE_EPI_SWIGLU, N=192) == L.MOE_ERR_INVALID   # gate/up halves of 64
     assert call(dtype=7) == L.MOE_ERR_INVALID
+
+
+def test_stage_enum_matches_binding():
+    text = open(L.HEADER).read()
+    body = re.search(r"enum \{\s*(MOE_STAGE_ROUTER = 0,.*?MOE_NUM_STAGES)\s*\}", text, re.S).group(1)
+    names = re.findall(r"MOE_STAGE_(\w+)", body)
+    assert [n.lower() for n in names] == L.STAGES
+
+
+def test_stage_timing_without_records(lib):
+    # nothing recorded: no HIP call is made, every slot reads zero
+    assert lib.moe_stage_timing(1) == L.MOE_OK
+    ms = (ctypes.c_double * L.MOE_NUM_STAGES)(*([7.0] * L.MOE_NUM_STAGES))
+    n = (ctypes.c_int64 * L.MOE_NUM_STAGES)(*([7] * L.MOE_NUM_STAGES))
+    assert lib.moe_stage_times(ms, n) == L.MOE_OK
+    assert list(ms) == [0.0] * L.MOE_NUM_STAGES and list(n) == [0] * L.MOE_NUM_STAGES
+    assert lib.moe_stage_times(None, n) == L.MOE_ERR_INVALID
+    assert lib.moe_stage_timing(0) == L.MOE_OK
