@@ -32,7 +32,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="moe7b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-tokens", type=int, default=8192, help="token sample for the oracle timing")
+    p.add_argument("--cpu-tokens", type=int, default=16384, help="token sample for the oracle timing")
     p.add_argument("--pmc-probe", action="store_true",
                    help="run one forward, one 1 GiB device copy and one gate/up GEMM launch, then exit "
                         "(the program that rocprofv3 --pmc passes count)")
