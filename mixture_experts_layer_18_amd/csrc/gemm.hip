@@ -256,10 +256,41 @@ static bool use_mfma(const GemmProblem& p) {
 }
 
 size_t gemm_workspace_bytes(const GemmProblem& p) {
-  if (use_mfma(p)) return 0;
+  if (use_mfma(p)) return gemm_mfma_workspace_bytes(p);
   const int s = simt_splits(p);
   if (s <= 1) return 0;
   return (size_t)s * p.G * p.N * p.K * sizeof(float);
+}
+
+// Same sum, four consecutive elements per thread (n a multiple of 4).
+template <typename TC>
+__global__ __launch_bounds__(256) void split_reduce4_kernel(const float4* __restrict__ part,
+                                                            int nsplit, int64_t n4,
+                                                            TC* __restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n4) return;
+  float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int p = 0; p < nsplit; ++p) {
+    const float4 v = part[(int64_t)p * n4 + i];
+    s.x += v.x; s.y += v.y; s.z += v.z; s.w += v.w;
+  }
+  Elem<TC>::store(C, 4 * i, s.x);
+  Elem<TC>::store(C, 4 * i + 1, s.y);
+  Elem<TC>::store(C, 4 * i + 2, s.z);
+  Elem<TC>::store(C, 4 * i + 3, s.w);
+}
+
+hipError_t launch_split_reduce(const float* part, int nsplit, int64_t n, void* out, int dtype,
+                               hipStream_t st) {
+  if (n == 0) return hipSuccess;
+  if (n % 4) return hipErrorInvalidValue;
+  const int64_t n4 = n / 4;
+  const dim3 grid((unsigned)cdiv64(n4, 256));
+  if (dtype == MOE_BF16)
+    split_reduce4_kernel<bf16_t><<<grid, dim3(256), 0, st>>>((const float4*)part, nsplit, n4, (bf16_t*)out);
+  else
+    split_reduce4_kernel<float><<<grid, dim3(256), 0, st>>>((const float4*)part, nsplit, n4, (float*)out);
+  return hipGetLastError();
 }
 
 hipError_t launch_split_reduce_f32(const float* part, int nsplit, int64_t n, float* out,
@@ -321,7 +352,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, 
   ka.aux = p.aux;
   ka.part = (float*)ws;
   ka.nsplit = 1;
-  if (use_mfma(p)) return launch_gemm_mfma(p, st);
+  if (use_mfma(p)) return launch_gemm_mfma(p, ws, ws_bytes, st);
   ka.nsplit = simt_splits(p);
   if (ka.nsplit > 1 && ws_bytes < gemm_workspace_bytes(p)) return hipErrorInvalidValue;
   // fp32 layers and the fp32 router products (A and/or B may be bf16 there)

@@ -43,6 +43,8 @@ struct Args {
   const bf16_t* B;
   bf16_t* C;
   bf16_t* aux;
+  int splits;   // TN: row slices per group (> 1: fp32 partials in `part`)
+  float* part;  // [splits][G][N][K]
 };
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
@@ -106,14 +108,6 @@ MOE_DEV void store_tile_row(bf16_t* row, const float* v, int kh, int64_t lim) {
   }
 }
 
-MOE_DEV void load4_bf16(const bf16_t* p, float* v) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  v[0] = bf16_lo(w.x);
-  v[1] = bf16_hi(w.x);
-  v[2] = bf16_lo(w.y);
-  v[3] = bf16_hi(w.y);
-}
-
 // ---- fragment reads (lane l: tile row l%32, reduction values (l/32)*8 .. +7)
 // Swizzle of a reduction-contiguous tile with rows of 2*BK bytes: the 16-byte
 // chunk c of row r sits at slot c ^ kc_swz(r).  16 consecutive rows read at
@@ -172,15 +166,25 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
   // ---------------------------------------------------------------- tile
   int g;
   int64_t i_lo, i_hi, j0, r_lo = 0, r_hi, ncols;
+  int split = 0;
   if (LAYOUT == MOE_GEMM_TN) {
     const int ti_n = (int)cdiv64(N, TM), tj_n = (int)cdiv64(K, TN);
     const int per_g = ti_n * tj_n;
-    const int L = xcd_remap(blockIdx.x, a.G * per_g);
+    int L = xcd_remap(blockIdx.x, a.G * per_g * a.splits);
+    split = L / (a.G * per_g);
+    L -= split * (a.G * per_g);
     g = L / per_g;
     const int rem = L - g * per_g;
     const int ti = rem / tj_n, tj = rem - ti * tj_n;
     r_lo = a.offsets[g];
     r_hi = a.offsets[g + 1];
+    if (a.splits > 1) {
+      // slice `split` of the group's rows, in whole k-steps
+      const int64_t chunk = cdiv64(cdiv64(r_hi - r_lo, a.splits), BK) * BK;
+      const int64_t lo = r_lo + split * chunk;
+      r_lo = lo < r_hi ? lo : r_hi;
+      r_hi = lo + chunk < r_hi ? lo + chunk : r_hi;
+    }
     i_lo = (int64_t)ti * TM;
     i_hi = i_lo + TM < N ? i_lo + TM : N;
     j0 = (int64_t)tj * TN;
@@ -367,6 +371,77 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
   const int r32 = lane & 31, kh = lane >> 5;
   bf16_t* C = a.C;
   bf16_t* X = a.aux;
+
+  if constexpr (EPI == MOE_EPI_DSWIGLU) {
+    // The pre-activations G|U of the wave's rows are brought into LDS with
+    // full-row DMA (one 1 KB instruction per 1024/RBW rows) in two phases,
+    // instead of per-lane 8-byte loads, then read in the accumulator layout.
+    constexpr int RBW = WN * 2;          // bytes of one wave-tile row of G (or U)
+    constexpr int CPW = RBW / 16;        // 16-byte chunks per row
+    constexpr int RPI = 1024 / RBW;      // rows per DMA instruction
+    constexpr int NI = 32 / RPI;         // instructions per 32-row block of G (or U)
+    constexpr int WBUF = 16384;          // LDS bytes per wave
+    constexpr int IPP = WBUF / (64 * RBW);  // 32-row blocks per phase
+    static_assert(IPP >= 1 && FI % IPP == 0 && 4 * WBUF <= STAGES * SB, "epilogue staging");
+    // slot of chunk c in row r: c ^ swz(r) (16 consecutive rows read at one
+    // chunk hit distinct 16-byte bank groups)
+    auto swz = [](int r) __attribute__((always_inline)) { return RBW >= 256 ? (r & 15) : ((r >> 1) & 7); };
+    __syncthreads();  // every wave has finished reading the last k-step
+    const char* wbuf = smem + wave * WBUF;
+    const uint32_t wbase = smem_base + wave * WBUF;
+    const int lrow = lane / CPW, lchunk = lane % CPW;
+#pragma unroll
+    for (int ph = 0; ph < FI / IPP; ++ph) {
+      if (ph > 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): reads of the buffer done
+#pragma unroll
+      for (int u = 0; u < IPP; ++u)
+#pragma unroll
+        for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+          for (int q = 0; q < NI; ++q) {
+            const int r = q * RPI + lrow;
+            int64_t i = i_lo + wp * WM + (ph * IPP + u) * 32 + r;
+            i = i < i_hi ? i : i_hi - 1;
+            int64_t col = j0 + wq * WN + (int64_t)((lchunk ^ swz(r)) * 8);
+            col = col < K - 8 ? col : K - 8;
+            dma16(X + i * 2 * K + gu * K + col,
+                  __builtin_amdgcn_readfirstlane(wbase + ((u * 2 + gu) * NI + q) * 1024));
+          }
+      wait_vmcnt<0>();
+#pragma unroll
+      for (int u = 0; u < IPP; ++u) {
+        const int it = ph * IPP + u;
+        const int64_t i = i_lo + wp * WM + it * 32 + r32;
+        const char* Gb = wbuf + (u * 2) * NI * 1024;
+        const char* Ub = Gb + NI * 1024;
+#pragma unroll
+        for (int jt = 0; jt < FJ; ++jt) {
+          const int64_t c = j0 + wq * WN + jt * 32;
+          float dG[16], dU[16];
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int off = r32 * RBW + (((jt * 4 + gq) ^ swz(r32)) << 4) + kh * 8;
+            const u32x2 gw = *reinterpret_cast<const u32x2*>(Gb + off);
+            const u32x2 uw = *reinterpret_cast<const u32x2*>(Ub + off);
+            const float Gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+            const float Uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = sigmoid_f(Gv[e]);
+              const float dh = acc[it][jt][gq * 4 + e];
+              dG[gq * 4 + e] = dh * Uv[e] * sg * (1.0f + Gv[e] * (1.0f - sg));
+              dU[gq * 4 + e] = dh * Gv[e] * sg;
+            }
+          }
+          if (i < i_hi) {
+            store_tile_row(C + i * 2 * K + c, dG, kh, ncols - c);
+            store_tile_row(C + i * 2 * K + K + c, dU, kh, ncols - c);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int it = 0; it < FI; ++it) {
     const int64_t i = i_lo + wp * WM + it * 32 + r32;
@@ -398,27 +473,18 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
 #pragma unroll
       for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
       if (LAYOUT == MOE_GEMM_TN) {
-        store_tile_row(C + ((int64_t)g * N + i) * K + c, v, kh, lim);
-      } else if (EPI == MOE_EPI_DSWIGLU) {
-        float dG[16], dU[16];
+        if (a.splits > 1) {
+          // fp32 partial of this row slice: 4 groups of 4 consecutive columns
+          if (lim > 0) {
+            float* prow = a.part + (((int64_t)split * a.G + g) * N + i) * K + c;
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int64_t j = c + gq * 8 + kh * 4;
-          float Gv[4] = {0.f, 0.f, 0.f, 0.f}, Uv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (j < ncols) {
-            load4_bf16(X + i * 2 * K + j, Gv);
-            load4_bf16(X + i * 2 * K + K + j, Uv);
+            for (int gq = 0; gq < 4; ++gq)
+              *reinterpret_cast<float4*>(prow + gq * 8 + kh * 4) =
+                  make_float4(v[gq * 4], v[gq * 4 + 1], v[gq * 4 + 2], v[gq * 4 + 3]);
           }
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float sg = sigmoid_f(Gv[u]);
-            const float dh = v[gq * 4 + u];
-            dG[gq * 4 + u] = dh * Uv[u] * sg * (1.0f + Gv[u] * (1.0f - sg));
-            dU[gq * 4 + u] = dh * Gv[u] * sg;
-          }
+        } else {
+          store_tile_row(C + ((int64_t)g * N + i) * K + c, v, kh, lim);
         }
-        store_tile_row(C + i * 2 * K + c, dG, kh, lim);
-        store_tile_row(C + i * 2 * K + K + c, dU, kh, lim);
       } else {
         store_tile_row(C + i * ncols + c, v, kh, lim);
       }
@@ -430,7 +496,7 @@ template <int LAYOUT, int EPI, int TM, int TN, int BK, int STAGES, int OCC>
 static hipError_t run(const Args& a, hipStream_t st) {
   int64_t nb;
   if (LAYOUT == MOE_GEMM_TN) {
-    nb = a.G * cdiv64(a.N, TM) * cdiv64(a.K, TN);
+    nb = a.G * cdiv64(a.N, TM) * cdiv64(a.K, TN) * a.splits;
   } else {
     const int64_t ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? a.N / 2 : a.N) : a.K;
     const int64_t colw = (EPI == MOE_EPI_SWIGLU) ? TN / 2 : TN;
@@ -438,7 +504,9 @@ static hipError_t run(const Args& a, hipStream_t st) {
   }
   if (nb == 0) return hipSuccess;
   gemm_kernel<LAYOUT, EPI, TM, TN, BK, STAGES, OCC><<<dim3((unsigned)nb), dim3(256), 0, st>>>(a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || LAYOUT != MOE_GEMM_TN || a.splits <= 1) return e;
+  return launch_split_reduce(a.part, a.splits, (int64_t)a.G * a.N * a.K, a.C, MOE_BF16, st);
 }
 
 // 32-deep k-steps, 3 in flight: 72 KB of LDS and at most 256 registers per
@@ -461,8 +529,30 @@ static hipError_t pick(const Args& a, hipStream_t st) {
 
 }  // namespace mf
 
-hipError_t launch_gemm_mfma(const GemmProblem& p, hipStream_t st) {
+// Weight gradients whose output tiles alone cannot fill the chip (the shared
+// experts: one group) split each group's rows into slices written as fp32
+// partials and summed afterwards in slice order.
+int gemm_mfma_tn_splits(const GemmProblem& p) {
+  if (p.layout != MOE_GEMM_TN || p.G <= 0) return 1;
+  const int64_t tiles = p.G * cdiv64(p.N, 256) * cdiv64(p.K, 128);
+  if (tiles >= 1024) return 1;
+  int64_t s = cdiv64(1024, tiles);
+  const int64_t by_rows = (p.M_total / p.G) / 512;
+  s = s < by_rows ? s : by_rows;
+  s = s < 16 ? s : 16;
+  return s > 1 ? (int)s : 1;
+}
+
+size_t gemm_mfma_workspace_bytes(const GemmProblem& p) {
+  const int s = gemm_mfma_tn_splits(p);
+  return s > 1 ? (size_t)s * p.G * p.N * p.K * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_mfma(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st) {
   mf::Args a;
+  a.splits = gemm_mfma_tn_splits(p);
+  a.part = (float*)ws;
+  if (a.splits > 1 && (!ws || ws_bytes < gemm_mfma_workspace_bytes(p))) return hipErrorInvalidValue;
   a.G = (int)p.G;
   a.M_total = p.M_total;
   a.N = p.N;

@@ -27,7 +27,13 @@ struct GemmProblem {
 };
 size_t gemm_workspace_bytes(const GemmProblem& p);
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);
-hipError_t launch_gemm_mfma(const GemmProblem& p, hipStream_t st);  // bf16 operands only
+hipError_t launch_gemm_mfma(const GemmProblem& p, void* ws, size_t ws_bytes,
+                            hipStream_t st);  // bf16 operands only
+int gemm_mfma_tn_splits(const GemmProblem& p);
+size_t gemm_mfma_workspace_bytes(const GemmProblem& p);
+// out[i] = sum over p < nsplit of part[p * n + i], in order, rounded once to dtype
+hipError_t launch_split_reduce(const float* part, int nsplit, int64_t n, void* out, int dtype,
+                               hipStream_t st);
 
 hipError_t launch_split_reduce_f32(const float* part, int nsplit, int64_t n, float* out,
                                   hipStream_t st);

@@ -148,6 +148,7 @@ GEMM_CASES = [
     ("bf16", 6, 150, 256, 192),
     ("bf16", 5, 40, 384, 128),
     ("f32", 4, 70, 192, 128),
+    ("bf16", 3, 300, 128, 256),   # data gradient on 128 x 256 tiles
 ]
 
 
@@ -221,6 +222,32 @@ def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
         out = host(C)
         assert np.all(out[1] == 0.0), "empty group must give zero"
         assert_rounded(out, ref, dtype, "C")
+
+
+@pytest.mark.parametrize("rows", [[4096], [4000], [5000, 37]], ids=["one-4096", "one-4000", "big-small"])
+def test_weight_gradient_row_slices(rows):
+    """Weight gradients with few output tiles and long groups run as row
+    slices with fp32 partials summed in order (empty slices included)."""
+    print(f"[gemm] TN slices rows={rows}", flush=True)
+    G, N, K = len(rows), 256, 384
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(rows)
+    Mt = int(off[-1])
+    g = np.random.default_rng(sum(rows))
+    A = _rand(g, (Mt, N), "bf16")
+    B = _rand(g, (Mt, K), "bf16")
+    ws_n = M.grouped_gemm_workspace_bytes("TN", "bf16", G, Mt, N, K)
+    assert ws_n > 0, "this shape is expected to use row slices"
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    C = torch.full((G, N, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm("TN", "none", "bf16", G, Mt, N, K, dev(off), dev(A), dev(B), C, None, ws)
+    torch.cuda.synchronize()
+    f64 = lambda a: synth.as_f64(a, "bf16")  # noqa: E731
+    ref = np.stack([f64(A[off[e]:off[e + 1]]).T @ f64(B[off[e]:off[e + 1]]) for e in range(G)])
+    assert_rounded(host(C), ref, "bf16", "C")
+    with pytest.raises(M.MoeError):
+        M.moe_grouped_gemm("TN", "none", "bf16", G, Mt, N, K, dev(off), dev(A), dev(B), C, None,
+                           ws[: ws_n // 2])
 
 
 def _dswiglu_ref(dY, Wd_e, Gm, U):
