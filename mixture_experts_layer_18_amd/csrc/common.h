@@ -15,19 +15,20 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 struct alignas(16) u32x4 { uint32_t x, y, z, w; };
 struct alignas(8) u32x2 { uint32_t x, y; };
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
 MOE_DEV float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
-MOE_DEV bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
+// Two fp32 -> packed bf16 (lo in bits 0..15), round to nearest even, one
+// v_cvt_pk_bf16_f32 on gfx950.
+MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-MOE_DEV uint32_t pack_bf16x2(float lo, float hi) {
-  return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
-}
+// fp32 -> bf16, round to nearest even.
+MOE_DEV bf16_t f32_to_bf16(float f) { return (bf16_t)(pack_bf16x2(f, 0.0f) & 0xffffu); }
 
 MOE_DEV float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 MOE_DEV float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -43,8 +44,10 @@ template <> struct Elem<bf16_t> {
   static MOE_DEV void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
 };
 
-MOE_DEV float silu_f(float z) { return z / (1.0f + __expf(-z)); }
-MOE_DEV float sigmoid_f(float z) { return 1.0f / (1.0f + __expf(-z)); }
+// sigmoid and silu through the hardware exp and reciprocal (about 1 ulp each;
+// every caller rounds the result to bf16 or accumulates it in fp32)
+MOE_DEV float sigmoid_f(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+MOE_DEV float silu_f(float z) { return z * sigmoid_f(z); }
 
 // Sum over the 64 lanes of a wavefront, identical result in every lane.
 // The butterfly order is fixed, so the result is deterministic.
