@@ -45,8 +45,9 @@ def parse():
 # ---- HBM traffic of the dominant kernel, from two rocprofv3 --pmc passes
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_moe7b_bf16_traffic.txt")
-GATE_UP_KERNEL = "mf::gemm_kernel<0, 1,"
-KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_mfma.hip",
+GATE_UP_KERNEL = "pk::gemm_kernel<0, 1>"
+KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_big.hip",
+                  "mixture_experts_layer_18_amd/csrc/gemm_common.h",
                   "mixture_experts_layer_18_amd/csrc/common.h",
                   "mixture_experts_layer_18_amd/csrc/kernels.h"]
 

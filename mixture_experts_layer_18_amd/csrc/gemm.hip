@@ -256,7 +256,7 @@ static bool use_mfma(const GemmProblem& p) {
 }
 
 size_t gemm_workspace_bytes(const GemmProblem& p) {
-  if (use_mfma(p)) return gemm_mfma_workspace_bytes(p);
+  if (use_mfma(p)) return gemm_big_supported(p) ? 0 : gemm_mfma_workspace_bytes(p);
   const int s = simt_splits(p);
   if (s <= 1) return 0;
   return (size_t)s * p.G * p.N * p.K * sizeof(float);
@@ -352,7 +352,10 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, 
   ka.aux = p.aux;
   ka.part = (float*)ws;
   ka.nsplit = 1;
-  if (use_mfma(p)) return launch_gemm_mfma(p, ws, ws_bytes, st);
+  if (use_mfma(p)) {
+    if (gemm_big_supported(p)) return launch_gemm_big(p, st);
+    return launch_gemm_mfma(p, ws, ws_bytes, st);
+  }
   ka.nsplit = simt_splits(p);
   if (ka.nsplit > 1 && ws_bytes < gemm_workspace_bytes(p)) return hipErrorInvalidValue;
   // fp32 layers and the fp32 router products (A and/or B may be bf16 there)

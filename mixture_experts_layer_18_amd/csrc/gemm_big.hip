@@ -1,0 +1,421 @@
+// Persistent bf16 grouped GEMM on gfx950 matrix cores with 256 x 256 tiles.
+//
+// Experts run as grouped GEMMs (Apex-3 code page, "What's inside", row
+// "Fine-grained MoE"; Ultimate MoE Training Handbook, section 2.5).  This
+// kernel covers the long products of the layer:
+//   NT  C[m,n]   = sum_k A[m,k] B[g,n,k]        forward (+ SwiGLU epilogue)
+//   NN  C[m,k]   = sum_n A[m,n] B[g,n,k]        data gradient
+//   TN  C[g,n,k] = sum_{m in g} A[m,n] B[m,k]   weight gradient
+//
+// Why this shape (measured on MI355X):
+//  * one 4-wave workgroup per CU, each wave owning 128 x 128 outputs (256
+//    fp32 accumulators in AGPRs): per flop this moves a third fewer bytes
+//    through the global->LDS DMA path and through LDS reads than two
+//    128 x 256 workgroups per CU, and those two paths are what limits the
+//    matrix cores once the accumulator loop is tight;
+//  * four 32-deep LDS stages (128 KB), three in flight;
+//  * one barrier per k-step, placed between its two 16-deep halves: before
+//    it the wave runs the first half's MFMAs while the second half's
+//    fragments arrive; after it, the next stage's first-half fragments are
+//    requested and the second half's MFMAs run interleaved with the DMA
+//    issue of the stage three steps ahead;
+//  * every k-step issues the same number of vector-memory instructions
+//    (past the end of the reduction, 4-byte pads into a scratch LDS area), so
+//    every wait count is a constant and the loop body has one copy;
+//  * persistent: workgroup w on XCD w%8 walks tiles L = n*W + (w%8)*(W/8) +
+//    w/8, so the W/8 workgroups of one XCD work on neighbouring tiles (shared
+//    A rows and B columns in that XCD's L2); the first stages of the next tile
+//    are fetched before the current tile's epilogue;
+//  * DMA addresses are a wave-uniform tile base in SGPRs plus a 32-bit
+//    per-lane offset recomputed at every issue (few live registers).
+// Operands whose reduction dimension is contiguous (NT both, NN's A) sit in
+// LDS as [256 rows][32] with 16-byte chunks XOR-swizzled by row; strided ones
+// (NN's B, TN both) as [32][256] swizzled by k-row and are read with
+// ds_read_b64_tr_b16 transposes.
+#include "gemm_common.h"
+
+namespace moe {
+namespace pk {
+using namespace gk;
+
+constexpr int TM = 256, TN = 256, BK = 32, STAGES = 4, NW = 4;
+constexpr int WM = 128, WN = 128, FI = WM / 32, FJ = WN / 32;
+constexpr int PB = TM * BK * 2, QB = TN * BK * 2, SB = PB + QB;
+constexpr int LP = PB / (1024 * NW), LQ = QB / (1024 * NW), LT = LP + LQ;
+constexpr int KRB = BK * 2;                    // row bytes, reduction-contiguous layout
+constexpr int SRB = TM * 2;                    // row bytes, reduction-strided layout
+constexpr int PAD_BYTES = LT * 256;            // scratch LDS for the 4-byte pads
+static_assert(TM == TN, "one strided row width");
+static_assert((FI * FJ) % LT == 0, "MFMAs per DMA slot");
+
+struct Args {
+  int G;
+  int64_t M_total, N, K;
+  const int32_t* offsets;
+  const bf16_t* A;
+  const bf16_t* B;
+  bf16_t* C;
+  bf16_t* aux;
+};
+
+struct Tile {
+  int g;
+  int64_t i_lo, i_hi;  // output rows (NT/NN: permuted rows of group g; TN: rows of C[g])
+  int64_t j0;          // first output column
+  int64_t r_lo, r_hi;  // reduction range (TN: the group's rows; else [0, K or N))
+};
+
+template <int LAYOUT, int EPI>
+__global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
+  constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
+  constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
+  __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB + PAD_BYTES];
+  __shared__ int s_pref[256];
+  __shared__ int scratch[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t N = a.N, K = a.K;
+  const int nwg = gridDim.x, per = nwg >> 3;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+
+  // ------------------------------------------------------------ tile table
+  int total, tn_n, mt_total = 0;
+  int64_t ncols;
+  if (LAYOUT == MOE_GEMM_TN) {
+    ncols = K;
+    tn_n = (int)cdiv64(K, TN);
+    total = a.G * (int)cdiv64(N, TM) * tn_n;
+  } else {
+    int n = 0;
+    if (tid < a.G) n = (a.offsets[tid + 1] - a.offsets[tid] + TM - 1) / TM;
+    const int ex = block_exclusive_scan256(n, scratch, &mt_total);
+    if (tid < a.G) s_pref[tid] = ex;
+    __syncthreads();
+    ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? N / 2 : N) : K;
+    const int colw = (EPI == MOE_EPI_SWIGLU) ? TN / 2 : TN;
+    tn_n = (int)cdiv64(ncols, colw);
+    total = mt_total * tn_n;
+  }
+
+  auto tile_of = [&](int L) __attribute__((always_inline)) {
+    Tile t;
+    if (LAYOUT == MOE_GEMM_TN) {
+      const int per_g = (int)cdiv64(N, TM) * tn_n;
+      const int g = L / per_g, rem = L - g * per_g;
+      const int ti = rem / tn_n, tj = rem - ti * tn_n;
+      t.g = __builtin_amdgcn_readfirstlane(g);
+      t.r_lo = __builtin_amdgcn_readfirstlane(a.offsets[t.g]);
+      t.r_hi = __builtin_amdgcn_readfirstlane(a.offsets[t.g + 1]);
+      t.i_lo = (int64_t)__builtin_amdgcn_readfirstlane(ti) * TM;
+      t.i_hi = t.i_lo + TM < N ? t.i_lo + TM : N;
+      t.j0 = (int64_t)__builtin_amdgcn_readfirstlane(tj) * TN;
+    } else {
+      const int tguess = L / tn_n;
+      int lo = 0, hi = a.G;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (s_pref[mid] <= tguess) lo = mid; else hi = mid;
+      }
+      const int g = lo;
+      // inside a group: blocks of NB column tiles x all row tiles, so the
+      // per workgroups of one XCD share the group's rows and weight columns
+      const int mt = (g + 1 < a.G ? s_pref[g + 1] : mt_total) - s_pref[g];
+      const int l = L - s_pref[g] * tn_n;
+      int NB = per / mt;
+      NB = NB < 1 ? 1 : (NB > tn_n ? tn_n : NB);
+      const int blk = l / (mt * NB);
+      const int nbw = (tn_n - blk * NB) < NB ? (tn_n - blk * NB) : NB;
+      const int rem = l - blk * mt * NB;
+      const int tm_local = rem / nbw;
+      const int tn = blk * NB + (rem - tm_local * nbw);
+      t.g = __builtin_amdgcn_readfirstlane(g);
+      const int glo = __builtin_amdgcn_readfirstlane(a.offsets[t.g]);
+      const int ghi = __builtin_amdgcn_readfirstlane(a.offsets[t.g + 1]);
+      t.i_lo = glo + (int64_t)__builtin_amdgcn_readfirstlane(tm_local) * TM;
+      t.i_hi = t.i_lo + TM < ghi ? t.i_lo + TM : ghi;
+      const int colw = (EPI == MOE_EPI_SWIGLU) ? TN / 2 : TN;
+      t.j0 = (int64_t)__builtin_amdgcn_readfirstlane(tn) * colw;
+      t.r_lo = 0;
+      t.r_hi = (LAYOUT == MOE_GEMM_NT) ? K : N;
+    }
+    return t;
+  };
+
+  const char* Ab = (const char*)a.A;
+  const char* Bb = (const char*)a.B;
+  const uint32_t smem_base = lds_addr(smem);
+  const uint32_t pad_lds = smem_base + STAGES * SB;
+  const int64_t F = N / 2;
+
+  // Instruction q (0..LT-1) of k-step kt of tile t: q < LP fills the P tile,
+  // the rest the Q tile.  `ln` is the lane id (an opaque copy per call site).
+  auto issue = [&](const Tile& t, int64_t kt, int q, int ln) __attribute__((always_inline)) {
+    const uint32_t st = smem_base + (uint32_t)(kt % STAGES) * SB;
+    const bool isP = q < LP;
+    const int i = isP ? q : q - LP;
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(st + (isP ? 0 : PB) + (i * NW + wave) * 1024);
+    if ((isP && P_KC) || (!isP && Q_KC)) {
+      // [256 rows][32]: 16 rows of 64 bytes per instruction
+      const int row = (i * NW + wave) * 16 + (ln >> 2);
+      const int chunk = (ln & 3) ^ ((row >> 2) & 3);
+      const uint32_t kb = (uint32_t)(kt * BK * 2) + chunk * 16;
+      if (isP) {
+        const int nrows = (int)(t.i_hi - t.i_lo);
+        const int r = row < nrows ? row : nrows - 1;
+        const int64_t ld = (LAYOUT == MOE_GEMM_NT) ? K : N;
+        dma16_off(Ab + t.i_lo * ld * 2, (uint32_t)r * (uint32_t)(ld * 2) + kb, dst);
+      } else {  // NT's B rows
+        uint32_t roff;
+        if (EPI == MOE_EPI_SWIGLU) {
+          // wave tile columns in 32-wide blocks: gate, up, gate, up
+          const int wq_ = row / WN, jt = (row % WN) / 32, jj = row % 32;
+          roff = (uint32_t)((jt & 1) * F) + wq_ * (WN / 2) + (jt >> 1) * 32 + jj;
+        } else {
+          const int nr = (int)(N - t.j0);
+          roff = row < nr ? row : nr - 1;
+        }
+        dma16_off(Bb + ((int64_t)t.g * N + t.j0) * K * 2, roff * (uint32_t)(K * 2) + kb, dst);
+      }
+    } else {
+      // [32][256]: 2 k-rows of 512 bytes per instruction
+      const int kr = (i * NW + wave) * 2 + (ln >> 5);
+      const int chunk = (ln & 31) ^ ((kr & 3) << 2);
+      if (LAYOUT == MOE_GEMM_NN) {  // B[g, n, k]: k-row n, columns k
+        int64_t col = t.j0 + chunk * 8;
+        col = col < K - 8 ? col : K - 8;
+        const uint32_t off = (uint32_t)((kt * BK + kr) * K + col) * 2;
+        dma16_off(Bb + (int64_t)t.g * N * K * 2, off, dst);
+      } else {  // TN: A[m, n] or B[m, k], rows of the group
+        const int64_t ld = isP ? N : K;
+        const int64_t c0 = isP ? t.i_lo : t.j0;
+        int64_t col = c0 + chunk * 8;
+        col = col < ld - 8 ? col : ld - 8;
+        const int64_t rows = t.r_hi - t.r_lo;
+        int64_t r = kt * BK + kr;
+        r = r < rows ? r : rows - 1;
+        dma16_off((isP ? Ab : Bb) + t.r_lo * ld * 2, (uint32_t)(r * ld + col) * 2, dst);
+      }
+    }
+  };
+  // TN: zero the rows of k-step kt past the group end that this lane loaded
+  // (called after the lane's own DMA for kt completed, before the barrier)
+  auto zero_tail = [&](const Tile& t, int64_t kt) __attribute__((always_inline)) {
+    if (LAYOUT != MOE_GEMM_TN) return;
+    const int64_t rows = t.r_hi - t.r_lo;
+    if ((kt + 1) * BK <= rows) return;
+    char* st = smem + (kt % STAGES) * SB;
+    const uint4 z = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int q = 0; q < LT; ++q) {
+      const int i = q < LP ? q : q - LP;
+      const int kr = (i * NW + wave) * 2 + (lane >> 5);
+      if (kt * BK + kr >= rows)
+        *reinterpret_cast<uint4*>(st + (q < LP ? 0 : PB) + (i * NW + wave) * 1024 + lane * 16) = z;
+    }
+  };
+  auto stage_dma = [&](const Tile& t, int64_t s, int64_t nk, int ln) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < LT; ++q) {
+      if (s < nk) issue(t, s, q, ln);
+      else dma4_pad(Ab, pad_lds + q * 256);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  auto frag_p = [&](const char* st, int it, int ks) __attribute__((always_inline)) {
+    const int row = (wave >> 1) * WM + it * 32;
+    return P_KC ? frag_kc<BK>(st, row, ks, lane) : frag_tr<SRB>(st, row, ks, lane);
+  };
+  auto frag_q = [&](const char* st, int jt, int ks) __attribute__((always_inline)) {
+    const int row = (wave & 1) * WN + jt * 32;
+    return Q_KC ? frag_kc<BK>(st + PB, row, ks, lane) : frag_tr<SRB>(st + PB, row, ks, lane);
+  };
+
+  const int wp = wave >> 1, wq = wave & 1;
+  const int r32 = lane & 31, kh = lane >> 5;
+  int L = xcd * per + slot;
+  if (L >= total) return;
+  Tile t = tile_of(L);
+  int64_t nk = (t.r_hi - t.r_lo + BK - 1) / BK;
+  {
+    const int ln = opaque_i(lane);
+#pragma unroll
+    for (int s = 0; s < STAGES; ++s) stage_dma(t, s, nk, ln);
+  }
+
+  while (true) {
+    // the previous tile's stores and this tile's first stages are complete
+    wait_vmcnt<0>();
+    if (nk > 0) zero_tail(t, 0);
+    lds_barrier();
+    f32x16_t acc[FI][FJ];
+#pragma unroll
+    for (int it = 0; it < FI; ++it)
+#pragma unroll
+      for (int jt = 0; jt < FJ; ++jt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
+    bf16x8_t pa0[FI], qb0[FJ], pa1[FI], qb1[FJ];
+#pragma unroll
+    for (int it = 0; it < FI; ++it) pa0[it] = frag_p(smem, it, 0);
+#pragma unroll
+    for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(smem, jt, 0);
+    const int ln = opaque_i(lane);
+    for (int64_t kt = 0; kt < nk; ++kt) {
+      const char* sP = smem + (kt % STAGES) * SB;
+#pragma unroll
+      for (int it = 0; it < FI; ++it) pa1[it] = frag_p(sP, it, 1);
+#pragma unroll
+      for (int jt = 0; jt < FJ; ++jt) qb1[jt] = frag_q(sP, jt, 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int it = 0; it < FI; ++it)
+#pragma unroll
+        for (int jt = 0; jt < FJ; ++jt)
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb0[jt], pa0[it], acc[it][jt], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // k-step kt+1 landed for this wave (kt+2, kt+3 may be in flight); after
+      // the barrier every wave has it and is done reading k-step kt
+      wait_vmcnt<2 * LT>();
+      if (kt + 1 < nk) zero_tail(t, kt + 1);
+      lds_barrier();
+      const char* nP = smem + ((kt + 1) % STAGES) * SB;
+#pragma unroll
+      for (int it = 0; it < FI; ++it) pa0[it] = frag_p(nP, it, 0);
+#pragma unroll
+      for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(nP, jt, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      const bool real = kt + STAGES < nk;
+#pragma unroll
+      for (int q = 0; q < LT; ++q) {
+#pragma unroll
+        for (int u = 0; u < (FI * FJ) / LT; ++u) {
+          const int m = q * ((FI * FJ) / LT) + u, it = m / FJ, jt = m % FJ;
+          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb1[jt], pa1[it], acc[it][jt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (real) issue(t, kt + STAGES, q, ln);
+        else dma4_pad(Ab, pad_lds + q * 256);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    // every wave is done with this tile's LDS stages: fetch the next tile's
+    // first stages, then write this tile's results
+    lds_barrier();
+    const int Ln = L + nwg;
+    const bool more = Ln < total;
+    Tile tn = t;
+    int64_t nk_n = 0;
+    if (more) {
+      tn = tile_of(Ln);
+      nk_n = (tn.r_hi - tn.r_lo + BK - 1) / BK;
+      const int lp = opaque_i(lane);
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) stage_dma(tn, s, nk_n, lp);
+    }
+
+    // -------------------------------------------------------- epilogue
+    bf16_t* C = a.C;
+    bf16_t* X = a.aux;
+#pragma unroll
+    for (int it = 0; it < FI; ++it) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
+      if (i >= t.i_hi) continue;
+      if (EPI == MOE_EPI_SWIGLU) {
+        // block jt holds gate columns for even jt, up columns for odd jt
+        if (X) {
+#pragma unroll
+          for (int jt = 0; jt < FJ; ++jt) {
+            const int64_t c = (jt & 1) * F + t.j0 + wq * (WN / 2) + (jt >> 1) * 32;
+            float v[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = opaque(acc[it][jt][u]);
+            store_tile_row(X + i * N + c, v, kh, 32);
+          }
+        }
+#pragma unroll
+        for (int jt = 0; jt < FJ / 2; ++jt) {
+          const int64_t c = t.j0 + wq * (WN / 2) + jt * 32;
+          float h[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u)
+            h[u] = silu_f(opaque(acc[it][2 * jt][u])) * opaque(acc[it][2 * jt + 1][u]);
+          store_tile_row(C + i * F + c, h, kh, 32);
+        }
+      } else {
+#pragma unroll
+        for (int jt = 0; jt < FJ; ++jt) {
+          const int64_t c = t.j0 + wq * WN + jt * 32;
+          float v[16];
+#pragma unroll
+          for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
+          bf16_t* row = (LAYOUT == MOE_GEMM_TN) ? C + ((int64_t)t.g * N + i) * K : C + i * ncols;
+          store_tile_row(row + c, v, kh, ncols - c);
+        }
+      }
+    }
+    if (!more) break;
+    L = Ln;
+    t = tn;
+    nk = nk_n;
+  }
+}
+
+// Workgroups of the persistent grid: one per CU.
+static int grid_size() {
+  static int n = 0;
+  if (n == 0) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    n = (cus + 7) / 8 * 8;
+  }
+  return n;
+}
+
+template <int LAYOUT, int EPI>
+static hipError_t run(const Args& a, hipStream_t st) {
+  if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
+  gemm_kernel<LAYOUT, EPI><<<dim3((unsigned)grid_size()), dim3(256), 0, st>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pk
+
+// Which products this kernel takes (the rest go to the two-workgroup kernel):
+// NT with either epilogue when the row widths fit 256-wide tiles (SwiGLU: the
+// hidden width a multiple of 128, so that a tile pairs 128 gate with 128 up
+// columns), and the weight gradient when it has enough tiles to fill the chip
+// without row slices.
+bool gemm_big_supported(const GemmProblem& p) {
+  if (p.ta != MOE_BF16 || p.tb != MOE_BF16 || p.tc != MOE_BF16 || p.G > 256) return false;
+  if (p.layout == MOE_GEMM_NT) {
+    if (p.epilogue == MOE_EPI_SWIGLU) return (p.N / 2) % 128 == 0;
+    return p.epilogue == MOE_EPI_NONE;
+  }
+  if (p.layout == MOE_GEMM_TN) return p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256;
+  if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE;
+  return false;
+}
+
+hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
+  pk::Args a;
+  a.G = (int)p.G;
+  a.M_total = p.M_total;
+  a.N = p.N;
+  a.K = p.K;
+  a.offsets = p.offsets;
+  a.A = (const bf16_t*)p.A;
+  a.B = (const bf16_t*)p.B;
+  a.C = (bf16_t*)p.C;
+  a.aux = (bf16_t*)p.aux;
+  if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE>(a, st);
+  if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU>(a, st);
+  if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NN, MOE_EPI_NONE>(a, st);
+  if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_TN, MOE_EPI_NONE>(a, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

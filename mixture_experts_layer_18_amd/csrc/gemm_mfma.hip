@@ -29,10 +29,11 @@
 //  * tile order is XCD-aware: the hardware deals workgroups to the 8 XCDs
 //    round-robin, so linear tile ids are remapped to give every XCD a
 //    contiguous range, keeping the tiles of one expert inside one L2.
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace moe {
 namespace mf {
+using namespace gk;
 
 
 struct Args {
@@ -46,99 +47,6 @@ struct Args {
   int splits;   // TN: row slices per group (> 1: fp32 partials in `part`)
   float* part;  // [splits][G][N][K]
 };
-
-typedef short s16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) char lds_char;
-
-// One 16-byte-per-lane DMA from global memory into LDS at m0 + 16*lane.
-MOE_DEV void dma16(const void* g, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_base)
-               : "memory", "m0");
-}
-
-// s_waitcnt vmcnt(n) (expcnt and lgkmcnt left unconstrained)
-template <int n>
-MOE_DEV void wait_vmcnt() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
-MOE_DEV uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(const lds_char*)p; }
-
-// Consecutive workgroup ids go to XCD 0,1,..,7,0,..; return the logical tile
-// so that XCD x owns a contiguous block of the nb tiles.
-MOE_DEV int xcd_remap(int bid, int nb) {
-  const int q = nb >> 3, r = nb & 7;
-  const int x = bid & 7, local = bid >> 3;
-  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
-}
-
-MOE_DEV void store4_bf16(bf16_t* p, const float* v) {
-  u32x2 o;
-  o.x = pack_bf16x2(v[0], v[1]);
-  o.y = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<u32x2*>(p) = o;
-}
-// Store one 32-column MFMA tile row from its fp32 accumulator layout as
-// 16-byte chunks.  Lane l (kh = l/32) holds columns gq*8 + kh*4 + 0..3 of
-// groups gq = 0..3 (v[gq*4..+3]); lanes l and l+32 share the row.  For each
-// pair of groups (2p, 2p+1) the two lanes swap halves (v_permlane32_swap) so
-// that lane kh ends with the 8 consecutive columns of group 2p+kh.
-// `row` points at the tile's column 0 in the output row; columns at or past
-// `lim` (relative to that point) are not written.
-MOE_DEV void store_tile_row(bf16_t* row, const float* v, int kh, int64_t lim) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const float* lo = v + 8 * p;
-    const float* hi = v + 8 * p + 4;
-    const uint32_t lo0 = pack_bf16x2(lo[0], lo[1]), lo1 = pack_bf16x2(lo[2], lo[3]);
-    const uint32_t hi0 = pack_bf16x2(hi[0], hi[1]), hi1 = pack_bf16x2(hi[2], hi[3]);
-    const uint32_t s0 = kh ? lo0 : hi0, s1 = kh ? lo1 : hi1;
-    const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
-    const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
-    const uint32_t q0 = kh ? r0[0] : r0[1], q1 = kh ? r1[0] : r1[1];
-    u32x4 o;
-    if (kh == 0) {
-      o.x = lo0; o.y = lo1; o.z = q0; o.w = q1;
-    } else {
-      o.x = q0; o.y = q1; o.z = hi0; o.w = hi1;
-    }
-    const int c = (2 * p + kh) * 8;
-    if (c < lim) *reinterpret_cast<u32x4*>(row + c) = o;
-  }
-}
-
-// ---- fragment reads (lane l: tile row l%32, reduction values (l/32)*8 .. +7)
-// Swizzle of a reduction-contiguous tile with rows of 2*BK bytes: the 16-byte
-// chunk c of row r sits at slot c ^ kc_swz(r).  16 consecutive rows read at
-// the same chunk then cover all 16 bank groups of 256 bytes.
-template <int BK>
-MOE_DEV int kc_swz(int r) {
-  return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3);
-}
-template <int BK>
-MOE_DEV bf16x8_t frag_kc(const char* region, int row, int ks, int lane) {
-  const int r = row + (lane & 31);
-  const int c = ks * 2 + (lane >> 5);
-  return *reinterpret_cast<const bf16x8_t*>(region + r * (2 * BK) + ((c ^ kc_swz<BK>(r)) << 4));
-}
-// Reduction-strided tile [BK][R] (row bytes RB): chunk c of k-row k sits at
-// slot c ^ 4*(k%4); two transpose reads give k = base+0..3 and base+4..7.
-MOE_DEV int tr_swz(int k) { return (k & 3) << 2; }
-template <int RB>
-MOE_DEV bf16x8_t frag_tr(const char* region, int row, int ks, int lane) {
-  const int L = lane & 15, grp = lane >> 4;
-  const int n = row + (grp & 1) * 16 + (L & 3) * 4;
-  const int k1 = ks * 16 + (grp >> 1) * 8 + (L >> 2);
-  const int k2 = k1 + 4;
-  const int o1 = k1 * RB + (((n >> 3) ^ tr_swz(k1)) << 4) + (n & 7) * 2;
-  const int o2 = k2 * RB + (((n >> 3) ^ tr_swz(k2)) << 4) + (n & 7) * 2;
-  const s16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(region + o1));
-  const s16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(region + o2));
-  typedef short s16x8_t __attribute__((ext_vector_type(8)));
-  const s16x8_t v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return __builtin_bit_cast(bf16x8_t, v);
-}
 
 // workgroups resident on one XCD at a time (32 CUs x 2)
 constexpr int kResident = 64;

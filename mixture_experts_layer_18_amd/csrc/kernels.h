@@ -29,6 +29,9 @@ size_t gemm_workspace_bytes(const GemmProblem& p);
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);
 hipError_t launch_gemm_mfma(const GemmProblem& p, void* ws, size_t ws_bytes,
                             hipStream_t st);  // bf16 operands only
+// persistent 256 x 256 kernel (gemm_big.hip) for the products it supports
+bool gemm_big_supported(const GemmProblem& p);
+hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st);
 int gemm_mfma_tn_splits(const GemmProblem& p);
 size_t gemm_mfma_workspace_bytes(const GemmProblem& p);
 // out[i] = sum over p < nsplit of part[p * n + i], in order, rounded once to dtype

@@ -224,6 +224,27 @@ def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
         assert_rounded(out, ref, dtype, "C")
 
 
+def test_weight_gradient_many_groups():
+    """A weight gradient with enough 256 x 256 output tiles for the persistent
+    kernel: ragged groups, an empty group and one group four times the mean."""
+    G, mean, N, K = 64, 100, 1024, 1024
+    print(f"[gemm] TN persistent G={G} N={N} K={K}", flush=True)
+    off = _groups(91, G, mean, empty=(3, 40), big=17)
+    Mt = int(off[-1])
+    g = np.random.default_rng(92)
+    A = _rand(g, (Mt, N), "bf16")
+    B = _rand(g, (Mt, K), "bf16")
+    assert M.grouped_gemm_workspace_bytes("TN", "bf16", G, Mt, N, K) == 0
+    C = torch.full((G, N, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm("TN", "none", "bf16", G, Mt, N, K, dev(off), dev(A), dev(B), C)
+    torch.cuda.synchronize()
+    f64 = lambda a: synth.as_f64(a, "bf16")  # noqa: E731
+    ref = np.stack([f64(A[off[e]:off[e + 1]]).T @ f64(B[off[e]:off[e + 1]]) for e in range(G)])
+    out = host(C)
+    assert np.all(out[3] == 0.0) and np.all(out[40] == 0.0), "empty groups must give zero"
+    assert_rounded(out, ref, "bf16", "C")
+
+
 @pytest.mark.parametrize("rows", [[4096], [4000], [5000, 37]], ids=["one-4096", "one-4000", "big-small"])
 def test_weight_gradient_row_slices(rows):
     """Weight gradients with few output tiles and long groups run as row
