@@ -73,7 +73,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   __shared__ int s_pref[256];
   __shared__ int scratch[4];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
   const int64_t N = a.N, K = a.K;
   const int nwg = gridDim.x, per = nwg >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
@@ -306,17 +307,20 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     const bool more = Ln < total;
     Tile tn = t;
     int64_t nk_n = 0;
-    if (more) {
-      tn = tile_of(Ln);
-      nk_n = (tn.r_hi - tn.r_lo + BK - 1) / BK;
-      const int lp = opaque_i(lane);
+    auto prefetch_next = [&]() __attribute__((always_inline)) {
+      if (more) {
+        tn = tile_of(Ln);
+        nk_n = (tn.r_hi - tn.r_lo + BK - 1) / BK;
+        const int lp = opaque_i(lane);
 #pragma unroll
-      for (int s = 0; s < STAGES; ++s) stage_dma(tn, s, nk_n, lp);
-    }
+        for (int s = 0; s < STAGES; ++s) stage_dma(tn, s, nk_n, lp);
+      }
+    };
 
     // -------------------------------------------------------- epilogue
     bf16_t* C = a.C;
     bf16_t* X = a.aux;
+    prefetch_next();
 #pragma unroll
     for (int it = 0; it < FI; ++it) {
       __builtin_amdgcn_sched_barrier(0);
@@ -385,17 +389,18 @@ static hipError_t run(const Args& a, hipStream_t st) {
 }  // namespace pk
 
 // Which products this kernel takes (the rest go to the two-workgroup kernel):
-// NT with either epilogue when the row widths fit 256-wide tiles (SwiGLU: the
-// hidden width a multiple of 128, so that a tile pairs 128 gate with 128 up
-// columns), and the weight gradient when it has enough tiles to fill the chip
-// without row slices.
+// NT with either epilogue (SwiGLU: the hidden width a multiple of 128, so that
+// a tile pairs 128 gate with 128 up columns), the plain data gradient, and the
+// weight gradient when its columns come in whole 256-wide tiles and it has
+// enough tiles to fill the chip without row slices.
 bool gemm_big_supported(const GemmProblem& p) {
   if (p.ta != MOE_BF16 || p.tb != MOE_BF16 || p.tc != MOE_BF16 || p.G > 256) return false;
   if (p.layout == MOE_GEMM_NT) {
     if (p.epilogue == MOE_EPI_SWIGLU) return (p.N / 2) % 128 == 0;
     return p.epilogue == MOE_EPI_NONE;
   }
-  if (p.layout == MOE_GEMM_TN) return p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256;
+  if (p.layout == MOE_GEMM_TN)  // whole 256-wide column tiles only (else 256 x 128 tiles waste less)
+    return p.K % 256 == 0 && p.G * cdiv64(p.N, 256) * (p.K / 256) >= 4 * 256;
   if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE;
   return false;
 }
