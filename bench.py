@@ -267,6 +267,18 @@ def main():
         "unpermute_sum": T * (2 * d * (k + 1) + 8 * k + 4 * E + sh),  # dx_perm, pos, idx, dlogits,
                                                                       # dx_shared in; dx out
     }
+    def timed_ms(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
     stage_out = {}
     for name, (ms, n) in stages.items():
         if n == 0:
@@ -289,6 +301,13 @@ def main():
     ach = fl_gu / t_gu / 1e12
     tr = measured_traffic() if args.config == "moe7b_bf16" else None
     fwd_tflops = (fl_gu + fl_dn) / (t_gu + t_dn) / 1e12
+    # practical HBM ceiling on this device: a 1 GiB device-to-device copy
+    # (read + write), timed with events on the same stream
+    cbuf = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    cdst = torch.empty_like(cbuf)
+    t_copy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
+    copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
+    del cbuf, cdst
     hbm3 = ["route", "permute", "combine"]
     hbm3_us = sum(stage_out[n]["us"] for n in hbm3)
     hbm3_gbs = sum(hbm_bytes[n] for n in hbm3) / (hbm3_us * 1e-6) / 1e9
@@ -324,7 +343,10 @@ def main():
             "tflops": fwd_tflops, "frac_of_peak": fwd_tflops / PEAK_BF16_TFLOPS,
             "gate_up_us": t_gu * 1e6, "down_us": t_dn * 1e6,
         },
-        "route_permute_combine_hbm": {"gbs": hbm3_gbs, "frac": hbm3_gbs / PEAK_HBM_GBS, "us": hbm3_us},
+        "route_permute_combine_hbm": {"gbs": hbm3_gbs, "frac": hbm3_gbs / PEAK_HBM_GBS, "us": hbm3_us,
+                                      "frac_of_copy": hbm3_gbs / copy_gbs},
+        "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
+                             "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
         "stages": stage_out,
         "loads": {"max_over_mean": float(counts.max() / counts.mean()), "empty": int((counts == 0).sum())},
     }
