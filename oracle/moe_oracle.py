@@ -50,7 +50,10 @@ Parity pins (tests/test_oracle_pins.py): dense-masked brute force, torch fp64
 autograd, central finite differences, single-expert == dense, granularity
 identity, permutation invariants, gate renormalisation, bias-selects-only,
 brute-force top-k, the softmax Jacobian special case and the Handbook's
-parameter count.  Every function below is covered by at least one pin.
+parameter count; for the router training terms, torch fp64 autograd of each
+loss, the single-expert loss of exactly 1, balanced loads, the z-loss closed
+form and the bias update on balanced and skewed loads.  Every function below
+is covered by at least one pin.
 """
 from __future__ import annotations
 
@@ -312,7 +315,116 @@ def router_backward(dgate, scores32, idx, score, renorm):
     return s * (dscore - (s * dscore).sum(axis=1, keepdims=True))
 
 
-def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False):
+# ----------------------------------------------------------------------------- router training terms
+# Apex-3 code page ("What's inside", "Fine-grained MoE"; "Run it yourself":
+# router_bias_update=proportional, router_bias_rate 1e-3 in training and 0.01
+# in the benchmark, seq_aux_alpha=1e-3); Ultimate MoE Training Handbook 2.5
+# (an auxiliary load-balancing loss with coefficient 1e-3, equal to exactly 1
+# with a single expert); KempnerForge README ("Features": router z-loss;
+# "MoE roadmap": sequence aux loss, adaptive bias, z-loss).
+
+def routing_distribution(logits32, score):
+    """q[t, e]: the router's distribution over all E experts, fp64.
+    softmax: the probabilities; sigmoid: the scores normalised to sum 1."""
+    l = np.asarray(logits32, F32).astype(F64)
+    if score == "softmax":
+        z = np.exp(l - l.max(axis=1, keepdims=True))
+        return z / z.sum(axis=1, keepdims=True)
+    s = 1.0 / (1.0 + np.exp(-l))
+    return s / s.sum(axis=1, keepdims=True)
+
+
+def _dlogits_from_dq(logits32, score, dq):
+    """Chain a gradient w.r.t. q (routing_distribution) back to the logits."""
+    l = np.asarray(logits32, F32).astype(F64)
+    if score == "softmax":
+        q = routing_distribution(logits32, score)
+        return q * (dq - (q * dq).sum(axis=1, keepdims=True))
+    s = 1.0 / (1.0 + np.exp(-l))
+    S = s.sum(axis=1, keepdims=True)
+    q = s / S
+    ds = (dq - (q * dq).sum(axis=1, keepdims=True)) / S
+    return ds * s * (1.0 - s)
+
+
+def aux_loss(logits32, counts, k, score, coeff):
+    """Load-balancing loss over the whole batch: coeff * E * sum_e f_e P_e with
+    f_e = counts_e / (T k) (share of the assignments, no gradient) and
+    P_e = mean over tokens of q[t, e].  Returns (value, dlogits [T, E])."""
+    q = routing_distribution(logits32, score)
+    T, E = q.shape
+    f = np.asarray(counts, F64) / (T * k)
+    P = q.mean(axis=0)
+    value = coeff * E * float((f * P).sum())
+    dq = np.broadcast_to(coeff * E * f / T, (T, E))
+    return value, _dlogits_from_dq(logits32, score, dq)
+
+
+def seq_aux_loss(logits32, idx, k, score, coeff, seq_len):
+    """The same balance measured per sequence of seq_len tokens and averaged
+    over the sequences: f^s_e = E/(k S) * #(tokens of s that picked e),
+    P^s_e = mean over the tokens of s of q[t, e]."""
+    q = routing_distribution(logits32, score)
+    T, E = q.shape
+    S = seq_len if seq_len else T
+    n = T // S
+    value = 0.0
+    dq = np.zeros((T, E))
+    for sq in range(n):
+        t0, t1 = sq * S, (sq + 1) * S
+        c = np.bincount(np.asarray(idx[t0:t1]).reshape(-1), minlength=E).astype(F64)
+        f = c * E / (k * S)
+        P = q[t0:t1].mean(axis=0)
+        value += float((f * P).sum())
+        dq[t0:t1] = f / S
+    value *= coeff / n
+    return value, _dlogits_from_dq(logits32, score, dq * coeff / n)
+
+
+def z_loss(logits32, coeff):
+    """coeff * mean over tokens of logsumexp(l_t)^2; gradient
+    coeff * 2/T * lse_t * softmax(l_t)."""
+    l = np.asarray(logits32, F32).astype(F64)
+    T = l.shape[0]
+    m = l.max(axis=1, keepdims=True)
+    z = np.exp(l - m)
+    lse = (m + np.log(z.sum(axis=1, keepdims=True)))
+    value = coeff * float((lse[:, 0] ** 2).mean())
+    return value, coeff * 2.0 / T * lse * (z / z.sum(axis=1, keepdims=True))
+
+
+def router_terms(logits32, idx, counts, k, score, terms):
+    """Sum of the enabled terms: (values dict, dlogits [T, E]).  terms holds
+    aux_coeff, seq_aux_coeff, z_coeff and seq_len (0: one sequence)."""
+    T, E = np.asarray(logits32).shape
+    dl = np.zeros((T, E))
+    vals = {"aux": 0.0, "seq_aux": 0.0, "z": 0.0}
+    if terms.get("aux_coeff", 0.0):
+        vals["aux"], g = aux_loss(logits32, counts, k, score, terms["aux_coeff"])
+        dl += g
+    if terms.get("seq_aux_coeff", 0.0):
+        vals["seq_aux"], g = seq_aux_loss(logits32, idx, k, score, terms["seq_aux_coeff"],
+                                          terms.get("seq_len", 0))
+        dl += g
+    if terms.get("z_coeff", 0.0):
+        vals["z"], g = z_loss(logits32, terms["z_coeff"])
+        dl += g
+    return vals, dl
+
+
+def bias_update(bias32, counts, T, k, rate):
+    """Proportional load-balancing bias update after a step: each expert's
+    bias moves by rate * (mean load - its load) / mean load, mean load
+    T k / E; evaluated in fp64 and rounded once to fp32."""
+    b = np.asarray(bias32, F32).astype(F64)
+    E = b.shape[0]
+    mean = T * k / E
+    c = np.asarray(counts, F64)
+    return (b + F64(np.float32(rate)) * (mean - c) / mean).astype(F32)
+
+
+def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False,
+             terms=None):
     """Backward pass for upstream gradient dy [T, d], reusing ``forward``'s dict.
 
     Returns dict: dx [T,d], d_w_gateup [E,2f,d], d_w_down [E,d,f],
@@ -369,6 +481,9 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
         out["dx_shared"] = None
 
     dlogits = router_backward(dgate, fwd["scores"], idx, score, renorm)
+    if terms is not None:
+        out["router_terms"], dl_terms = router_terms(fwd["logits"], idx, fwd["counts"], k, score, terms)
+        dlogits = dlogits + dl_terms
     wr = np.asarray(w_router, F32).astype(F64)
     out["d_logits"] = dlogits
     out["d_w_router"] = dlogits.T @ x

@@ -325,3 +325,95 @@ def test_p13_softmax_backward_is_the_softmax_jacobian():
     lt = torch.tensor(l.astype(F64), requires_grad=True)
     (torch.softmax(lt, 1) * torch.tensor(dp)).sum().backward()
     assert _rel(dl, lt.grad.numpy()) < 1e-6
+
+
+# --------------------------------------------------------------------------- router training terms
+def _torch_terms(l32, idx, counts, k, score, aux, seq_aux, zc, seq_len):
+    """The three losses written directly in torch fp64 (autograd gives the
+    reference dlogits): switch-style balance, per-sequence balance, z-loss."""
+    l = torch.tensor(l32.astype(F64), requires_grad=True)
+    T, E = l.shape
+    if score == "softmax":
+        q = torch.softmax(l, dim=1)
+    else:
+        s = torch.sigmoid(l)
+        q = s / s.sum(dim=1, keepdim=True)
+    f = torch.tensor(np.asarray(counts, F64)) / (T * k)
+    L_aux = aux * E * (f * q.mean(dim=0)).sum()
+    S = seq_len or T
+    n = T // S
+    L_seq = 0.0
+    for sq in range(n):
+        onehot = torch.zeros(S, E, dtype=torch.float64)
+        onehot.scatter_(1, torch.tensor(idx[sq * S:(sq + 1) * S].astype(np.int64)), 1.0)
+        fs = onehot.sum(dim=0) * E / (k * S)
+        L_seq = L_seq + (fs * q[sq * S:(sq + 1) * S].mean(dim=0)).sum()
+    L_seq = seq_aux * L_seq / n
+    L_z = zc * (torch.logsumexp(l, dim=1) ** 2).mean()
+    total = L_aux + L_seq + L_z
+    total.backward()
+    return float(L_aux), float(L_seq), float(L_z), l.grad.numpy()
+
+
+@pytest.mark.parametrize("score", ["softmax", "sigmoid"])
+def test_router_terms_match_torch_autograd(score):
+    g = np.random.default_rng(21)
+    T, E, k, S = 96, 8, 2, 32
+    l = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    idx, _ = O.select_topk(l, k)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    terms = dict(aux_coeff=1e-3, seq_aux_coeff=2e-3, z_coeff=3e-3, seq_len=S)
+    vals, dl = O.router_terms(l, idx, counts, k, score, terms)
+    ra, rs, rz, rg = _torch_terms(l, idx, counts, k, score, 1e-3, 2e-3, 3e-3, S)
+    assert abs(vals["aux"] - ra) <= 1e-15 + 1e-13 * abs(ra)
+    assert abs(vals["seq_aux"] - rs) <= 1e-15 + 1e-13 * abs(rs)
+    assert abs(vals["z"] - rz) <= 1e-15 + 1e-13 * abs(rz)
+    assert _rel(dl, rg) < 1e-12
+
+
+def test_router_terms_single_expert_balance_loss_is_one():
+    """One expert (E = k = 1): both balance losses equal their coefficient
+    exactly (the Handbook's load balance loss of exactly 1), with zero
+    gradient; the z-loss is mean(l^2) with gradient 2 l / T."""
+    g = np.random.default_rng(22)
+    l = g.standard_normal((40, 1)).astype(np.float32)
+    idx = np.zeros((40, 1), np.int32)
+    for score in ("softmax", "sigmoid"):
+        v, dl = O.aux_loss(l, [40], 1, score, 1.0)
+        assert v == 1.0 and np.all(dl == 0.0)
+        v, dl = O.seq_aux_loss(l, idx, 1, score, 1.0, 8)
+        assert abs(v - 1.0) < 1e-15 and np.all(dl == 0.0)
+    v, dl = O.z_loss(l, 1.0)
+    l64 = l.astype(F64)
+    assert abs(v - float((l64 ** 2).mean())) < 1e-14
+    assert np.max(np.abs(dl - 2.0 * l64 / 40)) < 1e-15
+
+
+def test_router_terms_closed_forms():
+    """Uniform routing and perfectly balanced loads give a balance loss equal to
+    its coefficient; equal logits c give z = (c + ln E)^2 and a gradient of
+    2 (c + ln E) / (T E) on every logit."""
+    T, E, k = 64, 8, 2
+    l = np.full((T, E), 0.75, np.float32)
+    counts = np.full(E, T * k // E)
+    for score in ("softmax", "sigmoid"):
+        v, _ = O.aux_loss(l, counts, k, score, 1.0)
+        assert abs(v - 1.0) < 1e-14
+    c = F64(np.float32(0.75))
+    v, dl = O.z_loss(l, 1.0)
+    assert abs(v - (c + np.log(E)) ** 2) < 1e-13
+    assert np.max(np.abs(dl - 2.0 * (c + np.log(E)) / (T * E))) < 1e-15
+
+
+def test_bias_update_moves_toward_balance():
+    T, k, E, rate = 1024, 4, 8, 0.01
+    b = np.linspace(-0.1, 0.1, E).astype(np.float32)
+    # balanced loads: no change at all
+    assert np.array_equal(O.bias_update(b, np.full(E, T * k // E), T, k, rate), b)
+    # skewed loads: overloaded experts go down, underloaded up, in proportion
+    counts = np.array([1024, 512, 512, 512, 512, 512, 256, 256])
+    nb = O.bias_update(b, counts, T, k, rate).astype(F64)
+    mean = T * k / E
+    want = b.astype(F64) + F64(np.float32(rate)) * (mean - counts) / mean
+    assert np.max(np.abs(nb - want)) <= 2.0 ** -24 * np.max(np.abs(want))
+    assert nb[0] < b[0] and nb[-1] > b[-1] and abs(nb[1] - b[1]) <= 2.0 ** -24
