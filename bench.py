@@ -33,6 +33,10 @@ def parse():
     p.add_argument("--config", default="moe7b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="token sample for the oracle timing")
+    p.add_argument("--router-terms", action="store_true",
+                   help="add the router training terms to every step: balance loss 1e-3, per-sequence balance "
+                        "loss 1e-3 over 4096-token sequences, z-loss 1e-3, and the proportional bias update "
+                        "at rate 1e-3")
     p.add_argument("--pmc-probe", action="store_true",
                    help="run one forward, one 1 GiB device copy and one gate/up GEMM launch, then exit "
                         "(the program that rocprofv3 --pmc passes count)")
@@ -204,9 +208,14 @@ def main():
     wsb = M.alloc_workspace(desc, "backward")
     stream = torch.cuda.current_stream()
 
+    terms = dict(aux_coeff=1e-3, seq_aux_coeff=1e-3, z_coeff=1e-3, seq_len=4096) if args.router_terms else None
+    losses = torch.zeros(4, dtype=torch.float32, device="cuda") if args.router_terms else None
+
     def step():
         M.moe_forward(desc, w, x, y, saved, wsf, stream)
-        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, stream)
+        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, stream, terms=terms, losses=losses)
+        if args.router_terms and cfg.score == "sigmoid":
+            M.moe_bias_update(desc, saved["counts"], 1e-3, w["bias"], stream)
 
     if args.pmc_probe:
         M.moe_forward(desc, w, x, y, saved, wsf, stream)
@@ -331,6 +340,7 @@ def main():
                         f"{cfg.f_shared}",
             "tokens_per_step": T, "d_model": d, "experts": E, "top_k": k, "d_ff": f,
             "shared": f"{cfg.n_shared}x{cfg.f_shared}", "parallelism": "single GPU",
+            "router_terms": terms,
         },
         "roofline": {
             "kernel": "gate/up grouped GEMM + SwiGLU (forward, NT)",

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 /* ---------------------------------------------------------------- status */
 enum {
@@ -130,6 +130,28 @@ typedef struct moe_grads {
   void *d_s_gateup;   /* [2F, d], NULL if F = 0           */
   void *d_s_down;     /* [d, F], NULL if F = 0            */
 } moe_grads_t;
+
+/* Router training terms added by moe_backward (each 0 = off).  With q[t,e]
+ * the router's distribution over the E experts (softmax probabilities, or the
+ * sigmoid scores normalised to sum 1):
+ *   aux     = aux_coeff * E * sum_e f_e P_e,  f_e = counts_e / (T k),
+ *             P_e = mean over tokens of q[t,e]          (Handbook 2.5, the
+ *             auxiliary balance loss with coefficient 1e-3)
+ *   seq_aux = seq_aux_coeff * mean over sequences s of sum_e f^s_e P^s_e,
+ *             f^s_e = E/(k S) * #(tokens of s picking e), P^s_e = mean over
+ *             s of q[t,e]                                (Apex-3 "Run it
+ *             yourself", seq_aux_alpha; KempnerForge "MoE roadmap")
+ *   z       = z_coeff * mean over tokens of logsumexp(l_t)^2 (KempnerForge
+ *             "Features": router z-loss)
+ * The load shares f carry no gradient; the gradients reach the logits
+ * through q (and the softmax for z).  seq_len must divide T (0: the whole
+ * batch is one sequence); coefficients must be finite and >= 0. */
+typedef struct {
+  float aux_coeff;
+  float seq_aux_coeff;
+  float z_coeff;
+  int32_t seq_len;
+} moe_router_terms_t;
 
 /* grouped GEMM layouts and epilogues (see moe_grouped_gemm) */
 enum { MOE_GEMM_NT = 0, MOE_GEMM_NN = 1, MOE_GEMM_TN = 2 };
@@ -232,10 +254,26 @@ int moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *x, v
  * unpermute-sum of the input gradient.
  *   x [T, d] (the forward input), saved (from moe_forward), dy [T, d] (in),
  *   dx [T, d] (out), grads (out)
+ *   terms   NULL, or router training terms whose gradients are added to the
+ *           router gradient (and so to d_w_router and dx)
+ *   losses  NULL, or device float[3] receiving the aux, seq_aux and z values
+ *           (requires terms)
  *   ws >= moe_workspace_bytes(desc, MOE_WS_BACKWARD) */
 int moe_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *x,
                  const moe_saved_t *saved, const void *dy, void *dx, const moe_grads_t *grads,
-                 void *ws, size_t ws_bytes, void *stream);
+                 const moe_router_terms_t *terms, float *losses, void *ws, size_t ws_bytes,
+                 void *stream);
+
+/* Proportional load-balancing update of the sigmoid router's selection bias
+ * after a step (Apex-3 code page: the per-expert bias balances the load
+ * without a loss term; router_bias_update=proportional with router_bias_rate
+ * 1e-3 in training and 0.01 in the benchmark):
+ *   bias[e] += rate * (T k / E - counts[e]) / (T k / E)
+ * evaluated in fp64 and rounded once to fp32.
+ *   counts [E] int32 (device, from moe_forward), bias [E] fp32 (device, in/out)
+ * MOE_ERR_INVALID for a non-finite rate or null pointers (T > 0). */
+int moe_bias_update(const moe_desc_t *desc, const int32_t *counts, float rate, float *bias,
+                    void *stream);
 
 /* ---------------------------------------------------------------- timing */
 
@@ -260,6 +298,7 @@ enum {
   MOE_STAGE_SHARED_GATE_UP_DGRAD,
   MOE_STAGE_ROUTER_WGRAD,
   MOE_STAGE_UNPERMUTE_SUM,
+  MOE_STAGE_ROUTER_TERMS,          /* balance losses and z-loss (when requested) */
   MOE_NUM_STAGES
 };
 

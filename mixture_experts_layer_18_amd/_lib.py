@@ -23,7 +23,7 @@ MOE_ROUTE_BLOCK = 32
 STAGES = ["router", "route", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine",
           "combine_bwd", "down_dgrad", "down_wgrad", "gate_up_wgrad", "gate_up_dgrad", "shared_down_dgrad",
           "shared_down_wgrad", "shared_gate_up_wgrad", "shared_gate_up_dgrad", "router_wgrad",
-          "unpermute_sum"]
+          "unpermute_sum", "router_terms"]
 MOE_NUM_STAGES = len(STAGES)
 
 
@@ -42,6 +42,11 @@ class MoeSaved(ctypes.Structure):
     _fields_ = [("logits", c_vp), ("idx", c_vp), ("gate", c_vp), ("counts", c_vp), ("offsets", c_vp),
                 ("pos", c_vp), ("src", c_vp), ("x_perm", c_vp), ("preact", c_vp), ("h", c_vp),
                 ("y_perm", c_vp), ("s_preact", c_vp), ("s_h", c_vp)]
+
+
+class MoeRouterTerms(ctypes.Structure):
+    _fields_ = [("aux_coeff", ctypes.c_float), ("seq_aux_coeff", ctypes.c_float), ("z_coeff", ctypes.c_float),
+                ("seq_len", c_i32)]
 
 
 class MoeGrads(ctypes.Structure):
@@ -63,7 +68,8 @@ SIGNATURES = {
     "moe_combine": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_forward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, c_vp, _P(MoeSaved), c_vp, c_sz, c_vp]),
     "moe_backward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, _P(MoeSaved), c_vp, c_vp, _P(MoeGrads),
-                             c_vp, c_sz, c_vp]),
+                             _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
+    "moe_bias_update": (c_i32, [_P(MoeDesc), c_vp, ctypes.c_float, c_vp, c_vp]),
     "moe_stage_timing": (c_i32, [c_i32]),
     "moe_stage_times": (c_i32, [_P(ctypes.c_double), _P(c_i64)]),
 }

@@ -115,13 +115,28 @@ def moe_forward(desc, weights: dict, x, y, saved: dict, ws, stream=None):
                                 ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
 
 
-def moe_backward(desc, weights: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None):
+def moe_backward(desc, weights: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None, terms=None,
+                 losses=None):
+    """terms: None or dict(aux_coeff=, seq_aux_coeff=, z_coeff=, seq_len=); losses: None or a float32
+    device tensor of 3 elements receiving the aux, seq_aux and z values."""
     w = _weights(weights)
     s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
     g = L.MoeGrads(*(_p(grads.get(n)) for n in GRAD_FIELDS))
+    rt = None
+    if terms is not None:
+        rt = ctypes.byref(L.MoeRouterTerms(aux_coeff=float(terms.get("aux_coeff", 0.0)),
+                                           seq_aux_coeff=float(terms.get("seq_aux_coeff", 0.0)),
+                                           z_coeff=float(terms.get("z_coeff", 0.0)),
+                                           seq_len=int(terms.get("seq_len", 0))))
     _check(L.load().moe_backward(ctypes.byref(desc), ctypes.byref(w), _p(x), ctypes.byref(s), _p(dy), _p(dx),
-                                 ctypes.byref(g), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
-           "moe_backward")
+                                 ctypes.byref(g), rt, _p(losses), _p(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "moe_backward")
+
+
+def moe_bias_update(desc, counts, rate, bias, stream=None):
+    """bias [E] fp32 (in place) += rate * (mean load - counts) / mean load."""
+    _check(L.load().moe_bias_update(ctypes.byref(desc), _p(counts), float(rate), _p(bias), _stream(stream)),
+           "moe_bias_update")
 
 
 # ------------------------------------------------------------------ buffers (torch device memory)

@@ -110,6 +110,7 @@ size_t fwd_ws(const moe_desc_t* d, void* ws, FwdWs* out) {
 }
 
 struct BwdWs {
+  void* terms;
   void* dy_perm;   // [A, d]; reused for dx_perm once the down gradients are done
   void* dgu;       // [A, 2f]
   float* dlogits;  // [T, E]
@@ -128,6 +129,7 @@ size_t bwd_ws(const moe_desc_t* d, void* ws, BwdWs* out) {
   w.dy_perm = c.take((size_t)A * D * es);
   w.dgu = c.take((size_t)A * 2 * f * es);
   w.dlogits = (float*)c.take((size_t)T * d->num_experts * sizeof(float));
+  w.terms = c.take(router_terms_ws_bytes(T, d->num_experts));
   w.s_dgu = F > 0 ? c.take((size_t)T * 2 * F * es) : nullptr;
   w.dx_shared = F > 0 ? c.take((size_t)T * D * es) : nullptr;
   w.one_group = (int32_t*)c.take(2 * sizeof(int32_t));
@@ -372,9 +374,19 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
 
 int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
                  const moe_saved_t* sv, const void* dy, void* dx, const moe_grads_t* g,
-                 void* ws, size_t ws_bytes, void* stream) {
+                 const moe_router_terms_t* terms, float* losses, void* ws, size_t ws_bytes,
+                 void* stream) {
   int s = check_desc(d);
   if (s) return s;
+  if (losses && !terms) return MOE_ERR_INVALID;
+  if (terms) {
+    const float cs[3] = {terms->aux_coeff, terms->seq_aux_coeff, terms->z_coeff};
+    for (float c : cs)
+      if (!(c >= 0.0f) || c > 3.0e38f) return MOE_ERR_INVALID;  // also rejects NaN
+    if (terms->seq_len < 0 || (terms->seq_len > 0 && d->num_tokens % terms->seq_len))
+      return MOE_ERR_INVALID;
+    if (!aligned16(losses)) return MOE_ERR_ALIGN;
+  }
   if (!w || !sv || !g) return MOE_ERR_INVALID;
   const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
   const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
@@ -403,6 +415,18 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
                              d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
                              bw.dlogits, st));
+  // 1b. router training terms: their gradients join the router gradient
+  if (terms && T > 0 && !sv->counts) return MOE_ERR_INVALID;
+  // terms_grad: some term adds gradient; the kernels also run for the loss
+  // values alone
+  const bool terms_grad = terms && (terms->aux_coeff > 0.0f || terms->seq_aux_coeff > 0.0f ||
+                                    terms->z_coeff > 0.0f);
+  if (terms_grad || losses) {
+    MOE_STAGE(MOE_STAGE_ROUTER_TERMS,
+              launch_router_terms(sv->logits, sv->idx, sv->counts, (int)T, (int)E, (int)k, d->score,
+                                  terms->aux_coeff, terms->seq_aux_coeff, terms->z_coeff,
+                                  terms->seq_len, bw.dlogits, losses, bw.terms, st));
+  }
   // 2. down data gradient fused with the SwiGLU derivative -> dG | dU
   MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
                                  sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
@@ -439,10 +463,26 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   MOE_STAGE(MOE_STAGE_ROUTER_WGRAD, launch_router_wgrad(bw.dlogits, x, dt, (int)T, (int)D, (int)E, (float*)bw.gemm,
                               g->d_w_router, st));
   // 8. input gradient: permuted rows + shared + router terms
-  const int dense_router = (d->score == MOE_SOFTMAX && !d->renorm) ? 1 : 0;
+  // the router term of dx runs over all experts when every logit can carry
+  // gradient: a softmax without renormalisation, or any router with the
+  // balance or z-loss terms on
+  const int dense_router = ((d->score == MOE_SOFTMAX && !d->renorm) || terms_grad) ? 1 : 0;
   MOE_STAGE(MOE_STAGE_UNPERMUTE_SUM, launch_unpermute_sum(dt, dx_perm, sv->pos, F > 0 ? bw.dx_shared : nullptr, bw.dlogits,
                                sv->idx, w->w_router, dense_router, (int)T, (int)D, (int)E, (int)k,
                                dx, st));
+  return MOE_OK;
+}
+
+int moe_bias_update(const moe_desc_t* d, const int32_t* counts, float rate, float* bias,
+                    void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (!(rate == rate) || rate > 3.0e38f || rate < -3.0e38f) return MOE_ERR_INVALID;
+  if (d->num_tokens == 0) return MOE_OK;
+  if (!counts || !bias) return MOE_ERR_INVALID;
+  if (!aligned16(counts) || !aligned16(bias)) return MOE_ERR_ALIGN;
+  MOE_TRY(launch_bias_update(counts, (int)d->num_tokens, (int)d->num_experts, (int)d->top_k, rate, bias,
+                             (hipStream_t)stream));
   return MOE_OK;
 }
 

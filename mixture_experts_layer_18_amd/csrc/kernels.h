@@ -49,6 +49,16 @@ int router_wgrad_splits(int T, int d, int E);
 hipError_t launch_router_wgrad(const float* dl, const void* x, int dtype, int T, int d, int E,
                                float* part, float* dw, hipStream_t st);
 
+// ---- router training terms
+size_t router_terms_ws_bytes(int64_t T, int64_t E);
+// dlogits += gradients of the enabled terms; losses (nullable): aux, seq_aux, z
+hipError_t launch_router_terms(const float* logits, const int32_t* idx, const int32_t* counts,
+                               int T, int E, int k, int score, float aux_coeff,
+                               float seq_aux_coeff, float z_coeff, int seq_len, float* dlogits,
+                               float* losses, void* ws, hipStream_t st);
+hipError_t launch_bias_update(const int32_t* counts, int T, int E, int k, float rate, float* bias,
+                              hipStream_t st);
+
 // ---- combine and backward helpers
 hipError_t launch_combine(int dtype, const void* y_perm, const float* gate, const int32_t* pos,
                           const void* shared_y, void* y, int T, int d, int k, hipStream_t st);

@@ -28,7 +28,7 @@ def upload_layer(cfg, inp):
     return w
 
 
-def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False):
+def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False, terms=None):
     desc = M.desc_from_config(cfg)
     w = upload_layer(cfg, inp) if weights is None else weights
     x = dev(inp["x"]) if x is None else x
@@ -42,8 +42,9 @@ def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False
         grads = M.alloc_grads(desc)
         dx = torch.empty_like(x)
         wsb = M.alloc_workspace(desc, "backward")
-        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb)
-        out.update(dx=dx, grads=grads)
+        losses = torch.zeros(4, dtype=torch.float32, device="cuda") if terms is not None else None
+        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, terms=terms, losses=losses)
+        out.update(dx=dx, grads=grads, losses=losses)
     torch.cuda.synchronize()
     if keep_device:
         return out
@@ -52,6 +53,8 @@ def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False
                offsets=saved["offsets"].cpu().numpy())
     if backward:
         res["dx"] = host(out["dx"])
+        if out["losses"] is not None:
+            res["losses"] = out["losses"][:3].cpu().numpy()
         for n, t in out["grads"].items():
             if t is not None:
                 res[n] = host(t)
@@ -68,7 +71,7 @@ def oracle_inputs(cfg, inp):
                 dy=f(inp.get("dy")) if inp.get("dy") is not None else None)
 
 
-def oracle_run(cfg, oi, backward, tokens=None):
+def oracle_run(cfg, oi, backward, tokens=None, terms=None):
     x = oi["x"] if tokens is None else oi["x"][tokens]
     fw = O.forward(x, oi["w_router"], oi["bias"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"],
                    top_k=cfg.k, score=cfg.score, renorm=cfg.renorm)
@@ -76,7 +79,7 @@ def oracle_run(cfg, oi, backward, tokens=None):
     if backward:
         dy = oi["dy"] if tokens is None else oi["dy"][tokens]
         bw = O.backward(x, oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fw, dy,
-                        score=cfg.score, renorm=cfg.renorm)
+                        score=cfg.score, renorm=cfg.renorm, terms=terms)
     return fw, bw
 
 

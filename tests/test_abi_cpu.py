@@ -21,7 +21,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -91,8 +91,8 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert lib.moe_forward(ctypes.byref(d), None, a, a, ctypes.byref(s), a, 1 << 30, None) == L.MOE_ERR_INVALID
     g = L.MoeGrads(a, a, a, None, None)
     s.preact = None
-    assert lib.moe_backward(ctypes.byref(d), ctypes.byref(w), a, ctypes.byref(s), a, a, ctypes.byref(g), a,
-                            1 << 30, None) == L.MOE_ERR_INVALID
+    assert lib.moe_backward(ctypes.byref(d), ctypes.byref(w), a, ctypes.byref(s), a, a, ctypes.byref(g), None,
+                            None, a, 1 << 30, None) == L.MOE_ERR_INVALID
     # shared experts declared but no shared weights
     d2 = make_desc(64, 128, 8, 2, 256, 1, 128, "sigmoid", True, "bf16")
     s2 = L.MoeSaved(*([a] * 13))
@@ -136,3 +136,32 @@ def test_stage_timing_without_records(lib):
     assert list(ms) == [0.0] * L.MOE_NUM_STAGES and list(n) == [0] * L.MOE_NUM_STAGES
     assert lib.moe_stage_times(None, n) == L.MOE_ERR_INVALID
     assert lib.moe_stage_timing(0) == L.MOE_OK
+
+
+def test_router_terms_and_bias_update_argument_checks(lib):
+    """Host-side rejection of bad router-term arguments (no launch happens)."""
+    d = make_desc(64, 128, 8, 2, 256, 0, 0, "sigmoid", True, "bf16")
+    a = ctypes.c_void_p(1 << 20)
+    w = L.MoeWeights(a, a, a, a, None, None)
+    s = L.MoeSaved(*([a] * 11 + [None, None]))
+    g = L.MoeGrads(a, a, a, None, None)
+    big = 1 << 34
+
+    def bwd(terms, losses=None):
+        return lib.moe_backward(ctypes.byref(d), ctypes.byref(w), a, ctypes.byref(s), a, a, ctypes.byref(g),
+                                None if terms is None else ctypes.byref(terms), losses, a, big, None)
+
+    # losses without terms, a negative or NaN coefficient, a sequence length not dividing T
+    assert bwd(None, a) == L.MOE_ERR_INVALID
+    assert bwd(L.MoeRouterTerms(-1e-3, 0.0, 0.0, 0)) == L.MOE_ERR_INVALID
+    assert bwd(L.MoeRouterTerms(float("nan"), 0.0, 0.0, 0)) == L.MOE_ERR_INVALID
+    assert bwd(L.MoeRouterTerms(0.0, 1e-3, 0.0, 48)) == L.MOE_ERR_INVALID
+    assert bwd(L.MoeRouterTerms(0.0, 1e-3, 0.0, -1)) == L.MOE_ERR_INVALID
+    assert bwd(L.MoeRouterTerms(1e-3, 0.0, 0.0, 0), ctypes.c_void_p((1 << 20) + 4)) == L.MOE_ERR_ALIGN
+    # bias update: NaN rate, null pointers, misaligned counts
+    assert lib.moe_bias_update(ctypes.byref(d), a, float("nan"), a, None) == L.MOE_ERR_INVALID
+    assert lib.moe_bias_update(ctypes.byref(d), None, 0.01, a, None) == L.MOE_ERR_INVALID
+    assert lib.moe_bias_update(ctypes.byref(d), ctypes.c_void_p((1 << 20) + 4), 0.01, a, None) == L.MOE_ERR_ALIGN
+    # zero tokens: nothing to do
+    d0 = make_desc(0, 128, 8, 2, 256, 0, 0, "sigmoid", True, "bf16")
+    assert lib.moe_bias_update(ctypes.byref(d0), None, 0.01, None, None) == L.MOE_OK
