@@ -498,3 +498,70 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
 def expert_parameter_count(d_model, d_ff):
     """Weights in one SwiGLU expert without bias: three d_model x d_ff matrices."""
     return 3 * int(d_model) * int(d_ff)
+
+
+# ----------------------------------------------------------------------------- fp8 (e4m3) experts
+# Apex-3 code page ("What's inside": FP8 through torchao; "Run it yourself":
+# --precision fp8_rowwise); KempnerForge README ("MoE roadmap": FP8 mixed
+# precision).  Format: OCP e4m3 -- 1 sign, 4 exponent (bias 7), 3 mantissa
+# bits; exponent 0 holds the subnormals m/8 * 2^-6; 0x7f / 0xff are NaN; the
+# largest finite value is 448 (no infinities).
+
+def e4m3_decode(codes):
+    """Value of each e4m3 code (uint8 array) as fp64."""
+    c = np.asarray(codes, np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 15
+    m = c & 7
+    val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(F64) - 7.0))
+    val = np.where((e == 15) & (m == 7), np.nan, val)
+    return sign * val
+
+
+def _e4m3_table():
+    codes = np.arange(128, dtype=np.uint8)
+    v = e4m3_decode(codes)
+    ok = ~np.isnan(v)
+    return v[ok], codes[ok]
+
+
+def e4m3_encode(x):
+    """Round fp64/fp32 values to the nearest e4m3 value, ties to the even code
+    (the one with mantissa bit 0), values beyond +-448 clamped to +-448."""
+    vals, codes = _e4m3_table()            # ascending 0 .. 448
+    a = np.minimum(np.abs(np.asarray(x, F64)), 448.0)
+    hi = np.searchsorted(vals, a, side="left")      # first value >= a
+    hi = np.minimum(hi, len(vals) - 1)
+    lo = np.maximum(hi - 1, 0)
+    exact = vals[hi] == a
+    dlo = a - vals[lo]
+    dhi = vals[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (codes[hi] % 2 == 0))
+    c = np.where(exact | pick_hi, codes[hi], codes[lo])
+    neg = np.signbit(np.asarray(x, F64))
+    return (c | np.where(neg, 0x80, 0)).astype(np.uint8)
+
+
+def quantize_rowwise(x):
+    """Row-wise scaling: s_r = amax_r / 448 (fp32; 1 for an all-zero row),
+    q = e4m3(x / s_r) with the division in fp32.  Returns (codes uint8, s fp32)."""
+    x32 = np.asarray(x, F32)
+    amax = np.abs(x32).max(axis=1)
+    s = np.where(amax > 0, (amax / np.float32(448.0)).astype(F32), np.float32(1.0)).astype(F32)
+    q = e4m3_encode((x32 / s[:, None]).astype(F32))
+    return q, s
+
+
+def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets):
+    """C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k] over the
+    decoded codes, for the rows m of group g; fp64."""
+    A = e4m3_decode(a_codes)
+    B = e4m3_decode(b_codes)
+    G, N, _ = B.shape
+    C = np.zeros((A.shape[0], N))
+    for g in range(G):
+        r0, r1 = int(offsets[g]), int(offsets[g + 1])
+        if r1 > r0:
+            C[r0:r1] = (A[r0:r1] @ B[g].T) * np.asarray(a_scale, F64)[r0:r1, None] * \
+                np.asarray(b_scale, F64)[g][None, :]
+    return C

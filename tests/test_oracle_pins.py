@@ -417,3 +417,80 @@ def test_bias_update_moves_toward_balance():
     want = b.astype(F64) + F64(np.float32(rate)) * (mean - counts) / mean
     assert np.max(np.abs(nb - want)) <= 2.0 ** -24 * np.max(np.abs(want))
     assert nb[0] < b[0] and nb[-1] > b[-1] and abs(nb[1] - b[1]) <= 2.0 ** -24
+
+
+# --------------------------------------------------------------------------- fp8 (e4m3)
+def test_e4m3_decode_table_against_the_format():
+    """Every code against the format written out by hand: the named values of
+    the OCP e4m3 definition."""
+    v = O.e4m3_decode(np.arange(256, dtype=np.uint8))
+    assert v[0x00] == 0.0 and v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert v[0x01] == 2.0 ** -9                 # smallest subnormal
+    assert v[0x07] == 7 * 2.0 ** -9             # largest subnormal
+    assert v[0x08] == 2.0 ** -6                 # smallest normal
+    assert v[0x38] == 1.0 and v[0xb8] == -1.0
+    assert v[0x7e] == 448.0 and v[0xfe] == -448.0
+    assert np.isnan(v[0x7f]) and np.isnan(v[0xff])
+    finite = v[~np.isnan(v)]
+    assert len(finite) == 254 and len(np.unique(finite)) == 253     # +0 and -0 compare equal
+
+
+def test_e4m3_encode_rounding():
+    vals = O.e4m3_decode(np.arange(0x7f, dtype=np.uint8))
+    # every finite value encodes to itself
+    assert np.array_equal(O.e4m3_decode(O.e4m3_encode(vals)), vals)
+    # midpoints go to the even code; a hair either side goes to the nearest
+    lo, hi = vals[:-1], vals[1:]
+    mid = (lo + hi) / 2
+    enc = O.e4m3_encode(mid)
+    codes_lo = np.arange(0x7e, dtype=np.uint8)
+    want = np.where(codes_lo % 2 == 0, codes_lo, codes_lo + 1)
+    assert np.array_equal(enc, want)
+    assert np.array_equal(O.e4m3_encode(np.nextafter(mid, 0)), codes_lo)
+    assert np.array_equal(O.e4m3_encode(np.nextafter(mid, np.inf)), codes_lo + 1)
+    # clamping and sign
+    assert O.e4m3_encode([1000.0])[0] == 0x7e and O.e4m3_encode([-1000.0])[0] == 0xfe
+    assert O.e4m3_encode([-1.0])[0] == 0xb8
+
+
+def test_fp8_rowwise_gemm_factorises():
+    """The scaled product equals the product of the dequantised operands, and
+    quantisation error per element is at most half a step of e4m3 (relative
+    2^-4 of the value, or 2^-10 of the row scale in the subnormal range)."""
+    g = np.random.default_rng(31)
+    x = g.standard_normal((40, 64)).astype(np.float32)
+    w = (g.standard_normal((3, 24, 64)) / 8).astype(np.float32)
+    qx, sx = O.quantize_rowwise(x)
+    qw, sw = O.quantize_rowwise(w.reshape(-1, 64))
+    qw = qw.reshape(3, 24, 64)
+    sw = sw.reshape(3, 24)
+    off = np.array([0, 10, 10, 40])
+    C = O.grouped_gemm_fp8_nt(qx, sx, qw, sw, off)
+    xd = O.e4m3_decode(qx) * sx[:, None]
+    wd = O.e4m3_decode(qw) * sw[:, :, None]
+    ref = np.zeros_like(C)
+    ref[0:10] = xd[0:10] @ wd[0].T
+    ref[10:40] = xd[10:40] @ wd[2].T
+    assert np.max(np.abs(C - ref)) <= 1e-12 * np.max(np.abs(ref))
+    assert np.all(C[0:10].shape == (10, 24))
+    err = np.abs(xd - x.astype(np.float64))
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, sx[:, None].astype(np.float64) * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-12))
+    # the row maximum maps to 448 exactly
+    assert np.all(np.max(np.abs(O.e4m3_decode(qx)), axis=1) == 448.0)
+
+
+def test_e4m3_encode_matches_brute_force_nearest():
+    """Random values against a nearest-value search over all finite codes
+    written independently (ties to the even code)."""
+    g = np.random.default_rng(32)
+    x = np.concatenate([g.standard_normal(3000) * 40, g.standard_normal(1000) * 0.01])
+    codes = np.arange(0x7f, dtype=np.uint8)
+    table = O.e4m3_decode(codes)
+    for v in x:
+        a = min(abs(v), 448.0)
+        d = np.abs(table - a)
+        best = np.where(d == d.min())[0]
+        c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        want = c | (0x80 if v < 0 else 0)
+        assert O.e4m3_encode([v])[0] == want, v
