@@ -23,6 +23,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE layer fwd+bwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_FP8_TFLOPS = 5000.0
 
 
 def parse():
@@ -32,6 +33,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="moe7b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the fp8 gate/up measurement")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="token sample for the oracle timing")
     p.add_argument("--router-terms", action="store_true",
                    help="add the router training terms to every step: balance loss 1e-3, per-sequence balance "
@@ -49,7 +51,7 @@ def parse():
 # ---- HBM traffic of the dominant kernel, from two rocprofv3 --pmc passes
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_moe7b_bf16_traffic.txt")
-GATE_UP_KERNEL = "pk::gemm_kernel<0, 1>"
+GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false>"
 KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_big.hip",
                   "mixture_experts_layer_18_amd/csrc/gemm_common.h",
                   "mixture_experts_layer_18_amd/csrc/common.h",
@@ -163,6 +165,32 @@ def cpu_baseline(cfg, inp, ntok):
     return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"first {ntok} of {cfg.T} tokens of {cfg.name}, fp64 numpy forward+backward, "
                       f"{dt:.1f} s wall, BLAS threads = all {cores} host cores"}
+
+
+def fp8_gate_up(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
+    """The forward gate/up product in fp8 (e4m3, row-wise scales) on the same
+    permuted tokens and routing: the activation quantisation and the scaled
+    fp8 grouped GEMM with the SwiGLU epilogue, each timed on its own with
+    events (outside the layer step, which stays bf16)."""
+    import torch
+    A, d, E, f = cfg.T * cfg.k, cfg.d, cfg.E, cfg.f
+    xq = torch.empty(A, d, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(A, dtype=torch.float32, device="cuda")
+    wq = torch.empty(E * 2 * f, d, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(E * 2 * f, dtype=torch.float32, device="cuda")
+    h = torch.empty(A, f, dtype=torch.bfloat16, device="cuda")
+    aux = torch.empty(A, 2 * f, dtype=torch.bfloat16, device="cuda")
+    M.moe_quantize_fp8(w["w_gateup"].reshape(E * 2 * f, d), wq, ws, stream)
+    t_q = timed_ms(lambda: M.moe_quantize_fp8(saved["x_perm"], xq, xs, stream), 20) * 1e-3
+    t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("swiglu", E, A, 2 * f, d, saved["offsets"], xq, xs, wq, ws,
+                                                  h, aux, stream), 20) * 1e-3
+    tf = flop / t_g / 1e12
+    q_bytes = A * (2 * d + d + 4)   # bf16 rows in; codes and scales out
+    return {"gemm_us": t_g * 1e6, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS, "peak": PEAK_FP8_TFLOPS,
+            "quantize_us": t_q * 1e6, "quantize_gbs": q_bytes / t_q / 1e9,
+            "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
+            "what": "e4m3 row-wise scaled grouped GEMM + SwiGLU on the forward gate/up shape; "
+                    "activation quantisation timed separately, weights quantised once"}
 
 
 def main():
@@ -317,6 +345,7 @@ def main():
     t_copy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
     del cbuf, cdst
+    fp8 = fp8_gate_up(M, cfg, saved, w, stream, timed_ms, fl_gu, t_gu) if not args.no_fp8 else None
     hbm3 = ["route", "permute", "combine"]
     hbm3_us = sum(stage_out[n]["us"] for n in hbm3)
     hbm3_gbs = sum(hbm_bytes[n] for n in hbm3) / (hbm3_us * 1e-6) / 1e9
@@ -358,6 +387,7 @@ def main():
         "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                              "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
         "stages": stage_out,
+        "fp8_gate_up": fp8,
         "loads": {"max_over_mean": float(counts.max() / counts.mean()), "empty": int((counts == 0).sum())},
     }
     if not args.no_cpu_baseline:

@@ -275,6 +275,32 @@ int moe_backward(const moe_desc_t *desc, const moe_weights_t *w, const void *x,
 int moe_bias_update(const moe_desc_t *desc, const int32_t *counts, float rate, float *bias,
                     void *stream);
 
+/* ---------------------------------------------------------------- fp8 experts */
+
+/* Row-wise fp8 quantisation (Apex-3 code page: FP8 through torchao,
+ * --precision fp8_rowwise).  For each row r of x [rows, cols] (dtype bf16 or
+ * fp32): s_r = amax_r / 448 in fp32 (1 for an all-zero row), and
+ * q[r, c] = e4m3(x[r, c] / s_r), the quotient in fp32, clamped to +-448 and
+ * rounded to nearest even onto the OCP e4m3 grid.
+ *   q [rows, cols] uint8 codes (out), scale [rows] fp32 (out)
+ * cols a multiple of 64; pointers 16-byte aligned. */
+int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void *x, uint8_t *q, float *scale,
+                     void *stream);
+
+/* fp8 grouped GEMM, forward (NT) layout, with row scales:
+ *   C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k]
+ * for the rows m of group g (group_offsets as in moe_grouped_gemm), fp32
+ * accumulation of the exact e4m3 products, rounded once to bf16.
+ *   A [M_total, K], B [G, N, K] uint8 e4m3 codes; a_scale [M_total],
+ *   b_scale [G, N] fp32; C [M_total, N] bf16 (MOE_EPI_NONE) or, with
+ *   MOE_EPI_SWIGLU, C [M_total, N/2] = silu(gate) * up of the scaled
+ *   products and aux [M_total, N] bf16 the scaled pre-activations (or NULL).
+ * K a multiple of 64, N a multiple of 64 (SwiGLU: N/2 a multiple of 128),
+ * 1 <= G <= 256; pointers 16-byte aligned. */
+int moe_grouped_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
+                         const int32_t *group_offsets, const uint8_t *A, const float *a_scale,
+                         const uint8_t *B, const float *b_scale, void *C, void *aux, void *stream);
+
 /* ---------------------------------------------------------------- timing */
 
 /* Stages of moe_forward / moe_backward, for the per-stage timing below. */

@@ -70,6 +70,9 @@ SIGNATURES = {
     "moe_backward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, _P(MoeSaved), c_vp, c_vp, _P(MoeGrads),
                              _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
     "moe_bias_update": (c_i32, [_P(MoeDesc), c_vp, ctypes.c_float, c_vp, c_vp]),
+    "moe_quantize_fp8": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "moe_grouped_gemm_fp8": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_vp, c_vp]),
     "moe_stage_timing": (c_i32, [c_i32]),
     "moe_stage_times": (c_i32, [_P(ctypes.c_double), _P(c_i64)]),
 }

@@ -139,6 +139,20 @@ def moe_bias_update(desc, counts, rate, bias, stream=None):
            "moe_bias_update")
 
 
+def moe_quantize_fp8(x, q, scale, stream=None):
+    """Row-wise e4m3 quantisation of x [rows, cols] (bf16 or fp32) into q (uint8) and scale (fp32)."""
+    dt = L.MOE_BF16 if x.dtype == torch.bfloat16 else L.MOE_F32
+    rows, cols = x.shape[0], x.numel() // max(x.shape[0], 1)
+    _check(L.load().moe_quantize_fp8(rows, cols, dt, _p(x), _p(q), _p(scale), _stream(stream)), "moe_quantize_fp8")
+
+
+def moe_grouped_gemm_fp8(epilogue, G, M_total, N, K, group_offsets, A, a_scale, B, b_scale, C, aux=None,
+                         stream=None):
+    _check(L.load().moe_grouped_gemm_fp8(EPILOGUES[epilogue], G, M_total, N, K, _p(group_offsets), _p(A),
+                                         _p(a_scale), _p(B), _p(b_scale), _p(C), _p(aux), _stream(stream)),
+           "moe_grouped_gemm_fp8")
+
+
 # ------------------------------------------------------------------ buffers (torch device memory)
 def alloc_saved(desc, device="cuda", training=True) -> dict:
     T, d, E, k, f = desc.num_tokens, desc.d_model, desc.num_experts, desc.top_k, desc.d_ff

@@ -473,6 +473,34 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   return MOE_OK;
 }
 
+int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void* x, uint8_t* q, float* scale,
+                     void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 64 || cols > (int64_t(1) << 24)) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scale) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return MOE_ERR_ALIGN;
+  MOE_TRY(launch_quantize_fp8(x, dtype, rows, (int)cols, q, scale, (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
+                         const int32_t* offsets, const uint8_t* A, const float* a_scale,
+                         const uint8_t* B, const float* b_scale, void* C, void* aux, void* stream) {
+  if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU) return MOE_ERR_INVALID;
+  if (G < 1 || G > 256 || M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64) return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_SWIGLU && (N / 2) % 128) return MOE_ERR_INVALID;
+  if (M >= (int64_t(1) << 31) || N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (!offsets) return MOE_ERR_INVALID;
+  if (M > 0 && (!A || !a_scale || !B || !b_scale || !C)) return MOE_ERR_INVALID;
+  const void* ptrs[] = {offsets, A, a_scale, B, b_scale, C, aux};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(launch_gemm_fp8(epi, G, M, N, K, offsets, A, a_scale, B, b_scale, C, aux, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_bias_update(const moe_desc_t* d, const int32_t* counts, float rate, float* bias,
                     void* stream) {
   int s = check_desc(d);

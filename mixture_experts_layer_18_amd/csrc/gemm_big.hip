@@ -56,6 +56,8 @@ struct Args {
   const bf16_t* B;
   bf16_t* C;
   bf16_t* aux;
+  const float* a_scale;  // fp8: per-row scales of A [M_total]
+  const float* b_scale;  // fp8: per-row scales of B [G, N]
 };
 
 struct Tile {
@@ -65,10 +67,16 @@ struct Tile {
   int64_t r_lo, r_hi;  // reduction range (TN: the group's rows; else [0, K or N))
 };
 
-template <int LAYOUT, int EPI>
+// F8: A and B hold OCP e4m3 codes (one byte each) with row scales; a k-step
+// then covers 64 elements (still 64 bytes per LDS row) and one
+// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) per 32x32 tile.
+template <int LAYOUT, int EPI, bool F8>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
   constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
+  static_assert(!F8 || LAYOUT == MOE_GEMM_NT, "fp8 operands: forward layout only");
+  constexpr int ES = F8 ? 1 : 2;         // bytes per operand element
+  constexpr int BKE = BK * 2 / ES;       // elements per k-step (64 bytes per row)
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB + PAD_BYTES];
   __shared__ int s_pref[256];
   __shared__ int scratch[4];
@@ -159,12 +167,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
       // [256 rows][32]: 16 rows of 64 bytes per instruction
       const int row = (i * NW + wave) * 16 + (ln >> 2);
       const int chunk = (ln & 3) ^ ((row >> 2) & 3);
-      const uint32_t kb = (uint32_t)(kt * BK * 2) + chunk * 16;
+      const uint32_t kb = (uint32_t)(kt * BK * 2) + chunk * 16;  // 64 bytes per row per k-step
       if (isP) {
         const int nrows = (int)(t.i_hi - t.i_lo);
         const int r = row < nrows ? row : nrows - 1;
         const int64_t ld = (LAYOUT == MOE_GEMM_NT) ? K : N;
-        dma16_off(Ab + t.i_lo * ld * 2, (uint32_t)r * (uint32_t)(ld * 2) + kb, dst);
+        dma16_off(Ab + t.i_lo * ld * ES, (uint32_t)r * (uint32_t)(ld * ES) + kb, dst);
       } else {  // NT's B rows
         uint32_t roff;
         if (EPI == MOE_EPI_SWIGLU) {
@@ -175,7 +183,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
           const int nr = (int)(N - t.j0);
           roff = row < nr ? row : nr - 1;
         }
-        dma16_off(Bb + ((int64_t)t.g * N + t.j0) * K * 2, roff * (uint32_t)(K * 2) + kb, dst);
+        dma16_off(Bb + ((int64_t)t.g * N + t.j0) * K * ES, roff * (uint32_t)(K * ES) + kb, dst);
       }
     } else {
       // [32][256]: 2 k-rows of 512 bytes per instruction
@@ -237,7 +245,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   int L = xcd * per + slot;
   if (L >= total) return;
   Tile t = tile_of(L);
-  int64_t nk = (t.r_hi - t.r_lo + BK - 1) / BK;
+  int64_t nk = (t.r_hi - t.r_lo + BKE - 1) / BKE;
   {
     const int ln = opaque_i(lane);
 #pragma unroll
@@ -256,48 +264,104 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
       for (int jt = 0; jt < FJ; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
-    bf16x8_t pa0[FI], qb0[FJ], pa1[FI], qb1[FJ];
+    if constexpr (F8) {
+      // both 32-byte halves of a lane's row fragment feed one MFMA: the
+      // fragments of stage kt are complete before the step starts; the
+      // first two row blocks' MFMAs run, the barrier, then the next
+      // stage's fragments are requested while the other two row blocks'
+      // MFMAs run interleaved with the DMA issue
+      typedef int v4i_t __attribute__((ext_vector_type(4)));
+      typedef int v8i_t __attribute__((ext_vector_type(8)));
+      auto frag8 = [&](const char* st, int row) __attribute__((always_inline)) {
+        const v4i_t lo = __builtin_bit_cast(v4i_t, frag_kc<BK>(st, row, 0, lane));
+        const v4i_t hi = __builtin_bit_cast(v4i_t, frag_kc<BK>(st, row, 1, lane));
+        return (v8i_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      v8i_t P[FI], Q[FJ];
 #pragma unroll
-    for (int it = 0; it < FI; ++it) pa0[it] = frag_p(smem, it, 0);
+      for (int it = 0; it < FI; ++it) P[it] = frag8(smem, wp * WM + it * 32);
 #pragma unroll
-    for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(smem, jt, 0);
-    const int ln = opaque_i(lane);
-    for (int64_t kt = 0; kt < nk; ++kt) {
-      const char* sP = smem + (kt % STAGES) * SB;
+      for (int jt = 0; jt < FJ; ++jt) Q[jt] = frag8(smem + PB, wq * WN + jt * 32);
+      const int ln = opaque_i(lane);
+      for (int64_t kt = 0; kt < nk; ++kt) {
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int it = 0; it < FI; ++it) pa1[it] = frag_p(sP, it, 1);
+        for (int it = 0; it < FI / 2; ++it)
 #pragma unroll
-      for (int jt = 0; jt < FJ; ++jt) qb1[jt] = frag_q(sP, jt, 1);
-      __builtin_amdgcn_sched_barrier(0);
+          for (int jt = 0; jt < FJ; ++jt)
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
+                                                                          0x7f7f7f7f, 0, 0x7f7f7f7f);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<2 * LT>();
+        lds_barrier();
+        const char* nP = smem + ((kt + 1) % STAGES) * SB;
+        v8i_t Pn[FI], Qn[FJ];
 #pragma unroll
-      for (int it = 0; it < FI; ++it)
+        for (int it = 0; it < FI; ++it) Pn[it] = frag8(nP, wp * WM + it * 32);
 #pragma unroll
-        for (int jt = 0; jt < FJ; ++jt)
-          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb0[jt], pa0[it], acc[it][jt], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      // k-step kt+1 landed for this wave (kt+2, kt+3 may be in flight); after
-      // the barrier every wave has it and is done reading k-step kt
-      wait_vmcnt<2 * LT>();
-      if (kt + 1 < nk) zero_tail(t, kt + 1);
-      lds_barrier();
-      const char* nP = smem + ((kt + 1) % STAGES) * SB;
+        for (int jt = 0; jt < FJ; ++jt) Qn[jt] = frag8(nP + PB, wq * WN + jt * 32);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool real = kt + STAGES < nk;
+        static_assert((FI / 2) * FJ == LT, "one MFMA per DMA slot");
 #pragma unroll
-      for (int it = 0; it < FI; ++it) pa0[it] = frag_p(nP, it, 0);
-#pragma unroll
-      for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(nP, jt, 0);
-      __builtin_amdgcn_sched_barrier(0);
-      const bool real = kt + STAGES < nk;
-#pragma unroll
-      for (int q = 0; q < LT; ++q) {
-#pragma unroll
-        for (int u = 0; u < (FI * FJ) / LT; ++u) {
-          const int m = q * ((FI * FJ) / LT) + u, it = m / FJ, jt = m % FJ;
-          acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb1[jt], pa1[it], acc[it][jt], 0, 0, 0);
+        for (int q = 0; q < LT; ++q) {
+          const int it = FI / 2 + q / FJ, jt = q % FJ;
+          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
+                                                                        0x7f7f7f7f, 0, 0x7f7f7f7f);
+          __builtin_amdgcn_sched_barrier(0);
+          if (real) issue(t, kt + STAGES, q, ln);
+          else dma4_pad(Ab, pad_lds + q * 256);
+          __builtin_amdgcn_sched_barrier(0);
         }
+#pragma unroll
+        for (int it = 0; it < FI; ++it) P[it] = Pn[it];
+#pragma unroll
+        for (int jt = 0; jt < FJ; ++jt) Q[jt] = Qn[jt];
+      }
+    } else {
+    bf16x8_t pa0[FI], qb0[FJ], pa1[FI], qb1[FJ];
+  #pragma unroll
+      for (int it = 0; it < FI; ++it) pa0[it] = frag_p(smem, it, 0);
+  #pragma unroll
+      for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(smem, jt, 0);
+      const int ln = opaque_i(lane);
+      for (int64_t kt = 0; kt < nk; ++kt) {
+        const char* sP = smem + (kt % STAGES) * SB;
+  #pragma unroll
+        for (int it = 0; it < FI; ++it) pa1[it] = frag_p(sP, it, 1);
+  #pragma unroll
+        for (int jt = 0; jt < FJ; ++jt) qb1[jt] = frag_q(sP, jt, 1);
         __builtin_amdgcn_sched_barrier(0);
-        if (real) issue(t, kt + STAGES, q, ln);
-        else dma4_pad(Ab, pad_lds + q * 256);
+  #pragma unroll
+        for (int it = 0; it < FI; ++it)
+  #pragma unroll
+          for (int jt = 0; jt < FJ; ++jt)
+            acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb0[jt], pa0[it], acc[it][jt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        // k-step kt+1 landed for this wave (kt+2, kt+3 may be in flight); after
+        // the barrier every wave has it and is done reading k-step kt
+        wait_vmcnt<2 * LT>();
+        if (kt + 1 < nk) zero_tail(t, kt + 1);
+        lds_barrier();
+        const char* nP = smem + ((kt + 1) % STAGES) * SB;
+  #pragma unroll
+        for (int it = 0; it < FI; ++it) pa0[it] = frag_p(nP, it, 0);
+  #pragma unroll
+        for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(nP, jt, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        const bool real = kt + STAGES < nk;
+  #pragma unroll
+        for (int q = 0; q < LT; ++q) {
+  #pragma unroll
+          for (int u = 0; u < (FI * FJ) / LT; ++u) {
+            const int m = q * ((FI * FJ) / LT) + u, it = m / FJ, jt = m % FJ;
+            acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb1[jt], pa1[it], acc[it][jt], 0, 0, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          if (real) issue(t, kt + STAGES, q, ln);
+          else dma4_pad(Ab, pad_lds + q * 256);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     // every wave is done with this tile's LDS stages: fetch the next tile's
@@ -310,7 +374,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     auto prefetch_next = [&]() __attribute__((always_inline)) {
       if (more) {
         tn = tile_of(Ln);
-        nk_n = (tn.r_hi - tn.r_lo + BK - 1) / BK;
+        nk_n = (tn.r_hi - tn.r_lo + BKE - 1) / BKE;
         const int lp = opaque_i(lane);
 #pragma unroll
         for (int s = 0; s < STAGES; ++s) stage_dma(tn, s, nk_n, lp);
@@ -321,11 +385,22 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     bf16_t* C = a.C;
     bf16_t* X = a.aux;
     prefetch_next();
+    // fp8: the row scale of this lane's output row per row block, and the
+    // column scales of the 16 columns a lane holds in a 32-wide block
+    auto col_scales = [&](int64_t brow, float* sc) __attribute__((always_inline)) {
+      const float* p = a.b_scale + (int64_t)t.g * N + brow + kh * 4;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const float4 v = *reinterpret_cast<const float4*>(p + gq * 8);
+        sc[gq * 4] = v.x; sc[gq * 4 + 1] = v.y; sc[gq * 4 + 2] = v.z; sc[gq * 4 + 3] = v.w;
+      }
+    };
 #pragma unroll
     for (int it = 0; it < FI; ++it) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
       if (i >= t.i_hi) continue;
+      const float sa = F8 ? a.a_scale[i] : 1.0f;
       if (EPI == MOE_EPI_SWIGLU) {
         // block jt holds gate columns for even jt, up columns for odd jt
         if (X) {
@@ -335,6 +410,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
             float v[16];
 #pragma unroll
             for (int u = 0; u < 16; ++u) v[u] = opaque(acc[it][jt][u]);
+            if constexpr (F8) {
+              float sc[16];
+              col_scales(c, sc);
+#pragma unroll
+              for (int u = 0; u < 16; ++u) v[u] = v[u] * sa * sc[u];
+            }
             store_tile_row(X + i * N + c, v, kh, 32);
           }
         }
@@ -342,9 +423,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
         for (int jt = 0; jt < FJ / 2; ++jt) {
           const int64_t c = t.j0 + wq * (WN / 2) + jt * 32;
           float h[16];
+          if constexpr (F8) {
+            float sg[16], su[16];
+            col_scales(c, sg);
+            col_scales(F + c, su);
 #pragma unroll
-          for (int u = 0; u < 16; ++u)
-            h[u] = silu_f(opaque(acc[it][2 * jt][u])) * opaque(acc[it][2 * jt + 1][u]);
+            for (int u = 0; u < 16; ++u)
+              h[u] = silu_f(opaque(acc[it][2 * jt][u]) * sa * sg[u]) * (opaque(acc[it][2 * jt + 1][u]) * sa * su[u]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+              h[u] = silu_f(opaque(acc[it][2 * jt][u])) * opaque(acc[it][2 * jt + 1][u]);
+          }
           store_tile_row(C + i * F + c, h, kh, 32);
         }
       } else {
@@ -352,8 +442,15 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
         for (int jt = 0; jt < FJ; ++jt) {
           const int64_t c = t.j0 + wq * WN + jt * 32;
           float v[16];
+          if constexpr (F8) {
+            float sc[16];
+            col_scales(c, sc);
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
+            for (int u = 0; u < 16; ++u) v[u] = agpr_read(acc[it][jt][u]) * sa * sc[u];
+          } else {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
+          }
           bf16_t* row = (LAYOUT == MOE_GEMM_TN) ? C + ((int64_t)t.g * N + i) * K : C + i * ncols;
           store_tile_row(row + c, v, kh, ncols - c);
         }
@@ -379,10 +476,10 @@ static int grid_size() {
   return n;
 }
 
-template <int LAYOUT, int EPI>
+template <int LAYOUT, int EPI, bool F8 = false>
 static hipError_t run(const Args& a, hipStream_t st) {
   if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI><<<dim3((unsigned)grid_size()), dim3(256), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, F8><<<dim3((unsigned)grid_size()), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -416,6 +513,7 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
   a.B = (const bf16_t*)p.B;
   a.C = (bf16_t*)p.C;
   a.aux = (bf16_t*)p.aux;
+  a.a_scale = a.b_scale = nullptr;
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE>(a, st);
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU>(a, st);
   if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NN, MOE_EPI_NONE>(a, st);
@@ -423,4 +521,27 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+}  // namespace moe
+
+namespace moe {
+// fp8 forward products: C (bf16) = a_scale[m] b_scale[g,n] sum_k A[m,k] B[g,n,k]
+hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
+                           const int32_t* offsets, const uint8_t* A, const float* a_scale,
+                           const uint8_t* B, const float* b_scale, void* C, void* aux, hipStream_t st) {
+  pk::Args a;
+  a.G = (int)G;
+  a.M_total = M_total;
+  a.N = N;
+  a.K = K;
+  a.offsets = offsets;
+  a.A = (const bf16_t*)A;
+  a.B = (const bf16_t*)B;
+  a.C = (bf16_t*)C;
+  a.aux = (bf16_t*)aux;
+  a.a_scale = a_scale;
+  a.b_scale = b_scale;
+  if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true>(a, st);
+  if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true>(a, st);
+  return hipErrorInvalidValue;
+}
 }  // namespace moe

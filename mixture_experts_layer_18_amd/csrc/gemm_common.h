@@ -125,6 +125,14 @@ MOE_DEV float opaque(float v) {
   asm volatile("" : "+v"(v));
   return v;
 }
+// An accumulator value read with an explicit v_accvgpr_read: the value must
+// stay in an AGPR until here, which keeps the allocator from moving all the
+// accumulators into VGPRs for an epilogue that scales them.
+MOE_DEV float agpr_read(float v) {
+  float o;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(o) : "a"(v));
+  return o;
+}
 MOE_DEV int opaque_i(int v) {
   asm volatile("" : "+v"(v));
   return v;

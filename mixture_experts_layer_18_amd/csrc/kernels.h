@@ -32,6 +32,12 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, void* ws, size_t ws_bytes,
 // persistent 256 x 256 kernel (gemm_big.hip) for the products it supports
 bool gemm_big_supported(const GemmProblem& p);
 hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st);
+// fp8 (e4m3) forward products with row scales, persistent kernel
+hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
+                           const int32_t* offsets, const uint8_t* A, const float* a_scale,
+                           const uint8_t* B, const float* b_scale, void* C, void* aux, hipStream_t st);
+hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,
+                               hipStream_t st);
 int gemm_mfma_tn_splits(const GemmProblem& p);
 size_t gemm_mfma_workspace_bytes(const GemmProblem& p);
 // out[i] = sum over p < nsplit of part[p * n + i], in order, rounded once to dtype

@@ -53,10 +53,12 @@ def assert_close(gpu, ref, dtype, what=""):
     return r
 
 
-def assert_rounded(gpu, ref, dtype, what=""):
+def assert_rounded(gpu, ref, dtype, what="", extra=0.0):
     """Outputs stored once in `dtype` after fp32 accumulation: each element
     may differ from the exact value by one rounding (half an ulp: 2^-8
-    relative for bf16, 2^-24 for fp32) plus fp32 accumulation noise."""
+    relative for bf16, 2^-24 for fp32) plus fp32 accumulation noise.
+    `extra` (scalar or per element) widens the bound by an error the value
+    inherits from its inputs before that rounding."""
     gpu = np.asarray(gpu, np.float64)
     ref = np.asarray(ref, np.float64)
     rms = np.sqrt(np.mean(ref * ref))
@@ -65,8 +67,12 @@ def assert_rounded(gpu, ref, dtype, what=""):
         assert r <= 1e-5, f"{what}: rel-L2 {r:.3e} > 1e-5"
         return r
     assert r <= 1e-2, f"{what}: rel-L2 {r:.3e} > 1e-2"
-    bound = 2.0 ** -8 * np.abs(ref) * (1 + 1e-3) + 1e-4 * rms
+    bound = 2.0 ** -8 * np.abs(ref) * (1 + 1e-3) + 1e-4 * rms + extra
     bad = np.abs(gpu - ref) > bound
+    if bad.any():
+        w = np.argsort(-(np.abs(gpu - ref) / bound).ravel())[:5]
+        print(f"{what}: worst gpu / ref / bound:",
+              [(float(gpu.ravel()[i]), float(ref.ravel()[i]), float(bound.ravel()[i])) for i in w], flush=True)
     assert not bad.any(), f"{what}: {bad.sum()} elements beyond one bf16 rounding"
     return r
 

@@ -165,3 +165,22 @@ def test_router_terms_and_bias_update_argument_checks(lib):
     # zero tokens: nothing to do
     d0 = make_desc(0, 128, 8, 2, 256, 0, 0, "sigmoid", True, "bf16")
     assert lib.moe_bias_update(ctypes.byref(d0), None, 0.01, None, None) == L.MOE_OK
+
+
+def test_fp8_argument_checks(lib):
+    a = ctypes.c_void_p(1 << 20)
+    # quantize: columns not a multiple of 64, bad dtype, misaligned, zero rows
+    assert lib.moe_quantize_fp8(10, 100, L.MOE_BF16, a, a, a, None) == L.MOE_ERR_INVALID
+    assert lib.moe_quantize_fp8(10, 128, 7, a, a, a, None) == L.MOE_ERR_INVALID
+    assert lib.moe_quantize_fp8(10, 128, L.MOE_BF16, ctypes.c_void_p((1 << 20) + 2), a, a, None) == L.MOE_ERR_ALIGN
+    assert lib.moe_quantize_fp8(0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    # gemm: layout limits
+    args = (a, a, a, a, a, a, None, None)
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_DSWIGLU, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 0, 100, 256, 128, *args) == L.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 100, 256, 96, *args) == L.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_SWIGLU, 4, 100, 384, 128, *args) == L.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 100, 256, 128, a, a, a, a, a,
+                                    ctypes.c_void_p((1 << 20) + 4), None, None) == L.MOE_ERR_ALIGN
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 0, 256, 128, a, None, None, None, None, None, None,
+                                    None) == L.MOE_OK
