@@ -34,6 +34,8 @@ def parse():
     p.add_argument("--config", default="moe7b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the fp8 gate/up measurement")
+    p.add_argument("--permuted-copy", action="store_true",
+                   help="materialise the permuted token rows (x_perm) instead of gathering them")
     p.add_argument("--cpu-tokens", type=int, default=16384, help="token sample for the oracle timing")
     p.add_argument("--router-terms", action="store_true",
                    help="add the router training terms to every step: balance loss 1e-3, per-sequence balance "
@@ -51,7 +53,8 @@ def parse():
 # ---- HBM traffic of the dominant kernel, from two rocprofv3 --pmc passes
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_moe7b_bf16_traffic.txt")
-GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false>"
+# the routed gate/up product: forward layout, SwiGLU, bf16, rows gathered
+GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false, true>"
 KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_big.hip",
                   "mixture_experts_layer_18_amd/csrc/gemm_common.h",
                   "mixture_experts_layer_18_amd/csrc/common.h",
@@ -167,7 +170,7 @@ def cpu_baseline(cfg, inp, ntok):
                       f"{dt:.1f} s wall, BLAS threads = all {cores} host cores"}
 
 
-def fp8_gate_up(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
+def fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, flop, bf16_s):
     """The forward gate/up product in fp8 (e4m3, row-wise scales) on the same
     permuted tokens and routing: the activation quantisation and the scaled
     fp8 grouped GEMM with the SwiGLU epilogue, each timed on its own with
@@ -181,7 +184,9 @@ def fp8_gate_up(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
     h = torch.empty(A, f, dtype=torch.bfloat16, device="cuda")
     aux = torch.empty(A, 2 * f, dtype=torch.bfloat16, device="cuda")
     M.moe_quantize_fp8(w["w_gateup"].reshape(E * 2 * f, d), wq, ws, stream)
-    t_q = timed_ms(lambda: M.moe_quantize_fp8(saved["x_perm"], xq, xs, stream), 20) * 1e-3
+    # the routed token rows (the fp8 product reads a permuted copy)
+    x_perm = saved["x_perm"] if saved["x_perm"] is not None else x[saved["tok"].long()].contiguous()
+    t_q = timed_ms(lambda: M.moe_quantize_fp8(x_perm, xq, xs, stream), 20) * 1e-3
     t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("swiglu", E, A, 2 * f, d, saved["offsets"], xq, xs, wq, ws,
                                                   h, aux, stream), 20) * 1e-3
     tf = flop / t_g / 1e12
@@ -230,7 +235,8 @@ def main():
     dy = dev(inp["dy"])
     y = torch.empty_like(x)
     dx = torch.empty_like(x)
-    saved = M.alloc_saved(desc)
+    gather = not args.permuted_copy
+    saved = M.alloc_saved(desc, gather=gather)
     grads = M.alloc_grads(desc)
     wsf = M.alloc_workspace(desc, "forward")
     wsb = M.alloc_workspace(desc, "backward")
@@ -252,9 +258,14 @@ def main():
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
-        M.moe_grouped_gemm("NT", "swiglu", cfg.dtype, cfg.E, cfg.T * cfg.k, 2 * cfg.f, cfg.d,
-                           saved["offsets"], saved["x_perm"], w["w_gateup"], saved["h"],
-                           saved["preact"], None, stream)
+        if gather:
+            M.moe_grouped_gemm_gather("NT", "swiglu", cfg.E, cfg.T * cfg.k, 2 * cfg.f, cfg.d, saved["offsets"],
+                                      x, w["w_gateup"], saved["h"], saved["tok"], cfg.T, saved["preact"],
+                                      stream)
+        else:
+            M.moe_grouped_gemm("NT", "swiglu", cfg.dtype, cfg.E, cfg.T * cfg.k, 2 * cfg.f, cfg.d,
+                               saved["offsets"], saved["x_perm"], w["w_gateup"], saved["h"],
+                               saved["preact"], None, stream)
         torch.cuda.synchronize()
         print("pmc probe done", flush=True)
         return
@@ -297,7 +308,8 @@ def main():
     sh = 2 * d if F else 0
     hbm_bytes = {
         "route": T * (4 * E + 8 * k),                                 # logits in; idx, gate out
-        "permute": T * (2 * d * (1 + k) + 8 * k),                     # x in, x_perm, pos, src out
+        # idx in; pos, src, tok out (and with a permuted copy: x in, x_perm out)
+        "permute": T * (16 * k + (0 if gather else 2 * d * (1 + k))),
         "combine": T * (2 * d * (k + 1) + 8 * k + sh),                # y_perm, gate, pos, shared in; y out
         "combine_bwd": T * (2 * d * (2 * k + 1) + 12 * k + 8 * E),    # dy, y_perm, gate, pos, idx, logits
                                                                       # in; dy_perm, dlogits out
@@ -333,8 +345,9 @@ def main():
     t_gu = stage_out["gate_up"]["us"] * 1e-6
     t_dn = stage_out["down"]["us"] * 1e-6
     fl_gu, fl_dn = flops["gate_up"], flops["down"]
-    # each operand byte once: x_perm and W_gateup read, preact and h written
-    algo_bytes = 2.0 * (A * d + E * 2 * f * d + A * 2 * f + A * f)
+    # each operand byte once: the token rows (x once when gathered, through
+    # the int32 token map; else x_perm) and W_gateup read, preact and h written
+    algo_bytes = 2.0 * ((T * d + 2 * A) if gather else A * d) + 2.0 * (E * 2 * f * d + A * 2 * f + A * f)
     ach = fl_gu / t_gu / 1e12
     tr = measured_traffic() if args.config == "moe7b_bf16" else None
     fwd_tflops = (fl_gu + fl_dn) / (t_gu + t_dn) / 1e12
@@ -345,7 +358,7 @@ def main():
     t_copy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
     del cbuf, cdst
-    fp8 = fp8_gate_up(M, cfg, saved, w, stream, timed_ms, fl_gu, t_gu) if not args.no_fp8 else None
+    fp8 = fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, fl_gu, t_gu) if not args.no_fp8 else None
     hbm3 = ["route", "permute", "combine"]
     hbm3_us = sum(stage_out[n]["us"] for n in hbm3)
     hbm3_gbs = sum(hbm_bytes[n] for n in hbm3) / (hbm3_us * 1e-6) / 1e9
@@ -369,6 +382,7 @@ def main():
                         f"{cfg.f_shared}",
             "tokens_per_step": T, "d_model": d, "experts": E, "top_k": k, "d_ff": f,
             "shared": f"{cfg.n_shared}x{cfg.f_shared}", "parallelism": "single GPU",
+            "token_rows": "gathered through the token map" if gather else "permuted copy (x_perm)",
             "router_terms": terms,
         },
         "roofline": {

@@ -52,7 +52,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 /* ---------------------------------------------------------------- status */
 enum {
@@ -113,7 +113,13 @@ typedef struct moe_saved {
   int32_t *offsets;  /* [E+1] exclusive prefix of counts                      */
   int32_t *pos;      /* [A] permuted row of assignment a = t*k + j            */
   int32_t *src;      /* [A] assignment held by permuted row p (inverse of pos) */
-  void *x_perm;      /* [A, d] token rows in expert-contiguous order          */
+  int32_t *tok;      /* [A] token of permuted row p (src[p] / k)              */
+  void *x_perm;      /* [A, d] token rows in expert-contiguous order, or NULL:
+                        then the routed gate/up products (forward and weight
+                        gradient) read the rows of x through tok, and no
+                        permuted copy is written (bf16 layers with d a multiple
+                        of 256, d_ff of 128 and T*d <= 2^31; else
+                        MOE_ERR_UNSUPPORTED)                                  */
   void *preact;      /* [A, 2f] gate|up pre-activations; may be NULL in an
                         inference-only forward (then backward is invalid)     */
   void *h;           /* [A, f] silu(G) * U                                    */
@@ -205,11 +211,13 @@ int moe_route(const moe_desc_t *desc, const float *logits, const float *bias, in
  *   pos     [T*k] (out): row of assignment a = t*k + j; rows of one expert
  *           are ordered by increasing a (stable)
  *   src     [T*k] (out): src[pos[a]] = a
- *   x_perm  [T*k, d] (out): x_perm[pos[t*k+j]] = x[t]
+ *   tok     [T*k] (out) or NULL: tok[p] = src[p] / k, the token of row p
+ *   x_perm  [T*k, d] (out): x_perm[pos[t*k+j]] = x[t]; or NULL (no copy)
  *   ws      >= moe_workspace_bytes(desc, MOE_WS_PERMUTE) bytes of scratch */
 int moe_permute(const moe_desc_t *desc, const void *x, const int32_t *idx,
                 const int32_t *block_hist, int32_t *counts, int32_t *offsets, int32_t *pos,
-                int32_t *src, void *x_perm, void *ws, size_t ws_bytes, void *stream);
+                int32_t *src, int32_t *tok, void *x_perm, void *ws, size_t ws_bytes,
+                void *stream);
 
 /* Grouped GEMM over G groups of rows ("experts run as grouped GEMMs", Apex-3
  * "Fine-grained MoE"; Handbook 2.5 grouped GEMM for the local experts).
@@ -232,6 +240,23 @@ int moe_permute(const moe_desc_t *desc, const void *x, const int32_t *idx,
 int moe_grouped_gemm(int layout, int epilogue, int dtype, int64_t G, int64_t M_total, int64_t N,
                      int64_t K, const int32_t *group_offsets, const void *A, const void *B, void *C,
                      void *aux, void *ws, size_t ws_bytes, void *stream);
+
+/* The grouped GEMM of moe_grouped_gemm with the routed rows gathered from
+ * the un-permuted token matrix (gather-on-load: the permuted copy of the
+ * tokens is never materialised).  bf16 only, no workspace.
+ *   MOE_GEMM_NT (MOE_EPI_NONE or MOE_EPI_SWIGLU): A is the token matrix
+ *        [src_rows, K]; routed row m reads A[rows[m]].
+ *   MOE_GEMM_TN (MOE_EPI_NONE): B is the token matrix [src_rows, K];
+ *        routed row m of the reduction reads B[rows[m]].
+ *   rows [M_total] int32 (device), each in [0, src_rows) (not checked on the
+ *        device: the caller's contract; moe_permute's tok satisfies it).
+ * Shapes as for moe_grouped_gemm, and: NT SwiGLU needs N/2 a multiple of 128;
+ * TN needs K a multiple of 256; src_rows * K * 2 <= 2^32; 1 <= G <= 256.
+ * Otherwise MOE_ERR_UNSUPPORTED. */
+int moe_grouped_gemm_gather(int layout, int epilogue, int64_t G, int64_t M_total, int64_t N,
+                            int64_t K, const int32_t *group_offsets, const void *A, const void *B,
+                            void *C, void *aux, const int32_t *rows, int64_t src_rows,
+                            void *stream);
 
 /* Weighted combine / unpermute ("the experts' output must be returned",
  * Handbook 2.5):  y[t] = sum_{j<k} gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t])

@@ -40,7 +40,7 @@ class MoeWeights(ctypes.Structure):
 
 class MoeSaved(ctypes.Structure):
     _fields_ = [("logits", c_vp), ("idx", c_vp), ("gate", c_vp), ("counts", c_vp), ("offsets", c_vp),
-                ("pos", c_vp), ("src", c_vp), ("x_perm", c_vp), ("preact", c_vp), ("h", c_vp),
+                ("pos", c_vp), ("src", c_vp), ("tok", c_vp), ("x_perm", c_vp), ("preact", c_vp), ("h", c_vp),
                 ("y_perm", c_vp), ("s_preact", c_vp), ("s_h", c_vp)]
 
 
@@ -62,7 +62,10 @@ SIGNATURES = {
     "moe_workspace_bytes": (c_sz, [_P(MoeDesc), c_i32]),
     "moe_grouped_gemm_workspace_bytes": (c_sz, [c_i32, c_i32, c_i64, c_i64, c_i64, c_i64]),
     "moe_route": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
-    "moe_permute": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
+    "moe_permute": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
+                            c_vp]),
+    "moe_grouped_gemm_gather": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                        c_vp, c_vp, c_i64, c_vp]),
     "moe_grouped_gemm": (c_i32, [c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                                  c_vp, c_vp, c_sz, c_vp]),
     "moe_combine": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),

@@ -79,9 +79,10 @@ def moe_route(desc, logits, bias, idx, gate, block_hist, stream=None):
                               _stream(stream)), "moe_route")
 
 
-def moe_permute(desc, x, idx, block_hist, counts, offsets, pos, src, x_perm, ws, stream=None):
+def moe_permute(desc, x, idx, block_hist, counts, offsets, pos, src, x_perm, ws, stream=None, tok=None):
+    """x_perm may be None (no row copy); tok (int32 [T*k]) receives the token of each permuted row."""
     _check(L.load().moe_permute(ctypes.byref(desc), _p(x), _p(idx), _p(block_hist), _p(counts), _p(offsets),
-                                _p(pos), _p(src), _p(x_perm), _p(ws), ws.numel() * ws.element_size(),
+                                _p(pos), _p(src), _p(tok), _p(x_perm), _p(ws), ws.numel() * ws.element_size(),
                                 _stream(stream)), "moe_permute")
 
 
@@ -91,6 +92,14 @@ def moe_grouped_gemm(layout, epilogue, dtype, G, M_total, N, K, group_offsets, A
     _check(L.load().moe_grouped_gemm(LAYOUTS[layout], EPILOGUES[epilogue], DTYPES[dtype], G, M_total, N, K,
                                      _p(group_offsets), _p(A), _p(B), _p(C), _p(aux), _p(ws), nbytes,
                                      _stream(stream)), "moe_grouped_gemm")
+
+
+def moe_grouped_gemm_gather(layout, epilogue, G, M_total, N, K, group_offsets, A, B, C, rows, src_rows,
+                            aux=None, stream=None):
+    """bf16 grouped GEMM reading the routed rows of the token matrix through `rows` (NT: A, TN: B)."""
+    _check(L.load().moe_grouped_gemm_gather(LAYOUTS[layout], EPILOGUES[epilogue], G, M_total, N, K,
+                                            _p(group_offsets), _p(A), _p(B), _p(C), _p(aux), _p(rows),
+                                            src_rows, _stream(stream)), "moe_grouped_gemm_gather")
 
 
 def moe_combine(desc, y_perm, gate, pos, shared_y, y, stream=None):
@@ -103,7 +112,8 @@ def _weights(w: dict) -> L.MoeWeights:
                                                   "s_down")))
 
 
-SAVED_FIELDS = ("logits", "idx", "gate", "counts", "offsets", "pos", "src", "x_perm", "preact", "h", "y_perm",
+SAVED_FIELDS = ("logits", "idx", "gate", "counts", "offsets", "pos", "src", "tok", "x_perm", "preact", "h",
+                "y_perm",
                 "s_preact", "s_h")
 GRAD_FIELDS = ("d_w_router", "d_w_gateup", "d_w_down", "d_s_gateup", "d_s_down")
 
@@ -154,7 +164,8 @@ def moe_grouped_gemm_fp8(epilogue, G, M_total, N, K, group_offsets, A, a_scale, 
 
 
 # ------------------------------------------------------------------ buffers (torch device memory)
-def alloc_saved(desc, device="cuda", training=True) -> dict:
+def alloc_saved(desc, device="cuda", training=True, gather=False) -> dict:
+    """gather=True: no permuted token copy (x_perm None); the gate/up products read x through tok."""
     T, d, E, k, f = desc.num_tokens, desc.d_model, desc.num_experts, desc.top_k, desc.d_ff
     F = desc.num_shared * desc.d_ff_shared
     A = T * k
@@ -163,7 +174,7 @@ def alloc_saved(desc, device="cuda", training=True) -> dict:
     out = dict(logits=e(T, E, dtype=torch.float32), idx=e(T, k, dtype=torch.int32),
                gate=e(T, k, dtype=torch.float32), counts=e(E, dtype=torch.int32),
                offsets=e(E + 1, dtype=torch.int32), pos=e(A, dtype=torch.int32), src=e(A, dtype=torch.int32),
-               x_perm=e(A, d), preact=e(A, 2 * f) if training else None, h=e(A, f), y_perm=e(A, d),
+               tok=e(A, dtype=torch.int32), x_perm=None if gather else e(A, d), preact=e(A, 2 * f) if training else None, h=e(A, f), y_perm=e(A, d),
                s_preact=e(T, 2 * F) if (F and training) else None, s_h=e(T, F) if F else None)
     return out
 

@@ -265,19 +265,19 @@ int moe_route(const moe_desc_t* d, const float* logits, const float* bias, int32
 
 int moe_permute(const moe_desc_t* d, const void* x, const int32_t* idx,
                 const int32_t* block_hist, int32_t* counts, int32_t* offsets, int32_t* pos,
-                int32_t* src, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
+                int32_t* src, int32_t* tok, void* x_perm, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(d);
   if (s) return s;
   if (!counts || !offsets) return MOE_ERR_INVALID;
-  if (d->num_tokens > 0 && (!x || !idx || !block_hist || !pos || !src || !x_perm || !ws))
+  if (d->num_tokens > 0 && (!idx || !block_hist || !pos || !src || !ws || (x_perm && !x)))
     return MOE_ERR_INVALID;
-  const void* ptrs[] = {x, idx, block_hist, counts, offsets, pos, src, x_perm, ws};
+  const void* ptrs[] = {x, idx, block_hist, counts, offsets, pos, src, tok, x_perm, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
   if (ws_bytes < moe_workspace_bytes(d, MOE_WS_PERMUTE)) return MOE_ERR_WORKSPACE;
   return hip_status(launch_permute(x, d->dtype, idx, block_hist, (int)d->num_tokens,
                                    (int)d->d_model, (int)d->num_experts, (int)d->top_k,
-                                   (int32_t*)ws, counts, offsets, pos, src, x_perm,
+                                   (int32_t*)ws, counts, offsets, pos, src, tok, x_perm,
                                    (hipStream_t)stream));
 }
 
@@ -298,6 +298,26 @@ int moe_grouped_gemm(int layout, int epi, int dtype, int64_t G, int64_t M, int64
   return hip_status(launch_grouped_gemm(p, ws, ws_bytes, (hipStream_t)stream));
 }
 
+int moe_grouped_gemm_gather(int layout, int epi, int64_t G, int64_t M, int64_t N, int64_t K,
+                            const int32_t* off, const void* A, const void* B, void* C, void* aux,
+                            const int32_t* rows, int64_t src_rows, void* stream) {
+  int s = check_gemm(layout, epi, MOE_BF16, G, M, N, K);
+  if (s) return s;
+  if (!off || !B || !C || src_rows < 0) return MOE_ERR_INVALID;
+  if (M > 0 && (!A || !rows)) return MOE_ERR_INVALID;
+  const void* ptrs[] = {off, A, B, C, aux, rows};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (layout == MOE_GEMM_NN || epi == MOE_EPI_DSWIGLU || (layout == MOE_GEMM_TN && epi != MOE_EPI_NONE))
+    return MOE_ERR_UNSUPPORTED;
+  // row byte offsets of the token matrix are 32-bit in the kernel
+  if (src_rows * K * 2 > (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  GemmProblem p = gp(layout, epi, MOE_BF16, MOE_BF16, MOE_BF16, G, M, N, K, off, A, B, C, aux);
+  p.rows = rows ? rows : off;  // M = 0: any non-null map selects the gathered kernel
+  if (!gemm_big_supported(p)) return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_grouped_gemm(p, nullptr, 0, (hipStream_t)stream));
+}
+
 int moe_combine(const moe_desc_t* d, const void* y_perm, const float* gate, const int32_t* pos,
                 const void* shared_y, void* y, void* stream) {
   int s = check_desc(d);
@@ -311,6 +331,22 @@ int moe_combine(const moe_desc_t* d, const void* y_perm, const float* gate, cons
                                    (hipStream_t)stream));
 }
 
+// Layers whose routed gate/up products can read the token rows through the
+// row map (saved.x_perm == NULL): the persistent kernel takes the forward
+// product and, for training, the weight gradient; row byte offsets fit 32 bits.
+static int gather_supported(const moe_desc_t* d, bool training) {
+  const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, f = d->d_ff;
+  if (d->dtype != MOE_BF16 || T * D * 2 > (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  static const int32_t dummy = 0;
+  GemmProblem fw = gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, MOE_BF16, MOE_BF16, MOE_BF16, E, T * d->top_k, 2 * f, D,
+                      0, 0, 0, 0, 0);
+  GemmProblem wg = gp(MOE_GEMM_TN, MOE_EPI_NONE, MOE_BF16, MOE_BF16, MOE_BF16, E, T * d->top_k, 2 * f, D,
+                      0, 0, 0, 0, 0);
+  fw.rows = wg.rows = &dummy;
+  if (!gemm_big_supported(fw) || (training && !gemm_big_supported(wg))) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
 int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
                 const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(d);
@@ -322,15 +358,22 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
   if (F > 0 && (!w->s_gateup || !w->s_down)) return MOE_ERR_INVALID;
   if (!sv->counts || !sv->offsets) return MOE_ERR_INVALID;
+  // no permuted copy of the tokens: the gate/up products gather them (with
+  // no tokens there is nothing to gather)
+  const bool gather = T > 0 && !sv->x_perm;
   if (T > 0 && (!x || !y || !sv->logits || !sv->idx || !sv->gate || !sv->pos || !sv->src ||
-                !sv->x_perm || !sv->h || !sv->y_perm || !ws || (F > 0 && !sv->s_h)))
+                (gather && !sv->tok) || !sv->h || !sv->y_perm || !ws || (F > 0 && !sv->s_h)))
     return MOE_ERR_INVALID;
   const void* ptrs[] = {x, y, w->w_router, w->bias, w->w_gateup, w->w_down, w->s_gateup,
                         w->s_down, sv->logits, sv->idx, sv->gate, sv->counts, sv->offsets,
-                        sv->pos, sv->src, sv->x_perm, sv->preact, sv->h, sv->y_perm,
+                        sv->pos, sv->src, sv->tok, sv->x_perm, sv->preact, sv->h, sv->y_perm,
                         sv->s_preact, sv->s_h, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (gather) {
+    s = gather_supported(d, sv->preact != nullptr);
+    if (s) return s;
+  }
   if (ws_bytes < moe_workspace_bytes(d, MOE_WS_FORWARD)) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (T == 0) {
@@ -348,11 +391,13 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
                        (int)k, d->score, d->renorm, sv->idx, sv->gate, fw.hist, st));
   // 3. permutation into expert-contiguous rows
   MOE_STAGE(MOE_STAGE_PERMUTE, launch_permute(x, dt, sv->idx, fw.hist, (int)T, (int)D, (int)E, (int)k, fw.base,
-                         sv->counts, sv->offsets, sv->pos, sv->src, sv->x_perm, st));
-  // 4. gate/up grouped GEMM with the SwiGLU activation
-  MOE_STAGE(MOE_STAGE_GATE_UP, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D,
-                                 sv->offsets, sv->x_perm, w->w_gateup, sv->h, sv->preact),
-                              nullptr, 0, st));
+                         sv->counts, sv->offsets, sv->pos, sv->src, sv->tok, sv->x_perm, st));
+  // 4. gate/up grouped GEMM with the SwiGLU activation (rows of x_perm, or of
+  // x gathered through tok)
+  GemmProblem gu = gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D, sv->offsets,
+                      gather ? x : sv->x_perm, w->w_gateup, sv->h, sv->preact);
+  gu.rows = gather ? sv->tok : nullptr;
+  MOE_STAGE(MOE_STAGE_GATE_UP, launch_grouped_gemm(gu, nullptr, 0, st));
   // 5. down grouped GEMM
   MOE_STAGE(MOE_STAGE_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
                                  sv->h, w->w_down, sv->y_perm, nullptr),
@@ -397,15 +442,20 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
     return MOE_ERR_INVALID;
   if (F > 0 && T > 0 && (!sv->s_h || !sv->s_preact)) return MOE_ERR_INVALID;
   if (!sv->offsets) return MOE_ERR_INVALID;
+  const bool gather = T > 0 && !sv->x_perm;
   if (T > 0 && (!x || !dy || !dx || !sv->logits || !sv->idx || !sv->gate || !sv->pos ||
-                !sv->x_perm || !sv->preact || !sv->h || !sv->y_perm || !ws))
+                (gather && !sv->tok) || !sv->preact || !sv->h || !sv->y_perm || !ws))
     return MOE_ERR_INVALID;
   const void* ptrs[] = {x, dy, dx, w->w_router, w->w_gateup, w->w_down, w->s_gateup, w->s_down,
-                        sv->logits, sv->idx, sv->gate, sv->offsets, sv->pos, sv->x_perm,
+                        sv->logits, sv->idx, sv->gate, sv->offsets, sv->pos, sv->tok, sv->x_perm,
                         sv->preact, sv->h, sv->y_perm, sv->s_preact, sv->s_h, g->d_w_router,
                         g->d_w_gateup, g->d_w_down, g->d_s_gateup, g->d_s_down, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (gather) {
+    s = gather_supported(d, true);
+    if (s) return s;
+  }
   if (ws_bytes < moe_workspace_bytes(d, MOE_WS_BACKWARD)) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   BwdWs bw;
@@ -435,10 +485,11 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
                                  bw.dy_perm, sv->h, g->d_w_down, nullptr),
                               bw.gemm, bw.gemm_bytes, st));
-  // 4. gate/up weight gradient
-  MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
-                                 sv->offsets, bw.dgu, sv->x_perm, g->d_w_gateup, nullptr),
-                              bw.gemm, bw.gemm_bytes, st));
+  // 4. gate/up weight gradient (token rows of x_perm, or of x through tok)
+  GemmProblem guw = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D, sv->offsets, bw.dgu,
+                       gather ? x : sv->x_perm, g->d_w_gateup, nullptr);
+  guw.rows = gather ? sv->tok : nullptr;
+  MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(guw, bw.gemm, bw.gemm_bytes, st));
   // 5. gate/up data gradient (written over dy_perm, which is no longer needed)
   void* dx_perm = bw.dy_perm;
   MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,

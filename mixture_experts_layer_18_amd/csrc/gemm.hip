@@ -339,6 +339,8 @@ static hipError_t dispatch_simt(const KArgs& ka, const GemmProblem& p, hipStream
 }
 
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st) {
+  // gathered rows: the persistent kernel only
+  if (p.rows && !gemm_big_supported(p)) return hipErrorInvalidValue;
   if (p.M_total == 0 && p.layout != MOE_GEMM_TN) return hipSuccess;
   KArgs ka;
   ka.G = (int)p.G;

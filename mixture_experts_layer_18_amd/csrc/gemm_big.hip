@@ -32,6 +32,14 @@
 // LDS as [256 rows][32] with 16-byte chunks XOR-swizzled by row; strided ones
 // (NN's B, TN both) as [32][256] swizzled by k-row and are read with
 // ds_read_b64_tr_b16 transposes.
+//
+// Gathered rows (GA): the operand indexed by the routed rows -- NT's A, TN's
+// B -- is read through a row map from the un-permuted token matrix, so the
+// permuted copy of the tokens is never written.  NT: each lane's four A rows
+// are fixed for a tile; their byte offsets are loaded once per tile.  TN: the
+// rows change every k-step; each wave DMAs the 32 map entries of stage s + 3
+// into a small LDS ring together with stage s's operands, so the entries a
+// DMA issue needs have landed (by the same wait) three steps before use.
 #include "gemm_common.h"
 
 namespace moe {
@@ -58,7 +66,9 @@ struct Args {
   bf16_t* aux;
   const float* a_scale;  // fp8: per-row scales of A [M_total]
   const float* b_scale;  // fp8: per-row scales of B [G, N]
+  const int32_t* rows;   // GA: source row of each routed row (NT: of A, TN: of B)
 };
+constexpr int RING = 8;  // GA TN: map stages held per wave
 
 struct Tile {
   int g;
@@ -70,16 +80,21 @@ struct Tile {
 // F8: A and B hold OCP e4m3 codes (one byte each) with row scales; a k-step
 // then covers 64 elements (still 64 bytes per LDS row) and one
 // v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) per 32x32 tile.
-template <int LAYOUT, int EPI, bool F8>
+template <int LAYOUT, int EPI, bool F8, bool GA>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
   constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
   static_assert(!F8 || LAYOUT == MOE_GEMM_NT, "fp8 operands: forward layout only");
+  static_assert(!GA || (!F8 && LAYOUT != MOE_GEMM_NN), "gathered rows: bf16 NT or TN");
+  constexpr bool GN = GA && LAYOUT == MOE_GEMM_NT;  // A rows gathered, fixed per tile
+  constexpr bool GT = GA && LAYOUT == MOE_GEMM_TN;  // B k-rows gathered through the ring
+  constexpr int LV = LT + (GT ? 1 : 0);             // vector-memory instructions per k-step
   constexpr int ES = F8 ? 1 : 2;         // bytes per operand element
   constexpr int BKE = BK * 2 / ES;       // elements per k-step (64 bytes per row)
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB + PAD_BYTES];
   __shared__ int s_pref[256];
   __shared__ int scratch[4];
+  __shared__ __attribute__((aligned(256))) int ring[GT ? NW * RING * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
@@ -154,11 +169,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   const char* Bb = (const char*)a.B;
   const uint32_t smem_base = lds_addr(smem);
   const uint32_t pad_lds = smem_base + STAGES * SB;
+  const uint32_t ring_base = lds_addr(ring);
   const int64_t F = N / 2;
 
   // Instruction q (0..LT-1) of k-step kt of tile t: q < LP fills the P tile,
   // the rest the Q tile.  `ln` is the lane id (an opaque copy per call site).
-  auto issue = [&](const Tile& t, int64_t kt, int q, int ln) __attribute__((always_inline)) {
+  // gv: GN, the byte offsets of the lane's LP A rows; GT, the source rows of
+  // the lane's LQ B k-rows of this k-step.
+  auto issue = [&](const Tile& t, int64_t kt, int q, int ln, const uint32_t* gv) __attribute__((always_inline)) {
     const uint32_t st = smem_base + (uint32_t)(kt % STAGES) * SB;
     const bool isP = q < LP;
     const int i = isP ? q : q - LP;
@@ -168,7 +186,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
       const int row = (i * NW + wave) * 16 + (ln >> 2);
       const int chunk = (ln & 3) ^ ((row >> 2) & 3);
       const uint32_t kb = (uint32_t)(kt * BK * 2) + chunk * 16;  // 64 bytes per row per k-step
-      if (isP) {
+      if (isP && GN) {
+        dma16_off(Ab, gv[i] + kb, dst);
+      } else if (isP) {
         const int nrows = (int)(t.i_hi - t.i_lo);
         const int r = row < nrows ? row : nrows - 1;
         const int64_t ld = (LAYOUT == MOE_GEMM_NT) ? K : N;
@@ -199,10 +219,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
         const int64_t c0 = isP ? t.i_lo : t.j0;
         int64_t col = c0 + chunk * 8;
         col = col < ld - 8 ? col : ld - 8;
-        const int64_t rows = t.r_hi - t.r_lo;
-        int64_t r = kt * BK + kr;
-        r = r < rows ? r : rows - 1;
-        dma16_off((isP ? Ab : Bb) + t.r_lo * ld * 2, (uint32_t)(r * ld + col) * 2, dst);
+        if (GT && !isP) {
+          dma16_off(Bb, (gv[i] * (uint32_t)ld + (uint32_t)col) * 2u, dst);
+        } else {
+          const int64_t rows = t.r_hi - t.r_lo;
+          int64_t r = kt * BK + kr;
+          r = r < rows ? r : rows - 1;
+          dma16_off((isP ? Ab : Bb) + t.r_lo * ld * 2, (uint32_t)(r * ld + col) * 2, dst);
+        }
       }
     }
   };
@@ -222,12 +246,64 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
         *reinterpret_cast<uint4*>(st + (q < LP ? 0 : PB) + (i * NW + wave) * 1024 + lane * 16) = z;
     }
   };
-  auto stage_dma = [&](const Tile& t, int64_t s, int64_t nk, int ln) __attribute__((always_inline)) {
+  // GT: the map entries of k-step s (32 rows, clamped to the group) into ring
+  // slot s % RING of this wave; past the reduction a pad
+  auto ring_dma = [&](const Tile& t, int64_t s, int64_t nk, int ln) __attribute__((always_inline)) {
+    if (s < nk) {
+      const int64_t rows = t.r_hi - t.r_lo;
+      int64_t r = s * BK + (ln & 31);
+      r = r < rows ? r : rows - 1;
+      dma4_off(a.rows + t.r_lo, (uint32_t)r * 4u,
+               __builtin_amdgcn_readfirstlane(ring_base + (wave * RING + (int)(s % RING)) * 256));
+    } else {
+      dma4_pad(Ab, pad_lds);
+    }
+  };
+  // GN: byte offsets of the lane's A rows in tile t
+  auto row_offsets = [&](const Tile& t, uint32_t* ao, int ln) __attribute__((always_inline)) {
+    const int nrows = (int)(t.i_hi - t.i_lo);
+#pragma unroll
+    for (int i = 0; i < LP; ++i) {
+      const int row = (i * NW + wave) * 16 + (ln >> 2);
+      const int r = row < nrows ? row : nrows - 1;
+      ao[i] = (uint32_t)a.rows[t.i_lo + r] * (uint32_t)(K * ES);
+    }
+  };
+  // GT: source rows of the lane's B k-rows of k-step s, read directly
+  auto direct_rows = [&](const Tile& t, int64_t s, uint32_t* gr, int ln) __attribute__((always_inline)) {
+    const int64_t rows = t.r_hi - t.r_lo;
+#pragma unroll
+    for (int i = 0; i < LQ; ++i) {
+      const int kr = (i * NW + wave) * 2 + (ln >> 5);
+      int64_t r = s * BK + kr;
+      r = r < rows ? r : rows - 1;
+      gr[i] = rows > 0 ? (uint32_t)a.rows[t.r_lo + r] : 0u;
+    }
+  };
+  // one k-step's operand DMA (GT: preceded by the map entries of k-step s+3)
+  auto stage_dma = [&](const Tile& t, int64_t s, int64_t nk, int ln, const uint32_t* gv)
+                       __attribute__((always_inline)) {
+    if constexpr (GT) {
+      ring_dma(t, s + 3, nk, ln);
+      __builtin_amdgcn_sched_barrier(0);
+    }
 #pragma unroll
     for (int q = 0; q < LT; ++q) {
-      if (s < nk) issue(t, s, q, ln);
+      if (s < nk) issue(t, s, q, ln, gv);
       else dma4_pad(Ab, pad_lds + q * 256);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // the first STAGES k-steps of tile t (GN: ao holds its row offsets; GT:
+  // gr the source rows of its first STAGES k-steps)
+  auto prologue = [&](const Tile& t, int64_t nk, int ln, const uint32_t* ao, const uint32_t (*gr)[LQ])
+                      __attribute__((always_inline)) {
+    if constexpr (GT) {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) stage_dma(t, s, nk, ln, gr[s]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < STAGES; ++s) stage_dma(t, s, nk, ln, ao);
     }
   };
 
@@ -246,10 +322,16 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   if (L >= total) return;
   Tile t = tile_of(L);
   int64_t nk = (t.r_hi - t.r_lo + BKE - 1) / BKE;
+  uint32_t aoff[LP] = {0u, 0u, 0u, 0u};
+  static_assert(LP == 4, "row offsets per lane");
   {
     const int ln = opaque_i(lane);
+    uint32_t gr[STAGES][LQ];
+    if constexpr (GN) row_offsets(t, aoff, ln);
+    if constexpr (GT)
 #pragma unroll
-    for (int s = 0; s < STAGES; ++s) stage_dma(t, s, nk, ln);
+      for (int s = 0; s < STAGES; ++s) direct_rows(t, s, gr[s], ln);
+    prologue(t, nk, ln, aoff, gr);
   }
 
   while (true) {
@@ -257,6 +339,23 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     wait_vmcnt<0>();
     if (nk > 0) zero_tail(t, 0);
     lds_barrier();
+    // GA: the next tile's row map is loaded now, so that it has arrived by
+    // the time the next tile's first stages are issued
+    const int Ln = L + nwg;
+    const bool more = Ln < total;
+    Tile tn = t;
+    int64_t nk_n = 0;
+    uint32_t aoff_n[LP] = {0u, 0u, 0u, 0u};
+    uint32_t gr_n[STAGES][LQ];
+    if (GA && more) {
+      tn = tile_of(Ln);
+      nk_n = (tn.r_hi - tn.r_lo + BKE - 1) / BKE;
+      const int lp = opaque_i(lane);
+      if constexpr (GN) row_offsets(tn, aoff_n, lp);
+      if constexpr (GT)
+#pragma unroll
+        for (int s = 0; s < STAGES; ++s) direct_rows(tn, s, gr_n[s], lp);
+    }
     f32x16_t acc[FI][FJ];
 #pragma unroll
     for (int it = 0; it < FI; ++it)
@@ -292,7 +391,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
             acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
                                                                           0x7f7f7f7f, 0, 0x7f7f7f7f);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<2 * LT>();
+        wait_vmcnt<2 * LV>();
         lds_barrier();
         const char* nP = smem + ((kt + 1) % STAGES) * SB;
         v8i_t Pn[FI], Qn[FJ];
@@ -309,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
           acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
                                                                         0x7f7f7f7f, 0, 0x7f7f7f7f);
           __builtin_amdgcn_sched_barrier(0);
-          if (real) issue(t, kt + STAGES, q, ln);
+          if (real) issue(t, kt + STAGES, q, ln, aoff);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -340,8 +439,18 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
         __builtin_amdgcn_sched_barrier(0);
         // k-step kt+1 landed for this wave (kt+2, kt+3 may be in flight); after
         // the barrier every wave has it and is done reading k-step kt
-        wait_vmcnt<2 * LT>();
+        wait_vmcnt<2 * LV>();
         if (kt + 1 < nk) zero_tail(t, kt + 1);
+        // GT: the map entries of k-step kt + STAGES landed with k-step kt + 1;
+        // read before the barrier, whose LDS wait then covers them (after it
+        // the 4-bit LDS counter could not single them out from the fragment
+        // reads that follow)
+        uint32_t gq[LQ];
+        if constexpr (GT) {
+          const int* rs = ring + (wave * RING + (int)((kt + STAGES) % RING)) * 64;
+#pragma unroll
+          for (int i = 0; i < LQ; ++i) gq[i] = (uint32_t)rs[(i * NW + wave) * 2 + (lane >> 5)];
+        }
         lds_barrier();
         const char* nP = smem + ((kt + 1) % STAGES) * SB;
   #pragma unroll
@@ -358,8 +467,12 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
             acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb1[jt], pa1[it], acc[it][jt], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
-          if (real) issue(t, kt + STAGES, q, ln);
+          if (real) issue(t, kt + STAGES, q, ln, GT ? gq : aoff);
           else dma4_pad(Ab, pad_lds + q * 256);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (GT) {
+          ring_dma(t, kt + STAGES + 3, nk, ln);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -367,17 +480,14 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     // every wave is done with this tile's LDS stages: fetch the next tile's
     // first stages, then write this tile's results
     lds_barrier();
-    const int Ln = L + nwg;
-    const bool more = Ln < total;
-    Tile tn = t;
-    int64_t nk_n = 0;
     auto prefetch_next = [&]() __attribute__((always_inline)) {
       if (more) {
-        tn = tile_of(Ln);
-        nk_n = (tn.r_hi - tn.r_lo + BKE - 1) / BKE;
+        if constexpr (!GA) {
+          tn = tile_of(Ln);
+          nk_n = (tn.r_hi - tn.r_lo + BKE - 1) / BKE;
+        }
         const int lp = opaque_i(lane);
-#pragma unroll
-        for (int s = 0; s < STAGES; ++s) stage_dma(tn, s, nk_n, lp);
+        prologue(tn, nk_n, lp, aoff_n, gr_n);
       }
     };
 
@@ -460,6 +570,8 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     L = Ln;
     t = tn;
     nk = nk_n;
+#pragma unroll
+    for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
   }
 }
 
@@ -476,10 +588,10 @@ static int grid_size() {
   return n;
 }
 
-template <int LAYOUT, int EPI, bool F8 = false>
+template <int LAYOUT, int EPI, bool F8 = false, bool GA = false>
 static hipError_t run(const Args& a, hipStream_t st) {
   if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI, F8><<<dim3((unsigned)grid_size()), dim3(256), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, F8, GA><<<dim3((unsigned)grid_size()), dim3(256), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -492,12 +604,17 @@ static hipError_t run(const Args& a, hipStream_t st) {
 // enough tiles to fill the chip without row slices.
 bool gemm_big_supported(const GemmProblem& p) {
   if (p.ta != MOE_BF16 || p.tb != MOE_BF16 || p.tc != MOE_BF16 || p.G > 256) return false;
+  if (p.rows && p.layout == MOE_GEMM_NN) return false;
   if (p.layout == MOE_GEMM_NT) {
     if (p.epilogue == MOE_EPI_SWIGLU) return (p.N / 2) % 128 == 0;
     return p.epilogue == MOE_EPI_NONE;
   }
-  if (p.layout == MOE_GEMM_TN)  // whole 256-wide column tiles only (else 256 x 128 tiles waste less)
-    return p.K % 256 == 0 && p.G * cdiv64(p.N, 256) * (p.K / 256) >= 4 * 256;
+  if (p.layout == MOE_GEMM_TN) {  // whole 256-wide column tiles only (else 256 x 128 tiles waste less)
+    if (p.K % 256) return false;
+    // few tiles: row slices on the two-workgroup kernel fill the chip better,
+    // but gathered rows are read by this kernel only
+    return p.rows || p.G * cdiv64(p.N, 256) * (p.K / 256) >= 4 * 256;
+  }
   if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE;
   return false;
 }
@@ -514,6 +631,16 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
   a.C = (bf16_t*)p.C;
   a.aux = (bf16_t*)p.aux;
   a.a_scale = a.b_scale = nullptr;
+  a.rows = p.rows;
+  if (p.rows) {
+    if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE)
+      return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, false, true>(a, st);
+    if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU)
+      return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, false, true>(a, st);
+    if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE)
+      return pk::run<MOE_GEMM_TN, MOE_EPI_NONE, false, true>(a, st);
+    return hipErrorInvalidValue;
+  }
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE>(a, st);
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU>(a, st);
   if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NN, MOE_EPI_NONE>(a, st);
@@ -540,6 +667,7 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
   a.aux = (bf16_t*)aux;
   a.a_scale = a_scale;
   a.b_scale = b_scale;
+  a.rows = nullptr;
   if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true>(a, st);
   if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true>(a, st);
   return hipErrorInvalidValue;

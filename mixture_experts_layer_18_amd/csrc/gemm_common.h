@@ -103,6 +103,12 @@ MOE_DEV void dma16_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
                : "memory", "m0");
 }
 
+// 4 bytes per lane from sbase + voff into LDS at m0 + 4*lane.
+MOE_DEV void dma4_off(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "s"(lds_base)
+               : "memory", "m0");
+}
+
 // A 4-byte-per-lane DMA into a scratch LDS area: one vector-memory
 // instruction that moves almost nothing, used where a fixed instruction count
 // per step keeps the wait counts compile-time constants.

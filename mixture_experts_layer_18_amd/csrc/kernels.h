@@ -11,7 +11,7 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
                         int renorm, int32_t* idx, float* gate, int32_t* hist, hipStream_t st);
 hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const int32_t* hist, int T,
                           int d, int E, int k, int32_t* base, int32_t* counts, int32_t* offsets,
-                          int32_t* pos, int32_t* src, void* x_perm, hipStream_t st);
+                          int32_t* pos, int32_t* src, int32_t* tok, void* x_perm, hipStream_t st);
 
 // ---- grouped GEMM
 // Element types of the operands: A, B and C each f32 or bf16 (MOE_F32 / MOE_BF16).
@@ -24,6 +24,9 @@ struct GemmProblem {
   const void* B;
   void* C;
   void* aux;
+  // optional row map of the operand indexed by the routed rows (NT: A, TN:
+  // B): routed row r reads row rows[r] of that operand (persistent kernel)
+  const int32_t* rows = nullptr;
 };
 size_t gemm_workspace_bytes(const GemmProblem& p);
 hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);

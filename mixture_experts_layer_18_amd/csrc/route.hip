@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void permute_kernel(
     const TX* __restrict__ x, const int32_t* __restrict__ idx, const int32_t* __restrict__ counts,
     const int32_t* __restrict__ base, int T, int d, int E, int k, int nblk,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pos, int32_t* __restrict__ src,
-    TX* __restrict__ x_perm) {
+    int32_t* __restrict__ tok, TX* __restrict__ x_perm) {
   static_assert(MOE_ROUTE_BLOCK == 32, "one mask word per expert");
   __shared__ int s_off[256];
   __shared__ uint32_t s_mask[256];
@@ -221,8 +221,11 @@ __global__ __launch_bounds__(256) void permute_kernel(
     const int a = t0 * k + i;
     pos[a] = p;
     src[p] = a;
+    if (tok) tok[p] = t0 + tl;
     s_pos[i] = p;
   }
+  // without x_perm the products read the token rows through tok
+  if (!x_perm) return;
   __syncthreads();
   // row copies: the workgroup walks (token, 16-byte chunk) pairs with
   // consecutive threads on consecutive chunks, four pairs per thread in
@@ -271,7 +274,7 @@ hipError_t launch_route(const float* logits, const float* bias, int T, int E, in
 
 hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const int32_t* hist, int T,
                           int d, int E, int k, int32_t* base, int32_t* counts, int32_t* offsets,
-                          int32_t* pos, int32_t* src, void* x_perm, hipStream_t st) {
+                          int32_t* pos, int32_t* src, int32_t* tok, void* x_perm, hipStream_t st) {
   const int nblk = (int)cdiv64(T, MOE_ROUTE_BLOCK);
   hist_scan_kernel<<<dim3(E), dim3(256), 0, st>>>(hist, nblk, base, counts);
   if (nblk == 0) {
@@ -280,10 +283,10 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const in
   }
   if (dtype == MOE_BF16)
     permute_kernel<bf16_t><<<dim3(nblk), dim3(256), 0, st>>>(
-        (const bf16_t*)x, idx, counts, base, T, d, E, k, nblk, offsets, pos, src, (bf16_t*)x_perm);
+        (const bf16_t*)x, idx, counts, base, T, d, E, k, nblk, offsets, pos, src, tok, (bf16_t*)x_perm);
   else
     permute_kernel<float><<<dim3(nblk), dim3(256), 0, st>>>(
-        (const float*)x, idx, counts, base, T, d, E, k, nblk, offsets, pos, src, (float*)x_perm);
+        (const float*)x, idx, counts, base, T, d, E, k, nblk, offsets, pos, src, tok, (float*)x_perm);
   return hipGetLastError();
 }
 

@@ -28,11 +28,12 @@ def upload_layer(cfg, inp):
     return w
 
 
-def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False, terms=None):
+def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False, terms=None, gather=False):
+    """gather: no permuted token copy; the gate/up products read x through the token map."""
     desc = M.desc_from_config(cfg)
     w = upload_layer(cfg, inp) if weights is None else weights
     x = dev(inp["x"]) if x is None else x
-    saved = M.alloc_saved(desc, training=backward)
+    saved = M.alloc_saved(desc, training=backward, gather=gather)
     y = torch.empty_like(x)
     ws = M.alloc_workspace(desc, "forward")
     M.moe_forward(desc, w, x, y, saved, ws)
@@ -122,9 +123,9 @@ def check_routing(cfg, g_logits, g_idx, fw, tokens=None):
     return same_set
 
 
-def compare_full(cfg, inp, backward):
+def compare_full(cfg, inp, backward, gather=False):
     """Full comparison on a layer small enough for the oracle to run whole."""
-    g = run_gpu(cfg, inp, backward)
+    g = run_gpu(cfg, inp, backward, gather=gather)
     oi = oracle_inputs(cfg, inp)
     fw, bw = oracle_run(cfg, oi, backward)
     same = check_routing(cfg, g["logits"], g["idx"], fw)

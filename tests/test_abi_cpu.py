@@ -21,7 +21,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -33,7 +33,7 @@ def test_status_strings(lib):
 def test_struct_layout_matches_header():
     assert ctypes.sizeof(L.MoeDesc) == 7 * 8 + 4 * 4
     assert ctypes.sizeof(L.MoeWeights) == 6 * 8
-    assert ctypes.sizeof(L.MoeSaved) == 13 * 8
+    assert ctypes.sizeof(L.MoeSaved) == 14 * 8
     assert ctypes.sizeof(L.MoeGrads) == 5 * 8
 
 
@@ -83,9 +83,9 @@ def test_null_and_misaligned_pointers_rejected(lib):
     assert lib.moe_route(ctypes.byref(d), mis, None, a, a, a, None) == L.MOE_ERR_ALIGN
     assert lib.moe_combine(ctypes.byref(d), a, a, a, None, None, None) == L.MOE_ERR_INVALID
     # workspace too small
-    assert lib.moe_permute(ctypes.byref(d), a, a, a, a, a, a, a, a, a, 16, None) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_permute(ctypes.byref(d), a, a, a, a, a, a, a, a, a, a, 16, None) == L.MOE_ERR_WORKSPACE
     w = L.MoeWeights(a, None, a, a, None, None)
-    s = L.MoeSaved(*([a] * 13))
+    s = L.MoeSaved(*([a] * 14))
     assert lib.moe_forward(ctypes.byref(d), ctypes.byref(w), a, a, ctypes.byref(s), a, 16, None) == \
         L.MOE_ERR_WORKSPACE
     assert lib.moe_forward(ctypes.byref(d), None, a, a, ctypes.byref(s), a, 1 << 30, None) == L.MOE_ERR_INVALID
@@ -95,7 +95,7 @@ def test_null_and_misaligned_pointers_rejected(lib):
                             None, a, 1 << 30, None) == L.MOE_ERR_INVALID
     # shared experts declared but no shared weights
     d2 = make_desc(64, 128, 8, 2, 256, 1, 128, "sigmoid", True, "bf16")
-    s2 = L.MoeSaved(*([a] * 13))
+    s2 = L.MoeSaved(*([a] * 14))
     assert lib.moe_forward(ctypes.byref(d2), ctypes.byref(w), a, a, ctypes.byref(s2), a, 1 << 30, None) == \
         L.MOE_ERR_INVALID
 
@@ -184,3 +184,38 @@ def test_fp8_argument_checks(lib):
                                     ctypes.c_void_p((1 << 20) + 4), None, None) == L.MOE_ERR_ALIGN
     assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 0, 256, 128, a, None, None, None, None, None, None,
                                     None) == L.MOE_OK
+
+
+def test_gather_argument_checks(lib):
+    """The gathered-row GEMM and the layer without a permuted token copy:
+    unsupported layouts and shapes and missing maps are rejected on the host."""
+    a = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10004)
+    NT, NN, TN = L.MOE_GEMM_NT, L.MOE_GEMM_NN, L.MOE_GEMM_TN
+    NONE, SWIGLU = L.MOE_EPI_NONE, L.MOE_EPI_SWIGLU
+    gg = lib.moe_grouped_gemm_gather
+    assert gg(NN, NONE, 4, 64, 256, 256, a, a, a, a, None, a, 100, None) == L.MOE_ERR_UNSUPPORTED
+    assert gg(TN, SWIGLU, 4, 64, 256, 256, a, a, a, a, a, a, 100, None) == L.MOE_ERR_INVALID
+    assert gg(TN, NONE, 4, 64, 256, 192, a, a, a, a, None, a, 100, None) == L.MOE_ERR_UNSUPPORTED  # K % 256
+    assert gg(NT, SWIGLU, 4, 64, 384, 256, a, a, a, a, a, a, 100, None) == L.MOE_ERR_UNSUPPORTED  # F % 128
+    assert gg(NT, NONE, 4, 64, 256, 4096, a, a, a, a, None, a, 1 << 20, None) == L.MOE_ERR_UNSUPPORTED
+    assert gg(NT, NONE, 4, 64, 256, 256, a, a, a, a, None, None, 100, None) == L.MOE_ERR_INVALID   # no map
+    assert gg(NT, NONE, 4, 64, 256, 256, a, a, a, a, None, mis, 100, None) == L.MOE_ERR_ALIGN
+    assert gg(NT, NONE, 4, 64, 256, 256, a, a, a, a, None, a, -1, None) == L.MOE_ERR_INVALID
+    # layer without x_perm
+    w = L.MoeWeights(a, None, a, a, None, None)
+    s = L.MoeSaved(*([a] * 14))
+    s.x_perm = None
+    f32 = make_desc(64, 256, 8, 2, 256, 0, 0, "softmax", False, "f32")
+    assert lib.moe_forward(ctypes.byref(f32), ctypes.byref(w), a, a, ctypes.byref(s), a, 1 << 30, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    odd = make_desc(64, 192, 8, 2, 256, 0, 0, "softmax", False, "bf16")   # d % 256: no gathered weight gradient
+    assert lib.moe_forward(ctypes.byref(odd), ctypes.byref(w), a, a, ctypes.byref(s), a, 1 << 30, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    g = L.MoeGrads(a, a, a, None, None)
+    assert lib.moe_backward(ctypes.byref(odd), ctypes.byref(w), a, ctypes.byref(s), a, a, ctypes.byref(g), None,
+                            None, a, 1 << 30, None) == L.MOE_ERR_UNSUPPORTED
+    s.tok = None
+    ok = make_desc(64, 256, 8, 2, 256, 0, 0, "softmax", False, "bf16")
+    assert lib.moe_forward(ctypes.byref(ok), ctypes.byref(w), a, a, ctypes.byref(s), a, 1 << 30, None) == \
+        L.MOE_ERR_INVALID

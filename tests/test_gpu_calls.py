@@ -108,9 +108,16 @@ def test_permute_bit_exact(cfg):
     src = torch.empty(T * k, dtype=torch.int32, device="cuda")
     x_perm = torch.empty(T * k, d, dtype=x.dtype, device="cuda")
     ws = M.alloc_workspace(desc, "permute")
-    M.moe_permute(desc, x, idx, hist, counts, offsets, pos, src, x_perm, ws)
+    tok = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    M.moe_permute(desc, x, idx, hist, counts, offsets, pos, src, x_perm, ws, tok=tok)
     torch.cuda.synchronize()
     oc, oo, op, os_ = O.permute_indices(idx.cpu().numpy(), E)
+    assert np.array_equal(tok.cpu().numpy(), os_ // k)
+    # without the row copy: the same indices
+    pos2, src2, tok2 = torch.full_like(pos, -1), torch.full_like(src, -1), torch.full_like(tok, -1)
+    M.moe_permute(desc, x, idx, hist, counts, offsets, pos2, src2, None, ws, tok=tok2)
+    torch.cuda.synchronize()
+    assert torch.equal(pos2, pos) and torch.equal(src2, src) and torch.equal(tok2, tok)
     assert np.array_equal(counts.cpu().numpy(), oc)
     assert np.array_equal(offsets.cpu().numpy(), oo)
     assert oo[-1] == T * k
