@@ -79,7 +79,9 @@ struct Tile {
 
 // F8: A and B hold OCP e4m3 codes (one byte each) with row scales; a k-step
 // then covers 64 elements (still 64 bytes per LDS row) and one
-// v_mfma_scale_f32_32x32x64_f8f6f4 (unit block scales) per 32x32 tile.
+// matrix-core product per 32x32 tile: the f8f6f4 builtin with zero scale
+// operands, which the compiler emits as the unscaled
+// v_mfma_f32_32x32x64_f8f6f4 (one instruction, no scale prefix).
 template <int LAYOUT, int EPI, bool F8, bool GA>
 __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
@@ -364,11 +366,13 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
     if constexpr (F8) {
-      // both 32-byte halves of a lane's row fragment feed one MFMA: the
-      // fragments of stage kt are complete before the step starts; the
-      // first two row blocks' MFMAs run, the barrier, then the next
-      // stage's fragments are requested while the other two row blocks'
-      // MFMAs run interleaved with the DMA issue
+      // Both 32-byte halves of a lane's row fragment feed one MFMA, so a
+      // k-step cannot be split in reduction halves as in the bf16 loop; it is
+      // split in row blocks instead.  Entering step kt, Q (all column blocks)
+      // and P[0..1] of stage kt are in registers.  The step reads P[2..3] of
+      // stage kt while the MFMAs of row blocks 0..1 run, waits and passes
+      // the barrier, requests Q and P[0..1] of stage kt+1, then runs the
+      // MFMAs of row blocks 2..3 interleaved with the DMA issue.
       typedef int v4i_t __attribute__((ext_vector_type(4)));
       typedef int v8i_t __attribute__((ext_vector_type(8)));
       auto frag8 = [&](const char* st, int row) __attribute__((always_inline)) {
@@ -376,44 +380,51 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
         const v4i_t hi = __builtin_bit_cast(v4i_t, frag_kc<BK>(st, row, 1, lane));
         return (v8i_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
       };
-      v8i_t P[FI], Q[FJ];
+      constexpr int FH = FI / 2;
+      v8i_t P[FH], Q[FJ];
 #pragma unroll
-      for (int it = 0; it < FI; ++it) P[it] = frag8(smem, wp * WM + it * 32);
+      for (int it = 0; it < FH; ++it) P[it] = frag8(smem, wp * WM + it * 32);
 #pragma unroll
       for (int jt = 0; jt < FJ; ++jt) Q[jt] = frag8(smem + PB, wq * WN + jt * 32);
       const int ln = opaque_i(lane);
       for (int64_t kt = 0; kt < nk; ++kt) {
+        const char* sP = smem + (kt % STAGES) * SB;
+        v8i_t P2[FH];
+#pragma unroll
+        for (int it = 0; it < FH; ++it) P2[it] = frag8(sP, wp * WM + (FH + it) * 32);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int it = 0; it < FI / 2; ++it)
+        for (int it = 0; it < FH; ++it)
 #pragma unroll
           for (int jt = 0; jt < FJ; ++jt)
             acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
-                                                                          0x7f7f7f7f, 0, 0x7f7f7f7f);
+                                                                          0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
+        // k-step kt+1 landed for this wave; after the barrier every wave has
+        // it and none reads stage kt from LDS any more
         wait_vmcnt<2 * LV>();
         lds_barrier();
         const char* nP = smem + ((kt + 1) % STAGES) * SB;
-        v8i_t Pn[FI], Qn[FJ];
-#pragma unroll
-        for (int it = 0; it < FI; ++it) Pn[it] = frag8(nP, wp * WM + it * 32);
+        v8i_t Pn[FH], Qn[FJ];
 #pragma unroll
         for (int jt = 0; jt < FJ; ++jt) Qn[jt] = frag8(nP + PB, wq * WN + jt * 32);
+#pragma unroll
+        for (int it = 0; it < FH; ++it) Pn[it] = frag8(nP, wp * WM + it * 32);
         __builtin_amdgcn_sched_barrier(0);
         const bool real = kt + STAGES < nk;
-        static_assert((FI / 2) * FJ == LT, "one MFMA per DMA slot");
+        static_assert(FH * FJ == LT, "one MFMA per DMA slot");
 #pragma unroll
         for (int q = 0; q < LT; ++q) {
-          const int it = FI / 2 + q / FJ, jt = q % FJ;
-          acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
-                                                                        0x7f7f7f7f, 0, 0x7f7f7f7f);
+          const int it = q / FJ, jt = q % FJ;
+          acc[FH + it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+              Q[jt], P2[it], acc[FH + it][jt], 0, 0, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, aoff);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int it = 0; it < FI; ++it) P[it] = Pn[it];
+        for (int it = 0; it < FH; ++it) P[it] = Pn[it];
 #pragma unroll
         for (int jt = 0; jt < FJ; ++jt) Q[jt] = Qn[jt];
       }

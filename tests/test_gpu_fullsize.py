@@ -24,6 +24,9 @@ if torch.cuda.is_available():
     from tests import layer_runner as R
 
 FULL = [c for c in synth.CONFIGS if c.backward] + [synth.CONFIG_BY_NAME["finegrained_bf16"]]
+# the benchmark's launch configuration gathers the token rows (no permuted
+# copy); the 7B-style layer also runs with the permuted copy
+CASES = [(c, True) for c in FULL] + [(synth.CONFIG_BY_NAME["moe7b_bf16"], False)]
 
 
 def _sample(T, n, seed, allowed=None):
@@ -33,9 +36,10 @@ def _sample(T, n, seed, allowed=None):
     return s
 
 
-@pytest.mark.parametrize("cfg", FULL, ids=[c.name for c in FULL])
-def test_full_size_layer(cfg):
-    print(f"[full] {cfg.name}: generating inputs", flush=True)
+@pytest.mark.parametrize("cfg,gather", CASES,
+                         ids=[c.name + ("" if gth else "-permuted-copy") for c, gth in CASES])
+def test_full_size_layer(cfg, gather):
+    print(f"[full] {cfg.name} gather={gather}: generating inputs", flush=True)
     inp = synth.make_inputs(cfg, with_dy=True)
     nsamp = 256 if cfg.T <= 16384 else 128
     desc = M.desc_from_config(cfg)
@@ -43,7 +47,7 @@ def test_full_size_layer(cfg):
     x = dev(inp["x"])
     dy = dev(inp["dy"])
     print(f"[full] {cfg.name}: GPU forward+backward", flush=True)
-    g = R.run_gpu(cfg, inp, backward=True, weights=w, x=x, dy=dy, keep_device=True)
+    g = R.run_gpu(cfg, inp, backward=True, weights=w, x=x, dy=dy, keep_device=True, gather=gather)
     g_logits = g["saved"]["logits"].cpu().numpy()
     g_idx = g["saved"]["idx"].cpu().numpy()
     counts = g["saved"]["counts"].cpu().numpy()
