@@ -54,7 +54,7 @@ def parse():
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_moe7b_bf16_traffic.txt")
 # the routed gate/up product: forward layout, SwiGLU, bf16, rows gathered
-GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false, true>"
+GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false, true, 8>"
 KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_big.hip",
                   "mixture_experts_layer_18_amd/csrc/gemm_common.h",
                   "mixture_experts_layer_18_amd/csrc/common.h",

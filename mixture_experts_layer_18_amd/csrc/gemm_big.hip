@@ -8,11 +8,16 @@
 //   TN  C[g,n,k] = sum_{m in g} A[m,n] B[m,k]   weight gradient
 //
 // Why this shape (measured on MI355X):
-//  * one 4-wave workgroup per CU, each wave owning 128 x 128 outputs (256
-//    fp32 accumulators in AGPRs): per flop this moves a third fewer bytes
-//    through the global->LDS DMA path and through LDS reads than two
-//    128 x 256 workgroups per CU, and those two paths are what limits the
-//    matrix cores once the accumulator loop is tight;
+//  * one workgroup per CU owning a 256 x 256 tile: the largest tile whose
+//    fp32 accumulators fit the CU's registers, so the fewest operand bytes
+//    per flop through the global->LDS DMA path and the LDS reads;
+//  * 8 waves, two per SIMD, each owning 128 x 64 outputs (128 accumulators):
+//    with one wave per SIMD (4 waves of 128 x 128) every DMA instruction
+//    stalls that wave's MFMA issue for ~25 cycles (a probe: 32 MFMAs take
+//    508 ns alone, 603 ns with 8 DMA instructions among them); with two
+//    waves per SIMD one wave's DMA issue overlaps the other's MFMAs.  This
+//    costs 1.5x the LDS fragment reads and measured 7-19 % faster per
+//    product (TN most);
 //  * four 32-deep LDS stages (128 KB), three in flight;
 //  * one barrier per k-step, placed between its two 16-deep halves: before
 //    it the wave runs the first half's MFMAs while the second half's
@@ -46,15 +51,28 @@ namespace moe {
 namespace pk {
 using namespace gk;
 
-constexpr int TM = 256, TN = 256, BK = 32, STAGES = 4, NW = 4;
-constexpr int WM = 128, WN = 128, FI = WM / 32, FJ = WN / 32;
+constexpr int TM = 256, TN = 256, BK = 32, STAGES = 4;
 constexpr int PB = TM * BK * 2, QB = TN * BK * 2, SB = PB + QB;
-constexpr int LP = PB / (1024 * NW), LQ = QB / (1024 * NW), LT = LP + LQ;
 constexpr int KRB = BK * 2;                    // row bytes, reduction-contiguous layout
 constexpr int SRB = TM * 2;                    // row bytes, reduction-strided layout
-constexpr int PAD_BYTES = LT * 256;            // scratch LDS for the 4-byte pads
 static_assert(TM == TN, "one strided row width");
-static_assert((FI * FJ) % LT == 0, "MFMAs per DMA slot");
+
+// Wave layout of the 256 x 256 tile.  4 waves: 2 x 2 waves of 128 x 128
+// (256 accumulators each, one wave per SIMD).  8 waves: 2 x 4 waves of
+// 128 x 64 (128 accumulators, two waves per SIMD): a wave's DMA issue then
+// overlaps the other wave's MFMAs, for 1.5x the LDS fragment reads.
+template <int NW_>
+struct Waves {
+  static constexpr int NW = NW_;
+  static constexpr int WM = 128, WN = (NW_ == 4) ? 128 : 64;
+  static constexpr int WPR = TN / WN;          // waves along a tile row
+  static constexpr int FI = WM / 32, FJ = WN / 32;
+  static constexpr int LP = PB / (1024 * NW), LQ = QB / (1024 * NW), LT = LP + LQ;
+  static constexpr int PAD_BYTES = LT * 256;   // scratch LDS for the 4-byte pads
+  static_assert(NW_ == 4 || NW_ == 8, "4 or 8 waves");
+  static_assert(WPR * (TM / WM) == NW, "waves cover the tile");
+  static_assert((FI * FJ) % LT == 0, "MFMAs per DMA slot");
+};
 
 struct Args {
   int G;
@@ -70,6 +88,31 @@ struct Args {
 };
 constexpr int RING = 8;  // GA TN: map stages held per wave
 
+// Exclusive prefix sum over the workgroup's threads (NW waves) of one value
+// per thread; *total receives the sum.
+template <int NW>
+MOE_DEV int block_scan(int v, int* scratch, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) scratch[wave] = incl;
+  __syncthreads();
+  int wbase = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const int sv = scratch[w];
+    if (w < wave) wbase += sv;
+    tot += sv;
+  }
+  __syncthreads();
+  *total = tot;
+  return wbase + incl - v;
+}
+
 struct Tile {
   int g;
   int64_t i_lo, i_hi;  // output rows (NT/NN: permuted rows of group g; TN: rows of C[g])
@@ -82,8 +125,11 @@ struct Tile {
 // matrix-core product per 32x32 tile: the f8f6f4 builtin with zero scale
 // operands, which the compiler emits as the unscaled
 // v_mfma_f32_32x32x64_f8f6f4 (one instruction, no scale prefix).
-template <int LAYOUT, int EPI, bool F8, bool GA>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
+template <int LAYOUT, int EPI, bool F8, bool GA, int NWV>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
+  using WV = Waves<NWV>;
+  constexpr int NW = WV::NW, WM = WV::WM, WN = WV::WN, WPR = WV::WPR, FI = WV::FI, FJ = WV::FJ;
+  constexpr int LP = WV::LP, LQ = WV::LQ, LT = WV::LT, PAD_BYTES = WV::PAD_BYTES;
   constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
   constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
   static_assert(!F8 || LAYOUT == MOE_GEMM_NT, "fp8 operands: forward layout only");
@@ -95,7 +141,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   constexpr int BKE = BK * 2 / ES;       // elements per k-step (64 bytes per row)
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB + PAD_BYTES];
   __shared__ int s_pref[256];
-  __shared__ int scratch[4];
+  __shared__ int scratch[NW];
   __shared__ __attribute__((aligned(256))) int ring[GT ? NW * RING * 64 : 1];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -114,7 +160,7 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   } else {
     int n = 0;
     if (tid < a.G) n = (a.offsets[tid + 1] - a.offsets[tid] + TM - 1) / TM;
-    const int ex = block_exclusive_scan256(n, scratch, &mt_total);
+    const int ex = block_scan<NW>(n, scratch, &mt_total);
     if (tid < a.G) s_pref[tid] = ex;
     __syncthreads();
     ncols = (LAYOUT == MOE_GEMM_NT) ? (EPI == MOE_EPI_SWIGLU ? N / 2 : N) : K;
@@ -310,22 +356,23 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
   };
 
   auto frag_p = [&](const char* st, int it, int ks) __attribute__((always_inline)) {
-    const int row = (wave >> 1) * WM + it * 32;
+    const int row = (wave / WPR) * WM + it * 32;
     return P_KC ? frag_kc<BK>(st, row, ks, lane) : frag_tr<SRB>(st, row, ks, lane);
   };
   auto frag_q = [&](const char* st, int jt, int ks) __attribute__((always_inline)) {
-    const int row = (wave & 1) * WN + jt * 32;
+    const int row = (wave % WPR) * WN + jt * 32;
     return Q_KC ? frag_kc<BK>(st + PB, row, ks, lane) : frag_tr<SRB>(st + PB, row, ks, lane);
   };
 
-  const int wp = wave >> 1, wq = wave & 1;
+  const int wp = wave / WPR, wq = wave % WPR;
   const int r32 = lane & 31, kh = lane >> 5;
   int L = xcd * per + slot;
   if (L >= total) return;
   Tile t = tile_of(L);
   int64_t nk = (t.r_hi - t.r_lo + BKE - 1) / BKE;
-  uint32_t aoff[LP] = {0u, 0u, 0u, 0u};
-  static_assert(LP == 4, "row offsets per lane");
+  uint32_t aoff[LP];
+#pragma unroll
+  for (int i = 0; i < LP; ++i) aoff[i] = 0u;
   {
     const int ln = opaque_i(lane);
     uint32_t gr[STAGES][LQ];
@@ -347,7 +394,9 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(Args a) {
     const bool more = Ln < total;
     Tile tn = t;
     int64_t nk_n = 0;
-    uint32_t aoff_n[LP] = {0u, 0u, 0u, 0u};
+    uint32_t aoff_n[LP];
+#pragma unroll
+    for (int i = 0; i < LP; ++i) aoff_n[i] = 0u;
     uint32_t gr_n[STAGES][LQ];
     if (GA && more) {
       tn = tile_of(Ln);
@@ -599,10 +648,12 @@ static int grid_size() {
   return n;
 }
 
-template <int LAYOUT, int EPI, bool F8 = false, bool GA = false>
+// waves per workgroup (Waves<4> is the one-wave-per-SIMD layout it replaced)
+constexpr int kWaves = 8;
+template <int LAYOUT, int EPI, bool F8 = false, bool GA = false, int NWV = kWaves>
 static hipError_t run(const Args& a, hipStream_t st) {
   if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI, F8, GA><<<dim3((unsigned)grid_size()), dim3(256), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, F8, GA, NWV><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -611,8 +662,8 @@ static hipError_t run(const Args& a, hipStream_t st) {
 // Which products this kernel takes (the rest go to the two-workgroup kernel):
 // NT with either epilogue (SwiGLU: the hidden width a multiple of 128, so that
 // a tile pairs 128 gate with 128 up columns), the plain data gradient, and the
-// weight gradient when its columns come in whole 256-wide tiles and it has
-// enough tiles to fill the chip without row slices.
+// weight gradient when it has enough 256 x 256 tiles to fill
+// the chip without row slices (gathered rows: any tile count).
 bool gemm_big_supported(const GemmProblem& p) {
   if (p.ta != MOE_BF16 || p.tb != MOE_BF16 || p.tc != MOE_BF16 || p.G > 256) return false;
   if (p.rows && p.layout == MOE_GEMM_NN) return false;
@@ -620,12 +671,16 @@ bool gemm_big_supported(const GemmProblem& p) {
     if (p.epilogue == MOE_EPI_SWIGLU) return (p.N / 2) % 128 == 0;
     return p.epilogue == MOE_EPI_NONE;
   }
-  if (p.layout == MOE_GEMM_TN) {  // whole 256-wide column tiles only (else 256 x 128 tiles waste less)
-    if (p.K % 256) return false;
-    // few tiles: row slices on the two-workgroup kernel fill the chip better,
-    // but gathered rows are read by this kernel only
-    return p.rows || p.G * cdiv64(p.N, 256) * (p.K / 256) >= 4 * 256;
+  if (p.layout == MOE_GEMM_TN) {
+      // few tiles: row slices on the two-workgroup kernel fill the chip better,
+    // but gathered rows are read by this kernel only.  A partial last column
+    // tile (K not a multiple of 256) is clamped on load and masked on store.
+    if (p.rows) return p.K % 256 == 0;
+    return p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256;
   }
+  // the dSwiGLU data gradient stays on the two-workgroup kernel, whose
+  // epilogue stages G | U through LDS: loading them per lane here measured
+  // 4-12 % slower
   if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE;
   return false;
 }

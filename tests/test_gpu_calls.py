@@ -231,10 +231,12 @@ def test_grouped_gemm_against_oracle(dtype, G, mean, N, K, layout, epi):
         assert_rounded(out, ref, dtype, "C")
 
 
-def test_weight_gradient_many_groups():
+@pytest.mark.parametrize("G,N,K", [(64, 1024, 1024), (128, 1024, 320)], ids=["whole-tiles", "partial-columns"])
+def test_weight_gradient_many_groups(G, N, K):
     """A weight gradient with enough 256 x 256 output tiles for the persistent
-    kernel: ragged groups, an empty group and one group four times the mean."""
-    G, mean, N, K = 64, 100, 1024, 1024
+    kernel: ragged groups, an empty group and one group four times the mean;
+    K = 320 leaves a partial last column tile."""
+    mean = 100
     print(f"[gemm] TN persistent G={G} N={N} K={K}", flush=True)
     off = _groups(91, G, mean, empty=(3, 40), big=17)
     Mt = int(off[-1])
