@@ -552,6 +552,17 @@ def quantize_rowwise(x):
     return q, s
 
 
+def quantize_tensorwise(x):
+    """Tensor-wise scaling: one scale s = amax / 448 over every element (fp32;
+    1 for an all-zero tensor), q = e4m3(x / s) with the division in fp32.
+    Returns (codes uint8, s as an fp32 scalar)."""
+    x32 = np.asarray(x, F32)
+    amax = np.float32(np.abs(x32).max()) if x32.size else np.float32(0.0)
+    s = np.float32(amax / np.float32(448.0)) if amax > 0 else np.float32(1.0)
+    q = e4m3_encode((x32 / s).astype(F32))
+    return q, s
+
+
 def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets):
     """C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k] over the
     decoded codes, for the rows m of group g; fp64."""

@@ -494,3 +494,32 @@ def test_e4m3_encode_matches_brute_force_nearest():
         c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
         want = c | (0x80 if v < 0 else 0)
         assert O.e4m3_encode([v])[0] == want, v
+
+
+def test_fp8_tensorwise_quantisation():
+    """One scale for the whole tensor: the largest magnitude maps to 448
+    exactly, every element is reproduced within half an e4m3 step, a
+    one-row tensor quantises as the row-wise scheme does, a power-of-two
+    rescaling of x rescales s and leaves the codes unchanged, and an all-zero
+    tensor gets s = 1 and zero codes."""
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((40, 96)) * np.exp(g.uniform(-3, 3, (40, 1)))).astype(np.float32)
+    q, s = O.quantize_tensorwise(x)
+    assert s.dtype == np.float32 and q.shape == x.shape
+    v = O.e4m3_decode(q)
+    assert np.max(np.abs(v)) == 448.0
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert abs(v[i]) == 448.0
+    # half a step: 2^-4 relative for normal values, 2^-10 absolute in the
+    # subnormal range (values below 2^-6), both in units of s, plus the fp32
+    # rounding of the quotient
+    y = x.astype(np.float64) / np.float64(s)
+    err = np.abs(v - y)
+    assert np.all(err <= np.maximum(np.abs(y) * 2.0 ** -4, 2.0 ** -10) * (1 + 1e-6))
+    q1, s1 = O.quantize_tensorwise(x[3:4])
+    qr, sr = O.quantize_rowwise(x[3:4])
+    assert s1 == sr[0] and np.array_equal(q1, qr)
+    q2, s2 = O.quantize_tensorwise(x * np.float32(8.0))
+    assert s2 == s * np.float32(8.0) and np.array_equal(q2, q)
+    qz, sz = O.quantize_tensorwise(np.zeros((3, 64), np.float32))
+    assert sz == 1.0 and not qz.any()
