@@ -312,6 +312,18 @@ int moe_bias_update(const moe_desc_t *desc, const int32_t *counts, float rate, f
 int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void *x, uint8_t *q, float *scale,
                      void *stream);
 
+/* Tensor-wise fp8 quantisation (the Apex-3 code page's "tensorwise" fp8
+ * recipe): one scale s = amax / 448 over every element of x [rows, cols]
+ * (fp32; 1 for an all-zero tensor), q[r, c] = e4m3(x[r, c] / s) as in
+ * moe_quantize_fp8.  s is written to every entry of scale [rows], so that
+ * moe_grouped_gemm_fp8 takes either scaling.
+ *   ws >= moe_quantize_fp8_tensorwise_workspace_bytes(rows) bytes of device
+ *   scratch (the row maxima and the scale)
+ * cols a multiple of 64; pointers 16-byte aligned.  Deterministic. */
+size_t moe_quantize_fp8_tensorwise_workspace_bytes(int64_t rows);
+int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const void *x, uint8_t *q,
+                                float *scale, void *ws, size_t ws_bytes, void *stream);
+
 /* fp8 grouped GEMM, forward (NT) layout, with row scales:
  *   C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k]
  * for the rows m of group g (group_offsets as in moe_grouped_gemm), fp32

@@ -156,6 +156,18 @@ def moe_quantize_fp8(x, q, scale, stream=None):
     _check(L.load().moe_quantize_fp8(rows, cols, dt, _p(x), _p(q), _p(scale), _stream(stream)), "moe_quantize_fp8")
 
 
+def moe_quantize_fp8_tensorwise(x, q, scale, ws=None, stream=None):
+    """Tensor-wise e4m3 quantisation of x [rows, cols]: one scale, written to every entry of scale [rows]."""
+    dt = L.MOE_BF16 if x.dtype == torch.bfloat16 else L.MOE_F32
+    rows, cols = x.shape[0], x.numel() // max(x.shape[0], 1)
+    need = L.load().moe_quantize_fp8_tensorwise_workspace_bytes(rows)
+    if ws is None:
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+    _check(L.load().moe_quantize_fp8_tensorwise(rows, cols, dt, _p(x), _p(q), _p(scale), _p(ws),
+                                                ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_quantize_fp8_tensorwise")
+
+
 def moe_grouped_gemm_fp8(epilogue, G, M_total, N, K, group_offsets, A, a_scale, B, b_scale, C, aux=None,
                          stream=None):
     _check(L.load().moe_grouped_gemm_fp8(EPILOGUES[epilogue], G, M_total, N, K, _p(group_offsets), _p(A),

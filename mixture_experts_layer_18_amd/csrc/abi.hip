@@ -535,6 +535,23 @@ int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void* x, uint8
   return MOE_OK;
 }
 
+size_t moe_quantize_fp8_tensorwise_workspace_bytes(int64_t rows) {
+  return rows < 0 ? 0 : quantize_fp8_tensorwise_ws_bytes(rows);
+}
+
+int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const void* x, uint8_t* q,
+                                float* scale, void* ws, size_t ws_bytes, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 64 || cols > (int64_t(1) << 24)) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scale || !ws) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale) || !aligned16(ws)) return MOE_ERR_ALIGN;
+  if (ws_bytes < quantize_fp8_tensorwise_ws_bytes(rows)) return MOE_ERR_WORKSPACE;
+  MOE_TRY(launch_quantize_fp8_tensorwise(x, dtype, rows, (int)cols, q, scale, (float*)ws,
+                                         (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
                          const int32_t* offsets, const uint8_t* A, const float* a_scale,
                          const uint8_t* B, const float* b_scale, void* C, void* aux, void* stream) {

@@ -1,56 +1,60 @@
-// Row-wise fp8 (OCP e4m3) quantisation for the fp8 expert GEMMs (gfx950).
+// fp8 (OCP e4m3) quantisation for the fp8 expert GEMMs (gfx950).
 //
 // Apex-3 code page ("What's inside": FP8 through torchao; "Run it yourself":
-// --precision fp8_rowwise); KempnerForge README ("MoE roadmap": FP8 mixed
-// precision).  Each row r of x is scaled by s_r = amax_r / 448 (fp32; 1 for
-// an all-zero row) and every element becomes e4m3(x / s_r): the division in
-// fp32, then round-to-nearest-even onto the e4m3 grid by v_cvt_pk_fp8_f32
-// (which turns values beyond 464 into NaN, so the quotient is first clamped
-// to +-448).  One wavefront per row; 16-byte loads, 8-byte stores.
+// --precision fp8_rowwise, --fp8-recipe tensorwise); KempnerForge README
+// ("MoE roadmap": FP8 mixed precision).
+//
+// Row-wise: each row r of x is scaled by s_r = amax_r / 448 (fp32; 1 for an
+// all-zero row).  Tensor-wise: one s = amax / 448 over the whole tensor (1 if
+// it is all zero), written to every row's scale so that the same scaled GEMM
+// consumes either.  Every element becomes e4m3(x / s): the division in fp32,
+// then round-to-nearest-even onto the e4m3 grid by v_cvt_pk_fp8_f32 (which
+// turns values beyond 464 into NaN, so the quotient is first clamped to
+// +-448).  One wavefront per row; 16-byte loads, 8-byte stores.  Maxima are
+// exact, so every result is deterministic.
 #include "kernels.h"
 
 namespace moe {
+namespace q8 {
+
+constexpr int V = 8;  // elements per 16-byte load (bf16) / two loads (fp32)
 
 template <typename TX>
-__global__ __launch_bounds__(256) void quantize_rowwise_kernel(const TX* __restrict__ x, int64_t R,
-                                                               int C, uint8_t* __restrict__ q,
-                                                               float* __restrict__ scale) {
-  const int lane = threadIdx.x & 63;
-  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= R) return;
-  const TX* row = x + r * C;
-  constexpr int V = 8;  // elements per 16-byte load (bf16) / two loads (fp32)
+MOE_DEV void load8(const TX* row, int c, float* f) {
+  if constexpr (sizeof(TX) == 2) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(row + c);
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+    f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+  } else {
+    const float4 a = reinterpret_cast<const float4*>(row + c)[0];
+    const float4 b = reinterpret_cast<const float4*>(row + c)[1];
+    f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
+  }
+}
+
+// max |x| over one row, the same value in every lane of the wave
+template <typename TX>
+MOE_DEV float row_amax(const TX* row, int C, int lane) {
   float amax = 0.0f;
   for (int c = lane * V; c < C; c += 64 * V) {
     float f[V];
-    if constexpr (sizeof(TX) == 2) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(row + c);
-      f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-      f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-    } else {
-      const float4 a = reinterpret_cast<const float4*>(row + c)[0];
-      const float4 b = reinterpret_cast<const float4*>(row + c)[1];
-      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    }
+    load8(row, c, f);
 #pragma unroll
     for (int u = 0; u < V; ++u) amax = fmaxf(amax, fabsf(f[u]));
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-  const float s = amax > 0.0f ? amax / 448.0f : 1.0f;
-  if (lane == 0) scale[r] = s;
-  uint8_t* qrow = q + r * C;
+  return amax;
+}
+
+MOE_DEV float scale_of(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
+
+// q = e4m3(clamp(x / s)) for one row
+template <typename TX>
+MOE_DEV void encode_row(const TX* row, int C, float s, uint8_t* qrow, int lane) {
   for (int c = lane * V; c < C; c += 64 * V) {
     float f[V];
-    if constexpr (sizeof(TX) == 2) {
-      const u32x4 v = *reinterpret_cast<const u32x4*>(row + c);
-      f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-      f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-    } else {
-      const float4 a = reinterpret_cast<const float4*>(row + c)[0];
-      const float4 b = reinterpret_cast<const float4*>(row + c)[1];
-      f[0] = a.x; f[1] = a.y; f[2] = a.z; f[3] = a.w; f[4] = b.x; f[5] = b.y; f[6] = b.z; f[7] = b.w;
-    }
+    load8(row, c, f);
 #pragma unroll
     for (int u = 0; u < V; ++u) f[u] = fminf(fmaxf(f[u] / s, -448.0f), 448.0f);
     u32x2 o;
@@ -62,14 +66,82 @@ __global__ __launch_bounds__(256) void quantize_rowwise_kernel(const TX* __restr
   }
 }
 
+template <typename TX>
+__global__ __launch_bounds__(256) void rowwise_kernel(const TX* __restrict__ x, int64_t R, int C,
+                                                      uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float s = scale_of(row_amax(x + r * C, C, lane));
+  if (lane == 0) scale[r] = s;
+  encode_row(x + r * C, C, s, q + r * C, lane);
+}
+
+// tensor-wise, pass 1: the maximum of each row
+template <typename TX>
+__global__ __launch_bounds__(256) void row_amax_kernel(const TX* __restrict__ x, int64_t R, int C,
+                                                       float* __restrict__ amax) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float m = row_amax(x + r * C, C, lane);
+  if (lane == 0) amax[r] = m;
+}
+
+// pass 2: one workgroup takes the maximum over the rows and writes the scale
+// after them
+__global__ __launch_bounds__(256) void tensor_scale_kernel(float* __restrict__ amax, int64_t R) {
+  __shared__ float sh[4];
+  float m = 0.0f;
+  for (int64_t r = threadIdx.x; r < R; r += 256) m = fmaxf(m, amax[r]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if ((threadIdx.x & 63) == 0) sh[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) amax[R] = scale_of(fmaxf(fmaxf(sh[0], sh[1]), fmaxf(sh[2], sh[3])));
+}
+
+// pass 3: every row with the tensor's scale
+template <typename TX>
+__global__ __launch_bounds__(256) void with_scale_kernel(const TX* __restrict__ x, int64_t R, int C,
+                                                         const float* __restrict__ s_ptr,
+                                                         uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int lane = threadIdx.x & 63;
+  const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= R) return;
+  const float s = *s_ptr;
+  if (lane == 0) scale[r] = s;
+  encode_row(x + r * C, C, s, q + r * C, lane);
+}
+
+}  // namespace q8
+
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,
                                hipStream_t st) {
   if (R == 0) return hipSuccess;
   const dim3 grid((unsigned)cdiv64(R, 4));
   if (dtype == MOE_BF16)
-    quantize_rowwise_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, q, scale);
+    q8::rowwise_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, q, scale);
   else
-    quantize_rowwise_kernel<float><<<grid, 256, 0, st>>>((const float*)x, R, C, q, scale);
+    q8::rowwise_kernel<float><<<grid, 256, 0, st>>>((const float*)x, R, C, q, scale);
+  return hipGetLastError();
+}
+
+size_t quantize_fp8_tensorwise_ws_bytes(int64_t R) { return (size_t)(R + 1) * sizeof(float); }
+
+hipError_t launch_quantize_fp8_tensorwise(const void* x, int dtype, int64_t R, int C, uint8_t* q,
+                                          float* scale, float* ws, hipStream_t st) {
+  if (R == 0) return hipSuccess;
+  const dim3 grid((unsigned)cdiv64(R, 4));
+  if (dtype == MOE_BF16)
+    q8::row_amax_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, ws);
+  else
+    q8::row_amax_kernel<float><<<grid, 256, 0, st>>>((const float*)x, R, C, ws);
+  q8::tensor_scale_kernel<<<1, 256, 0, st>>>(ws, R);
+  if (dtype == MOE_BF16)
+    q8::with_scale_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, ws + R, q, scale);
+  else
+    q8::with_scale_kernel<float><<<grid, 256, 0, st>>>((const float*)x, R, C, ws + R, q, scale);
   return hipGetLastError();
 }
 

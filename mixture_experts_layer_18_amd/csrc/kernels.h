@@ -41,6 +41,9 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
                            const uint8_t* B, const float* b_scale, void* C, void* aux, hipStream_t st);
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,
                                hipStream_t st);
+size_t quantize_fp8_tensorwise_ws_bytes(int64_t R);
+hipError_t launch_quantize_fp8_tensorwise(const void* x, int dtype, int64_t R, int C, uint8_t* q,
+                                          float* scale, float* ws, hipStream_t st);
 int gemm_mfma_tn_splits(const GemmProblem& p);
 size_t gemm_mfma_workspace_bytes(const GemmProblem& p);
 // out[i] = sum over p < nsplit of part[p * n + i], in order, rounded once to dtype

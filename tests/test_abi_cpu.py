@@ -174,6 +174,14 @@ def test_fp8_argument_checks(lib):
     assert lib.moe_quantize_fp8(10, 128, 7, a, a, a, None) == L.MOE_ERR_INVALID
     assert lib.moe_quantize_fp8(10, 128, L.MOE_BF16, ctypes.c_void_p((1 << 20) + 2), a, a, None) == L.MOE_ERR_ALIGN
     assert lib.moe_quantize_fp8(0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    # tensor-wise: the same checks, and the scratch size (row maxima + scale)
+    tw = lib.moe_quantize_fp8_tensorwise
+    assert lib.moe_quantize_fp8_tensorwise_workspace_bytes(10) == 44
+    assert tw(10, 100, L.MOE_BF16, a, a, a, a, 64, None) == L.MOE_ERR_INVALID
+    assert tw(10, 128, L.MOE_BF16, a, a, a, None, 64, None) == L.MOE_ERR_INVALID
+    assert tw(10, 128, L.MOE_BF16, a, a, a, ctypes.c_void_p((1 << 20) + 4), 64, None) == L.MOE_ERR_ALIGN
+    assert tw(10, 128, L.MOE_BF16, a, a, a, a, 40, None) == L.MOE_ERR_WORKSPACE
+    assert tw(0, 128, L.MOE_F32, None, None, None, None, 0, None) == L.MOE_OK
     # gemm: layout limits
     args = (a, a, a, a, a, a, None, None)
     assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_DSWIGLU, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID

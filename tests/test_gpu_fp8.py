@@ -41,6 +41,56 @@ def test_quantize_rowwise_bit_exact():
     assert np.array_equal(q.cpu().numpy(), qo)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_tensorwise_bit_exact(dtype):
+    g = np.random.default_rng(43)
+    xf = (g.standard_normal((257, 384)) * np.exp(g.uniform(-4, 4, (257, 1)))).astype(np.float32)
+    xf[9] = 0
+    if dtype == "bf16":
+        xb = synth.f32_to_bf16_bits(xf)
+        xv = synth.bf16_bits_to_f32(xb)
+        x = dev(xb)
+    else:
+        xv = xf
+        x = torch.from_numpy(xf).cuda()
+    q = torch.empty(x.shape[0], x.shape[1], dtype=torch.uint8, device="cuda")
+    s = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_tensorwise(x, q, s)
+    torch.cuda.synchronize()
+    qo, so = O.quantize_tensorwise(xv)
+    assert np.all(s.cpu().numpy() == so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+    # an all-zero tensor
+    z = torch.zeros(5, 64, dtype=x.dtype, device="cuda")
+    qz = torch.full((5, 64), 7, dtype=torch.uint8, device="cuda")
+    sz = torch.empty(5, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_tensorwise(z, qz, sz)
+    torch.cuda.synchronize()
+    assert np.all(sz.cpu().numpy() == 1.0) and not qz.cpu().numpy().any()
+
+
+def test_grouped_gemm_fp8_tensorwise_activations():
+    """Tensor-wise activations with row-wise weights through the same GEMM."""
+    g = np.random.default_rng(44)
+    G, N, K = 4, 256, 256
+    off = np.array([0, 90, 90, 300, 333], np.int32)
+    Mt = int(off[-1])
+    ab = _bf16(g, (Mt, K))
+    bb = _bf16(g, (G * N, K), 1 / np.sqrt(K))
+    a = dev(ab)
+    qa = torch.empty(Mt, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(Mt, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_tensorwise(a, qa, sa)
+    qb, sb = _quant_gpu(bb)
+    qao, sao = O.quantize_tensorwise(synth.bf16_bits_to_f32(ab))
+    qbo, sbo = O.quantize_rowwise(synth.bf16_bits_to_f32(bb))
+    ref = O.grouped_gemm_fp8_nt(qao, np.full(Mt, sao, np.float32), qbo.reshape(G, N, K), sbo.reshape(G, N), off)
+    C = torch.empty(Mt, N, dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm_fp8("none", G, Mt, N, K, dev(off), qa, sa, qb, sb, C)
+    torch.cuda.synchronize()
+    assert_rounded(host(C), ref, "bf16", "C")
+
+
 @pytest.mark.parametrize("epi,N", [("none", 384), ("swiglu", 512)])
 def test_grouped_gemm_fp8_against_oracle(epi, N):
     g = np.random.default_rng(42 + N)
