@@ -554,6 +554,89 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     // -------------------------------------------------------- epilogue
     bf16_t* C = a.C;
     bf16_t* X = a.aux;
+    if constexpr (EPI == MOE_EPI_DSWIGLU) {
+      // NN data gradient through SwiGLU: the product is dH; aux holds the
+      // forward pre-activations G | U ([M, 2K]); C receives
+      // dG = dH U silu'(G) | dU = dH silu(G).  Each wave brings the G and U
+      // rows of its outputs into its own 16 KB of the (now idle) LDS stages
+      // with full-row DMA, two 32-row blocks per phase, and reads them in the
+      // accumulator layout; the next tile's first stages are fetched after.
+      constexpr int RBW = WN * 2;               // bytes of one wave-tile row of G (or U)
+      constexpr int CPW = RBW / 16;             // 16-byte chunks per row
+      constexpr int RPI = 1024 / RBW;           // rows per DMA instruction
+      constexpr int NI = 32 / RPI;              // instructions per 32-row block of G (or U)
+      constexpr int WBUF = 16384;               // LDS bytes per wave
+      constexpr int IPP = WBUF / (64 * RBW);    // 32-row blocks per phase
+      static_assert(IPP >= 1 && FI % IPP == 0 && NW * WBUF <= STAGES * SB, "epilogue staging");
+      // slot of chunk c in row r: c ^ swz(r), so that the 32 rows a read
+      // instruction touches at one chunk spread over the banks
+      auto swz = [](int r) __attribute__((always_inline)) { return RBW >= 256 ? (r & 15) : ((r >> 1) & 7); };
+      const char* wbuf = smem + wave * WBUF;
+      const uint32_t wbase = smem_base + wave * WBUF;
+      const int lrow = lane / CPW, lchunk = lane % CPW;
+      const int64_t K2 = 2 * K;
+#pragma unroll
+      for (int ph = 0; ph < FI / IPP; ++ph) {
+        if (ph > 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the last phase's reads are done
+#pragma unroll
+        for (int u = 0; u < IPP; ++u)
+#pragma unroll
+          for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+            for (int q = 0; q < NI; ++q) {
+              const int r = q * RPI + lrow;
+              int64_t i = t.i_lo + wp * WM + (ph * IPP + u) * 32 + r;
+              i = i < t.i_hi ? i : t.i_hi - 1;
+              int64_t col = t.j0 + wq * WN + (int64_t)((lchunk ^ swz(r)) * 8);
+              col = col < K - 8 ? col : K - 8;
+              dma16(X + i * K2 + gu * K + col,
+                    __builtin_amdgcn_readfirstlane(wbase + ((u * 2 + gu) * NI + q) * 1024));
+            }
+        wait_vmcnt<0>();
+#pragma unroll
+        for (int u = 0; u < IPP; ++u) {
+          const int it = ph * IPP + u;
+          const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
+          const char* Gb = wbuf + (u * 2) * NI * 1024;
+          const char* Ub = Gb + NI * 1024;
+#pragma unroll
+          for (int jt = 0; jt < FJ; ++jt) {
+            const int64_t c = t.j0 + wq * WN + jt * 32;
+            float dG[16], dU[16];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int off = r32 * RBW + (((jt * 4 + gq) ^ swz(r32)) << 4) + kh * 8;
+              const u32x2 gw = *reinterpret_cast<const u32x2*>(Gb + off);
+              const u32x2 uw = *reinterpret_cast<const u32x2*>(Ub + off);
+              const float Gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
+              const float Uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float sg = sigmoid_f(Gv[e]);
+                const float dh = acc[it][jt][gq * 4 + e];
+                dG[gq * 4 + e] = dh * Uv[e] * sg * (1.0f + Gv[e] * (1.0f - sg));
+                dU[gq * 4 + e] = dh * Gv[e] * sg;
+              }
+            }
+            if (i < t.i_hi && c < K) {
+              store_tile_row(C + i * K2 + c, dG, kh, K - c);
+              store_tile_row(C + i * K2 + K + c, dU, kh, K - c);
+            }
+          }
+        }
+      }
+      // every wave is done reading its staging area before the next tile's
+      // stages overwrite it
+      lds_barrier();
+      prefetch_next();
+      if (!more) break;
+      L = Ln;
+      t = tn;
+      nk = nk_n;
+#pragma unroll
+      for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
+      continue;
+    }
     prefetch_next();
     // fp8: the row scale of this lane's output row per row block, and the
     // column scales of the 16 columns a lane holds in a 32-wide block
@@ -678,10 +761,7 @@ bool gemm_big_supported(const GemmProblem& p) {
     if (p.rows) return p.K % 256 == 0;
     return p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256;
   }
-  // the dSwiGLU data gradient stays on the two-workgroup kernel, whose
-  // epilogue stages G | U through LDS: loading them per lane here measured
-  // 4-12 % slower
-  if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE;
+  if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE || p.epilogue == MOE_EPI_DSWIGLU;
   return false;
 }
 
@@ -710,6 +790,8 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE>(a, st);
   if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU>(a, st);
   if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NN, MOE_EPI_NONE>(a, st);
+  if (p.layout == MOE_GEMM_NN && p.epilogue == MOE_EPI_DSWIGLU)
+    return pk::run<MOE_GEMM_NN, MOE_EPI_DSWIGLU>(a, st);
   if (p.layout == MOE_GEMM_TN && p.epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_TN, MOE_EPI_NONE>(a, st);
   return hipErrorInvalidValue;
 }
