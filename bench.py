@@ -359,7 +359,9 @@ def main():
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
     del cbuf, cdst
     fp8 = fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, fl_gu, t_gu) if not args.no_fp8 else None
-    hbm3 = ["route", "permute", "combine"]
+    # the streaming memory-bound stages (route and the index-only permute are
+    # latency-bound at these sizes)
+    hbm3 = ["combine", "combine_bwd", "unpermute_sum"]
     hbm3_us = sum(stage_out[n]["us"] for n in hbm3)
     hbm3_gbs = sum(hbm_bytes[n] for n in hbm3) / (hbm3_us * 1e-6) / 1e9
 
@@ -396,7 +398,7 @@ def main():
             "tflops": fwd_tflops, "frac_of_peak": fwd_tflops / PEAK_BF16_TFLOPS,
             "gate_up_us": t_gu * 1e6, "down_us": t_dn * 1e6,
         },
-        "route_permute_combine_hbm": {"gbs": hbm3_gbs, "frac": hbm3_gbs / PEAK_HBM_GBS, "us": hbm3_us,
+        "combine_stages_hbm": {"stages": hbm3, "gbs": hbm3_gbs, "frac": hbm3_gbs / PEAK_HBM_GBS, "us": hbm3_us,
                                       "frac_of_copy": hbm3_gbs / copy_gbs},
         "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                              "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
