@@ -72,3 +72,37 @@ def test_zero_tokens_is_a_noop():
     g = R.run_gpu(cfg, inp, backward=True)
     assert np.all(g["counts"] == 0) and np.all(g["offsets"] == 0)
     assert np.all(g["d_w_gateup"] == 0) and np.all(g["d_w_router"] == 0)
+
+
+# ----------------------------------------------------------------------------- limits and degenerate routings
+@pytest.mark.parametrize("gather", [False, True], ids=["permuted-copy", "gathered"])
+def test_maximum_experts_and_top_k(gather):
+    """E = 256 experts (the most the router and the grouped GEMMs take) with
+    top-16: 256 small groups, some of them empty."""
+    cfg = SMALL_BF16.replace(name="max_ek", T=700, d=256, E=256, k=16, f=128, n_shared=1, f_shared=128)
+    print(f"[layer] E=256 k=16 gather={gather}", flush=True)
+    g, fw, bw, same = R.compare_full(cfg, synth.make_inputs(cfg), backward=True, gather=gather, degenerate=True)
+    assert g["counts"].sum() == cfg.T * cfg.k
+
+
+def test_single_token():
+    cfg = SMALL_BF16.replace(name="one_token", T=1)
+    print("[layer] one token", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=True, degenerate=True)
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["permuted-copy", "gathered"])
+def test_every_token_to_one_expert(gather):
+    """A selection bias far above every score sends all tokens to expert 2
+    (top-1): one group holds every row, the others are empty, and the gates
+    renormalise to exactly 1."""
+    cfg = SMALL_BF16.replace(name="one_expert", T=900, d=256, E=8, k=1, f=256, n_shared=0, f_shared=0)
+    inp = synth.make_inputs(cfg)
+    inp["bias"] = np.zeros(cfg.E, np.float32)
+    inp["bias"][2] = 10.0
+    print(f"[layer] every token to one expert gather={gather}", flush=True)
+    g, fw, bw, same = R.compare_full(cfg, inp, backward=True, gather=gather, degenerate=True)
+    assert g["counts"][2] == cfg.T and g["counts"].sum() == cfg.T
+    assert np.all(g["gate"] == 1.0)
+    empty = [e for e in range(cfg.E) if e != 2]
+    assert np.all(g["d_w_gateup"][empty] == 0) and np.all(g["d_w_down"][empty] == 0)
