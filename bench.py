@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--pmc-probe", action="store_true",
                    help="run one forward, one 1 GiB device copy and one gate/up GEMM launch, then exit "
                         "(the program that rocprofv3 --pmc passes count)")
+    p.add_argument("--trace-summarize", metavar="TRACE_DIR",
+                   help="write the kernel-trace summary of a profiled run (rocprofv3 --kernel-trace --stats "
+                        "--output-format csv -o bench) to profiles/moe7b_bf16_fwd_bwd_kernel_stats.txt")
     p.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn the counter CSVs of a FETCH_SIZE pass and a WRITE_SIZE pass over "
                         "--pmc-probe into the traffic record under profiles/")
@@ -94,6 +97,68 @@ def _probe_values(rows, counter):
         raise SystemExit(f"no device copy dispatch before the GEMM with {counter}")
     c = max(copies, key=lambda r: int(r["Dispatch_Id"]))
     return float(c["Counter_Value"]) * 1024.0, float(g["Counter_Value"]) * 1024.0
+
+
+TRACE_COMMAND = ("rocprofv3 --kernel-trace --stats --output-format csv -d <root>/gpurun_out/prof -o bench -- "
+                 "python3 <root>/bench.py --steps 5 --warmup 2 --no-cpu-baseline")
+
+
+def trace_summarize(d):
+    """Per-kernel statistics of a profiled bench run, and the same trace cut
+    into layer steps (each step starts at a router-logits launch), one line
+    per launch position within a step."""
+    import collections
+    import csv
+    stats = list(csv.DictReader(open(os.path.join(d, "bench_kernel_stats.csv"))))
+    trace = list(csv.DictReader(open(os.path.join(d, "bench_kernel_trace.csv"))))
+    trace.sort(key=lambda r: int(r["Start_Timestamp"]))
+    dur = lambda r: (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3  # noqa: E731
+    short = lambda r: r["Kernel_Name"].split("(")[0].replace("void ", "")  # noqa: E731
+    L = ["Kernel durations of the MoE layer forward+backward, moe7b_bf16 (T=16384, d_model=2048, E=64, "
+         "sigmoid top-6, d_ff=1408, 2 shared x 1408), bf16, one MI355X; 5 timed + 2 warm-up steps", "",
+         "Commands (from the repository root):", "  cd /tmp && export TMPDIR=/tmp", "  " + TRACE_COMMAND,
+         "  python bench.py --trace-summarize gpurun_out/prof", "", "rocprofv3 --stats (per kernel symbol):", ""]
+    L.append(f"{'kernel':<92s} {'calls':>5s} {'avg us':>9s} {'min us':>9s} {'max us':>9s} {'%':>6s}")
+    for r in stats:
+        L.append(f"{r['Name'][:92]:<92s} {int(r['Calls']):5d} {float(r['AverageNs'])/1e3:9.1f} "
+                 f"{float(r['MinNs'])/1e3:9.1f} {float(r['MaxNs'])/1e3:9.1f} {float(r['Percentage']):6.2f}")
+    steps, cur = [], None
+    for r in trace:
+        if "router_logits_kernel" in r["Kernel_Name"]:
+            cur = []
+            steps.append(cur)
+        if cur is not None:
+            cur.append(r)
+    # the last step also holds the launches after the timed steps (the
+    # separate measurements); cut it to the length of the first step
+    after = []
+    if len(steps) > 1 and len(steps[-1]) > len(steps[0]):
+        after = steps[-1][len(steps[0]):]
+        steps[-1] = steps[-1][:len(steps[0])]
+    agg = collections.OrderedDict()
+    for st in steps:
+        seen = collections.Counter()
+        for r in st:
+            seen[short(r)] += 1
+            agg.setdefault(f"{short(r)} #{seen[short(r)]}", []).append(dur(r))
+    L += ["", f"Same trace, one line per launch of a step ({len(steps)} steps; #n = n-th launch of that",
+          "kernel within the step, in launch order):", ""]
+    L.append(f"{'kernel #occurrence':<70s} {'calls':>5s} {'avg us':>9s} {'min us':>9s}")
+    for k, v in agg.items():
+        L.append(f"{k[:70]:<70s} {len(v):5d} {sum(v)/len(v):9.1f} {min(v):9.1f}")
+    if after:
+        aft = collections.OrderedDict()
+        for r in after:
+            aft.setdefault(short(r), []).append(dur(r))
+        L += ["", "Launches after the layer steps (the separate measurements: the copy-ceiling",
+              "copies and the fp8 gate/up product with its activation quantisation):", ""]
+        L.append(f"{'kernel':<70s} {'calls':>5s} {'avg us':>9s} {'min us':>9s}")
+        for k, v in aft.items():
+            L.append(f"{k[:70]:<70s} {len(v):5d} {sum(v)/len(v):9.1f} {min(v):9.1f}")
+    out = os.path.join(ROOT, "profiles", "moe7b_bf16_fwd_bwd_kernel_stats.txt")
+    with open(out, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("wrote", out)
 
 
 def pmc_summarize(fetch_dir, write_dir):
@@ -200,6 +265,9 @@ def fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, flop, bf16_s):
 
 def main():
     args = parse()
+    if args.trace_summarize:
+        trace_summarize(args.trace_summarize)
+        return
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize)
         return
