@@ -1,13 +1,21 @@
-// Router products in fp32 on the gfx950 matrix cores (v_mfma_f32_32x32x2_f32).
+// Router products in fp32 on the gfx950 matrix cores.
 //
 // The router runs in fp32 (Ultimate MoE Training Handbook, section 2.5, the
 // fp32 router dtype): the logits l = x W_r^T and the weight gradient
 // dW_r = dl^T x are fp32 products with fp32 accumulation of a bf16 or fp32 x
 // against the fp32 router weight.  E <= 256 experts makes these thin GEMMs:
-//  * forward: a workgroup (4 waves) computes 64 tokens x 64 experts; each wave
-//    one 32 x 32 tile, the reduction over d staged through LDS in 32-deep
-//    steps (x widened to fp32 on its way in), next step prefetched into
+//  * forward, fp32 x: a workgroup (4 waves) computes 64 tokens x 64 experts
+//    on v_mfma_f32_32x32x2_f32; each wave one 32 x 32 tile, the reduction
+//    over d staged through LDS in 32-deep steps, next step prefetched into
 //    registers;
+//  * forward, bf16 x: the same tiles on the bf16 matrix cores.  Each fp32
+//    weight is split into three bf16 parts, w = hi + mid + lo exactly (each
+//    part takes the next 8 significant bits of what the previous left, with
+//    round-to-nearest), so x w = x hi + x mid + x lo where every product of
+//    two bf16 values is exact in fp32, and the sum is accumulated in fp32:
+//    the fp32 product up to the order of the fp32 additions, at the bf16
+//    matrix-core rate (three 32x32x16 MFMAs per 16-deep step against eight
+//    32x32x2 fp32 ones);
 //  * weight gradient: a workgroup computes 64 experts x 64 columns of d over
 //    a slice of the tokens; slices are summed afterwards in a fixed order, so
 //    the result is deterministic.
@@ -85,6 +93,116 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const TX* __restrict
   }
 }
 
+// logits[T, E] = x[T, d] . W_r[E, d]^T for bf16 x, 64-deep steps.  LDS holds
+// per step x [64][64] and the three parts of W [3][64][64] as bf16 rows of
+// 128 bytes whose 16-byte chunks are XOR-swizzled by row; two buffers, one
+// barrier per step.
+constexpr int SBK = 64;                         // reduction step (bf16 path)
+constexpr int SROW = SBK * 2;                   // bytes per LDS row
+constexpr int STILE = 64 * SROW;                // one 64-row tile (8 KB)
+
+MOE_DEV int sw_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
+
+__global__ __launch_bounds__(256) void router_logits_split_kernel(const bf16_t* __restrict__ x,
+                                                                  const float* __restrict__ w, int T,
+                                                                  int d, int E,
+                                                                  float* __restrict__ logits) {
+  __shared__ __attribute__((aligned(16))) char sm[2][4 * STILE];  // [buffer][x, hi, mid, lo]
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  // loader: thread -> row tid/4, 16 consecutive k at (tid%4)*16 (two 16-byte chunks)
+  const int lr = tid >> 2, lc = (tid & 3) * 2;
+  const int tr = min(t0 + lr, T - 1), er = min(e0 + lr, E - 1);
+  const bf16_t* xp = x + (int64_t)tr * d + lc * 8;
+  const float* wp = w + (int64_t)er * d + lc * 8;
+  // two steps of operands in flight in registers (sets 0 and 1); plain
+  // vector variables, no arrays, so that they stay in registers
+  struct Ops {
+    u32x4 x0, x1;
+    float4 w0, w1, w2, w3;
+  };
+  Ops o0, o1;
+  // past the end the last step is reloaded (not used): no branch in the loop
+  auto gload = [&](int k0, Ops& o) __attribute__((always_inline)) {
+    k0 = k0 < d ? k0 : d - SBK;
+    const u32x4* xq = reinterpret_cast<const u32x4*>(xp + k0);
+    const float4* wq = reinterpret_cast<const float4*>(wp + k0);
+    o.x0 = xq[0];
+    o.x1 = xq[1];
+    o.w0 = wq[0];
+    o.w1 = wq[1];
+    o.w2 = wq[2];
+    o.w3 = wq[3];
+  };
+  // three-way split of 4 weights into packed bf16 pairs: hi, mid, lo
+  auto split4 = [](float4 v, u32x2& h, u32x2& m, u32x2& l) __attribute__((always_inline)) {
+    h.x = pack_bf16x2(v.x, v.y);
+    h.y = pack_bf16x2(v.z, v.w);
+    const float r0 = v.x - bf16_lo(h.x), r1 = v.y - bf16_hi(h.x);
+    const float r2 = v.z - bf16_lo(h.y), r3 = v.w - bf16_hi(h.y);
+    m.x = pack_bf16x2(r0, r1);
+    m.y = pack_bf16x2(r2, r3);
+    l.x = pack_bf16x2(r0 - bf16_lo(m.x), r1 - bf16_hi(m.x));
+    l.y = pack_bf16x2(r2 - bf16_lo(m.y), r3 - bf16_hi(m.y));
+  };
+  auto put = [&](char* buf, int chunk, u32x4 xv, float4 wa, float4 wb) __attribute__((always_inline)) {
+    u32x2 ha, ma, la, hb, mb, lb;
+    split4(wa, ha, ma, la);
+    split4(wb, hb, mb, lb);
+    const int off = lr * SROW + (sw_slot(lr, chunk) << 4);
+    *reinterpret_cast<u32x4*>(buf + off) = xv;
+    *reinterpret_cast<u32x4*>(buf + STILE + off) = u32x4{ha.x, ha.y, hb.x, hb.y};
+    *reinterpret_cast<u32x4*>(buf + 2 * STILE + off) = u32x4{ma.x, ma.y, mb.x, mb.y};
+    *reinterpret_cast<u32x4*>(buf + 3 * STILE + off) = u32x4{la.x, la.y, lb.x, lb.y};
+  };
+  auto lstore = [&](char* buf, const Ops& o) __attribute__((always_inline)) {
+    put(buf, lc, o.x0, o.w0, o.w1);
+    put(buf, lc + 1, o.x1, o.w2, o.w3);
+  };
+  const int wt = wave >> 1, we = wave & 1;  // this wave's 32-token x 32-expert tile
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  const int xr = wt * 32 + (lane & 31), wr = we * 32 + (lane & 31);
+  auto compute = [&](const char* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < SBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(buf + xr * SROW + (sw_slot(xr, c) << 4));
+#pragma unroll
+      for (int part = 1; part <= 3; ++part) {
+        const bf16x8_t bw =
+            *reinterpret_cast<const bf16x8_t*>(buf + part * STILE + wr * SROW + (sw_slot(wr, c) << 4));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bw, acc, 0, 0, 0);
+      }
+    }
+  };
+  // steps in pairs so that each register set has a fixed name: step j uses
+  // set j % 2 and LDS buffer j % 2; the loads of step j + 2 are issued while
+  // step j is computed
+  // d is a multiple of 2 * SBK (the launcher sends other widths to the fp32 kernel)
+  gload(0, o0);
+  gload(SBK, o1);
+  for (int k0 = 0; k0 < d; k0 += 2 * SBK) {
+    lstore(sm[0], o0);
+    __syncthreads();
+    gload(k0 + 2 * SBK, o0);
+    compute(sm[0]);
+    lstore(sm[1], o1);
+    __syncthreads();
+    gload(k0 + 3 * SBK, o1);
+    compute(sm[1]);
+  }
+  // lane: expert (lane%32) of the wave tile, tokens (v/4)*8 + (lane/32)*4 + v%4
+  const int e = e0 + we * 32 + (lane & 31);
+  if (e >= E) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int t = t0 + wt * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    if (t < T) logits[(int64_t)t * E + e] = acc[v];
+  }
+}
+
 // part[s][E][d] = sum over tokens of slice s of dl[t, e] x[t, :]
 template <typename TX>
 __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restrict__ dl,
@@ -149,7 +267,9 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T,
                                 float* logits, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv64(T, 64), (unsigned)cdiv64(E, 64)), block(256);
-  if (dtype == MOE_BF16)
+  if (dtype == MOE_BF16 && d % (2 * rt::SBK) == 0)
+    rt::router_logits_split_kernel<<<grid, block, 0, st>>>((const bf16_t*)x, w, T, d, E, logits);
+  else if (dtype == MOE_BF16)
     rt::router_logits_kernel<bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, w, T, d, E, logits);
   else
     rt::router_logits_kernel<float><<<grid, block, 0, st>>>((const float*)x, w, T, d, E, logits);

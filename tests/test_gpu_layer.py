@@ -106,3 +106,11 @@ def test_every_token_to_one_expert(gather):
     assert np.all(g["gate"] == 1.0)
     empty = [e for e in range(cfg.E) if e != 2]
     assert np.all(g["d_w_gateup"][empty] == 0) and np.all(g["d_w_down"][empty] == 0)
+
+
+def test_forward_bf16_width_not_multiple_of_128():
+    """d = 192: the bf16 router product falls back to the fp32 matrix cores
+    (the split-weight kernel steps 128 columns at a time)."""
+    cfg = SMALL_BF16.replace(name="d192", T=300, d=192)
+    print("[layer] bf16 d=192 fwd", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=False)
