@@ -124,7 +124,7 @@ def trace_summarize(d):
                  f"{float(r['MinNs'])/1e3:9.1f} {float(r['MaxNs'])/1e3:9.1f} {float(r['Percentage']):6.2f}")
     steps, cur = [], None
     for r in trace:
-        if "router_logits_kernel" in r["Kernel_Name"]:
+        if "router_logits" in r["Kernel_Name"]:
             cur = []
             steps.append(cur)
         if cur is not None:
@@ -375,6 +375,7 @@ def main():
     }
     sh = 2 * d if F else 0
     hbm_bytes = {
+        "router": T * (2 * d + 4 * E),                                # x in, logits out
         "route": T * (4 * E + 8 * k),                                 # logits in; idx, gate out
         # idx in; pos, src, tok out (and with a permuted copy: x in, x_perm out)
         "permute": T * (16 * k + (0 if gather else 2 * d * (1 + k))),
@@ -402,7 +403,11 @@ def main():
             continue
         us = ms * 1e3 / n
         e = {"us": us, "launches": n}
-        if name in flops:
+        if name == "router" and cfg.dtype == "bf16":
+            # the fp32 product on the bf16 matrix cores (three exact partial
+            # products per term): bound by streaming x, rated against HBM
+            e.update(tflops=flops[name] / (us * 1e-6) / 1e12)
+        elif name in flops:
             tf = flops[name] / (us * 1e-6) / 1e12
             peak = 157.3 if name.startswith("router") else PEAK_BF16_TFLOPS
             e.update(tflops=tf, frac=tf / peak)
