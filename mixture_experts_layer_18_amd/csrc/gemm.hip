@@ -7,9 +7,12 @@
 // SwiGLU activation, and the data-gradient of the down product is fused with
 // the SwiGLU derivative.
 //
-// Two kernel families share one tile scheduler:
-//  * bf16 operands: matrix-core kernels (gemm_mfma.hip);
-//  * fp32 operands (and the fp32 router GEMMs): 64x64x16 FMA tiles (here).
+// The dispatcher below picks the kernel of each product:
+//  * bf16 operands: the persistent 256 x 256 matrix-core kernel
+//    (gemm_big.hip) where it takes the product, else the two-workgroup
+//    matrix-core kernel (gemm_mfma.hip: the weight gradients with few output
+//    tiles, as row slices);
+//  * fp32 operands: 64x64x16 FMA tiles (here).
 //
 // Rows of a group form a ragged M dimension: M-tiles are enumerated group
 // after group from the device-side offsets, so nothing is copied to the host
