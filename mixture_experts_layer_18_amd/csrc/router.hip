@@ -18,7 +18,8 @@
 //    32x32x2 fp32 ones);
 //  * weight gradient: a workgroup computes 64 experts x 64 columns of d over
 //    a slice of the tokens; slices are summed afterwards in a fixed order, so
-//    the result is deterministic.
+//    the result is deterministic.  For bf16 x on the bf16 matrix cores with
+//    dlogits split the same way (below); for fp32 x on the fp32 ones.
 #include "kernels.h"
 
 namespace moe {
@@ -254,6 +255,96 @@ __global__ __launch_bounds__(256) void router_wgrad_kernel(const float* __restri
   }
 }
 
+// part[s][E][d] for bf16 x on the bf16 matrix cores: dl (fp32) is split
+// exactly into three bf16 parts as the weight is in the forward, so every
+// partial product is exact and the sums accumulate in fp32.  Per 32-token
+// step LDS holds the three parts of dl as [64 experts][32 tokens] and x as
+// [64 columns][32 tokens] (bf16, 64-byte rows, 16-byte chunks XOR-swizzled
+// by row): the token axis is the reduction, so both operands are stored
+// transposed.  Loads run along experts (columns), 8 (4) bytes per lane.
+constexpr int WBK = 32;                          // tokens per step
+constexpr int WROW = WBK * 2;                    // bytes per LDS row
+constexpr int WTILE = 64 * WROW;                 // one 64-row tile (4 KB)
+
+MOE_DEV int wslot(int r, int c) { return c ^ ((r >> 2) & 3); }
+
+__global__ __launch_bounds__(256) void router_wgrad_split_kernel(const float* __restrict__ dl,
+                                                                 const bf16_t* __restrict__ x, int T,
+                                                                 int d, int E, int tok_per_split,
+                                                                 float* __restrict__ part) {
+  __shared__ __attribute__((aligned(16))) char sm[4 * WTILE];  // dl hi, mid, lo; x
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c0 = blockIdx.x * 64, e0 = blockIdx.y * 64, s = blockIdx.z;
+  const int tlo = s * tok_per_split, thi = min(T, tlo + tok_per_split);
+  // loader: thread -> a pair of experts (columns) p = tid % 32 and four
+  // consecutive tokens q*4 .. q*4+3 with q = tid / 32
+  const int p = tid & 31, q = tid >> 5;
+  const int ep = min(e0 + 2 * p, E - 2);          // E is even (>= 2) on this path
+  const int cp = c0 + 2 * p;
+  const int we = wave >> 1, wc = wave & 1;        // this wave's 32-expert x 32-column tile
+  f32x16_t acc;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+  for (int tb = tlo; tb < thi; tb += WBK) {
+    float2 dv[4];
+    uint32_t xv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = tb + q * 4 + u;
+      if (t < thi) {
+        dv[u] = *reinterpret_cast<const float2*>(dl + (int64_t)t * E + ep);
+        xv[u] = *reinterpret_cast<const uint32_t*>(x + (int64_t)t * d + cp);
+      } else {
+        dv[u] = float2{0.0f, 0.0f};
+        xv[u] = 0u;
+      }
+    }
+    // experts beyond E (a partial expert block) contribute zero
+    const bool e_ok0 = e0 + 2 * p < E, e_ok1 = e0 + 2 * p + 1 < E;
+    __syncthreads();  // the previous step's fragments have been read
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      // the four tokens of expert (column) 2p + h, split and packed
+      float f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) f[u] = (h ? (e_ok1 ? dv[u].y : 0.0f) : (e_ok0 ? dv[u].x : 0.0f));
+      const uint32_t h0 = pack_bf16x2(f[0], f[1]), h1 = pack_bf16x2(f[2], f[3]);
+      const float r0 = f[0] - bf16_lo(h0), r1 = f[1] - bf16_hi(h0);
+      const float r2 = f[2] - bf16_lo(h1), r3 = f[3] - bf16_hi(h1);
+      const uint32_t m0 = pack_bf16x2(r0, r1), m1 = pack_bf16x2(r2, r3);
+      const uint32_t l0 = pack_bf16x2(r0 - bf16_lo(m0), r1 - bf16_hi(m0));
+      const uint32_t l1 = pack_bf16x2(r2 - bf16_lo(m1), r3 - bf16_hi(m1));
+      const uint32_t xa = h ? (xv[0] >> 16) | (xv[1] & 0xffff0000u) : (xv[0] & 0xffffu) | (xv[1] << 16);
+      const uint32_t xb = h ? (xv[2] >> 16) | (xv[3] & 0xffff0000u) : (xv[2] & 0xffffu) | (xv[3] << 16);
+      const int r = 2 * p + h;
+      const int off = r * WROW + (wslot(r, q >> 1) << 4) + (q & 1) * 8;
+      *reinterpret_cast<u32x2*>(sm + off) = u32x2{h0, h1};
+      *reinterpret_cast<u32x2*>(sm + WTILE + off) = u32x2{m0, m1};
+      *reinterpret_cast<u32x2*>(sm + 2 * WTILE + off) = u32x2{l0, l1};
+      *reinterpret_cast<u32x2*>(sm + 3 * WTILE + off) = u32x2{xa, xb};
+    }
+    __syncthreads();
+    const int ar = we * 32 + (lane & 31), br = wc * 32 + (lane & 31);
+#pragma unroll
+    for (int ks = 0; ks < WBK / 16; ++ks) {
+      const int c = ks * 2 + (lane >> 5);
+      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(sm + 3 * WTILE + br * WROW + (wslot(br, c) << 4));
+#pragma unroll
+      for (int pt = 0; pt < 3; ++pt) {
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sm + pt * WTILE + ar * WROW + (wslot(ar, c) << 4));
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+      }
+    }
+  }
+  // lane: column (lane%32) of the wave tile, experts (v/4)*8 + (lane/32)*4 + v%4
+  const int col = c0 + wc * 32 + (lane & 31);
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int e = e0 + we * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+    if (e < E) part[((int64_t)s * E + e) * d + col] = acc[v];
+  }
+}
+
 }  // namespace rt
 
 int router_wgrad_splits(int T, int d, int E) {
@@ -282,7 +373,9 @@ hipError_t launch_router_wgrad(const float* dl, const void* x, int dtype, int T,
   const int per = (int)cdiv64(T > 0 ? T : 1, S);
   dim3 grid((unsigned)cdiv64(d, 64), (unsigned)cdiv64(E, 64), (unsigned)S), block(256);
   float* out = S > 1 ? part : dw;
-  if (dtype == MOE_BF16)
+  if (dtype == MOE_BF16 && E % 2 == 0)
+    rt::router_wgrad_split_kernel<<<grid, block, 0, st>>>(dl, (const bf16_t*)x, T, d, E, per, out);
+  else if (dtype == MOE_BF16)
     rt::router_wgrad_kernel<bf16_t><<<grid, block, 0, st>>>(dl, (const bf16_t*)x, T, d, E, per, out);
   else
     rt::router_wgrad_kernel<float><<<grid, block, 0, st>>>(dl, (const float*)x, T, d, E, per, out);
