@@ -114,3 +114,11 @@ def test_forward_bf16_width_not_multiple_of_128():
     cfg = SMALL_BF16.replace(name="d192", T=300, d=192)
     print("[layer] bf16 d=192 fwd", flush=True)
     R.compare_full(cfg, synth.make_inputs(cfg), backward=False)
+
+
+def test_backward_bf16_odd_expert_count():
+    """E = 7: the bf16 router weight gradient falls back to the fp32 matrix
+    cores (the split kernel loads expert pairs)."""
+    cfg = SMALL_BF16.replace(name="e7", T=300, E=7, k=2, f=128, n_shared=0, f_shared=0)
+    print("[layer] bf16 E=7 fwd+bwd", flush=True)
+    R.compare_full(cfg, synth.make_inputs(cfg), backward=True)
