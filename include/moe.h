@@ -182,6 +182,18 @@ size_t moe_route_hist_elems(const moe_desc_t *desc);
 /* Bytes of device workspace the named call needs (0 if desc is invalid). */
 size_t moe_workspace_bytes(const moe_desc_t *desc, int which);
 
+/* The saved buffers of moe_forward (moe_saved_t) in one caller allocation.
+ * flags: MOE_SAVED_TRAINING keeps the pre-activations the backward needs
+ * (preact, s_preact); MOE_SAVED_PERMUTED_COPY keeps x_perm (else the
+ * gate/up products gather the token rows through tok).
+ *   moe_saved_bytes: bytes of that allocation (0 if desc or flags are invalid)
+ *   moe_saved_carve: fills *saved with 256-byte aligned fields inside base
+ *     (fields the flags leave out are NULL); base 256-byte aligned, bytes >=
+ *     moe_saved_bytes(desc, flags); no device access. */
+enum { MOE_SAVED_TRAINING = 1, MOE_SAVED_PERMUTED_COPY = 2 };
+size_t moe_saved_bytes(const moe_desc_t *desc, int flags);
+int moe_saved_carve(const moe_desc_t *desc, int flags, void *base, size_t bytes, moe_saved_t *saved);
+
 /* Bytes of device workspace moe_grouped_gemm needs for this problem. */
 size_t moe_grouped_gemm_workspace_bytes(int layout, int dtype, int64_t G, int64_t M_total,
                                         int64_t N, int64_t K);

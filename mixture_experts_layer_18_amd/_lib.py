@@ -19,6 +19,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GEMM_NT, MOE_GEMM_NN, MOE_GEMM_TN = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
 MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
+MOE_SAVED_TRAINING, MOE_SAVED_PERMUTED_COPY = 1, 2
 MOE_ROUTE_BLOCK = 32
 STAGES = ["router", "route", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine",
           "combine_bwd", "down_dgrad", "down_wgrad", "gate_up_wgrad", "gate_up_dgrad", "shared_down_dgrad",
@@ -64,6 +65,8 @@ SIGNATURES = {
     "moe_route": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_permute": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_sz,
                             c_vp]),
+    "moe_saved_bytes": (c_sz, [_P(MoeDesc), c_i32]),
+    "moe_saved_carve": (c_i32, [_P(MoeDesc), c_i32, c_vp, c_sz, _P(MoeSaved)]),
     "moe_grouped_gemm_gather": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                                         c_vp, c_vp, c_i64, c_vp]),
     "moe_grouped_gemm": (c_i32, [c_i32, c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,

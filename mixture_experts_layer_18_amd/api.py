@@ -7,6 +7,8 @@ the HIP library.  Buffer allocation helpers use torch for device memory.
 from __future__ import annotations
 
 import ctypes
+
+import numpy as np
 from typing import Optional
 
 import torch
@@ -188,6 +190,35 @@ def alloc_saved(desc, device="cuda", training=True, gather=False) -> dict:
                offsets=e(E + 1, dtype=torch.int32), pos=e(A, dtype=torch.int32), src=e(A, dtype=torch.int32),
                tok=e(A, dtype=torch.int32), x_perm=None if gather else e(A, d), preact=e(A, 2 * f) if training else None, h=e(A, f), y_perm=e(A, d),
                s_preact=e(T, 2 * F) if (F and training) else None, s_h=e(T, F) if F else None)
+    return out
+
+
+def alloc_saved_one_buffer(desc, device="cuda", training=True, gather=False) -> dict:
+    """The saved buffers as views into one allocation laid out by moe_saved_carve
+    (the "_buffer" entry keeps it alive)."""
+    T, d, E, k, f = desc.num_tokens, desc.d_model, desc.num_experts, desc.top_k, desc.d_ff
+    F = desc.num_shared * desc.d_ff_shared
+    A = T * k
+    dt = TORCH_DTYPE[desc.dtype]
+    flags = (L.MOE_SAVED_TRAINING if training else 0) | (0 if gather else L.MOE_SAVED_PERMUTED_COPY)
+    lib = L.load()
+    n = lib.moe_saved_bytes(ctypes.byref(desc), flags)
+    buf = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    s = L.MoeSaved()
+    _check(lib.moe_saved_carve(ctypes.byref(desc), flags, _p(buf), buf.numel(), ctypes.byref(s)), "moe_saved_carve")
+    shapes = dict(logits=((T, E), torch.float32), idx=((T, k), torch.int32), gate=((T, k), torch.float32),
+                  counts=((E,), torch.int32), offsets=((E + 1,), torch.int32), pos=((A,), torch.int32),
+                  src=((A,), torch.int32), tok=((A,), torch.int32), x_perm=((A, d), dt), preact=((A, 2 * f), dt),
+                  h=((A, f), dt), y_perm=((A, d), dt), s_preact=((T, 2 * F), dt), s_h=((T, F), dt))
+    out = {"_buffer": buf}
+    for name, (shape, t) in shapes.items():
+        ptr = getattr(s, name)
+        if ptr is None:
+            out[name] = None
+            continue
+        off = ptr - buf.data_ptr()
+        nbytes = int(np.prod(shape)) * torch.empty((), dtype=t).element_size()
+        out[name] = buf[off:off + nbytes].view(t).view(*shape)
     return out
 
 

@@ -230,6 +230,54 @@ size_t moe_workspace_bytes(const moe_desc_t* d, int which) {
   }
 }
 
+// The saved buffers of moe_forward in one allocation: each field 256-byte
+// aligned, in struct order; fields the flags leave out stay NULL.
+static size_t saved_layout(const moe_desc_t* d, int flags, char* base, moe_saved_t* out) {
+  const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
+  const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
+  const size_t es = d->dtype == MOE_BF16 ? 2 : 4;
+  const bool training = flags & MOE_SAVED_TRAINING, copy = flags & MOE_SAVED_PERMUTED_COPY;
+  size_t off = 0;
+  auto take = [&](size_t bytes, bool want) -> void* {
+    if (!want) return nullptr;
+    void* p = base ? base + off : nullptr;
+    off += (bytes + 255) / 256 * 256;
+    return p;
+  };
+  moe_saved_t s;
+  s.logits = (float*)take((size_t)T * E * 4, true);
+  s.idx = (int32_t*)take((size_t)T * k * 4, true);
+  s.gate = (float*)take((size_t)T * k * 4, true);
+  s.counts = (int32_t*)take((size_t)E * 4, true);
+  s.offsets = (int32_t*)take((size_t)(E + 1) * 4, true);
+  s.pos = (int32_t*)take((size_t)A * 4, true);
+  s.src = (int32_t*)take((size_t)A * 4, true);
+  s.tok = (int32_t*)take((size_t)A * 4, true);
+  s.x_perm = take((size_t)A * D * es, copy);
+  s.preact = take((size_t)A * 2 * f * es, training);
+  s.h = take((size_t)A * f * es, true);
+  s.y_perm = take((size_t)A * D * es, true);
+  s.s_preact = take((size_t)T * 2 * F * es, training && F > 0);
+  s.s_h = take((size_t)T * F * es, F > 0);
+  if (out) *out = s;
+  return off;
+}
+
+size_t moe_saved_bytes(const moe_desc_t* d, int flags) {
+  if (check_desc(d) != MOE_OK || (flags & ~3)) return 0;
+  return saved_layout(d, flags, nullptr, nullptr);
+}
+
+int moe_saved_carve(const moe_desc_t* d, int flags, void* base, size_t bytes, moe_saved_t* out) {
+  int s = check_desc(d);
+  if (s) return s;
+  if ((flags & ~3) || !base || !out) return MOE_ERR_INVALID;
+  if (((uintptr_t)base & 255) != 0) return MOE_ERR_ALIGN;
+  if (bytes < saved_layout(d, flags, nullptr, nullptr)) return MOE_ERR_WORKSPACE;
+  saved_layout(d, flags, (char*)base, out);
+  return MOE_OK;
+}
+
 static int check_gemm(int layout, int epi, int dtype, int64_t G, int64_t M, int64_t N, int64_t K) {
   if (layout < MOE_GEMM_NT || layout > MOE_GEMM_TN) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_SWIGLU && layout != MOE_GEMM_NT) return MOE_ERR_INVALID;

@@ -227,3 +227,42 @@ def test_gather_argument_checks(lib):
     ok = make_desc(64, 256, 8, 2, 256, 0, 0, "softmax", False, "bf16")
     assert lib.moe_forward(ctypes.byref(ok), ctypes.byref(w), a, a, ctypes.byref(s), a, 1 << 30, None) == \
         L.MOE_ERR_INVALID
+
+
+def test_saved_layout_in_one_allocation(lib):
+    """moe_saved_bytes / moe_saved_carve: every field the flags ask for is
+    256-byte aligned, inside the allocation and disjoint from the others;
+    the others are NULL.  Host arithmetic only."""
+    d = make_desc(1000, 256, 16, 4, 192, 2, 128, "sigmoid", True, "bf16")
+    T, D, E, k, f, F = 1000, 256, 16, 4, 192, 256
+    A = T * k
+    es = 2
+    sizes = dict(logits=T * E * 4, idx=T * k * 4, gate=T * k * 4, counts=E * 4, offsets=(E + 1) * 4, pos=A * 4,
+                 src=A * 4, tok=A * 4, x_perm=A * D * es, preact=A * 2 * f * es, h=A * f * es, y_perm=A * D * es,
+                 s_preact=T * 2 * F * es, s_h=T * F * es)
+    base = 1 << 30
+    for flags in (0, L.MOE_SAVED_TRAINING, L.MOE_SAVED_PERMUTED_COPY,
+                  L.MOE_SAVED_TRAINING | L.MOE_SAVED_PERMUTED_COPY):
+        n = lib.moe_saved_bytes(ctypes.byref(d), flags)
+        s = L.MoeSaved()
+        assert lib.moe_saved_carve(ctypes.byref(d), flags, ctypes.c_void_p(base), n, ctypes.byref(s)) == L.MOE_OK
+        spans = []
+        for name, size in sizes.items():
+            p = getattr(s, name)
+            want = not ((name in ("preact", "s_preact") and not flags & L.MOE_SAVED_TRAINING) or
+                        (name == "x_perm" and not flags & L.MOE_SAVED_PERMUTED_COPY))
+            if not want:
+                assert p is None, name
+                continue
+            assert p is not None and p % 256 == 0 and base <= p and p + size <= base + n, name
+            spans.append((p, p + size))
+        spans.sort()
+        assert all(a[1] <= b[0] for a, b in zip(spans, spans[1:]))
+        assert lib.moe_saved_carve(ctypes.byref(d), flags, ctypes.c_void_p(base), n - 1,
+                                   ctypes.byref(s)) == L.MOE_ERR_WORKSPACE
+    assert lib.moe_saved_bytes(ctypes.byref(d), 4) == 0
+    s = L.MoeSaved()
+    assert lib.moe_saved_carve(ctypes.byref(d), 0, ctypes.c_void_p(base + 16), 1 << 30, ctypes.byref(s)) == \
+        L.MOE_ERR_ALIGN
+    assert lib.moe_saved_carve(ctypes.byref(d), 8, ctypes.c_void_p(base), 1 << 30, ctypes.byref(s)) == \
+        L.MOE_ERR_INVALID

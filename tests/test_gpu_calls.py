@@ -130,6 +130,26 @@ def test_permute_bit_exact(cfg):
     assert torch.equal(xb, xs[src_t])
 
 
+def test_permute_then_combine_is_the_identity():
+    """Permuted copies of the token rows, combined with renormalised gates
+    (1/k each, k = 4 so that every step is exact), give x back bit for bit."""
+    cfg = synth.CONFIG_BY_NAME["moe7b_bf16"].replace(T=777, d=256, E=16, k=4)
+    inp, logits = _logits_for(cfg)
+    desc, idx, gate, hist = _route_gpu(cfg, logits, inp["bias"])
+    T, k, E, d = cfg.T, cfg.k, cfg.E, cfg.d
+    x = dev(inp["x"])
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    src = torch.empty(T * k, dtype=torch.int32, device="cuda")
+    x_perm = torch.empty(T * k, d, dtype=x.dtype, device="cuda")
+    M.moe_permute(desc, x, idx, hist, counts, offsets, pos, src, x_perm, M.alloc_workspace(desc, "permute"))
+    y = torch.empty_like(x)
+    M.moe_combine(desc, x_perm, torch.full((T, k), 0.25, dtype=torch.float32, device="cuda"), pos, None, y)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), x.view(torch.int16))
+
+
 # ----------------------------------------------------------------------------- grouped GEMM
 def _groups(seed, G, mean, empty=(), big=None):
     g = np.random.default_rng(seed)

@@ -122,3 +122,27 @@ def test_backward_bf16_odd_expert_count():
     cfg = SMALL_BF16.replace(name="e7", T=300, E=7, k=2, f=128, n_shared=0, f_shared=0)
     print("[layer] bf16 E=7 fwd+bwd", flush=True)
     R.compare_full(cfg, synth.make_inputs(cfg), backward=True)
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["permuted-copy", "gathered"])
+def test_saved_buffers_in_one_allocation(gather):
+    """The saved buffers carved from one allocation (moe_saved_carve) give the
+    same bits as separate allocations."""
+    import mixture_experts_layer_18_amd as M
+    cfg = SMALL_BF16.replace(name="carved", d=256, f=256)
+    inp = synth.make_inputs(cfg)
+    desc = M.desc_from_config(cfg)
+    w = R.upload_layer(cfg, inp)
+    x = R.dev(inp["x"])
+    dy = R.dev(inp["dy"])
+    outs = []
+    for saved in (M.alloc_saved(desc, gather=gather), M.alloc_saved_one_buffer(desc, gather=gather)):
+        y = torch.empty_like(x)
+        M.moe_forward(desc, w, x, y, saved, M.alloc_workspace(desc, "forward"))
+        grads = M.alloc_grads(desc)
+        dx = torch.empty_like(x)
+        M.moe_backward(desc, w, x, saved, dy, dx, grads, M.alloc_workspace(desc, "backward"))
+        torch.cuda.synchronize()
+        outs.append([y, dx] + [g for g in grads.values() if g is not None])
+    for a, b in zip(*outs):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
