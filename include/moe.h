@@ -385,6 +385,10 @@ enum {
  * what was recorded; moe_stage_timing(0) stops recording. */
 int moe_stage_timing(int enable);
 
+/* As moe_stage_timing, for the stages whose bit (1 << stage) is set in mask
+ * only (0 stops recording): fewer event pairs in a timed region. */
+int moe_stage_timing_mask(uint32_t mask);
+
 /* Waits for every recorded stage, adds its elapsed milliseconds to
  * ms[stage] and 1 to launches[stage] (both arrays of MOE_NUM_STAGES, written
  * in full), and clears the records.  MOE_ERR_HIP if an event query fails. */

@@ -238,10 +238,17 @@ def alloc_workspace(desc, which: str, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
-def stage_timing(enable: bool):
+def stage_timing(enable: bool, stages=None):
     """Start (clearing earlier records) or stop per-stage event timing of
-    moe_forward / moe_backward."""
-    _check(L.load().moe_stage_timing(int(bool(enable))), "moe_stage_timing")
+    moe_forward / moe_backward; `stages` (names from STAGES) limits it to
+    those stages."""
+    if stages is None or not enable:
+        _check(L.load().moe_stage_timing(int(bool(enable))), "moe_stage_timing")
+        return
+    mask = 0
+    for name in stages:
+        mask |= 1 << L.STAGES.index(name)
+    _check(L.load().moe_stage_timing_mask(mask), "moe_stage_timing_mask")
 
 
 def stage_times() -> dict:

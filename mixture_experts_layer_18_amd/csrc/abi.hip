@@ -154,7 +154,7 @@ struct StageRec {
 };
 constexpr size_t kMaxStageRecs = size_t(1) << 16;
 std::mutex g_timing_mu;
-bool g_timing = false;
+uint32_t g_timing = 0;          // bit s: stage s is timed
 std::vector<StageRec> g_recs;   // recorded, not yet read
 std::vector<StageRec> g_spare;  // event pairs ready for reuse
 
@@ -162,7 +162,7 @@ std::vector<StageRec> g_spare;  // event pairs ready for reuse
 StageRec stage_begin(int stage, hipStream_t st) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   StageRec r{-1, nullptr, nullptr};
-  if (!g_timing || g_recs.size() >= kMaxStageRecs) return r;
+  if (!((g_timing >> stage) & 1u) || g_recs.size() >= kMaxStageRecs) return r;
   if (!g_spare.empty()) {
     r = g_spare.back();
     g_spare.pop_back();
@@ -630,13 +630,15 @@ int moe_bias_update(const moe_desc_t* d, const int32_t* counts, float rate, floa
   return MOE_OK;
 }
 
-int moe_stage_timing(int enable) {
+int moe_stage_timing_mask(uint32_t mask) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   for (const StageRec& r : g_recs) g_spare.push_back(r);
   g_recs.clear();
-  g_timing = enable != 0;
+  g_timing = mask & ((1u << MOE_NUM_STAGES) - 1u);
   return MOE_OK;
 }
+
+int moe_stage_timing(int enable) { return moe_stage_timing_mask(enable ? ~0u : 0u); }
 
 int moe_stage_times(double* ms, int64_t* launches) {
   if (!ms || !launches) return MOE_ERR_INVALID;

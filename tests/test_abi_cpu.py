@@ -136,6 +136,11 @@ def test_stage_timing_without_records(lib):
     assert list(ms) == [0.0] * L.MOE_NUM_STAGES and list(n) == [0] * L.MOE_NUM_STAGES
     assert lib.moe_stage_times(None, n) == L.MOE_ERR_INVALID
     assert lib.moe_stage_timing(0) == L.MOE_OK
+    # a stage mask: still nothing recorded without launches
+    assert lib.moe_stage_timing_mask(1 << L.STAGES.index("gate_up")) == L.MOE_OK
+    assert lib.moe_stage_times(ms, n) == L.MOE_OK
+    assert all(n[i] == 0 for i in range(L.MOE_NUM_STAGES))
+    assert lib.moe_stage_timing_mask(0) == L.MOE_OK
 
 
 def test_router_terms_and_bias_update_argument_checks(lib):
