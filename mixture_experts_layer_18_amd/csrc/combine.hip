@@ -279,6 +279,18 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(
     int64_t row[KK];
 #pragma unroll
     for (int j = 0; j < KK; ++j) row[j] = (int64_t)pos[tk + j] * d;
+    // sparse router term: the picked experts' dlogits and W_r rows are fixed
+    // for the token, so their W_r chunks load together with the slot rows
+    float dls[KK];
+    const float* wrow[KK];
+    if (!dense_router) {
+#pragma unroll
+      for (int j = 0; j < KK; ++j) {
+        const int e = idx[tk + j];
+        dls[j] = dlogits[(int64_t)t * E + e];
+        wrow[j] = w_router + (int64_t)e * d;
+      }
+    }
 #pragma unroll 2
     for (int c = lane; c < nvec; c += 64) {
       float v[KK][VN];
@@ -286,6 +298,16 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(
       for (int j = 0; j < KK; ++j) Vec<T>::load(dx_perm + row[j] + (int64_t)c * VN, v[j]);
       float sh[VN];
       if (dx_shared) Vec<T>::load(dx_shared + (int64_t)t * d + (int64_t)c * VN, sh);
+      float wv[KK][VN];
+      if (!dense_router) {
+#pragma unroll
+        for (int j = 0; j < KK; ++j)
+#pragma unroll
+          for (int u = 0; u < VN; u += 4) {
+            const float4 q = *reinterpret_cast<const float4*>(wrow[j] + (int64_t)c * VN + u);
+            wv[j][u] = q.x; wv[j][u + 1] = q.y; wv[j][u + 2] = q.z; wv[j][u + 3] = q.w;
+          }
+      }
       float acc[VN];
 #pragma unroll
       for (int u = 0; u < VN; ++u) acc[u] = 0.0f;
@@ -297,12 +319,18 @@ __global__ __launch_bounds__(256) void unpermute_sum_kernel(
 #pragma unroll
         for (int u = 0; u < VN; ++u) acc[u] += sh[u];
       }
-      for (int j = 0; j < nr; ++j) {
-        const int e = dense_router ? j : idx[tk + j];
-        const float dl = dlogits[(int64_t)t * E + e];
-        const float* wr = w_router + (int64_t)e * d + (int64_t)c * VN;
+      if (!dense_router) {
 #pragma unroll
-        for (int u = 0; u < VN; ++u) acc[u] = fmaf(dl, wr[u], acc[u]);
+        for (int j = 0; j < KK; ++j)
+#pragma unroll
+          for (int u = 0; u < VN; ++u) acc[u] = fmaf(dls[j], wv[j][u], acc[u]);
+      } else {
+        for (int e = 0; e < E; ++e) {
+          const float dl = dlogits[(int64_t)t * E + e];
+          const float* wr = w_router + (int64_t)e * d + (int64_t)c * VN;
+#pragma unroll
+          for (int u = 0; u < VN; ++u) acc[u] = fmaf(dl, wr[u], acc[u]);
+        }
       }
       Vec<T>::store(dx + (int64_t)t * d + (int64_t)c * VN, acc);
     }
