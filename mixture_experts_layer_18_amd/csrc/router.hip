@@ -285,9 +285,10 @@ __global__ __launch_bounds__(256) void router_wgrad_split_kernel(const float* __
   f32x16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
-  for (int tb = tlo; tb < thi; tb += WBK) {
-    float2 dv[4];
-    uint32_t xv[4];
+  // experts beyond E (a partial expert block) contribute zero
+  const bool e_ok0 = e0 + 2 * p < E, e_ok1 = e0 + 2 * p + 1 < E;
+  // the operands of the step at token tb (zero past the slice end)
+  auto gload = [&](int tb, float2* dv, uint32_t* xv) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = tb + q * 4 + u;
@@ -299,9 +300,9 @@ __global__ __launch_bounds__(256) void router_wgrad_split_kernel(const float* __
         xv[u] = 0u;
       }
     }
-    // experts beyond E (a partial expert block) contribute zero
-    const bool e_ok0 = e0 + 2 * p < E, e_ok1 = e0 + 2 * p + 1 < E;
-    __syncthreads();  // the previous step's fragments have been read
+  };
+  // dl split exactly into three bf16 parts and x, transposed into LDS
+  auto stage = [&](const float2* dv, const uint32_t* xv) __attribute__((always_inline)) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       // the four tokens of expert (column) 2p + h, split and packed
@@ -323,8 +324,9 @@ __global__ __launch_bounds__(256) void router_wgrad_split_kernel(const float* __
       *reinterpret_cast<u32x2*>(sm + 2 * WTILE + off) = u32x2{l0, l1};
       *reinterpret_cast<u32x2*>(sm + 3 * WTILE + off) = u32x2{xa, xb};
     }
-    __syncthreads();
-    const int ar = we * 32 + (lane & 31), br = wc * 32 + (lane & 31);
+  };
+  const int ar = we * 32 + (lane & 31), br = wc * 32 + (lane & 31);
+  auto compute = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < WBK / 16; ++ks) {
       const int c = ks * 2 + (lane >> 5);
@@ -334,6 +336,26 @@ __global__ __launch_bounds__(256) void router_wgrad_split_kernel(const float* __
         const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sm + pt * WTILE + ar * WROW + (wslot(ar, c) << 4));
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
+    }
+  };
+  // steps in pairs, one register set per parity: the loads of step j + 2 are
+  // in flight while step j is staged and computed
+  float2 dA[4], dB[4];
+  uint32_t xA[4], xB[4];
+  gload(tlo, dA, xA);
+  gload(tlo + WBK, dB, xB);
+  for (int tb = tlo; tb < thi; tb += 2 * WBK) {
+    __syncthreads();  // the previous step's fragments have been read
+    stage(dA, xA);
+    gload(tb + 2 * WBK, dA, xA);
+    __syncthreads();
+    compute();
+    if (tb + WBK < thi) {  // uniform over the workgroup
+      __syncthreads();
+      stage(dB, xB);
+      gload(tb + 3 * WBK, dB, xB);
+      __syncthreads();
+      compute();
     }
   }
   // lane: column (lane%32) of the wave tile, experts (v/4)*8 + (lane/32)*4 + v%4
