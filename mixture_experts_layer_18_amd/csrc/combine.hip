@@ -19,11 +19,13 @@ namespace moe {
 template <typename T> struct Vec;
 template <> struct Vec<bf16_t> {
   static constexpr int N = 8;
-  static MOE_DEV void load(const bf16_t* p, float* f) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+  typedef u32x4 raw_t;
+  static MOE_DEV raw_t load_raw(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+  static MOE_DEV void unpack(const raw_t& v, float* f) {
     f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
     f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z); f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
   }
+  static MOE_DEV void load(const bf16_t* p, float* f) { unpack(load_raw(p), f); }
   static MOE_DEV void store(bf16_t* p, const float* f) {
     u32x4 v;
     v.x = pack_bf16x2(f[0], f[1]); v.y = pack_bf16x2(f[2], f[3]);
@@ -33,14 +35,20 @@ template <> struct Vec<bf16_t> {
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
-  static MOE_DEV void load(const float* p, float* f) {
-    const float4 v = *reinterpret_cast<const float4*>(p);
+  typedef float4 raw_t;
+  static MOE_DEV raw_t load_raw(const float* p) { return *reinterpret_cast<const float4*>(p); }
+  static MOE_DEV void unpack(const raw_t& v, float* f) {
     f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
   }
+  static MOE_DEV void load(const float* p, float* f) { unpack(load_raw(p), f); }
   static MOE_DEV void store(float* p, const float* f) {
     *reinterpret_cast<float4*>(p) = make_float4(f[0], f[1], f[2], f[3]);
   }
 };
+
+// 16-byte chunks per lane whose loads the combine backward issues together
+// (64 lanes x CG chunks of a row per group)
+constexpr int CG = 4;
 
 // y[t] = sum_j gate[t,j] * y_perm[pos[t*k+j]] (+ shared_y[t]), fp32, one rounding.
 // One wavefront per token.  KK > 0 fixes the number of slots at compile time,
@@ -140,22 +148,38 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
       g[j] = gate[tk + j];
       dot[j] = 0.0f;
     }
-#pragma unroll 2
-    for (int c = lane; c < nvec; c += 64) {
-      float dv[VN];
-      Vec<T>::load(dy + (int64_t)t * d + (int64_t)c * VN, dv);
-      float v[KK][VN];
+    // groups of CG chunks: every load of a group is issued before any of its
+    // stores, so the loads are in flight together (a load issued after a
+    // pending store is waited for together with that store)
+    for (int c0 = lane; c0 < nvec; c0 += 64 * CG) {
+      typename Vec<T>::raw_t dr[CG], vr[CG][KK];
 #pragma unroll
-      for (int j = 0; j < KK; ++j) Vec<T>::load(y_perm + row[j] + (int64_t)c * VN, v[j]);
+      for (int i = 0; i < CG; ++i) {
+        const int c = c0 + 64 * i;
+        if (c < nvec) {
+          dr[i] = Vec<T>::load_raw(dy + (int64_t)t * d + (int64_t)c * VN);
 #pragma unroll
-      for (int j = 0; j < KK; ++j) {
-        float o[VN];
-#pragma unroll
-        for (int u = 0; u < VN; ++u) {
-          dot[j] = fmaf(dv[u], v[j][u], dot[j]);
-          o[u] = g[j] * dv[u];
+          for (int j = 0; j < KK; ++j) vr[i][j] = Vec<T>::load_raw(y_perm + row[j] + (int64_t)c * VN);
         }
-        Vec<T>::store(dy_perm + row[j] + (int64_t)c * VN, o);
+      }
+#pragma unroll
+      for (int i = 0; i < CG; ++i) {
+        const int c = c0 + 64 * i;
+        if (c < nvec) {
+          float dv[VN];
+          Vec<T>::unpack(dr[i], dv);
+#pragma unroll
+          for (int j = 0; j < KK; ++j) {
+            float v[VN], o[VN];
+            Vec<T>::unpack(vr[i][j], v);
+#pragma unroll
+            for (int u = 0; u < VN; ++u) {
+              dot[j] = fmaf(dv[u], v[u], dot[j]);
+              o[u] = g[j] * dv[u];
+            }
+            Vec<T>::store(dy_perm + row[j] + (int64_t)c * VN, o);
+          }
+        }
       }
     }
 #pragma unroll
