@@ -15,7 +15,7 @@ import torch
 
 import synth
 from oracle import moe_oracle as O
-from tests.gpu_util import assert_close, dev, host, max_abs_over_rms
+from tests.gpu_util import assert_close, assert_rounded, dev, host, max_abs_over_rms
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,61 @@ def test_full_size_layer(cfg, gather):
     out_dx2 = host(dx2)
     assert np.all(out_dx2[np.setdiff1d(np.arange(cfg.T), S2)] == 0.0)
     assert_close(out_dx2[S2], bw2["dx"], cfg.dtype, "dx (masked)")
+
+
+def test_full_size_fp8_gate_up():
+    """The fp8 forward gate/up product in the configuration the benchmark times
+    (7B-style layer, 98304 routed rows, row-wise e4m3 scales, SwiGLU
+    epilogue), checked on sampled rows of six experts: the largest, the
+    smallest non-empty one and four more.  The oracle quantises the sampled
+    token rows and those experts' weights from the bf16 inputs itself; the
+    GPU's codes and scales must equal its codes and scales bit for bit, and
+    its pre-activations and h must be within one bf16 rounding of the
+    oracle's fp8 product."""
+    cfg = synth.CONFIG_BY_NAME["moe7b_bf16"]
+    print(f"[full] {cfg.name} fp8 gate/up: generating inputs", flush=True)
+    inp = synth.make_inputs(cfg, with_dy=False)
+    w = R.upload_layer(cfg, inp)
+    x = dev(inp["x"])
+    g = R.run_gpu(cfg, inp, backward=False, weights=w, x=x, keep_device=True, gather=True)
+    saved = g["saved"]
+    A, d, E, f = cfg.T * cfg.k, cfg.d, cfg.E, cfg.f
+    x_perm = x[saved["tok"].long()].contiguous()
+    xq = torch.empty(A, d, dtype=torch.uint8, device="cuda")
+    xs = torch.empty(A, dtype=torch.float32, device="cuda")
+    wq = torch.empty(E * 2 * f, d, dtype=torch.uint8, device="cuda")
+    ws = torch.empty(E * 2 * f, dtype=torch.float32, device="cuda")
+    h = torch.empty(A, f, dtype=torch.bfloat16, device="cuda")
+    aux = torch.empty(A, 2 * f, dtype=torch.bfloat16, device="cuda")
+    print(f"[full] {cfg.name} fp8 gate/up: GPU quantisation and grouped GEMM", flush=True)
+    M.moe_quantize_fp8(w["w_gateup"].reshape(E * 2 * f, d), wq, ws)
+    M.moe_quantize_fp8(x_perm, xq, xs)
+    M.moe_grouped_gemm_fp8("swiglu", E, A, 2 * f, d, saved["offsets"], xq, xs, wq, ws, h, aux)
+    torch.cuda.synchronize()
+
+    off = saved["offsets"].cpu().numpy().astype(np.int64)
+    tok = saved["tok"].cpu().numpy().astype(np.int64)
+    counts = np.diff(off)
+    nz = np.where(counts > 0)[0]
+    rng = np.random.default_rng(7)
+    experts = [int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])]
+    experts += [int(e) for e in rng.choice(np.setdiff1d(nz, experts), size=4, replace=False)]
+    h_all, aux_all = host(h), host(aux)
+    xq_h, xs_h = xq.cpu().numpy(), xs.cpu().numpy()
+    wq_h, ws_h = wq.cpu().numpy(), ws.cpu().numpy()
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, size=min(30, hi - lo))]))
+        print(f"[full] fp8 gate/up: expert {e} ({hi - lo} rows), {rows.size} sampled", flush=True)
+        qa, sa = O.quantize_rowwise(synth.as_f64(inp["x"][tok[rows]], "bf16"))
+        qb, sb = O.quantize_rowwise(synth.as_f64(inp["w_gateup"][e], "bf16"))
+        assert np.array_equal(xq_h[rows], qa) and np.array_equal(xs_h[rows], sa), "token row codes/scales"
+        wr = slice(e * 2 * f, (e + 1) * 2 * f)
+        assert np.array_equal(wq_h[wr], qb) and np.array_equal(ws_h[wr], sb), "weight codes/scales"
+        ref = O.grouped_gemm_fp8_nt(qa, sa, qb[None], sb[None], np.array([0, rows.size]))
+        assert_rounded(aux_all[rows], ref, "bf16", f"pre-activations, expert {e}")
+        Gm, U = ref[:, :f], ref[:, f:]
+        err = 1e-4 * np.sqrt(np.mean(ref * ref))
+        sg = 1.0 / (1.0 + np.exp(-Gm))
+        inherited = (np.abs(sg * (1.0 + Gm * (1.0 - sg)) * U) + np.abs(O.silu(Gm))) * err
+        assert_rounded(h_all[rows], O.silu(Gm) * U, "bf16", f"h, expert {e}", extra=inherited)
