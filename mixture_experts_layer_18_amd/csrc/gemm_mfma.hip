@@ -437,18 +437,10 @@ static hipError_t pick(const Args& a, hipStream_t st) {
 
 }  // namespace mf
 
-// Compute units of the current device (256 on MI355X if the query fails).
-static int cu_count() {
-  static int n = 0;
-  if (n == 0) {
-    int dev = 0, cus = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-      cus = 256;
-    n = cus;
-  }
-  return n;
-}
+// Compute units of an MI355X.  The slice count below is a host-side
+// function of the problem only (no device query), so the workspace queries
+// stay pure host arithmetic and always agree with the launch.
+constexpr int kMi355xCUs = 256;
 
 // Weight gradients whose output tiles alone cannot fill the chip (the shared
 // experts: one group) split each group's rows into slices written as fp32
@@ -460,7 +452,7 @@ static int cu_count() {
 int gemm_mfma_tn_splits(const GemmProblem& p) {
   if (p.layout != MOE_GEMM_TN || p.G <= 0) return 1;
   const int64_t tiles = p.G * cdiv64(p.N, 256) * cdiv64(p.K, 128);
-  const int64_t slots = 2 * (int64_t)cu_count();
+  const int64_t slots = 2 * (int64_t)kMi355xCUs;
   const int64_t rows = p.M_total / p.G;
   const double slice_us = (double)p.G * (double)p.N * (double)p.K * 8.0 / 4.5e6;
   int best = 1;

@@ -53,6 +53,21 @@ def test_queries(lib):
     assert lib.moe_grouped_gemm_workspace_bytes(L.MOE_GEMM_NT, L.MOE_BF16, 8, 100, 128, 128) == 0
 
 
+def test_weight_gradient_slice_counts(lib):
+    """Row-slice counts of weight gradients with few output tiles, read back
+    through the workspace size (slices x G x N x K fp32 partials): the
+    shared-expert products of the 7B-style layer take 4 and 5 slices (a third
+    workgroup round of 32 workgroups is what 3 and 6 would leave), the large
+    layer's need none, and slices keep at least 512 rows."""
+    ws = lambda G, M, N, K: lib.moe_grouped_gemm_workspace_bytes(L.MOE_GEMM_TN, L.MOE_BF16, G, M, N, K)  # noqa: E731
+    assert ws(1, 16384, 5632, 2048) == 4 * 5632 * 2048 * 4
+    assert ws(1, 16384, 2048, 2816) == 5 * 2048 * 2816 * 4
+    assert ws(1, 65536, 4096, 4096) == 0
+    assert ws(1, 4096, 256, 384) == 8 * 256 * 384 * 4
+    assert ws(1, 4000, 256, 384) == 7 * 256 * 384 * 4
+    assert ws(1, 600, 256, 384) == 0
+
+
 BAD = [
     dict(E=0), dict(E=257), dict(k=0), dict(k=17), dict(k=9, E=8), dict(d=100), dict(f=96),
     dict(T=-1), dict(score=2), dict(renorm=2), dict(dtype=3), dict(reserved=1), dict(n_shared=1, f_shared=0),
