@@ -637,6 +637,50 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
       continue;
     }
+    // The plain forward product stores through LDS: each wave stages its
+    // 128 x 64 bf16 results in its own 16 KB of the idle stages (16-byte
+    // chunks XOR-swizzled by row) and then writes 8 full 128-byte rows per
+    // instruction instead of 32-byte pieces of 32 rows; the next tile's first
+    // stages are fetched after (measured 2-5 % faster on the down products;
+    // the data gradients measured slower this way and the weight gradients
+    // would spill, so they keep the direct stores).
+    constexpr bool LDS_EPI = (LAYOUT == MOE_GEMM_NT && EPI == MOE_EPI_NONE && !F8);
+    if constexpr (LDS_EPI) {
+      static_assert(WN == 64 && FJ == 2 && WM * WN * 2 == 16384 && NW * 16384 <= STAGES * SB, "staging layout");
+      char* wb = smem + wave * 16384;
+#pragma unroll
+      for (int it = 0; it < FI; ++it)
+#pragma unroll
+        for (int jt = 0; jt < FJ; ++jt) {
+          const int r = it * 32 + r32;
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const u32x2 pk = {pack_bf16x2(opaque(acc[it][jt][gq * 4]), opaque(acc[it][jt][gq * 4 + 1])),
+                              pack_bf16x2(opaque(acc[it][jt][gq * 4 + 2]), opaque(acc[it][jt][gq * 4 + 3]))};
+            const int cc = jt * 4 + gq;  // 16-byte chunk of the 128-byte row
+            *reinterpret_cast<u32x2*>(wb + r * 128 + ((cc ^ (r & 7)) << 4) + kh * 8) = pk;
+          }
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done
+      const int lr = lane >> 3, lc = lane & 7;
+#pragma unroll
+      for (int q = 0; q < WM / 8; ++q) {
+        const int r = q * 8 + lr;
+        const u32x4 val = *reinterpret_cast<const u32x4*>(wb + r * 128 + ((lc ^ (r & 7)) << 4));
+        const int64_t i = t.i_lo + wp * WM + r;
+        const int64_t c = t.j0 + wq * WN + lc * 8;
+        if (i < t.i_hi && c < ncols) *reinterpret_cast<u32x4*>(a.C + i * ncols + c) = val;
+      }
+      lds_barrier();  // every wave is done with its staging area
+      prefetch_next();
+      if (!more) break;
+      L = Ln;
+      t = tn;
+      nk = nk_n;
+#pragma unroll
+      for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
+      continue;
+    }
     prefetch_next();
     // fp8: the row scale of this lane's output row per row block, and the
     // column scales of the 16 columns a lane holds in a 32-wide block
