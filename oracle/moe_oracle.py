@@ -563,6 +563,23 @@ def quantize_tensorwise(x):
     return q, s
 
 
+def quantize_rowwise_transposed(w):
+    """Row-wise quantisation along the first axis of each matrix: for
+    w [G, R, C], codes [G, C, R] and scales [G, C], the codes of column c of
+    w[g] stored as row c (its transpose), one scale per column:
+    s[g, c] = amax_r |w[g, r, c]| / 448.  A product that reduces over R (the
+    data gradient dX = dGU . W with W [2f, d]) then runs in the forward
+    layout with the weight operand as rows (FP2: one scale per row along the
+    reduction dimension)."""
+    w = np.asarray(w, F32)
+    G, R, C = w.shape
+    codes = np.empty((G, C, R), np.uint8)
+    scales = np.empty((G, C), F32)
+    for g in range(G):
+        codes[g], scales[g] = quantize_rowwise(w[g].T)
+    return codes, scales
+
+
 def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets):
     """C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k] over the
     decoded codes, for the rows m of group g; fp64."""

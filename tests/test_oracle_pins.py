@@ -480,6 +480,36 @@ def test_fp8_rowwise_gemm_factorises():
     assert np.all(np.max(np.abs(O.e4m3_decode(qx)), axis=1) == 448.0)
 
 
+def test_fp8_transposed_quantisation():
+    """Codes [G, C, R] of w [G, R, C] quantised along R: every code decodes,
+    times its column's scale, to within half an e4m3 step of w[g, r, c] (so
+    the transposed index mapping is right), every column's maximum maps to
+    exactly 448, an all-zero column gets scale 1 and zero codes, and the
+    data-gradient product dX = A . W computed in the forward layout with
+    these codes equals the product of the dequantised operands."""
+    g = np.random.default_rng(37)
+    w = (g.standard_normal((2, 48, 16)) * np.exp(g.standard_normal(16))[None, None, :]).astype(np.float32)
+    w[1, :, 5] = 0.0
+    q, s = O.quantize_rowwise_transposed(w)
+    assert q.shape == (2, 16, 48) and s.shape == (2, 16)
+    wd = O.e4m3_decode(q) * s[:, :, None]                  # [G, C, R]
+    ref = np.swapaxes(w, 1, 2).astype(np.float64)
+    bound = np.maximum(np.abs(ref) * 2.0 ** -4, s[:, :, None].astype(np.float64) * 2.0 ** -10)
+    assert np.all(np.abs(wd - ref) <= bound * (1 + 1e-12))
+    nz = np.ones((2, 16), bool)
+    nz[1, 5] = False
+    assert np.all(np.max(np.abs(O.e4m3_decode(q)), axis=2)[nz] == 448.0)
+    assert s[1, 5] == 1.0 and np.all(q[1, 5] == 0)
+    # A [M, R] quantised row-wise, W as [G, C, R] rows: C[m, c] = sum_r A[m, r] W[g, r, c]
+    a = g.standard_normal((30, 48)).astype(np.float32)
+    qa, sa = O.quantize_rowwise(a)
+    off = np.array([0, 12, 30])
+    C = O.grouped_gemm_fp8_nt(qa, sa, q, s, off)
+    ad = O.e4m3_decode(qa) * sa[:, None]
+    exp = np.concatenate([ad[0:12] @ np.swapaxes(wd[0], 0, 1), ad[12:30] @ np.swapaxes(wd[1], 0, 1)])
+    assert np.max(np.abs(C - exp)) <= 1e-12 * np.max(np.abs(exp))
+
+
 def test_e4m3_encode_matches_brute_force_nearest():
     """Random values against a nearest-value search over all finite codes
     written independently (ties to the even code)."""
