@@ -324,6 +324,22 @@ int moe_bias_update(const moe_desc_t *desc, const int32_t *counts, float rate, f
 int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void *x, uint8_t *q, float *scale,
                      void *stream);
 
+/* Row-wise fp8 quantisation along the first axis of each matrix, stored
+ * transposed (the weight of a data-gradient product, e.g. dX = dGU . W_gu
+ * with W_gu[e] [2f, d], quantised along its reduction dimension 2f and laid
+ * out [d, 2f] so that moe_grouped_gemm_fp8 runs the product in its forward
+ * layout; Apex-3 code page, "What's inside": fp8 row-wise GEMMs):
+ *   x [G, rows, cols] (MOE_F32 or MOE_BF16, in)
+ *   scale [G, cols] fp32 (out): s[g, c] = max_r |x[g, r, c]| / 448 (1 for an
+ *         all-zero column)
+ *   q [G, cols, rows] uint8 e4m3 codes (out): q[g, c, r] = e4m3(x[g, r, c] / s[g, c])
+ *         with the quotient an fp32 division clamped to +-448, round to
+ *         nearest even
+ * rows and cols multiples of 64 (rows <= 2^24, cols <= 2^22), 0 <= G <= 65535;
+ * pointers 16-byte aligned.  Deterministic. */
+int moe_quantize_fp8_transposed(int64_t G, int64_t rows, int64_t cols, int dtype, const void *x,
+                                uint8_t *q, float *scale, void *stream);
+
 /* Tensor-wise fp8 quantisation (the Apex-3 code page's "tensorwise" fp8
  * recipe): one scale s = amax / 448 over every element of x [rows, cols]
  * (fp32; 1 for an all-zero tensor), q[r, c] = e4m3(x[r, c] / s) as in

@@ -77,6 +77,7 @@ SIGNATURES = {
                              _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
     "moe_bias_update": (c_i32, [_P(MoeDesc), c_vp, ctypes.c_float, c_vp, c_vp]),
     "moe_quantize_fp8": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "moe_quantize_fp8_transposed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_quantize_fp8_tensorwise_workspace_bytes": (c_sz, [c_i64]),
     "moe_quantize_fp8_tensorwise": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "moe_grouped_gemm_fp8": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,

@@ -158,6 +158,14 @@ def moe_quantize_fp8(x, q, scale, stream=None):
     _check(L.load().moe_quantize_fp8(rows, cols, dt, _p(x), _p(q), _p(scale), _stream(stream)), "moe_quantize_fp8")
 
 
+def moe_quantize_fp8_transposed(w, q, scale, stream=None):
+    """w [G, R, C] -> codes q [G, C, R] and scales [G, C], quantised along R."""
+    dt = L.MOE_BF16 if w.dtype == torch.bfloat16 else L.MOE_F32
+    G, R, C = w.shape
+    _check(L.load().moe_quantize_fp8_transposed(G, R, C, dt, _p(w), _p(q), _p(scale), _stream(stream)),
+           "moe_quantize_fp8_transposed")
+
+
 def moe_quantize_fp8_tensorwise(x, q, scale, ws=None, stream=None):
     """Tensor-wise e4m3 quantisation of x [rows, cols]: one scale, written to every entry of scale [rows]."""
     dt = L.MOE_BF16 if x.dtype == torch.bfloat16 else L.MOE_F32

@@ -583,6 +583,18 @@ int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void* x, uint8
   return MOE_OK;
 }
 
+int moe_quantize_fp8_transposed(int64_t G, int64_t rows, int64_t cols, int dtype, const void* x,
+                                uint8_t* q, float* scale, void* stream) {
+  if (G < 0 || G > 65535 || rows < 0 || cols <= 0 || rows % 64 || cols % 64) return MOE_ERR_INVALID;
+  if (rows > (int64_t(1) << 24) || cols > (int64_t(1) << 22)) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (G == 0 || rows == 0) return MOE_OK;
+  if (!x || !q || !scale) return MOE_ERR_INVALID;
+  if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return MOE_ERR_ALIGN;
+  MOE_TRY(launch_quantize_fp8_transposed(x, dtype, G, rows, cols, q, scale, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 size_t moe_quantize_fp8_tensorwise_workspace_bytes(int64_t rows) {
   return rows < 0 ? 0 : quantize_fp8_tensorwise_ws_bytes(rows);
 }

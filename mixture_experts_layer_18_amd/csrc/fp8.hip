@@ -114,7 +114,101 @@ __global__ __launch_bounds__(256) void with_scale_kernel(const TX* __restrict__ 
   encode_row(x + r * C, C, s, q + r * C, lane);
 }
 
+// ---- along the first axis, stored transposed: x [G, R, C] -> q [G, C, R],
+// scale [G, C] = amax_r |x[g, r, c]| / 448 (the weight of a data-gradient
+// product quantised along its reduction dimension, laid out for the forward
+// product).  R and C are multiples of 64.
+
+template <typename TX>
+MOE_DEV void load4(const TX* p, float* f) {
+  if constexpr (sizeof(TX) == 2) {
+    const u32x2 v = *reinterpret_cast<const u32x2*>(p);
+    f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x); f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  } else {
+    const float4 v = *reinterpret_cast<const float4*>(p);
+    f[0] = v.x; f[1] = v.y; f[2] = v.z; f[3] = v.w;
+  }
+}
+
+// pass 1: one workgroup per (64 columns, matrix g): thread t takes columns
+// 8 * (t % 8) .. +7 of every 32nd row from row t / 8; the 32 partial maxima of
+// each column are combined through LDS
+template <typename TX>
+__global__ __launch_bounds__(256) void col_scale_kernel(const TX* __restrict__ x, int64_t R, int64_t C,
+                                                        float* __restrict__ scale) {
+  __shared__ float part[32][65];
+  const int t = threadIdx.x, cq = (t & 7) * 8, rp = t >> 3;
+  const int64_t g = blockIdx.y, c0 = (int64_t)blockIdx.x * 64;
+  const TX* base = x + g * R * C + c0 + cq;
+  float m[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m[u] = 0.0f;
+  for (int64_t r = rp; r < R; r += 32) {
+    float f[8];
+    load4(base + r * C, f);
+    load4(base + r * C + 4, f + 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], fabsf(f[u]));
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) part[rp][cq + u] = m[u];
+  __syncthreads();
+  if (t < 64) {
+    float a = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, part[i][t]);
+    scale[g * C + c0 + t] = scale_of(a);
+  }
+}
+
+// pass 2: one workgroup per 64 x 64 tile (rows r0.., columns c0.. of matrix
+// g): thread t encodes rows 4 (t / 16) .. +3 of columns 4 (t % 16) .. +3,
+// packs each column's 4 codes into one word of an LDS tile [column][row],
+// and the tile leaves as 64-byte runs of each output row q[g, c, r0..]
+template <typename TX>
+__global__ __launch_bounds__(256) void encode_transposed_kernel(const TX* __restrict__ x, int64_t R,
+                                                                int64_t C, const float* __restrict__ scale,
+                                                                uint8_t* __restrict__ q) {
+  constexpr int PITCH = 80;  // bytes per LDS column (64 codes + 16), 16-byte aligned
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
+  const int t = threadIdx.x, rr = (t >> 4) * 4, cc = (t & 15) * 4;
+  const int64_t g = blockIdx.z, r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
+  float s[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s[u] = scale[g * C + c0 + cc + u];
+  float f[4][4];  // [row][column]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) load4(x + (g * R + r0 + rr + i) * C + c0 + cc, f[i]);
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(f[i][u] / s[u], -448.0f), 448.0f);
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+    *reinterpret_cast<uint32_t*>(tile + (cc + u) * PITCH + rr) = w;
+  }
+  __syncthreads();
+  const int oc = t >> 2, orr = (t & 3) * 16;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(tile + oc * PITCH + orr);
+  *reinterpret_cast<u32x4*>(q + (g * C + c0 + oc) * R + r0 + orr) = v;
+}
+
 }  // namespace q8
+
+hipError_t launch_quantize_fp8_transposed(const void* x, int dtype, int64_t G, int64_t R, int64_t C,
+                                          uint8_t* q, float* scale, hipStream_t st) {
+  if (G == 0 || R == 0) return hipSuccess;
+  const dim3 g1((unsigned)(C / 64), (unsigned)G), g2((unsigned)(C / 64), (unsigned)(R / 64), (unsigned)G);
+  if (dtype == MOE_BF16) {
+    q8::col_scale_kernel<bf16_t><<<g1, 256, 0, st>>>((const bf16_t*)x, R, C, scale);
+    q8::encode_transposed_kernel<bf16_t><<<g2, 256, 0, st>>>((const bf16_t*)x, R, C, scale, q);
+  } else {
+    q8::col_scale_kernel<float><<<g1, 256, 0, st>>>((const float*)x, R, C, scale);
+    q8::encode_transposed_kernel<float><<<g2, 256, 0, st>>>((const float*)x, R, C, scale, q);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,
                                hipStream_t st) {

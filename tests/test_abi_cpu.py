@@ -202,6 +202,16 @@ def test_fp8_argument_checks(lib):
     assert tw(10, 128, L.MOE_BF16, a, a, a, ctypes.c_void_p((1 << 20) + 4), 64, None) == L.MOE_ERR_ALIGN
     assert tw(10, 128, L.MOE_BF16, a, a, a, a, 40, None) == L.MOE_ERR_WORKSPACE
     assert tw(0, 128, L.MOE_F32, None, None, None, None, 0, None) == L.MOE_OK
+    # transposed (along the first axis): rows and columns multiples of 64, dtype, alignment, empty
+    tq = lib.moe_quantize_fp8_transposed
+    assert tq(2, 100, 128, L.MOE_BF16, a, a, a, None) == L.MOE_ERR_INVALID
+    assert tq(2, 128, 96, L.MOE_BF16, a, a, a, None) == L.MOE_ERR_INVALID
+    assert tq(-1, 128, 128, L.MOE_BF16, a, a, a, None) == L.MOE_ERR_INVALID
+    assert tq(2, 128, 128, 5, a, a, a, None) == L.MOE_ERR_INVALID
+    assert tq(2, 128, 128, L.MOE_BF16, a, None, a, None) == L.MOE_ERR_INVALID
+    assert tq(2, 128, 128, L.MOE_F32, a, a, ctypes.c_void_p((1 << 20) + 8), None) == L.MOE_ERR_ALIGN
+    assert tq(0, 128, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    assert tq(3, 0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
     # gemm: layout limits
     args = (a, a, a, a, a, a, None, None)
     assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_DSWIGLU, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID

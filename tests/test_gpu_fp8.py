@@ -130,3 +130,56 @@ def test_grouped_gemm_fp8_against_oracle(epi, N):
         dsilu = sg * (1.0 + Gm * (1.0 - sg))
         inherited = (np.abs(dsilu * U) + np.abs(O.silu(Gm))) * e
         assert_rounded(host(C), O.silu(Gm) * U, "bf16", "h", extra=inherited)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_quantize_transposed_bit_exact(dtype):
+    """Quantisation along the first axis, stored transposed: codes and scales
+    equal the oracle's bit for bit (an all-zero column, extreme values, 320
+    columns: five 64-column tiles)."""
+    g = np.random.default_rng(43)
+    G, R, C = 3, 192, 320
+    w = (g.standard_normal((G, R, C)) * np.exp(g.standard_normal(C))[None, None, :]).astype(np.float32)
+    w[1, :, 7] = 0.0
+    w[2, 5, :4] = np.array([1e-30, -2e-9, 6e4, -3.0], np.float32)
+    if dtype == "bf16":
+        wb = synth.f32_to_bf16_bits(w)
+        src, ref_in = dev(wb), synth.bf16_bits_to_f32(wb)
+    else:
+        src, ref_in = torch.from_numpy(w).cuda(), w
+    q = torch.empty(G, C, R, dtype=torch.uint8, device="cuda")
+    s = torch.empty(G, C, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_transposed(src, q, s)
+    torch.cuda.synchronize()
+    qo, so = O.quantize_rowwise_transposed(ref_in)
+    assert np.array_equal(s.cpu().numpy(), so)
+    assert np.array_equal(q.cpu().numpy(), qo)
+
+
+def test_fp8_data_gradient_against_oracle():
+    """The data gradient dX = dGU . W (W [G, N, K], reduction over N) in fp8:
+    dGU quantised row-wise, W quantised along N and stored transposed, the
+    product run by the forward-layout fp8 GEMM; ragged groups and an empty
+    one."""
+    g = np.random.default_rng(44)
+    G, N, K = 5, 384, 256
+    m = g.integers(30, 260, size=G)
+    m[2] = 0
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(m)
+    Mt = int(off[-1])
+    db = _bf16(g, (Mt, N), 0.1)
+    wb = _bf16(g, (G, N, K), 1 / np.sqrt(N))
+    qa, sa = _quant_gpu(db)
+    qw = torch.empty(G, K, N, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(G, K, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_transposed(dev(wb), qw, sw)
+    C = torch.empty(Mt, K, dtype=torch.bfloat16, device="cuda")
+    print(f"[fp8] data gradient G={G} M={Mt} N={N} K={K}", flush=True)
+    M.moe_grouped_gemm_fp8("none", G, Mt, K, N, dev(off), qa, sa, qw, sw, C)
+    torch.cuda.synchronize()
+    qao, sao = O.quantize_rowwise(synth.bf16_bits_to_f32(db))
+    qwo, swo = O.quantize_rowwise_transposed(synth.bf16_bits_to_f32(wb))
+    assert np.array_equal(qw.cpu().numpy(), qwo) and np.array_equal(sw.cpu().numpy(), swo)
+    ref = O.grouped_gemm_fp8_nt(qao, sao, qwo, swo, off)
+    assert_rounded(host(C), ref, "bf16", "dX")
