@@ -264,6 +264,32 @@ def fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, flop, bf16_s):
                     "activation quantisation timed separately, weights quantised once"}
 
 
+def fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
+    """The gate/up data gradient dX = dGU . W_gu in fp8 on the same routing:
+    dGU (synthetic, N(0, 0.01^2), the layer's shape) quantised row-wise, W_gu
+    quantised along its reduction dimension and stored transposed (once,
+    outside the timing), the product on the forward-layout fp8 grouped GEMM;
+    quantisation and product each timed on its own with events."""
+    import torch
+    A, d, E, f = cfg.T * cfg.k, cfg.d, cfg.E, cfg.f
+    g = torch.Generator(device="cuda").manual_seed(11)
+    dgu = (torch.randn(A, 2 * f, device="cuda", generator=g) * 0.01).to(torch.bfloat16)
+    aq = torch.empty(A, 2 * f, dtype=torch.uint8, device="cuda")
+    asc = torch.empty(A, dtype=torch.float32, device="cuda")
+    wq = torch.empty(E, d, 2 * f, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(E, d, dtype=torch.float32, device="cuda")
+    dx = torch.empty(A, d, dtype=torch.bfloat16, device="cuda")
+    M.moe_quantize_fp8_transposed(w["w_gateup"].reshape(E, 2 * f, d), wq, wsc, stream)
+    t_q = timed_ms(lambda: M.moe_quantize_fp8(dgu, aq, asc, stream), 20) * 1e-3
+    t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("none", E, A, d, 2 * f, saved["offsets"], aq, asc, wq, wsc,
+                                                  dx, None, stream), 20) * 1e-3
+    tf = flop / t_g / 1e12
+    return {"gemm_us": t_g * 1e6, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS, "peak": PEAK_FP8_TFLOPS,
+            "quantize_us": t_q * 1e6, "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
+            "what": "e4m3 gate/up data gradient (dGU row-wise, W_gu quantised along 2f and stored transposed "
+                    "once) on the forward-layout fp8 grouped GEMM; dGU quantisation timed separately"}
+
+
 def main():
     args = parse()
     if args.trace_summarize:
@@ -444,6 +470,9 @@ def main():
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
     del cbuf, cdst
     fp8 = fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, fl_gu, t_gu) if not args.no_fp8 else None
+    fp8_dg = (fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flops["gate_up_dgrad"],
+                                stage_out["gate_up_dgrad"]["us"] * 1e-6)
+              if not args.no_fp8 and "gate_up_dgrad" in stage_out else None)
     # the streaming memory-bound stages (route and the index-only permute are
     # latency-bound at these sizes)
     hbm3 = ["combine", "combine_bwd", "unpermute_sum"]
@@ -489,6 +518,7 @@ def main():
                              "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
         "stages": stage_out,
         "fp8_gate_up": fp8,
+        "fp8_gate_up_dgrad": fp8_dg,
         "loads": {"max_over_mean": float(counts.max() / counts.mean()), "empty": int((counts == 0).sum())},
     }
     if not args.no_cpu_baseline:
