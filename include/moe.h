@@ -359,7 +359,12 @@ int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const voi
  *   A [M_total, K], B [G, N, K] uint8 e4m3 codes; a_scale [M_total],
  *   b_scale [G, N] fp32; C [M_total, N] bf16 (MOE_EPI_NONE) or, with
  *   MOE_EPI_SWIGLU, C [M_total, N/2] = silu(gate) * up of the scaled
- *   products and aux [M_total, N] bf16 the scaled pre-activations (or NULL).
+ *   products and aux [M_total, N] bf16 the scaled pre-activations (or NULL);
+ *   with MOE_EPI_DSWIGLU the data gradient through SwiGLU: the scaled product
+ *   is dH [M_total, N], aux [M_total, 2N] bf16 (in, required) holds the
+ *   forward pre-activations G | U, and C [M_total, 2N] receives
+ *   dG = dH U silu'(G) | dU = dH silu(G) (the down projection's data
+ *   gradient with B the down weight from moe_quantize_fp8_transposed).
  * K a multiple of 64, N a multiple of 64 (SwiGLU: N/2 a multiple of 128),
  * 1 <= G <= 256; pointers 16-byte aligned. */
 int moe_grouped_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,

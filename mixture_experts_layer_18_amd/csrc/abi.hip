@@ -615,8 +615,9 @@ int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const voi
 int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
                          const int32_t* offsets, const uint8_t* A, const float* a_scale,
                          const uint8_t* B, const float* b_scale, void* C, void* aux, void* stream) {
-  if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU) return MOE_ERR_INVALID;
+  if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU && epi != MOE_EPI_DSWIGLU) return MOE_ERR_INVALID;
   if (G < 1 || G > 256 || M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64) return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_DSWIGLU && M > 0 && !aux) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_SWIGLU && (N / 2) % 128) return MOE_ERR_INVALID;
   if (M >= (int64_t(1) << 31) || N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
   if (!offsets) return MOE_ERR_INVALID;

@@ -554,9 +554,25 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     // -------------------------------------------------------- epilogue
     bf16_t* C = a.C;
     bf16_t* X = a.aux;
+    // fp8: the row scale of this lane's output row per row block, and the
+    // column scales of the 16 columns a lane holds in a 32-wide block
+    // (columns at or past N, never stored, read the last four scales: a
+    // last column tile narrower than 256 stays inside b_scale)
+    auto col_scales = [&](int64_t brow, float* sc) __attribute__((always_inline)) {
+      const float* p = a.b_scale + (int64_t)t.g * N;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        int64_t cidx = brow + kh * 4 + gq * 8;
+        cidx = cidx < N - 4 ? cidx : N - 4;
+        const float4 v = *reinterpret_cast<const float4*>(p + cidx);
+        sc[gq * 4] = v.x; sc[gq * 4 + 1] = v.y; sc[gq * 4 + 2] = v.z; sc[gq * 4 + 3] = v.w;
+      }
+    };
     if constexpr (EPI == MOE_EPI_DSWIGLU) {
-      // NN data gradient through SwiGLU: the product is dH; aux holds the
-      // forward pre-activations G | U ([M, 2K]); C receives
+      // Data gradient through SwiGLU (NN bf16, or NT fp8 with the weight
+      // stored transposed): the product is dH (fp8: times the row and column
+      // scales); aux holds the forward pre-activations G | U ([M, 2W] for
+      // output width W); C receives
       // dG = dH U silu'(G) | dU = dH silu(G).  Each wave brings the G and U
       // rows of its outputs into its own 16 KB of the (now idle) LDS stages
       // with full-row DMA, two 32-row blocks per phase, and reads them in the
@@ -574,7 +590,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       const char* wbuf = smem + wave * WBUF;
       const uint32_t wbase = smem_base + wave * WBUF;
       const int lrow = lane / CPW, lchunk = lane % CPW;
-      const int64_t K2 = 2 * K;
+      const int64_t K2 = 2 * ncols;
 #pragma unroll
       for (int ph = 0; ph < FI / IPP; ++ph) {
         if (ph > 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the last phase's reads are done
@@ -588,8 +604,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
               int64_t i = t.i_lo + wp * WM + (ph * IPP + u) * 32 + r;
               i = i < t.i_hi ? i : t.i_hi - 1;
               int64_t col = t.j0 + wq * WN + (int64_t)((lchunk ^ swz(r)) * 8);
-              col = col < K - 8 ? col : K - 8;
-              dma16(X + i * K2 + gu * K + col,
+              col = col < ncols - 8 ? col : ncols - 8;
+              dma16(X + i * K2 + gu * ncols + col,
                     __builtin_amdgcn_readfirstlane(wbase + ((u * 2 + gu) * NI + q) * 1024));
             }
         wait_vmcnt<0>();
@@ -597,12 +613,15 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         for (int u = 0; u < IPP; ++u) {
           const int it = ph * IPP + u;
           const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
+          // fp8: the row's scale (padding rows, never stored, read the last row's)
+          const float sa = F8 ? a.a_scale[i < t.i_hi ? i : t.i_hi - 1] : 1.0f;
           const char* Gb = wbuf + (u * 2) * NI * 1024;
           const char* Ub = Gb + NI * 1024;
 #pragma unroll
           for (int jt = 0; jt < FJ; ++jt) {
             const int64_t c = t.j0 + wq * WN + jt * 32;
-            float dG[16], dU[16];
+            float dG[16], dU[16], sc[16];
+            if constexpr (F8) col_scales(c, sc);
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const int off = r32 * RBW + (((jt * 4 + gq) ^ swz(r32)) << 4) + kh * 8;
@@ -613,14 +632,15 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const float sg = sigmoid_f(Gv[e]);
-                const float dh = acc[it][jt][gq * 4 + e];
+                const float dh = F8 ? agpr_read(acc[it][jt][gq * 4 + e]) * sa * sc[gq * 4 + e]
+                                    : acc[it][jt][gq * 4 + e];
                 dG[gq * 4 + e] = dh * Uv[e] * sg * (1.0f + Gv[e] * (1.0f - sg));
                 dU[gq * 4 + e] = dh * Gv[e] * sg;
               }
             }
-            if (i < t.i_hi && c < K) {
-              store_tile_row(C + i * K2 + c, dG, kh, K - c);
-              store_tile_row(C + i * K2 + K + c, dU, kh, K - c);
+            if (i < t.i_hi && c < ncols) {
+              store_tile_row(C + i * K2 + c, dG, kh, ncols - c);
+              store_tile_row(C + i * K2 + ncols + c, dU, kh, ncols - c);
             }
           }
         }
@@ -682,16 +702,6 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       continue;
     }
     prefetch_next();
-    // fp8: the row scale of this lane's output row per row block, and the
-    // column scales of the 16 columns a lane holds in a 32-wide block
-    auto col_scales = [&](int64_t brow, float* sc) __attribute__((always_inline)) {
-      const float* p = a.b_scale + (int64_t)t.g * N + brow + kh * 4;
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const float4 v = *reinterpret_cast<const float4*>(p + gq * 8);
-        sc[gq * 4] = v.x; sc[gq * 4 + 1] = v.y; sc[gq * 4 + 2] = v.z; sc[gq * 4 + 3] = v.w;
-      }
-    };
 #pragma unroll
     for (int it = 0; it < FI; ++it) {
       __builtin_amdgcn_sched_barrier(0);
@@ -862,6 +872,7 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
   a.rows = nullptr;
   if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true>(a, st);
   if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true>(a, st);
+  if (epilogue == MOE_EPI_DSWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_DSWIGLU, true>(a, st);
   return hipErrorInvalidValue;
 }
 }  // namespace moe

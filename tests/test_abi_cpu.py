@@ -214,7 +214,8 @@ def test_fp8_argument_checks(lib):
     assert tq(3, 0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
     # gemm: layout limits
     args = (a, a, a, a, a, a, None, None)
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_DSWIGLU, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_DSWIGLU, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID  # no aux
+    assert lib.moe_grouped_gemm_fp8(3, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID
     assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 0, 100, 256, 128, *args) == L.MOE_ERR_INVALID
     assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 100, 256, 96, *args) == L.MOE_ERR_INVALID
     assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_SWIGLU, 4, 100, 384, 128, *args) == L.MOE_ERR_INVALID

@@ -183,3 +183,44 @@ def test_fp8_data_gradient_against_oracle():
     assert np.array_equal(qw.cpu().numpy(), qwo) and np.array_equal(sw.cpu().numpy(), swo)
     ref = O.grouped_gemm_fp8_nt(qao, sao, qwo, swo, off)
     assert_rounded(host(C), ref, "bf16", "dX")
+
+
+def test_fp8_down_data_gradient_dswiglu_against_oracle():
+    """The down projection's data gradient in fp8 with the dSwiGLU epilogue:
+    dH = dY~ . W_d[e] (W_d [G, d, f], reduction over d) with dY~ quantised
+    row-wise and W_d quantised along d and stored transposed, run in the
+    forward layout; the epilogue turns dH and the pre-activations G | U into
+    dG | dU.  Ragged groups and an empty one."""
+    g = np.random.default_rng(45)
+    G, d, f = 4, 256, 384
+    m = g.integers(30, 260, size=G)
+    m[1] = 0
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(m)
+    Mt = int(off[-1])
+    dyb = _bf16(g, (Mt, d))
+    wdb = _bf16(g, (G, d, f), 1 / np.sqrt(d))
+    preb = _bf16(g, (Mt, 2 * f))
+    qa, sa = _quant_gpu(dyb)
+    qw = torch.empty(G, f, d, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(G, f, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_transposed(dev(wdb), qw, sw)
+    C = torch.empty(Mt, 2 * f, dtype=torch.bfloat16, device="cuda")
+    print(f"[fp8] down data gradient + dSwiGLU G={G} M={Mt} d={d} f={f}", flush=True)
+    M.moe_grouped_gemm_fp8("dswiglu", G, Mt, f, d, dev(off), qa, sa, qw, sw, C, dev(preb))
+    torch.cuda.synchronize()
+    qao, sao = O.quantize_rowwise(synth.bf16_bits_to_f32(dyb))
+    qwo, swo = O.quantize_rowwise_transposed(synth.bf16_bits_to_f32(wdb))
+    dH = O.grouped_gemm_fp8_nt(qao, sao, qwo, swo, off)
+    pre = synth.bf16_bits_to_f32(preb).astype(np.float64)
+    Gm, U = pre[:, :f], pre[:, f:]
+    z = np.zeros((Mt, 1))
+    zw = np.zeros((f, 1))
+    _, _, _, _, dG, dU = O.swiglu_ffn_backward(z, zw, zw, np.eye(f), Gm, U, O.silu(Gm) * U, dH)
+    # dG and dU are one rounding of dH times a factor of the pre-activations;
+    # dH may carry the accumulation noise allowed for a product (1e-4 of its
+    # RMS), which reaches dG through |U silu'(G)| and dU through |silu(G)|
+    e = 1e-4 * np.sqrt(np.mean(dH * dH))
+    sg = 1.0 / (1.0 + np.exp(-Gm))
+    inherited = np.concatenate([np.abs(U * sg * (1.0 + Gm * (1.0 - sg))), np.abs(O.silu(Gm))], axis=1) * e
+    assert_rounded(host(C), np.concatenate([dG, dU], axis=1), "bf16", "dG | dU", extra=inherited)
