@@ -290,6 +290,33 @@ def fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
                     "once) on the forward-layout fp8 grouped GEMM; dGU quantisation timed separately"}
 
 
+def fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
+    """The down projection's data gradient in fp8 with the dSwiGLU epilogue
+    on the same routing: dY~ (synthetic, N(0, 0.2^2), the layer's shape)
+    quantised row-wise, W_d quantised along d and stored transposed (once,
+    outside the timing), the layer's own pre-activations G | U; quantisation
+    and product each timed on its own with events."""
+    import torch
+    A, d, E, f = cfg.T * cfg.k, cfg.d, cfg.E, cfg.f
+    g = torch.Generator(device="cuda").manual_seed(13)
+    dyp = (torch.randn(A, d, device="cuda", generator=g) * 0.2).to(torch.bfloat16)
+    aq = torch.empty(A, d, dtype=torch.uint8, device="cuda")
+    asc = torch.empty(A, dtype=torch.float32, device="cuda")
+    wq = torch.empty(E, f, d, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(E, f, dtype=torch.float32, device="cuda")
+    dgu = torch.empty(A, 2 * f, dtype=torch.bfloat16, device="cuda")
+    M.moe_quantize_fp8_transposed(w["w_down"].reshape(E, d, f), wq, wsc, stream)
+    t_q = timed_ms(lambda: M.moe_quantize_fp8(dyp, aq, asc, stream), 20) * 1e-3
+    t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("dswiglu", E, A, f, d, saved["offsets"], aq, asc, wq, wsc,
+                                                  dgu, saved["preact"], stream), 20) * 1e-3
+    tf = flop / t_g / 1e12
+    return {"gemm_us": t_g * 1e6, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS, "peak": PEAK_FP8_TFLOPS,
+            "quantize_us": t_q * 1e6, "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
+            "what": "e4m3 down data gradient with the dSwiGLU epilogue (dY~ row-wise, W_d quantised along d and "
+                    "stored transposed once) on the forward-layout fp8 grouped GEMM; dY~ quantisation timed "
+                    "separately"}
+
+
 def main():
     args = parse()
     if args.trace_summarize:
@@ -473,6 +500,9 @@ def main():
     fp8_dg = (fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flops["gate_up_dgrad"],
                                 stage_out["gate_up_dgrad"]["us"] * 1e-6)
               if not args.no_fp8 and "gate_up_dgrad" in stage_out else None)
+    fp8_dd = (fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flops["down_dgrad"],
+                             stage_out["down_dgrad"]["us"] * 1e-6)
+              if not args.no_fp8 and "down_dgrad" in stage_out and saved.get("preact") is not None else None)
     # the streaming memory-bound stages (route and the index-only permute are
     # latency-bound at these sizes)
     hbm3 = ["combine", "combine_bwd", "unpermute_sum"]
@@ -519,6 +549,7 @@ def main():
         "stages": stage_out,
         "fp8_gate_up": fp8,
         "fp8_gate_up_dgrad": fp8_dg,
+        "fp8_down_dgrad": fp8_dd,
         "loads": {"max_over_mean": float(counts.max() / counts.mean()), "empty": int((counts == 0).sum())},
     }
     if not args.no_cpu_baseline:

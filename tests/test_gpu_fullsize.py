@@ -206,3 +206,59 @@ def test_full_size_fp8_gate_up_data_gradient():
             "transposed weight codes/scales"
         ref = O.grouped_gemm_fp8_nt(qa, sa, qw, sw, np.array([0, rows.size]))
         assert_rounded(dx_all[rows], ref, "bf16", f"dX, expert {e}")
+
+
+def test_full_size_fp8_down_data_gradient():
+    """The fp8 down data gradient with the dSwiGLU epilogue as the benchmark
+    times it (7B-style routing, 98304 rows, dY~ ~ N(0, 0.2^2) and the
+    pre-activations G | U ~ N(0, 1) drawn on the host, W_d quantised along d
+    and stored transposed), checked on sampled rows of six experts: codes and
+    scales bit-exact, dG | dU within one bf16 rounding plus the noise dH may
+    carry through the dSwiGLU factors."""
+    cfg = synth.CONFIG_BY_NAME["moe7b_bf16"]
+    print(f"[full] {cfg.name} fp8 down data gradient: generating inputs", flush=True)
+    inp = synth.make_inputs(cfg, with_dy=False)
+    w = R.upload_layer(cfg, inp)
+    x = dev(inp["x"])
+    g = R.run_gpu(cfg, inp, backward=False, weights=w, x=x, keep_device=True, gather=True)
+    A, d, E, f = cfg.T * cfg.k, cfg.d, cfg.E, cfg.f
+    rng = np.random.default_rng(14)
+    dyb = synth.f32_to_bf16_bits((rng.standard_normal((A, d), dtype=np.float32) * 0.2).astype(np.float32))
+    preb = synth.f32_to_bf16_bits(rng.standard_normal((A, 2 * f), dtype=np.float32))
+    aq = torch.empty(A, d, dtype=torch.uint8, device="cuda")
+    asc = torch.empty(A, dtype=torch.float32, device="cuda")
+    wq = torch.empty(E, f, d, dtype=torch.uint8, device="cuda")
+    wsc = torch.empty(E, f, dtype=torch.float32, device="cuda")
+    dgu = torch.empty(A, 2 * f, dtype=torch.bfloat16, device="cuda")
+    print(f"[full] {cfg.name} fp8 down data gradient: GPU quantisation and grouped GEMM", flush=True)
+    M.moe_quantize_fp8(dev(dyb), aq, asc)
+    M.moe_quantize_fp8_transposed(w["w_down"].reshape(E, d, f), wq, wsc)
+    M.moe_grouped_gemm_fp8("dswiglu", E, A, f, d, g["saved"]["offsets"], aq, asc, wq, wsc, dgu, dev(preb))
+    torch.cuda.synchronize()
+
+    off = g["saved"]["offsets"].cpu().numpy().astype(np.int64)
+    counts = np.diff(off)
+    nz = np.where(counts > 0)[0]
+    experts = [int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])]
+    experts += [int(e) for e in rng.choice(np.setdiff1d(nz, experts), size=4, replace=False)]
+    out, aq_h, asc_h = host(dgu), aq.cpu().numpy(), asc.cpu().numpy()
+    z, zw = None, np.zeros((f, 1))
+    for e in experts:
+        lo, hi = int(off[e]), int(off[e + 1])
+        rows = np.unique(np.concatenate([[lo, hi - 1], rng.integers(lo, hi, size=min(30, hi - lo))]))
+        print(f"[full] fp8 down data gradient: expert {e} ({hi - lo} rows), {rows.size} sampled", flush=True)
+        qa, sa = O.quantize_rowwise(synth.bf16_bits_to_f32(dyb[rows]))
+        qw, sw = O.quantize_rowwise_transposed(synth.as_f64(inp["w_down"][e], "bf16")[None])
+        assert np.array_equal(aq_h[rows], qa) and np.array_equal(asc_h[rows], sa), "dY~ row codes/scales"
+        assert np.array_equal(wq[e].cpu().numpy(), qw[0]) and np.array_equal(wsc[e].cpu().numpy(), sw[0]), \
+            "transposed weight codes/scales"
+        dH = O.grouped_gemm_fp8_nt(qa, sa, qw, sw, np.array([0, rows.size]))
+        pre = synth.bf16_bits_to_f32(preb[rows]).astype(np.float64)
+        Gm, U = pre[:, :f], pre[:, f:]
+        z = np.zeros((rows.size, 1))
+        _, _, _, _, dG, dU = O.swiglu_ffn_backward(z, zw, zw, np.eye(f), Gm, U, O.silu(Gm) * U, dH)
+        err = 1e-4 * np.sqrt(np.mean(dH * dH))
+        sg = 1.0 / (1.0 + np.exp(-Gm))
+        inherited = np.concatenate([np.abs(U * sg * (1.0 + Gm * (1.0 - sg))), np.abs(O.silu(Gm))], axis=1) * err
+        assert_rounded(out[rows], np.concatenate([dG, dU], axis=1), "bf16", f"dG | dU, expert {e}",
+                       extra=inherited)
