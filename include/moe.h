@@ -28,8 +28,11 @@
  * Conventions for every call:
  *  - All tensor pointers are DEVICE pointers to row-major, contiguous data,
  *    16-byte aligned (else MOE_ERR_ALIGN).  The caller owns every buffer;
- *    the library allocates nothing, frees nothing and keeps no state between
- *    calls.  Workspaces are caller-provided, sized by the query functions.
+ *    the compute calls allocate no memory, free nothing and keep no state
+ *    between calls.  Workspaces are caller-provided, sized by the query
+ *    functions.  The one stateful part is the per-stage timing aid
+ *    (moe_stage_timing below): while enabled it creates HIP events and keeps
+ *    process-wide records of them.
  *  - bf16 means IEEE bfloat16 bit patterns (uint16 storage).
  *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
  *    default stream).  No call synchronises or copies device->host: counts
@@ -39,8 +42,8 @@
  *    failures return MOE_ERR_HIP.  Nothing aborts or throws across the ABI.
  *  - Results are bitwise deterministic for fixed inputs (no float atomics).
  *  - Every output element is written (empty experts get zero weight grads).
- *  - The library is stateless; concurrent calls on different streams with
- *    disjoint outputs are safe.
+ *  - Apart from the timing aid, the library is stateless; concurrent calls on
+ *    different streams with disjoint outputs are safe.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

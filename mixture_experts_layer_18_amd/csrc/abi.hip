@@ -189,11 +189,22 @@ void stage_end(StageRec r, hipStream_t st) {
     g_spare.push_back(r);
 }
 
+// A stage whose launch failed: its event pair goes back unrecorded.
+void stage_abort(StageRec r) {
+  if (r.stage < 0) return;
+  std::lock_guard<std::mutex> lk(g_timing_mu);
+  g_spare.push_back(r);
+}
+
 // Runs the launches of one stage between its two events.
 #define MOE_STAGE(stage, expr)                    \
   do {                                            \
     const StageRec _r = stage_begin((stage), st); \
-    MOE_TRY(expr);                                \
+    const hipError_t _e = (expr);                 \
+    if (_e != hipSuccess) {                       \
+      stage_abort(_r);                            \
+      return MOE_ERR_HIP;                         \
+    }                                             \
     stage_end(_r, st);                            \
   } while (0)
 
@@ -395,8 +406,9 @@ static int gather_supported(const moe_desc_t* d, bool training) {
   return MOE_OK;
 }
 
-int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
-                const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
+// The forward pass of moe_forward on the workspace ws (ws_bytes of it).
+static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
+                        const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(d);
   if (s) return s;
   if (!w || !sv) return MOE_ERR_INVALID;
@@ -463,6 +475,11 @@ int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void
   MOE_STAGE(MOE_STAGE_COMBINE, launch_combine(dt, sv->y_perm, sv->gate, sv->pos, F > 0 ? y : nullptr, y, (int)T,
                          (int)D, (int)k, st));
   return MOE_OK;
+}
+
+int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
+                const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(d, w, x, y, sv, ws, ws_bytes, stream);
 }
 
 int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,

@@ -801,21 +801,34 @@ static hipError_t run(const Args& a, hipStream_t st) {
 // a tile pairs 128 gate with 128 up columns), the plain data gradient, and the
 // weight gradient when it has enough 256 x 256 tiles to fill
 // the chip without row slices (gathered rows: any tile count).
+//
+// Operand DMA offsets are 32-bit byte offsets from a per-tile base: NT's
+// SwiGLU weight rows span one expert's whole [N, K] block (gate and up
+// halves), NN's strided weight likewise, and TN's operands one group's rows.
+// Products whose offsets could pass 2^32 bytes go to the two-workgroup kernel
+// (64-bit addresses).
 bool gemm_big_supported(const GemmProblem& p) {
   if (p.ta != MOE_BF16 || p.tb != MOE_BF16 || p.tc != MOE_BF16 || p.G > 256) return false;
   if (p.rows && p.layout == MOE_GEMM_NN) return false;
+  const int64_t lim = int64_t(1) << 32;
   if (p.layout == MOE_GEMM_NT) {
-    if (p.epilogue == MOE_EPI_SWIGLU) return (p.N / 2) % 128 == 0;
+    if (p.epilogue == MOE_EPI_SWIGLU) return (p.N / 2) % 128 == 0 && p.N * p.K * 2 <= lim;
     return p.epilogue == MOE_EPI_NONE;
   }
   if (p.layout == MOE_GEMM_TN) {
-      // few tiles: row slices on the two-workgroup kernel fill the chip better,
+    // few tiles: row slices on the two-workgroup kernel fill the chip better,
     // but gathered rows are read by this kernel only.  A partial last column
     // tile (K not a multiple of 256) is clamped on load and masked on store.
+    // Gathered rows: the row map's offsets are bounded by the caller's token
+    // count (src_rows * K * 2 <= 2^32, checked where the map is accepted);
+    // the group's own rows (A) by M_total * N * 2.
+    if (p.M_total * p.N * 2 > lim) return false;
     if (p.rows) return p.K % 256 == 0;
+    if (p.M_total * p.K * 2 > lim) return false;
     return p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256;
   }
-  if (p.layout == MOE_GEMM_NN) return p.epilogue == MOE_EPI_NONE || p.epilogue == MOE_EPI_DSWIGLU;
+  if (p.layout == MOE_GEMM_NN)
+    return (p.epilogue == MOE_EPI_NONE || p.epilogue == MOE_EPI_DSWIGLU) && p.N * p.K * 2 <= lim;
   return false;
 }
 

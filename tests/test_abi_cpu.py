@@ -68,6 +68,22 @@ def test_weight_gradient_slice_counts(lib):
     assert ws(1, 600, 256, 384) == 0
 
 
+def test_persistent_kernel_offset_limit(lib):
+    """The persistent kernel's operand DMA uses 32-bit byte offsets from a
+    group's first row.  A one-group weight gradient whose operand spans more
+    than 2^32 bytes goes to the two-workgroup kernel (64-bit addresses, row
+    slices with fp32 partials: a nonzero workspace); at exactly 2^32 bytes the
+    last 16-byte load still starts below 2^32 and the persistent kernel (no
+    workspace) takes it."""
+    ws = lambda G, M, N, K: lib.moe_grouped_gemm_workspace_bytes(L.MOE_GEMM_TN, L.MOE_BF16, G, M, N, K)  # noqa: E731
+    # 131072 tokens x (2 x 4096 shared experts): 131072 * 16384 * 2 = 2^32 bytes
+    assert ws(1, 131072, 16384, 4096) == 0
+    assert ws(1, 131072, 16448, 4096) > 0
+    # the other operand (K columns) is bounded the same way
+    assert ws(1, 131072, 4096, 16384) == 0
+    assert ws(1, 131072, 4096, 16448) > 0
+
+
 BAD = [
     dict(E=0), dict(E=257), dict(k=0), dict(k=17), dict(k=9, E=8), dict(d=100), dict(f=96),
     dict(T=-1), dict(score=2), dict(renorm=2), dict(dtype=3), dict(reserved=1), dict(n_shared=1, f_shared=0),
