@@ -288,6 +288,24 @@ int moe_combine(const moe_desc_t *desc, const void *y_perm, const float *gate,
 int moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *x, void *y,
                 const moe_saved_t *saved, void *ws, size_t ws_bytes, void *stream);
 
+/* moe_forward for callers that cannot allocate device memory or pass a
+ * workspace: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  Same arguments and results as moe_forward (bit for
+ * bit: the same kernels) without ws; its scratch (the routing histogram, its
+ * scan and a one-group offset table) lives in a device array of
+ * MOE_STATIC_SCRATCH_BYTES inside the library, one copy per GPU, held until
+ * the process ends.  Allocates nothing and calls no allocating routine.
+ *   MOE_ERR_WORKSPACE when the layer needs more scratch than that
+ *   (moe_workspace_bytes(desc, MOE_WS_FORWARD) > MOE_STATIC_SCRATCH_BYTES,
+ *   which is about E * ceil(T / 32) > 2^20 with E experts and T tokens).
+ * Every call on one GPU shares that GPU's array: calls that overlap in time
+ * on one GPU (different streams, or different host threads) race and must
+ * not be issued; calls in one stream are ordered and safe.  The stream must
+ * belong to the current device. */
+#define MOE_STATIC_SCRATCH_BYTES (8u << 20)
+int moe_forward_no_workspace(const moe_desc_t *desc, const moe_weights_t *w, const void *x, void *y,
+                             const moe_saved_t *saved, void *stream);
+
 /* Whole backward pass for upstream gradient dy [T, d]: combine backward
  * (gate gradient), router backward (through the gates only; the bias gets no
  * gradient), down and gate/up data and weight gradients, shared experts,

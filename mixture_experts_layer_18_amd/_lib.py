@@ -73,6 +73,7 @@ SIGNATURES = {
                                  c_vp, c_vp, c_sz, c_vp]),
     "moe_combine": (c_i32, [_P(MoeDesc), c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_forward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, c_vp, _P(MoeSaved), c_vp, c_sz, c_vp]),
+    "moe_forward_no_workspace": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, c_vp, _P(MoeSaved), c_vp]),
     "moe_backward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, _P(MoeSaved), c_vp, c_vp, _P(MoeGrads),
                              _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
     "moe_bias_update": (c_i32, [_P(MoeDesc), c_vp, ctypes.c_float, c_vp, c_vp]),

@@ -127,6 +127,14 @@ def moe_forward(desc, weights: dict, x, y, saved: dict, ws, stream=None):
                                 ws.numel() * ws.element_size(), _stream(stream)), "moe_forward")
 
 
+def moe_forward_no_workspace(desc, weights: dict, x, y, saved: dict, stream=None):
+    """moe_forward with the library's own device scratch instead of a workspace."""
+    w = _weights(weights)
+    s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
+    _check(L.load().moe_forward_no_workspace(ctypes.byref(desc), ctypes.byref(w), _p(x), _p(y), ctypes.byref(s),
+                                             _stream(stream)), "moe_forward_no_workspace")
+
+
 def moe_backward(desc, weights: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None, terms=None,
                  losses=None):
     """terms: None or dict(aux_coeff=, seq_aux_coeff=, z_coeff=, seq_len=); losses: None or a float32

@@ -208,6 +208,36 @@ void stage_abort(StageRec r) {
     stage_end(_r, st);                            \
   } while (0)
 
+// ---- the device-resident scratch of moe_forward_no_workspace
+// One copy per GPU, held until the process ends.  Host code never uses the
+// array's name as an address: its device address is looked up once per
+// device with hipGetSymbolAddress (with that device current) and kept here.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device).
+int scratch_device_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -480,6 +510,18 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
 int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
                 const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
   return forward_impl(d, w, x, y, sv, ws, ws_bytes, stream);
+}
+
+int moe_forward_no_workspace(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
+                             const moe_saved_t* sv, void* stream) {
+  const int s = check_desc(d);
+  if (s) return s;
+  const size_t need = fwd_ws(d, nullptr, nullptr);
+  if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int r = scratch_device_ptr(&ws);
+  if (r) return r;
+  return forward_impl(d, w, x, y, sv, ws, MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
 int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,

@@ -84,6 +84,17 @@ def test_persistent_kernel_offset_limit(lib):
     assert ws(1, 131072, 4096, 16448) > 0
 
 
+def test_no_workspace_forward_rejects_large_layers(lib):
+    """moe_forward_no_workspace keeps its scratch in a fixed device array of
+    MOE_STATIC_SCRATCH_BYTES (8 MiB): a layer whose forward scratch (two int32
+    tables of E x ceil(T/32) entries) exceeds it is rejected on the host."""
+    d = make_desc(131072, 2048, 256, 8, 512, 0, 0, "sigmoid", True, "bf16")
+    assert lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_FORWARD) > 8 << 20
+    assert lib.moe_forward_no_workspace(ctypes.byref(d), None, None, None, None, None) == L.MOE_ERR_WORKSPACE
+    bad = make_desc(64, 100, 8, 2, 256, 0, 0, "softmax", False, "f32")
+    assert lib.moe_forward_no_workspace(ctypes.byref(bad), None, None, None, None, None) == L.MOE_ERR_INVALID
+
+
 BAD = [
     dict(E=0), dict(E=257), dict(k=0), dict(k=17), dict(k=9, E=8), dict(d=100), dict(f=96),
     dict(T=-1), dict(score=2), dict(renorm=2), dict(dtype=3), dict(reserved=1), dict(n_shared=1, f_shared=0),
