@@ -47,6 +47,9 @@ def parse():
     p.add_argument("--trace-summarize", metavar="TRACE_DIR",
                    help="write the kernel-trace summary of a profiled run (rocprofv3 --kernel-trace --stats "
                         "--output-format csv -o bench) to profiles/moe7b_bf16_fwd_bwd_kernel_stats.txt")
+    p.add_argument("--pmc-report", nargs="+", metavar="PASS_DIR",
+                   help="turn the counter CSVs of the pmc_mfma, pmc_ea_read and pmc_ea_write passes over "
+                        "--pmc-probe into the per-product counter table under profiles/")
     p.add_argument("--pmc-summarize", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                    help="turn the counter CSVs of a FETCH_SIZE pass and a WRITE_SIZE pass over "
                         "--pmc-probe into the traffic record under profiles/")
@@ -198,6 +201,158 @@ def pmc_summarize(fetch_dir, write_dir):
     print("\n".join(lines))
 
 
+# ---- matrix-core utilisation, clock and LDS behaviour of every product
+COUNTER_FILE = os.path.join(ROOT, "profiles", "gemm_counters_moe7b_bf16.txt")
+PMC_PASSES = {
+    "mfma": "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU_MFMA_MOPS_F8 SQ_BUSY_CU_CYCLES "
+            "GRBM_GUI_ACTIVE GRBM_COUNT",
+    "lds": "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_INSTS_LDS SQ_WAVE_CYCLES",
+    "ea_read": "TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum",
+    "ea_write": "TCC_EA0_WRREQ_sum TCC_EA0_WRREQ_64B_sum",
+}
+SIMDS, XCDS, CUS = 1024, 8, 256
+# the probe's launches, in order, named by stage (kernel symbol prefix,
+# occurrence among the probe's dispatches of that symbol)
+PROBE_STAGES = [
+    ("pk::gemm_kernel<0, 1, false, true, 8>", 1, "gate_up (in the forward)"),
+    ("pk::gemm_kernel<0, 0, false, false, 8>", 1, "down"),
+    ("pk::gemm_kernel<0, 1, false, false, 8>", 1, "shared_gate_up"),
+    ("pk::gemm_kernel<0, 0, false, false, 8>", 2, "shared_down"),
+    ("pk::gemm_kernel<0, 1, false, true, 8>", 2, "gate_up (alone, after the copy)"),
+    ("pk::gemm_kernel<1, 2, false, false, 8>", 1, "down_dgrad (dSwiGLU)"),
+    ("pk::gemm_kernel<2, 0, false, false, 8>", 1, "down_wgrad"),
+    ("pk::gemm_kernel<2, 0, false, true, 8>", 1, "gate_up_wgrad"),
+    ("pk::gemm_kernel<1, 0, false, false, 8>", 1, "gate_up_dgrad"),
+    ("pk::gemm_kernel<1, 2, false, false, 8>", 2, "shared_down_dgrad"),
+    ("mf::gemm_kernel<2, 0,", 1, "shared_down_wgrad (two-workgroup kernel)"),
+    ("mf::gemm_kernel<2, 0,", 2, "shared_gate_up_wgrad (two-workgroup kernel)"),
+    ("pk::gemm_kernel<1, 0, false, false, 8>", 2, "shared_gate_up_dgrad"),
+    ("pk::gemm_kernel<0, 1, true, false, 8>", 1, "fp8 gate_up"),
+]
+PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counters} -d <root>/gpurun_out/pmc_{name} -o run "
+               "--output-format csv -- python3 <root>/bench.py --pmc-probe")
+
+
+def _dispatches(d):
+    """{dispatch id: (kernel name, duration ns, {counter: value})} of one pass."""
+    out = {}
+    for r in _counter_rows(d):
+        i = int(r["Dispatch_Id"])
+        if i not in out:
+            out[i] = (r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), {})
+        out[i][2][r["Counter_Name"]] = float(r["Counter_Value"])
+    return out
+
+
+def pmc_report(dirs):
+    """Per-product counter table of the probe from the passes in dirs
+    (directories named pmc_<pass>): matrix-core busy share, shader clock,
+    LDS bank conflicts, and the memory-side read/write bytes by request size,
+    scaled by what the same counters read for the 1 GiB device copy."""
+    passes = {}
+    for d in dirs:
+        name = os.path.basename(os.path.normpath(d))[len("pmc_"):]
+        passes[name] = _dispatches(d)
+    # dispatch ids are per process (one process per pass); the probe's launch
+    # sequence is the same in each, so ids line up across passes
+    base = passes["mfma"]
+    seen = {}
+    rows = []
+    copy_id = max(i for i, (k, _, _) in base.items() if "copyBuffer" in k)
+    prefixes = {pre for pre, _, _ in PROBE_STAGES}
+    for i in sorted(base):
+        k, dur, cv = base[i]
+        pre = next((p for p in prefixes if k.replace("void ", "").startswith("moe::" + p)), None)
+        if pre is None:
+            continue
+        seen[pre] = seen.get(pre, 0) + 1
+        for p, occ, label in PROBE_STAGES:
+            if p == pre and occ == seen[pre]:
+                rows.append((label, i, k, dur))
+    def cal(pname, keys):
+        ids = passes.get(pname)
+        if ids is None:
+            return None
+        c = ids[copy_id][2]
+        return {kk: c.get(kk, 0.0) for kk in keys}
+    rd_keys = ["TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"]
+    wr_keys = ["TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_64B_sum"]
+
+    def rd_bytes(c):
+        n, n32, n64, n128 = (c.get(kk, 0.0) for kk in rd_keys)
+        return 32 * n32 + 64 * n64 + 128 * n128, n - n32 - n64 - n128
+
+    def wr_bytes(c):
+        n, n64 = (c.get(kk, 0.0) for kk in wr_keys)
+        return 64 * n64 + 32 * (n - n64)
+    crd = cal("ea_read", rd_keys)
+    cwr = cal("ea_write", wr_keys)
+    rd_fac = rd_bytes(crd)[0] / COPY_BYTES if crd else None
+    wr_fac = wr_bytes(cwr) / COPY_BYTES if cwr else None
+    L = ["Hardware counters of every grouped-GEMM product of one moe7b_bf16 layer step (T=16384, d_model=2048,",
+         "E=64, sigmoid top-6, d_ff=1408, 2 shared x 1408, bf16; rows gathered), one MI355X, one dispatch each.",
+         "", "Commands (from the repository root; one counter set per pass, each pass its own run):",
+         "  cd /tmp && export TMPDIR=/tmp"]
+    for pname, ctrs in PMC_PASSES.items():
+        L.append("  " + PMC_COMMAND.format(counters=ctrs, name=pname))
+    L += ["  python bench.py --pmc-report " + " ".join(f"gpurun_out/pmc_{n}" for n in PMC_PASSES), "",
+          "mfma busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): the share of the",
+          "kernel's cycles in which a SIMD's matrix core was busy.  clock = GRBM_GUI_ACTIVE / 8 / duration.",
+          "flop check = SQ_INSTS_VALU_MFMA_MOPS_* x 512 (the matrix-core work actually issued, padding rows",
+          "included).  lds conflict = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE.  read / write = memory-side",
+          "bytes from the request counts by size (32/64/128 B), divided by the factor the same counters read",
+          "for the 1 GiB copy (read {}, write {}).".format(
+              "n/a" if rd_fac is None else f"{rd_fac:.4f}", "n/a" if wr_fac is None else f"{wr_fac:.4f}"), ""]
+    L.append(f"{'product':<44s} {'us':>8s} {'mfma busy':>9s} {'clock':>6s} {'issued TFLOP':>12s} "
+             f"{'lds conf':>8s} {'read GB':>8s} {'write GB':>8s}")
+    recs = {}
+    for label, i, k, dur in rows:
+        cv = dict(base[i][2])
+        if "lds" in passes:
+            cv.update({kk: v for kk, v in passes["lds"][i][2].items() if kk.startswith("SQ_LDS")})
+        gui = cv.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+        busy = cv.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * SIMDS) if gui else 0.0
+        clk = gui / dur if dur else 0.0  # cycles per ns = GHz
+        mops = cv.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + cv.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0)
+        lc = cv.get("SQ_LDS_BANK_CONFLICT", 0.0) / max(cv.get("SQ_LDS_IDX_ACTIVE", 0.0), 1.0)
+        rb = wb = None
+        if "ea_read" in passes and rd_fac:
+            rb = rd_bytes(passes["ea_read"][i][2])[0] / rd_fac
+        if "ea_write" in passes and wr_fac:
+            wb = wr_bytes(passes["ea_write"][i][2]) / wr_fac
+        recs[label] = {"us": dur / 1e3, "mfma_busy": busy, "clock_ghz": clk, "issued_flop": mops * 512,
+                       "lds_conflict": lc, "read_bytes": rb, "write_bytes": wb}
+        L.append(f"{label[:44]:<44s} {dur/1e3:8.1f} {100*busy:8.1f}% {clk:6.2f} {mops*512/1e12:12.1f} "
+                 f"{100*lc:7.2f}% {'' if rb is None else f'{rb/1e9:8.3f}':>8s} "
+                 f"{'' if wb is None else f'{wb/1e9:8.3f}':>8s}")
+    if crd:
+        b, other = rd_bytes(crd)
+        L += ["", f"copy calibration (1 GiB read + 1 GiB written): read requests 32B {crd[rd_keys[1]]:.0f}, 64B "
+              f"{crd[rd_keys[2]]:.0f}, 128B {crd[rd_keys[3]]:.0f}, unclassified {other:.0f}; write requests "
+              f"{cwr[wr_keys[0]] if cwr else 0:.0f} ({cwr[wr_keys[1]] if cwr else 0:.0f} of 64B)"]
+    rec = {"kernel_source_sha": kernel_source_hash(), "products": recs, "read_factor": rd_fac,
+           "write_factor": wr_fac}
+    L += ["", "record: " + json.dumps(rec)]
+    os.makedirs(os.path.dirname(COUNTER_FILE), exist_ok=True)
+    with open(COUNTER_FILE, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L))
+
+
+def measured_counters():
+    """The counter record of the products, or None when it is missing or the
+    kernel sources changed since it was taken."""
+    try:
+        with open(COUNTER_FILE) as fh:
+            rec = [ln for ln in fh if ln.startswith("record: ")]
+        rec = json.loads(rec[-1][len("record: "):])
+    except (OSError, IndexError, ValueError):
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_hash():
+        return None
+    return rec
+
+
 def measured_traffic():
     """Traffic bytes per launch from the committed record, or None when the
     record is missing or the kernel source changed since it was taken."""
@@ -325,6 +480,9 @@ def main():
     if args.pmc_summarize:
         pmc_summarize(*args.pmc_summarize)
         return
+    if args.pmc_report:
+        pmc_report(args.pmc_report)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this MoE layer build has no multi-GPU path "
               "(expert-parallel sharding is described in DESIGN.md but not built)", file=sys.stderr)
@@ -374,12 +532,17 @@ def main():
             M.moe_bias_update(desc, saved["counts"], 1e-3, w["bias"], stream)
 
     if args.pmc_probe:
+        # one forward, a 1 GiB device copy (the counters' calibration), the
+        # gate/up product alone, then one backward and the fp8 gate/up product
+        # with its activation quantisation: every product of the layer is one
+        # counted dispatch
         M.moe_forward(desc, w, x, y, saved, wsf, stream)
         src = torch.ones(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         dst.copy_(src)
         torch.cuda.synchronize()
+        del src, dst
         if gather:
             M.moe_grouped_gemm_gather("NT", "swiglu", cfg.E, cfg.T * cfg.k, 2 * cfg.f, cfg.d, saved["offsets"],
                                       x, w["w_gateup"], saved["h"], saved["tok"], cfg.T, saved["preact"],
@@ -389,6 +552,20 @@ def main():
                                saved["offsets"], saved["x_perm"], w["w_gateup"], saved["h"],
                                saved["preact"], None, stream)
         torch.cuda.synchronize()
+        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, stream)
+        torch.cuda.synchronize()
+        if not args.no_fp8 and cfg.dtype == "bf16":
+            A, d_, E_, f_ = cfg.T * cfg.k, cfg.d, cfg.E, cfg.f
+            xq = torch.empty(A, d_, dtype=torch.uint8, device="cuda")
+            xs = torch.empty(A, dtype=torch.float32, device="cuda")
+            wq = torch.empty(E_ * 2 * f_, d_, dtype=torch.uint8, device="cuda")
+            wsc = torch.empty(E_ * 2 * f_, dtype=torch.float32, device="cuda")
+            M.moe_quantize_fp8(w["w_gateup"].reshape(E_ * 2 * f_, d_), wq, wsc, stream)
+            xp = saved["x_perm"] if saved["x_perm"] is not None else x[saved["tok"].long()].contiguous()
+            M.moe_quantize_fp8(xp, xq, xs, stream)
+            M.moe_grouped_gemm_fp8("swiglu", E_, A, 2 * f_, d_, saved["offsets"], xq, xs, wq, wsc, saved["h"],
+                                   saved["preact"], stream)
+            torch.cuda.synchronize()
         print("pmc probe done", flush=True)
         return
 
@@ -488,6 +665,8 @@ def main():
     algo_bytes = 2.0 * ((T * d + 2 * A) if gather else A * d) + 2.0 * (E * 2 * f * d + A * 2 * f + A * f)
     ach = fl_gu / t_gu / 1e12
     tr = measured_traffic() if args.config == "moe7b_bf16" else None
+    ctr = measured_counters() if args.config == "moe7b_bf16" else None
+    gu_ctr = (ctr or {}).get("products", {}).get("gate_up (alone, after the copy)")
     fwd_tflops = (fl_gu + fl_dn) / (t_gu + t_dn) / 1e12
     # practical HBM ceiling on this device: a 1 GiB device-to-device copy
     # (read + write), timed with events on the same stream
@@ -537,6 +716,10 @@ def main():
             "frac": ach / PEAK_BF16_TFLOPS, "traffic": None if tr is None else tr["traffic_bytes"],
             "flop_per_launch": fl_gu, "avg_launch_us": t_gu * 1e6,
             "algorithmic_bytes_per_launch": algo_bytes,
+            # from the committed counter record (rocprofv3 --pmc over --pmc-probe), null once the
+            # kernel sources change: share of cycles the matrix cores were busy, and the shader clock
+            "mfma_busy": None if gu_ctr is None else gu_ctr["mfma_busy"],
+            "clock_ghz": None if gu_ctr is None else gu_ctr["clock_ghz"],
         },
         "grouped_gemm_fwd": {
             "tflops": fwd_tflops, "frac_of_peak": fwd_tflops / PEAK_BF16_TFLOPS,
