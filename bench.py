@@ -21,9 +21,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer fwd+bwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
+METRIC_FWD = "MoE layer fwd tokens/s; grouped-GEMM TFLOP/s as % of bf16 MFMA peak"
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 PEAK_FP8_TFLOPS = 5000.0
+PEAK_FP32_TFLOPS = 157.3
+FLUSH_BYTES = 512 << 20
 
 
 def parse():
@@ -33,6 +36,11 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="moe7b_bf16")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--all-configs-summarize", metavar="LOG",
+                   help="rebuild the all-configs table under profiles/ from the JSON lines of an --all-configs run")
+    p.add_argument("--all-configs", action="store_true",
+                   help="run every layer configuration (forward workloads forward only) with its oracle baseline "
+                        "on a token sample, and write the table under profiles/")
     p.add_argument("--no-fp8", action="store_true", help="skip the fp8 gate/up measurement")
     p.add_argument("--permuted-copy", action="store_true",
                    help="materialise the permuted token rows (x_perm) instead of gathering them")
@@ -65,6 +73,11 @@ KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_big.hip",
                   "mixture_experts_layer_18_amd/csrc/gemm_common.h",
                   "mixture_experts_layer_18_amd/csrc/common.h",
                   "mixture_experts_layer_18_amd/csrc/kernels.h"]
+
+
+def progress(msg):
+    """A progress line on stderr (stdout carries the JSON result only)."""
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
 def kernel_source_hash():
@@ -367,8 +380,9 @@ def measured_traffic():
     return rec
 
 
-def cpu_baseline(cfg, inp, ntok):
-    """The oracle (fp64 numpy) forward + backward on the first ntok tokens."""
+def cpu_baseline(cfg, inp, ntok, training=True):
+    """The oracle (fp64 numpy) on the first ntok tokens: forward + backward,
+    or the forward alone for a forward workload."""
     import numpy as np
 
     import synth
@@ -377,21 +391,23 @@ def cpu_baseline(cfg, inp, ntok):
     f = lambda a: synth.as_f64(a, cfg.dtype)  # noqa: E731
     w32 = lambda a: synth.bf16_bits_to_f32(a) if (a is not None and a.dtype == np.uint16) else a  # noqa: E731
     x = f(inp["x"][:ntok])
-    dy = f(inp["dy"][:ntok])
     wgu, wd = w32(inp["w_gateup"]), w32(inp["w_down"])
-    sgu, sd = f(inp["s_gateup"]), f(inp["s_down"])
+    sgu, sd = f(inp.get("s_gateup")), f(inp.get("s_down"))
+    dy = f(inp["dy"][:ntok]) if training else None
     t0 = time.perf_counter()
     fw = O.forward(x, inp["w_router"], inp["bias"], wgu, wd, sgu, sd, top_k=cfg.k, score=cfg.score,
                    renorm=cfg.renorm)
-    O.backward(x, inp["w_router"], wgu, wd, sgu, sd, fw, dy, score=cfg.score, renorm=cfg.renorm)
+    if training:
+        O.backward(x, inp["w_router"], wgu, wd, sgu, sd, fw, dy, score=cfg.score, renorm=cfg.renorm)
     dt = time.perf_counter() - t0
     cores = len(os.sched_getaffinity(0))
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"first {ntok} of {cfg.T} tokens of {cfg.name}, fp64 numpy forward+backward, "
+    what = "forward+backward" if training else "forward"
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle", "tokens": ntok,
+            "sample": f"first {ntok} of {cfg.T} tokens of {cfg.name}, fp64 numpy {what}, "
                       f"{dt:.1f} s wall, BLAS threads = all {cores} host cores"}
 
 
-def fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, flop, bf16_s):
+def fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, flop, bf16_s, gather=True):
     """The forward gate/up product in fp8 (e4m3, row-wise scales) on the same
     permuted tokens and routing: the activation quantisation and the scaled
     fp8 grouped GEMM with the SwiGLU epilogue, each timed on its own with
@@ -410,10 +426,19 @@ def fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, flop, bf16_s):
     t_q = timed_ms(lambda: M.moe_quantize_fp8(x_perm, xq, xs, stream), 20) * 1e-3
     t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("swiglu", E, A, 2 * f, d, saved["offsets"], xq, xs, wq, ws,
                                                   h, aux, stream), 20) * 1e-3
+    # the bf16 product on the same rows, timed the same way (20 back-to-back launches)
+    if gather:
+        t_b = timed_ms(lambda: M.moe_grouped_gemm_gather("NT", "swiglu", E, A, 2 * f, d, saved["offsets"], x,
+                                                         w["w_gateup"], h, saved["tok"], cfg.T, aux, stream),
+                       20) * 1e-3
+    else:
+        t_b = timed_ms(lambda: M.moe_grouped_gemm("NT", "swiglu", "bf16", E, A, 2 * f, d, saved["offsets"], x_perm,
+                                                  w["w_gateup"], h, aux, None, stream), 20) * 1e-3
     tf = flop / t_g / 1e12
     q_bytes = A * (2 * d + d + 4)   # bf16 rows in; codes and scales out
     return {"gemm_us": t_g * 1e6, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS, "peak": PEAK_FP8_TFLOPS,
             "quantize_us": t_q * 1e6, "quantize_gbs": q_bytes / t_q / 1e9,
+            "bf16_same_loop_us": t_b * 1e6, "speedup_same_loop_incl_quantize": t_b / (t_g + t_q),
             "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
             "what": "e4m3 row-wise scaled grouped GEMM + SwiGLU on the forward gate/up shape; "
                     "activation quantisation timed separately, weights quantised once"}
@@ -438,9 +463,14 @@ def fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
     t_q = timed_ms(lambda: M.moe_quantize_fp8(dgu, aq, asc, stream), 20) * 1e-3
     t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("none", E, A, d, 2 * f, saved["offsets"], aq, asc, wq, wsc,
                                                   dx, None, stream), 20) * 1e-3
+    # the bf16 product dX = dGU . W_gu on the same operands, timed the same way
+    t_b = timed_ms(lambda: M.moe_grouped_gemm("NN", "none", "bf16", E, A, 2 * f, d, saved["offsets"], dgu,
+                                              w["w_gateup"], dx, None, None, stream), 20) * 1e-3
     tf = flop / t_g / 1e12
     return {"gemm_us": t_g * 1e6, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS, "peak": PEAK_FP8_TFLOPS,
-            "quantize_us": t_q * 1e6, "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
+            "quantize_us": t_q * 1e6, "bf16_same_loop_us": t_b * 1e6,
+            "speedup_same_loop_incl_quantize": t_b / (t_g + t_q),
+            "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
             "what": "e4m3 gate/up data gradient (dGU row-wise, W_gu quantised along 2f and stored transposed "
                     "once) on the forward-layout fp8 grouped GEMM; dGU quantisation timed separately"}
 
@@ -464,42 +494,35 @@ def fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
     t_q = timed_ms(lambda: M.moe_quantize_fp8(dyp, aq, asc, stream), 20) * 1e-3
     t_g = timed_ms(lambda: M.moe_grouped_gemm_fp8("dswiglu", E, A, f, d, saved["offsets"], aq, asc, wq, wsc,
                                                   dgu, saved["preact"], stream), 20) * 1e-3
+    # the bf16 product with the same epilogue on the same operands, timed the same way
+    t_b = timed_ms(lambda: M.moe_grouped_gemm("NN", "dswiglu", "bf16", E, A, d, f, saved["offsets"], dyp,
+                                              w["w_down"], dgu, saved["preact"], None, stream), 20) * 1e-3
     tf = flop / t_g / 1e12
     return {"gemm_us": t_g * 1e6, "tflops": tf, "frac": tf / PEAK_FP8_TFLOPS, "peak": PEAK_FP8_TFLOPS,
-            "quantize_us": t_q * 1e6, "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
+            "quantize_us": t_q * 1e6, "bf16_same_loop_us": t_b * 1e6,
+            "speedup_same_loop_incl_quantize": t_b / (t_g + t_q),
+            "speedup_vs_bf16_incl_quantize": bf16_s / (t_g + t_q),
             "what": "e4m3 down data gradient with the dSwiGLU epilogue (dY~ row-wise, W_d quantised along d and "
                     "stored transposed once) on the forward-layout fp8 grouped GEMM; dY~ quantisation timed "
                     "separately"}
 
 
-def main():
-    args = parse()
-    if args.trace_summarize:
-        trace_summarize(args.trace_summarize)
-        return
-    if args.pmc_summarize:
-        pmc_summarize(*args.pmc_summarize)
-        return
-    if args.pmc_report:
-        pmc_report(args.pmc_report)
-        return
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this MoE layer build has no multi-GPU path "
-              "(expert-parallel sharding is described in DESIGN.md but not built)", file=sys.stderr)
-        sys.exit(2)
-
+def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
+    """One configuration: inputs resident in HBM, W warm-up steps, K timed
+    steps (each after a cache flush, each timed with its own event pair),
+    per-stage timing over separate steps, the dominant kernel's roofline and
+    the oracle timed on a token sample.  Returns the result dict."""
     import numpy as np
     import torch
 
     import mixture_experts_layer_18_amd as M
     import synth
-    from mixture_experts_layer_18_amd import _lib
 
-    _lib.load()
-    assert torch.cuda.is_available(), "no GPU"
-    torch.cuda.set_device(0)
-    cfg = synth.CONFIG_BY_NAME[args.config]
-    inp = synth.make_inputs(cfg, with_dy=True)
+    cfg = synth.CONFIG_BY_NAME[cfg_name]
+    training = cfg.backward
+    progress(f"{cfg.name}: generating inputs")
+    inp = synth.make_inputs(cfg, with_dy=training or pmc_probe)
+    progress(f"{cfg.name}: inputs ready")
 
     def dev(a):
         if a is None:
@@ -512,14 +535,17 @@ def main():
     desc = M.desc_from_config(cfg)
     w = {k: dev(inp.get(k)) for k in ("w_router", "bias", "w_gateup", "w_down", "s_gateup", "s_down")}
     x = dev(inp["x"])
-    dy = dev(inp["dy"])
+    dy = dev(inp.get("dy"))
     y = torch.empty_like(x)
     dx = torch.empty_like(x)
-    gather = not args.permuted_copy
-    saved = M.alloc_saved(desc, gather=gather)
-    grads = M.alloc_grads(desc)
+    # bf16 layers gather the token rows through the token map; the fp32 layer
+    # (vector-ALU products) reads a permuted copy
+    gather = not args.permuted_copy and cfg.dtype == "bf16"
+    # a forward-only workload is an inference forward: no pre-activations kept
+    saved = M.alloc_saved(desc, gather=gather, training=training or pmc_probe)
+    grads = M.alloc_grads(desc) if (training or pmc_probe) else None
     wsf = M.alloc_workspace(desc, "forward")
-    wsb = M.alloc_workspace(desc, "backward")
+    wsb = M.alloc_workspace(desc, "backward") if (training or pmc_probe) else None
     stream = torch.cuda.current_stream()
 
     terms = dict(aux_coeff=1e-3, seq_aux_coeff=1e-3, z_coeff=1e-3, seq_len=4096) if args.router_terms else None
@@ -527,11 +553,12 @@ def main():
 
     def step():
         M.moe_forward(desc, w, x, y, saved, wsf, stream)
-        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, stream, terms=terms, losses=losses)
-        if args.router_terms and cfg.score == "sigmoid":
-            M.moe_bias_update(desc, saved["counts"], 1e-3, w["bias"], stream)
+        if training:
+            M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, stream, terms=terms, losses=losses)
+            if args.router_terms and cfg.score == "sigmoid":
+                M.moe_bias_update(desc, saved["counts"], 1e-3, w["bias"], stream)
 
-    if args.pmc_probe:
+    if pmc_probe:
         # one forward, a 1 GiB device copy (the counters' calibration), the
         # gate/up product alone, then one backward and the fp8 gate/up product
         # with its activation quantisation: every product of the layer is one
@@ -567,8 +594,12 @@ def main():
                                    saved["preact"], stream)
             torch.cuda.synchronize()
         print("pmc probe done", flush=True)
-        return
+        return None
 
+    # a 512 MiB buffer rewritten before each timed step (outside its events)
+    # evicts the L2s (8 x 4 MB) and the 256 MB Infinity Cache, so no step
+    # starts on operands the previous one left in cache
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -577,18 +608,22 @@ def main():
     # the other stages are timed in a separate pass below, so that their
     # event pairs do not sit in the headline steps (they cost ~1 %)
     M.stage_timing(True, stages=["gate_up"])
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for _ in range(args.steps):
+    for e0, e1 in evs:
+        flush_buf.fill_(1.0)
+        e0.record(stream)
         step()
-    ev1.record(stream)
+        e1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     timed_stages = M.stage_times()
     M.stage_timing(False)
-    ms_step = ev0.elapsed_time(ev1) / args.steps
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    progress(f"{cfg.name}: timed {args.steps} steps, {sum(step_ms) / len(step_ms):.3f} ms per step")
+    ms_step = sum(step_ms) / len(step_ms)
+    del flush_buf
     # every stage, over separate steps after the timed region
     M.stage_timing(True)
     for _ in range(min(args.steps, 10)):
@@ -597,10 +632,10 @@ def main():
     stages = M.stage_times()
     M.stage_timing(False)
     stages["gate_up"] = timed_stages["gate_up"]
-    tokens_per_s = cfg.T * args.steps / wall
-
+    tokens_per_s = cfg.T / (ms_step * 1e-3)
     T, d, E, k, f, F = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, cfg.n_shared * cfg.f_shared
     A = T * k
+    es = 2 if cfg.dtype == "bf16" else 4     # bytes per activation / weight element
     counts = saved["counts"].cpu().numpy()
     # algorithmic work of one launch of each stage: flops of the products
     # (2 per multiply-add, no padding), bytes of the memory-bound stages with
@@ -614,18 +649,18 @@ def main():
         "shared_down_dgrad": 2.0 * T * d * F, "shared_down_wgrad": 2.0 * T * d * F,
         "shared_gate_up_wgrad": 2.0 * T * 2 * F * d, "shared_gate_up_dgrad": 2.0 * T * 2 * F * d,
     }
-    sh = 2 * d if F else 0
+    sh = es * d if F else 0
     hbm_bytes = {
-        "router": T * (2 * d + 4 * E),                                # x in, logits out
-        "router_wgrad": T * (2 * d + 4 * E),                          # x, dlogits in
-        "route": T * (4 * E + 8 * k),                                 # logits in; idx, gate out
+        "router": T * (es * d + 4 * E),                                # x in, logits out
+        "router_wgrad": T * (es * d + 4 * E),                          # x, dlogits in
+        "route": T * (4 * E + 8 * k),                                  # logits in; idx, gate out
         # idx in; pos, src, tok out (and with a permuted copy: x in, x_perm out)
-        "permute": T * (16 * k + (0 if gather else 2 * d * (1 + k))),
-        "combine": T * (2 * d * (k + 1) + 8 * k + sh),                # y_perm, gate, pos, shared in; y out
-        "combine_bwd": T * (2 * d * (2 * k + 1) + 12 * k + 8 * E),    # dy, y_perm, gate, pos, idx, logits
-                                                                      # in; dy_perm, dlogits out
-        "unpermute_sum": T * (2 * d * (k + 1) + 8 * k + 4 * E + sh),  # dx_perm, pos, idx, dlogits,
-                                                                      # dx_shared in; dx out
+        "permute": T * (16 * k + (0 if gather else es * d * (1 + k))),
+        "combine": T * (es * d * (k + 1) + 8 * k + sh),                # y_perm, gate, pos, shared in; y out
+        "combine_bwd": T * (es * d * (2 * k + 1) + 12 * k + 8 * E),    # dy, y_perm, gate, pos, idx, logits
+                                                                       # in; dy_perm, dlogits out
+        "unpermute_sum": T * (es * d * (k + 1) + 8 * k + 4 * E + sh),  # dx_perm, pos, idx, dlogits,
+                                                                       # dx_shared in; dx out
     }
     def timed_ms(fn, reps):
         fn()
@@ -651,7 +686,7 @@ def main():
             e.update(tflops=flops[name] / (us * 1e-6) / 1e12)
         elif name in flops:
             tf = flops[name] / (us * 1e-6) / 1e12
-            peak = 157.3 if name.startswith("router") else PEAK_BF16_TFLOPS
+            peak = PEAK_FP32_TFLOPS if (name.startswith("router") or cfg.dtype == "f32") else PEAK_BF16_TFLOPS
             e.update(tflops=tf, frac=tf / peak)
         if name in hbm_bytes:
             gbs = hbm_bytes[name] / (us * 1e-6) / 1e9
@@ -660,12 +695,16 @@ def main():
     t_gu = stage_out["gate_up"]["us"] * 1e-6
     t_dn = stage_out["down"]["us"] * 1e-6
     fl_gu, fl_dn = flops["gate_up"], flops["down"]
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_FP32_TFLOPS
     # each operand byte once: the token rows (x once when gathered, through
-    # the int32 token map; else x_perm) and W_gateup read, preact and h written
-    algo_bytes = 2.0 * ((T * d + 2 * A) if gather else A * d) + 2.0 * (E * 2 * f * d + A * 2 * f + A * f)
+    # the int32 token map; else x_perm) and W_gateup read, preact (training
+    # only) and h written
+    algo_bytes = (es * ((T * d + 2 * A) if gather else A * d)
+                  + es * (E * 2 * f * d + (A * 2 * f if training else 0) + A * f))
     ach = fl_gu / t_gu / 1e12
-    tr = measured_traffic() if args.config == "moe7b_bf16" else None
-    ctr = measured_counters() if args.config == "moe7b_bf16" else None
+    main_cfg = cfg.name == "moe7b_bf16" and gather and not args.router_terms
+    tr = measured_traffic() if main_cfg else None
+    ctr = measured_counters() if main_cfg else None
     gu_ctr = (ctr or {}).get("products", {}).get("gate_up (alone, after the copy)")
     fwd_tflops = (fl_gu + fl_dn) / (t_gu + t_dn) / 1e12
     # practical HBM ceiling on this device: a 1 GiB device-to-device copy
@@ -675,21 +714,27 @@ def main():
     t_copy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
     del cbuf, cdst
-    fp8 = fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, fl_gu, t_gu) if not args.no_fp8 else None
+    with_fp8 = not args.no_fp8 and cfg.dtype == "bf16" and training
+    fp8 = fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, fl_gu, t_gu, gather) if with_fp8 else None
     fp8_dg = (fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flops["gate_up_dgrad"],
                                 stage_out["gate_up_dgrad"]["us"] * 1e-6)
-              if not args.no_fp8 and "gate_up_dgrad" in stage_out else None)
+              if with_fp8 and "gate_up_dgrad" in stage_out else None)
     fp8_dd = (fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flops["down_dgrad"],
                              stage_out["down_dgrad"]["us"] * 1e-6)
-              if not args.no_fp8 and "down_dgrad" in stage_out and saved.get("preact") is not None else None)
+              if with_fp8 and "down_dgrad" in stage_out and saved.get("preact") is not None else None)
     # the streaming memory-bound stages (route and the index-only permute are
     # latency-bound at these sizes)
-    hbm3 = ["combine", "combine_bwd", "unpermute_sum"]
+    hbm3 = [n for n in ("combine", "combine_bwd", "unpermute_sum") if n in stage_out]
     hbm3_us = sum(stage_out[n]["us"] for n in hbm3)
     hbm3_gbs = sum(hbm_bytes[n] for n in hbm3) / (hbm3_us * 1e-6) / 1e9
+    # the routing front end: router logits, top-k and gates, permutation
+    front = [n for n in ("router", "route", "permute") if n in stage_out]
+    front_us = sum(stage_out[n]["us"] for n in front)
+    front_bytes = sum(hbm_bytes[n] for n in front)
+    pass_name = "fwd+bwd" if training else "fwd (inference: no pre-activations kept)"
 
     res = {
-        "metric": METRIC,
+        "metric": METRIC if training else METRIC_FWD,
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -702,7 +747,7 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic (seeded N(0,1) tokens, N(0,1/fan_in) weights, random init)",
         "config": {
-            "workload": f"{cfg.name}: MoE layer fwd+bwd, T={T} tokens, d_model={d}, E={E} experts, "
+            "workload": f"{cfg.name}: MoE layer {pass_name}, T={T} tokens, d_model={d}, E={E} experts, "
                         f"{cfg.score} top-{k}, expert d_ff={f}, {cfg.n_shared} shared experts d_ff="
                         f"{cfg.f_shared}",
             "tokens_per_step": T, "d_model": d, "experts": E, "top_k": k, "d_ff": f,
@@ -710,10 +755,17 @@ def main():
             "token_rows": "gathered through the token map" if gather else "permuted copy (x_perm)",
             "router_terms": terms,
         },
+        "timing": {
+            "method": "each timed step after a 512 MiB buffer write (L2 and Infinity Cache flush) outside its "
+                      "own HIP event pair; value = tokens / mean step time; per-stage times from up to 10 "
+                      "further steps with event pairs around every stage (the gate/up stage's from the timed "
+                      "steps themselves)",
+            "step_ms_min": min(step_ms), "step_ms_max": max(step_ms), "region_wall_s": wall,
+        },
         "roofline": {
             "kernel": "gate/up grouped GEMM + SwiGLU (forward, NT)",
-            "bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-            "frac": ach / PEAK_BF16_TFLOPS, "traffic": None if tr is None else tr["traffic_bytes"],
+            "bound": "mfma", "achieved": ach, "peak": peak, "unit": "TFLOP/s",
+            "frac": ach / peak, "traffic": None if tr is None else tr["traffic_bytes"],
             "flop_per_launch": fl_gu, "avg_launch_us": t_gu * 1e6,
             "algorithmic_bytes_per_launch": algo_bytes,
             # from the committed counter record (rocprofv3 --pmc over --pmc-probe), null once the
@@ -722,11 +774,12 @@ def main():
             "clock_ghz": None if gu_ctr is None else gu_ctr["clock_ghz"],
         },
         "grouped_gemm_fwd": {
-            "tflops": fwd_tflops, "frac_of_peak": fwd_tflops / PEAK_BF16_TFLOPS,
+            "tflops": fwd_tflops, "frac_of_peak": fwd_tflops / peak,
             "gate_up_us": t_gu * 1e6, "down_us": t_dn * 1e6,
         },
+        "front_end": {"stages": front, "us": front_us, "gbs": front_bytes / (front_us * 1e-6) / 1e9},
         "combine_stages_hbm": {"stages": hbm3, "gbs": hbm3_gbs, "frac": hbm3_gbs / PEAK_HBM_GBS, "us": hbm3_us,
-                                      "frac_of_copy": hbm3_gbs / copy_gbs},
+                               "frac_of_copy": hbm3_gbs / copy_gbs},
         "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                              "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
         "stages": stage_out,
@@ -736,8 +789,105 @@ def main():
         "loads": {"max_over_mean": float(counts.max() / counts.mean()), "empty": int((counts == 0).sum())},
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_tokens)
-    print(json.dumps(res), flush=True)
+        progress(f"{cfg.name}: oracle on {min(cpu_tokens, cfg.T)} tokens")
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, cpu_tokens, training)
+    return res
+
+
+ALL_CONFIGS_FILE = os.path.join(ROOT, "profiles", "all_configs_moe_layer.txt")
+# oracle token samples of the all-configs run (about 10-30 s of host work each)
+ALL_CONFIGS_CPU_TOKENS = {"tiny_fp32": 256, "finegrained_bf16": 4096, "moe7b_bf16": 2048, "skew_bf16": 2048,
+                          "large_bf16": 256}
+
+
+def all_configs(args):
+    """Every layer of the scope's table, each with its own pass (forward for
+    the forward workloads, forward + backward for the others): one JSON line
+    per layer on stdout, then the table under profiles/."""
+    import synth
+    rows = []
+    for c in synth.CONFIGS:
+        print(f"[all-configs] {c.name}", file=sys.stderr, flush=True)
+        r = run_config(args, c.name, ALL_CONFIGS_CPU_TOKENS.get(c.name, 256))
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+    write_all_configs(rows, args.steps, args.warmup)
+
+
+def write_all_configs(rows, steps, warmup, log=None):
+    L = ["The MoE layer on every configuration of the scope's table, one MI355X (bf16 products on the matrix",
+         "cores; the fp32 layer on the vector ALUs), inputs resident in HBM, caches flushed before each timed step.",
+         "", "Commands (from the repository root):",
+         f"  python bench.py --all-configs --steps {steps} --warmup {warmup} > gpurun_out/bench_all.log",
+         "  python bench.py --all-configs-summarize gpurun_out/bench_all.log", "",
+         "gate/up = the routed gate/up grouped GEMM + SwiGLU, the dominant kernel (fraction of the 2.5 PFLOP/s bf16",
+         "peak; fp32: of 157.3 TFLOP/s).  front end = router logits + top-k/gates + permutation.  combine stages =",
+         "combine (+ combine backward and unpermute-sum with the backward), algorithmic bytes over their time.",
+         "The forward workloads run an inference forward (no pre-activations kept).  oracle = the fp64 numpy",
+         "oracle on a token sample of the same layer and pass, all host cores.", ""]
+    L.append(f"{'layer':<18s} {'pass':<8s} {'ms/step':>9s} {'tokens/s':>11s} {'gate/up TF':>10s} {'frac':>6s} "
+             f"{'front us':>9s} {'comb GB/s':>9s} {'oracle tok/s':>12s} {'sample':>7s} {'cores':>5s}")
+    for r in rows:
+        cb = r.get("cpu_baseline") or {}
+        L.append(f"{r['config']['workload'].split(':')[0]:<18s} "
+                 f"{'fwd+bwd' if 'fwd+bwd' in r['config']['workload'] else 'fwd':<8s} {r['ms_per_step']:9.3f} "
+                 f"{r['value']:11.0f} {r['roofline']['achieved']:10.1f} {r['roofline']['frac']:6.3f} "
+                 f"{r['front_end']['us']:9.1f} {r['combine_stages_hbm']['gbs']:9.0f} "
+                 f"{cb.get('value', float('nan')):12.1f} {cb.get('tokens', 0):7d} {cb.get('cores', 0):5d}")
+    names = [r["config"]["workload"].split(":")[0] for r in rows]
+    stages = []
+    for r in rows:
+        stages += [n for n in r["stages"] if n not in stages]
+    L += ["", "Per-stage mean time (us) and rate (TFLOP/s for products, GB/s of algorithmic bytes otherwise):", ""]
+    L.append(f"{'stage':<22s}" + "".join(f"{n:>22s}" for n in names))
+    for st in stages:
+        cells = []
+        for r in rows:
+            e = r["stages"].get(st)
+            if e is None:
+                cells.append(f"{'-':>22s}")
+                continue
+            rate = f"{e['tflops']:.0f} TF" if "tflops" in e and "gbs" not in e else (
+                f"{e['gbs']:.0f} GB/s" if "gbs" in e else "")
+            cells.append(f"{e['us']:10.1f} {rate:>11s}")
+        L.append(f"{st:<22s}" + "".join(cells))
+    with open(ALL_CONFIGS_FILE, "w") as fh:
+        fh.write("\n".join(L) + "\n")
+    print("\n".join(L), file=sys.stderr, flush=True)
+
+
+def main():
+    args = parse()
+    if args.trace_summarize:
+        trace_summarize(args.trace_summarize)
+        return
+    if args.pmc_summarize:
+        pmc_summarize(*args.pmc_summarize)
+        return
+    if args.pmc_report:
+        pmc_report(args.pmc_report)
+        return
+    if args.all_configs_summarize:
+        with open(args.all_configs_summarize) as fh:
+            rows = [json.loads(ln) for ln in fh if ln.startswith("{")]
+        write_all_configs(rows, rows[0]["steps"], rows[0]["warmup"])
+        return
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this MoE layer build has no multi-GPU path "
+              "(expert-parallel sharding is described in DESIGN.md but not built)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mixture_experts_layer_18_amd import _lib
+    _lib.load()
+    assert torch.cuda.is_available(), "no GPU"
+    torch.cuda.set_device(0)
+    if args.all_configs:
+        all_configs(args)
+        return
+    res = run_config(args, args.config, args.cpu_tokens, pmc_probe=args.pmc_probe)
+    if res is not None:
+        print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

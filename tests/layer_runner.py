@@ -5,9 +5,10 @@ Comparison protocol (same for every layer size):
   * routing indices: bit-exact on every token whose oracle selection margin
     (k-th minus (k+1)-th key) is >= 1e-3; on the other tokens the GPU's
     choice must be valid: each picked key >= the oracle's k-th key - 1e-3;
-  * outputs and input gradients: compared on tokens whose GPU routing equals
-    the oracle's; weight gradients over everything (a near-tie flip moves one
-    token's contribution, far below the tolerance);
+  * outputs, input gradients and weight gradients: compared on every token,
+    with the oracle re-run on the GPU's routing (its expert indices forced,
+    its gates recomputed from the oracle's own scores) wherever a near-tie
+    made the two choose differently; the number of such tokens is reported;
   * tolerance: fp32 rel-L2 <= 1e-5; bf16 rel-L2 <= 1e-2 and
     max-abs <= 5e-2 * RMS(reference)."""
 import numpy as np
@@ -123,6 +124,24 @@ def check_routing(cfg, g_logits, g_idx, fw, tokens=None):
     return same_set
 
 
+def oracle_on_gpu_routing(cfg, oi, g_idx, backward, fw, bw, tokens=None, terms=None):
+    """The oracle's forward (and backward) with the GPU's expert choice forced,
+    when any token's choice (set or slot order) differs from the oracle's own;
+    otherwise the given results.  Returns (fw, bw, flipped token count)."""
+    gi = g_idx if tokens is None else g_idx[tokens]
+    flips = int(np.sum(np.any(gi != fw["idx"], axis=1)))
+    if flips == 0:
+        return fw, bw, 0
+    x = oi["x"] if tokens is None else oi["x"][tokens]
+    fw = O.forward(x, oi["w_router"], oi["bias"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"],
+                   top_k=cfg.k, score=cfg.score, renorm=cfg.renorm, forced_idx=gi)
+    if backward:
+        dy = oi["dy"] if tokens is None else oi["dy"][tokens]
+        bw = O.backward(x, oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fw, dy,
+                        score=cfg.score, renorm=cfg.renorm, terms=terms)
+    return fw, bw, flips
+
+
 def compare_full(cfg, inp, backward, gather=False, degenerate=False):
     """Full comparison on a layer small enough for the oracle to run whole.
     degenerate: the routed weight gradients are compared expert by expert
@@ -131,10 +150,13 @@ def compare_full(cfg, inp, backward, gather=False, degenerate=False):
     oi = oracle_inputs(cfg, inp)
     fw, bw = oracle_run(cfg, oi, backward)
     same = check_routing(cfg, g["logits"], g["idx"], fw)
-    assert_close(g["y"][same], fw["y"][same], cfg.dtype, "y")
+    fw, bw, flips = oracle_on_gpu_routing(cfg, oi, g["idx"], backward, fw, bw)
+    print(f"[compare] {cfg.name}: tokens on a near-tie choice other than the oracle's: {flips} of {cfg.T}",
+          flush=True)
+    assert_close(g["y"], fw["y"], cfg.dtype, "y")
     assert np.array_equal(g["counts"].sum(), cfg.T * cfg.k)
     if backward:
-        assert_close(g["dx"][same], bw["dx"][same], cfg.dtype, "dx")
+        assert_close(g["dx"], bw["dx"], cfg.dtype, "dx")
         if degenerate and cfg.dtype != "f32":
             assert_close_per_expert(g["d_w_gateup"], bw["d_w_gateup"], "dW_gateup")
             assert_close_per_expert(g["d_w_down"], bw["d_w_down"], "dW_down")

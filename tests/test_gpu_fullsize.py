@@ -3,11 +3,18 @@ configuration the benchmark times.
 
 The oracle cannot run a full 16k- or 64k-token layer in seconds, so:
   * routing is checked on every token (logits are cheap);
-  * y and dx are checked on a token sample (each depends only on its own token);
-  * weight gradients come from a second backward pass whose upstream gradient
-    is zero outside a token sample S: every weight gradient is then a sum over
-    S alone, which the oracle computes exactly on that subset, while the GPU
-    still runs every kernel over all T tokens and all experts.
+  * the oracle follows the GPU's routing (its expert indices forced, gates
+    from its own scores), so a near-tie that chose differently is compared,
+    not dropped;
+  * up to 16384 tokens the oracle runs the whole batch: y, dx and every
+    gradient are compared on every token;
+  * at 65536 tokens, y and dx are compared on 4096 tokens, among them the
+    tokens at the first and last permuted row of every 256-row tile of every
+    expert (each output depends only on its own token); the weight gradients
+    come from a second backward pass whose upstream gradient is zero outside
+    a uniform quarter of the tokens: every weight gradient is then a sum over
+    that sample alone, which the oracle computes exactly, while the GPU still
+    runs every kernel over all tokens and all experts.
 """
 import numpy as np
 import pytest
@@ -29,11 +36,25 @@ FULL = [c for c in synth.CONFIGS if c.backward] + [synth.CONFIG_BY_NAME["finegra
 CASES = [(c, True) for c in FULL] + [(synth.CONFIG_BY_NAME["moe7b_bf16"], False)]
 
 
-def _sample(T, n, seed, allowed=None):
+def _sample(T, n, seed, must=()):
+    """n tokens (at least): the tokens in `must`, then random others."""
     g = np.random.default_rng(seed)
-    pool = np.arange(T) if allowed is None else np.where(allowed)[0]
-    s = np.sort(g.choice(pool, size=min(n, pool.size), replace=False))
-    return s
+    must = np.unique(np.asarray(must, np.int64))
+    rest = np.setdiff1d(np.arange(T), must)
+    extra = g.choice(rest, size=max(0, min(n - must.size, rest.size)), replace=False)
+    return np.sort(np.concatenate([must, extra]))
+
+
+def _tile_edge_tokens(offsets, tok, tile=256):
+    """Tokens at the first and last permuted row of every 256-row tile of
+    every expert (the rows where the grouped GEMM's tiles and ragged tails
+    begin and end)."""
+    rows = []
+    for e in range(offsets.size - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for r0 in range(lo, hi, tile):
+            rows += [r0, min(r0 + tile, hi) - 1]
+    return tok[np.asarray(rows, np.int64)] if rows else np.zeros(0, np.int64)
 
 
 @pytest.mark.parametrize("cfg,gather", CASES,
@@ -41,7 +62,6 @@ def _sample(T, n, seed, allowed=None):
 def test_full_size_layer(cfg, gather):
     print(f"[full] {cfg.name} gather={gather}: generating inputs", flush=True)
     inp = synth.make_inputs(cfg, with_dy=True)
-    nsamp = 256 if cfg.T <= 16384 else 128
     desc = M.desc_from_config(cfg)
     w = R.upload_layer(cfg, inp)
     x = dev(inp["x"])
@@ -51,6 +71,8 @@ def test_full_size_layer(cfg, gather):
     g_logits = g["saved"]["logits"].cpu().numpy()
     g_idx = g["saved"]["idx"].cpu().numpy()
     counts = g["saved"]["counts"].cpu().numpy()
+    offsets = g["saved"]["offsets"].cpu().numpy().astype(np.int64)
+    tok = g["saved"]["tok"].cpu().numpy().astype(np.int64)
     assert counts.sum() == cfg.T * cfg.k
     assert torch.isfinite(g["y"].float()).all() and torch.isfinite(g["dx"].float()).all()
 
@@ -62,24 +84,52 @@ def test_full_size_layer(cfg, gather):
     keys = O.selection_keys(logits, scores, inp["bias"], cfg.score)
     oidx, margin = O.select_topk(keys, cfg.k)
     fw_r = dict(logits=logits, keys=keys, idx=oidx, margin=margin)
-    same = R.check_routing(cfg, g_logits, g_idx, fw_r)
-    print(f"[full] {cfg.name}: tokens routed to another set {int((~same).sum())}, margin<1e-3 "
+    R.check_routing(cfg, g_logits, g_idx, fw_r)
+    flips = int(np.sum(np.any(g_idx != oidx, axis=1)))
+    print(f"[full] {cfg.name}: tokens on a near-tie choice other than the oracle's {flips}, margin<1e-3 "
           f"{int((margin < R.MARGIN).sum())}", flush=True)
     if cfg.bias == "zipf":
         assert (counts == 0).sum() >= 4
 
-    # --- y and dx on a token sample
-    S = _sample(cfg.T, nsamp, 1, allowed=same)
     oi = R.oracle_inputs(cfg, inp)
-    print(f"[full] {cfg.name}: oracle on {S.size} sampled tokens", flush=True)
-    fw, bw = R.oracle_run(cfg, oi, True, tokens=S)
-    assert np.array_equal(np.sort(fw["idx"], axis=1), np.sort(g_idx[S], axis=1))
+    if cfg.T <= 16384:
+        # --- the whole batch: the oracle on every token (on the GPU's
+        # routing), y, dx and every gradient compared in full
+        print(f"[full] {cfg.name}: oracle forward+backward on all {cfg.T} tokens", flush=True)
+        fw = O.forward(oi["x"], oi["w_router"], oi["bias"], oi["w_gateup"], oi["w_down"], oi["s_gateup"],
+                       oi["s_down"], top_k=cfg.k, score=cfg.score, renorm=cfg.renorm, forced_idx=g_idx)
+        bw = O.backward(oi["x"], oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fw,
+                        oi["dy"], score=cfg.score, renorm=cfg.renorm)
+        assert_close(host(g["y"]), fw["y"], cfg.dtype, "y")
+        assert_close(host(g["dx"]), bw["dx"], cfg.dtype, "dx")
+        _compare_grads(cfg, g["grads"], bw)
+        return
+
+    # --- 64k tokens: a token sample S with every expert's tile-edge rows plus
+    # random tokens (4096), the oracle on the GPU's routing (indices forced:
+    # no token excluded) for y and dx
+    edges = _tile_edge_tokens(offsets, tok)
+    S = _sample(cfg.T, max(4096, np.unique(edges).size), 1, must=edges)
+    print(f"[full] {cfg.name}: oracle on {S.size} sampled tokens ({np.unique(edges).size} at tile edges)",
+          flush=True)
+    fw = O.forward(oi["x"][S], oi["w_router"], oi["bias"], oi["w_gateup"], oi["w_down"], oi["s_gateup"],
+                   oi["s_down"], top_k=cfg.k, score=cfg.score, renorm=cfg.renorm, forced_idx=g_idx[S])
+    bw = O.backward(oi["x"][S], oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fw,
+                    oi["dy"][S], score=cfg.score, renorm=cfg.renorm)
     assert_close(host(g["y"])[S], fw["y"], cfg.dtype, "y")
     assert_close(host(g["dx"])[S], bw["dx"], cfg.dtype, "dx")
+    del fw, bw
 
-    # --- weight gradients: upstream gradient only on a sample S2, large enough
-    # that each expert's gradient sums over many rows as in the real workload
-    S2 = _sample(cfg.T, 2048 if cfg.T <= 16384 else 4096, 2, allowed=same)
+    # --- weight gradients: a second backward whose upstream gradient is zero
+    # outside a uniform sample S2 of a quarter of the tokens, so every weight
+    # gradient is a sum over S2 alone (each expert keeps its share of rows)
+    S2 = _sample(cfg.T, cfg.T // 4, 2)
+    print(f"[full] {cfg.name}: oracle forward+backward on {S2.size} uniformly sampled tokens", flush=True)
+    fw = O.forward(oi["x"][S2], oi["w_router"], oi["bias"], oi["w_gateup"], oi["w_down"], oi["s_gateup"],
+                   oi["s_down"], top_k=cfg.k, score=cfg.score, renorm=cfg.renorm, forced_idx=g_idx[S2])
+    bw = O.backward(oi["x"][S2], oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fw,
+                    oi["dy"][S2], score=cfg.score, renorm=cfg.renorm)
+    del fw
     mask = torch.zeros(cfg.T, 1, dtype=dy.dtype, device="cuda")
     mask[torch.from_numpy(S2).cuda()] = 1
     dy2 = (dy * mask).contiguous()
@@ -89,20 +139,27 @@ def test_full_size_layer(cfg, gather):
     print(f"[full] {cfg.name}: GPU backward with masked upstream gradient", flush=True)
     M.moe_backward(desc, w, x, g["saved"], dy2, dx2, grads, wsb)
     torch.cuda.synchronize()
-    fw2, bw2 = R.oracle_run(cfg, oi, True, tokens=S2)
+    _compare_grads(cfg, grads, bw)
+    out_dx2 = host(dx2)
+    assert np.all(out_dx2[np.setdiff1d(np.arange(cfg.T), S2)] == 0.0)
+    assert_close(out_dx2[S2], bw["dx"], cfg.dtype, "dx (masked)")
+
+
+def _compare_grads(cfg, grads, bw):
     for name in ("d_w_gateup", "d_w_down", "d_s_gateup", "d_s_down"):
         if grads[name] is None:
             continue
         gv = host(grads[name])
-        print(f"[full] {cfg.name}: {name} rel-L2 {R.rel_l2(gv, bw2[name]):.2e} "
-              f"max-abs/RMS {max_abs_over_rms(gv, bw2[name]):.2e}", flush=True)
-        assert_close(gv, bw2[name], cfg.dtype, name)
+        ref = bw[name]
+        rms = np.sqrt(np.mean(ref * ref))
+        big = np.abs(ref) >= rms
+        print(f"[full] {cfg.name}: {name} rel-L2 {R.rel_l2(gv, ref):.2e} max-abs/RMS "
+              f"{max_abs_over_rms(gv, ref):.2e} (max|ref|/RMS {np.abs(ref).max() / rms:.1f}, worst relative "
+              f"error where |ref| >= RMS {np.max(np.abs(gv[big] - ref[big]) / np.abs(ref[big])):.2e})", flush=True)
+        assert_close(gv, ref, cfg.dtype, name)
     # the router gradient is fp32; its reference runs through bf16-rounded
     # expert outputs on the GPU, so it is held to the bf16 layer bar
-    assert_close(grads["d_w_router"].cpu().numpy(), bw2["d_w_router"], cfg.dtype, "d_w_router")
-    out_dx2 = host(dx2)
-    assert np.all(out_dx2[np.setdiff1d(np.arange(cfg.T), S2)] == 0.0)
-    assert_close(out_dx2[S2], bw2["dx"], cfg.dtype, "dx (masked)")
+    assert_close(grads["d_w_router"].cpu().numpy(), bw["d_w_router"], cfg.dtype, "d_w_router")
 
 
 def test_full_size_fp8_gate_up():

@@ -406,17 +406,65 @@ def test_router_terms_closed_forms():
 
 
 def test_bias_update_moves_toward_balance():
+    """The proportional bias update (reading of the Apex-3 page's
+    router_bias_update=proportional) pinned by what "proportional to the
+    relative load error" fixes, without writing the rule out again:
+    balanced loads leave the bias unchanged; the step is linear in the load
+    error (doubling every expert's excess load doubles every step, exactly:
+    a power-of-two scaling); it depends on the loads only relative to the
+    mean (T and the counts scaled together give the same step); the steps
+    sum to zero (the loads always sum to T k); an expert with no load moves
+    up by the rate and one at twice the mean load down by the rate; and the
+    step grows with the overload (monotone)."""
     T, k, E, rate = 1024, 4, 8, 0.01
+    m = T * k // E
     b = np.linspace(-0.1, 0.1, E).astype(np.float32)
+    z = np.zeros(E, np.float32)
     # balanced loads: no change at all
-    assert np.array_equal(O.bias_update(b, np.full(E, T * k // E), T, k, rate), b)
-    # skewed loads: overloaded experts go down, underloaded up, in proportion
-    counts = np.array([1024, 512, 512, 512, 512, 512, 256, 256])
-    nb = O.bias_update(b, counts, T, k, rate).astype(F64)
-    mean = T * k / E
-    want = b.astype(F64) + F64(np.float32(rate)) * (mean - counts) / mean
-    assert np.max(np.abs(nb - want)) <= 2.0 ** -24 * np.max(np.abs(want))
-    assert nb[0] < b[0] and nb[-1] > b[-1] and abs(nb[1] - b[1]) <= 2.0 ** -24
+    assert np.array_equal(O.bias_update(b, np.full(E, m), T, k, rate), b)
+    # linear in the load error (Sum of the error is zero, so both are valid loads)
+    err = np.array([256, -128, 64, -64, 0, -32, -32, -64])
+    assert err.sum() == 0
+    s1 = O.bias_update(z, m + err, T, k, rate)
+    s2 = O.bias_update(z, m + 2 * err, T, k, rate)
+    assert np.array_equal(s2, 2 * s1)
+    # relative loads only: T and the counts doubled together, same step
+    assert np.array_equal(O.bias_update(b, m + err, T, k, rate), O.bias_update(b, 2 * (m + err), 2 * T, k, rate))
+    # the steps balance out
+    assert abs(float(s1.astype(F64).sum())) <= E * 2.0 ** -24 * float(np.abs(s1).max())
+    # no load: up by the rate; twice the mean: down by the rate
+    c = np.array([0, 2 * m, m, m, m, m, m, m])
+    s = O.bias_update(z, c, T, k, rate)
+    assert s[0] == np.float32(rate) and s[1] == -np.float32(rate) and np.all(s[2:] == 0)
+    # monotone: more load, lower bias
+    c = np.array([1024, 768, 640, 512, 384, 320, 256, 192])
+    assert c.sum() == T * k
+    nb = O.bias_update(z, c, T, k, rate)
+    assert np.all(np.diff(nb.astype(F64)) > 0)
+
+
+def test_balance_loss_values_independent_of_their_formula():
+    """Values of the balance losses fixed without retyping them: the
+    per-sequence loss over one sequence equals the batch loss (both measure
+    the same loads); over n copies of one sequence it equals that sequence's
+    loss; and with every token on expert 0 (k = 1) and a router certain of it
+    the batch loss is coeff * E (the most unbalanced case)."""
+    g = np.random.default_rng(23)
+    T, E, k = 64, 8, 2
+    l = (g.standard_normal((T, E)) * 1.5).astype(np.float32)
+    idx, _ = O.select_topk(l, k)
+    counts = np.bincount(idx.reshape(-1), minlength=E)
+    for score in ("softmax", "sigmoid"):
+        va, _ = O.aux_loss(l, counts, k, score, 1.0)
+        vs, _ = O.seq_aux_loss(l, idx, k, score, 1.0, T)
+        assert abs(va - vs) <= 1e-14 * abs(va)
+        l3, i3 = np.tile(l, (3, 1)), np.tile(idx, (3, 1))
+        v3, _ = O.seq_aux_loss(l3, i3, k, score, 1.0, T)
+        assert abs(v3 - vs) <= 1e-14 * abs(vs)
+    l1 = np.zeros((T, E), np.float32)
+    l1[:, 0] = 60.0
+    v, _ = O.aux_loss(l1, np.array([T] + [0] * (E - 1)), 1, "softmax", 1.0)
+    assert abs(v - E) <= 1e-12
 
 
 # --------------------------------------------------------------------------- fp8 (e4m3)
