@@ -237,7 +237,8 @@ int moe_permute(const moe_desc_t *desc, const void *x, const int32_t *idx,
 /* Grouped GEMM over G groups of rows ("experts run as grouped GEMMs", Apex-3
  * "Fine-grained MoE"; Handbook 2.5 grouped GEMM for the local experts).
  * group_offsets: device int32 [G+1], non-decreasing, offsets[0] = 0,
- * offsets[G] = M_total; group g owns rows [offsets[g], offsets[g+1]).
+ * offsets[G] = M_total; group g owns rows [offsets[g], offsets[g+1]).  With
+ * G = 1 it may be NULL: one group of all M_total rows.
  * Accumulation is fp32; C is rounded once to `dtype`.
  *   MOE_GEMM_NT (forward):  C[m,n] = sum_k A[m,k] B[g,n,k]
  *        A [M_total,K], B [G,N,K], C [M_total,N]
@@ -291,8 +292,8 @@ int moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *x, v
 /* moe_forward for callers that cannot allocate device memory or pass a
  * workspace: code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc.  Same arguments and results as moe_forward (bit for
- * bit: the same kernels) without ws; its scratch (the routing histogram, its
- * scan and a one-group offset table) lives in a device array of
+ * bit: the same kernels) without ws; its scratch (the routing histogram and
+ * its scan) lives in a device array of
  * MOE_STATIC_SCRATCH_BYTES inside the library, one copy per GPU, held until
  * the process ends.  Allocates nothing and calls no allocating routine.
  *   MOE_ERR_WORKSPACE when the layer needs more scratch than that
@@ -375,7 +376,8 @@ int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const voi
 
 /* fp8 grouped GEMM, forward (NT) layout, with row scales:
  *   C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k]
- * for the rows m of group g (group_offsets as in moe_grouped_gemm), fp32
+ * for the rows m of group g (group_offsets as in moe_grouped_gemm, NULL for
+ * one group), fp32
  * accumulation of the exact e4m3 products, rounded once to bf16.
  *   A [M_total, K], B [G, N, K] uint8 e4m3 codes; a_scale [M_total],
  *   b_scale [G, N] fp32; C [M_total, N] bf16 (MOE_EPI_NONE) or, with

@@ -96,7 +96,6 @@ size_t backward_gemm_ws(const moe_desc_t* d) {
 struct FwdWs {
   int32_t* hist;
   int32_t* base;
-  int32_t* one_group;  // [0, T]
 };
 size_t fwd_ws(const moe_desc_t* d, void* ws, FwdWs* out) {
   Carve c(ws);
@@ -104,7 +103,6 @@ size_t fwd_ws(const moe_desc_t* d, void* ws, FwdWs* out) {
   FwdWs w;
   w.hist = (int32_t*)c.take(nb);
   w.base = (int32_t*)c.take(nb);
-  w.one_group = (int32_t*)c.take(2 * sizeof(int32_t));
   if (out) *out = w;
   return c.off;
 }
@@ -116,7 +114,6 @@ struct BwdWs {
   float* dlogits;  // [T, E]
   void* s_dgu;     // [T, 2F]
   void* dx_shared; // [T, d]
-  int32_t* one_group;
   void* gemm;      // split partials
   size_t gemm_bytes;
 };
@@ -132,7 +129,6 @@ size_t bwd_ws(const moe_desc_t* d, void* ws, BwdWs* out) {
   w.terms = c.take(router_terms_ws_bytes(T, d->num_experts));
   w.s_dgu = F > 0 ? c.take((size_t)T * 2 * F * es) : nullptr;
   w.dx_shared = F > 0 ? c.take((size_t)T * D * es) : nullptr;
-  w.one_group = (int32_t*)c.take(2 * sizeof(int32_t));
   w.gemm_bytes = backward_gemm_ws(d);
   w.gemm = c.take(w.gemm_bytes);
   if (out) *out = w;
@@ -375,7 +371,7 @@ int moe_grouped_gemm(int layout, int epi, int dtype, int64_t G, int64_t M, int64
                      void* ws, size_t ws_bytes, void* stream) {
   int s = check_gemm(layout, epi, dtype, G, M, N, K);
   if (s) return s;
-  if (!off || !B || !C) return MOE_ERR_INVALID;
+  if ((!off && G != 1) || !B || !C) return MOE_ERR_INVALID;
   if (M > 0 && !A) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_DSWIGLU && !aux) return MOE_ERR_INVALID;
   const void* ptrs[] = {off, A, B, C, aux, ws};
@@ -392,7 +388,7 @@ int moe_grouped_gemm_gather(int layout, int epi, int64_t G, int64_t M, int64_t N
                             const int32_t* rows, int64_t src_rows, void* stream) {
   int s = check_gemm(layout, epi, MOE_BF16, G, M, N, K);
   if (s) return s;
-  if (!off || !B || !C || src_rows < 0) return MOE_ERR_INVALID;
+  if ((!off && G != 1) || !B || !C || src_rows < 0) return MOE_ERR_INVALID;
   if (M > 0 && (!A || !rows)) return MOE_ERR_INVALID;
   const void* ptrs[] = {off, A, B, C, aux, rows};
   for (const void* p : ptrs)
@@ -402,7 +398,9 @@ int moe_grouped_gemm_gather(int layout, int epi, int64_t G, int64_t M, int64_t N
   // row byte offsets of the token matrix are 32-bit in the kernel
   if (src_rows * K * 2 > (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
   GemmProblem p = gp(layout, epi, MOE_BF16, MOE_BF16, MOE_BF16, G, M, N, K, off, A, B, C, aux);
-  p.rows = rows ? rows : off;  // M = 0: any non-null map selects the gathered kernel
+  // M = 0: any non-null device pointer selects the gathered kernel (with no
+  // routed rows the map is never read)
+  p.rows = rows ? rows : (off ? off : (const int32_t*)C);
   if (!gemm_big_supported(p)) return MOE_ERR_UNSUPPORTED;
   return hip_status(launch_grouped_gemm(p, nullptr, 0, (hipStream_t)stream));
 }
@@ -473,12 +471,17 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
   }
   FwdWs fw;
   fwd_ws(d, ws, &fw);
-  MOE_TRY(launch_group_offsets_1(fw.one_group, (int32_t)T, st));
-  // 1. router logits in fp32
-  MOE_STAGE(MOE_STAGE_ROUTER, launch_router_logits(x, dt, w->w_router, (int)T, (int)D, (int)E, sv->logits, st));
-  // 2. scores, top-k, gates, per-block histogram
-  MOE_STAGE(MOE_STAGE_ROUTE, launch_route(sv->logits, d->score == MOE_SIGMOID ? w->bias : nullptr, (int)T, (int)E,
-                       (int)k, d->score, d->renorm, sv->idx, sv->gate, fw.hist, st));
+  // 1. router logits in fp32, 2. scores, top-k, gates, per-block histogram
+  // (one kernel when a workgroup holds all E logits of its tokens)
+  const float* rbias = d->score == MOE_SIGMOID ? w->bias : nullptr;
+  if (router_route_fused(dt, (int)D, (int)E)) {
+    MOE_STAGE(MOE_STAGE_ROUTER, launch_router_route(x, w->w_router, (int)T, (int)D, (int)E, sv->logits, rbias,
+                                                    (int)k, d->score, d->renorm, sv->idx, sv->gate, fw.hist, st));
+  } else {
+    MOE_STAGE(MOE_STAGE_ROUTER, launch_router_logits(x, dt, w->w_router, (int)T, (int)D, (int)E, sv->logits, st));
+    MOE_STAGE(MOE_STAGE_ROUTE, launch_route(sv->logits, rbias, (int)T, (int)E, (int)k, d->score, d->renorm,
+                                            sv->idx, sv->gate, fw.hist, st));
+  }
   // 3. permutation into expert-contiguous rows
   MOE_STAGE(MOE_STAGE_PERMUTE, launch_permute(x, dt, sv->idx, fw.hist, (int)T, (int)D, (int)E, (int)k, fw.base,
                          sv->counts, sv->offsets, sv->pos, sv->src, sv->tok, sv->x_perm, st));
@@ -495,10 +498,10 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
   // 6. shared experts on every token; their output lands in y
   if (F > 0) {
     MOE_STAGE(MOE_STAGE_SHARED_GATE_UP, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, 1, T, 2 * F, D,
-                                   fw.one_group, x, w->s_gateup, sv->s_h, sv->s_preact),
+                                   nullptr, x, w->s_gateup, sv->s_h, sv->s_preact),
                                 nullptr, 0, st));
     MOE_STAGE(MOE_STAGE_SHARED_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
-                                   fw.one_group, sv->s_h, w->s_down, y, nullptr),
+                                   nullptr, sv->s_h, w->s_down, y, nullptr),
                                 nullptr, 0, st));
   }
   // 7. weighted combine (+ shared output)
@@ -567,7 +570,6 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   hipStream_t st = (hipStream_t)stream;
   BwdWs bw;
   bwd_ws(d, ws, &bw);
-  MOE_TRY(launch_group_offsets_1(bw.one_group, (int32_t)T, st));
   // 1. combine backward + router backward (dlogits)
   MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
                              d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
@@ -605,16 +607,16 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   // 6. shared experts
   if (F > 0) {
     MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
-                                   bw.one_group, dy, w->s_down, bw.s_dgu, sv->s_preact),
+                                   nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
                                 nullptr, 0, st));
     MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
-                                   bw.one_group, dy, sv->s_h, g->d_s_down, nullptr),
+                                   nullptr, dy, sv->s_h, g->d_s_down, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
     MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
-                                   bw.one_group, bw.s_dgu, x, g->d_s_gateup, nullptr),
+                                   nullptr, bw.s_dgu, x, g->d_s_gateup, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
     MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
-                                   bw.one_group, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
+                                   nullptr, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
                                 nullptr, 0, st));
   }
   // 7. router weight gradient (fp32)
@@ -679,7 +681,7 @@ int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
   if (epi == MOE_EPI_DSWIGLU && M > 0 && !aux) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_SWIGLU && (N / 2) % 128) return MOE_ERR_INVALID;
   if (M >= (int64_t(1) << 31) || N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
-  if (!offsets) return MOE_ERR_INVALID;
+  if (!offsets && G != 1) return MOE_ERR_INVALID;
   if (M > 0 && (!A || !a_scale || !B || !b_scale || !C)) return MOE_ERR_INVALID;
   const void* ptrs[] = {offsets, A, a_scale, B, b_scale, C, aux};
   for (const void* p : ptrs)

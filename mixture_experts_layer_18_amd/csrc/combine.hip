@@ -392,12 +392,6 @@ __global__ void fill_i32_kernel(int32_t* p, int64_t n, int32_t v) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = v;
 }
-__global__ void group_offsets_1_kernel(int32_t* o, int32_t M) {
-  if (threadIdx.x == 0) {
-    o[0] = 0;
-    o[1] = M;
-  }
-}
 
 // Dispatch a kernel template on the slot count: 1..8 at compile time, other
 // counts through the generic loop (KK = 0).
@@ -463,11 +457,6 @@ hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* p
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st) {
   if (n <= 0) return hipSuccess;
   fill_i32_kernel<<<dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st>>>(p, n, v);
-  return hipGetLastError();
-}
-
-hipError_t launch_group_offsets_1(int32_t* offsets, int32_t M, hipStream_t st) {
-  group_offsets_1_kernel<<<dim3(1), dim3(64), 0, st>>>(offsets, M);
   return hipGetLastError();
 }
 

@@ -59,6 +59,12 @@ MOE_DEV float wave_sum(float v) {
 
 MOE_DEV int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// First row of group g of a grouped product: offsets[g], or with no offset
+// table (offsets == NULL, one group) 0 for g = 0 and M (all rows) for g = 1.
+MOE_DEV int group_row(const int32_t* offsets, int g, int64_t M) {
+  return offsets ? offsets[g] : (g == 0 ? 0 : (int)M);
+}
+
 // Number of blocks of `b` covering `a` (host and device).
 __host__ __device__ inline int64_t cdiv64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 

@@ -41,11 +41,11 @@ struct RowTile {
 // Tile tm of the concatenation of every group's ceil(rows/BMt) row tiles.
 // Block-wide (all 256 threads call it); G <= 256.
 template <int BMt>
-MOE_DEV RowTile find_row_tile(const int32_t* __restrict__ offsets, int G, int tm, int* s_pref,
+MOE_DEV RowTile find_row_tile(const int32_t* __restrict__ offsets, int G, int64_t M, int tm, int* s_pref,
                               int* scratch) {
   const int tid = threadIdx.x;
   int n = 0;
-  if (tid < G) n = (offsets[tid + 1] - offsets[tid] + BMt - 1) / BMt;
+  if (tid < G) n = (group_row(offsets, tid + 1, M) - group_row(offsets, tid, M) + BMt - 1) / BMt;
   int tot;
   const int ex = block_exclusive_scan256(n, scratch, &tot);
   if (tid < G) s_pref[tid] = ex;
@@ -64,8 +64,8 @@ MOE_DEV RowTile find_row_tile(const int32_t* __restrict__ offsets, int G, int tm
       hi = mid;
   }
   r.g = lo;
-  r.m_lo = offsets[lo] + (tm - s_pref[lo]) * BMt;
-  r.m_hi = min(r.m_lo + BMt, offsets[lo + 1]);
+  r.m_lo = group_row(offsets, lo, M) + (tm - s_pref[lo]) * BMt;
+  r.m_hi = min(r.m_lo + BMt, group_row(offsets, lo + 1, M));
   return r;
 }
 
@@ -100,14 +100,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(KArgs a) {
     g = blockIdx.z / a.nsplit;
     split = blockIdx.z % a.nsplit;
     int rl, rh;
-    split_range(a.offsets[g], a.offsets[g + 1], split, a.nsplit, BR, &rl, &rh);
+    split_range(group_row(a.offsets, g, a.M_total), group_row(a.offsets, g + 1, a.M_total), split, a.nsplit, BR, &rl, &rh);
     r_lo = rl;
     r_hi = rh;
     i_lo = (int64_t)blockIdx.y * BM;
     i_hi = min(i_lo + BM, N);
     ncols = K;
   } else {
-    const RowTile rt = find_row_tile<BM>(a.offsets, a.G, blockIdx.y, s_pref, scratch);
+    const RowTile rt = find_row_tile<BM>(a.offsets, a.G, a.M_total, blockIdx.y, s_pref, scratch);
     if (!rt.valid) return;
     g = rt.g;
     i_lo = rt.m_lo;

@@ -159,7 +159,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     total = a.G * (int)cdiv64(N, TM) * tn_n;
   } else {
     int n = 0;
-    if (tid < a.G) n = (a.offsets[tid + 1] - a.offsets[tid] + TM - 1) / TM;
+    if (tid < a.G) n = (group_row(a.offsets, tid + 1, a.M_total) - group_row(a.offsets, tid, a.M_total) + TM - 1) / TM;
     const int ex = block_scan<NW>(n, scratch, &mt_total);
     if (tid < a.G) s_pref[tid] = ex;
     __syncthreads();
@@ -176,8 +176,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       const int g = L / per_g, rem = L - g * per_g;
       const int ti = rem / tn_n, tj = rem - ti * tn_n;
       t.g = __builtin_amdgcn_readfirstlane(g);
-      t.r_lo = __builtin_amdgcn_readfirstlane(a.offsets[t.g]);
-      t.r_hi = __builtin_amdgcn_readfirstlane(a.offsets[t.g + 1]);
+      t.r_lo = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g, a.M_total));
+      t.r_hi = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g + 1, a.M_total));
       t.i_lo = (int64_t)__builtin_amdgcn_readfirstlane(ti) * TM;
       t.i_hi = t.i_lo + TM < N ? t.i_lo + TM : N;
       t.j0 = (int64_t)__builtin_amdgcn_readfirstlane(tj) * TN;
@@ -201,8 +201,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       const int tm_local = rem / nbw;
       const int tn = blk * NB + (rem - tm_local * nbw);
       t.g = __builtin_amdgcn_readfirstlane(g);
-      const int glo = __builtin_amdgcn_readfirstlane(a.offsets[t.g]);
-      const int ghi = __builtin_amdgcn_readfirstlane(a.offsets[t.g + 1]);
+      const int glo = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g, a.M_total));
+      const int ghi = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g + 1, a.M_total));
       t.i_lo = glo + (int64_t)__builtin_amdgcn_readfirstlane(tm_local) * TM;
       t.i_hi = t.i_lo + TM < ghi ? t.i_lo + TM : ghi;
       const int colw = (EPI == MOE_EPI_SWIGLU) ? TN / 2 : TN;

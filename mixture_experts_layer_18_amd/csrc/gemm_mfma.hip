@@ -84,8 +84,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
     g = L / per_g;
     const int rem = L - g * per_g;
     const int ti = rem / tj_n, tj = rem - ti * tj_n;
-    r_lo = a.offsets[g];
-    r_hi = a.offsets[g + 1];
+    r_lo = group_row(a.offsets, g, a.M_total);
+    r_hi = group_row(a.offsets, g + 1, a.M_total);
     if (a.splits > 1) {
       // slice `split` of the group's rows, in whole k-steps
       const int64_t chunk = cdiv64(cdiv64(r_hi - r_lo, a.splits), BK) * BK;
@@ -99,7 +99,7 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
     ncols = K;
   } else {
     int n = 0;
-    if (tid < a.G) n = (a.offsets[tid + 1] - a.offsets[tid] + TM - 1) / TM;
+    if (tid < a.G) n = (group_row(a.offsets, tid + 1, a.M_total) - group_row(a.offsets, tid, a.M_total) + TM - 1) / TM;
     int mt_total;
     const int ex = block_exclusive_scan256(n, scratch, &mt_total);
     if (tid < a.G) s_pref[tid] = ex;
@@ -130,8 +130,8 @@ __global__ __launch_bounds__(256, OCC) void gemm_kernel(Args a) {
     const int rem = l - blk * mt * NB;
     const int tm_local = rem / nbw;
     const int tn = blk * NB + (rem - tm_local * nbw);
-    i_lo = a.offsets[g] + (int64_t)tm_local * TM;
-    const int64_t gend = a.offsets[g + 1];
+    i_lo = group_row(a.offsets, g, a.M_total) + (int64_t)tm_local * TM;
+    const int64_t gend = group_row(a.offsets, g + 1, a.M_total);
     i_hi = i_lo + TM < gend ? i_lo + TM : gend;
     j0 = (int64_t)tn * colw;
     r_hi = (LAYOUT == MOE_GEMM_NT) ? K : N;

@@ -58,6 +58,12 @@ hipError_t launch_split_reduce_f32(const float* part, int nsplit, int64_t n, flo
 // ---- fp32 router products (matrix cores)
 hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T, int d, int E,
                                 float* logits, hipStream_t st);
+// the forward's router logits with the routing of moe_route fused in (bf16 x,
+// d a multiple of 128, E <= 64): logits, idx, gate and the block histogram
+bool router_route_fused(int dtype, int d, int E);
+hipError_t launch_router_route(const void* x, const float* w, int T, int d, int E, float* logits,
+                               const float* bias, int k, int score, int renorm, int32_t* idx, float* gate,
+                               int32_t* hist, hipStream_t st);
 int router_wgrad_splits(int T, int d, int E);
 // dw[E, d] = dl[T, E]^T x[T, d]; `part` holds router_wgrad_splits(..) * E * d floats
 hipError_t launch_router_wgrad(const float* dl, const void* x, int dtype, int T, int d, int E,
@@ -85,6 +91,5 @@ hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* p
                                 const float* w_router, int dense_router, int T, int d, int E,
                                 int k, void* dx, hipStream_t st);
 hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t st);
-hipError_t launch_group_offsets_1(int32_t* offsets, int32_t M, hipStream_t st);
 
 }  // namespace moe

@@ -7,49 +7,9 @@
 // Handbook, section 2.5, fp32 router dtype).  Permutation sends each token's
 // row to its selected experts in expert-contiguous order (Handbook 2.5:
 // tokens are sent to the selected experts).
-#include "kernels.h"
+#include "route_common.h"
 
 namespace moe {
-
-// Map an fp32 key to an unsigned integer with the same order.  -0 is folded
-// onto +0 and NaN onto the very bottom, so NaN keys are picked last.
-MOE_DEV uint32_t ordered_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;  // NaN
-  if (u == 0x80000000u) u = 0u;                     // -0 -> +0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Candidate code: key in the high word, (0xffffffff - expert) in the low word,
-// so the maximum is the best key and, among equal keys, the lowest expert.
-MOE_DEV uint64_t cand_code(float key, int e) {
-  return ((uint64_t)ordered_bits(key) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
-}
-
-template <int L>
-MOE_DEV uint64_t group_max_u64(uint64_t v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) {
-    uint64_t o = __shfl_xor(v, m, L);
-    v = o > v ? o : v;
-  }
-  return v;
-}
-template <int L>
-MOE_DEV double group_sum_f64(double v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) v += __shfl_xor(v, m, L);
-  return v;
-}
-template <int L>
-MOE_DEV float group_max_f32(float v) {
-#pragma unroll
-  for (int m = L / 2; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, L));
-  return v;
-}
-
-// sigmoid evaluated in fp64 and rounded once to fp32
-MOE_DEV float sigmoid_rounded(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
 
 // One group of L lanes handles one token; lane i holds experts i, i+L, ...
 // (V = ceil(E / L) values).  A workgroup of 256 threads handles one block of
@@ -71,80 +31,8 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   for (int tl = tid / L; tl < MOE_ROUTE_BLOCK; tl += GROUPS) {
     const int t = blk * MOE_ROUTE_BLOCK + tl;
     if (t >= T) break;  // uniform within the group
-    const float* lrow = logits + (int64_t)t * E;
-    float lv[V];
-    float sc[V];
-    uint64_t cand[V];
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int e = li + v * L;
-      lv[v] = (e < E) ? lrow[e] : -INFINITY;
-    }
-    if (score == MOE_SIGMOID) {
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int e = li + v * L;
-        sc[v] = sigmoid_rounded(lv[v]);
-        const float key = bias ? (sc[v] + (e < E ? bias[e] : 0.0f)) : sc[v];
-        cand[v] = (e < E) ? cand_code(key, e) : 0ull;
-      }
-    } else {
-      float m = lv[0];
-#pragma unroll
-      for (int v = 1; v < V; ++v) m = fmaxf(m, lv[v]);
-      m = group_max_f32<L>(m);
-      double z[V], zs = 0.0;
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int e = li + v * L;
-        z[v] = (e < E) ? exp((double)lv[v] - (double)m) : 0.0;
-        zs += z[v];
-      }
-      zs = group_sum_f64<L>(zs);
-#pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const int e = li + v * L;
-        sc[v] = (float)(z[v] / zs);
-        cand[v] = (e < E) ? cand_code(lv[v], e) : 0ull;
-      }
-    }
-    // k rounds of group arg-max; slot j's expert and score land in lane j
-    int my_e = 0;
-    float my_s = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      uint64_t b = cand[0];
-#pragma unroll
-      for (int v = 1; v < V; ++v) b = cand[v] > b ? cand[v] : b;
-      b = group_max_u64<L>(b);
-      const int e = (int)(0xffffffffu - (uint32_t)(b & 0xffffffffu));
-      const int owner = e % L, ov = e / L;
-      float s_own = 0.0f;
-#pragma unroll
-      for (int v = 0; v < V; ++v)
-        if (v == ov) s_own = sc[v];
-      if (li == owner) {
-#pragma unroll
-        for (int v = 0; v < V; ++v)
-          if (v == ov) cand[v] = 0ull;
-      }
-      const float s_e = __shfl(s_own, owner, L);
-      if (li == j) {
-        my_e = e;
-        my_s = s_e;
-      }
-    }
-    double gsum = (li < k) ? (double)my_s : 0.0;
-    gsum = group_sum_f64<L>(gsum);
-    if (li < k) {
-      float g;
-      if (score == MOE_SOFTMAX && !renorm)
-        g = my_s;
-      else
-        g = (float)((double)my_s / gsum);
-      idx[(int64_t)t * k + li] = my_e;
-      gate[(int64_t)t * k + li] = g;
-      atomicAdd(&s_hist[my_e], 1);
-    }
+    rte::route_token<L, V>(logits + (int64_t)t * E, bias, E, k, score, renorm, li, idx + (int64_t)t * k,
+                           gate + (int64_t)t * k, s_hist);
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) hist[(int64_t)e * nblk + blk] = s_hist[e];

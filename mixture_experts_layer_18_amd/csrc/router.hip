@@ -20,7 +20,7 @@
 //    a slice of the tokens; slices are summed afterwards in a fixed order, so
 //    the result is deterministic.  For bf16 x on the bf16 matrix cores with
 //    dlogits split the same way (below); for fp32 x on the fp32 ones.
-#include "kernels.h"
+#include "route_common.h"
 
 namespace moe {
 namespace rt {
@@ -104,15 +104,35 @@ constexpr int STILE = 64 * SROW;                // one 64-row tile (8 KB)
 
 MOE_DEV int sw_slot(int r, int c) { return c ^ ((r >> 1) & 7); }
 
-__global__ __launch_bounds__(256) void router_logits_split_kernel(const bf16_t* __restrict__ x,
-                                                                  const float* __restrict__ w, int T,
-                                                                  int d, int E,
-                                                                  float* __restrict__ logits) {
-  __shared__ __attribute__((aligned(16))) char sm[2][4 * STILE];  // [buffer][x, hi, mid, lo]
+// Routing of the kernel's own logits (ROUTE: E <= 64, so one workgroup holds
+// every logit of its 64 tokens, two blocks of MOE_ROUTE_BLOCK): top-k, gates
+// and the two blocks' expert histograms, as moe_route computes them.
+struct RouteOut {
+  const float* bias;
+  int k, score, renorm, nblk;
+  int32_t* idx;
+  float* gate;
+  int32_t* hist;
+};
+
+// KG groups of 4 waves split the reduction: group g takes the steps
+// g, g + KG, g + 2 KG, ... with LDS buffers of its own, and the groups' sums
+// are added in group order at the end (deterministic).  With KG = 2 two
+// waves share each SIMD, so one wave's weight splitting, LDS traffic and
+// barrier wait run under the other's MFMAs (one 4-wave workgroup per CU
+// serialises them).
+template <bool ROUTE, int KG>
+__global__ __launch_bounds__(256 * KG) void router_logits_split_kernel(const bf16_t* __restrict__ x,
+                                                                       const float* __restrict__ w, int T,
+                                                                       int d, int E,
+                                                                       float* __restrict__ logits,
+                                                                       RouteOut ro) {
+  __shared__ __attribute__((aligned(16))) char sm[2 * KG][4 * STILE];  // [group, buffer][x, hi, mid, lo]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int grp = wave >> 2, ltid = tid & 255;
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  // loader: thread -> row tid/4, 16 consecutive k at (tid%4)*16 (two 16-byte chunks)
-  const int lr = tid >> 2, lc = (tid & 3) * 2;
+  // loader: thread -> row ltid/4, 16 consecutive k at (ltid%4)*16 (two 16-byte chunks)
+  const int lr = ltid >> 2, lc = (ltid & 3) * 2;
   const int tr = min(t0 + lr, T - 1), er = min(e0 + lr, E - 1);
   const bf16_t* xp = x + (int64_t)tr * d + lc * 8;
   const float* wp = w + (int64_t)er * d + lc * 8;
@@ -160,7 +180,8 @@ __global__ __launch_bounds__(256) void router_logits_split_kernel(const bf16_t* 
     put(buf, lc, o.x0, o.w0, o.w1);
     put(buf, lc + 1, o.x1, o.w2, o.w3);
   };
-  const int wt = wave >> 1, we = wave & 1;  // this wave's 32-token x 32-expert tile
+  const int wl = wave & 3;
+  const int wt = wl >> 1, we = wl & 1;  // this wave's 32-token x 32-expert tile
   f32x16_t acc;
 #pragma unroll
   for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -178,29 +199,83 @@ __global__ __launch_bounds__(256) void router_logits_split_kernel(const bf16_t* 
       }
     }
   };
-  // steps in pairs so that each register set has a fixed name: step j uses
-  // set j % 2 and LDS buffer j % 2; the loads of step j + 2 are issued while
-  // step j is computed
-  // d is a multiple of 2 * SBK (the launcher sends other widths to the fp32 kernel)
-  gload(0, o0);
-  gload(SBK, o1);
-  for (int k0 = 0; k0 < d; k0 += 2 * SBK) {
-    lstore(sm[0], o0);
+  // step j of group g reads k0 = (j KG + g) SBK; register set j % 2, LDS
+  // buffer j % 2 of the group; the loads of step j + 2 are in flight while
+  // step j is computed.  One barrier per step separates its LDS stores from
+  // its fragment reads; a buffer is rewritten two steps later, after the next
+  // step's barrier, which every wave passes only once done reading it.
+  // d is a multiple of 2 KG SBK (the launcher sends other widths elsewhere).
+  char* b0 = sm[2 * grp];
+  char* b1 = sm[2 * grp + 1];
+  const int kstep = KG * SBK;
+  gload(grp * SBK, o0);
+  gload(grp * SBK + kstep, o1);
+  for (int k0 = grp * SBK; k0 < d; k0 += 2 * kstep) {
+    lstore(b0, o0);
     __syncthreads();
-    gload(k0 + 2 * SBK, o0);
-    compute(sm[0]);
-    lstore(sm[1], o1);
+    gload(k0 + 2 * kstep, o0);
+    compute(b0);
+    lstore(b1, o1);
     __syncthreads();
-    gload(k0 + 3 * SBK, o1);
-    compute(sm[1]);
+    gload(k0 + 3 * kstep, o1);
+    compute(b1);
   }
+  if constexpr (KG == 2) {
+    // group 1's sums join group 0's (fixed order), through LDS
+    __syncthreads();  // every wave is done with the operand buffers
+    float* red = reinterpret_cast<float*>(&sm[0][0]);
+    if (grp == 1) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) red[(wl * 16 + v) * 64 + lane] = acc[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] += red[(wl * 16 + v) * 64 + lane];
+  }
+  // group 0 writes the results; group 1 only takes part in the barriers below
+  const bool out = grp == 0;
   // lane: expert (lane%32) of the wave tile, tokens (v/4)*8 + (lane/32)*4 + v%4
   const int e = e0 + we * 32 + (lane & 31);
-  if (e >= E) return;
+  if constexpr (!ROUTE) {
+    if (!out || e >= E) return;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    const int t = t0 + wt * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-    if (t < T) logits[(int64_t)t * E + e] = acc[v];
+    for (int v = 0; v < 16; ++v) {
+      const int t = t0 + wt * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+      if (t < T) logits[(int64_t)t * E + e] = acc[v];
+    }
+  } else {
+    // the 64 x E logits into LDS (rows padded to 65), then one group of 16
+    // lanes per token routes from there
+    constexpr int LPAD = 65;
+    __syncthreads();  // every wave is done with the operand buffers (and the group sums)
+    float* ls = reinterpret_cast<float*>(&sm[0][0]);
+    int* s_hist = reinterpret_cast<int*>(ls + 64 * LPAD);  // [2 blocks][64 experts]
+    if (out && e < E) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tl = wt * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        ls[tl * LPAD + (e - e0)] = acc[v];
+        if (t0 + tl < T) logits[(int64_t)(t0 + tl) * E + e] = acc[v];
+      }
+    }
+    if (tid < 128) s_hist[tid] = 0;
+    __syncthreads();
+    // every wave routes: 16 lanes per token, 16 KG tokens per pass
+    {
+      const int li = tid & 15;
+      for (int tl = tid >> 4; tl < 64; tl += 16 * KG) {
+        const int t = t0 + tl;
+        if (t >= T) break;  // uniform within the 16-lane group
+        rte::route_token<16, 4>(ls + tl * LPAD, ro.bias, E, ro.k, ro.score, ro.renorm, li,
+                                ro.idx + (int64_t)t * ro.k, ro.gate + (int64_t)t * ro.k,
+                                s_hist + (tl >> 5) * 64);
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < 2 * E; i += 256 * KG) {
+      const int b = blockIdx.x * 2 + i / E, ee = i % E;
+      if (b < ro.nblk) ro.hist[(int64_t)ee * ro.nblk + b] = s_hist[(i / E) * 64 + ee];
+    }
   }
 }
 
@@ -380,12 +455,41 @@ hipError_t launch_router_logits(const void* x, int dtype, const float* w, int T,
                                 float* logits, hipStream_t st) {
   if (T == 0) return hipSuccess;
   dim3 grid((unsigned)cdiv64(T, 64), (unsigned)cdiv64(E, 64)), block(256);
-  if (dtype == MOE_BF16 && d % (2 * rt::SBK) == 0)
-    rt::router_logits_split_kernel<<<grid, block, 0, st>>>((const bf16_t*)x, w, T, d, E, logits);
+  if (dtype == MOE_BF16 && d % (4 * rt::SBK) == 0)
+    rt::router_logits_split_kernel<false, 2><<<grid, dim3(512), 0, st>>>((const bf16_t*)x, w, T, d, E, logits,
+                                                                        rt::RouteOut{});
+  else if (dtype == MOE_BF16 && d % (2 * rt::SBK) == 0)
+    rt::router_logits_split_kernel<false, 1><<<grid, block, 0, st>>>((const bf16_t*)x, w, T, d, E, logits,
+                                                                      rt::RouteOut{});
   else if (dtype == MOE_BF16)
     rt::router_logits_kernel<bf16_t><<<grid, block, 0, st>>>((const bf16_t*)x, w, T, d, E, logits);
   else
     rt::router_logits_kernel<float><<<grid, block, 0, st>>>((const float*)x, w, T, d, E, logits);
+  return hipGetLastError();
+}
+
+bool router_route_fused(int dtype, int d, int E) { return dtype == MOE_BF16 && d % (2 * rt::SBK) == 0 && E <= 64; }
+
+hipError_t launch_router_route(const void* x, const float* w, int T, int d, int E, float* logits,
+                               const float* bias, int k, int score, int renorm, int32_t* idx, float* gate,
+                               int32_t* hist, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  rt::RouteOut ro;
+  ro.bias = bias;
+  ro.k = k;
+  ro.score = score;
+  ro.renorm = renorm;
+  ro.nblk = (int)cdiv64(T, MOE_ROUTE_BLOCK);
+  ro.idx = idx;
+  ro.gate = gate;
+  ro.hist = hist;
+  static_assert(2 * MOE_ROUTE_BLOCK == 64, "two histogram blocks per workgroup");
+  if (d % (4 * rt::SBK) == 0)
+    rt::router_logits_split_kernel<true, 2><<<dim3((unsigned)cdiv64(T, 64)), dim3(512), 0, st>>>(
+        (const bf16_t*)x, w, T, d, E, logits, ro);
+  else
+    rt::router_logits_split_kernel<true, 1><<<dim3((unsigned)cdiv64(T, 64)), dim3(256), 0, st>>>(
+        (const bf16_t*)x, w, T, d, E, logits, ro);
   return hipGetLastError();
 }
 

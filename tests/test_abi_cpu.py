@@ -88,7 +88,10 @@ def test_no_workspace_forward_rejects_large_layers(lib):
     """moe_forward_no_workspace keeps its scratch in a fixed device array of
     MOE_STATIC_SCRATCH_BYTES (8 MiB): a layer whose forward scratch (two int32
     tables of E x ceil(T/32) entries) exceeds it is rejected on the host."""
-    d = make_desc(131072, 2048, 256, 8, 512, 0, 0, "sigmoid", True, "bf16")
+    # E * ceil(T/32) = 2^20 fits exactly; one more block of 32 tokens does not
+    d0 = make_desc(131072, 2048, 256, 8, 512, 0, 0, "sigmoid", True, "bf16")
+    assert lib.moe_workspace_bytes(ctypes.byref(d0), L.MOE_WS_FORWARD) == 8 << 20
+    d = make_desc(131072 + 32, 2048, 256, 8, 512, 0, 0, "sigmoid", True, "bf16")
     assert lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_FORWARD) > 8 << 20
     assert lib.moe_forward_no_workspace(ctypes.byref(d), None, None, None, None, None) == L.MOE_ERR_WORKSPACE
     bad = make_desc(64, 100, 8, 2, 256, 0, 0, "softmax", False, "f32")
@@ -160,6 +163,11 @@ def test_grouped_gemm_argument_checks(lib):
     assert call(K=96) == L.MOE_ERR_INVALID
     assert call(epi=L.MOE_EPI_SWIGLU, N=192) == L.MOE_ERR_INVALID   # gate/up halves of 64
     assert call(dtype=7) == L.MOE_ERR_INVALID
+    # no offset table: allowed for one group only (validation fails before any launch)
+    assert lib.moe_grouped_gemm(L.MOE_GEMM_NT, L.MOE_EPI_NONE, L.MOE_BF16, 4, 100, 128, 128, None, a, a, a, a,
+                                None, 0, None) == L.MOE_ERR_INVALID
+    assert lib.moe_grouped_gemm(L.MOE_GEMM_NT, L.MOE_EPI_NONE, L.MOE_BF16, 1, 100, 128, 127, None, a, a, a, a,
+                                None, 0, None) == L.MOE_ERR_INVALID
 
 
 def test_stage_enum_matches_binding():

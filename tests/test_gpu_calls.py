@@ -328,3 +328,46 @@ def test_combine_against_oracle(dtype):
         torch.cuda.synchronize()
         ref = O.combine(synth.as_f64(y_perm, dtype), gate, pos, None if sh is None else synth.as_f64(sh, dtype))
         assert_rounded(host(y), ref, dtype, "y")
+
+
+FUSED_ROUTE = [
+    ("moe7b_bf16", dict(T=1000)),                                    # E = 64, ragged last block
+    ("finegrained_bf16", dict(T=4096)),                              # E = 64, top-8
+    ("moe7b_bf16", dict(name="e16_softmax", T=300, d=256, E=16, k=4, f=128, n_shared=0, f_shared=0,
+                        score="softmax", renorm=True, bias=None)),   # E < 64, softmax renormalised
+    ("moe7b_bf16", dict(name="e64_softmax", T=777, d=256, E=64, k=2, f=128, n_shared=0, f_shared=0,
+                        score="softmax", renorm=False, bias=None)),  # softmax without renormalisation
+]
+
+
+@pytest.mark.parametrize("base,kw", FUSED_ROUTE, ids=[f"{b}-{kw.get('name', kw['T'])}" for b, kw in FUSED_ROUTE])
+def test_forward_routing_matches_moe_route(base, kw):
+    """The forward pass routes its own logits inside the router kernel (bf16
+    tokens, E <= 64); moe_route and moe_permute on those same logits must
+    give the same indices, gates, counts, offsets and permutation bit for bit."""
+    cfg = synth.CONFIG_BY_NAME[base].replace(**kw)
+    inp = synth.make_inputs(cfg)
+    desc = M.desc_from_config(cfg)
+    w = {n: dev(inp.get(n)) for n in ("w_router", "bias", "w_gateup", "w_down", "s_gateup", "s_down")}
+    x = dev(inp["x"])
+    y = torch.empty_like(x)
+    saved = M.alloc_saved(desc, training=False, gather=True)
+    M.moe_forward(desc, w, x, y, saved, M.alloc_workspace(desc, "forward"))
+    torch.cuda.synchronize()
+    T, k, E = cfg.T, cfg.k, cfg.E
+    idx = torch.empty(T, k, dtype=torch.int32, device="cuda")
+    gate = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    hist = torch.empty(max(M.route_hist_elems(desc), 1), dtype=torch.int32, device="cuda")
+    M.moe_route(desc, saved["logits"], w["bias"] if cfg.score == "sigmoid" else None, idx, gate, hist)
+    A = T * k
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offsets = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    pos = torch.empty(A, dtype=torch.int32, device="cuda")
+    src = torch.empty(A, dtype=torch.int32, device="cuda")
+    tok = torch.empty(A, dtype=torch.int32, device="cuda")
+    M.moe_permute(desc, x, idx, hist, counts, offsets, pos, src, None, M.alloc_workspace(desc, "permute"), tok=tok)
+    torch.cuda.synchronize()
+    for name, a, b in (("idx", saved["idx"], idx), ("gate", saved["gate"], gate), ("counts", saved["counts"], counts),
+                       ("offsets", saved["offsets"], offsets), ("pos", saved["pos"], pos), ("src", saved["src"], src),
+                       ("tok", saved["tok"], tok)):
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{cfg.name}: {name} differs"
