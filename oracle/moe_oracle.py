@@ -52,8 +52,11 @@ identity, permutation invariants, gate renormalisation, bias-selects-only,
 brute-force top-k, the softmax Jacobian special case and the Handbook's
 parameter count; for the router training terms, torch fp64 autograd of each
 loss, the single-expert loss of exactly 1, balanced loads, the z-loss closed
-form and the bias update on balanced and skewed loads.  Every function below
-is covered by at least one pin.
+form and the bias update on balanced and skewed loads; for the fp8 mode, the
+e4m3 format table and rounding, exactness of every product on the e4m3 grid,
+the half-step error bound off it, power-of-two equivariance of the whole
+layer, closeness to the exact layer and the bf16 rounding rule.  Every
+function below is covered by at least one pin.
 """
 from __future__ import annotations
 
@@ -183,7 +186,8 @@ def _split_gateup(w_gateup):
 
 # ----------------------------------------------------------------------------- layer
 def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
-            top_k, score, renorm=False, forced_idx=None):
+            top_k, score, renorm=False, forced_idx=None, fp8=False, forced_h=None,
+            forced_s_h=None):
     """Forward pass of the MoE layer on the tokens of ``x``.
 
     x: [T, d]; w_router: [E, d] fp32; bias: [E] fp32 or None (sigmoid only);
@@ -194,6 +198,12 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
     ``forced_idx`` replaces the selection (used to follow another
     implementation's choice on near-tied tokens); gates are then recomputed
     from this oracle's own scores for the forced experts.
+
+    ``fp8``: the expert products (routed and shared) run as e4m3 products
+    with row-wise scales (``swiglu_ffn_fp8``); the router stays fp32.
+    ``forced_h`` / ``forced_s_h`` replace the bf16 copy of H that the down
+    products quantise (permuted rows / token rows): another implementation's
+    rounding of the same H, used where its fp32 sums round the other way.
 
     Returns a dict with every intermediate of the layer."""
     x = np.asarray(x, F64)
@@ -221,8 +231,13 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         if r1 == r0:
             continue
-        G, U, H, Y = swiglu_ffn(x_perm[r0:r1], np.asarray(wg_all[e], F64),
-                                np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64))
+        if fp8:
+            G, U, H, Y = swiglu_ffn_fp8(x_perm[r0:r1], np.asarray(wg_all[e], F64),
+                                        np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64),
+                                        None if forced_h is None else forced_h[r0:r1])
+        else:
+            G, U, H, Y = swiglu_ffn(x_perm[r0:r1], np.asarray(wg_all[e], F64),
+                                    np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64))
         preact[r0:r1, :f] = G
         preact[r0:r1, f:] = U
         h[r0:r1] = H
@@ -234,7 +249,10 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
 
     if s_gateup is not None:
         sg, su = _split_gateup(np.asarray(s_gateup, F64))
-        Gs, Us, Hs, ys = swiglu_ffn(x, sg, su, np.asarray(s_down, F64))
+        if fp8:
+            Gs, Us, Hs, ys = swiglu_ffn_fp8(x, sg, su, np.asarray(s_down, F64), forced_s_h)
+        else:
+            Gs, Us, Hs, ys = swiglu_ffn(x, sg, su, np.asarray(s_down, F64))
         out.update(s_preact=np.concatenate([Gs, Us], axis=1), s_h=Hs, ys=ys)
     else:
         ys = np.zeros((T, d), F64)
@@ -424,12 +442,15 @@ def bias_update(bias32, counts, T, k, rate):
 
 
 def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False,
-             terms=None):
+             terms=None, fp8=False):
     """Backward pass for upstream gradient dy [T, d], reusing ``forward``'s dict.
 
     Returns dict: dx [T,d], d_w_gateup [E,2f,d], d_w_down [E,d,f],
     d_s_gateup / d_s_down (or None), d_w_router [E,d], d_logits [T,E],
-    dgate [T,k], plus the permuted intermediates dy_perm, dgu, dx_perm."""
+    dgate [T,k], plus the permuted intermediates dy_perm, dgu, dx_perm.
+
+    ``fp8``: the expert data gradients (routed and shared) run as e4m3
+    products (``swiglu_ffn_backward_fp8``); weight gradients stay exact."""
     x = np.asarray(x, F64)
     dy = np.asarray(dy, F64)
     T, d = x.shape
@@ -451,7 +472,8 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
             continue
         G = fwd["preact"][r0:r1, :f]
         U = fwd["preact"][r0:r1, f:]
-        dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward(
+        ffn_bwd = swiglu_ffn_backward_fp8 if fp8 else swiglu_ffn_backward
+        dz, dWg, dWu, dWd, dG, dU = ffn_bwd(
             fwd["x_perm"][r0:r1], np.asarray(wg_all[e], F64), np.asarray(wu_all[e], F64),
             np.asarray(w_down[e], F64), G, U, fwd["h"][r0:r1], dy_perm[r0:r1])
         d_w_gateup[e, :f] = dWg
@@ -469,8 +491,9 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
         Fs = sg.shape[0]
         Gs = fwd["s_preact"][:, :Fs]
         Us = fwd["s_preact"][:, Fs:]
-        dxs, dSg, dSu, dSd, _, _ = swiglu_ffn_backward(x, sg, su, np.asarray(s_down, F64),
-                                                       Gs, Us, fwd["s_h"], dy)
+        ffn_bwd = swiglu_ffn_backward_fp8 if fp8 else swiglu_ffn_backward
+        dxs, dSg, dSu, dSd, _, _ = ffn_bwd(x, sg, su, np.asarray(s_down, F64),
+                                           Gs, Us, fwd["s_h"], dy)
         out["d_s_gateup"] = np.concatenate([dSg, dSu], axis=0)
         out["d_s_down"] = dSd
         out["dx_shared"] = dxs
@@ -593,3 +616,66 @@ def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets):
             C[r0:r1] = (A[r0:r1] @ B[g].T) * np.asarray(a_scale, F64)[r0:r1, None] * \
                 np.asarray(b_scale, F64)[g][None, :]
     return C
+
+
+# ----------------------------------------------------------------------------- fp8 layer
+# The expert products of the layer in e4m3 (Apex-3 code page, "Run it
+# yourself": the fp8_rowwise precision; KempnerForge README, "MoE roadmap":
+# FP8 mixed precision).  Readings, where the pages name only the recipe:
+#   - every product quantises both operands row-wise along its reduction
+#     dimension, from the operands' current values (activations per row,
+#     weights per output row in the forward, per reduction-dimension column for
+#     the data gradients);
+#   - an activation is quantised from its bf16 copy, the copy the bf16 layer
+#     stores (H, the gate-weighted dY, dG | dU), so that the rounding to bf16
+#     precedes the quantisation as it does on a device that keeps bf16
+#     activations; the router stays fp32;
+#   - weight gradients stay in the layer's own precision (exact here), the
+#     row-wise recipe with high-precision weight gradients.
+
+def round_bf16(v):
+    """The bf16 value a stored fp32 result takes: v rounded to fp32, then to
+    the nearest bf16 (8 significand bits), ties to the even one (fp64 out)."""
+    v32 = np.ascontiguousarray(np.asarray(v, F64).astype(F32))
+    b = v32.view(np.uint32).astype(np.uint64)
+    b = ((b + 0x7FFF + ((b >> 16) & 1)) >> 16) << 16
+    return b.astype(np.uint32).view(F32).astype(F64)
+
+
+def fp8_product(a, b):
+    """a [M, K] times b [N, K]^T with each operand quantised row-wise along K
+    (``quantize_rowwise``) and the scaled e4m3 product taken exactly (fp64)."""
+    a = np.asarray(a, F64)
+    qa, sa = quantize_rowwise(a)
+    qb, sb = quantize_rowwise(b)
+    return grouped_gemm_fp8_nt(qa, sa, qb[None], sb[None], np.array([0, a.shape[0]]))
+
+
+def swiglu_ffn_fp8(z, w_gate, w_up, w_down, forced_h=None):
+    """``swiglu_ffn`` with both products in e4m3: G | U = fp8(z) . fp8(W_g | W_u)^T,
+    H = silu(G) U (fp64), Y = fp8(bf16(H)) . fp8(W_d)^T; ``forced_h`` replaces
+    bf16(H) as the down product's input.  Returns (G, U, H, Y) like
+    ``swiglu_ffn``, H unrounded."""
+    f = w_gate.shape[0]
+    GU = fp8_product(z, np.concatenate([w_gate, w_up], axis=0))
+    G, U = GU[:, :f], GU[:, f:]
+    H = silu(G) * U
+    Hb = round_bf16(H) if forced_h is None else np.asarray(forced_h, F64)
+    return G, U, H, fp8_product(Hb, w_down)
+
+
+def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY):
+    """``swiglu_ffn_backward`` with the two data gradients in e4m3:
+    dH = fp8(bf16(dY)) . fp8 of W_d along its rows d (W_d^T quantised
+    row-wise), dz = fp8(bf16(dG | dU)) . fp8 of W_g | W_u along 2f; the
+    weight gradients are exact (fp64).  Same return values."""
+    dH = fp8_product(round_bf16(dY), np.asarray(w_down, F64).T)
+    sg = 1.0 / (1.0 + np.exp(-G))
+    dG = dH * U * sg * (1.0 + G * (1.0 - sg))
+    dU = dH * (G * sg)
+    dW_d = dY.T @ H
+    dW_g = dG.T @ z
+    dW_u = dU.T @ z
+    w_gu = np.concatenate([w_gate, w_up], axis=0)
+    dz = fp8_product(round_bf16(np.concatenate([dG, dU], axis=1)), w_gu.T)
+    return dz, dW_g, dW_u, dW_d, dG, dU

@@ -601,3 +601,145 @@ def test_fp8_tensorwise_quantisation():
     assert s2 == s * np.float32(8.0) and np.array_equal(q2, q)
     qz, sz = O.quantize_tensorwise(np.zeros((3, 64), np.float32))
     assert sz == 1.0 and not qz.any()
+
+
+# --------------------------------------------------------------------------- fp8 layer
+def _e4m3_grid(g, R, C, p, cols=False):
+    """[R, C] values on the e4m3 grid times 2^-p, every row's largest magnitude
+    exactly 448 * 2^-p (with ``cols`` every column's too), so that row-wise
+    quantisation (of the matrix, and with ``cols`` of its transpose) is exact:
+    scale 2^-p, codes equal to the values."""
+    codes = g.integers(0, 0x7e, size=(R, C)).astype(np.uint8)       # 0 .. 416
+    m = O.e4m3_decode(codes) * np.where(g.random((R, C)) < 0.5, -1.0, 1.0)
+    r = np.arange(R)
+    m[r, r % C] = 448.0 * np.where(r % 2, -1.0, 1.0)
+    if cols:
+        c = np.arange(C)
+        m[c % R, c] = 448.0
+    return m * 2.0 ** -p
+
+
+def _grid_layer(seed, T, d, E, k, f, Fs, score, renorm):
+    g = np.random.default_rng(seed)
+    L = _rand_layer(seed, T, d, E, k, f, Fs, score, renorm)
+    L["x"] = _e4m3_grid(g, T, d, 7)
+    L["w_gateup"] = np.stack([_e4m3_grid(g, 2 * f, d, 10) for _ in range(E)])
+    L["w_down"] = np.stack([_e4m3_grid(g, d, f, 10, cols=True) for _ in range(E)])
+    if Fs:
+        L["s_gateup"] = _e4m3_grid(g, 2 * Fs, d, 10)
+        L["s_down"] = _e4m3_grid(g, d, Fs, 10, cols=True)
+    L["dy"] = _e4m3_grid(g, T, d, 6)
+    return L
+
+
+def test_fp8_product_exact_on_the_grid_and_bounded_off_it():
+    """fp8_product equals the exact product when both operands are on the
+    e4m3 grid with row maxima 448 * 2^-p, and off the grid stays within the
+    half-step bound: each quantised element is within 2^-4 of its value
+    relative (normal range) plus half the smallest subnormal step."""
+    g = np.random.default_rng(71)
+    a = _e4m3_grid(g, 40, 96, 5)
+    b = _e4m3_grid(g, 24, 96, 9)
+    assert np.array_equal(O.fp8_product(a, b), a @ b.T)
+    a = g.standard_normal((40, 96))
+    b = g.standard_normal((24, 96))
+    sa = np.abs(a).max(1) / 448.0
+    sb = np.abs(b).max(1) / 448.0
+    ea = np.abs(a) * 2.0 ** -4 + sa[:, None] * 2.0 ** -10
+    eb = np.abs(b) * 2.0 ** -4 + sb[:, None] * 2.0 ** -10
+    bound = ea @ np.abs(b).T + np.abs(a) @ eb.T + ea @ eb.T
+    err = np.abs(O.fp8_product(a, b) - a @ b.T)
+    assert np.all(err <= bound * (1 + 1e-6))
+    assert err.max() > 0
+
+
+def test_round_bf16_against_the_format():
+    """round_bf16: exact bf16 values stay, the midpoint between two bf16
+    neighbours goes to the one with an even last significand bit, one fp32
+    ulp either side of it goes to the nearer; fp64 input is rounded to fp32
+    first."""
+    one, nxt = 1.0, 1.0 + 2.0 ** -7                       # neighbours; 1.0 has the even bit
+    assert O.round_bf16([one, nxt, -nxt, 0.0])[1] == nxt
+    mid = 1.0 + 2.0 ** -8
+    assert O.round_bf16([mid])[0] == one
+    assert O.round_bf16([mid + 2.0 ** -23])[0] == nxt
+    assert O.round_bf16([mid - 2.0 ** -23])[0] == one
+    mid2 = nxt + 2.0 ** -8                                 # between nxt (odd) and 1 + 2^-6 (even)
+    assert O.round_bf16([mid2])[0] == 1.0 + 2.0 ** -6
+    # within half an fp32 ulp below the midpoint: fp32 rounding lands on it first
+    assert O.round_bf16([mid2 - 2.0 ** -26])[0] == 1.0 + 2.0 ** -6
+    v = np.random.default_rng(3).standard_normal(1000) * 1e3
+    r = O.round_bf16(v)
+    assert np.all(np.abs(r - v) <= np.abs(v) * 2.0 ** -8 * (1 + 1e-6))
+    bits = r.astype(np.float32).view(np.uint32)
+    assert not np.any(bits & 0xFFFF)
+
+
+@pytest.mark.parametrize("score,Fs", [("softmax", 8), ("sigmoid", 0)])
+def test_fp8_layer_exact_on_the_e4m3_grid(score, Fs):
+    """Tokens and weights on the e4m3 grid (row maxima 448 * 2^-p): the fp8
+    layer's gate/up pre-activations equal the exact layer's bit for bit, and
+    so do its down outputs when the down products take a bf16 H that is on the
+    grid (forced).  With top-1 routing (gate exactly 1) and dy on the grid,
+    the down data gradient is exact too: dG | dU and dW_down equal the exact
+    backward's."""
+    T, d, E, k, f = 24, 48, 4, 1, 32
+    L = _grid_layer(5, T, d, E, k, f, Fs, score, True)
+    ex = _fwd(L)
+    g = np.random.default_rng(9)
+    fh = _e4m3_grid(g, T * k, f, 3)
+    fsh = _e4m3_grid(g, T, Fs, 3) if Fs else None
+    f8 = _fwd(L, fp8=True, forced_h=fh, forced_s_h=fsh)
+    assert np.array_equal(f8["idx"], ex["idx"])
+    assert np.array_equal(f8["preact"], ex["preact"])
+    assert np.array_equal(f8["h"], ex["h"])
+    for e in range(E):
+        r0, r1 = ex["offsets"][e], ex["offsets"][e + 1]
+        assert np.array_equal(f8["y_perm"][r0:r1], fh[r0:r1] @ L["w_down"][e].T)
+    if Fs:
+        assert np.array_equal(f8["s_preact"], ex["s_preact"])
+        assert np.array_equal(f8["ys"], fsh @ L["s_down"].T)
+    assert np.all(ex["gate"] == 1.0)
+    b_ex = _bwd(L, ex)
+    b_8 = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                     f8, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True)
+    assert np.array_equal(b_8["dgu"], b_ex["dgu"])
+    assert np.array_equal(b_8["d_w_down"][:, :, :], b_ex["d_w_down"])
+
+
+def test_fp8_layer_power_of_two_equivariance():
+    """Scaling W_down (routed and shared) by 2^3 scales y exactly by 2^3, and
+    scaling dy by 2^-2 scales dx and every weight gradient exactly by 2^-2:
+    each quantisation scale follows its operand, so a dropped or misplaced
+    scale breaks the identity (random layer, off the grid)."""
+    L = _rand_layer(11, 40, 32, 6, 2, 16, 16, "sigmoid", True)
+    f1 = _fwd(L, fp8=True)
+    L2 = dict(L, w_down=L["w_down"] * 8.0, s_down=L["s_down"] * 8.0)
+    f2 = _fwd(L2, fp8=True)
+    assert np.array_equal(f2["y"], 8.0 * f1["y"])
+    b1 = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                    f1, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True)
+    b2 = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                    f1, L["dy"] * 0.25, score=L["score"], renorm=L["renorm"], fp8=True)
+    for key in ("dx", "d_w_gateup", "d_w_down", "d_s_gateup", "d_s_down", "d_w_router"):
+        assert np.array_equal(b2[key], 0.25 * b1[key]), key
+
+
+@pytest.mark.parametrize("case", CASES[:4])
+def test_fp8_layer_close_to_the_exact_layer(case):
+    """Off the grid the fp8 layer is the exact layer up to e4m3 rounding: y, dx
+    and the weight gradients within a few per cent (rel-L2) of the exact
+    layer, and not equal to it.  A transposed operand, a wrong expert's
+    weights or a lost term would be off by order one."""
+    L = _rand_layer(*case)
+    ex = _fwd(L)
+    f8 = _fwd(L, fp8=True, forced_idx=ex["idx"])
+    b_ex = _bwd(L, ex)
+    b_8 = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                     f8, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True)
+    checks = [(f8["y"], ex["y"]), (b_8["dx"], b_ex["dx"]), (b_8["d_w_gateup"], b_ex["d_w_gateup"]),
+              (b_8["d_w_down"], b_ex["d_w_down"])]
+    if L["s_gateup"] is not None:
+        checks += [(b_8["d_s_gateup"], b_ex["d_s_gateup"]), (b_8["d_s_down"], b_ex["d_s_down"])]
+    for got, want in checks:
+        assert 1e-4 < _rel(got, want) < 0.08, _rel(got, want)
