@@ -530,15 +530,24 @@ def expert_parameter_count(d_model, d_ff):
 # bits; exponent 0 holds the subnormals m/8 * 2^-6; 0x7f / 0xff are NaN; the
 # largest finite value is 448 (no infinities).
 
-def e4m3_decode(codes):
-    """Value of each e4m3 code (uint8 array) as fp64."""
-    c = np.asarray(codes, np.uint8).astype(np.int64)
+def _e4m3_values():
+    """Value of each of the 256 e4m3 codes (index = code), fp64."""
+    c = np.arange(256, dtype=np.int64)
     sign = np.where(c & 0x80, -1.0, 1.0)
     e = (c >> 3) & 15
     m = c & 7
     val = np.where(e == 0, m / 8.0 * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e.astype(F64) - 7.0))
     val = np.where((e == 15) & (m == 7), np.nan, val)
     return sign * val
+
+
+_E4M3_VALUES = _e4m3_values()
+
+
+def e4m3_decode(codes):
+    """Value of each e4m3 code (uint8 array) as fp64 (a lookup in the table of
+    all 256 codes)."""
+    return _E4M3_VALUES[np.asarray(codes, np.uint8)]
 
 
 def _e4m3_table():
@@ -629,7 +638,8 @@ def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets):
 #   - an activation is quantised from its bf16 copy, the copy the bf16 layer
 #     stores (H, the gate-weighted dY, dG | dU), so that the rounding to bf16
 #     precedes the quantisation as it does on a device that keeps bf16
-#     activations; the router stays fp32;
+#     activations; dG | dU are formed from the bf16 copies of G and U, the
+#     pre-activations the layer saves; the router stays fp32;
 #   - weight gradients stay in the layer's own precision (exact here), the
 #     row-wise recipe with high-precision weight gradients.
 
@@ -668,11 +678,15 @@ def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY):
     """``swiglu_ffn_backward`` with the two data gradients in e4m3:
     dH = fp8(bf16(dY)) . fp8 of W_d along its rows d (W_d^T quantised
     row-wise), dz = fp8(bf16(dG | dU)) . fp8 of W_g | W_u along 2f; the
-    weight gradients are exact (fp64).  Same return values."""
+    weight gradients are exact (fp64).  dG | dU, which the second product
+    quantises, come from the pre-activations as the layer stores them (bf16),
+    so that this quantisation sees the values a bf16 layer holds.  Same
+    return values."""
     dH = fp8_product(round_bf16(dY), np.asarray(w_down, F64).T)
-    sg = 1.0 / (1.0 + np.exp(-G))
-    dG = dH * U * sg * (1.0 + G * (1.0 - sg))
-    dU = dH * (G * sg)
+    Gb, Ub = round_bf16(G), round_bf16(U)
+    sg = 1.0 / (1.0 + np.exp(-Gb))
+    dG = dH * Ub * sg * (1.0 + Gb * (1.0 - sg))
+    dU = dH * (Gb * sg)
     dW_d = dY.T @ H
     dW_g = dG.T @ z
     dW_u = dU.T @ z

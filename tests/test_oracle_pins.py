@@ -619,10 +619,16 @@ def _e4m3_grid(g, R, C, p, cols=False):
     return m * 2.0 ** -p
 
 
-def _grid_layer(seed, T, d, E, k, f, Fs, score, renorm):
+def _grid_layer(seed, T, d, E, k, f, Fs, score, renorm, one_hot=False):
+    """A layer on the e4m3 grid.  one_hot: each token row has one nonzero
+    element (448 * 2^-7), so that every pre-activation is one product of two
+    e4m3 values (at most 8 significant bits): exact in bf16."""
     g = np.random.default_rng(seed)
     L = _rand_layer(seed, T, d, E, k, f, Fs, score, renorm)
     L["x"] = _e4m3_grid(g, T, d, 7)
+    if one_hot:
+        L["x"] = np.zeros((T, d))
+        L["x"][np.arange(T), g.integers(0, d, T)] = 448.0 * 2.0 ** -7
     L["w_gateup"] = np.stack([_e4m3_grid(g, 2 * f, d, 10) for _ in range(E)])
     L["w_down"] = np.stack([_e4m3_grid(g, d, f, 10, cols=True) for _ in range(E)])
     if Fs:
@@ -675,16 +681,17 @@ def test_round_bf16_against_the_format():
     assert not np.any(bits & 0xFFFF)
 
 
-@pytest.mark.parametrize("score,Fs", [("softmax", 8), ("sigmoid", 0)])
-def test_fp8_layer_exact_on_the_e4m3_grid(score, Fs):
+@pytest.mark.parametrize("score,Fs,one_hot", [("softmax", 8, False), ("sigmoid", 0, False),
+                                              ("softmax", 8, True), ("sigmoid", 0, True)])
+def test_fp8_layer_exact_on_the_e4m3_grid(score, Fs, one_hot):
     """Tokens and weights on the e4m3 grid (row maxima 448 * 2^-p): the fp8
     layer's gate/up pre-activations equal the exact layer's bit for bit, and
     so do its down outputs when the down products take a bf16 H that is on the
-    grid (forced).  With top-1 routing (gate exactly 1) and dy on the grid,
-    the down data gradient is exact too: dG | dU and dW_down equal the exact
-    backward's."""
+    grid (forced).  With one-hot token rows (pre-activations exact in bf16),
+    top-1 routing (gate exactly 1) and dy on the grid, the down data gradient
+    is exact too: dG | dU and dW_down equal the exact backward's."""
     T, d, E, k, f = 24, 48, 4, 1, 32
-    L = _grid_layer(5, T, d, E, k, f, Fs, score, True)
+    L = _grid_layer(5, T, d, E, k, f, Fs, score, True, one_hot)
     ex = _fwd(L)
     g = np.random.default_rng(9)
     fh = _e4m3_grid(g, T * k, f, 3)
@@ -700,6 +707,9 @@ def test_fp8_layer_exact_on_the_e4m3_grid(score, Fs):
         assert np.array_equal(f8["s_preact"], ex["s_preact"])
         assert np.array_equal(f8["ys"], fsh @ L["s_down"].T)
     assert np.all(ex["gate"] == 1.0)
+    if not one_hot:
+        return
+    assert np.array_equal(O.round_bf16(ex["preact"]), ex["preact"])
     b_ex = _bwd(L, ex)
     b_8 = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
                      f8, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True)
