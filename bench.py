@@ -507,6 +507,90 @@ def fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
                     "separately"}
 
 
+def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops):
+    """The whole layer through the fp8 calls (moe_forward_fp8 and, for a
+    training workload, moe_backward_fp8) on the same inputs, timed like the
+    bf16 step: a cache flush before each step, one event pair per step.  The
+    e4m3 weight copies are written once per weight update and timed on their
+    own; the step time excludes them, the second speedup includes them."""
+    import torch
+
+    w8 = M.alloc_fp8_weights(desc, backward=training)
+    quant = lambda: M.moe_fp8_weights_quantize(desc, w, w8, True, training, stream)  # noqa: E731
+    quant()
+    saved = M.alloc_saved(desc, gather=True, training=training)
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    grads = M.alloc_grads(desc) if training else None
+    wsf = M.alloc_workspace(desc, "forward_fp8")
+    wsb = M.alloc_workspace(desc, "backward_fp8") if training else None
+
+    def step():
+        M.moe_forward_fp8(desc, w, w8, x, y, saved, wsf, stream)
+        if training:
+            M.moe_backward_fp8(desc, w, w8, x, saved, dy, dx, grads, wsb, stream)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for e0, e1 in evs:
+        flush_buf.fill_(1.0)
+        e0.record(stream)
+        step()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    step_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+    ms = sum(step_ms) / len(step_ms)
+    qa = torch.cuda.Event(enable_timing=True)
+    qb = torch.cuda.Event(enable_timing=True)
+    flush_buf.fill_(1.0)
+    qa.record(stream)
+    quant()
+    qb.record(stream)
+    torch.cuda.synchronize()
+    q_ms = qa.elapsed_time(qb)
+    del flush_buf
+    M.stage_timing(True)
+    for _ in range(min(steps, 5)):
+        step()
+    torch.cuda.synchronize()
+    st = M.stage_times()
+    M.stage_timing(False)
+    stages = {}
+    for name, (sms, n) in st.items():
+        if n == 0:
+            continue
+        e = {"us": sms * 1e3 / n, "launches": n}
+        if name in flops and not name.startswith("router"):
+            per = n // min(steps, 5)
+            tf = flops[name] / (sms * 1e-3 / n) / 1e12 if per == 1 else None
+            if tf is not None and name in FP8_PRODUCTS:
+                e.update(tflops=tf, frac_fp8=tf / PEAK_FP8_TFLOPS)
+            elif tf is not None:
+                e.update(tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
+        stages[name] = e
+    progress(f"{cfg.name}: fp8 layer {ms:.3f} ms per step, weight copies {q_ms:.3f} ms")
+    return {
+        "ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
+        "step_ms_min": min(step_ms), "step_ms_max": max(step_ms),
+        "speedup_vs_bf16_step": bf16_ms / ms,
+        "weight_copies_ms": q_ms,
+        "speedup_incl_weight_copies": bf16_ms / (ms + q_ms),
+        "stages": stages,
+        "what": "moe_forward_fp8" + (" + moe_backward_fp8" if training else "") +
+                ": e4m3 row-wise expert products (forward" + (" and both data gradients" if training else "") +
+                "), activations quantised in the step (stage fp8_quantize), bf16 weight gradients; the e4m3 "
+                "weight copies (moe_fp8_weights_quantize) are written once per weight update and timed "
+                "separately (weight_copies_ms)",
+    }
+
+
+FP8_PRODUCTS = ("gate_up", "down", "shared_gate_up", "shared_down", "down_dgrad", "gate_up_dgrad",
+                "shared_down_dgrad", "shared_gate_up_dgrad")
+
+
 def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
     """One configuration: inputs resident in HBM, W warm-up steps, K timed
     steps (each after a cache flush, each timed with its own event pair),
@@ -722,6 +806,9 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
     fp8_dd = (fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flops["down_dgrad"],
                              stage_out["down_dgrad"]["us"] * 1e-6)
               if with_fp8 and "down_dgrad" in stage_out and saved.get("preact") is not None else None)
+    fp8_ok = cfg.dtype == "bf16" and cfg.f % 128 == 0 and (cfg.n_shared * cfg.f_shared) % 128 == 0
+    fp8_whole = (fp8_layer(M, cfg, desc, w, x, dy, training, stream, args.steps, ms_step, flops)
+                 if not args.no_fp8 and fp8_ok else None)
     # the streaming memory-bound stages (route and the index-only permute are
     # latency-bound at these sizes)
     hbm3 = [n for n in ("combine", "combine_bwd", "unpermute_sum") if n in stage_out]
@@ -783,6 +870,7 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
         "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                              "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
         "stages": stage_out,
+        "fp8_layer": fp8_whole,
         "fp8_gate_up": fp8,
         "fp8_gate_up_dgrad": fp8_dg,
         "fp8_down_dgrad": fp8_dd,

@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 /* ---------------------------------------------------------------- status */
 enum {
@@ -167,7 +167,13 @@ enum { MOE_GEMM_NT = 0, MOE_GEMM_NN = 1, MOE_GEMM_TN = 2 };
 enum { MOE_EPI_NONE = 0, MOE_EPI_SWIGLU = 1, MOE_EPI_DSWIGLU = 2 };
 
 /* workspace kinds for moe_workspace_bytes */
-enum { MOE_WS_PERMUTE = 0, MOE_WS_FORWARD = 1, MOE_WS_BACKWARD = 2 };
+enum {
+  MOE_WS_PERMUTE = 0,
+  MOE_WS_FORWARD = 1,
+  MOE_WS_BACKWARD = 2,
+  MOE_WS_FORWARD_FP8 = 3,  /* moe_forward_fp8  */
+  MOE_WS_BACKWARD_FP8 = 4  /* moe_backward_fp8 */
+};
 
 /* ---------------------------------------------------------------- queries */
 
@@ -394,6 +400,93 @@ int moe_grouped_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, in
                          const int32_t *group_offsets, const uint8_t *A, const float *a_scale,
                          const uint8_t *B, const float *b_scale, void *C, void *aux, void *stream);
 
+/* moe_grouped_gemm_fp8 (MOE_EPI_NONE or MOE_EPI_SWIGLU) with the rows of A
+ * gathered: routed row m reads the codes A[rows[m]] [src_rows, K] and the
+ * scale a_scale[rows[m]] (a_scale [src_rows]), so that token rows quantised
+ * once per token feed all k of their assignments.  rows [M_total] int32
+ * (device), each in [0, src_rows) (not checked on the device: moe_permute's
+ * tok satisfies it).  src_rows * K <= 2^32, else MOE_ERR_UNSUPPORTED. */
+int moe_grouped_gemm_fp8_gather(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
+                                const int32_t *group_offsets, const uint8_t *A, const float *a_scale,
+                                const uint8_t *B, const float *b_scale, void *C, void *aux,
+                                const int32_t *rows, int64_t src_rows, void *stream);
+
+/* ---------------------------------------------------------------- fp8 layer */
+
+/* e4m3 copies of the expert weights for the fp8 layer calls (Apex-3 code
+ * page, "Run it yourself": the fp8_rowwise precision of the whole model;
+ * KempnerForge README, "MoE roadmap": FP8 mixed precision).  Each copy is
+ * quantised row-wise along the reduction dimension of the product it feeds
+ * (codes as in moe_quantize_fp8), F = num_shared * d_ff_shared:
+ *   forward layout (moe_forward_fp8), along d resp. f:
+ *     gateup_q [E, 2f, d], gateup_s [E, 2f];  down_q [E, d, f], down_s [E, d]
+ *     s_gateup_q [2F, d], s_gateup_s [2F];    s_down_q [d, F], s_down_s [d]
+ *   data-gradient layout (moe_backward_fp8), along 2f resp. d, stored
+ *   transposed as moe_quantize_fp8_transposed writes them:
+ *     gateup_tq [E, d, 2f], gateup_ts [E, d]; down_tq [E, f, d], down_ts [E, f]
+ *     s_gateup_tq [d, 2F], s_gateup_ts [d];   s_down_tq [F, d], s_down_ts [F]
+ * Shared fields are NULL when F = 0.  Caller-owned device buffers. */
+typedef struct moe_fp8_weights {
+  uint8_t *gateup_q;    float *gateup_s;
+  uint8_t *down_q;      float *down_s;
+  uint8_t *gateup_tq;   float *gateup_ts;
+  uint8_t *down_tq;     float *down_ts;
+  uint8_t *s_gateup_q;  float *s_gateup_s;
+  uint8_t *s_down_q;    float *s_down_s;
+  uint8_t *s_gateup_tq; float *s_gateup_ts;
+  uint8_t *s_down_tq;   float *s_down_ts;
+} moe_fp8_weights_t;
+
+/* which layouts moe_fp8_weights_quantize writes (a bit mask) */
+enum { MOE_FP8_FORWARD_LAYOUT = 1, MOE_FP8_BACKWARD_LAYOUT = 2 };
+
+/* Writes the e4m3 copies of the expert weights in w (bf16 layer) into the
+ * buffers of w8: the forward layout (parts & MOE_FP8_FORWARD_LAYOUT), the
+ * data-gradient layout (parts & MOE_FP8_BACKWARD_LAYOUT), or both.  Run once
+ * per weight update; the fp8 layer calls read these copies and never the
+ * bf16 weights' values for their expert products.  Deterministic.
+ * MOE_ERR_UNSUPPORTED for layers moe_forward_fp8 does not take. */
+int moe_fp8_weights_quantize(const moe_desc_t *desc, const moe_weights_t *w,
+                             const moe_fp8_weights_t *w8, int parts, void *stream);
+
+/* moe_forward with the expert products in e4m3 (the fp8_rowwise recipe named
+ * above): the token rows x are quantised row-wise once per token and the
+ * routed gate/up product gathers them through saved->tok (one scale per
+ * token); H = silu(G) * U is stored in bf16 (saved->h) and that bf16 copy is
+ * quantised row-wise for the down product; the shared experts likewise.  The
+ * router (fp32), routing, permutation and combine are those of moe_forward,
+ * and the saved buffers are the same (saved->preact holds the scaled fp8
+ * pre-activations rounded to bf16).  Products accumulate the exact e4m3
+ * products in fp32 and are rounded once to bf16.
+ *   w    the layer's weights: the router (w_router, bias) is read; the expert
+ *        fields may be NULL
+ *   w8   forward-layout copies (moe_fp8_weights_quantize)
+ *   ws  >= moe_workspace_bytes(desc, MOE_WS_FORWARD_FP8)
+ * bf16 layers with d_ff and num_shared * d_ff_shared multiples of 128 and
+ * T * d <= 2^32; else MOE_ERR_UNSUPPORTED.  saved->x_perm, when given, is
+ * filled as in moe_forward (for a backward that reads it). */
+int moe_forward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp8_weights_t *w8,
+                    const void *x, void *y, const moe_saved_t *saved, void *ws, size_t ws_bytes,
+                    void *stream);
+
+/* moe_backward with the expert data gradients in e4m3: the gate-weighted
+ * upstream rows dY~ (bf16) are quantised row-wise for dH = dY~ W_d (with the
+ * SwiGLU derivative fused), dG | dU (bf16) row-wise for dX~ = (dG | dU) W_gu,
+ * against the data-gradient copies of w8; the shared experts likewise (dy
+ * itself for their down product).  Weight gradients stay bf16 products of the
+ * bf16 activations with fp32 accumulation (the row-wise recipe with
+ * high-precision weight gradients); the router backward is that of
+ * moe_backward.  Arguments as moe_backward, plus
+ *   w8   data-gradient-layout copies (moe_fp8_weights_quantize)
+ *   ws  >= moe_workspace_bytes(desc, MOE_WS_BACKWARD_FP8)
+ * w's bf16 expert weights are required (the backward reads no fp8 copy of
+ * them for the weight gradients, but checks them as moe_backward does).
+ * Same layer limits as moe_forward_fp8. */
+int moe_backward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp8_weights_t *w8,
+                     const void *x, const moe_saved_t *saved, const void *dy, void *dx,
+                     const moe_grads_t *grads, const moe_router_terms_t *terms, float *losses,
+                     void *ws, size_t ws_bytes, void *stream);
+
 /* ---------------------------------------------------------------- timing */
 
 /* Stages of moe_forward / moe_backward, for the per-stage timing below. */
@@ -418,6 +511,7 @@ enum {
   MOE_STAGE_ROUTER_WGRAD,
   MOE_STAGE_UNPERMUTE_SUM,
   MOE_STAGE_ROUTER_TERMS,          /* balance losses and z-loss (when requested) */
+  MOE_STAGE_FP8_QUANTIZE,          /* fp8 layer calls: activation quantisation */
   MOE_NUM_STAGES
 };
 

@@ -18,13 +18,14 @@ MOE_F32, MOE_BF16 = 0, 1
 MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GEMM_NT, MOE_GEMM_NN, MOE_GEMM_TN = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
-MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD = 0, 1, 2
+MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD, MOE_WS_FORWARD_FP8, MOE_WS_BACKWARD_FP8 = 0, 1, 2, 3, 4
+MOE_FP8_FORWARD_LAYOUT, MOE_FP8_BACKWARD_LAYOUT = 1, 2
 MOE_SAVED_TRAINING, MOE_SAVED_PERMUTED_COPY = 1, 2
 MOE_ROUTE_BLOCK = 32
 STAGES = ["router", "route", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine",
           "combine_bwd", "down_dgrad", "down_wgrad", "gate_up_wgrad", "gate_up_dgrad", "shared_down_dgrad",
           "shared_down_wgrad", "shared_gate_up_wgrad", "shared_gate_up_dgrad", "router_wgrad",
-          "unpermute_sum", "router_terms"]
+          "unpermute_sum", "router_terms", "fp8_quantize"]
 MOE_NUM_STAGES = len(STAGES)
 
 
@@ -43,6 +44,15 @@ class MoeSaved(ctypes.Structure):
     _fields_ = [("logits", c_vp), ("idx", c_vp), ("gate", c_vp), ("counts", c_vp), ("offsets", c_vp),
                 ("pos", c_vp), ("src", c_vp), ("tok", c_vp), ("x_perm", c_vp), ("preact", c_vp), ("h", c_vp),
                 ("y_perm", c_vp), ("s_preact", c_vp), ("s_h", c_vp)]
+
+
+FP8_WEIGHT_FIELDS = ("gateup_q", "gateup_s", "down_q", "down_s", "gateup_tq", "gateup_ts", "down_tq", "down_ts",
+                     "s_gateup_q", "s_gateup_s", "s_down_q", "s_down_s", "s_gateup_tq", "s_gateup_ts",
+                     "s_down_tq", "s_down_ts")
+
+
+class MoeFp8Weights(ctypes.Structure):
+    _fields_ = [(n, c_vp) for n in FP8_WEIGHT_FIELDS]
 
 
 class MoeRouterTerms(ctypes.Structure):
@@ -76,6 +86,13 @@ SIGNATURES = {
     "moe_forward_no_workspace": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, c_vp, _P(MoeSaved), c_vp]),
     "moe_backward": (c_i32, [_P(MoeDesc), _P(MoeWeights), c_vp, _P(MoeSaved), c_vp, c_vp, _P(MoeGrads),
                              _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
+    "moe_forward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_vp, c_vp, _P(MoeSaved), c_vp,
+                                c_sz, c_vp]),
+    "moe_backward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_vp, _P(MoeSaved), c_vp, c_vp,
+                                 _P(MoeGrads), _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
+    "moe_fp8_weights_quantize": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_i32, c_vp]),
+    "moe_grouped_gemm_fp8_gather": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                            c_vp, c_vp, c_vp, c_i64, c_vp]),
     "moe_bias_update": (c_i32, [_P(MoeDesc), c_vp, ctypes.c_float, c_vp, c_vp]),
     "moe_quantize_fp8": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_quantize_fp8_transposed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),

@@ -67,7 +67,8 @@ def route_hist_elems(desc) -> int:
 
 
 def workspace_bytes(desc, which: str) -> int:
-    w = {"permute": L.MOE_WS_PERMUTE, "forward": L.MOE_WS_FORWARD, "backward": L.MOE_WS_BACKWARD}[which]
+    w = {"permute": L.MOE_WS_PERMUTE, "forward": L.MOE_WS_FORWARD, "backward": L.MOE_WS_BACKWARD,
+         "forward_fp8": L.MOE_WS_FORWARD_FP8, "backward_fp8": L.MOE_WS_BACKWARD_FP8}[which]
     return int(L.load().moe_workspace_bytes(ctypes.byref(desc), w))
 
 
@@ -135,6 +136,15 @@ def moe_forward_no_workspace(desc, weights: dict, x, y, saved: dict, stream=None
                                              _stream(stream)), "moe_forward_no_workspace")
 
 
+def _terms(terms):
+    if terms is None:
+        return None
+    return ctypes.byref(L.MoeRouterTerms(aux_coeff=float(terms.get("aux_coeff", 0.0)),
+                                         seq_aux_coeff=float(terms.get("seq_aux_coeff", 0.0)),
+                                         z_coeff=float(terms.get("z_coeff", 0.0)),
+                                         seq_len=int(terms.get("seq_len", 0))))
+
+
 def moe_backward(desc, weights: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None, terms=None,
                  losses=None):
     """terms: None or dict(aux_coeff=, seq_aux_coeff=, z_coeff=, seq_len=); losses: None or a float32
@@ -142,15 +152,42 @@ def moe_backward(desc, weights: dict, x, saved: dict, dy, dx, grads: dict, ws, s
     w = _weights(weights)
     s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
     g = L.MoeGrads(*(_p(grads.get(n)) for n in GRAD_FIELDS))
-    rt = None
-    if terms is not None:
-        rt = ctypes.byref(L.MoeRouterTerms(aux_coeff=float(terms.get("aux_coeff", 0.0)),
-                                           seq_aux_coeff=float(terms.get("seq_aux_coeff", 0.0)),
-                                           z_coeff=float(terms.get("z_coeff", 0.0)),
-                                           seq_len=int(terms.get("seq_len", 0))))
     _check(L.load().moe_backward(ctypes.byref(desc), ctypes.byref(w), _p(x), ctypes.byref(s), _p(dy), _p(dx),
-                                 ctypes.byref(g), rt, _p(losses), _p(ws), ws.numel() * ws.element_size(),
+                                 ctypes.byref(g), _terms(terms), _p(losses), _p(ws), ws.numel() * ws.element_size(),
                                  _stream(stream)), "moe_backward")
+
+
+def _fp8_weights(w8: dict) -> L.MoeFp8Weights:
+    return L.MoeFp8Weights(*(_p(w8.get(n)) for n in L.FP8_WEIGHT_FIELDS))
+
+
+def moe_fp8_weights_quantize(desc, weights: dict, w8: dict, forward=True, backward=True, stream=None):
+    """Writes the e4m3 copies of the expert weights into the buffers of w8 (alloc_fp8_weights)."""
+    parts = (L.MOE_FP8_FORWARD_LAYOUT if forward else 0) | (L.MOE_FP8_BACKWARD_LAYOUT if backward else 0)
+    w = _weights(weights)
+    q = _fp8_weights(w8)
+    _check(L.load().moe_fp8_weights_quantize(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(q), parts,
+                                             _stream(stream)), "moe_fp8_weights_quantize")
+
+
+def moe_forward_fp8(desc, weights: dict, w8: dict, x, y, saved: dict, ws, stream=None):
+    w = _weights(weights)
+    q = _fp8_weights(w8)
+    s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
+    _check(L.load().moe_forward_fp8(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(q), _p(x), _p(y),
+                                    ctypes.byref(s), _p(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_forward_fp8")
+
+
+def moe_backward_fp8(desc, weights: dict, w8: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None,
+                     terms=None, losses=None):
+    w = _weights(weights)
+    q = _fp8_weights(w8)
+    s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
+    g = L.MoeGrads(*(_p(grads.get(n)) for n in GRAD_FIELDS))
+    _check(L.load().moe_backward_fp8(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(q), _p(x), ctypes.byref(s),
+                                     _p(dy), _p(dx), ctypes.byref(g), _terms(terms), _p(losses), _p(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "moe_backward_fp8")
 
 
 def moe_bias_update(desc, counts, rate, bias, stream=None):
@@ -191,6 +228,14 @@ def moe_grouped_gemm_fp8(epilogue, G, M_total, N, K, group_offsets, A, a_scale, 
     _check(L.load().moe_grouped_gemm_fp8(EPILOGUES[epilogue], G, M_total, N, K, _p(group_offsets), _p(A),
                                          _p(a_scale), _p(B), _p(b_scale), _p(C), _p(aux), _stream(stream)),
            "moe_grouped_gemm_fp8")
+
+
+def moe_grouped_gemm_fp8_gather(epilogue, G, M_total, N, K, group_offsets, A, a_scale, B, b_scale, C, rows,
+                                src_rows, aux=None, stream=None):
+    """fp8 grouped GEMM reading routed row m's codes and scale at rows[m] of A [src_rows, K] / a_scale."""
+    _check(L.load().moe_grouped_gemm_fp8_gather(EPILOGUES[epilogue], G, M_total, N, K, _p(group_offsets), _p(A),
+                                                _p(a_scale), _p(B), _p(b_scale), _p(C), _p(aux), _p(rows),
+                                                src_rows, _stream(stream)), "moe_grouped_gemm_fp8_gather")
 
 
 # ------------------------------------------------------------------ buffers (torch device memory)
@@ -247,6 +292,27 @@ def alloc_grads(desc, device="cuda") -> dict:
                 d_w_down=torch.empty(E, d, f, dtype=dt, device=device),
                 d_s_gateup=torch.empty(2 * F, d, dtype=dt, device=device) if F else None,
                 d_s_down=torch.empty(d, F, dtype=dt, device=device) if F else None)
+
+
+def alloc_fp8_weights(desc, device="cuda", forward=True, backward=True) -> dict:
+    """Buffers for the e4m3 copies of the expert weights (layouts of moe_fp8_weights_t)."""
+    d, E, f = desc.d_model, desc.num_experts, desc.d_ff
+    F = desc.num_shared * desc.d_ff_shared
+    u8, f32 = torch.uint8, torch.float32
+    shapes = {}
+    if forward:
+        shapes.update(gateup_q=((E, 2 * f, d), u8), gateup_s=((E, 2 * f), f32), down_q=((E, d, f), u8),
+                      down_s=((E, d), f32))
+        if F:
+            shapes.update(s_gateup_q=((2 * F, d), u8), s_gateup_s=((2 * F,), f32), s_down_q=((d, F), u8),
+                          s_down_s=((d,), f32))
+    if backward:
+        shapes.update(gateup_tq=((E, d, 2 * f), u8), gateup_ts=((E, d), f32), down_tq=((E, f, d), u8),
+                      down_ts=((E, f), f32))
+        if F:
+            shapes.update(s_gateup_tq=((d, 2 * F), u8), s_gateup_ts=((d,), f32), s_down_tq=((F, d), u8),
+                          s_down_ts=((F,), f32))
+    return {n: torch.empty(sh, dtype=dt, device=device) for n, (sh, dt) in shapes.items()}
 
 
 def alloc_workspace(desc, which: str, device="cuda") -> torch.Tensor:

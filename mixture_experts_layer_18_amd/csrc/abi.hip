@@ -96,13 +96,27 @@ size_t backward_gemm_ws(const moe_desc_t* d) {
 struct FwdWs {
   int32_t* hist;
   int32_t* base;
+  uint8_t* xq;  // fp8: token rows [T, d] and their scales [T]
+  float* xs;
+  uint8_t* hq;  // fp8: hidden rows, routed [A, f] then shared [T, F], and scales
+  float* hs;
 };
-size_t fwd_ws(const moe_desc_t* d, void* ws, FwdWs* out) {
+size_t fwd_ws(const moe_desc_t* d, bool fp8, void* ws, FwdWs* out) {
   Carve c(ws);
   const size_t nb = (size_t)d->num_experts * nblocks(d) * sizeof(int32_t);
-  FwdWs w;
+  FwdWs w{};
   w.hist = (int32_t*)c.take(nb);
   w.base = (int32_t*)c.take(nb);
+  if (fp8) {
+    const size_t T = (size_t)d->num_tokens, A = T * (size_t)d->top_k;
+    const size_t hrows = A > T ? A : T;
+    const size_t hq = A * (size_t)d->d_ff > T * (size_t)shared_width(d) ? A * (size_t)d->d_ff
+                                                                          : T * (size_t)shared_width(d);
+    w.xq = (uint8_t*)c.take(T * (size_t)d->d_model);
+    w.xs = (float*)c.take(T * sizeof(float));
+    w.hq = (uint8_t*)c.take(hq);
+    w.hs = (float*)c.take(hrows * sizeof(float));
+  }
   if (out) *out = w;
   return c.off;
 }
@@ -116,8 +130,10 @@ struct BwdWs {
   void* dx_shared; // [T, d]
   void* gemm;      // split partials
   size_t gemm_bytes;
+  uint8_t* q;      // fp8: the quantised operand of each data gradient in turn
+  float* qs;       // and its row scales
 };
-size_t bwd_ws(const moe_desc_t* d, void* ws, BwdWs* out) {
+size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out) {
   Carve c(ws);
   const int64_t T = d->num_tokens, D = d->d_model, f = d->d_ff, A = T * d->top_k;
   const int64_t F = shared_width(d);
@@ -131,6 +147,16 @@ size_t bwd_ws(const moe_desc_t* d, void* ws, BwdWs* out) {
   w.dx_shared = F > 0 ? c.take((size_t)T * D * es) : nullptr;
   w.gemm_bytes = backward_gemm_ws(d);
   w.gemm = c.take(w.gemm_bytes);
+  w.q = nullptr;
+  w.qs = nullptr;
+  if (fp8) {
+    // dY~ [A, d], dG|dU [A, 2f], dy [T, d], shared dG|dU [T, 2F]
+    const size_t szs[] = {(size_t)A * D, (size_t)A * 2 * f, (size_t)T * D, (size_t)T * 2 * F};
+    size_t qb = 0;
+    for (size_t z : szs) qb = z > qb ? z : qb;
+    w.q = (uint8_t*)c.take(qb);
+    w.qs = (float*)c.take((size_t)(A > T ? A : T) * sizeof(float));
+  }
   if (out) *out = w;
   return c.off;
 }
@@ -261,8 +287,10 @@ size_t moe_workspace_bytes(const moe_desc_t* d, int which) {
   if (check_desc(d) != MOE_OK) return 0;
   switch (which) {
     case MOE_WS_PERMUTE: return align_up((size_t)d->num_experts * nblocks(d) * sizeof(int32_t));
-    case MOE_WS_FORWARD: return fwd_ws(d, nullptr, nullptr);
-    case MOE_WS_BACKWARD: return bwd_ws(d, nullptr, nullptr);
+    case MOE_WS_FORWARD: return fwd_ws(d, false, nullptr, nullptr);
+    case MOE_WS_BACKWARD: return bwd_ws(d, false, nullptr, nullptr);
+    case MOE_WS_FORWARD_FP8: return fwd_ws(d, true, nullptr, nullptr);
+    case MOE_WS_BACKWARD_FP8: return bwd_ws(d, true, nullptr, nullptr);
     default: return 0;
   }
 }
@@ -434,21 +462,48 @@ static int gather_supported(const moe_desc_t* d, bool training) {
   return MOE_OK;
 }
 
-// The forward pass of moe_forward on the workspace ws (ws_bytes of it).
-static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
-                        const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
+// The fp8 layer calls: bf16 layers whose SwiGLU products pair 128 gate with
+// 128 up columns per tile, and whose token rows (gathered as fp8 codes) have
+// 32-bit byte offsets.
+static int fp8_layer_supported(const moe_desc_t* d) {
+  if (d->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+  if (d->d_ff % 128 || shared_width(d) % 128) return MOE_ERR_UNSUPPORTED;
+  if (d->num_tokens * d->d_model > (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The forward pass of moe_forward (w8 NULL) or moe_forward_fp8 on the
+// workspace ws (ws_bytes of it).
+static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
+                        const void* x, void* y, const moe_saved_t* sv, void* ws, size_t ws_bytes,
+                        void* stream) {
   int s = check_desc(d);
   if (s) return s;
   if (!w || !sv) return MOE_ERR_INVALID;
   const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
   const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
   const int dt = d->dtype;
-  if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
-  if (F > 0 && (!w->s_gateup || !w->s_down)) return MOE_ERR_INVALID;
+  const bool fp8 = w8 != nullptr;
+  if (!w->w_router) return MOE_ERR_INVALID;
+  if (fp8) {
+    s = fp8_layer_supported(d);
+    if (s) return s;
+    if (!w8->gateup_q || !w8->gateup_s || !w8->down_q || !w8->down_s) return MOE_ERR_INVALID;
+    if (F > 0 && (!w8->s_gateup_q || !w8->s_gateup_s || !w8->s_down_q || !w8->s_down_s))
+      return MOE_ERR_INVALID;
+    const void* p8[] = {w8->gateup_q, w8->gateup_s, w8->down_q, w8->down_s, w8->s_gateup_q,
+                        w8->s_gateup_s, w8->s_down_q, w8->s_down_s};
+    for (const void* p : p8)
+      if (!aligned16(p)) return MOE_ERR_ALIGN;
+  } else {
+    if (!w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
+    if (F > 0 && (!w->s_gateup || !w->s_down)) return MOE_ERR_INVALID;
+  }
   if (!sv->counts || !sv->offsets) return MOE_ERR_INVALID;
   // no permuted copy of the tokens: the gate/up products gather them (with
-  // no tokens there is nothing to gather)
-  const bool gather = T > 0 && !sv->x_perm;
+  // no tokens there is nothing to gather); the fp8 products always gather
+  // the quantised token rows
+  const bool gather = T > 0 && (fp8 || !sv->x_perm);
   if (T > 0 && (!x || !y || !sv->logits || !sv->idx || !sv->gate || !sv->pos || !sv->src ||
                 (gather && !sv->tok) || !sv->h || !sv->y_perm || !ws || (F > 0 && !sv->s_h)))
     return MOE_ERR_INVALID;
@@ -458,11 +513,11 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
                         sv->s_preact, sv->s_h, ws};
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
-  if (gather) {
+  if (gather && !fp8) {
     s = gather_supported(d, sv->preact != nullptr);
     if (s) return s;
   }
-  if (ws_bytes < moe_workspace_bytes(d, MOE_WS_FORWARD)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe_workspace_bytes(d, fp8 ? MOE_WS_FORWARD_FP8 : MOE_WS_FORWARD)) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   if (T == 0) {
     MOE_TRY(launch_fill_i32(sv->counts, E, 0, st));
@@ -470,7 +525,7 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
     return MOE_OK;
   }
   FwdWs fw;
-  fwd_ws(d, ws, &fw);
+  fwd_ws(d, fp8, ws, &fw);
   // 1. router logits in fp32, 2. scores, top-k, gates, per-block histogram
   // (one kernel when a workgroup holds all E logits of its tokens)
   const float* rbias = d->score == MOE_SIGMOID ? w->bias : nullptr;
@@ -485,24 +540,44 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
   // 3. permutation into expert-contiguous rows
   MOE_STAGE(MOE_STAGE_PERMUTE, launch_permute(x, dt, sv->idx, fw.hist, (int)T, (int)D, (int)E, (int)k, fw.base,
                          sv->counts, sv->offsets, sv->pos, sv->src, sv->tok, sv->x_perm, st));
-  // 4. gate/up grouped GEMM with the SwiGLU activation (rows of x_perm, or of
-  // x gathered through tok)
-  GemmProblem gu = gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D, sv->offsets,
-                      gather ? x : sv->x_perm, w->w_gateup, sv->h, sv->preact);
-  gu.rows = gather ? sv->tok : nullptr;
-  MOE_STAGE(MOE_STAGE_GATE_UP, launch_grouped_gemm(gu, nullptr, 0, st));
-  // 5. down grouped GEMM
-  MOE_STAGE(MOE_STAGE_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
-                                 sv->h, w->w_down, sv->y_perm, nullptr),
-                              nullptr, 0, st));
-  // 6. shared experts on every token; their output lands in y
-  if (F > 0) {
-    MOE_STAGE(MOE_STAGE_SHARED_GATE_UP, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, 1, T, 2 * F, D,
-                                   nullptr, x, w->s_gateup, sv->s_h, sv->s_preact),
+  if (fp8) {
+    // 4. token rows in e4m3 (one scale per token), gate/up product on the
+    // routed rows gathered through tok, SwiGLU; 5. hidden rows in e4m3, down
+    // product; 6. the same for the shared experts (no gather)
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(x, dt, T, (int)D, fw.xq, fw.xs, st));
+    MOE_STAGE(MOE_STAGE_GATE_UP, launch_gemm_fp8(MOE_EPI_SWIGLU, E, A, 2 * f, D, sv->offsets, fw.xq, fw.xs,
+                                                 w8->gateup_q, w8->gateup_s, sv->h, sv->preact, sv->tok, st));
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(sv->h, dt, A, (int)f, fw.hq, fw.hs, st));
+    MOE_STAGE(MOE_STAGE_DOWN, launch_gemm_fp8(MOE_EPI_NONE, E, A, D, f, sv->offsets, fw.hq, fw.hs, w8->down_q,
+                                              w8->down_s, sv->y_perm, nullptr, nullptr, st));
+    if (F > 0) {
+      MOE_STAGE(MOE_STAGE_SHARED_GATE_UP,
+                launch_gemm_fp8(MOE_EPI_SWIGLU, 1, T, 2 * F, D, nullptr, fw.xq, fw.xs, w8->s_gateup_q,
+                                w8->s_gateup_s, sv->s_h, sv->s_preact, nullptr, st));
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(sv->s_h, dt, T, (int)F, fw.hq, fw.hs, st));
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN, launch_gemm_fp8(MOE_EPI_NONE, 1, T, D, F, nullptr, fw.hq, fw.hs,
+                                                       w8->s_down_q, w8->s_down_s, y, nullptr, nullptr, st));
+    }
+  } else {
+    // 4. gate/up grouped GEMM with the SwiGLU activation (rows of x_perm, or of
+    // x gathered through tok)
+    GemmProblem gu = gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, E, A, 2 * f, D, sv->offsets,
+                        gather ? x : sv->x_perm, w->w_gateup, sv->h, sv->preact);
+    gu.rows = gather ? sv->tok : nullptr;
+    MOE_STAGE(MOE_STAGE_GATE_UP, launch_grouped_gemm(gu, nullptr, 0, st));
+    // 5. down grouped GEMM
+    MOE_STAGE(MOE_STAGE_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
+                                   sv->h, w->w_down, sv->y_perm, nullptr),
                                 nullptr, 0, st));
-    MOE_STAGE(MOE_STAGE_SHARED_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
-                                   nullptr, sv->s_h, w->s_down, y, nullptr),
-                                nullptr, 0, st));
+    // 6. shared experts on every token; their output lands in y
+    if (F > 0) {
+      MOE_STAGE(MOE_STAGE_SHARED_GATE_UP, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_SWIGLU, dt, dt, dt, 1, T, 2 * F, D,
+                                     nullptr, x, w->s_gateup, sv->s_h, sv->s_preact),
+                                  nullptr, 0, st));
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN, launch_grouped_gemm(gp(MOE_GEMM_NT, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
+                                     nullptr, sv->s_h, w->s_down, y, nullptr),
+                                  nullptr, 0, st));
+    }
   }
   // 7. weighted combine (+ shared output)
   MOE_STAGE(MOE_STAGE_COMBINE, launch_combine(dt, sv->y_perm, sv->gate, sv->pos, F > 0 ? y : nullptr, y, (int)T,
@@ -512,25 +587,33 @@ static int forward_impl(const moe_desc_t* d, const moe_weights_t* w, const void*
 
 int moe_forward(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
                 const moe_saved_t* sv, void* ws, size_t ws_bytes, void* stream) {
-  return forward_impl(d, w, x, y, sv, ws, ws_bytes, stream);
+  return forward_impl(d, w, nullptr, x, y, sv, ws, ws_bytes, stream);
+}
+
+int moe_forward_fp8(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
+                    const void* x, void* y, const moe_saved_t* sv, void* ws, size_t ws_bytes,
+                    void* stream) {
+  if (!w8) return MOE_ERR_INVALID;
+  return forward_impl(d, w, w8, x, y, sv, ws, ws_bytes, stream);
 }
 
 int moe_forward_no_workspace(const moe_desc_t* d, const moe_weights_t* w, const void* x, void* y,
                              const moe_saved_t* sv, void* stream) {
   const int s = check_desc(d);
   if (s) return s;
-  const size_t need = fwd_ws(d, nullptr, nullptr);
+  const size_t need = fwd_ws(d, false, nullptr, nullptr);
   if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
   void* ws = nullptr;
   const int r = scratch_device_ptr(&ws);
   if (r) return r;
-  return forward_impl(d, w, x, y, sv, ws, MOE_STATIC_SCRATCH_BYTES, stream);
+  return forward_impl(d, w, nullptr, x, y, sv, ws, MOE_STATIC_SCRATCH_BYTES, stream);
 }
 
-int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
-                 const moe_saved_t* sv, const void* dy, void* dx, const moe_grads_t* g,
-                 const moe_router_terms_t* terms, float* losses, void* ws, size_t ws_bytes,
-                 void* stream) {
+// The backward pass of moe_backward (w8 NULL) or moe_backward_fp8.
+static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
+                         const void* x, const moe_saved_t* sv, const void* dy, void* dx,
+                         const moe_grads_t* g, const moe_router_terms_t* terms, float* losses,
+                         void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(d);
   if (s) return s;
   if (losses && !terms) return MOE_ERR_INVALID;
@@ -546,10 +629,22 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   const int64_t T = d->num_tokens, D = d->d_model, E = d->num_experts, k = d->top_k;
   const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
   const int dt = d->dtype;
+  const bool fp8 = w8 != nullptr;
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
   if (!g->d_w_router || !g->d_w_gateup || !g->d_w_down) return MOE_ERR_INVALID;
   if (F > 0 && (!w->s_gateup || !w->s_down || !g->d_s_gateup || !g->d_s_down))
     return MOE_ERR_INVALID;
+  if (fp8) {
+    s = fp8_layer_supported(d);
+    if (s) return s;
+    if (!w8->gateup_tq || !w8->gateup_ts || !w8->down_tq || !w8->down_ts) return MOE_ERR_INVALID;
+    if (F > 0 && (!w8->s_gateup_tq || !w8->s_gateup_ts || !w8->s_down_tq || !w8->s_down_ts))
+      return MOE_ERR_INVALID;
+    const void* p8[] = {w8->gateup_tq, w8->gateup_ts, w8->down_tq, w8->down_ts, w8->s_gateup_tq,
+                        w8->s_gateup_ts, w8->s_down_tq, w8->s_down_ts};
+    for (const void* p : p8)
+      if (!aligned16(p)) return MOE_ERR_ALIGN;
+  }
   if (F > 0 && T > 0 && (!sv->s_h || !sv->s_preact)) return MOE_ERR_INVALID;
   if (!sv->offsets) return MOE_ERR_INVALID;
   const bool gather = T > 0 && !sv->x_perm;
@@ -566,10 +661,10 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
     s = gather_supported(d, true);
     if (s) return s;
   }
-  if (ws_bytes < moe_workspace_bytes(d, MOE_WS_BACKWARD)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe_workspace_bytes(d, fp8 ? MOE_WS_BACKWARD_FP8 : MOE_WS_BACKWARD)) return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   BwdWs bw;
-  bwd_ws(d, ws, &bw);
+  bwd_ws(d, fp8, ws, &bw);
   // 1. combine backward + router backward (dlogits)
   MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
                              d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
@@ -586,10 +681,17 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
                                   terms->aux_coeff, terms->seq_aux_coeff, terms->z_coeff,
                                   terms->seq_len, bw.dlogits, losses, bw.terms, st));
   }
-  // 2. down data gradient fused with the SwiGLU derivative -> dG | dU
-  MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
-                                 sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
-                              nullptr, 0, st));
+  // 2. down data gradient fused with the SwiGLU derivative -> dG | dU (fp8:
+  // dY~ in e4m3 per row against W_d quantised along d, stored transposed)
+  if (fp8) {
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dy_perm, dt, A, (int)D, bw.q, bw.qs, st));
+    MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_gemm_fp8(MOE_EPI_DSWIGLU, E, A, f, D, sv->offsets, bw.q, bw.qs,
+                                                    w8->down_tq, w8->down_ts, bw.dgu, sv->preact, nullptr, st));
+  } else {
+    MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
+                                   sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
+                                nullptr, 0, st));
+  }
   // 3. down weight gradient
   MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
                                  bw.dy_perm, sv->h, g->d_w_down, nullptr),
@@ -599,25 +701,46 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
                        gather ? x : sv->x_perm, g->d_w_gateup, nullptr);
   guw.rows = gather ? sv->tok : nullptr;
   MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(guw, bw.gemm, bw.gemm_bytes, st));
-  // 5. gate/up data gradient (written over dy_perm, which is no longer needed)
+  // 5. gate/up data gradient (written over dy_perm, which is no longer needed;
+  // fp8: dG | dU in e4m3 per row against W_gu quantised along 2f, transposed)
   void* dx_perm = bw.dy_perm;
-  MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
-                                 sv->offsets, bw.dgu, w->w_gateup, dx_perm, nullptr),
-                              nullptr, 0, st));
+  if (fp8) {
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dgu, dt, A, (int)(2 * f), bw.q, bw.qs, st));
+    MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_gemm_fp8(MOE_EPI_NONE, E, A, D, 2 * f, sv->offsets, bw.q, bw.qs,
+                                                       w8->gateup_tq, w8->gateup_ts, dx_perm, nullptr, nullptr, st));
+  } else {
+    MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
+                                   sv->offsets, bw.dgu, w->w_gateup, dx_perm, nullptr),
+                                nullptr, 0, st));
+  }
   // 6. shared experts
   if (F > 0) {
-    MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
-                                   nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
-                                nullptr, 0, st));
+    if (fp8) {
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q, bw.qs, st));
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD,
+                launch_gemm_fp8(MOE_EPI_DSWIGLU, 1, T, F, D, nullptr, bw.q, bw.qs, w8->s_down_tq, w8->s_down_ts,
+                                bw.s_dgu, sv->s_preact, nullptr, st));
+    } else {
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
+                                     nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
+                                  nullptr, 0, st));
+    }
     MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
                                    nullptr, dy, sv->s_h, g->d_s_down, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
     MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
                                    nullptr, bw.s_dgu, x, g->d_s_gateup, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
-    MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
-                                   nullptr, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
-                                nullptr, 0, st));
+    if (fp8) {
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.s_dgu, dt, T, (int)(2 * F), bw.q, bw.qs, st));
+      MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD,
+                launch_gemm_fp8(MOE_EPI_NONE, 1, T, D, 2 * F, nullptr, bw.q, bw.qs, w8->s_gateup_tq,
+                                w8->s_gateup_ts, bw.dx_shared, nullptr, nullptr, st));
+    } else {
+      MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
+                                     nullptr, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
+                                  nullptr, 0, st));
+    }
   }
   // 7. router weight gradient (fp32)
   MOE_STAGE(MOE_STAGE_ROUTER_WGRAD, launch_router_wgrad(bw.dlogits, x, dt, (int)T, (int)D, (int)E, (float*)bw.gemm,
@@ -630,6 +753,64 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
   MOE_STAGE(MOE_STAGE_UNPERMUTE_SUM, launch_unpermute_sum(dt, dx_perm, sv->pos, F > 0 ? bw.dx_shared : nullptr, bw.dlogits,
                                sv->idx, w->w_router, dense_router, (int)T, (int)D, (int)E, (int)k,
                                dx, st));
+  return MOE_OK;
+}
+
+int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
+                 const moe_saved_t* sv, const void* dy, void* dx, const moe_grads_t* g,
+                 const moe_router_terms_t* terms, float* losses, void* ws, size_t ws_bytes,
+                 void* stream) {
+  return backward_impl(d, w, nullptr, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
+}
+
+int moe_backward_fp8(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
+                     const void* x, const moe_saved_t* sv, const void* dy, void* dx,
+                     const moe_grads_t* g, const moe_router_terms_t* terms, float* losses, void* ws,
+                     size_t ws_bytes, void* stream) {
+  if (!w8) return MOE_ERR_INVALID;
+  return backward_impl(d, w, w8, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
+}
+
+int moe_fp8_weights_quantize(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
+                             int parts, void* stream) {
+  int s = check_desc(d);
+  if (s) return s;
+  if (!w || !w8 || parts < 1 || parts > 3) return MOE_ERR_INVALID;
+  s = fp8_layer_supported(d);
+  if (s) return s;
+  const int64_t D = d->d_model, E = d->num_experts, f = d->d_ff, F = shared_width(d);
+  const int dt = d->dtype;
+  const bool fwd = parts & MOE_FP8_FORWARD_LAYOUT, bwd = parts & MOE_FP8_BACKWARD_LAYOUT;
+  if (!w->w_gateup || !w->w_down || (F > 0 && (!w->s_gateup || !w->s_down))) return MOE_ERR_INVALID;
+  if (fwd && (!w8->gateup_q || !w8->gateup_s || !w8->down_q || !w8->down_s ||
+              (F > 0 && (!w8->s_gateup_q || !w8->s_gateup_s || !w8->s_down_q || !w8->s_down_s))))
+    return MOE_ERR_INVALID;
+  if (bwd && (!w8->gateup_tq || !w8->gateup_ts || !w8->down_tq || !w8->down_ts ||
+              (F > 0 && (!w8->s_gateup_tq || !w8->s_gateup_ts || !w8->s_down_tq || !w8->s_down_ts))))
+    return MOE_ERR_INVALID;
+  const void* ptrs[] = {w->w_gateup, w->w_down, w->s_gateup, w->s_down, w8->gateup_q, w8->gateup_s,
+                        w8->down_q, w8->down_s, w8->gateup_tq, w8->gateup_ts, w8->down_tq, w8->down_ts,
+                        w8->s_gateup_q, w8->s_gateup_s, w8->s_down_q, w8->s_down_s, w8->s_gateup_tq,
+                        w8->s_gateup_ts, w8->s_down_tq, w8->s_down_ts};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  hipStream_t st = (hipStream_t)stream;
+  if (fwd) {
+    MOE_TRY(launch_quantize_fp8(w->w_gateup, dt, E * 2 * f, (int)D, w8->gateup_q, w8->gateup_s, st));
+    MOE_TRY(launch_quantize_fp8(w->w_down, dt, E * D, (int)f, w8->down_q, w8->down_s, st));
+    if (F > 0) {
+      MOE_TRY(launch_quantize_fp8(w->s_gateup, dt, 2 * F, (int)D, w8->s_gateup_q, w8->s_gateup_s, st));
+      MOE_TRY(launch_quantize_fp8(w->s_down, dt, D, (int)F, w8->s_down_q, w8->s_down_s, st));
+    }
+  }
+  if (bwd) {
+    MOE_TRY(launch_quantize_fp8_transposed(w->w_gateup, dt, E, 2 * f, D, w8->gateup_tq, w8->gateup_ts, st));
+    MOE_TRY(launch_quantize_fp8_transposed(w->w_down, dt, E, D, f, w8->down_tq, w8->down_ts, st));
+    if (F > 0) {
+      MOE_TRY(launch_quantize_fp8_transposed(w->s_gateup, dt, 1, 2 * F, D, w8->s_gateup_tq, w8->s_gateup_ts, st));
+      MOE_TRY(launch_quantize_fp8_transposed(w->s_down, dt, 1, D, F, w8->s_down_tq, w8->s_down_ts, st));
+    }
+  }
   return MOE_OK;
 }
 
@@ -687,7 +868,30 @@ int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
   for (const void* p : ptrs)
     if (!aligned16(p)) return MOE_ERR_ALIGN;
   if (M == 0) return MOE_OK;
-  MOE_TRY(launch_gemm_fp8(epi, G, M, N, K, offsets, A, a_scale, B, b_scale, C, aux, (hipStream_t)stream));
+  MOE_TRY(launch_gemm_fp8(epi, G, M, N, K, offsets, A, a_scale, B, b_scale, C, aux, nullptr,
+                          (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_fp8_gather(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
+                                const int32_t* offsets, const uint8_t* A, const float* a_scale,
+                                const uint8_t* B, const float* b_scale, void* C, void* aux,
+                                const int32_t* rows, int64_t src_rows, void* stream) {
+  if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU) return MOE_ERR_INVALID;
+  if (G < 1 || G > 256 || M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64 || src_rows < 0)
+    return MOE_ERR_INVALID;
+  if (epi == MOE_EPI_SWIGLU && (N / 2) % 128) return MOE_ERR_INVALID;
+  if (M >= (int64_t(1) << 31) || N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  // row byte offsets of the gathered codes are 32-bit in the kernel
+  if (src_rows * K > (int64_t(1) << 32)) return MOE_ERR_UNSUPPORTED;
+  if (!offsets && G != 1) return MOE_ERR_INVALID;
+  if (M > 0 && (!A || !a_scale || !B || !b_scale || !C || !rows)) return MOE_ERR_INVALID;
+  const void* ptrs[] = {offsets, A, a_scale, B, b_scale, C, aux, rows};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  if (M == 0) return MOE_OK;
+  MOE_TRY(launch_gemm_fp8(epi, G, M, N, K, offsets, A, a_scale, B, b_scale, C, aux, rows,
+                          (hipStream_t)stream));
   return MOE_OK;
 }
 

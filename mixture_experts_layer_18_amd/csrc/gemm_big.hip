@@ -133,7 +133,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
   constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
   static_assert(!F8 || LAYOUT == MOE_GEMM_NT, "fp8 operands: forward layout only");
-  static_assert(!GA || (!F8 && LAYOUT != MOE_GEMM_NN), "gathered rows: bf16 NT or TN");
+  static_assert(!GA || LAYOUT != MOE_GEMM_NN, "gathered rows: NT or TN");
+  static_assert(!GA || EPI != MOE_EPI_DSWIGLU, "gathered rows: no dSwiGLU epilogue");
   constexpr bool GN = GA && LAYOUT == MOE_GEMM_NT;  // A rows gathered, fixed per tile
   constexpr bool GT = GA && LAYOUT == MOE_GEMM_TN;  // B k-rows gathered through the ring
   constexpr int LV = LT + (GT ? 1 : 0);             // vector-memory instructions per k-step
@@ -707,7 +708,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
       if (i >= t.i_hi) continue;
-      const float sa = F8 ? a.a_scale[i] : 1.0f;
+      // fp8: the scale of the row's source (GN: a token row, per token)
+      const float sa = F8 ? a.a_scale[GN ? a.rows[i] : i] : 1.0f;
       if (EPI == MOE_EPI_SWIGLU) {
         // block jt holds gate columns for even jt, up columns for odd jt
         if (X) {
@@ -866,10 +868,13 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
 }  // namespace moe
 
 namespace moe {
-// fp8 forward products: C (bf16) = a_scale[m] b_scale[g,n] sum_k A[m,k] B[g,n,k]
+// fp8 forward products: C (bf16) = a_scale[m] b_scale[g,n] sum_k A[m,k] B[g,n,k];
+// with rows, A's row m and its scale are read at rows[m] (plain and SwiGLU
+// epilogues)
 hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,
-                           const uint8_t* B, const float* b_scale, void* C, void* aux, hipStream_t st) {
+                           const uint8_t* B, const float* b_scale, void* C, void* aux,
+                           const int32_t* rows, hipStream_t st) {
   pk::Args a;
   a.G = (int)G;
   a.M_total = M_total;
@@ -882,7 +887,12 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
   a.aux = (bf16_t*)aux;
   a.a_scale = a_scale;
   a.b_scale = b_scale;
-  a.rows = nullptr;
+  a.rows = rows;
+  if (rows) {
+    if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true, true>(a, st);
+    if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true, true>(a, st);
+    return hipErrorInvalidValue;
+  }
   if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true>(a, st);
   if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true>(a, st);
   if (epilogue == MOE_EPI_DSWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_DSWIGLU, true>(a, st);

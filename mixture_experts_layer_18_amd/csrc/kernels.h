@@ -38,7 +38,8 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st);
 // fp8 (e4m3) forward products with row scales, persistent kernel
 hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,
-                           const uint8_t* B, const float* b_scale, void* C, void* aux, hipStream_t st);
+                           const uint8_t* B, const float* b_scale, void* C, void* aux,
+                           const int32_t* rows, hipStream_t st);
 hipError_t launch_quantize_fp8_transposed(const void* x, int dtype, int64_t G, int64_t R, int64_t C,
                                           uint8_t* q, float* scale, hipStream_t st);
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,

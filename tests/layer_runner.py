@@ -29,23 +29,36 @@ def upload_layer(cfg, inp):
     return w
 
 
-def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False, terms=None, gather=False):
-    """gather: no permuted token copy; the gate/up products read x through the token map."""
+def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False, terms=None, gather=False,
+            fp8=False):
+    """gather: no permuted token copy; the gate/up products read x through the token map.
+    fp8: the fp8 layer calls (moe_forward_fp8 / moe_backward_fp8) on e4m3 copies of the
+    expert weights written by moe_fp8_weights_quantize."""
     desc = M.desc_from_config(cfg)
     w = upload_layer(cfg, inp) if weights is None else weights
     x = dev(inp["x"]) if x is None else x
     saved = M.alloc_saved(desc, training=backward, gather=gather)
     y = torch.empty_like(x)
-    ws = M.alloc_workspace(desc, "forward")
-    M.moe_forward(desc, w, x, y, saved, ws)
-    out = dict(y=y, saved=saved)
+    w8 = None
+    if fp8:
+        w8 = M.alloc_fp8_weights(desc, backward=backward)
+        M.moe_fp8_weights_quantize(desc, w, w8, forward=True, backward=backward)
+        M.moe_forward_fp8(desc, w, w8, x, y, saved, M.alloc_workspace(desc, "forward_fp8"))
+    else:
+        ws = M.alloc_workspace(desc, "forward")
+        M.moe_forward(desc, w, x, y, saved, ws)
+    out = dict(y=y, saved=saved, w8=w8)
     if backward:
         dy = dev(inp["dy"]) if dy is None else dy
         grads = M.alloc_grads(desc)
         dx = torch.empty_like(x)
-        wsb = M.alloc_workspace(desc, "backward")
         losses = torch.zeros(4, dtype=torch.float32, device="cuda") if terms is not None else None
-        M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, terms=terms, losses=losses)
+        if fp8:
+            M.moe_backward_fp8(desc, w, w8, x, saved, dy, dx, grads, M.alloc_workspace(desc, "backward_fp8"),
+                               terms=terms, losses=losses)
+        else:
+            wsb = M.alloc_workspace(desc, "backward")
+            M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, terms=terms, losses=losses)
         out.update(dx=dx, grads=grads, losses=losses)
     torch.cuda.synchronize()
     if keep_device:
@@ -83,6 +96,16 @@ def oracle_run(cfg, oi, backward, tokens=None, terms=None):
         bw = O.backward(x, oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fw, dy,
                         score=cfg.score, renorm=cfg.renorm, terms=terms)
     return fw, bw
+
+
+def oracle_routing(cfg, oi):
+    """The oracle's router on every token (logits, keys, its own top-k and
+    margins), without the experts: enough for check_routing."""
+    logits = O.router_logits(oi["x"], oi["w_router"])
+    scores = O.router_scores(logits, cfg.score)
+    keys = O.selection_keys(logits, scores, oi["bias"], cfg.score)
+    idx, margin = O.select_topk(keys, cfg.k)
+    return dict(logits=logits, scores=scores, keys=keys, idx=idx, margin=margin)
 
 
 def check_routing(cfg, g_logits, g_idx, fw, tokens=None):

@@ -21,7 +21,7 @@ def test_exports_every_declared_function(lib):
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(L.SIGNATURES)
-    assert lib.moe_abi_version() == 3
+    assert lib.moe_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -35,6 +35,10 @@ def test_struct_layout_matches_header():
     assert ctypes.sizeof(L.MoeWeights) == 6 * 8
     assert ctypes.sizeof(L.MoeSaved) == 14 * 8
     assert ctypes.sizeof(L.MoeGrads) == 5 * 8
+    assert ctypes.sizeof(L.MoeFp8Weights) == 16 * 8
+    text = open(L.HEADER).read()
+    body = re.search(r"typedef struct moe_fp8_weights \{(.*?)\} moe_fp8_weights_t;", text, re.S).group(1)
+    assert tuple(re.findall(r"\*(\w+);", body)) == L.FP8_WEIGHT_FIELDS
 
 
 def test_queries(lib):
@@ -332,3 +336,80 @@ def test_saved_layout_in_one_allocation(lib):
         L.MOE_ERR_ALIGN
     assert lib.moe_saved_carve(ctypes.byref(d), 8, ctypes.c_void_p(base), 1 << 30, ctypes.byref(s)) == \
         L.MOE_ERR_INVALID
+
+
+def test_fp8_layer_workspace_sizes(lib):
+    """The fp8 layer calls add their quantised operands to the bf16 calls'
+    workspaces: the forward the token codes [T, d] with one scale per token and
+    the larger of the routed [A, f] and shared [T, F] hidden codes with their
+    scales; the backward the largest data-gradient operand (here dG | dU,
+    [A, 2f]) with one scale per row."""
+    T, dm, E, k, f, F = 16384, 2048, 64, 6, 1408, 2 * 1408
+    d = make_desc(T, dm, E, k, f, 2, 1408, "sigmoid", True, "bf16")
+    A = T * k
+    fw = lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_FORWARD)
+    bw = lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_BACKWARD)
+    fw8 = lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_FORWARD_FP8)
+    bw8 = lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_BACKWARD_FP8)
+    assert fw8 - fw >= T * dm + T * 4 + A * f + A * 4
+    assert fw8 - fw < T * dm + T * 4 + A * f + A * 4 + 4 * 256
+    assert bw8 - bw >= A * 2 * f + A * 4
+    assert bw8 - bw < A * 2 * f + A * 4 + 2 * 256
+    assert A * f > T * F
+
+
+def test_fp8_layer_argument_checks(lib):
+    """Host-side rejection for the fp8 layer calls: layers they do not take
+    (fp32, a hidden width not a multiple of 128), a missing or misaligned fp8
+    weight, a short workspace; and for the weight quantiser and the gathered
+    fp8 GEMM.  No check reaches the GPU."""
+    a = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10004)
+    d = make_desc(64, 256, 8, 2, 256, 1, 128, "sigmoid", True, "bf16")
+    w = L.MoeWeights(a, a, a, a, a, a)
+    s = L.MoeSaved(*([a] * 14))
+    q = L.MoeFp8Weights(*([a] * 16))
+    fwd = lambda dd, qq, nb: lib.moe_forward_fp8(ctypes.byref(dd), ctypes.byref(w), qq, a, a,  # noqa: E731
+                                                 ctypes.byref(s), a, nb, None)
+    assert fwd(d, ctypes.byref(q), 16) == L.MOE_ERR_WORKSPACE
+    assert fwd(d, None, 1 << 30) == L.MOE_ERR_INVALID
+    f32 = make_desc(64, 256, 8, 2, 256, 1, 128, "sigmoid", True, "f32")
+    assert fwd(f32, ctypes.byref(q), 1 << 30) == L.MOE_ERR_UNSUPPORTED
+    odd = make_desc(64, 256, 8, 2, 192, 0, 0, "sigmoid", True, "bf16")
+    assert fwd(odd, ctypes.byref(q), 1 << 30) == L.MOE_ERR_UNSUPPORTED
+    odd_shared = make_desc(64, 256, 8, 2, 256, 1, 64, "sigmoid", True, "bf16")
+    assert fwd(odd_shared, ctypes.byref(q), 1 << 30) == L.MOE_ERR_UNSUPPORTED
+    q2 = L.MoeFp8Weights(*([a] * 16))
+    q2.down_s = None
+    assert fwd(d, ctypes.byref(q2), 1 << 30) == L.MOE_ERR_INVALID
+    q2.down_s = mis
+    assert fwd(d, ctypes.byref(q2), 1 << 30) == L.MOE_ERR_ALIGN
+    # the backward reads the data-gradient copies only
+    g = L.MoeGrads(a, a, a, a, a)
+    bwd = lambda qq, nb: lib.moe_backward_fp8(ctypes.byref(d), ctypes.byref(w), qq, a, ctypes.byref(s), a, a,  # noqa: E731
+                                              ctypes.byref(g), None, None, a, nb, None)
+    assert bwd(ctypes.byref(q), 16) == L.MOE_ERR_WORKSPACE
+    assert bwd(None, 1 << 30) == L.MOE_ERR_INVALID
+    q3 = L.MoeFp8Weights(*([a] * 16))
+    q3.s_down_tq = None
+    assert bwd(ctypes.byref(q3), 1 << 30) == L.MOE_ERR_INVALID
+    q3.s_down_tq = a
+    q3.gateup_q = None                       # forward copy: not read by the backward
+    assert bwd(ctypes.byref(q3), 16) == L.MOE_ERR_WORKSPACE
+    # the weight quantiser
+    assert lib.moe_fp8_weights_quantize(ctypes.byref(d), ctypes.byref(w), ctypes.byref(q), 0, None) == \
+        L.MOE_ERR_INVALID
+    assert lib.moe_fp8_weights_quantize(ctypes.byref(d), ctypes.byref(w), ctypes.byref(q), 4, None) == \
+        L.MOE_ERR_INVALID
+    assert lib.moe_fp8_weights_quantize(ctypes.byref(d), ctypes.byref(w), ctypes.byref(q3), 1, None) == \
+        L.MOE_ERR_INVALID
+    assert lib.moe_fp8_weights_quantize(ctypes.byref(f32), ctypes.byref(w), ctypes.byref(q), 3, None) == \
+        L.MOE_ERR_UNSUPPORTED
+    # the gathered fp8 GEMM
+    gg = lambda epi, M, K, src, rows: lib.moe_grouped_gemm_fp8_gather(  # noqa: E731
+        epi, 4, M, 256, K, a, a, a, a, a, a, None, rows, src, None)
+    assert gg(L.MOE_EPI_DSWIGLU, 100, 256, 64, a) == L.MOE_ERR_INVALID
+    assert gg(L.MOE_EPI_NONE, 100, 256, 64, None) == L.MOE_ERR_INVALID
+    assert gg(L.MOE_EPI_NONE, 100, 65536, (1 << 16) + 1, a) == L.MOE_ERR_UNSUPPORTED
+    assert gg(L.MOE_EPI_NONE, 100, 256, -1, a) == L.MOE_ERR_INVALID
+    assert gg(L.MOE_EPI_NONE, 0, 256, 0, None) == L.MOE_OK
