@@ -186,7 +186,7 @@ def _split_gateup(w_gateup):
 
 # ----------------------------------------------------------------------------- layer
 def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
-            top_k, score, renorm=False, forced_idx=None, fp8=False, forced_h=None,
+            top_k, score, renorm=False, forced_idx=None, forced_gate=None, fp8=False, forced_h=None,
             forced_s_h=None):
     """Forward pass of the MoE layer on the tokens of ``x``.
 
@@ -197,7 +197,9 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
 
     ``forced_idx`` replaces the selection (used to follow another
     implementation's choice on near-tied tokens); gates are then recomputed
-    from this oracle's own scores for the forced experts.
+    from this oracle's own scores for the forced experts, unless
+    ``forced_gate`` [T, k] (fp32) replaces them too: another implementation's
+    rounding of the same gate values.
 
     ``fp8``: the expert products (routed and shared) run as e4m3 products
     with row-wise scales (``swiglu_ffn_fp8``); the router stays fp32.
@@ -217,6 +219,8 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
     if forced_idx is not None:
         idx = np.asarray(forced_idx, np.int32).reshape(T, k)
     gate = gates_from_scores(scores, idx, score, renorm)
+    if forced_gate is not None:
+        gate = np.asarray(forced_gate, F32).reshape(T, k)
     counts, offsets, pos, src = permute_indices(idx, E)
 
     A = T * k
@@ -442,7 +446,7 @@ def bias_update(bias32, counts, T, k, rate):
 
 
 def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False,
-             terms=None, fp8=False):
+             terms=None, fp8=False, forced_dgu=None, forced_s_dgu=None):
     """Backward pass for upstream gradient dy [T, d], reusing ``forward``'s dict.
 
     Returns dict: dx [T,d], d_w_gateup [E,2f,d], d_w_down [E,d,f],
@@ -450,7 +454,11 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
     dgate [T,k], plus the permuted intermediates dy_perm, dgu, dx_perm.
 
     ``fp8``: the expert data gradients (routed and shared) run as e4m3
-    products (``swiglu_ffn_backward_fp8``); weight gradients stay exact."""
+    products (``swiglu_ffn_backward_fp8``); weight gradients stay exact.
+    ``forced_dgu`` [A, 2f] / ``forced_s_dgu`` [T, 2F] replace the bf16 copies
+    of dG | dU that the gate/up data gradients quantise (another
+    implementation's rounding of the same values); the returned dgu / s_dgu
+    are this oracle's own."""
     x = np.asarray(x, F64)
     dy = np.asarray(dy, F64)
     T, d = x.shape
@@ -472,10 +480,13 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
             continue
         G = fwd["preact"][r0:r1, :f]
         U = fwd["preact"][r0:r1, f:]
-        ffn_bwd = swiglu_ffn_backward_fp8 if fp8 else swiglu_ffn_backward
-        dz, dWg, dWu, dWd, dG, dU = ffn_bwd(
-            fwd["x_perm"][r0:r1], np.asarray(wg_all[e], F64), np.asarray(wu_all[e], F64),
-            np.asarray(w_down[e], F64), G, U, fwd["h"][r0:r1], dy_perm[r0:r1])
+        args = (fwd["x_perm"][r0:r1], np.asarray(wg_all[e], F64), np.asarray(wu_all[e], F64),
+                np.asarray(w_down[e], F64), G, U, fwd["h"][r0:r1], dy_perm[r0:r1])
+        if fp8:
+            dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward_fp8(
+                *args, None if forced_dgu is None else forced_dgu[r0:r1])
+        else:
+            dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward(*args)
         d_w_gateup[e, :f] = dWg
         d_w_gateup[e, f:] = dWu
         d_w_down[e] = dWd
@@ -491,15 +502,19 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
         Fs = sg.shape[0]
         Gs = fwd["s_preact"][:, :Fs]
         Us = fwd["s_preact"][:, Fs:]
-        ffn_bwd = swiglu_ffn_backward_fp8 if fp8 else swiglu_ffn_backward
-        dxs, dSg, dSu, dSd, _, _ = ffn_bwd(x, sg, su, np.asarray(s_down, F64),
-                                           Gs, Us, fwd["s_h"], dy)
+        args = (x, sg, su, np.asarray(s_down, F64), Gs, Us, fwd["s_h"], dy)
+        if fp8:
+            dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward_fp8(*args, forced_s_dgu)
+        else:
+            dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward(*args)
+        out["s_dgu"] = np.concatenate([dGs, dUs], axis=1)
         out["d_s_gateup"] = np.concatenate([dSg, dSu], axis=0)
         out["d_s_down"] = dSd
         out["dx_shared"] = dxs
     else:
         out["d_s_gateup"] = None
         out["d_s_down"] = None
+        out["s_dgu"] = None
         dxs = np.zeros((T, d), F64)
         out["dx_shared"] = None
 
@@ -674,14 +689,15 @@ def swiglu_ffn_fp8(z, w_gate, w_up, w_down, forced_h=None):
     return G, U, H, fp8_product(Hb, w_down)
 
 
-def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY):
+def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=None):
     """``swiglu_ffn_backward`` with the two data gradients in e4m3:
     dH = fp8(bf16(dY)) . fp8 of W_d along its rows d (W_d^T quantised
     row-wise), dz = fp8(bf16(dG | dU)) . fp8 of W_g | W_u along 2f; the
     weight gradients are exact (fp64).  dG | dU, which the second product
     quantises, come from the pre-activations as the layer stores them (bf16),
-    so that this quantisation sees the values a bf16 layer holds.  Same
-    return values."""
+    so that this quantisation sees the values a bf16 layer holds;
+    ``forced_dgu`` replaces that bf16 copy as the second product's input.
+    Same return values."""
     dH = fp8_product(round_bf16(dY), np.asarray(w_down, F64).T)
     Gb, Ub = round_bf16(G), round_bf16(U)
     sg = 1.0 / (1.0 + np.exp(-Gb))
@@ -691,5 +707,6 @@ def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY):
     dW_g = dG.T @ z
     dW_u = dU.T @ z
     w_gu = np.concatenate([w_gate, w_up], axis=0)
-    dz = fp8_product(round_bf16(np.concatenate([dG, dU], axis=1)), w_gu.T)
+    dgu_b = round_bf16(np.concatenate([dG, dU], axis=1)) if forced_dgu is None else np.asarray(forced_dgu, F64)
+    dz = fp8_product(dgu_b, w_gu.T)
     return dz, dW_g, dW_u, dW_d, dG, dU

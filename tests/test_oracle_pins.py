@@ -629,10 +629,10 @@ def _grid_layer(seed, T, d, E, k, f, Fs, score, renorm, one_hot=False):
     if one_hot:
         L["x"] = np.zeros((T, d))
         L["x"][np.arange(T), g.integers(0, d, T)] = 448.0 * 2.0 ** -7
-    L["w_gateup"] = np.stack([_e4m3_grid(g, 2 * f, d, 10) for _ in range(E)])
+    L["w_gateup"] = np.stack([_e4m3_grid(g, 2 * f, d, 10, cols=True) for _ in range(E)])
     L["w_down"] = np.stack([_e4m3_grid(g, d, f, 10, cols=True) for _ in range(E)])
     if Fs:
-        L["s_gateup"] = _e4m3_grid(g, 2 * Fs, d, 10)
+        L["s_gateup"] = _e4m3_grid(g, 2 * Fs, d, 10, cols=True)
         L["s_down"] = _e4m3_grid(g, d, Fs, 10, cols=True)
     L["dy"] = _e4m3_grid(g, T, d, 6)
     return L
@@ -715,6 +715,19 @@ def test_fp8_layer_exact_on_the_e4m3_grid(score, Fs, one_hot):
                      f8, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True)
     assert np.array_equal(b_8["dgu"], b_ex["dgu"])
     assert np.array_equal(b_8["d_w_down"][:, :, :], b_ex["d_w_down"])
+    # a forced dG | dU on the grid: the gate/up data gradient is its exact
+    # product with W_g | W_u (every column of which is on the grid too)
+    fd = _e4m3_grid(g, T * k, 2 * f, 4)
+    fsd = _e4m3_grid(g, T, 2 * Fs, 4) if Fs else None
+    b_f = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                     f8, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True, forced_dgu=fd,
+                     forced_s_dgu=fsd)
+    assert np.array_equal(b_f["dgu"], b_8["dgu"])
+    for e in range(E):
+        r0, r1 = ex["offsets"][e], ex["offsets"][e + 1]
+        assert np.array_equal(b_f["dx_perm"][r0:r1], fd[r0:r1] @ L["w_gateup"][e])
+    if Fs:
+        assert np.array_equal(b_f["dx_shared"], fsd @ L["s_gateup"])
 
 
 def test_fp8_layer_power_of_two_equivariance():
@@ -753,3 +766,13 @@ def test_fp8_layer_close_to_the_exact_layer(case):
         checks += [(b_8["d_s_gateup"], b_ex["d_s_gateup"]), (b_8["d_s_down"], b_ex["d_s_down"])]
     for got, want in checks:
         assert 1e-4 < _rel(got, want) < 0.08, _rel(got, want)
+
+
+def test_forced_gate_replaces_the_gates():
+    """forward's forced_gate: doubling every gate doubles the routed output
+    exactly (a layer without shared experts), and the routing stays."""
+    L = _rand_layer(13, 30, 16, 6, 2, 8, 0, "sigmoid", True)
+    f1 = _fwd(L)
+    f2 = _fwd(L, forced_idx=f1["idx"], forced_gate=2.0 * f1["gate"])
+    assert np.array_equal(f2["idx"], f1["idx"])
+    assert np.array_equal(f2["y"], 2.0 * f1["y"])
