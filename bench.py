@@ -798,6 +798,18 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
     t_copy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
     del cbuf, cdst
+    # practical matrix-core ceiling on this device: each instruction kind
+    # issued back to back on register operands (no memory traffic)
+    ck_out = torch.zeros(4, dtype=torch.float32, device="cuda")
+    mfma_ceiling = {}
+    for kind in ("bf16_32x32x16", "bf16_16x16x32", "e4m3_32x32x64", "e4m3_16x16x128"):
+        flop = [0.0]
+
+        def run_ceiling():
+            flop[0] = M.mfma_ceiling(kind, 3000, ck_out, stream)
+        t_ck = timed_ms(run_ceiling, 3) * 1e-3
+        mfma_ceiling[kind] = flop[0] / t_ck / 1e12
+    del ck_out
     with_fp8 = not args.no_fp8 and cfg.dtype == "bf16" and training
     fp8 = fp8_gate_up(M, cfg, x, saved, w, stream, timed_ms, fl_gu, t_gu, gather) if with_fp8 else None
     fp8_dg = (fp8_gate_up_dgrad(M, cfg, saved, w, stream, timed_ms, flops["gate_up_dgrad"],
@@ -869,6 +881,10 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
                                "frac_of_copy": hbm3_gbs / copy_gbs},
         "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
                              "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
+        "mfma_ceiling": {"tflops": mfma_ceiling,
+                         "gate_up_frac_of_ceiling": ach / mfma_ceiling["bf16_32x32x16"],
+                         "what": "moe_mfma_ceiling: 2 workgroups per CU of 8 waves issuing independent MFMAs of "
+                                 "one kind on register operands, no memory traffic; events over 3 launches"},
         "stages": stage_out,
         "fp8_layer": fp8_whole,
         "fp8_gate_up": fp8,
@@ -922,6 +938,26 @@ def write_all_configs(rows, steps, warmup, log=None):
                  f"{r['value']:11.0f} {r['roofline']['achieved']:10.1f} {r['roofline']['frac']:6.3f} "
                  f"{r['front_end']['us']:9.1f} {r['combine_stages_hbm']['gbs']:9.0f} "
                  f"{cb.get('value', float('nan')):12.1f} {cb.get('tokens', 0):7d} {cb.get('cores', 0):5d}")
+    L += ["", "The same layers through the fp8 calls (moe_forward_fp8 / moe_backward_fp8: e4m3 row-wise expert",
+          "products in the forward and both data gradients, bf16 weight gradients; the e4m3 weight copies are",
+          "written once per weight update and timed on their own).  Layers whose hidden widths are not multiples",
+          "of 128, or fp32 layers, have no fp8 calls.", ""]
+    L.append(f"{'layer':<18s} {'fp8 ms/step':>11s} {'tokens/s':>11s} {'vs bf16':>8s} {'weight copies ms':>16s} "
+             f"{'activation quant us':>19s}")
+    for r in rows:
+        f8 = r.get("fp8_layer")
+        if not f8:
+            continue
+        q = f8["stages"].get("fp8_quantize", {})
+        steps_q = q.get("launches", 0)
+        L.append(f"{r['config']['workload'].split(':')[0]:<18s} {f8['ms_per_step']:11.3f} {f8['tokens_per_s']:11.0f} "
+                 f"{f8['speedup_vs_bf16_step']:8.2f} {f8['weight_copies_ms']:16.3f} "
+                 f"{q.get('us', 0.0) * steps_q / max(1, min(steps, 5)):19.1f}")
+    ck = rows[0].get("mfma_ceiling") if rows else None
+    if ck:
+        L += ["", "Matrix-core ceiling measured on the same box (moe_mfma_ceiling: independent MFMAs on register "
+              "operands, no memory traffic), TFLOP/s: " +
+              ", ".join(f"{k} {v:.0f}" for k, v in ck["tflops"].items())]
     names = [r["config"]["workload"].split(":")[0] for r in rows]
     stages = []
     for r in rows:

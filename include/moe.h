@@ -532,6 +532,22 @@ int moe_stage_timing_mask(uint32_t mask);
  * in full), and clears the records.  MOE_ERR_HIP if an event query fails. */
 int moe_stage_times(double *ms, int64_t *launches);
 
+/* The matrix cores' sustained rate, a measurement aid (the compute
+ * counterpart of timing a device-to-device copy as the practical HBM
+ * ceiling): 2 workgroups per compute unit, 8 waves each, every wave running
+ * `iters` rounds of 8 independent MFMAs of one kind on register operands
+ * with finite pseudo-random data, no memory traffic.  *flop_per_launch
+ * (host) receives the launch's flops (2 per multiply-add); the caller times
+ * the launch on `stream`.  out: device float[1], receives a checksum.
+ * MOE_ERR_INVALID for an unknown kind or iters outside [1, 2^30]. */
+enum {
+  MOE_MFMA_BF16_32X32X16 = 0,  /* the bf16 products' instruction           */
+  MOE_MFMA_BF16_16X16X32 = 1,
+  MOE_MFMA_E4M3_32X32X64 = 2,  /* the fp8 products' instruction            */
+  MOE_MFMA_E4M3_16X16X128 = 3
+};
+int moe_mfma_ceiling(int kind, int64_t iters, float *out, double *flop_per_launch, void *stream);
+
 /* tokens per histogram block of moe_route / moe_permute */
 #define MOE_ROUTE_BLOCK 32
 

@@ -22,6 +22,7 @@ MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD, MOE_WS_FORWARD_FP8, MOE_WS_BACK
 MOE_FP8_FORWARD_LAYOUT, MOE_FP8_BACKWARD_LAYOUT = 1, 2
 MOE_SAVED_TRAINING, MOE_SAVED_PERMUTED_COPY = 1, 2
 MOE_ROUTE_BLOCK = 32
+MFMA_KINDS = ["bf16_32x32x16", "bf16_16x16x32", "e4m3_32x32x64", "e4m3_16x16x128"]
 STAGES = ["router", "route", "permute", "gate_up", "down", "shared_gate_up", "shared_down", "combine",
           "combine_bwd", "down_dgrad", "down_wgrad", "gate_up_wgrad", "gate_up_dgrad", "shared_down_dgrad",
           "shared_down_wgrad", "shared_gate_up_wgrad", "shared_gate_up_dgrad", "router_wgrad",
@@ -100,6 +101,7 @@ SIGNATURES = {
     "moe_quantize_fp8_tensorwise": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
     "moe_grouped_gemm_fp8": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_vp, c_vp]),
+    "moe_mfma_ceiling": (c_i32, [c_i32, c_i64, c_vp, _P(ctypes.c_double), c_vp]),
     "moe_stage_timing_mask": (c_i32, [ctypes.c_uint32]),
     "moe_stage_timing": (c_i32, [c_i32]),
     "moe_stage_times": (c_i32, [_P(ctypes.c_double), _P(c_i64)]),

@@ -320,6 +320,14 @@ def alloc_workspace(desc, which: str, device="cuda") -> torch.Tensor:
     return torch.empty(n, dtype=torch.uint8, device=device)
 
 
+def mfma_ceiling(kind: str, iters: int, out, stream=None) -> float:
+    """Launch the matrix-core rate kernel of one instruction kind (L.MFMA_KINDS); returns its flops."""
+    flop = ctypes.c_double(0.0)
+    _check(L.load().moe_mfma_ceiling(L.MFMA_KINDS.index(kind), int(iters), _p(out), ctypes.byref(flop),
+                                     _stream(stream)), "moe_mfma_ceiling")
+    return flop.value
+
+
 def stage_timing(enable: bool, stages=None):
     """Start (clearing earlier records) or stop per-stage event timing of
     moe_forward / moe_backward; `stages` (names from STAGES) limits it to

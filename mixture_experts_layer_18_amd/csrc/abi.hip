@@ -908,6 +908,19 @@ int moe_bias_update(const moe_desc_t* d, const int32_t* counts, float rate, floa
   return MOE_OK;
 }
 
+int moe_mfma_ceiling(int kind, int64_t iters, float* out, double* flop_per_launch, void* stream) {
+  if (kind < MOE_MFMA_BF16_32X32X16 || kind > MOE_MFMA_E4M3_16X16X128 || iters < 1 || iters > (int64_t(1) << 30))
+    return MOE_ERR_INVALID;
+  if (!out || !flop_per_launch) return MOE_ERR_INVALID;
+  if (!aligned16(out)) return MOE_ERR_ALIGN;
+  // multiply-adds of one instruction of each kind
+  static const double macs[4] = {32.0 * 32 * 16, 16.0 * 16 * 32, 32.0 * 32 * 64, 16.0 * 16 * 128};
+  const int grid = mfma_rate_grid();
+  *flop_per_launch = 2.0 * macs[kind] * 8.0 * (double)iters * (double)grid * 8.0;
+  MOE_TRY(launch_mfma_rate(kind, iters, out, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_stage_timing_mask(uint32_t mask) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   for (const StageRec& r : g_recs) g_spare.push_back(r);

@@ -13,6 +13,10 @@ hipError_t launch_permute(const void* x, int dtype, const int32_t* idx, const in
                           int d, int E, int k, int32_t* base, int32_t* counts, int32_t* offsets,
                           int32_t* pos, int32_t* src, int32_t* tok, void* x_perm, hipStream_t st);
 
+// ---- measurement aid: the matrix cores' sustained rate (ceiling.hip)
+int mfma_rate_grid();
+hipError_t launch_mfma_rate(int kind, int64_t iters, float* out, hipStream_t st);
+
 // ---- grouped GEMM
 // Element types of the operands: A, B and C each f32 or bf16 (MOE_F32 / MOE_BF16).
 struct GemmProblem {

@@ -413,3 +413,16 @@ def test_fp8_layer_argument_checks(lib):
     assert gg(L.MOE_EPI_NONE, 100, 65536, (1 << 16) + 1, a) == L.MOE_ERR_UNSUPPORTED
     assert gg(L.MOE_EPI_NONE, 100, 256, -1, a) == L.MOE_ERR_INVALID
     assert gg(L.MOE_EPI_NONE, 0, 256, 0, None) == L.MOE_OK
+
+
+def test_mfma_ceiling_argument_checks(lib):
+    """The matrix-core rate aid rejects unknown kinds, bad counts and null or
+    misaligned outputs on the host."""
+    a = ctypes.c_void_p(0x10000)
+    f = ctypes.c_double(0.0)
+    assert lib.moe_mfma_ceiling(4, 10, a, ctypes.byref(f), None) == L.MOE_ERR_INVALID
+    assert lib.moe_mfma_ceiling(-1, 10, a, ctypes.byref(f), None) == L.MOE_ERR_INVALID
+    assert lib.moe_mfma_ceiling(0, 0, a, ctypes.byref(f), None) == L.MOE_ERR_INVALID
+    assert lib.moe_mfma_ceiling(0, 10, None, ctypes.byref(f), None) == L.MOE_ERR_INVALID
+    assert lib.moe_mfma_ceiling(0, 10, ctypes.c_void_p(0x10004), ctypes.byref(f), None) == L.MOE_ERR_ALIGN
+    assert len(L.MFMA_KINDS) == 4
