@@ -132,6 +132,8 @@ struct BwdWs {
   size_t gemm_bytes;
   uint8_t* q;      // fp8: the quantised operand of each data gradient in turn
   float* qs;       // and its row scales
+  uint8_t* q_dy;   // fp8: dy's codes [T, d] and scales [T] (the shared down data gradient)
+  float* qs_dy;
 };
 size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out) {
   Carve c(ws);
@@ -149,6 +151,8 @@ size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out) {
   w.gemm = c.take(w.gemm_bytes);
   w.q = nullptr;
   w.qs = nullptr;
+  w.q_dy = nullptr;
+  w.qs_dy = nullptr;
   if (fp8) {
     // dY~ [A, d], dG|dU [A, 2f], dy [T, d], shared dG|dU [T, 2F]
     const size_t szs[] = {(size_t)A * D, (size_t)A * 2 * f, (size_t)T * D, (size_t)T * 2 * F};
@@ -156,6 +160,8 @@ size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out) {
     for (size_t z : szs) qb = z > qb ? z : qb;
     w.q = (uint8_t*)c.take(qb);
     w.qs = (float*)c.take((size_t)(A > T ? A : T) * sizeof(float));
+    w.q_dy = (uint8_t*)c.take((size_t)T * D);
+    w.qs_dy = (float*)c.take((size_t)T * sizeof(float));
   }
   if (out) *out = w;
   return c.off;
@@ -665,10 +671,19 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   hipStream_t st = (hipStream_t)stream;
   BwdWs bw;
   bwd_ws(d, fp8, ws, &bw);
-  // 1. combine backward + router backward (dlogits)
-  MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
-                             d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
-                             bw.dlogits, st));
+  // 1. combine backward + router backward (dlogits); fp8 (k <= 8): the
+  // same kernel also writes the e4m3 copies of dY~ and dy
+  const bool fused_q = fp8 && k <= 8;
+  if (fused_q) {
+    MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd_fp8(dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
+                                                            d->score, d->renorm, (int)T, (int)D, (int)E, (int)k,
+                                                            bw.dy_perm, bw.dlogits, bw.q, bw.qs, bw.q_dy, bw.qs_dy,
+                                                            st));
+  } else {
+    MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
+                               d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
+                               bw.dlogits, st));
+  }
   // 1b. router training terms: their gradients join the router gradient
   if (terms && T > 0 && !sv->counts) return MOE_ERR_INVALID;
   // terms_grad: some term adds gradient; the kernels also run for the loss
@@ -684,7 +699,7 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   // 2. down data gradient fused with the SwiGLU derivative -> dG | dU (fp8:
   // dY~ in e4m3 per row against W_d quantised along d, stored transposed)
   if (fp8) {
-    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dy_perm, dt, A, (int)D, bw.q, bw.qs, st));
+    if (!fused_q) MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dy_perm, dt, A, (int)D, bw.q, bw.qs, st));
     MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_gemm_fp8(MOE_EPI_DSWIGLU, E, A, f, D, sv->offsets, bw.q, bw.qs,
                                                     w8->down_tq, w8->down_ts, bw.dgu, sv->preact, nullptr, st));
   } else {
@@ -716,10 +731,10 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   // 6. shared experts
   if (F > 0) {
     if (fp8) {
-      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q, bw.qs, st));
+      if (!fused_q) MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q_dy, bw.qs_dy, st));
       MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD,
-                launch_gemm_fp8(MOE_EPI_DSWIGLU, 1, T, F, D, nullptr, bw.q, bw.qs, w8->s_down_tq, w8->s_down_ts,
-                                bw.s_dgu, sv->s_preact, nullptr, st));
+                launch_gemm_fp8(MOE_EPI_DSWIGLU, 1, T, F, D, nullptr, bw.q_dy, bw.qs_dy, w8->s_down_tq,
+                                w8->s_down_ts, bw.s_dgu, sv->s_preact, nullptr, st));
     } else {
       MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
                                      nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),

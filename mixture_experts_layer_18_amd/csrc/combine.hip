@@ -120,18 +120,50 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y_pe
 
 MOE_DEV float sigmoid_rounded_f(float l) { return (float)(1.0 / (1.0 + exp(-(double)l))); }
 
+// The e4m3 copies the fp8 backward quantises, written by the combine
+// backward from the rows it forms: the row-wise codes and scales of the
+// gate-weighted rows dy_perm (as rounded to bf16) and of dy itself.
+struct Fp8Rows {
+  uint8_t* q_perm;  // [A, d]
+  float* s_perm;    // [A]
+  uint8_t* q_dy;    // [T, d]
+  float* s_dy;      // [T]
+};
+
+// max |x| over one bf16 row of d elements (exact), in every lane of the wave
+MOE_DEV float bf16_row_amax(const bf16_t* row, int nvec, int lane) {
+  float amax = 0.0f;
+  for (int c = lane; c < nvec; c += 64) {
+    float f[8];
+    Vec<bf16_t>::load(row + (int64_t)c * 8, f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) amax = fmaxf(amax, fabsf(f[u]));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  return amax;
+}
+
+// The bf16 value a stored fp32 result takes (round to nearest even)
+MOE_DEV float bf16_round(float v) { return bf16_lo(pack_bf16x2(v, 0.0f)); }
+
 // Combine backward and router backward for one token per wavefront:
 //   dy_perm[pos[t,j]] = gate[t,j] * dy[t]
 //   dgate[t,j]        = <dy[t], y_perm[pos[t,j]]>          (fp32)
 //   dlogits[t,:]      from dgate through the gate function (selection fixed)
 // The row data is streamed chunk by chunk; with KK > 0 the KK slot rows of a
 // chunk are loaded together and the per-slot dot products kept in registers.
-template <typename T, int KK>
+// Q8 (bf16, KK > 0): also the e4m3 copies of Fp8Rows.  A gate-weighted row's
+// largest magnitude is bf16(gate * max|dy[t]|) exactly (rounding is monotone
+// and symmetric), so a first pass over dy[t] gives every slot's scale before
+// the rows are formed.
+template <typename T, int KK, bool Q8 = false>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ gate,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ idx,
     const float* __restrict__ logits, int score, int renorm, int Tn, int d, int E, int k,
-    T* __restrict__ dy_perm, float* __restrict__ dlogits) {
+    T* __restrict__ dy_perm, float* __restrict__ dlogits, Fp8Rows q8 = {}) {
+  static_assert(!Q8 || (KK > 0 && sizeof(T) == 2), "fp8 copies: bf16 rows, compile-time slots");
   constexpr int VN = Vec<T>::N;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -142,11 +174,23 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
   if constexpr (KK > 0) {
     int64_t row[KK];
     float g[KK], dot[KK];
+    float sq[KK > 0 ? KK : 1], s_dy = 1.0f;
 #pragma unroll
     for (int j = 0; j < KK; ++j) {
       row[j] = (int64_t)pos[tk + j] * d;
       g[j] = gate[tk + j];
       dot[j] = 0.0f;
+    }
+    if constexpr (Q8) {
+      const float amax = bf16_row_amax((const bf16_t*)dy + (int64_t)t * d, nvec, lane);
+      s_dy = fp8_row_scale(amax);
+#pragma unroll
+      for (int j = 0; j < KK; ++j) sq[j] = fp8_row_scale(bf16_round(g[j] * amax));
+      if (lane == 0) {
+        q8.s_dy[t] = s_dy;
+#pragma unroll
+        for (int j = 0; j < KK; ++j) q8.s_perm[pos[tk + j]] = sq[j];
+      }
     }
     // groups of CG chunks: every load of a group is issued before any of its
     // stores, so the loads are in flight together (a load issued after a
@@ -168,6 +212,8 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
         if (c < nvec) {
           float dv[VN];
           Vec<T>::unpack(dr[i], dv);
+          if constexpr (Q8)
+            *reinterpret_cast<u32x2*>(q8.q_dy + (int64_t)t * d + (int64_t)c * VN) = fp8_encode8(dv, s_dy);
 #pragma unroll
           for (int j = 0; j < KK; ++j) {
             float v[VN], o[VN];
@@ -178,6 +224,12 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
               o[u] = g[j] * dv[u];
             }
             Vec<T>::store(dy_perm + row[j] + (int64_t)c * VN, o);
+            if constexpr (Q8) {
+              float b[VN];
+#pragma unroll
+              for (int u = 0; u < VN; ++u) b[u] = bf16_round(o[u]);
+              *reinterpret_cast<u32x2*>(q8.q_perm + row[j] + (int64_t)c * VN) = fp8_encode8(b, sq[j]);
+            }
           }
         }
       }
@@ -435,6 +487,28 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, con
     MOE_K_DISPATCH(combine_bwd_kernel, float, (const float*)dy, (const float*)y_perm, gate, pos, idx,
                    logits, score, renorm, T, d, E, k, (float*)dy_perm, dlogits)
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd_fp8(const void* dy, const void* y_perm, const float* gate, const int32_t* pos,
+                                  const int32_t* idx, const float* logits, int score, int renorm, int T, int d,
+                                  int E, int k, void* dy_perm, float* dlogits, uint8_t* q_perm, float* s_perm,
+                                  uint8_t* q_dy, float* s_dy, hipStream_t st) {
+  if (T == 0) return hipSuccess;
+  if (k < 1 || k > 8) return hipErrorInvalidValue;
+  dim3 grid((unsigned)cdiv64(T, 4)), block(256);
+  const Fp8Rows q{q_perm, s_perm, q_dy, s_dy};
+#define MOE_Q8_CASE(K)                                                                                         \
+  case K:                                                                                                      \
+    combine_bwd_kernel<bf16_t, K, true><<<grid, block, 0, st>>>((const bf16_t*)dy, (const bf16_t*)y_perm, gate,   \
+                                                                pos, idx, logits, score, renorm, T, d, E, k,     \
+                                                                (bf16_t*)dy_perm, dlogits, q);                  \
+    break;
+  switch (k) {
+    MOE_Q8_CASE(1) MOE_Q8_CASE(2) MOE_Q8_CASE(3) MOE_Q8_CASE(4)
+    MOE_Q8_CASE(5) MOE_Q8_CASE(6) MOE_Q8_CASE(7) MOE_Q8_CASE(8)
+  }
+#undef MOE_Q8_CASE
   return hipGetLastError();
 }
 

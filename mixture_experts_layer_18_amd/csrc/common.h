@@ -51,6 +51,22 @@ MOE_DEV float silu_f(float z) { return z * sigmoid_f(z); }
 
 // Sum over the 64 lanes of a wavefront, identical result in every lane.
 // The butterfly order is fixed, so the result is deterministic.
+// Row-wise e4m3 quantisation of 8 values with the row's scale s: each
+// quotient f / s in IEEE fp32, clamped to +-448 (the conversion turns values
+// beyond 464 into NaN), rounded to nearest even by v_cvt_pk_fp8_f32.
+MOE_DEV float fp8_row_scale(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
+MOE_DEV u32x2 fp8_encode8(const float* f, float s) {
+  float v[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) v[u] = fminf(fmaxf(f[u] / s, -448.0f), 448.0f);
+  u32x2 o;
+  o.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+  o.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], o.x, true);
+  o.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+  o.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], o.y, true);
+  return o;
+}
+
 MOE_DEV float wave_sum(float v) {
 #pragma unroll
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);

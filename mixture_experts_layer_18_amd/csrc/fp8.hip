@@ -47,7 +47,7 @@ MOE_DEV float row_amax(const TX* row, int C, int lane) {
   return amax;
 }
 
-MOE_DEV float scale_of(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
+MOE_DEV float scale_of(float amax) { return fp8_row_scale(amax); }
 
 // q = e4m3(clamp(x / s)) for one row
 template <typename TX>
@@ -55,14 +55,7 @@ MOE_DEV void encode_row(const TX* row, int C, float s, uint8_t* qrow, int lane) 
   for (int c = lane * V; c < C; c += 64 * V) {
     float f[V];
     load8(row, c, f);
-#pragma unroll
-    for (int u = 0; u < V; ++u) f[u] = fminf(fmaxf(f[u] / s, -448.0f), 448.0f);
-    u32x2 o;
-    o.x = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
-    o.x = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], o.x, true);
-    o.y = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
-    o.y = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], o.y, true);
-    *reinterpret_cast<u32x2*>(qrow + c) = o;
+    *reinterpret_cast<u32x2*>(qrow + c) = fp8_encode8(f, s);
   }
 }
 

@@ -91,6 +91,12 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, con
                               const int32_t* pos, const int32_t* idx, const float* logits,
                               int score, int renorm, int T, int d, int E, int k, void* dy_perm,
                               float* dlogits, hipStream_t st);
+// combine backward that also writes the row-wise e4m3 copies of dy_perm and
+// dy (bf16 layers, 1 <= k <= 8)
+hipError_t launch_combine_bwd_fp8(const void* dy, const void* y_perm, const float* gate, const int32_t* pos,
+                                  const int32_t* idx, const float* logits, int score, int renorm, int T, int d,
+                                  int E, int k, void* dy_perm, float* dlogits, uint8_t* q_perm, float* s_perm,
+                                  uint8_t* q_dy, float* s_dy, hipStream_t st);
 hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* pos,
                                 const void* dx_shared, const float* dlogits, const int32_t* idx,
                                 const float* w_router, int dense_router, int T, int d, int E,

@@ -343,7 +343,9 @@ def test_fp8_layer_workspace_sizes(lib):
     workspaces: the forward the token codes [T, d] with one scale per token and
     the larger of the routed [A, f] and shared [T, F] hidden codes with their
     scales; the backward the largest data-gradient operand (here dG | dU,
-    [A, 2f]) with one scale per row."""
+    [A, 2f]) with one scale per row, and dy's codes [T, d] with one scale per
+    token (the shared down data gradient's operand, written by the combine
+    backward)."""
     T, dm, E, k, f, F = 16384, 2048, 64, 6, 1408, 2 * 1408
     d = make_desc(T, dm, E, k, f, 2, 1408, "sigmoid", True, "bf16")
     A = T * k
@@ -353,8 +355,8 @@ def test_fp8_layer_workspace_sizes(lib):
     bw8 = lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_BACKWARD_FP8)
     assert fw8 - fw >= T * dm + T * 4 + A * f + A * 4
     assert fw8 - fw < T * dm + T * 4 + A * f + A * 4 + 4 * 256
-    assert bw8 - bw >= A * 2 * f + A * 4
-    assert bw8 - bw < A * 2 * f + A * 4 + 2 * 256
+    assert bw8 - bw >= A * 2 * f + A * 4 + T * dm + T * 4
+    assert bw8 - bw < A * 2 * f + A * 4 + T * dm + T * 4 + 4 * 256
     assert A * f > T * F
 
 
