@@ -317,3 +317,71 @@ def test_fp8_layer_matches_its_products():
     torch.cuda.synchronize()
     assert torch.equal(h.view(torch.int16), sv["h"].view(torch.int16))
     assert torch.equal(aux.view(torch.int16), sv["preact"].view(torch.int16))
+
+
+def test_fp8_layer_full_size_experts():
+    """The 7B-style layer (16384 tokens, 64 experts, top-6, two shared
+    experts) through moe_forward_fp8 + moe_backward_fp8 in the benchmark's
+    launch configuration (token rows gathered), checked on every row of four
+    experts (the largest, the smallest non-empty one and two more): the
+    pre-activations, H and the down outputs (on the GPU's H) against the
+    oracle's fp8 products; dG | dU (formed through the public calls from the
+    same kernels, and shown to be the layer's own by the gate/up weight
+    gradient, bit for bit) against the oracle's on the GPU's dY~ rows and
+    stored pre-activations; and those experts' weight gradients, bf16
+    products of the GPU's bf16 operands, against their exact products."""
+    cfg = synth.CONFIG_BY_NAME["moe7b_bf16"]
+    print(f"[fp8 full] {cfg.name}: inputs", flush=True)
+    inp = synth.make_inputs(cfg, with_dy=True)
+    w = R.upload_layer(cfg, inp)
+    x, dy = dev(inp["x"]), dev(inp["dy"])
+    print(f"[fp8 full] {cfg.name}: GPU fp8 forward+backward", flush=True)
+    g = R.run_gpu(cfg, inp, backward=True, weights=w, x=x, dy=dy, keep_device=True, gather=True, fp8=True)
+    sv, w8 = g["saved"], g["w8"]
+    T, d, E, k, f = cfg.T, cfg.d, cfg.E, cfg.k, cfg.f
+    A = T * k
+    dgu, _, dh_rms = _gpu_dgu(cfg, sv, w8, dy)
+    dwg = torch.empty(E, 2 * f, d, dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm_gather("TN", "none", E, A, 2 * f, d, sv["offsets"], dgu, x, dwg, sv["tok"], T)
+    torch.cuda.synchronize()
+    assert torch.equal(dwg.view(torch.int16), g["grads"]["d_w_gateup"].view(torch.int16))
+    off = sv["offsets"].cpu().numpy().astype(np.int64)
+    tok = sv["tok"].cpu().numpy().astype(np.int64)
+    src = sv["src"].cpu().numpy().astype(np.int64)
+    gate = sv["gate"].cpu().numpy().reshape(-1)
+    counts = np.diff(off)
+    nz = np.where(counts > 0)[0]
+    rng = np.random.default_rng(21)
+    experts = [int(nz[np.argmax(counts[nz])]), int(nz[np.argmin(counts[nz])])]
+    experts += [int(e) for e in rng.choice(np.setdiff1d(nz, experts), size=2, replace=False)]
+    xf = synth.as_f64(inp["x"], "bf16")
+    dyf = synth.as_f64(inp["dy"], "bf16")
+    gu_all = synth.bf16_bits_to_f32(inp["w_gateup"])
+    dn_all = synth.bf16_bits_to_f32(inp["w_down"])
+    for e in experts:
+        r0, r1 = int(off[e]), int(off[e + 1])
+        print(f"[fp8 full] expert {e}: {r1 - r0} rows", flush=True)
+        tk = tok[r0:r1]
+        pre = host(sv["preact"][r0:r1])
+        gh = host(sv["h"][r0:r1])
+        ref = O.fp8_product(xf[tk], gu_all[e])
+        assert_rounded(pre, ref, "bf16", f"preact, expert {e}")
+        assert_rounded(gh, O.silu(ref[:, :f]) * ref[:, f:], "bf16", f"h, expert {e}", extra=_h_noise(ref, f))
+        assert_rounded(host(sv["y_perm"][r0:r1]), O.fp8_product(gh, dn_all[e]), "bf16", f"y_perm, expert {e}",
+                       extra=_fp8_sum_bound(gh, dn_all[e]))
+        # the gate-weighted rows: one fp32 product of the GPU's gate and dy, rounded once
+        dyp = O.round_bf16(gate[src[r0:r1]].astype(np.float64)[:, None] * dyf[tk])
+        dH = O.fp8_product(dyp, dn_all[e].astype(np.float64).T)
+        Gm, U = pre[:, :f], pre[:, f:]
+        sg = 1.0 / (1.0 + np.exp(-Gm))
+        dgu_ref = np.concatenate([dH * U * sg * (1.0 + Gm * (1.0 - sg)), dH * Gm * sg], axis=1)
+        gdgu = host(dgu[r0:r1])
+        assert_rounded(gdgu, dgu_ref, "bf16", f"dG | dU, expert {e}", extra=_dswiglu_noise(dh_rms[0], pre, f))
+        # weight gradients: bf16 products of the GPU's bf16 operands
+        rows = r1 - r0
+        wg_ref = gdgu.T @ xf[tk]
+        wg_acc = rows * 2.0 ** -24 * (np.abs(gdgu).T @ np.abs(xf[tk]))
+        assert_rounded(host(g["grads"]["d_w_gateup"][e]), wg_ref, "bf16", f"dW_gateup, expert {e}", extra=wg_acc)
+        wd_ref = dyp.T @ gh
+        wd_acc = rows * 2.0 ** -24 * (np.abs(dyp).T @ np.abs(gh))
+        assert_rounded(host(g["grads"]["d_w_down"][e]), wd_ref, "bf16", f"dW_down, expert {e}", extra=wd_acc)
