@@ -55,8 +55,10 @@ loss, the single-expert loss of exactly 1, balanced loads, the z-loss closed
 form and the bias update on balanced and skewed loads; for the fp8 mode, the
 e4m3 format table and rounding, exactness of every product on the e4m3 grid,
 the half-step error bound off it, power-of-two equivariance of the whole
-layer, closeness to the exact layer and the bf16 rounding rule.  Every
-function below is covered by at least one pin.
+layer, closeness to the exact layer and the bf16 rounding rule; for the e5m2
+gradient format, its decode table and rounding, brute-force nearest search,
+the row-wise half-step bound and exactness of the down data gradient on the
+e5m2 grid.  Every function below is covered by at least one pin.
 """
 from __future__ import annotations
 
@@ -446,7 +448,7 @@ def bias_update(bias32, counts, T, k, rate):
 
 
 def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False,
-             terms=None, fp8=False, forced_dgu=None, forced_s_dgu=None):
+             terms=None, fp8=False, forced_dgu=None, forced_s_dgu=None, fp8_grad_format="e4m3"):
     """Backward pass for upstream gradient dy [T, d], reusing ``forward``'s dict.
 
     Returns dict: dx [T,d], d_w_gateup [E,2f,d], d_w_down [E,d,f],
@@ -458,7 +460,8 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
     ``forced_dgu`` [A, 2f] / ``forced_s_dgu`` [T, 2F] replace the bf16 copies
     of dG | dU that the gate/up data gradients quantise (another
     implementation's rounding of the same values); the returned dgu / s_dgu
-    are this oracle's own."""
+    are this oracle's own.  ``fp8_grad_format``: "e4m3" or "e5m2" for the
+    gradient operands of the fp8 data gradients (the weights stay e4m3)."""
     x = np.asarray(x, F64)
     dy = np.asarray(dy, F64)
     T, d = x.shape
@@ -484,7 +487,7 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
                 np.asarray(w_down[e], F64), G, U, fwd["h"][r0:r1], dy_perm[r0:r1])
         if fp8:
             dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward_fp8(
-                *args, None if forced_dgu is None else forced_dgu[r0:r1])
+                *args, None if forced_dgu is None else forced_dgu[r0:r1], fp8_grad_format)
         else:
             dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward(*args)
         d_w_gateup[e, :f] = dWg
@@ -504,7 +507,7 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
         Us = fwd["s_preact"][:, Fs:]
         args = (x, sg, su, np.asarray(s_down, F64), Gs, Us, fwd["s_h"], dy)
         if fp8:
-            dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward_fp8(*args, forced_s_dgu)
+            dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward_fp8(*args, forced_s_dgu, fp8_grad_format)
         else:
             dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward(*args)
         out["s_dgu"] = np.concatenate([dGs, dUs], axis=1)
@@ -565,18 +568,21 @@ def e4m3_decode(codes):
     return _E4M3_VALUES[np.asarray(codes, np.uint8)]
 
 
-def _e4m3_table():
+def _table(values):
+    """(values, codes) of the non-negative finite codes of a format, ascending."""
     codes = np.arange(128, dtype=np.uint8)
-    v = e4m3_decode(codes)
-    ok = ~np.isnan(v)
-    return v[ok], codes[ok]
+    v = values[codes]
+    ok = np.isfinite(v)
+    order = np.argsort(v[ok], kind="stable")
+    return v[ok][order], codes[ok][order]
 
 
-def e4m3_encode(x):
-    """Round fp64/fp32 values to the nearest e4m3 value, ties to the even code
-    (the one with mantissa bit 0), values beyond +-448 clamped to +-448."""
-    vals, codes = _e4m3_table()            # ascending 0 .. 448
-    a = np.minimum(np.abs(np.asarray(x, F64)), 448.0)
+def _encode_nearest(x, values, vmax):
+    """Round values to the nearest value of a format whose non-negative codes
+    0..127 hold ascending magnitudes (sign in bit 7), ties to the even code
+    (the one with mantissa bit 0), magnitudes beyond vmax clamped to vmax."""
+    vals, codes = _table(values)
+    a = np.minimum(np.abs(np.asarray(x, F64)), vmax)
     hi = np.searchsorted(vals, a, side="left")      # first value >= a
     hi = np.minimum(hi, len(vals) - 1)
     lo = np.maximum(hi - 1, 0)
@@ -589,13 +595,55 @@ def e4m3_encode(x):
     return (c | np.where(neg, 0x80, 0)).astype(np.uint8)
 
 
-def quantize_rowwise(x):
-    """Row-wise scaling: s_r = amax_r / 448 (fp32; 1 for an all-zero row),
-    q = e4m3(x / s_r) with the division in fp32.  Returns (codes uint8, s fp32)."""
+def e4m3_encode(x):
+    """Round fp64/fp32 values to the nearest e4m3 value, ties to the even code
+    (the one with mantissa bit 0), values beyond +-448 clamped to +-448."""
+    return _encode_nearest(x, _E4M3_VALUES, 448.0)
+
+
+# OCP e5m2 (KempnerForge README, "Features": FP8 in E4M3 and E5M2): 1 sign,
+# 5 exponent (bias 15), 2 mantissa bits; exponent 0 holds the subnormals
+# m/4 * 2^-14; exponent 31 holds infinity (mantissa 0) and NaN; the largest
+# finite value is 57344.
+
+def _e5m2_values():
+    """Value of each of the 256 e5m2 codes (index = code), fp64."""
+    c = np.arange(256, dtype=np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 2) & 31
+    m = c & 3
+    val = np.where(e == 0, m / 4.0 * 2.0 ** -14, (1.0 + m / 4.0) * np.exp2(e.astype(F64) - 15.0))
+    val = np.where(e == 31, np.where(m == 0, np.inf, np.nan), val)
+    return sign * val
+
+
+_E5M2_VALUES = _e5m2_values()
+
+
+def e5m2_decode(codes):
+    """Value of each e5m2 code (uint8 array) as fp64."""
+    return _E5M2_VALUES[np.asarray(codes, np.uint8)]
+
+
+def e5m2_encode(x):
+    """Round values to the nearest finite e5m2 value, ties to the even code,
+    values beyond +-57344 clamped to +-57344."""
+    return _encode_nearest(x, _E5M2_VALUES, 57344.0)
+
+
+# the two formats: decoder, encoder, largest finite value
+FP8_FORMATS = {"e4m3": (e4m3_decode, e4m3_encode, 448.0), "e5m2": (e5m2_decode, e5m2_encode, 57344.0)}
+
+
+def quantize_rowwise(x, fmt="e4m3"):
+    """Row-wise scaling: s_r = amax_r / vmax (fp32; 1 for an all-zero row;
+    vmax = 448 for e4m3, 57344 for e5m2), q = fmt(x / s_r) with the division
+    in fp32.  Returns (codes uint8, s fp32)."""
+    _, encode, vmax = FP8_FORMATS[fmt]
     x32 = np.asarray(x, F32)
     amax = np.abs(x32).max(axis=1)
-    s = np.where(amax > 0, (amax / np.float32(448.0)).astype(F32), np.float32(1.0)).astype(F32)
-    q = e4m3_encode((x32 / s[:, None]).astype(F32))
+    s = np.where(amax > 0, (amax / np.float32(vmax)).astype(F32), np.float32(1.0)).astype(F32)
+    q = encode((x32 / s[:, None]).astype(F32))
     return q, s
 
 
@@ -627,10 +675,10 @@ def quantize_rowwise_transposed(w):
     return codes, scales
 
 
-def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets):
+def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets, a_fmt="e4m3"):
     """C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k] over the
-    decoded codes, for the rows m of group g; fp64."""
-    A = e4m3_decode(a_codes)
+    decoded codes (A in a_fmt, B in e4m3), for the rows m of group g; fp64."""
+    A = FP8_FORMATS[a_fmt][0](a_codes)
     B = e4m3_decode(b_codes)
     G, N, _ = B.shape
     C = np.zeros((A.shape[0], N))
@@ -667,13 +715,14 @@ def round_bf16(v):
     return b.astype(np.uint32).view(F32).astype(F64)
 
 
-def fp8_product(a, b):
+def fp8_product(a, b, a_fmt="e4m3"):
     """a [M, K] times b [N, K]^T with each operand quantised row-wise along K
-    (``quantize_rowwise``) and the scaled e4m3 product taken exactly (fp64)."""
+    (``quantize_rowwise``; a in a_fmt, b in e4m3) and the scaled product
+    taken exactly (fp64)."""
     a = np.asarray(a, F64)
-    qa, sa = quantize_rowwise(a)
+    qa, sa = quantize_rowwise(a, a_fmt)
     qb, sb = quantize_rowwise(b)
-    return grouped_gemm_fp8_nt(qa, sa, qb[None], sb[None], np.array([0, a.shape[0]]))
+    return grouped_gemm_fp8_nt(qa, sa, qb[None], sb[None], np.array([0, a.shape[0]]), a_fmt)
 
 
 def swiglu_ffn_fp8(z, w_gate, w_up, w_down, forced_h=None):
@@ -689,7 +738,7 @@ def swiglu_ffn_fp8(z, w_gate, w_up, w_down, forced_h=None):
     return G, U, H, fp8_product(Hb, w_down)
 
 
-def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=None):
+def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=None, grad_fmt="e4m3"):
     """``swiglu_ffn_backward`` with the two data gradients in e4m3:
     dH = fp8(bf16(dY)) . fp8 of W_d along its rows d (W_d^T quantised
     row-wise), dz = fp8(bf16(dG | dU)) . fp8 of W_g | W_u along 2f; the
@@ -697,8 +746,9 @@ def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=Non
     quantises, come from the pre-activations as the layer stores them (bf16),
     so that this quantisation sees the values a bf16 layer holds;
     ``forced_dgu`` replaces that bf16 copy as the second product's input.
-    Same return values."""
-    dH = fp8_product(round_bf16(dY), np.asarray(w_down, F64).T)
+    ``grad_fmt``: the format of the gradient operands (dY, dG | dU); the
+    weights stay e4m3.  Same return values."""
+    dH = fp8_product(round_bf16(dY), np.asarray(w_down, F64).T, grad_fmt)
     Gb, Ub = round_bf16(G), round_bf16(U)
     sg = 1.0 / (1.0 + np.exp(-Gb))
     dG = dH * Ub * sg * (1.0 + Gb * (1.0 - sg))
@@ -708,5 +758,5 @@ def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=Non
     dW_u = dU.T @ z
     w_gu = np.concatenate([w_gate, w_up], axis=0)
     dgu_b = round_bf16(np.concatenate([dG, dU], axis=1)) if forced_dgu is None else np.asarray(forced_dgu, F64)
-    dz = fp8_product(dgu_b, w_gu.T)
+    dz = fp8_product(dgu_b, w_gu.T, grad_fmt)
     return dz, dW_g, dW_u, dW_d, dG, dU

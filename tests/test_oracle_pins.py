@@ -776,3 +776,103 @@ def test_forced_gate_replaces_the_gates():
     f2 = _fwd(L, forced_idx=f1["idx"], forced_gate=2.0 * f1["gate"])
     assert np.array_equal(f2["idx"], f1["idx"])
     assert np.array_equal(f2["y"], 2.0 * f1["y"])
+
+
+# --------------------------------------------------------------------------- e5m2
+def test_e5m2_decode_table_against_the_format():
+    """Every code against the OCP e5m2 definition written out by hand."""
+    v = O.e5m2_decode(np.arange(256, dtype=np.uint8))
+    assert v[0x00] == 0.0 and v[0x80] == 0.0 and np.signbit(v[0x80])
+    assert v[0x01] == 2.0 ** -16                # smallest subnormal
+    assert v[0x03] == 3 * 2.0 ** -16            # largest subnormal
+    assert v[0x04] == 2.0 ** -14                # smallest normal
+    assert v[0x3c] == 1.0 and v[0xbc] == -1.0
+    assert v[0x3d] == 1.25 and v[0x3e] == 1.5 and v[0x3f] == 1.75
+    assert v[0x7b] == 57344.0 and v[0xfb] == -57344.0
+    assert v[0x7c] == np.inf and v[0xfc] == -np.inf
+    assert all(np.isnan(v[c]) for c in (0x7d, 0x7e, 0x7f, 0xfd, 0xfe, 0xff))
+    finite = v[np.isfinite(v)]
+    assert len(finite) == 248 and len(np.unique(finite)) == 247
+
+
+def test_e5m2_encode_rounding_and_brute_force():
+    """Finite values encode to themselves; midpoints go to the even code and a
+    hair either side to the nearer; magnitudes beyond 57344 clamp to it; and
+    random values match a nearest-value search over the finite codes written
+    independently."""
+    codes = np.arange(0x7c, dtype=np.uint8)
+    vals = O.e5m2_decode(codes)
+    assert np.array_equal(O.e5m2_decode(O.e5m2_encode(vals)), vals)
+    mid = (vals[:-1] + vals[1:]) / 2
+    lo = codes[:-1]
+    assert np.array_equal(O.e5m2_encode(mid), np.where(lo % 2 == 0, lo, lo + 1))
+    assert np.array_equal(O.e5m2_encode(np.nextafter(mid, 0)), lo)
+    assert np.array_equal(O.e5m2_encode(np.nextafter(mid, np.inf)), lo + 1)
+    assert O.e5m2_encode([1e6])[0] == 0x7b and O.e5m2_encode([-1e6])[0] == 0xfb
+    g = np.random.default_rng(33)
+    x = np.concatenate([g.standard_normal(2000) * 3000, g.standard_normal(1000) * 1e-4])
+    for v in x:
+        a = min(abs(v), 57344.0)
+        dd = np.abs(vals - a)
+        best = np.where(dd == dd.min())[0]
+        c = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert O.e5m2_encode([v])[0] == (c | (0x80 if v < 0 else 0)), v
+
+
+def test_e5m2_rowwise_quantisation_and_product():
+    """Row-wise e5m2: every row maximum maps to 57344 exactly, every element is
+    reproduced within half an e5m2 step (2^-3 of the value, or 2^-17 of the
+    row scale in the subnormal range), and the product with an e4m3 operand
+    equals the product of the two dequantised operands."""
+    g = np.random.default_rng(34)
+    x = (g.standard_normal((30, 64)) * np.exp(g.uniform(-4, 4, (30, 1)))).astype(np.float32)
+    q, s = O.quantize_rowwise(x, "e5m2")
+    xd = O.e5m2_decode(q) * s[:, None].astype(np.float64)
+    bound = np.maximum(np.abs(x) * 2.0 ** -3, s[:, None].astype(np.float64) * 2.0 ** -17)
+    assert np.all(np.abs(xd - x) <= bound * (1 + 1e-12))
+    assert np.all(np.max(np.abs(O.e5m2_decode(q)), axis=1) == 57344.0)
+    w = g.standard_normal((20, 64)).astype(np.float32)
+    qw, sw = O.quantize_rowwise(w)
+    C = O.grouped_gemm_fp8_nt(q, s, qw[None], sw[None], np.array([0, 30]), "e5m2")
+    ref = xd @ (O.e4m3_decode(qw) * sw[:, None].astype(np.float64)).T
+    assert np.max(np.abs(C - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
+def _e5m2_grid(g, R, C, p):
+    """[R, C] values on the e5m2 grid times 2^-p, each row's largest magnitude
+    exactly 57344 * 2^-p: row-wise e5m2 quantisation is then exact."""
+    codes = g.integers(0x10, 0x78, size=(R, C)).astype(np.uint8)     # moderate magnitudes
+    m = O.e5m2_decode(codes) * np.where(g.random((R, C)) < 0.5, -1.0, 1.0)
+    m[np.arange(R), np.arange(R) % C] = 57344.0
+    return m * 2.0 ** -p
+
+
+def test_fp8_layer_e5m2_gradients():
+    """The fp8 backward with e5m2 gradient operands: with one-hot tokens and
+    weights on the e4m3 grid, top-1 routing and dy on the e5m2 grid, the down
+    data gradient is exact (dG | dU equal the exact backward's); scaling dy by
+    2^-2 scales dx and every gradient by exactly 2^-2; off the grid it stays
+    close to the exact layer, further from it than the e4m3 gradients (one
+    mantissa bit fewer)."""
+    T, d, E, k, f = 24, 48, 4, 1, 32
+    L = _grid_layer(5, T, d, E, k, f, 8, "softmax", True, one_hot=True)
+    L["dy"] = _e5m2_grid(np.random.default_rng(8), T, d, 12)
+    ex = _fwd(L)
+    f8 = _fwd(L, fp8=True)
+    b_ex = _bwd(L, ex)
+    b_5 = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"],
+                     f8, L["dy"], score=L["score"], renorm=L["renorm"], fp8=True, fp8_grad_format="e5m2")
+    assert np.array_equal(b_5["dgu"], b_ex["dgu"])
+    L2 = _rand_layer(11, 40, 32, 6, 2, 16, 16, "sigmoid", True)
+    fw = _fwd(L2, fp8=True)
+    bw = lambda dy, fmt: O.backward(L2["x"], L2["w_router"], L2["w_gateup"], L2["w_down"],  # noqa: E731
+                                    L2["s_gateup"], L2["s_down"], fw, dy, score=L2["score"],
+                                    renorm=L2["renorm"], fp8=True, fp8_grad_format=fmt)
+    b1, b2 = bw(L2["dy"], "e5m2"), bw(L2["dy"] * 0.25, "e5m2")
+    for key in ("dx", "d_w_gateup", "d_w_down", "d_s_gateup", "d_s_down", "d_w_router"):
+        assert np.array_equal(b2[key], 0.25 * b1[key]), key
+    fx = _fwd(L2)
+    bx = _bwd(L2, fx)
+    b4 = bw(L2["dy"], "e4m3")
+    r5, r4 = _rel(b1["dx"], bx["dx"]), _rel(b4["dx"], bx["dx"])
+    assert 1e-4 < r4 < r5 < 0.15, (r4, r5)
