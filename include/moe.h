@@ -342,15 +342,22 @@ int moe_bias_update(const moe_desc_t *desc, const int32_t *counts, float rate, f
 
 /* ---------------------------------------------------------------- fp8 experts */
 
+/* fp8 formats (KempnerForge README, "Features": FP8 in E4M3 and E5M2): OCP
+ * e4m3 (4 exponent bits, bias 7, largest finite 448, no infinities) and OCP
+ * e5m2 (5 exponent bits, bias 15, largest finite 57344).  Row-wise scales are
+ * amax / 448 resp. amax / 57344. */
+enum { MOE_E4M3 = 0, MOE_E5M2 = 1 };
+
 /* Row-wise fp8 quantisation (Apex-3 code page: FP8 through torchao,
  * --precision fp8_rowwise).  For each row r of x [rows, cols] (dtype bf16 or
- * fp32): s_r = amax_r / 448 in fp32 (1 for an all-zero row), and
- * q[r, c] = e4m3(x[r, c] / s_r), the quotient in fp32, clamped to +-448 and
- * rounded to nearest even onto the OCP e4m3 grid.
+ * fp32): s_r = amax_r / vmax in fp32 (1 for an all-zero row; vmax = 448 for
+ * MOE_E4M3, 57344 for MOE_E5M2), and q[r, c] = fmt(x[r, c] / s_r), the
+ * quotient in fp32, clamped to +-vmax and rounded to nearest even onto the
+ * format's grid.
  *   q [rows, cols] uint8 codes (out), scale [rows] fp32 (out)
  * cols a multiple of 64; pointers 16-byte aligned. */
-int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void *x, uint8_t *q, float *scale,
-                     void *stream);
+int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, int format, const void *x, uint8_t *q,
+                     float *scale, void *stream);
 
 /* Row-wise fp8 quantisation along the first axis of each matrix, stored
  * transposed (the weight of a data-gradient product, e.g. dX = dGU . W_gu
@@ -382,6 +389,9 @@ int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const voi
 
 /* fp8 grouped GEMM, forward (NT) layout, with row scales:
  *   C[m, n] = a_scale[m] * b_scale[g, n] * sum_k A[m, k] B[g, n, k]
+ * with A's codes in a_format (MOE_E4M3, or MOE_E5M2 for the gradient operand
+ * of a data gradient: MOE_EPI_NONE or MOE_EPI_DSWIGLU only, else
+ * MOE_ERR_UNSUPPORTED) and B's in e4m3
  * for the rows m of group g (group_offsets as in moe_grouped_gemm, NULL for
  * one group), fp32
  * accumulation of the exact e4m3 products, rounded once to bf16.
@@ -396,12 +406,12 @@ int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const voi
  *   gradient with B the down weight from moe_quantize_fp8_transposed).
  * K a multiple of 64, N a multiple of 64 (SwiGLU: N/2 a multiple of 128),
  * 1 <= G <= 256; pointers 16-byte aligned. */
-int moe_grouped_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
+int moe_grouped_gemm_fp8(int epilogue, int a_format, int64_t G, int64_t M_total, int64_t N, int64_t K,
                          const int32_t *group_offsets, const uint8_t *A, const float *a_scale,
                          const uint8_t *B, const float *b_scale, void *C, void *aux, void *stream);
 
-/* moe_grouped_gemm_fp8 (MOE_EPI_NONE or MOE_EPI_SWIGLU) with the rows of A
- * gathered: routed row m reads the codes A[rows[m]] [src_rows, K] and the
+/* moe_grouped_gemm_fp8 (MOE_EPI_NONE or MOE_EPI_SWIGLU, e4m3 A) with the rows
+ * of A gathered: routed row m reads the codes A[rows[m]] [src_rows, K] and the
  * scale a_scale[rows[m]] (a_scale [src_rows]), so that token rows quantised
  * once per token feed all k of their assignments.  rows [M_total] int32
  * (device), each in [0, src_rows) (not checked on the device: moe_permute's
@@ -469,11 +479,13 @@ int moe_forward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp
                     const void *x, void *y, const moe_saved_t *saved, void *ws, size_t ws_bytes,
                     void *stream);
 
-/* moe_backward with the expert data gradients in e4m3: the gate-weighted
+/* moe_backward with the expert data gradients in fp8: the gate-weighted
  * upstream rows dY~ (bf16) are quantised row-wise for dH = dY~ W_d (with the
  * SwiGLU derivative fused), dG | dU (bf16) row-wise for dX~ = (dG | dU) W_gu,
- * against the data-gradient copies of w8; the shared experts likewise (dy
- * itself for their down product).  Weight gradients stay bf16 products of the
+ * against the e4m3 data-gradient copies of w8; the shared experts likewise
+ * (dy itself for their down product).  grad_format: MOE_E4M3, or MOE_E5M2
+ * for these gradient operands (the weights stay e4m3).  With k <= 8 the
+ * combine backward writes dY~'s and dy's codes as it forms the rows.  Weight gradients stay bf16 products of the
  * bf16 activations with fp32 accumulation (the row-wise recipe with
  * high-precision weight gradients); the router backward is that of
  * moe_backward.  Arguments as moe_backward, plus
@@ -483,7 +495,7 @@ int moe_forward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp
  * them for the weight gradients, but checks them as moe_backward does).
  * Same layer limits as moe_forward_fp8. */
 int moe_backward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp8_weights_t *w8,
-                     const void *x, const moe_saved_t *saved, const void *dy, void *dx,
+                     int grad_format, const void *x, const moe_saved_t *saved, const void *dy, void *dx,
                      const moe_grads_t *grads, const moe_router_terms_t *terms, float *losses,
                      void *ws, size_t ws_bytes, void *stream);
 

@@ -20,6 +20,8 @@ MOE_GEMM_NT, MOE_GEMM_NN, MOE_GEMM_TN = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
 MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD, MOE_WS_FORWARD_FP8, MOE_WS_BACKWARD_FP8 = 0, 1, 2, 3, 4
 MOE_FP8_FORWARD_LAYOUT, MOE_FP8_BACKWARD_LAYOUT = 1, 2
+MOE_E4M3, MOE_E5M2 = 0, 1
+FP8_FORMATS = {"e4m3": MOE_E4M3, "e5m2": MOE_E5M2}
 MOE_SAVED_TRAINING, MOE_SAVED_PERMUTED_COPY = 1, 2
 MOE_ROUTE_BLOCK = 32
 MFMA_KINDS = ["bf16_32x32x16", "bf16_16x16x32", "e4m3_32x32x64", "e4m3_16x16x128"]
@@ -89,18 +91,18 @@ SIGNATURES = {
                              _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
     "moe_forward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_vp, c_vp, _P(MoeSaved), c_vp,
                                 c_sz, c_vp]),
-    "moe_backward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_vp, _P(MoeSaved), c_vp, c_vp,
-                                 _P(MoeGrads), _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
+    "moe_backward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_i32, c_vp, _P(MoeSaved), c_vp,
+                                 c_vp, _P(MoeGrads), _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
     "moe_fp8_weights_quantize": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_i32, c_vp]),
     "moe_grouped_gemm_fp8_gather": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                             c_vp, c_vp, c_vp, c_i64, c_vp]),
     "moe_bias_update": (c_i32, [_P(MoeDesc), c_vp, ctypes.c_float, c_vp, c_vp]),
-    "moe_quantize_fp8": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
+    "moe_quantize_fp8": (c_i32, [c_i64, c_i64, c_i32, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_quantize_fp8_transposed": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp]),
     "moe_quantize_fp8_tensorwise_workspace_bytes": (c_sz, [c_i64]),
     "moe_quantize_fp8_tensorwise": (c_i32, [c_i64, c_i64, c_i32, c_vp, c_vp, c_vp, c_vp, c_sz, c_vp]),
-    "moe_grouped_gemm_fp8": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp,
-                                     c_vp, c_vp]),
+    "moe_grouped_gemm_fp8": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
+                                     c_vp, c_vp, c_vp]),
     "moe_mfma_ceiling": (c_i32, [c_i32, c_i64, c_vp, _P(ctypes.c_double), c_vp]),
     "moe_stage_timing_mask": (c_i32, [ctypes.c_uint32]),
     "moe_stage_timing": (c_i32, [c_i32]),

@@ -180,12 +180,14 @@ def moe_forward_fp8(desc, weights: dict, w8: dict, x, y, saved: dict, ws, stream
 
 
 def moe_backward_fp8(desc, weights: dict, w8: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None,
-                     terms=None, losses=None):
+                     terms=None, losses=None, grad_format="e4m3"):
+    """grad_format: "e4m3" or "e5m2" for the gradient operands of the fp8 data gradients."""
     w = _weights(weights)
     q = _fp8_weights(w8)
     s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
     g = L.MoeGrads(*(_p(grads.get(n)) for n in GRAD_FIELDS))
-    _check(L.load().moe_backward_fp8(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(q), _p(x), ctypes.byref(s),
+    _check(L.load().moe_backward_fp8(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(q), L.FP8_FORMATS[grad_format],
+                                     _p(x), ctypes.byref(s),
                                      _p(dy), _p(dx), ctypes.byref(g), _terms(terms), _p(losses), _p(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "moe_backward_fp8")
 
@@ -196,11 +198,13 @@ def moe_bias_update(desc, counts, rate, bias, stream=None):
            "moe_bias_update")
 
 
-def moe_quantize_fp8(x, q, scale, stream=None):
-    """Row-wise e4m3 quantisation of x [rows, cols] (bf16 or fp32) into q (uint8) and scale (fp32)."""
+def moe_quantize_fp8(x, q, scale, stream=None, fmt="e4m3"):
+    """Row-wise fp8 quantisation ("e4m3" or "e5m2") of x [rows, cols] (bf16 or fp32) into q (uint8) and
+    scale (fp32)."""
     dt = L.MOE_BF16 if x.dtype == torch.bfloat16 else L.MOE_F32
     rows, cols = x.shape[0], x.numel() // max(x.shape[0], 1)
-    _check(L.load().moe_quantize_fp8(rows, cols, dt, _p(x), _p(q), _p(scale), _stream(stream)), "moe_quantize_fp8")
+    _check(L.load().moe_quantize_fp8(rows, cols, dt, L.FP8_FORMATS[fmt], _p(x), _p(q), _p(scale), _stream(stream)),
+           "moe_quantize_fp8")
 
 
 def moe_quantize_fp8_transposed(w, q, scale, stream=None):
@@ -224,8 +228,10 @@ def moe_quantize_fp8_tensorwise(x, q, scale, ws=None, stream=None):
 
 
 def moe_grouped_gemm_fp8(epilogue, G, M_total, N, K, group_offsets, A, a_scale, B, b_scale, C, aux=None,
-                         stream=None):
-    _check(L.load().moe_grouped_gemm_fp8(EPILOGUES[epilogue], G, M_total, N, K, _p(group_offsets), _p(A),
+                         stream=None, a_fmt="e4m3"):
+    """a_fmt: the format of A's codes ("e4m3", or "e5m2" with the "none" / "dswiglu" epilogues)."""
+    _check(L.load().moe_grouped_gemm_fp8(EPILOGUES[epilogue], L.FP8_FORMATS[a_fmt], G, M_total, N, K,
+                                         _p(group_offsets), _p(A),
                                          _p(a_scale), _p(B), _p(b_scale), _p(C), _p(aux), _stream(stream)),
            "moe_grouped_gemm_fp8")
 

@@ -617,7 +617,7 @@ int moe_forward_no_workspace(const moe_desc_t* d, const moe_weights_t* w, const 
 
 // The backward pass of moe_backward (w8 NULL) or moe_backward_fp8.
 static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
-                         const void* x, const moe_saved_t* sv, const void* dy, void* dx,
+                         int grad_format, const void* x, const moe_saved_t* sv, const void* dy, void* dx,
                          const moe_grads_t* g, const moe_router_terms_t* terms, float* losses,
                          void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(d);
@@ -636,6 +636,8 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   const int64_t f = d->d_ff, F = shared_width(d), A = T * k;
   const int dt = d->dtype;
   const bool fp8 = w8 != nullptr;
+  if (grad_format != MOE_E4M3 && grad_format != MOE_E5M2) return MOE_ERR_INVALID;
+  const int gf = grad_format == MOE_E5M2 ? FP8_E5M2 : FP8_E4M3;
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
   if (!g->d_w_router || !g->d_w_gateup || !g->d_w_down) return MOE_ERR_INVALID;
   if (F > 0 && (!w->s_gateup || !w->s_down || !g->d_s_gateup || !g->d_s_down))
@@ -678,7 +680,7 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
     MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd_fp8(dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
                                                             d->score, d->renorm, (int)T, (int)D, (int)E, (int)k,
                                                             bw.dy_perm, bw.dlogits, bw.q, bw.qs, bw.q_dy, bw.qs_dy,
-                                                            st));
+                                                            st, gf));
   } else {
     MOE_STAGE(MOE_STAGE_COMBINE_BWD, launch_combine_bwd(dt, dy, sv->y_perm, sv->gate, sv->pos, sv->idx, sv->logits,
                                d->score, d->renorm, (int)T, (int)D, (int)E, (int)k, bw.dy_perm,
@@ -699,9 +701,10 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   // 2. down data gradient fused with the SwiGLU derivative -> dG | dU (fp8:
   // dY~ in e4m3 per row against W_d quantised along d, stored transposed)
   if (fp8) {
-    if (!fused_q) MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dy_perm, dt, A, (int)D, bw.q, bw.qs, st));
+    if (!fused_q)
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dy_perm, dt, A, (int)D, bw.q, bw.qs, st, gf));
     MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_gemm_fp8(MOE_EPI_DSWIGLU, E, A, f, D, sv->offsets, bw.q, bw.qs,
-                                                    w8->down_tq, w8->down_ts, bw.dgu, sv->preact, nullptr, st));
+                                                    w8->down_tq, w8->down_ts, bw.dgu, sv->preact, nullptr, st, gf));
   } else {
     MOE_STAGE(MOE_STAGE_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, E, A, D, f,
                                    sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
@@ -720,9 +723,10 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   // fp8: dG | dU in e4m3 per row against W_gu quantised along 2f, transposed)
   void* dx_perm = bw.dy_perm;
   if (fp8) {
-    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dgu, dt, A, (int)(2 * f), bw.q, bw.qs, st));
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.dgu, dt, A, (int)(2 * f), bw.q, bw.qs, st, gf));
     MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_gemm_fp8(MOE_EPI_NONE, E, A, D, 2 * f, sv->offsets, bw.q, bw.qs,
-                                                       w8->gateup_tq, w8->gateup_ts, dx_perm, nullptr, nullptr, st));
+                                                       w8->gateup_tq, w8->gateup_ts, dx_perm, nullptr, nullptr, st,
+                                                       gf));
   } else {
     MOE_STAGE(MOE_STAGE_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D,
                                    sv->offsets, bw.dgu, w->w_gateup, dx_perm, nullptr),
@@ -731,10 +735,11 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   // 6. shared experts
   if (F > 0) {
     if (fp8) {
-      if (!fused_q) MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q_dy, bw.qs_dy, st));
+      if (!fused_q)
+        MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q_dy, bw.qs_dy, st, gf));
       MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD,
                 launch_gemm_fp8(MOE_EPI_DSWIGLU, 1, T, F, D, nullptr, bw.q_dy, bw.qs_dy, w8->s_down_tq,
-                                w8->s_down_ts, bw.s_dgu, sv->s_preact, nullptr, st));
+                                w8->s_down_ts, bw.s_dgu, sv->s_preact, nullptr, st, gf));
     } else {
       MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
                                      nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
@@ -747,10 +752,10 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
                                    nullptr, bw.s_dgu, x, g->d_s_gateup, nullptr),
                                 bw.gemm, bw.gemm_bytes, st));
     if (fp8) {
-      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.s_dgu, dt, T, (int)(2 * F), bw.q, bw.qs, st));
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.s_dgu, dt, T, (int)(2 * F), bw.q, bw.qs, st, gf));
       MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD,
                 launch_gemm_fp8(MOE_EPI_NONE, 1, T, D, 2 * F, nullptr, bw.q, bw.qs, w8->s_gateup_tq,
-                                w8->s_gateup_ts, bw.dx_shared, nullptr, nullptr, st));
+                                w8->s_gateup_ts, bw.dx_shared, nullptr, nullptr, st, gf));
     } else {
       MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
                                      nullptr, bw.s_dgu, w->s_gateup, bw.dx_shared, nullptr),
@@ -775,15 +780,15 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
                  const moe_saved_t* sv, const void* dy, void* dx, const moe_grads_t* g,
                  const moe_router_terms_t* terms, float* losses, void* ws, size_t ws_bytes,
                  void* stream) {
-  return backward_impl(d, w, nullptr, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
+  return backward_impl(d, w, nullptr, MOE_E4M3, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
 }
 
 int moe_backward_fp8(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
-                     const void* x, const moe_saved_t* sv, const void* dy, void* dx,
+                     int grad_format, const void* x, const moe_saved_t* sv, const void* dy, void* dx,
                      const moe_grads_t* g, const moe_router_terms_t* terms, float* losses, void* ws,
                      size_t ws_bytes, void* stream) {
   if (!w8) return MOE_ERR_INVALID;
-  return backward_impl(d, w, w8, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
+  return backward_impl(d, w, w8, grad_format, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
 }
 
 int moe_fp8_weights_quantize(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
@@ -829,14 +834,16 @@ int moe_fp8_weights_quantize(const moe_desc_t* d, const moe_weights_t* w, const 
   return MOE_OK;
 }
 
-int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, const void* x, uint8_t* q, float* scale,
-                     void* stream) {
+int moe_quantize_fp8(int64_t rows, int64_t cols, int dtype, int format, const void* x, uint8_t* q,
+                     float* scale, void* stream) {
   if (rows < 0 || cols <= 0 || cols % 64 || cols > (int64_t(1) << 24)) return MOE_ERR_INVALID;
   if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (format != MOE_E4M3 && format != MOE_E5M2) return MOE_ERR_INVALID;
   if (rows == 0) return MOE_OK;
   if (!x || !q || !scale) return MOE_ERR_INVALID;
   if (!aligned16(x) || !aligned16(q) || !aligned16(scale)) return MOE_ERR_ALIGN;
-  MOE_TRY(launch_quantize_fp8(x, dtype, rows, (int)cols, q, scale, (hipStream_t)stream));
+  MOE_TRY(launch_quantize_fp8(x, dtype, rows, (int)cols, q, scale, (hipStream_t)stream,
+                              format == MOE_E5M2 ? FP8_E5M2 : FP8_E4M3));
   return MOE_OK;
 }
 
@@ -869,10 +876,13 @@ int moe_quantize_fp8_tensorwise(int64_t rows, int64_t cols, int dtype, const voi
   return MOE_OK;
 }
 
-int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
+int moe_grouped_gemm_fp8(int epi, int a_format, int64_t G, int64_t M, int64_t N, int64_t K,
                          const int32_t* offsets, const uint8_t* A, const float* a_scale,
                          const uint8_t* B, const float* b_scale, void* C, void* aux, void* stream) {
   if (epi != MOE_EPI_NONE && epi != MOE_EPI_SWIGLU && epi != MOE_EPI_DSWIGLU) return MOE_ERR_INVALID;
+  if (a_format != MOE_E4M3 && a_format != MOE_E5M2) return MOE_ERR_INVALID;
+  // e5m2 codes are the gradient operand of a data gradient: no SwiGLU epilogue
+  if (a_format == MOE_E5M2 && epi == MOE_EPI_SWIGLU) return MOE_ERR_UNSUPPORTED;
   if (G < 1 || G > 256 || M < 0 || N <= 0 || K <= 0 || N % 64 || K % 64) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_DSWIGLU && M > 0 && !aux) return MOE_ERR_INVALID;
   if (epi == MOE_EPI_SWIGLU && (N / 2) % 128) return MOE_ERR_INVALID;
@@ -884,7 +894,7 @@ int moe_grouped_gemm_fp8(int epi, int64_t G, int64_t M, int64_t N, int64_t K,
     if (!aligned16(p)) return MOE_ERR_ALIGN;
   if (M == 0) return MOE_OK;
   MOE_TRY(launch_gemm_fp8(epi, G, M, N, K, offsets, A, a_scale, B, b_scale, C, aux, nullptr,
-                          (hipStream_t)stream));
+                          (hipStream_t)stream, a_format == MOE_E5M2 ? FP8_E5M2 : FP8_E4M3));
   return MOE_OK;
 }
 

@@ -157,7 +157,7 @@ MOE_DEV float bf16_round(float v) { return bf16_lo(pack_bf16x2(v, 0.0f)); }
 // largest magnitude is bf16(gate * max|dy[t]|) exactly (rounding is monotone
 // and symmetric), so a first pass over dy[t] gives every slot's scale before
 // the rows are formed.
-template <typename T, int KK, bool Q8 = false>
+template <typename T, int KK, bool Q8 = false, int QF = FP8_E4M3>
 __global__ __launch_bounds__(256) void combine_bwd_kernel(
     const T* __restrict__ dy, const T* __restrict__ y_perm, const float* __restrict__ gate,
     const int32_t* __restrict__ pos, const int32_t* __restrict__ idx,
@@ -183,9 +183,9 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
     }
     if constexpr (Q8) {
       const float amax = bf16_row_amax((const bf16_t*)dy + (int64_t)t * d, nvec, lane);
-      s_dy = fp8_row_scale(amax);
+      s_dy = fp8_row_scale<QF>(amax);
 #pragma unroll
-      for (int j = 0; j < KK; ++j) sq[j] = fp8_row_scale(bf16_round(g[j] * amax));
+      for (int j = 0; j < KK; ++j) sq[j] = fp8_row_scale<QF>(bf16_round(g[j] * amax));
       if (lane == 0) {
         q8.s_dy[t] = s_dy;
 #pragma unroll
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
           float dv[VN];
           Vec<T>::unpack(dr[i], dv);
           if constexpr (Q8)
-            *reinterpret_cast<u32x2*>(q8.q_dy + (int64_t)t * d + (int64_t)c * VN) = fp8_encode8(dv, s_dy);
+            *reinterpret_cast<u32x2*>(q8.q_dy + (int64_t)t * d + (int64_t)c * VN) = fp8_encode8<QF>(dv, s_dy);
 #pragma unroll
           for (int j = 0; j < KK; ++j) {
             float v[VN], o[VN];
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void combine_bwd_kernel(
               float b[VN];
 #pragma unroll
               for (int u = 0; u < VN; ++u) b[u] = bf16_round(o[u]);
-              *reinterpret_cast<u32x2*>(q8.q_perm + row[j] + (int64_t)c * VN) = fp8_encode8(b, sq[j]);
+              *reinterpret_cast<u32x2*>(q8.q_perm + row[j] + (int64_t)c * VN) = fp8_encode8<QF>(b, sq[j]);
             }
           }
         }
@@ -493,20 +493,27 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, con
 hipError_t launch_combine_bwd_fp8(const void* dy, const void* y_perm, const float* gate, const int32_t* pos,
                                   const int32_t* idx, const float* logits, int score, int renorm, int T, int d,
                                   int E, int k, void* dy_perm, float* dlogits, uint8_t* q_perm, float* s_perm,
-                                  uint8_t* q_dy, float* s_dy, hipStream_t st) {
+                                  uint8_t* q_dy, float* s_dy, hipStream_t st, int fmt) {
   if (T == 0) return hipSuccess;
   if (k < 1 || k > 8) return hipErrorInvalidValue;
   dim3 grid((unsigned)cdiv64(T, 4)), block(256);
   const Fp8Rows q{q_perm, s_perm, q_dy, s_dy};
-#define MOE_Q8_CASE(K)                                                                                         \
-  case K:                                                                                                      \
-    combine_bwd_kernel<bf16_t, K, true><<<grid, block, 0, st>>>((const bf16_t*)dy, (const bf16_t*)y_perm, gate,   \
-                                                                pos, idx, logits, score, renorm, T, d, E, k,     \
-                                                                (bf16_t*)dy_perm, dlogits, q);                  \
+#define MOE_Q8_CASE(K, F)                                                                                        \
+  case K:                                                                                                        \
+    combine_bwd_kernel<bf16_t, K, true, F><<<grid, block, 0, st>>>((const bf16_t*)dy, (const bf16_t*)y_perm, gate, \
+                                                                   pos, idx, logits, score, renorm, T, d, E, k,    \
+                                                                   (bf16_t*)dy_perm, dlogits, q);                 \
     break;
-  switch (k) {
-    MOE_Q8_CASE(1) MOE_Q8_CASE(2) MOE_Q8_CASE(3) MOE_Q8_CASE(4)
-    MOE_Q8_CASE(5) MOE_Q8_CASE(6) MOE_Q8_CASE(7) MOE_Q8_CASE(8)
+  if (fmt == FP8_E5M2) {
+    switch (k) {
+      MOE_Q8_CASE(1, FP8_E5M2) MOE_Q8_CASE(2, FP8_E5M2) MOE_Q8_CASE(3, FP8_E5M2) MOE_Q8_CASE(4, FP8_E5M2)
+      MOE_Q8_CASE(5, FP8_E5M2) MOE_Q8_CASE(6, FP8_E5M2) MOE_Q8_CASE(7, FP8_E5M2) MOE_Q8_CASE(8, FP8_E5M2)
+    }
+  } else {
+    switch (k) {
+      MOE_Q8_CASE(1, FP8_E4M3) MOE_Q8_CASE(2, FP8_E4M3) MOE_Q8_CASE(3, FP8_E4M3) MOE_Q8_CASE(4, FP8_E4M3)
+      MOE_Q8_CASE(5, FP8_E4M3) MOE_Q8_CASE(6, FP8_E4M3) MOE_Q8_CASE(7, FP8_E4M3) MOE_Q8_CASE(8, FP8_E4M3)
+    }
   }
 #undef MOE_Q8_CASE
   return hipGetLastError();

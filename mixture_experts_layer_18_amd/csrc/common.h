@@ -51,19 +51,36 @@ MOE_DEV float silu_f(float z) { return z * sigmoid_f(z); }
 
 // Sum over the 64 lanes of a wavefront, identical result in every lane.
 // The butterfly order is fixed, so the result is deterministic.
-// Row-wise e4m3 quantisation of 8 values with the row's scale s: each
-// quotient f / s in IEEE fp32, clamped to +-448 (the conversion turns values
-// beyond 464 into NaN), rounded to nearest even by v_cvt_pk_fp8_f32.
-MOE_DEV float fp8_row_scale(float amax) { return amax > 0.0f ? amax / 448.0f : 1.0f; }
+// fp8 formats of the quantised operands: OCP e4m3 (largest finite 448) and
+// e5m2 (largest finite 57344)
+enum { FP8_E4M3 = 0, FP8_E5M2 = 1 };
+template <int FMT>
+MOE_DEV constexpr float fp8_max() { return FMT == FP8_E5M2 ? 57344.0f : 448.0f; }
+
+// Row-wise quantisation of 8 values with the row's scale s: each quotient
+// f / s in IEEE fp32, clamped to the format's largest finite value (the
+// conversions turn larger values into NaN or infinity), rounded to nearest
+// even by v_cvt_pk_fp8_f32 / v_cvt_pk_bf8_f32.
+template <int FMT = FP8_E4M3>
+MOE_DEV float fp8_row_scale(float amax) { return amax > 0.0f ? amax / fp8_max<FMT>() : 1.0f; }
+template <int FMT = FP8_E4M3>
 MOE_DEV u32x2 fp8_encode8(const float* f, float s) {
+  constexpr float M = fp8_max<FMT>();
   float v[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) v[u] = fminf(fmaxf(f[u] / s, -448.0f), 448.0f);
+  for (int u = 0; u < 8; ++u) v[u] = fminf(fmaxf(f[u] / s, -M), M);
   u32x2 o;
-  o.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-  o.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], o.x, true);
-  o.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
-  o.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], o.y, true);
+  if constexpr (FMT == FP8_E5M2) {
+    o.x = __builtin_amdgcn_cvt_pk_bf8_f32(v[0], v[1], 0, false);
+    o.x = __builtin_amdgcn_cvt_pk_bf8_f32(v[2], v[3], o.x, true);
+    o.y = __builtin_amdgcn_cvt_pk_bf8_f32(v[4], v[5], 0, false);
+    o.y = __builtin_amdgcn_cvt_pk_bf8_f32(v[6], v[7], o.y, true);
+  } else {
+    o.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    o.x = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], o.x, true);
+    o.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[4], v[5], 0, false);
+    o.y = __builtin_amdgcn_cvt_pk_fp8_f32(v[6], v[7], o.y, true);
+  }
   return o;
 }
 

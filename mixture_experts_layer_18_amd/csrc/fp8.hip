@@ -49,25 +49,25 @@ MOE_DEV float row_amax(const TX* row, int C, int lane) {
 
 MOE_DEV float scale_of(float amax) { return fp8_row_scale(amax); }
 
-// q = e4m3(clamp(x / s)) for one row
-template <typename TX>
+// q = fmt(clamp(x / s)) for one row
+template <typename TX, int FMT = FP8_E4M3>
 MOE_DEV void encode_row(const TX* row, int C, float s, uint8_t* qrow, int lane) {
   for (int c = lane * V; c < C; c += 64 * V) {
     float f[V];
     load8(row, c, f);
-    *reinterpret_cast<u32x2*>(qrow + c) = fp8_encode8(f, s);
+    *reinterpret_cast<u32x2*>(qrow + c) = fp8_encode8<FMT>(f, s);
   }
 }
 
-template <typename TX>
+template <typename TX, int FMT>
 __global__ __launch_bounds__(256) void rowwise_kernel(const TX* __restrict__ x, int64_t R, int C,
                                                       uint8_t* __restrict__ q, float* __restrict__ scale) {
   const int lane = threadIdx.x & 63;
   const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= R) return;
-  const float s = scale_of(row_amax(x + r * C, C, lane));
+  const float s = fp8_row_scale<FMT>(row_amax(x + r * C, C, lane));
   if (lane == 0) scale[r] = s;
-  encode_row(x + r * C, C, s, q + r * C, lane);
+  encode_row<TX, FMT>(x + r * C, C, s, q + r * C, lane);
 }
 
 // tensor-wise, pass 1: the maximum of each row
@@ -204,13 +204,20 @@ hipError_t launch_quantize_fp8_transposed(const void* x, int dtype, int64_t G, i
 }
 
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,
-                               hipStream_t st) {
+                               hipStream_t st, int fmt) {
   if (R == 0) return hipSuccess;
   const dim3 grid((unsigned)cdiv64(R, 4));
-  if (dtype == MOE_BF16)
-    q8::rowwise_kernel<bf16_t><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, q, scale);
-  else
-    q8::rowwise_kernel<float><<<grid, 256, 0, st>>>((const float*)x, R, C, q, scale);
+  if (fmt == FP8_E5M2) {
+    if (dtype == MOE_BF16)
+      q8::rowwise_kernel<bf16_t, FP8_E5M2><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, q, scale);
+    else
+      q8::rowwise_kernel<float, FP8_E5M2><<<grid, 256, 0, st>>>((const float*)x, R, C, q, scale);
+  } else {
+    if (dtype == MOE_BF16)
+      q8::rowwise_kernel<bf16_t, FP8_E4M3><<<grid, 256, 0, st>>>((const bf16_t*)x, R, C, q, scale);
+    else
+      q8::rowwise_kernel<float, FP8_E4M3><<<grid, 256, 0, st>>>((const float*)x, R, C, q, scale);
+  }
   return hipGetLastError();
 }
 

@@ -125,7 +125,10 @@ struct Tile {
 // matrix-core product per 32x32 tile: the f8f6f4 builtin with zero scale
 // operands, which the compiler emits as the unscaled
 // v_mfma_f32_32x32x64_f8f6f4 (one instruction, no scale prefix).
-template <int LAYOUT, int EPI, bool F8, bool GA, int NWV>
+// PF: the format of A's codes (P operand) in the fp8 products, FP8_E4M3 or
+// FP8_E5M2 (the matrix cores take the operand formats as instruction fields);
+// B's codes are e4m3.
+template <int LAYOUT, int EPI, bool F8, bool GA, int NWV, int PF = FP8_E4M3>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   using WV = Waves<NWV>;
   constexpr int NW = WV::NW, WM = WV::WM, WN = WV::WN, WPR = WV::WPR, FI = WV::FI, FJ = WV::FJ;
@@ -447,8 +450,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         for (int it = 0; it < FH; ++it)
 #pragma unroll
           for (int jt = 0; jt < FJ; ++jt)
-            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], 0, 0, 0,
-                                                                          0, 0, 0);
+            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], FP8_E4M3,
+                                                                          PF, 0, 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
         // k-step kt+1 landed for this wave; after the barrier every wave has
         // it and none reads stage kt from LDS any more
@@ -467,7 +470,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
         for (int q = 0; q < LT; ++q) {
           const int it = q / FJ, jt = q % FJ;
           acc[FH + it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              Q[jt], P2[it], acc[FH + it][jt], 0, 0, 0, 0, 0, 0);
+              Q[jt], P2[it], acc[FH + it][jt], FP8_E4M3, PF, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, aoff);
           else dma4_pad(Ab, pad_lds + q * 256);
@@ -789,10 +792,10 @@ static int grid_size() {
 
 // waves per workgroup (Waves<4> is the one-wave-per-SIMD layout it replaced)
 constexpr int kWaves = 8;
-template <int LAYOUT, int EPI, bool F8 = false, bool GA = false, int NWV = kWaves>
+template <int LAYOUT, int EPI, bool F8 = false, bool GA = false, int NWV = kWaves, int PF = FP8_E4M3>
 static hipError_t run(const Args& a, hipStream_t st) {
   if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI, F8, GA, NWV><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, F8, GA, NWV, PF><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a);
   return hipGetLastError();
 }
 
@@ -874,7 +877,7 @@ namespace moe {
 hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,
                            const uint8_t* B, const float* b_scale, void* C, void* aux,
-                           const int32_t* rows, hipStream_t st) {
+                           const int32_t* rows, hipStream_t st, int a_fmt) {
   pk::Args a;
   a.G = (int)G;
   a.M_total = M_total;
@@ -888,6 +891,14 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
   a.a_scale = a_scale;
   a.b_scale = b_scale;
   a.rows = rows;
+  if (a_fmt == FP8_E5M2) {
+    // e5m2 A codes: the data gradients' gradient operands
+    if (rows) return hipErrorInvalidValue;
+    if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true, false, pk::kWaves, FP8_E5M2>(a, st);
+    if (epilogue == MOE_EPI_DSWIGLU)
+      return pk::run<MOE_GEMM_NT, MOE_EPI_DSWIGLU, true, false, pk::kWaves, FP8_E5M2>(a, st);
+    return hipErrorInvalidValue;
+  }
   if (rows) {
     if (epilogue == MOE_EPI_NONE) return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, true, true>(a, st);
     if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true, true>(a, st);

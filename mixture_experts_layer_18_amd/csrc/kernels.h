@@ -43,11 +43,12 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st);
 hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,
                            const uint8_t* B, const float* b_scale, void* C, void* aux,
-                           const int32_t* rows, hipStream_t st);
+                           const int32_t* rows, hipStream_t st, int a_fmt = FP8_E4M3);
 hipError_t launch_quantize_fp8_transposed(const void* x, int dtype, int64_t G, int64_t R, int64_t C,
                                           uint8_t* q, float* scale, hipStream_t st);
+// row-wise quantisation; fmt FP8_E4M3 or FP8_E5M2
 hipError_t launch_quantize_fp8(const void* x, int dtype, int64_t R, int C, uint8_t* q, float* scale,
-                               hipStream_t st);
+                               hipStream_t st, int fmt = FP8_E4M3);
 size_t quantize_fp8_tensorwise_ws_bytes(int64_t R);
 hipError_t launch_quantize_fp8_tensorwise(const void* x, int dtype, int64_t R, int C, uint8_t* q,
                                           float* scale, float* ws, hipStream_t st);
@@ -96,7 +97,7 @@ hipError_t launch_combine_bwd(int dtype, const void* dy, const void* y_perm, con
 hipError_t launch_combine_bwd_fp8(const void* dy, const void* y_perm, const float* gate, const int32_t* pos,
                                   const int32_t* idx, const float* logits, int score, int renorm, int T, int d,
                                   int E, int k, void* dy_perm, float* dlogits, uint8_t* q_perm, float* s_perm,
-                                  uint8_t* q_dy, float* s_dy, hipStream_t st);
+                                  uint8_t* q_dy, float* s_dy, hipStream_t st, int fmt = FP8_E4M3);
 hipError_t launch_unpermute_sum(int dtype, const void* dx_perm, const int32_t* pos,
                                 const void* dx_shared, const float* dlogits, const int32_t* idx,
                                 const float* w_router, int dense_router, int T, int d, int E,

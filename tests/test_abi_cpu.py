@@ -229,10 +229,13 @@ def test_router_terms_and_bias_update_argument_checks(lib):
 def test_fp8_argument_checks(lib):
     a = ctypes.c_void_p(1 << 20)
     # quantize: columns not a multiple of 64, bad dtype, misaligned, zero rows
-    assert lib.moe_quantize_fp8(10, 100, L.MOE_BF16, a, a, a, None) == L.MOE_ERR_INVALID
-    assert lib.moe_quantize_fp8(10, 128, 7, a, a, a, None) == L.MOE_ERR_INVALID
-    assert lib.moe_quantize_fp8(10, 128, L.MOE_BF16, ctypes.c_void_p((1 << 20) + 2), a, a, None) == L.MOE_ERR_ALIGN
-    assert lib.moe_quantize_fp8(0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
+    E4, E5 = L.MOE_E4M3, L.MOE_E5M2
+    assert lib.moe_quantize_fp8(10, 100, L.MOE_BF16, E4, a, a, a, None) == L.MOE_ERR_INVALID
+    assert lib.moe_quantize_fp8(10, 128, 7, E4, a, a, a, None) == L.MOE_ERR_INVALID
+    assert lib.moe_quantize_fp8(10, 128, L.MOE_BF16, 2, a, a, a, None) == L.MOE_ERR_INVALID   # no such format
+    assert lib.moe_quantize_fp8(10, 128, L.MOE_BF16, E5, ctypes.c_void_p((1 << 20) + 2), a, a, None) == \
+        L.MOE_ERR_ALIGN
+    assert lib.moe_quantize_fp8(0, 128, L.MOE_BF16, E5, None, None, None, None) == L.MOE_OK
     # tensor-wise: the same checks, and the scratch size (row maxima + scale)
     tw = lib.moe_quantize_fp8_tensorwise
     assert lib.moe_quantize_fp8_tensorwise_workspace_bytes(10) == 44
@@ -253,15 +256,17 @@ def test_fp8_argument_checks(lib):
     assert tq(3, 0, 128, L.MOE_BF16, None, None, None, None) == L.MOE_OK
     # gemm: layout limits
     args = (a, a, a, a, a, a, None, None)
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_DSWIGLU, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID  # no aux
-    assert lib.moe_grouped_gemm_fp8(3, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 0, 100, 256, 128, *args) == L.MOE_ERR_INVALID
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 100, 256, 96, *args) == L.MOE_ERR_INVALID
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_SWIGLU, 4, 100, 384, 128, *args) == L.MOE_ERR_INVALID
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 100, 256, 128, a, a, a, a, a,
-                                    ctypes.c_void_p((1 << 20) + 4), None, None) == L.MOE_ERR_ALIGN
-    assert lib.moe_grouped_gemm_fp8(L.MOE_EPI_NONE, 4, 0, 256, 128, a, None, None, None, None, None, None,
-                                    None) == L.MOE_OK
+    gf = lib.moe_grouped_gemm_fp8
+    assert gf(L.MOE_EPI_DSWIGLU, E4, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID  # no aux
+    assert gf(3, E4, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID
+    assert gf(L.MOE_EPI_NONE, E4, 0, 100, 256, 128, *args) == L.MOE_ERR_INVALID
+    assert gf(L.MOE_EPI_NONE, E4, 4, 100, 256, 96, *args) == L.MOE_ERR_INVALID
+    assert gf(L.MOE_EPI_SWIGLU, E4, 4, 100, 384, 128, *args) == L.MOE_ERR_INVALID
+    assert gf(L.MOE_EPI_NONE, 2, 4, 100, 256, 128, *args) == L.MOE_ERR_INVALID       # no such format
+    assert gf(L.MOE_EPI_SWIGLU, E5, 4, 100, 512, 128, *args) == L.MOE_ERR_UNSUPPORTED  # e5m2: data gradients
+    assert gf(L.MOE_EPI_NONE, E4, 4, 100, 256, 128, a, a, a, a, a, ctypes.c_void_p((1 << 20) + 4), None,
+              None) == L.MOE_ERR_ALIGN
+    assert gf(L.MOE_EPI_NONE, E5, 4, 0, 256, 128, a, None, None, None, None, None, None, None) == L.MOE_OK
 
 
 def test_gather_argument_checks(lib):
@@ -388,9 +393,11 @@ def test_fp8_layer_argument_checks(lib):
     assert fwd(d, ctypes.byref(q2), 1 << 30) == L.MOE_ERR_ALIGN
     # the backward reads the data-gradient copies only
     g = L.MoeGrads(a, a, a, a, a)
-    bwd = lambda qq, nb: lib.moe_backward_fp8(ctypes.byref(d), ctypes.byref(w), qq, a, ctypes.byref(s), a, a,  # noqa: E731
-                                              ctypes.byref(g), None, None, a, nb, None)
+    bwd = lambda qq, nb, fmt=L.MOE_E4M3: lib.moe_backward_fp8(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(w), qq, fmt, a, ctypes.byref(s), a, a, ctypes.byref(g), None, None, a, nb, None)
     assert bwd(ctypes.byref(q), 16) == L.MOE_ERR_WORKSPACE
+    assert bwd(ctypes.byref(q), 16, L.MOE_E5M2) == L.MOE_ERR_WORKSPACE
+    assert bwd(ctypes.byref(q), 1 << 30, 3) == L.MOE_ERR_INVALID
     assert bwd(None, 1 << 30) == L.MOE_ERR_INVALID
     q3 = L.MoeFp8Weights(*([a] * 16))
     q3.s_down_tq = None

@@ -224,3 +224,67 @@ def test_fp8_down_data_gradient_dswiglu_against_oracle():
     sg = 1.0 / (1.0 + np.exp(-Gm))
     inherited = np.concatenate([np.abs(U * sg * (1.0 + Gm * (1.0 - sg))), np.abs(O.silu(Gm))], axis=1) * e
     assert_rounded(host(C), np.concatenate([dG, dU], axis=1), "bf16", "dG | dU", extra=inherited)
+
+
+def test_quantize_e5m2_bit_exact():
+    """Row-wise e5m2 codes and scales equal the oracle's bit for bit (an
+    all-zero row, extreme values, bf16 and fp32 inputs)."""
+    g = np.random.default_rng(46)
+    xf = (g.standard_normal((260, 384)) * np.exp(g.uniform(-6, 6, (260, 1)))).astype(np.float32)
+    xf[3] = 0.0
+    xf[4, :4] = np.array([1e-30, -6e4, 3.0, -2e-20], np.float32)
+    xb = synth.f32_to_bf16_bits(xf)
+    for x, ref_in in ((dev(xb), synth.bf16_bits_to_f32(xb)), (torch.from_numpy(xf).cuda(), xf)):
+        q = torch.empty(x.shape[0], x.shape[1], dtype=torch.uint8, device="cuda")
+        s = torch.empty(x.shape[0], dtype=torch.float32, device="cuda")
+        M.moe_quantize_fp8(x, q, s, fmt="e5m2")
+        torch.cuda.synchronize()
+        qo, so = O.quantize_rowwise(ref_in, "e5m2")
+        assert np.array_equal(s.cpu().numpy(), so)
+        assert np.array_equal(q.cpu().numpy(), qo)
+
+
+@pytest.mark.parametrize("epi", ["none", "dswiglu"])
+def test_grouped_gemm_e5m2_gradient_operand(epi):
+    """The fp8 product with e5m2 codes for A (a gradient) and e4m3 for B (a
+    weight quantised along its reduction dimension, stored transposed): the
+    gate/up data gradient (plain) and the down data gradient with the
+    dSwiGLU epilogue, ragged groups and an empty one, against the oracle's
+    product of the same codes."""
+    g = np.random.default_rng(47)
+    G, N, K = 4, 256, 384
+    m = g.integers(30, 260, size=G)
+    m[2] = 0
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(m)
+    Mt = int(off[-1])
+    ab = _bf16(g, (Mt, K), 0.05)
+    wb = _bf16(g, (G, K, N), 1 / np.sqrt(K))          # W [G, K(reduction), N], quantised along K
+    qa = torch.empty(Mt, K, dtype=torch.uint8, device="cuda")
+    sa = torch.empty(Mt, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8(dev(ab), qa, sa, fmt="e5m2")
+    qw = torch.empty(G, N, K, dtype=torch.uint8, device="cuda")
+    sw = torch.empty(G, N, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_transposed(dev(wb), qw, sw)
+    qao, sao = O.quantize_rowwise(synth.bf16_bits_to_f32(ab), "e5m2")
+    qwo, swo = O.quantize_rowwise_transposed(synth.bf16_bits_to_f32(wb))
+    ref = O.grouped_gemm_fp8_nt(qao, sao, qwo, swo, off, "e5m2")
+    print(f"[fp8] e5m2 A, {epi}: G={G} M={Mt} N={N} K={K}", flush=True)
+    if epi == "none":
+        C = torch.empty(Mt, N, dtype=torch.bfloat16, device="cuda")
+        M.moe_grouped_gemm_fp8("none", G, Mt, N, K, dev(off), qa, sa, qw, sw, C, a_fmt="e5m2")
+        torch.cuda.synchronize()
+        assert_rounded(host(C), ref, "bf16", "C")
+    else:
+        preb = _bf16(g, (Mt, 2 * N))
+        C = torch.empty(Mt, 2 * N, dtype=torch.bfloat16, device="cuda")
+        M.moe_grouped_gemm_fp8("dswiglu", G, Mt, N, K, dev(off), qa, sa, qw, sw, C, dev(preb), a_fmt="e5m2")
+        torch.cuda.synchronize()
+        pre = synth.bf16_bits_to_f32(preb).astype(np.float64)
+        Gm, U = pre[:, :N], pre[:, N:]
+        sg = 1.0 / (1.0 + np.exp(-Gm))
+        dG = ref * U * sg * (1.0 + Gm * (1.0 - sg))
+        dU = ref * Gm * sg
+        e = 1e-4 * np.sqrt(np.mean(ref * ref))
+        inherited = np.concatenate([np.abs(U * sg * (1.0 + Gm * (1.0 - sg))), np.abs(O.silu(Gm))], axis=1) * e
+        assert_rounded(host(C), np.concatenate([dG, dU], axis=1), "bf16", "dG | dU", extra=inherited)

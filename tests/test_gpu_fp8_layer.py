@@ -161,7 +161,7 @@ def _dswiglu_noise(dh_rms, pre, F):
     return np.concatenate([np.abs(U * sg * (1.0 + Gm * (1.0 - sg))), np.abs(O.silu(Gm))], axis=1) * e
 
 
-def _gpu_dgu(cfg, sv, w8, dy):
+def _gpu_dgu(cfg, sv, w8, dy, fmt="e4m3"):
     """dG | dU as moe_backward_fp8 forms them, from the same kernels through
     the public calls: the gate-weighted rows dY~ = bf16(gate * dy) (one fp32
     product, rounded to nearest even), their row-wise e4m3 copy, and the fp8
@@ -174,33 +174,36 @@ def _gpu_dgu(cfg, sv, w8, dy):
     dyp = (sv["gate"].reshape(-1)[src].unsqueeze(1) * dy.float()[src // k]).to(torch.bfloat16)
     q = torch.empty(A, d, dtype=torch.uint8, device="cuda")
     qs = torch.empty(A, dtype=torch.float32, device="cuda")
-    M.moe_quantize_fp8(dyp, q, qs)
+    M.moe_quantize_fp8(dyp, q, qs, fmt=fmt)
     dgu = torch.empty(A, 2 * f, dtype=torch.bfloat16, device="cuda")
     M.moe_grouped_gemm_fp8("dswiglu", E, A, f, d, sv["offsets"], q, qs, w8["down_tq"], w8["down_ts"], dgu,
-                           sv["preact"])
+                           sv["preact"], a_fmt=fmt)
     dh = torch.empty(A, f, dtype=torch.bfloat16, device="cuda")
-    M.moe_grouped_gemm_fp8("none", E, A, f, d, sv["offsets"], q, qs, w8["down_tq"], w8["down_ts"], dh)
+    M.moe_grouped_gemm_fp8("none", E, A, f, d, sv["offsets"], q, qs, w8["down_tq"], w8["down_ts"], dh,
+                           a_fmt=fmt)
     rms = [float(dh.float().pow(2).mean().sqrt())]
     s_dgu = None
     if F:
-        M.moe_quantize_fp8(dy, q[:T], qs[:T])
+        M.moe_quantize_fp8(dy, q[:T], qs[:T], fmt=fmt)
         s_dgu = torch.empty(T, 2 * F, dtype=torch.bfloat16, device="cuda")
         M.moe_grouped_gemm_fp8("dswiglu", 1, T, F, d, None, q[:T], qs[:T], w8["s_down_tq"], w8["s_down_ts"], s_dgu,
-                               sv["s_preact"])
+                               sv["s_preact"], a_fmt=fmt)
         sdh = torch.empty(T, F, dtype=torch.bfloat16, device="cuda")
-        M.moe_grouped_gemm_fp8("none", 1, T, F, d, None, q[:T], qs[:T], w8["s_down_tq"], w8["s_down_ts"], sdh)
+        M.moe_grouped_gemm_fp8("none", 1, T, F, d, None, q[:T], qs[:T], w8["s_down_tq"], w8["s_down_ts"], sdh,
+                               a_fmt=fmt)
         rms.append(float(sdh.float().pow(2).mean().sqrt()))
     return dgu, s_dgu, rms
 
 
-def _compare_fp8_layer(cfg, gather):
-    print(f"[fp8 layer] {cfg.name} gather={gather}: inputs", flush=True)
+def _compare_fp8_layer(cfg, gather, grad_format="e4m3"):
+    print(f"[fp8 layer] {cfg.name} gather={gather} gradients {grad_format}: inputs", flush=True)
     inp = synth.make_inputs(cfg, with_dy=True)
     desc = M.desc_from_config(cfg)
     w = R.upload_layer(cfg, inp)
     x, dy = dev(inp["x"]), dev(inp["dy"])
     print(f"[fp8 layer] {cfg.name}: GPU fp8 forward+backward", flush=True)
-    g = R.run_gpu(cfg, inp, backward=True, weights=w, x=x, dy=dy, keep_device=True, gather=gather, fp8=True)
+    g = R.run_gpu(cfg, inp, backward=True, weights=w, x=x, dy=dy, keep_device=True, gather=gather, fp8=True,
+                  grad_format=grad_format)
     sv, w8 = g["saved"], g["w8"]
     g_idx = sv["idx"].cpu().numpy()
     g_gate = sv["gate"].cpu().numpy()
@@ -245,7 +248,7 @@ def _compare_fp8_layer(cfg, gather):
     # by the same kernels through the public calls; the weight gradients that
     # read them show they are the ones moe_backward_fp8 formed (bit for bit)
     print(f"[fp8 layer] {cfg.name}: dG | dU through the public calls", flush=True)
-    dgu, s_dgu, dh_rms = _gpu_dgu(cfg, sv, w8, dy)
+    dgu, s_dgu, dh_rms = _gpu_dgu(cfg, sv, w8, dy, grad_format)
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     A = T * k
     dwg = torch.empty(E, 2 * f, d, dtype=torch.bfloat16, device="cuda")
@@ -269,7 +272,8 @@ def _compare_fp8_layer(cfg, gather):
     print(f"[fp8 layer] {cfg.name}: oracle fp8 backward (stored pre-activations and dG | dU forced)", flush=True)
     fwb = dict(fw, preact=gpre, s_preact=gspre)
     bw = O.backward(oi["x"], oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fwb,
-                    oi["dy"], score=cfg.score, renorm=cfg.renorm, fp8=True, forced_dgu=gdgu, forced_s_dgu=gsdgu)
+                    oi["dy"], score=cfg.score, renorm=cfg.renorm, fp8=True, forced_dgu=gdgu, forced_s_dgu=gsdgu,
+                    fp8_grad_format=grad_format)
     assert_rounded(gdgu, bw["dgu"], "bf16", "dG | dU", extra=_dswiglu_noise(dh_rms[0], gpre, f))
     if F:
         assert_rounded(gsdgu, bw["s_dgu"], "bf16", "shared dG | dU", extra=_dswiglu_noise(dh_rms[1], gspre, F))
@@ -287,6 +291,13 @@ def test_fp8_layer_small_against_oracle(gather):
     shared expert), forward and backward compared in full; with the permuted
     token copy the backward's weight gradient reads it instead of gathering."""
     _compare_fp8_layer(SMALL, gather)
+
+
+def test_fp8_layer_e5m2_gradients_against_oracle():
+    """The small fp8 layer with e5m2 gradient operands (dY~, dG | dU and the
+    shared ones quantised to e5m2, weights e4m3), forward and backward
+    compared in full."""
+    _compare_fp8_layer(SMALL, True, "e5m2")
 
 
 def test_fp8_layer_finegrained_against_oracle():
