@@ -58,7 +58,10 @@ the half-step error bound off it, power-of-two equivariance of the whole
 layer, closeness to the exact layer and the bf16 rounding rule; for the e5m2
 gradient format, its decode table and rounding, brute-force nearest search,
 the row-wise half-step bound and exactness of the down data gradient on the
-e5m2 grid.  Every function below is covered by at least one pin.
+e5m2 grid; for the fp8 weight gradients, exactness on the grid by columns
+(and of every weight gradient of a grid layer), the half-step bound and
+power-of-two equivariance.  Every function below is covered by at least one
+pin.
 """
 from __future__ import annotations
 
@@ -231,6 +234,7 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
     x_perm = x[tok_of_row]
     preact = np.empty((A, 2 * f), F64)
     h = np.empty((A, f), F64)
+    h_q = np.zeros((A, f), F64) if fp8 else None   # the bf16 H the fp8 down products quantised
     y_perm = np.empty((A, d), F64)
     wg_all, wu_all = _split_gateup(np.asarray(w_gateup))
     for e in range(E):
@@ -238,9 +242,10 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
         if r1 == r0:
             continue
         if fp8:
-            G, U, H, Y = swiglu_ffn_fp8(x_perm[r0:r1], np.asarray(wg_all[e], F64),
-                                        np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64),
-                                        None if forced_h is None else forced_h[r0:r1])
+            G, U, H, Y, Hq = swiglu_ffn_fp8(x_perm[r0:r1], np.asarray(wg_all[e], F64),
+                                            np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64),
+                                            None if forced_h is None else forced_h[r0:r1])
+            h_q[r0:r1] = Hq
         else:
             G, U, H, Y = swiglu_ffn(x_perm[r0:r1], np.asarray(wg_all[e], F64),
                                     np.asarray(wu_all[e], F64), np.asarray(w_down[e], F64))
@@ -251,18 +256,19 @@ def forward(x, w_router, bias, w_gateup, w_down, s_gateup=None, s_down=None, *,
 
     out = dict(logits=logits, scores=scores, keys=keys, idx=idx, margin=margin, gate=gate,
                counts=counts, offsets=offsets, pos=pos, src=src, x_perm=x_perm,
-               preact=preact, h=h, y_perm=y_perm)
+               preact=preact, h=h, y_perm=y_perm, h_q=h_q)
 
     if s_gateup is not None:
         sg, su = _split_gateup(np.asarray(s_gateup, F64))
+        Hsq = None
         if fp8:
-            Gs, Us, Hs, ys = swiglu_ffn_fp8(x, sg, su, np.asarray(s_down, F64), forced_s_h)
+            Gs, Us, Hs, ys, Hsq = swiglu_ffn_fp8(x, sg, su, np.asarray(s_down, F64), forced_s_h)
         else:
             Gs, Us, Hs, ys = swiglu_ffn(x, sg, su, np.asarray(s_down, F64))
-        out.update(s_preact=np.concatenate([Gs, Us], axis=1), s_h=Hs, ys=ys)
+        out.update(s_preact=np.concatenate([Gs, Us], axis=1), s_h=Hs, ys=ys, s_h_q=Hsq)
     else:
         ys = np.zeros((T, d), F64)
-        out.update(s_preact=None, s_h=None, ys=None)
+        out.update(s_preact=None, s_h=None, ys=None, s_h_q=None)
 
     out["y"] = combine(y_perm, gate, pos, ys)
     return out
@@ -448,7 +454,8 @@ def bias_update(bias32, counts, T, k, rate):
 
 
 def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score, renorm=False,
-             terms=None, fp8=False, forced_dgu=None, forced_s_dgu=None, fp8_grad_format="e4m3"):
+             terms=None, fp8=False, forced_dgu=None, forced_s_dgu=None, fp8_grad_format="e4m3",
+             fp8_wgrad=False):
     """Backward pass for upstream gradient dy [T, d], reusing ``forward``'s dict.
 
     Returns dict: dx [T,d], d_w_gateup [E,2f,d], d_w_down [E,d,f],
@@ -461,7 +468,10 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
     of dG | dU that the gate/up data gradients quantise (another
     implementation's rounding of the same values); the returned dgu / s_dgu
     are this oracle's own.  ``fp8_grad_format``: "e4m3" or "e5m2" for the
-    gradient operands of the fp8 data gradients (the weights stay e4m3)."""
+    gradient operands of the fp8 data gradients (the weights stay e4m3).
+    ``fp8_wgrad`` (with fp8): the weight gradients are e4m3 products too, of
+    operands quantised along each expert's rows (``wgrad_fp8``), H as the
+    forward's down products quantised it."""
     x = np.asarray(x, F64)
     dy = np.asarray(dy, F64)
     T, d = x.shape
@@ -487,7 +497,8 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
                 np.asarray(w_down[e], F64), G, U, fwd["h"][r0:r1], dy_perm[r0:r1])
         if fp8:
             dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward_fp8(
-                *args, None if forced_dgu is None else forced_dgu[r0:r1], fp8_grad_format)
+                *args, None if forced_dgu is None else forced_dgu[r0:r1], fp8_grad_format,
+                fwd["h_q"][r0:r1] if fp8_wgrad else None)
         else:
             dz, dWg, dWu, dWd, dG, dU = swiglu_ffn_backward(*args)
         d_w_gateup[e, :f] = dWg
@@ -507,7 +518,8 @@ def backward(x, w_router, w_gateup, w_down, s_gateup, s_down, fwd, dy, *, score,
         Us = fwd["s_preact"][:, Fs:]
         args = (x, sg, su, np.asarray(s_down, F64), Gs, Us, fwd["s_h"], dy)
         if fp8:
-            dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward_fp8(*args, forced_s_dgu, fp8_grad_format)
+            dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward_fp8(*args, forced_s_dgu, fp8_grad_format,
+                                                                    fwd["s_h_q"] if fp8_wgrad else None)
         else:
             dxs, dSg, dSu, dSd, dGs, dUs = swiglu_ffn_backward(*args)
         out["s_dgu"] = np.concatenate([dGs, dUs], axis=1)
@@ -704,7 +716,10 @@ def grouped_gemm_fp8_nt(a_codes, a_scale, b_codes, b_scale, offsets, a_fmt="e4m3
 #     activations; dG | dU are formed from the bf16 copies of G and U, the
 #     pre-activations the layer saves; the router stays fp32;
 #   - weight gradients stay in the layer's own precision (exact here), the
-#     row-wise recipe with high-precision weight gradients.
+#     row-wise recipe with high-precision weight gradients; or, with
+#     ``fp8_wgrad``, they are e4m3 products whose operands are quantised along
+#     their reduction dimension, the rows of one expert: one scale per
+#     (expert, column) of dY~, H, dG | dU and the token rows.
 
 def round_bf16(v):
     """The bf16 value a stored fp32 result takes: v rounded to fp32, then to
@@ -728,17 +743,19 @@ def fp8_product(a, b, a_fmt="e4m3"):
 def swiglu_ffn_fp8(z, w_gate, w_up, w_down, forced_h=None):
     """``swiglu_ffn`` with both products in e4m3: G | U = fp8(z) . fp8(W_g | W_u)^T,
     H = silu(G) U (fp64), Y = fp8(bf16(H)) . fp8(W_d)^T; ``forced_h`` replaces
-    bf16(H) as the down product's input.  Returns (G, U, H, Y) like
-    ``swiglu_ffn``, H unrounded."""
+    bf16(H) as the down product's input.  Returns (G, U, H, Y, Hb) like
+    ``swiglu_ffn`` with H unrounded, plus the bf16 H the down product
+    quantised."""
     f = w_gate.shape[0]
     GU = fp8_product(z, np.concatenate([w_gate, w_up], axis=0))
     G, U = GU[:, :f], GU[:, f:]
     H = silu(G) * U
     Hb = round_bf16(H) if forced_h is None else np.asarray(forced_h, F64)
-    return G, U, H, fp8_product(Hb, w_down)
+    return G, U, H, fp8_product(Hb, w_down), Hb
 
 
-def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=None, grad_fmt="e4m3"):
+def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=None, grad_fmt="e4m3",
+                            Hq=None):
     """``swiglu_ffn_backward`` with the two data gradients in e4m3:
     dH = fp8(bf16(dY)) . fp8 of W_d along its rows d (W_d^T quantised
     row-wise), dz = fp8(bf16(dG | dU)) . fp8 of W_g | W_u along 2f; the
@@ -747,16 +764,43 @@ def swiglu_ffn_backward_fp8(z, w_gate, w_up, w_down, G, U, H, dY, forced_dgu=Non
     so that this quantisation sees the values a bf16 layer holds;
     ``forced_dgu`` replaces that bf16 copy as the second product's input.
     ``grad_fmt``: the format of the gradient operands (dY, dG | dU); the
-    weights stay e4m3.  Same return values."""
+    weights stay e4m3.  ``Hq`` (the bf16 H the forward's down product
+    quantised) given: the weight gradients are e4m3 products too
+    (``wgrad_fp8``: dW_d from bf16(dY) and Hq, dW_g | dW_u from the quantised
+    dG | dU copy and z).  Same return values."""
     dH = fp8_product(round_bf16(dY), np.asarray(w_down, F64).T, grad_fmt)
     Gb, Ub = round_bf16(G), round_bf16(U)
     sg = 1.0 / (1.0 + np.exp(-Gb))
     dG = dH * Ub * sg * (1.0 + Gb * (1.0 - sg))
     dU = dH * (Gb * sg)
-    dW_d = dY.T @ H
-    dW_g = dG.T @ z
-    dW_u = dU.T @ z
     w_gu = np.concatenate([w_gate, w_up], axis=0)
     dgu_b = round_bf16(np.concatenate([dG, dU], axis=1)) if forced_dgu is None else np.asarray(forced_dgu, F64)
     dz = fp8_product(dgu_b, w_gu.T, grad_fmt)
+    if Hq is None:
+        dW_d = dY.T @ H
+        dW_g = dG.T @ z
+        dW_u = dU.T @ z
+    else:
+        f = w_gate.shape[0]
+        dW_d = wgrad_fp8(round_bf16(dY), Hq)
+        dW_gu = wgrad_fp8(dgu_b, z)
+        dW_g, dW_u = dW_gu[:f], dW_gu[f:]
     return dz, dW_g, dW_u, dW_d, dG, dU
+
+
+def quantize_colwise(x, fmt="e4m3"):
+    """Column-wise scaling over the rows of x [M, C]: s_c = amax_c / vmax (1
+    for an all-zero column), q = fmt(x / s_c); the row-wise scheme applied to
+    x^T.  Returns (codes [M, C], s [C])."""
+    q, s = quantize_rowwise(np.asarray(x, F64).T, fmt)
+    return q.T, s
+
+
+def wgrad_fp8(a, b):
+    """The weight gradient a^T b (a [M, N], b [M, K], reduction over the M
+    rows) in e4m3: both operands quantised column-wise, i.e. row-wise along
+    their reduction dimension (``quantize_colwise``), and the scaled product
+    C[n, k] = s_a[n] s_b[k] sum_m q_a[m, n] q_b[m, k] taken exactly (fp64)."""
+    qa, sa = quantize_colwise(a)
+    qb, sb = quantize_colwise(b)
+    return grouped_gemm_fp8_nt(qa.T, sa, qb.T[None], sb[None], np.array([0, qa.shape[1]]))

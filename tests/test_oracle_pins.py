@@ -876,3 +876,66 @@ def test_fp8_layer_e5m2_gradients():
     b4 = bw(L2["dy"], "e4m3")
     r5, r4 = _rel(b1["dx"], bx["dx"]), _rel(b4["dx"], bx["dx"])
     assert 1e-4 < r4 < r5 < 0.15, (r4, r5)
+
+
+# --------------------------------------------------------------------------- fp8 weight gradients
+def test_wgrad_fp8_exact_on_the_grid_and_bounded():
+    """wgrad_fp8(a, b) = a^T b when every column of both operands is on the
+    e4m3 grid with column maxima 448 * 2^-p (exact column-wise quantisation),
+    stays within the half-step bound off the grid, and follows a power-of-two
+    scaling of either operand exactly."""
+    g = np.random.default_rng(72)
+    a = _e4m3_grid(g, 20, 50, 6).T            # [50, 20]: columns on the grid
+    b = _e4m3_grid(g, 12, 50, 9).T            # [50, 12]
+    assert np.array_equal(O.wgrad_fp8(a, b), a.T @ b)
+    a = g.standard_normal((70, 20))
+    b = g.standard_normal((70, 12))
+    sa = np.abs(a).max(0) / 448.0
+    sb = np.abs(b).max(0) / 448.0
+    ea = np.abs(a) * 2.0 ** -4 + sa[None, :] * 2.0 ** -10
+    eb = np.abs(b) * 2.0 ** -4 + sb[None, :] * 2.0 ** -10
+    bound = ea.T @ np.abs(b) + np.abs(a).T @ eb + ea.T @ eb
+    err = np.abs(O.wgrad_fp8(a, b) - a.T @ b)
+    assert np.all(err <= bound * (1 + 1e-6)) and err.max() > 0
+    assert np.array_equal(O.wgrad_fp8(a * 4.0, b), 4.0 * O.wgrad_fp8(a, b))
+    q, s = O.quantize_colwise(a)
+    assert np.all(np.max(np.abs(O.e4m3_decode(q)), axis=0) == 448.0) and s.shape == (20,)
+
+
+def test_fp8_layer_weight_gradients():
+    """The fp8 backward with e4m3 weight gradients: one expert, top-1 (gate 1),
+    one-hot tokens, dy and the forced H and dG | dU on the grid by rows and by
+    columns -- every weight gradient is then the exact product of those
+    operands; off the grid the weight gradients stay within a few per cent of
+    the exact layer's and scale exactly with a power-of-two dy."""
+    T, d, E, k, f, Fs = 40, 48, 1, 1, 32, 16
+    L = _grid_layer(6, T, d, E, k, f, Fs, "softmax", True, one_hot=True)
+    g = np.random.default_rng(10)
+    L["dy"] = _e4m3_grid(g, T, d, 6, cols=True)
+    fh = _e4m3_grid(g, T, f, 3, cols=True)
+    fsh = _e4m3_grid(g, T, Fs, 3, cols=True)
+    fw = _fwd(L, fp8=True, forced_h=fh, forced_s_h=fsh)
+    assert np.array_equal(fw["h_q"], fh) and np.array_equal(fw["s_h_q"], fsh)
+    fd = _e4m3_grid(g, T, 2 * f, 4, cols=True)
+    fsd = _e4m3_grid(g, T, 2 * Fs, 4, cols=True)
+    bw = O.backward(L["x"], L["w_router"], L["w_gateup"], L["w_down"], L["s_gateup"], L["s_down"], fw, L["dy"],
+                    score=L["score"], renorm=L["renorm"], fp8=True, forced_dgu=fd, forced_s_dgu=fsd,
+                    fp8_wgrad=True)
+    x_perm = fw["x_perm"]
+    assert np.all(fw["gate"] == 1.0)
+    dyp = L["dy"][fw["src"] // k]
+    assert np.array_equal(bw["d_w_down"][0], dyp.T @ fh)
+    assert np.array_equal(bw["d_w_gateup"][0], fd.T @ x_perm)
+    assert np.array_equal(bw["d_s_down"], L["dy"].T @ fsh)
+    assert np.array_equal(bw["d_s_gateup"], fsd.T @ L["x"])
+    # off the grid
+    L2 = _rand_layer(12, 48, 32, 6, 2, 16, 16, "sigmoid", True)
+    f2 = _fwd(L2, fp8=True)
+    b = lambda dy, wg: O.backward(L2["x"], L2["w_router"], L2["w_gateup"], L2["w_down"],  # noqa: E731
+                                  L2["s_gateup"], L2["s_down"], f2, dy, score=L2["score"], renorm=L2["renorm"],
+                                  fp8=True, fp8_wgrad=wg)
+    b8, bh, b8q = b(L2["dy"], True), b(L2["dy"], False), b(L2["dy"] * 0.25, True)
+    for key in ("d_w_gateup", "d_w_down", "d_s_gateup", "d_s_down"):
+        assert 1e-4 < _rel(b8[key], bh[key]) < 0.08, key
+        assert np.array_equal(b8q[key], 0.25 * b8[key]), key
+    assert np.array_equal(b8["dx"], bh["dx"])
