@@ -507,7 +507,7 @@ def fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
                     "separately"}
 
 
-def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops):
+def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops, wgrad_fp8=False):
     """The whole layer through the fp8 calls (moe_forward_fp8 and, for a
     training workload, moe_backward_fp8) on the same inputs, timed like the
     bf16 step: a cache flush before each step, one event pair per step.  The
@@ -523,12 +523,12 @@ def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops):
     dx = torch.empty_like(x)
     grads = M.alloc_grads(desc) if training else None
     wsf = M.alloc_workspace(desc, "forward_fp8")
-    wsb = M.alloc_workspace(desc, "backward_fp8") if training else None
+    wsb = M.alloc_workspace(desc, "backward_fp8_wgrad" if wgrad_fp8 else "backward_fp8") if training else None
 
     def step():
         M.moe_forward_fp8(desc, w, w8, x, y, saved, wsf, stream)
         if training:
-            M.moe_backward_fp8(desc, w, w8, x, saved, dy, dx, grads, wsb, stream)
+            M.moe_backward_fp8(desc, w, w8, x, saved, dy, dx, grads, wsb, stream, wgrad_fp8=wgrad_fp8)
 
     for _ in range(2):
         step()
@@ -566,12 +566,14 @@ def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops):
         if name in flops and not name.startswith("router"):
             per = n // min(steps, 5)
             tf = flops[name] / (sms * 1e-3 / n) / 1e12 if per == 1 else None
-            if tf is not None and name in FP8_PRODUCTS:
+            fp8_names = FP8_PRODUCTS + (FP8_WGRADS if wgrad_fp8 else ())
+            if tf is not None and name in fp8_names:
                 e.update(tflops=tf, frac_fp8=tf / PEAK_FP8_TFLOPS)
             elif tf is not None:
                 e.update(tflops=tf, frac=tf / PEAK_BF16_TFLOPS)
         stages[name] = e
-    progress(f"{cfg.name}: fp8 layer {ms:.3f} ms per step, weight copies {q_ms:.3f} ms")
+    progress(f"{cfg.name}: fp8 layer{' (fp8 weight gradients)' if wgrad_fp8 else ''} {ms:.3f} ms per step, "
+             f"weight copies {q_ms:.3f} ms")
     return {
         "ms_per_step": ms, "tokens_per_s": cfg.T / (ms * 1e-3),
         "step_ms_min": min(step_ms), "step_ms_max": max(step_ms),
@@ -581,12 +583,15 @@ def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops):
         "stages": stages,
         "what": "moe_forward_fp8" + (" + moe_backward_fp8" if training else "") +
                 ": e4m3 row-wise expert products (forward" + (" and both data gradients" if training else "") +
-                "), activations quantised in the step (stage fp8_quantize), bf16 weight gradients; the e4m3 "
-                "weight copies (moe_fp8_weights_quantize) are written once per weight update and timed "
-                "separately (weight_copies_ms)",
+                (", and the weight gradients with operands quantised along each expert's rows" if wgrad_fp8
+                 else "") + "), activations quantised in the step (stage fp8_quantize)" +
+                ("" if wgrad_fp8 else ", bf16 weight gradients") + "; the e4m3 weight copies "
+                "(moe_fp8_weights_quantize) are written once per weight update and timed separately "
+                "(weight_copies_ms)",
     }
 
 
+FP8_WGRADS = ("down_wgrad", "gate_up_wgrad", "shared_down_wgrad", "shared_gate_up_wgrad")
 FP8_PRODUCTS = ("gate_up", "down", "shared_gate_up", "shared_down", "down_dgrad", "gate_up_dgrad",
                 "shared_down_dgrad", "shared_gate_up_dgrad")
 
@@ -821,6 +826,8 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
     fp8_ok = cfg.dtype == "bf16" and cfg.f % 128 == 0 and (cfg.n_shared * cfg.f_shared) % 128 == 0
     fp8_whole = (fp8_layer(M, cfg, desc, w, x, dy, training, stream, args.steps, ms_step, flops)
                  if not args.no_fp8 and fp8_ok else None)
+    fp8_whole_w = (fp8_layer(M, cfg, desc, w, x, dy, training, stream, args.steps, ms_step, flops, wgrad_fp8=True)
+                   if not args.no_fp8 and fp8_ok and training else None)
     # the streaming memory-bound stages (route and the index-only permute are
     # latency-bound at these sizes)
     hbm3 = [n for n in ("combine", "combine_bwd", "unpermute_sum") if n in stage_out]
@@ -887,6 +894,7 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
                                  "one kind on register operands, no memory traffic; events over 3 launches"},
         "stages": stage_out,
         "fp8_layer": fp8_whole,
+        "fp8_layer_fp8_weight_gradients": fp8_whole_w,
         "fp8_gate_up": fp8,
         "fp8_gate_up_dgrad": fp8_dg,
         "fp8_down_dgrad": fp8_dd,

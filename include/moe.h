@@ -171,8 +171,9 @@ enum {
   MOE_WS_PERMUTE = 0,
   MOE_WS_FORWARD = 1,
   MOE_WS_BACKWARD = 2,
-  MOE_WS_FORWARD_FP8 = 3,  /* moe_forward_fp8  */
-  MOE_WS_BACKWARD_FP8 = 4  /* moe_backward_fp8 */
+  MOE_WS_FORWARD_FP8 = 3,        /* moe_forward_fp8                         */
+  MOE_WS_BACKWARD_FP8 = 4,       /* moe_backward_fp8, bf16 weight gradients */
+  MOE_WS_BACKWARD_FP8_WGRAD = 5  /* moe_backward_fp8 with fp8 weight gradients */
 };
 
 /* ---------------------------------------------------------------- queries */
@@ -421,6 +422,34 @@ int moe_grouped_gemm_fp8_gather(int epilogue, int64_t G, int64_t M_total, int64_
                                 const uint8_t *B, const float *b_scale, void *C, void *aux,
                                 const int32_t *rows, int64_t src_rows, void *stream);
 
+/* fp8 weight-gradient operands: each column of x [M, C] (dtype bf16 or fp32)
+ * quantised to e4m3 over the rows of each of G groups (group g owns rows
+ * [offsets[g], offsets[g+1]); offsets NULL for one group of all M rows; with
+ * rows, group row m reads x[rows[m]], rows[m] in [0, src_rows)):
+ * scale[g, c] = max |x[., c]| over the group's rows / 448 (1 for none or all
+ * zero), codes stored transposed and padded: with P'_g the group's row count
+ * rounded up to 64 and P_g the sum of the earlier groups' P' (written to
+ * pad_offsets [G+1]), code (m, c) of group g sits at q[C * P_g + c * P'_g + m],
+ * zero for m past the group's rows.  This is row-wise quantisation along the
+ * reduction dimension of a weight gradient, whose reduction runs over one
+ * expert's tokens (Apex-3 code page, "Run it yourself": fp8_rowwise).
+ *   q: moe_quantize_fp8_colwise_bytes(G, M, C) bytes (an upper bound), scale
+ *   [G, C] fp32.  C a multiple of 64, 1 <= G <= 256. */
+size_t moe_quantize_fp8_colwise_bytes(int64_t G, int64_t M, int64_t C);
+int moe_quantize_fp8_colwise(int64_t G, int64_t M, int64_t C, int dtype, const int32_t *offsets,
+                             const int32_t *rows, int64_t src_rows, const void *x, int32_t *pad_offsets,
+                             uint8_t *q, float *scale, void *stream);
+
+/* fp8 weight gradient over the blocks of moe_quantize_fp8_colwise:
+ *   C[g, n, k] = a_scale[g, n] * b_scale[g, k] * sum_m A_g[n, m] B_g[k, m]
+ * with A the codes of an [M, N] operand and B of an [M, K] operand quantised
+ * with the same group offsets (pad_offsets from either call), fp32
+ * accumulation of the exact e4m3 products, one rounding to bf16;
+ * C [G, N, K] bf16 (groups without rows get zeros).  N, K multiples of 64. */
+int moe_grouped_gemm_fp8_wgrad(int64_t G, int64_t N, int64_t K, const int32_t *pad_offsets, const uint8_t *A,
+                               const float *a_scale, const uint8_t *B, const float *b_scale, void *C,
+                               void *stream);
+
 /* ---------------------------------------------------------------- fp8 layer */
 
 /* e4m3 copies of the expert weights for the fp8 layer calls (Apex-3 code
@@ -479,23 +508,27 @@ int moe_forward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp
                     const void *x, void *y, const moe_saved_t *saved, void *ws, size_t ws_bytes,
                     void *stream);
 
-/* moe_backward with the expert data gradients in fp8: the gate-weighted
+/* moe_backward with the expert products in fp8: the gate-weighted
  * upstream rows dY~ (bf16) are quantised row-wise for dH = dY~ W_d (with the
  * SwiGLU derivative fused), dG | dU (bf16) row-wise for dX~ = (dG | dU) W_gu,
  * against the e4m3 data-gradient copies of w8; the shared experts likewise
  * (dy itself for their down product).  grad_format: MOE_E4M3, or MOE_E5M2
  * for these gradient operands (the weights stay e4m3).  With k <= 8 the
- * combine backward writes dY~'s and dy's codes as it forms the rows.  Weight gradients stay bf16 products of the
+ * combine backward writes dY~'s and dy's codes as it forms the rows.
+ * wgrad_fp8 = 1: the weight gradients are e4m3 products too, of dY~ and H
+ * (down), dG | dU and the token rows (gate/up) quantised along each expert's
+ * rows (moe_quantize_fp8_colwise, moe_grouped_gemm_fp8_wgrad); 0: bf16.  Weight gradients stay bf16 products of the
  * bf16 activations with fp32 accumulation (the row-wise recipe with
  * high-precision weight gradients); the router backward is that of
  * moe_backward.  Arguments as moe_backward, plus
  *   w8   data-gradient-layout copies (moe_fp8_weights_quantize)
- *   ws  >= moe_workspace_bytes(desc, MOE_WS_BACKWARD_FP8)
- * w's bf16 expert weights are required (the backward reads no fp8 copy of
- * them for the weight gradients, but checks them as moe_backward does).
+ *   ws  >= moe_workspace_bytes(desc, MOE_WS_BACKWARD_FP8), or
+ *          MOE_WS_BACKWARD_FP8_WGRAD with wgrad_fp8
+ * w's bf16 expert weights are required (checked as moe_backward does).
  * Same layer limits as moe_forward_fp8. */
 int moe_backward_fp8(const moe_desc_t *desc, const moe_weights_t *w, const moe_fp8_weights_t *w8,
-                     int grad_format, const void *x, const moe_saved_t *saved, const void *dy, void *dx,
+                     int grad_format, int wgrad_fp8, const void *x, const moe_saved_t *saved, const void *dy,
+                     void *dx,
                      const moe_grads_t *grads, const moe_router_terms_t *terms, float *losses,
                      void *ws, size_t ws_bytes, void *stream);
 

@@ -19,6 +19,7 @@ MOE_SOFTMAX, MOE_SIGMOID = 0, 1
 MOE_GEMM_NT, MOE_GEMM_NN, MOE_GEMM_TN = 0, 1, 2
 MOE_EPI_NONE, MOE_EPI_SWIGLU, MOE_EPI_DSWIGLU = 0, 1, 2
 MOE_WS_PERMUTE, MOE_WS_FORWARD, MOE_WS_BACKWARD, MOE_WS_FORWARD_FP8, MOE_WS_BACKWARD_FP8 = 0, 1, 2, 3, 4
+MOE_WS_BACKWARD_FP8_WGRAD = 5
 MOE_FP8_FORWARD_LAYOUT, MOE_FP8_BACKWARD_LAYOUT = 1, 2
 MOE_E4M3, MOE_E5M2 = 0, 1
 FP8_FORMATS = {"e4m3": MOE_E4M3, "e5m2": MOE_E5M2}
@@ -91,8 +92,12 @@ SIGNATURES = {
                              _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
     "moe_forward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_vp, c_vp, _P(MoeSaved), c_vp,
                                 c_sz, c_vp]),
-    "moe_backward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_i32, c_vp, _P(MoeSaved), c_vp,
-                                 c_vp, _P(MoeGrads), _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
+    "moe_backward_fp8": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_i32, c_i32, c_vp, _P(MoeSaved),
+                                 c_vp, c_vp, _P(MoeGrads), _P(MoeRouterTerms), c_vp, c_vp, c_sz, c_vp]),
+    "moe_quantize_fp8_colwise_bytes": (c_sz, [c_i64, c_i64, c_i64]),
+    "moe_quantize_fp8_colwise": (c_i32, [c_i64, c_i64, c_i64, c_i32, c_vp, c_vp, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                         c_vp]),
+    "moe_grouped_gemm_fp8_wgrad": (c_i32, [c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp, c_vp]),
     "moe_fp8_weights_quantize": (c_i32, [_P(MoeDesc), _P(MoeWeights), _P(MoeFp8Weights), c_i32, c_vp]),
     "moe_grouped_gemm_fp8_gather": (c_i32, [c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                             c_vp, c_vp, c_vp, c_i64, c_vp]),

@@ -68,7 +68,8 @@ def route_hist_elems(desc) -> int:
 
 def workspace_bytes(desc, which: str) -> int:
     w = {"permute": L.MOE_WS_PERMUTE, "forward": L.MOE_WS_FORWARD, "backward": L.MOE_WS_BACKWARD,
-         "forward_fp8": L.MOE_WS_FORWARD_FP8, "backward_fp8": L.MOE_WS_BACKWARD_FP8}[which]
+         "forward_fp8": L.MOE_WS_FORWARD_FP8, "backward_fp8": L.MOE_WS_BACKWARD_FP8,
+         "backward_fp8_wgrad": L.MOE_WS_BACKWARD_FP8_WGRAD}[which]
     return int(L.load().moe_workspace_bytes(ctypes.byref(desc), w))
 
 
@@ -180,14 +181,15 @@ def moe_forward_fp8(desc, weights: dict, w8: dict, x, y, saved: dict, ws, stream
 
 
 def moe_backward_fp8(desc, weights: dict, w8: dict, x, saved: dict, dy, dx, grads: dict, ws, stream=None,
-                     terms=None, losses=None, grad_format="e4m3"):
-    """grad_format: "e4m3" or "e5m2" for the gradient operands of the fp8 data gradients."""
+                     terms=None, losses=None, grad_format="e4m3", wgrad_fp8=False):
+    """grad_format: "e4m3" or "e5m2" for the gradient operands of the fp8 data gradients; wgrad_fp8: the
+    weight gradients in e4m3 too (workspace "backward_fp8_wgrad")."""
     w = _weights(weights)
     q = _fp8_weights(w8)
     s = L.MoeSaved(*(_p(saved.get(n)) for n in SAVED_FIELDS))
     g = L.MoeGrads(*(_p(grads.get(n)) for n in GRAD_FIELDS))
     _check(L.load().moe_backward_fp8(ctypes.byref(desc), ctypes.byref(w), ctypes.byref(q), L.FP8_FORMATS[grad_format],
-                                     _p(x), ctypes.byref(s),
+                                     int(bool(wgrad_fp8)), _p(x), ctypes.byref(s),
                                      _p(dy), _p(dx), ctypes.byref(g), _terms(terms), _p(losses), _p(ws),
                                      ws.numel() * ws.element_size(), _stream(stream)), "moe_backward_fp8")
 
@@ -234,6 +236,25 @@ def moe_grouped_gemm_fp8(epilogue, G, M_total, N, K, group_offsets, A, a_scale, 
                                          _p(group_offsets), _p(A),
                                          _p(a_scale), _p(B), _p(b_scale), _p(C), _p(aux), _stream(stream)),
            "moe_grouped_gemm_fp8")
+
+
+def moe_quantize_fp8_colwise(x, G, offsets, pad_offsets, q, scale, rows=None, M=None, stream=None):
+    """e4m3 codes of each column of x over each group's rows, stored transposed and padded (the
+    operands of an fp8 weight gradient); x [src_rows, C] (read through rows when given, M rows)."""
+    dt = L.MOE_BF16 if x.dtype == torch.bfloat16 else L.MOE_F32
+    src_rows, C = x.shape
+    M = src_rows if M is None else M
+    _check(L.load().moe_quantize_fp8_colwise(G, M, C, dt, _p(offsets), _p(rows), src_rows, _p(x), _p(pad_offsets),
+                                             _p(q), _p(scale), _stream(stream)), "moe_quantize_fp8_colwise")
+
+
+def quantize_fp8_colwise_bytes(G, M, C) -> int:
+    return int(L.load().moe_quantize_fp8_colwise_bytes(G, M, C))
+
+
+def moe_grouped_gemm_fp8_wgrad(G, N, K, pad_offsets, A, a_scale, B, b_scale, C, stream=None):
+    _check(L.load().moe_grouped_gemm_fp8_wgrad(G, N, K, _p(pad_offsets), _p(A), _p(a_scale), _p(B), _p(b_scale),
+                                               _p(C), _stream(stream)), "moe_grouped_gemm_fp8_wgrad")
 
 
 def moe_grouped_gemm_fp8_gather(epilogue, G, M_total, N, K, group_offsets, A, a_scale, B, b_scale, C, rows,

@@ -134,8 +134,18 @@ struct BwdWs {
   float* qs;       // and its row scales
   uint8_t* q_dy;   // fp8: dy's codes [T, d] and scales [T] (the shared down data gradient)
   float* qs_dy;
+  // fp8 weight gradients: the two operands' padded transposed codes, their
+  // per-(group, column) scales, and the padded group offsets (routed, shared)
+  uint8_t* wa;
+  uint8_t* wb;
+  float* wsa;
+  float* wsb;
+  int32_t* pad;
+  int32_t* pad_s;
 };
-size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out) {
+// bytes of the padded transposed codes of C columns over M rows in G groups
+inline size_t colwise_bytes(int64_t G, int64_t M, int64_t C) { return (size_t)C * (size_t)(M + 63 * G); }
+size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out, bool wgrad8 = false) {
   Carve c(ws);
   const int64_t T = d->num_tokens, D = d->d_model, f = d->d_ff, A = T * d->top_k;
   const int64_t F = shared_width(d);
@@ -162,6 +172,28 @@ size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out) {
     w.qs = (float*)c.take((size_t)(A > T ? A : T) * sizeof(float));
     w.q_dy = (uint8_t*)c.take((size_t)T * D);
     w.qs_dy = (float*)c.take((size_t)T * sizeof(float));
+  }
+  w.wa = w.wb = nullptr;
+  w.wsa = w.wsb = nullptr;
+  w.pad = w.pad_s = nullptr;
+  if (fp8 && wgrad8) {
+    const int64_t E = d->num_experts;
+    // routed: dW_d (A' = dY~ [d], B' = H [f]), dW_gu (A' = dG|dU [2f], B' = x [d]);
+    // shared: dW_sd (dy [d], H_s [F]), dW_sgu (dG|dU_s [2F], x [d])
+    const size_t ra = D > 2 * f ? D : 2 * f, rb = D > f ? D : f;
+    const size_t sa = F > 0 ? (size_t)(D > 2 * F ? D : 2 * F) : 0, sb = F > 0 ? (size_t)(D > F ? D : F) : 0;
+    size_t qa = colwise_bytes(E, A, ra), qb = colwise_bytes(E, A, rb);
+    if (F > 0) {
+      qa = qa > colwise_bytes(1, T, sa) ? qa : colwise_bytes(1, T, sa);
+      qb = qb > colwise_bytes(1, T, sb) ? qb : colwise_bytes(1, T, sb);
+    }
+    const size_t fa = (size_t)E * ra > sa ? (size_t)E * ra : sa, fb = (size_t)E * rb > sb ? (size_t)E * rb : sb;
+    w.wa = (uint8_t*)c.take(qa);
+    w.wb = (uint8_t*)c.take(qb);
+    w.wsa = (float*)c.take(fa * sizeof(float));
+    w.wsb = (float*)c.take(fb * sizeof(float));
+    w.pad = (int32_t*)c.take((size_t)(E + 1) * sizeof(int32_t));
+    w.pad_s = (int32_t*)c.take(2 * sizeof(int32_t));
   }
   if (out) *out = w;
   return c.off;
@@ -297,6 +329,7 @@ size_t moe_workspace_bytes(const moe_desc_t* d, int which) {
     case MOE_WS_BACKWARD: return bwd_ws(d, false, nullptr, nullptr);
     case MOE_WS_FORWARD_FP8: return fwd_ws(d, true, nullptr, nullptr);
     case MOE_WS_BACKWARD_FP8: return bwd_ws(d, true, nullptr, nullptr);
+    case MOE_WS_BACKWARD_FP8_WGRAD: return bwd_ws(d, true, nullptr, nullptr, true);
     default: return 0;
   }
 }
@@ -617,7 +650,8 @@ int moe_forward_no_workspace(const moe_desc_t* d, const moe_weights_t* w, const 
 
 // The backward pass of moe_backward (w8 NULL) or moe_backward_fp8.
 static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
-                         int grad_format, const void* x, const moe_saved_t* sv, const void* dy, void* dx,
+                         int grad_format, int wgrad_fp8, const void* x, const moe_saved_t* sv, const void* dy,
+                         void* dx,
                          const moe_grads_t* g, const moe_router_terms_t* terms, float* losses,
                          void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(d);
@@ -637,6 +671,8 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   const int dt = d->dtype;
   const bool fp8 = w8 != nullptr;
   if (grad_format != MOE_E4M3 && grad_format != MOE_E5M2) return MOE_ERR_INVALID;
+  if (wgrad_fp8 != 0 && wgrad_fp8 != 1) return MOE_ERR_INVALID;
+  const bool wg8 = fp8 && wgrad_fp8;
   const int gf = grad_format == MOE_E5M2 ? FP8_E5M2 : FP8_E4M3;
   if (!w->w_router || !w->w_gateup || !w->w_down) return MOE_ERR_INVALID;
   if (!g->d_w_router || !g->d_w_gateup || !g->d_w_down) return MOE_ERR_INVALID;
@@ -669,10 +705,18 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
     s = gather_supported(d, true);
     if (s) return s;
   }
-  if (ws_bytes < moe_workspace_bytes(d, fp8 ? MOE_WS_BACKWARD_FP8 : MOE_WS_BACKWARD)) return MOE_ERR_WORKSPACE;
+  if (ws_bytes < moe_workspace_bytes(d, wg8 ? MOE_WS_BACKWARD_FP8_WGRAD
+                                            : (fp8 ? MOE_WS_BACKWARD_FP8 : MOE_WS_BACKWARD)))
+    return MOE_ERR_WORKSPACE;
   hipStream_t st = (hipStream_t)stream;
   BwdWs bw;
-  bwd_ws(d, fp8, ws, &bw);
+  bwd_ws(d, fp8, ws, &bw, wg8);
+  // an fp8 weight gradient: both operands quantised column-wise over each
+  // group's rows (stored transposed and padded), then the scaled product
+  auto quant_w = [&](const void* src, const int32_t* rows, const int32_t* offs, int G, int64_t M, int64_t C,
+                     int32_t* pad, uint8_t* q, float* sc) -> hipError_t {
+    return launch_quantize_fp8_colwise(src, dt, rows, offs, G, M, C, pad, q, sc, st);
+  };
   // 1. combine backward + router backward (dlogits); fp8 (k <= 8): the
   // same kernel also writes the e4m3 copies of dY~ and dy
   const bool fused_q = fp8 && k <= 8;
@@ -710,15 +754,27 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
                                    sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
                                 nullptr, 0, st));
   }
-  // 3. down weight gradient
-  MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets,
-                                 bw.dy_perm, sv->h, g->d_w_down, nullptr),
-                              bw.gemm, bw.gemm_bytes, st));
-  // 4. gate/up weight gradient (token rows of x_perm, or of x through tok)
-  GemmProblem guw = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D, sv->offsets, bw.dgu,
-                       gather ? x : sv->x_perm, g->d_w_gateup, nullptr);
-  guw.rows = gather ? sv->tok : nullptr;
-  MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(guw, bw.gemm, bw.gemm_bytes, st));
+  // 3. down weight gradient, 4. gate/up weight gradient (token rows of
+  // x_perm, or of x through tok)
+  if (wg8) {
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(bw.dy_perm, nullptr, sv->offsets, (int)E, A, D, bw.pad, bw.wa, bw.wsa));
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(sv->h, nullptr, sv->offsets, (int)E, A, f, bw.pad, bw.wb, bw.wsb));
+    MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_gemm_fp8_wgrad(E, D, f, bw.pad, bw.wa, bw.wsa, bw.wb, bw.wsb,
+                                                          g->d_w_down, st));
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(bw.dgu, nullptr, sv->offsets, (int)E, A, 2 * f, bw.pad, bw.wa, bw.wsa));
+    MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(gather ? x : sv->x_perm, gather ? sv->tok : nullptr, sv->offsets,
+                                              (int)E, A, D, bw.pad, bw.wb, bw.wsb));
+    MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_gemm_fp8_wgrad(E, 2 * f, D, bw.pad, bw.wa, bw.wsa, bw.wb, bw.wsb,
+                                                             g->d_w_gateup, st));
+  } else {
+    MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f,
+                                                           sv->offsets, bw.dy_perm, sv->h, g->d_w_down, nullptr),
+                                                        bw.gemm, bw.gemm_bytes, st));
+    GemmProblem guw = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D, sv->offsets, bw.dgu,
+                         gather ? x : sv->x_perm, g->d_w_gateup, nullptr);
+    guw.rows = gather ? sv->tok : nullptr;
+    MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(guw, bw.gemm, bw.gemm_bytes, st));
+  }
   // 5. gate/up data gradient (written over dy_perm, which is no longer needed;
   // fp8: dG | dU in e4m3 per row against W_gu quantised along 2f, transposed)
   void* dx_perm = bw.dy_perm;
@@ -745,12 +801,24 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
                                      nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
                                   nullptr, 0, st));
     }
-    MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
-                                   nullptr, dy, sv->s_h, g->d_s_down, nullptr),
-                                bw.gemm, bw.gemm_bytes, st));
-    MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D,
-                                   nullptr, bw.s_dgu, x, g->d_s_gateup, nullptr),
-                                bw.gemm, bw.gemm_bytes, st));
+    if (wg8) {
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(dy, nullptr, nullptr, 1, T, D, bw.pad_s, bw.wa, bw.wsa));
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(sv->s_h, nullptr, nullptr, 1, T, F, bw.pad_s, bw.wb, bw.wsb));
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_gemm_fp8_wgrad(1, D, F, bw.pad_s, bw.wa, bw.wsa, bw.wb, bw.wsb,
+                                                                   g->d_s_down, st));
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(bw.s_dgu, nullptr, nullptr, 1, T, 2 * F, bw.pad_s, bw.wa, bw.wsa));
+      MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(x, nullptr, nullptr, 1, T, D, bw.pad_s, bw.wb, bw.wsb));
+      MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_WGRAD, launch_gemm_fp8_wgrad(1, 2 * F, D, bw.pad_s, bw.wa, bw.wsa, bw.wb,
+                                                                      bw.wsb, g->d_s_gateup, st));
+    } else {
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F,
+                                                                    nullptr, dy, sv->s_h, g->d_s_down, nullptr),
+                                                                 bw.gemm, bw.gemm_bytes, st));
+      MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_WGRAD,
+                launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D, nullptr, bw.s_dgu, x,
+                                       g->d_s_gateup, nullptr),
+                                    bw.gemm, bw.gemm_bytes, st));
+    }
     if (fp8) {
       MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(bw.s_dgu, dt, T, (int)(2 * F), bw.q, bw.qs, st, gf));
       MOE_STAGE(MOE_STAGE_SHARED_GATE_UP_DGRAD,
@@ -780,15 +848,16 @@ int moe_backward(const moe_desc_t* d, const moe_weights_t* w, const void* x,
                  const moe_saved_t* sv, const void* dy, void* dx, const moe_grads_t* g,
                  const moe_router_terms_t* terms, float* losses, void* ws, size_t ws_bytes,
                  void* stream) {
-  return backward_impl(d, w, nullptr, MOE_E4M3, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
+  return backward_impl(d, w, nullptr, MOE_E4M3, 0, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
 }
 
 int moe_backward_fp8(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
-                     int grad_format, const void* x, const moe_saved_t* sv, const void* dy, void* dx,
-                     const moe_grads_t* g, const moe_router_terms_t* terms, float* losses, void* ws,
+                     int grad_format, int wgrad_fp8, const void* x, const moe_saved_t* sv, const void* dy,
+                     void* dx, const moe_grads_t* g, const moe_router_terms_t* terms, float* losses, void* ws,
                      size_t ws_bytes, void* stream) {
   if (!w8) return MOE_ERR_INVALID;
-  return backward_impl(d, w, w8, grad_format, x, sv, dy, dx, g, terms, losses, ws, ws_bytes, stream);
+  return backward_impl(d, w, w8, grad_format, wgrad_fp8, x, sv, dy, dx, g, terms, losses, ws, ws_bytes,
+                       stream);
 }
 
 int moe_fp8_weights_quantize(const moe_desc_t* d, const moe_weights_t* w, const moe_fp8_weights_t* w8,
@@ -917,6 +986,40 @@ int moe_grouped_gemm_fp8_gather(int epi, int64_t G, int64_t M, int64_t N, int64_
   if (M == 0) return MOE_OK;
   MOE_TRY(launch_gemm_fp8(epi, G, M, N, K, offsets, A, a_scale, B, b_scale, C, aux, rows,
                           (hipStream_t)stream));
+  return MOE_OK;
+}
+
+size_t moe_quantize_fp8_colwise_bytes(int64_t G, int64_t M, int64_t C) {
+  if (G < 1 || G > 256 || M < 0 || C <= 0) return 0;
+  return colwise_bytes(G, M, C);
+}
+
+int moe_quantize_fp8_colwise(int64_t G, int64_t M, int64_t C, int dtype, const int32_t* offsets,
+                             const int32_t* rows, int64_t src_rows, const void* x, int32_t* pad_offsets,
+                             uint8_t* q, float* scale, void* stream) {
+  if (G < 1 || G > 256 || M < 0 || C <= 0 || C % 64 || C > 65536 || src_rows < 0) return MOE_ERR_INVALID;
+  if (dtype != MOE_F32 && dtype != MOE_BF16) return MOE_ERR_INVALID;
+  if (M >= (int64_t(1) << 31)) return MOE_ERR_UNSUPPORTED;
+  if (!offsets && G != 1) return MOE_ERR_INVALID;
+  if (!pad_offsets || !q || !scale || (M > 0 && !x) || (rows && M > 0 && src_rows == 0)) return MOE_ERR_INVALID;
+  const void* ptrs[] = {offsets, rows, x, pad_offsets, q, scale};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  MOE_TRY(launch_quantize_fp8_colwise(x, dtype, rows, offsets, (int)G, M, C, pad_offsets, q, scale,
+                                      (hipStream_t)stream));
+  return MOE_OK;
+}
+
+int moe_grouped_gemm_fp8_wgrad(int64_t G, int64_t N, int64_t K, const int32_t* pad_offsets, const uint8_t* A,
+                               const float* a_scale, const uint8_t* B, const float* b_scale, void* C,
+                               void* stream) {
+  if (G < 1 || G > 256 || N <= 0 || K <= 0 || N % 64 || K % 64) return MOE_ERR_INVALID;
+  if (N > 65536 || K > 65536) return MOE_ERR_UNSUPPORTED;
+  if (!pad_offsets || !A || !a_scale || !B || !b_scale || !C) return MOE_ERR_INVALID;
+  const void* ptrs[] = {pad_offsets, A, a_scale, B, b_scale, C};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MOE_ERR_ALIGN;
+  MOE_TRY(launch_gemm_fp8_wgrad(G, N, K, pad_offsets, A, a_scale, B, b_scale, C, (hipStream_t)stream));
   return MOE_OK;
 }
 

@@ -187,7 +187,141 @@ __global__ __launch_bounds__(256) void encode_transposed_kernel(const TX* __rest
   *reinterpret_cast<u32x4*>(q + (g * C + c0 + oc) * R + r0 + orr) = v;
 }
 
+// ---- along the rows of each group of a row-major matrix, stored transposed
+// and padded: the operands of an fp8 weight gradient, whose reduction runs
+// over the rows of one group (one expert's tokens).  Group g owns rows
+// [offsets[g], offsets[g+1]) of x [M, C] (a row map, when given, names the
+// source row of each); its codes form the block q[C * P_g ...] of C rows of
+// P'_g = pad64(rows of g) bytes (row c holds column c of the group, zero past
+// its last row), P_g = sum of the earlier groups' P'; scale[g, c] =
+// max |x[., c]| over the group's rows / 448.
+
+// the padded group offsets P_g (G + 1 entries): one workgroup
+__global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int G, int64_t M,
+                                                          int32_t* __restrict__ pad_off) {
+  __shared__ int part[4];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int v = 0;
+  if (t < G) {
+    const int lo = offsets ? offsets[t] : 0, hi = offsets ? offsets[t + 1] : (int)M;
+    v = (hi - lo + 63) / 64 * 64;
+  }
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int u = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += u;
+  }
+  if (lane == 63) part[w] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < w; ++i) base += part[i];
+  if (t < G) pad_off[t] = base + incl - v;
+  if (t == 0) pad_off[G] = part[0] + part[1] + part[2] + part[3];
+}
+
+// pass 1: one workgroup per (64 columns, group): thread t takes columns
+// 8 (t % 8) .. +7 of every 32nd row of the group from row t / 8
+template <typename TX>
+__global__ __launch_bounds__(256) void seg_col_scale_kernel(const TX* __restrict__ x, const int32_t* __restrict__ rows,
+                                                            const int32_t* __restrict__ offsets, int64_t M,
+                                                            int64_t C, float* __restrict__ scale) {
+  __shared__ float part[32][65];
+  const int t = threadIdx.x, cq = (t & 7) * 8, rp = t >> 3;
+  const int g = blockIdx.y;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  const int64_t lo = offsets ? offsets[g] : 0, hi = offsets ? offsets[g + 1] : M;
+  float m[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) m[u] = 0.0f;
+  for (int64_t r = lo + rp; r < hi; r += 32) {
+    const int64_t src = rows ? (int64_t)rows[r] : r;
+    float f[8];
+    load4(x + src * C + c0 + cq, f);
+    load4(x + src * C + c0 + cq + 4, f + 4);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m[u] = fmaxf(m[u], fabsf(f[u]));
+  }
+#pragma unroll
+  for (int u = 0; u < 8; ++u) part[rp][cq + u] = m[u];
+  __syncthreads();
+  if (t < 64) {
+    float a = 0.0f;
+#pragma unroll 8
+    for (int i = 0; i < 32; ++i) a = fmaxf(a, part[i][t]);
+    scale[(int64_t)g * C + c0 + t] = scale_of(a);
+  }
+}
+
+// pass 2: one workgroup per 64 x 64 tile of the padded groups (blockIdx.y:
+// the 64-row tile counted over all groups' padded rows; beyond the last, none)
+template <typename TX>
+__global__ __launch_bounds__(256) void seg_encode_transposed_kernel(
+    const TX* __restrict__ x, const int32_t* __restrict__ rows, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pad_off, int G, int64_t M, int64_t C, const float* __restrict__ scale,
+    uint8_t* __restrict__ q) {
+  constexpr int PITCH = 80;
+  __shared__ __attribute__((aligned(16))) uint8_t tile[64 * PITCH];
+  const int tm = blockIdx.y;
+  if ((int64_t)tm * 64 >= pad_off[G]) return;
+  int lo_g = 0, hi_g = G;  // the group whose padded rows hold tile tm
+  while (hi_g - lo_g > 1) {
+    const int mid = (lo_g + hi_g) >> 1;
+    if (pad_off[mid] <= tm * 64) lo_g = mid; else hi_g = mid;
+  }
+  const int g = lo_g;
+  const int64_t pg = pad_off[g + 1] - pad_off[g], r0 = (int64_t)tm * 64 - pad_off[g];
+  const int64_t lo = offsets ? offsets[g] : 0, hi = offsets ? offsets[g + 1] : M;
+  const int t = threadIdx.x, rr = (t >> 4) * 4, cc = (t & 15) * 4;
+  const int64_t c0 = (int64_t)blockIdx.x * 64;
+  float s[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) s[u] = scale[(int64_t)g * C + c0 + cc + u];
+  float f[4][4];  // [row][column]
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int64_t r = lo + r0 + rr + i;
+    if (r < hi) {
+      const int64_t src = rows ? (int64_t)rows[r] : r;
+      load4(x + src * C + c0 + cc, f[i]);
+    } else {
+      f[i][0] = f[i][1] = f[i][2] = f[i][3] = 0.0f;
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = fminf(fmaxf(f[i][u] / s[u], -448.0f), 448.0f);
+    uint32_t w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+    *reinterpret_cast<uint32_t*>(tile + (cc + u) * PITCH + rr) = w;
+  }
+  __syncthreads();
+  const int oc = t >> 2, orr = (t & 3) * 16;
+  const u32x4 v = *reinterpret_cast<const u32x4*>(tile + oc * PITCH + orr);
+  *reinterpret_cast<u32x4*>(q + C * (int64_t)pad_off[g] + (c0 + oc) * pg + r0 + orr) = v;
+}
+
 }  // namespace q8
+
+hipError_t launch_quantize_fp8_colwise(const void* x, int dtype, const int32_t* rows, const int32_t* offsets,
+                                       int G, int64_t M, int64_t C, int32_t* pad_off, uint8_t* q, float* scale,
+                                       hipStream_t st) {
+  if (G < 1 || G > 256) return hipErrorInvalidValue;
+  q8::pad_offsets_kernel<<<1, 256, 0, st>>>(offsets, G, M, pad_off);
+  const dim3 g1((unsigned)(C / 64), (unsigned)G), g2((unsigned)(C / 64), (unsigned)(cdiv64(M, 64) + G));
+  if (dtype == MOE_BF16) {
+    q8::seg_col_scale_kernel<bf16_t><<<g1, 256, 0, st>>>((const bf16_t*)x, rows, offsets, M, C, scale);
+    q8::seg_encode_transposed_kernel<bf16_t><<<g2, 256, 0, st>>>((const bf16_t*)x, rows, offsets, pad_off, G, M,
+                                                                 C, scale, q);
+  } else {
+    q8::seg_col_scale_kernel<float><<<g1, 256, 0, st>>>((const float*)x, rows, offsets, M, C, scale);
+    q8::seg_encode_transposed_kernel<float><<<g2, 256, 0, st>>>((const float*)x, rows, offsets, pad_off, G, M,
+                                                                C, scale, q);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_fp8_transposed(const void* x, int dtype, int64_t G, int64_t R, int64_t C,
                                           uint8_t* q, float* scale, hipStream_t st) {

@@ -133,9 +133,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   using WV = Waves<NWV>;
   constexpr int NW = WV::NW, WM = WV::WM, WN = WV::WN, WPR = WV::WPR, FI = WV::FI, FJ = WV::FJ;
   constexpr int LP = WV::LP, LQ = WV::LQ, LT = WV::LT, PAD_BYTES = WV::PAD_BYTES;
-  constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN);
-  constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT);
-  static_assert(!F8 || LAYOUT == MOE_GEMM_NT, "fp8 operands: forward layout only");
+  // fp8 weight gradients (TN with F8) read both operands reduction-contiguous:
+  // the padded, transposed group blocks of the column-wise quantiser
+  constexpr bool W8 = F8 && LAYOUT == MOE_GEMM_TN;
+  constexpr bool P_KC = (LAYOUT != MOE_GEMM_TN) || W8;
+  constexpr bool Q_KC = (LAYOUT == MOE_GEMM_NT) || W8;
+  static_assert(!F8 || LAYOUT != MOE_GEMM_NN, "fp8 operands: forward layout or weight gradient");
+  static_assert(!W8 || (!GA && EPI == MOE_EPI_NONE), "fp8 weight gradient: plain");
   static_assert(!GA || LAYOUT != MOE_GEMM_NN, "gathered rows: NT or TN");
   static_assert(!GA || EPI != MOE_EPI_DSWIGLU, "gathered rows: no dSwiGLU epilogue");
   constexpr bool GN = GA && LAYOUT == MOE_GEMM_NT;  // A rows gathered, fixed per tile
@@ -240,11 +244,22 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       const uint32_t kb = (uint32_t)(kt * BK * 2) + chunk * 16;  // 64 bytes per row per k-step
       if (isP && GN) {
         dma16_off(Ab, gv[i] + kb, dst);
+      } else if (isP && W8) {
+        // group g's block of N rows of P'_g = r_hi - r_lo bytes at N * r_lo
+        const int nrows = (int)(t.i_hi - t.i_lo);
+        const int r = row < nrows ? row : nrows - 1;
+        const int64_t pg = t.r_hi - t.r_lo;
+        dma16_off(Ab + N * t.r_lo + t.i_lo * pg, (uint32_t)r * (uint32_t)pg + kb, dst);
       } else if (isP) {
         const int nrows = (int)(t.i_hi - t.i_lo);
         const int r = row < nrows ? row : nrows - 1;
         const int64_t ld = (LAYOUT == MOE_GEMM_NT) ? K : N;
         dma16_off(Ab + t.i_lo * ld * ES, (uint32_t)r * (uint32_t)(ld * ES) + kb, dst);
+      } else if (W8) {  // the weight gradient's B' rows (K per group)
+        const int nr = (int)(K - t.j0);
+        const int r = row < nr ? row : nr - 1;
+        const int64_t pg = t.r_hi - t.r_lo;
+        dma16_off(Bb + K * t.r_lo + t.j0 * pg, (uint32_t)r * (uint32_t)pg + kb, dst);
       } else {  // NT's B rows
         uint32_t roff;
         if (EPI == MOE_EPI_SWIGLU) {
@@ -285,7 +300,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   // TN: zero the rows of k-step kt past the group end that this lane loaded
   // (called after the lane's own DMA for kt completed, before the barrier)
   auto zero_tail = [&](const Tile& t, int64_t kt) __attribute__((always_inline)) {
-    if (LAYOUT != MOE_GEMM_TN) return;
+    if (LAYOUT != MOE_GEMM_TN || W8) return;  // W8: the padding holds zero codes
     const int64_t rows = t.r_hi - t.r_lo;
     if ((kt + 1) * BK <= rows) return;
     char* st = smem + (kt % STAGES) * SB;
@@ -563,11 +578,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     // (columns at or past N, never stored, read the last four scales: a
     // last column tile narrower than 256 stays inside b_scale)
     auto col_scales = [&](int64_t brow, float* sc) __attribute__((always_inline)) {
-      const float* p = a.b_scale + (int64_t)t.g * N;
+      // (W8: the output's columns are K per group)
+      const int64_t NC = W8 ? K : N;
+      const float* p = a.b_scale + (int64_t)t.g * NC;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         int64_t cidx = brow + kh * 4 + gq * 8;
-        cidx = cidx < N - 4 ? cidx : N - 4;
+        cidx = cidx < NC - 4 ? cidx : NC - 4;
         const float4 v = *reinterpret_cast<const float4*>(p + cidx);
         sc[gq * 4] = v.x; sc[gq * 4 + 1] = v.y; sc[gq * 4 + 2] = v.z; sc[gq * 4 + 3] = v.w;
       }
@@ -711,8 +728,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       __builtin_amdgcn_sched_barrier(0);
       const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
       if (i >= t.i_hi) continue;
-      // fp8: the scale of the row's source (GN: a token row, per token)
-      const float sa = F8 ? a.a_scale[GN ? a.rows[i] : i] : 1.0f;
+      // fp8: the scale of the row's source (GN: a token row, per token; W8:
+      // per group and output row)
+      const float sa = F8 ? a.a_scale[GN ? (int64_t)a.rows[i] : (W8 ? (int64_t)t.g * N + i : i)] : 1.0f;
       if (EPI == MOE_EPI_SWIGLU) {
         // block jt holds gate columns for even jt, up columns for odd jt
         if (X) {
@@ -908,5 +926,26 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
   if (epilogue == MOE_EPI_SWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_SWIGLU, true>(a, st);
   if (epilogue == MOE_EPI_DSWIGLU) return pk::run<MOE_GEMM_NT, MOE_EPI_DSWIGLU, true>(a, st);
   return hipErrorInvalidValue;
+}
+
+// fp8 weight gradient over the padded group blocks (pad_off: the padded group
+// offsets, which set each group's reduction range and block base)
+hipError_t launch_gemm_fp8_wgrad(int64_t G, int64_t N, int64_t K, const int32_t* pad_off, const uint8_t* A,
+                                 const float* a_scale, const uint8_t* B, const float* b_scale, void* C,
+                                 hipStream_t st) {
+  pk::Args a;
+  a.G = (int)G;
+  a.M_total = 0;
+  a.N = N;
+  a.K = K;
+  a.offsets = pad_off;
+  a.A = (const bf16_t*)A;
+  a.B = (const bf16_t*)B;
+  a.C = (bf16_t*)C;
+  a.aux = nullptr;
+  a.a_scale = a_scale;
+  a.b_scale = b_scale;
+  a.rows = nullptr;
+  return pk::run<MOE_GEMM_TN, MOE_EPI_NONE, true>(a, st);
 }
 }  // namespace moe

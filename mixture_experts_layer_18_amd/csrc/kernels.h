@@ -44,6 +44,17 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,
                            const uint8_t* B, const float* b_scale, void* C, void* aux,
                            const int32_t* rows, hipStream_t st, int a_fmt = FP8_E4M3);
+// column-wise over each group's rows, stored transposed and padded to
+// 64-row multiples (the operands of an fp8 weight gradient); writes the
+// padded group offsets pad_off [G+1] first
+hipError_t launch_quantize_fp8_colwise(const void* x, int dtype, const int32_t* rows, const int32_t* offsets,
+                                       int G, int64_t M, int64_t C, int32_t* pad_off, uint8_t* q, float* scale,
+                                       hipStream_t st);
+// fp8 weight gradient C[g] [N, K] = a_scale[g, n] b_scale[g, k] sum_m A'[n, m] B'[k, m]
+// over the padded, transposed group blocks of launch_quantize_fp8_colwise
+hipError_t launch_gemm_fp8_wgrad(int64_t G, int64_t N, int64_t K, const int32_t* pad_off, const uint8_t* A,
+                                 const float* a_scale, const uint8_t* B, const float* b_scale, void* C,
+                                 hipStream_t st);
 hipError_t launch_quantize_fp8_transposed(const void* x, int dtype, int64_t G, int64_t R, int64_t C,
                                           uint8_t* q, float* scale, hipStream_t st);
 // row-wise quantisation; fmt FP8_E4M3 or FP8_E5M2

@@ -30,7 +30,7 @@ def upload_layer(cfg, inp):
 
 
 def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False, terms=None, gather=False,
-            fp8=False, grad_format="e4m3"):
+            fp8=False, grad_format="e4m3", wgrad_fp8=False):
     """gather: no permuted token copy; the gate/up products read x through the token map.
     fp8: the fp8 layer calls (moe_forward_fp8 / moe_backward_fp8) on e4m3 copies of the
     expert weights written by moe_fp8_weights_quantize."""
@@ -54,8 +54,9 @@ def run_gpu(cfg, inp, backward, weights=None, x=None, dy=None, keep_device=False
         dx = torch.empty_like(x)
         losses = torch.zeros(4, dtype=torch.float32, device="cuda") if terms is not None else None
         if fp8:
-            M.moe_backward_fp8(desc, w, w8, x, saved, dy, dx, grads, M.alloc_workspace(desc, "backward_fp8"),
-                               terms=terms, losses=losses, grad_format=grad_format)
+            wsb = M.alloc_workspace(desc, "backward_fp8_wgrad" if wgrad_fp8 else "backward_fp8")
+            M.moe_backward_fp8(desc, w, w8, x, saved, dy, dx, grads, wsb, terms=terms, losses=losses,
+                               grad_format=grad_format, wgrad_fp8=wgrad_fp8)
         else:
             wsb = M.alloc_workspace(desc, "backward")
             M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, terms=terms, losses=losses)

@@ -393,11 +393,15 @@ def test_fp8_layer_argument_checks(lib):
     assert fwd(d, ctypes.byref(q2), 1 << 30) == L.MOE_ERR_ALIGN
     # the backward reads the data-gradient copies only
     g = L.MoeGrads(a, a, a, a, a)
-    bwd = lambda qq, nb, fmt=L.MOE_E4M3: lib.moe_backward_fp8(  # noqa: E731
-        ctypes.byref(d), ctypes.byref(w), qq, fmt, a, ctypes.byref(s), a, a, ctypes.byref(g), None, None, a, nb, None)
+    bwd = lambda qq, nb, fmt=L.MOE_E4M3, wg=0: lib.moe_backward_fp8(  # noqa: E731
+        ctypes.byref(d), ctypes.byref(w), qq, fmt, wg, a, ctypes.byref(s), a, a, ctypes.byref(g), None, None, a, nb,
+        None)
     assert bwd(ctypes.byref(q), 16) == L.MOE_ERR_WORKSPACE
     assert bwd(ctypes.byref(q), 16, L.MOE_E5M2) == L.MOE_ERR_WORKSPACE
     assert bwd(ctypes.byref(q), 1 << 30, 3) == L.MOE_ERR_INVALID
+    assert bwd(ctypes.byref(q), 1 << 30, L.MOE_E4M3, 2) == L.MOE_ERR_INVALID
+    need = lib.moe_workspace_bytes(ctypes.byref(d), L.MOE_WS_BACKWARD_FP8)
+    assert bwd(ctypes.byref(q), need, L.MOE_E4M3, 1) == L.MOE_ERR_WORKSPACE    # fp8 weight gradients need more
     assert bwd(None, 1 << 30) == L.MOE_ERR_INVALID
     q3 = L.MoeFp8Weights(*([a] * 16))
     q3.s_down_tq = None
@@ -435,3 +439,30 @@ def test_mfma_ceiling_argument_checks(lib):
     assert lib.moe_mfma_ceiling(0, 10, None, ctypes.byref(f), None) == L.MOE_ERR_INVALID
     assert lib.moe_mfma_ceiling(0, 10, ctypes.c_void_p(0x10004), ctypes.byref(f), None) == L.MOE_ERR_ALIGN
     assert len(L.MFMA_KINDS) == 4
+
+
+def test_fp8_weight_gradient_calls(lib):
+    """The column-wise quantiser's size query (an upper bound: every group's
+    rows rounded up to 64) and the host checks of both weight-gradient calls;
+    the fp8 weight-gradient workspace adds both operands' codes and scales."""
+    assert lib.moe_quantize_fp8_colwise_bytes(64, 98304, 2048) == 2048 * (98304 + 63 * 64)
+    assert lib.moe_quantize_fp8_colwise_bytes(0, 10, 64) == 0
+    a = ctypes.c_void_p(0x10000)
+    mis = ctypes.c_void_p(0x10004)
+    qc = lib.moe_quantize_fp8_colwise
+    assert qc(4, 100, 96, L.MOE_BF16, a, None, 0, a, a, a, a, None) == L.MOE_ERR_INVALID      # C % 64
+    assert qc(4, 100, 128, L.MOE_BF16, None, None, 0, a, a, a, a, None) == L.MOE_ERR_INVALID  # offsets, G > 1
+    assert qc(1, 100, 128, 9, None, None, 0, a, a, a, a, None) == L.MOE_ERR_INVALID
+    assert qc(1, 100, 128, L.MOE_BF16, None, None, 0, a, None, a, a, None) == L.MOE_ERR_INVALID
+    assert qc(1, 100, 128, L.MOE_BF16, None, mis, 10, a, a, a, a, None) == L.MOE_ERR_ALIGN
+    wg = lib.moe_grouped_gemm_fp8_wgrad
+    assert wg(0, 128, 128, a, a, a, a, a, a, None) == L.MOE_ERR_INVALID
+    assert wg(4, 100, 128, a, a, a, a, a, a, None) == L.MOE_ERR_INVALID
+    assert wg(4, 128, 128, a, a, a, a, None, a, None) == L.MOE_ERR_INVALID
+    assert wg(4, 128, 128, a, mis, a, a, a, a, None) == L.MOE_ERR_ALIGN
+    T, dm, E, k, f = 16384, 2048, 64, 6, 1408
+    dd = make_desc(T, dm, E, k, f, 2, 1408, "sigmoid", True, "bf16")
+    b8 = lib.moe_workspace_bytes(ctypes.byref(dd), L.MOE_WS_BACKWARD_FP8)
+    bw8 = lib.moe_workspace_bytes(ctypes.byref(dd), L.MOE_WS_BACKWARD_FP8_WGRAD)
+    A = T * k
+    assert bw8 - b8 >= (2 * f + dm) * (A + 63 * E) + E * (2 * f + dm) * 4

@@ -195,15 +195,34 @@ def _gpu_dgu(cfg, sv, w8, dy, fmt="e4m3"):
     return dgu, s_dgu, rms
 
 
-def _compare_fp8_layer(cfg, gather, grad_format="e4m3"):
-    print(f"[fp8 layer] {cfg.name} gather={gather} gradients {grad_format}: inputs", flush=True)
+def _fp8_wgrad_gpu(G, offsets, a, b, b_rows=None):
+    """An fp8 weight gradient C[g] = a_g^T b_g through the public calls: both
+    operands quantised column-wise over each group's rows (b read through
+    b_rows when given), then the scaled product.  Returns C [G, N, K] bf16."""
+    Mrows = a.shape[0]
+    N, K = a.shape[1], b.shape[1]
+    pad = torch.empty(G + 1, dtype=torch.int32, device="cuda")
+    qa = torch.empty(M.quantize_fp8_colwise_bytes(G, Mrows, N), dtype=torch.uint8, device="cuda")
+    qb = torch.empty(M.quantize_fp8_colwise_bytes(G, Mrows, K), dtype=torch.uint8, device="cuda")
+    sa = torch.empty(G, N, dtype=torch.float32, device="cuda")
+    sb = torch.empty(G, K, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_colwise(a, G, offsets, pad, qa, sa)
+    M.moe_quantize_fp8_colwise(b, G, offsets, pad, qb, sb, rows=b_rows, M=Mrows)
+    C = torch.empty(G, N, K, dtype=torch.bfloat16, device="cuda")
+    M.moe_grouped_gemm_fp8_wgrad(G, N, K, pad, qa, sa, qb, sb, C)
+    return C
+
+
+def _compare_fp8_layer(cfg, gather, grad_format="e4m3", wgrad_fp8=False):
+    print(f"[fp8 layer] {cfg.name} gather={gather} gradients {grad_format} fp8 weight gradients {wgrad_fp8}: inputs",
+          flush=True)
     inp = synth.make_inputs(cfg, with_dy=True)
     desc = M.desc_from_config(cfg)
     w = R.upload_layer(cfg, inp)
     x, dy = dev(inp["x"]), dev(inp["dy"])
     print(f"[fp8 layer] {cfg.name}: GPU fp8 forward+backward", flush=True)
     g = R.run_gpu(cfg, inp, backward=True, weights=w, x=x, dy=dy, keep_device=True, gather=gather, fp8=True,
-                  grad_format=grad_format)
+                  grad_format=grad_format, wgrad_fp8=wgrad_fp8)
     sv, w8 = g["saved"], g["w8"]
     g_idx = sv["idx"].cpu().numpy()
     g_gate = sv["gate"].cpu().numpy()
@@ -251,20 +270,26 @@ def _compare_fp8_layer(cfg, gather, grad_format="e4m3"):
     dgu, s_dgu, dh_rms = _gpu_dgu(cfg, sv, w8, dy, grad_format)
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     A = T * k
-    dwg = torch.empty(E, 2 * f, d, dtype=torch.bfloat16, device="cuda")
-    if gather:
-        M.moe_grouped_gemm_gather("TN", "none", E, A, 2 * f, d, sv["offsets"], dgu, x, dwg, sv["tok"], T)
+    if wgrad_fp8:
+        dwg = _fp8_wgrad_gpu(E, sv["offsets"], dgu, x if gather else sv["x_perm"], sv["tok"] if gather else None)
     else:
-        M.moe_grouped_gemm("TN", "none", "bf16", E, A, 2 * f, d, sv["offsets"], dgu, sv["x_perm"], dwg,
-                           ws=torch.empty(max(M.grouped_gemm_workspace_bytes("TN", "bf16", E, A, 2 * f, d), 16),
-                                          dtype=torch.uint8, device="cuda"))
+        dwg = torch.empty(E, 2 * f, d, dtype=torch.bfloat16, device="cuda")
+        if gather:
+            M.moe_grouped_gemm_gather("TN", "none", E, A, 2 * f, d, sv["offsets"], dgu, x, dwg, sv["tok"], T)
+        else:
+            M.moe_grouped_gemm("TN", "none", "bf16", E, A, 2 * f, d, sv["offsets"], dgu, sv["x_perm"], dwg,
+                               ws=torch.empty(max(M.grouped_gemm_workspace_bytes("TN", "bf16", E, A, 2 * f, d), 16),
+                                              dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert torch.equal(dwg.view(torch.int16), g["grads"]["d_w_gateup"].view(torch.int16))
     if F:
-        dsg = torch.empty(2 * F, d, dtype=torch.bfloat16, device="cuda")
-        nws = M.grouped_gemm_workspace_bytes("TN", "bf16", 1, T, 2 * F, d)
-        M.moe_grouped_gemm("TN", "none", "bf16", 1, T, 2 * F, d, None, s_dgu, x, dsg,
-                           ws=torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda"))
+        if wgrad_fp8:
+            dsg = _fp8_wgrad_gpu(1, None, s_dgu, x)[0]
+        else:
+            dsg = torch.empty(2 * F, d, dtype=torch.bfloat16, device="cuda")
+            nws = M.grouped_gemm_workspace_bytes("TN", "bf16", 1, T, 2 * F, d)
+            M.moe_grouped_gemm("TN", "none", "bf16", 1, T, 2 * F, d, None, s_dgu, x, dsg,
+                               ws=torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda"))
         torch.cuda.synchronize()
         assert torch.equal(dsg.view(torch.int16), g["grads"]["d_s_gateup"].view(torch.int16))
     gdgu = host(dgu)
@@ -273,7 +298,7 @@ def _compare_fp8_layer(cfg, gather, grad_format="e4m3"):
     fwb = dict(fw, preact=gpre, s_preact=gspre)
     bw = O.backward(oi["x"], oi["w_router"], oi["w_gateup"], oi["w_down"], oi["s_gateup"], oi["s_down"], fwb,
                     oi["dy"], score=cfg.score, renorm=cfg.renorm, fp8=True, forced_dgu=gdgu, forced_s_dgu=gsdgu,
-                    fp8_grad_format=grad_format)
+                    fp8_grad_format=grad_format, fp8_wgrad=wgrad_fp8)
     assert_rounded(gdgu, bw["dgu"], "bf16", "dG | dU", extra=_dswiglu_noise(dh_rms[0], gpre, f))
     if F:
         assert_rounded(gsdgu, bw["s_dgu"], "bf16", "shared dG | dU", extra=_dswiglu_noise(dh_rms[1], gspre, F))
@@ -298,6 +323,15 @@ def test_fp8_layer_e5m2_gradients_against_oracle():
     shared ones quantised to e5m2, weights e4m3), forward and backward
     compared in full."""
     _compare_fp8_layer(SMALL, True, "e5m2")
+
+
+@pytest.mark.parametrize("cfg", [SMALL, FINE], ids=["small", "finegrained"])
+def test_fp8_layer_fp8_weight_gradients_against_oracle(cfg):
+    """The fp8 layer with e4m3 weight gradients (operands quantised along each
+    expert's rows), forward and backward compared in full; every quantiser
+    input is the GPU's after the checks above, so the weight gradients are
+    compared against the oracle's fp8 products of the same codes."""
+    _compare_fp8_layer(cfg, True, "e4m3", True)
 
 
 def test_fp8_layer_finegrained_against_oracle():
@@ -396,3 +430,69 @@ def test_fp8_layer_full_size_experts():
         wd_ref = dyp.T @ gh
         wd_acc = rows * 2.0 ** -24 * (np.abs(dyp).T @ np.abs(gh))
         assert_rounded(host(g["grads"]["d_w_down"][e]), wd_ref, "bf16", f"dW_down, expert {e}", extra=wd_acc)
+
+
+def test_quantize_fp8_colwise_bit_exact():
+    """Column-wise codes over each group's rows, stored transposed and padded:
+    ragged groups, an empty one, a group of one row, rows read through a map;
+    codes and scales bit-exact against the oracle's, zero codes in the
+    padding, the padded offsets as defined."""
+    g = np.random.default_rng(48)
+    G, C = 6, 192
+    m = np.array([70, 0, 1, 130, 64, 33])
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(m)
+    Mrows = int(off[-1])
+    S = 400
+    xf = (g.standard_normal((S, C)) * np.exp(g.uniform(-3, 3, (1, C)))).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(xf)
+    rows = g.integers(0, S, size=Mrows).astype(np.int32)
+    pad = torch.empty(G + 1, dtype=torch.int32, device="cuda")
+    q = torch.full((M.quantize_fp8_colwise_bytes(G, Mrows, C),), 0x55, dtype=torch.uint8, device="cuda")
+    s = torch.empty(G, C, dtype=torch.float32, device="cuda")
+    M.moe_quantize_fp8_colwise(dev(xb), G, dev(off), pad, q, s, rows=torch.from_numpy(rows).cuda(), M=Mrows)
+    torch.cuda.synchronize()
+    pm = (m + 63) // 64 * 64
+    want_pad = np.concatenate([[0], np.cumsum(pm)])
+    assert np.array_equal(pad.cpu().numpy(), want_pad)
+    qh, sh = q.cpu().numpy(), s.cpu().numpy()
+    xv = synth.bf16_bits_to_f32(xb)
+    for e in range(G):
+        blk = qh[C * want_pad[e]: C * want_pad[e + 1]].reshape(C, pm[e])
+        if m[e] == 0:
+            assert np.all(sh[e] == 1.0)
+            continue
+        qo, so = O.quantize_colwise(xv[rows[off[e]:off[e + 1]]])
+        assert np.array_equal(sh[e], so), e
+        assert np.array_equal(blk[:, :m[e]], qo.T), e
+        assert not blk[:, m[e]:].any(), e
+
+
+def test_grouped_gemm_fp8_wgrad_against_oracle():
+    """The fp8 weight gradient C[g] = a_g^T b_g on ragged groups with an empty
+    one (its gradient zero): one bf16 rounding of the oracle's product of the
+    same column-wise codes, plus the fp32 summation bound."""
+    g = np.random.default_rng(49)
+    G, N, K = 5, 192, 320
+    m = np.array([300, 0, 129, 64, 211])
+    off = np.zeros(G + 1, np.int32)
+    off[1:] = np.cumsum(m)
+    Mrows = int(off[-1])
+    ab = _bf16(g, (Mrows, N), 0.1)
+    bb = _bf16(g, (Mrows, K))
+    C = _fp8_wgrad_gpu(G, dev(off), dev(ab), dev(bb))
+    torch.cuda.synchronize()
+    out = host(C)
+    av, bv = synth.bf16_bits_to_f32(ab).astype(np.float64), synth.bf16_bits_to_f32(bb).astype(np.float64)
+    for e in range(G):
+        if m[e] == 0:
+            assert not out[e].any()
+            continue
+        a_e, b_e = av[off[e]:off[e + 1]], bv[off[e]:off[e + 1]]
+        ref = O.wgrad_fp8(a_e, b_e)
+        qa, sa = O.quantize_colwise(a_e)
+        qb, sb = O.quantize_colwise(b_e)
+        Ad = np.abs(O.e4m3_decode(qa)) * sa[None, :]
+        Bd = np.abs(O.e4m3_decode(qb)) * sb[None, :]
+        acc = m[e] * 2.0 ** -24 * (Ad.T @ Bd)
+        assert_rounded(out[e], ref, "bf16", f"dW group {e}", extra=acc)
