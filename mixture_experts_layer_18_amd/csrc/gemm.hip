@@ -259,7 +259,7 @@ static bool use_mfma(const GemmProblem& p) {
 }
 
 size_t gemm_workspace_bytes(const GemmProblem& p) {
-  if (use_mfma(p)) return gemm_big_supported(p) ? 0 : gemm_mfma_workspace_bytes(p);
+  if (use_mfma(p)) return gemm_big_supported(p) ? gemm_big_workspace_bytes(p) : gemm_mfma_workspace_bytes(p);
   const int s = simt_splits(p);
   if (s <= 1) return 0;
   return (size_t)s * p.G * p.N * p.K * sizeof(float);
@@ -358,7 +358,7 @@ hipError_t launch_grouped_gemm(const GemmProblem& p, void* ws, size_t ws_bytes, 
   ka.part = (float*)ws;
   ka.nsplit = 1;
   if (use_mfma(p)) {
-    if (gemm_big_supported(p)) return launch_gemm_big(p, st);
+    if (gemm_big_supported(p)) return launch_gemm_big(p, ws, ws_bytes, st);
     return launch_gemm_mfma(p, ws, ws_bytes, st);
   }
   ka.nsplit = simt_splits(p);

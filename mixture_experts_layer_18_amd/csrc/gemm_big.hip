@@ -85,6 +85,7 @@ struct Args {
   const float* a_scale;  // fp8: per-row scales of A [M_total]
   const float* b_scale;  // fp8: per-row scales of B [G, N]
   const int32_t* rows;   // GA: source row of each routed row (NT: of A, TN: of B)
+  int nslice;            // SL: row slices of the one group (C: fp32 partials [nslice, N, K])
 };
 constexpr int RING = 8;  // GA TN: map stages held per wave
 
@@ -128,7 +129,11 @@ struct Tile {
 // PF: the format of A's codes (P operand) in the fp8 products, FP8_E4M3 or
 // FP8_E5M2 (the matrix cores take the operand formats as instruction fields);
 // B's codes are e4m3.
-template <int LAYOUT, int EPI, bool F8, bool GA, int NWV, int PF = FP8_E4M3>
+// SL: a one-group weight gradient with too few output tiles to fill the chip
+// runs as a.nslice equal row slices of the group (whole 32-row k-steps, the
+// last slice ragged); slice s writes its fp32 sums to C[s] ([nslice, N, K]),
+// which are added in slice order afterwards.
+template <int LAYOUT, int EPI, bool F8, bool GA, int NWV, int PF = FP8_E4M3, bool SL = false>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   using WV = Waves<NWV>;
   constexpr int NW = WV::NW, WM = WV::WM, WN = WV::WN, WPR = WV::WPR, FI = WV::FI, FJ = WV::FJ;
@@ -142,6 +147,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   static_assert(!W8 || (!GA && EPI == MOE_EPI_NONE), "fp8 weight gradient: plain");
   static_assert(!GA || LAYOUT != MOE_GEMM_NN, "gathered rows: NT or TN");
   static_assert(!GA || EPI != MOE_EPI_DSWIGLU, "gathered rows: no dSwiGLU epilogue");
+  static_assert(!SL || (LAYOUT == MOE_GEMM_TN && !F8 && !GA), "row slices: bf16 weight gradient");
   constexpr bool GN = GA && LAYOUT == MOE_GEMM_NT;  // A rows gathered, fixed per tile
   constexpr bool GT = GA && LAYOUT == MOE_GEMM_TN;  // B k-rows gathered through the ring
   constexpr int LV = LT + (GT ? 1 : 0);             // vector-memory instructions per k-step
@@ -164,7 +170,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   if (LAYOUT == MOE_GEMM_TN) {
     ncols = K;
     tn_n = (int)cdiv64(K, TN);
-    total = a.G * (int)cdiv64(N, TM) * tn_n;
+    total = (SL ? a.nslice : a.G) * (int)cdiv64(N, TM) * tn_n;
   } else {
     int n = 0;
     if (tid < a.G) n = (group_row(a.offsets, tid + 1, a.M_total) - group_row(a.offsets, tid, a.M_total) + TM - 1) / TM;
@@ -184,8 +190,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       const int g = L / per_g, rem = L - g * per_g;
       const int ti = rem / tn_n, tj = rem - ti * tn_n;
       t.g = __builtin_amdgcn_readfirstlane(g);
-      t.r_lo = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g, a.M_total));
-      t.r_hi = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g + 1, a.M_total));
+      if constexpr (SL) {
+        // slice g of the group's k-steps: kper whole steps each
+        const int64_t r0 = group_row(a.offsets, 0, a.M_total), r1 = group_row(a.offsets, 1, a.M_total);
+        const int64_t kper = cdiv64(cdiv64(r1 - r0, BK), a.nslice) * BK;
+        const int64_t lo = r0 + t.g * kper, hi = lo + kper;
+        t.r_lo = __builtin_amdgcn_readfirstlane((int)(lo < r1 ? lo : r1));
+        t.r_hi = __builtin_amdgcn_readfirstlane((int)(hi < r1 ? hi : r1));
+      } else {
+        t.r_lo = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g, a.M_total));
+        t.r_hi = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g + 1, a.M_total));
+      }
       t.i_lo = (int64_t)__builtin_amdgcn_readfirstlane(ti) * TM;
       t.i_hi = t.i_lo + TM < N ? t.i_lo + TM : N;
       t.j0 = (int64_t)__builtin_amdgcn_readfirstlane(tj) * TN;
@@ -781,6 +796,18 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
           }
+          if constexpr (SL) {
+            // fp32 partial of slice t.g: lane kh holds columns gq*8 + kh*4 .. +3
+            float* prow = reinterpret_cast<float*>(a.C) + ((int64_t)t.g * N + i) * K + c;
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int cc = gq * 8 + kh * 4;
+              if (c + cc < K)
+                *reinterpret_cast<float4*>(prow + cc) =
+                    make_float4(v[gq * 4], v[gq * 4 + 1], v[gq * 4 + 2], v[gq * 4 + 3]);
+            }
+            continue;
+          }
           bf16_t* row = (LAYOUT == MOE_GEMM_TN) ? C + ((int64_t)t.g * N + i) * K : C + i * ncols;
           store_tile_row(row + c, v, kh, ncols - c);
         }
@@ -810,20 +837,37 @@ static int grid_size() {
 
 // waves per workgroup (Waves<4> is the one-wave-per-SIMD layout it replaced)
 constexpr int kWaves = 8;
-template <int LAYOUT, int EPI, bool F8 = false, bool GA = false, int NWV = kWaves, int PF = FP8_E4M3>
+template <int LAYOUT, int EPI, bool F8 = false, bool GA = false, int NWV = kWaves, int PF = FP8_E4M3,
+          bool SL = false>
 static hipError_t run(const Args& a, hipStream_t st) {
   if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI, F8, GA, NWV, PF><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, F8, GA, NWV, PF, SL><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a);
   return hipGetLastError();
 }
 
 }  // namespace pk
 
+// A one-group weight gradient (shared experts) with fewer than 1024 output
+// tiles: the number of equal row slices that gives at least 128 tiles (half
+// the CUs) with every slice at least 32 k-steps long, 1 when the tiles alone
+// reach 128; 0 when no such split exists (the two-workgroup kernel takes it).
+// Measured on the 7B-style layer's shared experts: 176 tiles unsliced ran
+// 18 % faster than the two-workgroup kernel's row slices, 88 tiles unsliced
+// 50 % slower.
+static int one_group_slices(const GemmProblem& p) {
+  const int64_t tiles = cdiv64(p.N, 256) * cdiv64(p.K, 256);
+  const int64_t ks = cdiv64(p.M_total, 32);
+  int s = 1;
+  while (tiles * s < 128 && s < 8 && ks >= 2 * s * 32) s *= 2;
+  return tiles * s >= 128 ? s : 0;
+}
+
 // Which products this kernel takes (the rest go to the two-workgroup kernel):
 // NT with either epilogue (SwiGLU: the hidden width a multiple of 128, so that
 // a tile pairs 128 gate with 128 up columns), the plain data gradient, and the
-// weight gradient when it has enough 256 x 256 tiles to fill
-// the chip without row slices (gathered rows: any tile count).
+// weight gradient when it has enough 256 x 256 tiles to fill the chip without
+// row slices (gathered rows: any tile count), or is one group that row slices
+// of its own bring to 128 tiles.
 //
 // Operand DMA offsets are 32-bit byte offsets from a per-tile base: NT's
 // SwiGLU weight rows span one expert's whole [N, K] block (gate and up
@@ -848,14 +892,22 @@ bool gemm_big_supported(const GemmProblem& p) {
     if (p.M_total * p.N * 2 > lim) return false;
     if (p.rows) return p.K % 256 == 0;
     if (p.M_total * p.K * 2 > lim) return false;
-    return p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256;
+    if (p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256) return true;
+    return p.G == 1 && p.N % 8 == 0 && p.K % 8 == 0 && one_group_slices(p) > 0;
   }
   if (p.layout == MOE_GEMM_NN)
     return (p.epilogue == MOE_EPI_NONE || p.epilogue == MOE_EPI_DSWIGLU) && p.N * p.K * 2 <= lim;
   return false;
 }
 
-hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
+size_t gemm_big_workspace_bytes(const GemmProblem& p) {
+  if (p.layout != MOE_GEMM_TN || p.rows || p.G != 1 || p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256)
+    return 0;
+  const int s = one_group_slices(p);
+  return s > 1 ? (size_t)s * p.N * p.K * sizeof(float) : 0;
+}
+
+hipError_t launch_gemm_big(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st) {
   pk::Args a;
   a.G = (int)p.G;
   a.M_total = p.M_total;
@@ -868,6 +920,17 @@ hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st) {
   a.aux = (bf16_t*)p.aux;
   a.a_scale = a.b_scale = nullptr;
   a.rows = p.rows;
+  a.nslice = 1;
+  if (const size_t wsb = gemm_big_workspace_bytes(p)) {
+    // one group in row slices: fp32 partials in the workspace, summed in
+    // slice order into C
+    if (!ws || ws_bytes < wsb) return hipErrorInvalidValue;
+    a.nslice = one_group_slices(p);
+    a.C = (bf16_t*)ws;
+    hipError_t e = pk::run<MOE_GEMM_TN, MOE_EPI_NONE, false, false, pk::kWaves, FP8_E4M3, true>(a, st);
+    if (e != hipSuccess) return e;
+    return launch_split_reduce((const float*)ws, a.nslice, p.N * p.K, p.C, MOE_BF16, st);
+  }
   if (p.rows) {
     if (p.layout == MOE_GEMM_NT && p.epilogue == MOE_EPI_NONE)
       return pk::run<MOE_GEMM_NT, MOE_EPI_NONE, false, true>(a, st);
@@ -909,6 +972,7 @@ hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, 
   a.a_scale = a_scale;
   a.b_scale = b_scale;
   a.rows = rows;
+  a.nslice = 1;
   if (a_fmt == FP8_E5M2) {
     // e5m2 A codes: the data gradients' gradient operands
     if (rows) return hipErrorInvalidValue;
@@ -946,6 +1010,7 @@ hipError_t launch_gemm_fp8_wgrad(int64_t G, int64_t N, int64_t K, const int32_t*
   a.a_scale = a_scale;
   a.b_scale = b_scale;
   a.rows = nullptr;
+  a.nslice = 1;
   return pk::run<MOE_GEMM_TN, MOE_EPI_NONE, true>(a, st);
 }
 }  // namespace moe

@@ -38,7 +38,8 @@ hipError_t launch_gemm_mfma(const GemmProblem& p, void* ws, size_t ws_bytes,
                             hipStream_t st);  // bf16 operands only
 // persistent 256 x 256 kernel (gemm_big.hip) for the products it supports
 bool gemm_big_supported(const GemmProblem& p);
-hipError_t launch_gemm_big(const GemmProblem& p, hipStream_t st);
+size_t gemm_big_workspace_bytes(const GemmProblem& p);  // fp32 row-slice partials (one-group TN)
+hipError_t launch_gemm_big(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st);
 // fp8 (e4m3) forward products with row scales, persistent kernel
 hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,

@@ -59,14 +59,18 @@ def test_queries(lib):
 
 def test_weight_gradient_slice_counts(lib):
     """Row-slice counts of weight gradients with few output tiles, read back
-    through the workspace size (slices x G x N x K fp32 partials): the
-    shared-expert products of the 7B-style layer take 4 and 5 slices (a third
-    workgroup round of 32 workgroups is what 3 and 6 would leave), the large
-    layer's need none, and slices keep at least 512 rows."""
+    through the workspace size (slices x G x N x K fp32 partials).  One group
+    on the persistent kernel: sliced until it has 128 output tiles, each slice
+    at least 32 k-steps; so the 7B-style layer's shared gate/up weight gradient
+    (176 tiles) takes none and its shared down weight gradient (88 tiles) two,
+    and the large layer's need none.  Shapes that cannot reach 128 tiles go to
+    the two-workgroup kernel, whose slices keep at least 512 rows."""
     ws = lambda G, M, N, K: lib.moe_grouped_gemm_workspace_bytes(L.MOE_GEMM_TN, L.MOE_BF16, G, M, N, K)  # noqa: E731
-    assert ws(1, 16384, 5632, 2048) == 4 * 5632 * 2048 * 4
-    assert ws(1, 16384, 2048, 2816) == 5 * 2048 * 2816 * 4
+    assert ws(1, 16384, 5632, 2048) == 0
+    assert ws(1, 16384, 2048, 2816) == 2 * 2048 * 2816 * 4
     assert ws(1, 65536, 4096, 4096) == 0
+    # 20 tiles: 8 slices of 33 k-steps (the last one 26), 160 tiles
+    assert ws(1, 8195, 1024, 1280) == 8 * 1024 * 1280 * 4
     assert ws(1, 4096, 256, 384) == 8 * 256 * 384 * 4
     assert ws(1, 4000, 256, 384) == 7 * 256 * 384 * 4
     assert ws(1, 600, 256, 384) == 0

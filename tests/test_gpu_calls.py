@@ -300,6 +300,38 @@ def test_weight_gradient_row_slices(rows):
                            ws[: ws_n // 2])
 
 
+@pytest.mark.parametrize("Mt,N,K,slices", [(8195, 1024, 1280, 8), (4100, 2048, 2816, 2), (1000, 4096, 2048, 1)],
+                         ids=["20-tiles", "88-tiles", "128-tiles"])
+def test_one_group_weight_gradient_persistent(Mt, N, K, slices):
+    """A one-group weight gradient (the shared experts' shape) with fewer than
+    1024 output tiles on the persistent kernel: cut into equal row slices of
+    whole k-steps (the last one ragged) until 128 tiles run, fp32 partials
+    summed in slice order; with 128 tiles of its own, unsliced."""
+    print(f"[gemm] TN one group M={Mt} N={N} K={K} slices={slices}", flush=True)
+    ws_n = M.grouped_gemm_workspace_bytes("TN", "bf16", 1, Mt, N, K)
+    assert ws_n == (slices * N * K * 4 if slices > 1 else 0)
+    g = np.random.default_rng(Mt + N + K)
+    A = _rand(g, (Mt, N), "bf16")
+    B = _rand(g, (Mt, K), "bf16")
+    ws = torch.empty(max(ws_n, 256), dtype=torch.uint8, device="cuda")
+    C = torch.full((1, N, K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    off = np.array([0, Mt], np.int32)
+    M.moe_grouped_gemm("TN", "none", "bf16", 1, Mt, N, K, dev(off), dev(A), dev(B), C, None, ws)
+    torch.cuda.synchronize()
+    f64 = lambda a: synth.as_f64(a, "bf16")  # noqa: E731
+    ref = (f64(A).T @ f64(B))[None]
+    assert_rounded(host(C), ref, "bf16", "C")
+    # no offset table (one group) gives the same bits
+    C2 = torch.full_like(C, float("nan"))
+    M.moe_grouped_gemm("TN", "none", "bf16", 1, Mt, N, K, None, dev(A), dev(B), C2, None, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(C.view(torch.int16), C2.view(torch.int16))
+    if slices > 1:
+        with pytest.raises(M.MoeError):
+            M.moe_grouped_gemm("TN", "none", "bf16", 1, Mt, N, K, dev(off), dev(A), dev(B), C, None,
+                               ws[: ws_n // 2])
+
+
 def _dswiglu_ref(dY, Wd_e, Gm, U):
     """dG | dU of the oracle's SwiGLU backward with upstream dY through the
     down weight Wd_e [N, K] (here the product dH = dY Wd_e)."""
