@@ -155,6 +155,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   constexpr int BKE = BK * 2 / ES;       // elements per k-step (64 bytes per row)
   __shared__ __attribute__((aligned(1024))) char smem[STAGES * SB + PAD_BYTES];
   __shared__ int s_pref[256];
+  __shared__ int scratch_rows[LAYOUT == MOE_GEMM_TN ? 256 : 1];
   __shared__ int scratch[NW];
   __shared__ __attribute__((aligned(256))) int ring[GT ? NW * RING * 64 : 1];
 
@@ -171,6 +172,24 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     ncols = K;
     tn_n = (int)cdiv64(K, TN);
     total = (SL ? a.nslice : a.G) * (int)cdiv64(N, TM) * tn_n;
+    if (!SL && a.G > 1) {
+      // Groups in order of decreasing row count (ties: lower index first), so
+      // that the tiles of one round of the static walk reduce over similar
+      // lengths: s_pref[rank] = group.  A weight-gradient tile costs its
+      // group's rows, and experts' loads are ragged.
+      if (tid < a.G) scratch_rows[tid] = group_row(a.offsets, tid + 1, a.M_total) - group_row(a.offsets, tid, a.M_total);
+      __syncthreads();
+      if (tid < a.G) {
+        const int mine = scratch_rows[tid];
+        int rank = 0;
+        for (int h = 0; h < a.G; ++h) {
+          const int o = scratch_rows[h];
+          rank += (o > mine) || (o == mine && h < tid);
+        }
+        s_pref[rank] = tid;
+      }
+      __syncthreads();
+    }
   } else {
     int n = 0;
     if (tid < a.G) n = (group_row(a.offsets, tid + 1, a.M_total) - group_row(a.offsets, tid, a.M_total) + TM - 1) / TM;
@@ -187,7 +206,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     Tile t;
     if (LAYOUT == MOE_GEMM_TN) {
       const int per_g = (int)cdiv64(N, TM) * tn_n;
-      const int g = L / per_g, rem = L - g * per_g;
+      const int gs = L / per_g, rem = L - gs * per_g;
+      const int g = (!SL && a.G > 1) ? s_pref[gs] : gs;
       const int ti = rem / tn_n, tj = rem - ti * tn_n;
       t.g = __builtin_amdgcn_readfirstlane(g);
       if constexpr (SL) {
