@@ -507,6 +507,15 @@ def fp8_down_dgrad(M, cfg, saved, w, stream, timed_ms, flop, bf16_s):
                     "separately"}
 
 
+def paired_flops(flops):
+    """Stage flops when each routed weight gradient runs in one launch with
+    its shared-expert counterpart (stages down_wgrad and gate_up_wgrad)."""
+    fl = dict(flops)
+    fl["down_wgrad"] += fl["shared_down_wgrad"]
+    fl["gate_up_wgrad"] += fl["shared_gate_up_wgrad"]
+    return fl
+
+
 def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops, wgrad_fp8=False):
     """The whole layer through the fp8 calls (moe_forward_fp8 and, for a
     training workload, moe_backward_fp8) on the same inputs, timed like the
@@ -559,10 +568,15 @@ def fp8_layer(M, cfg, desc, w, x, dy, training, stream, steps, bf16_ms, flops, w
     st = M.stage_times()
     M.stage_timing(False)
     stages = {}
+    paired = (cfg.n_shared > 0 and training and st.get("shared_down_wgrad", (0.0, 0))[1] == 0)
+    if paired:
+        flops = paired_flops(flops)
     for name, (sms, n) in st.items():
         if n == 0:
             continue
         e = {"us": sms * 1e3 / n, "launches": n}
+        if paired and name in ("down_wgrad", "gate_up_wgrad"):
+            e["includes"] = "shared_" + name
         if name in flops and not name.startswith("router"):
             per = n // min(steps, 5)
             tf = flops[name] / (sms * 1e-3 / n) / 1e12 if per == 1 else None
@@ -763,6 +777,10 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
         torch.cuda.synchronize()
         return a.elapsed_time(b) / reps
 
+    # the shared experts' weight gradients run inside the routed launches
+    # when the two are paired (no shared weight-gradient stage of their own)
+    paired = F > 0 and training and stages.get("shared_down_wgrad", (0.0, 0))[1] == 0
+    fl_st = paired_flops(flops) if paired else flops
     stage_out = {}
     for name, (ms, n) in stages.items():
         if n == 0:
@@ -773,13 +791,15 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
             # the fp32 products on the bf16 matrix cores (three exact partial
             # products per term): bound by streaming x, rated against HBM
             e.update(tflops=flops[name] / (us * 1e-6) / 1e12)
-        elif name in flops:
-            tf = flops[name] / (us * 1e-6) / 1e12
+        elif name in fl_st:
+            tf = fl_st[name] / (us * 1e-6) / 1e12
             peak = PEAK_FP32_TFLOPS if (name.startswith("router") or cfg.dtype == "f32") else PEAK_BF16_TFLOPS
             e.update(tflops=tf, frac=tf / peak)
         if name in hbm_bytes:
             gbs = hbm_bytes[name] / (us * 1e-6) / 1e9
             e.update(gbs=gbs, frac=gbs / PEAK_HBM_GBS)
+        if paired and name in ("down_wgrad", "gate_up_wgrad"):
+            e["includes"] = "shared_" + name
         stage_out[name] = e
     t_gu = stage_out["gate_up"]["us"] * 1e-6
     t_dn = stage_out["down"]["us"] * 1e-6

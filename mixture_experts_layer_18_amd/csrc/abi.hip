@@ -128,6 +128,7 @@ struct BwdWs {
   float* dlogits;  // [T, E]
   void* s_dgu;     // [T, 2F]
   void* dx_shared; // [T, d]
+  int32_t* iota;   // [T] identity row map (shared experts)
   void* gemm;      // split partials
   size_t gemm_bytes;
   uint8_t* q;      // fp8: the quantised operand of each data gradient in turn
@@ -156,6 +157,9 @@ size_t bwd_ws(const moe_desc_t* d, bool fp8, void* ws, BwdWs* out, bool wgrad8 =
   w.dlogits = (float*)c.take((size_t)T * d->num_experts * sizeof(float));
   w.terms = c.take(router_terms_ws_bytes(T, d->num_experts));
   w.s_dgu = F > 0 ? c.take((size_t)T * 2 * F * es) : nullptr;
+  // the identity row map of the shared gate/up weight gradient when it runs
+  // in one launch with the routed one, whose token rows are gathered
+  w.iota = F > 0 ? (int32_t*)c.take((size_t)T * sizeof(int32_t)) : nullptr;
   w.dx_shared = F > 0 ? c.take((size_t)T * D * es) : nullptr;
   w.gemm_bytes = backward_gemm_ws(d);
   w.gemm = c.take(w.gemm_bytes);
@@ -754,9 +758,48 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
                                    sv->offsets, bw.dy_perm, w->w_down, bw.dgu, sv->preact),
                                 nullptr, 0, st));
   }
+  // the shared experts' down data gradient (-> their dG | dU)
+  auto shared_down_dgrad = [&]() -> int {
+    if (fp8) {
+      if (!fused_q)
+        MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q_dy, bw.qs_dy, st, gf));
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD,
+                launch_gemm_fp8(MOE_EPI_DSWIGLU, 1, T, F, D, nullptr, bw.q_dy, bw.qs_dy, w8->s_down_tq,
+                                w8->s_down_ts, bw.s_dgu, sv->s_preact, nullptr, st, gf));
+    } else {
+      MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
+                                     nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
+                                  nullptr, 0, st));
+    }
+    return MOE_OK;
+  };
+  // bf16 weight gradients with shared experts: each routed weight gradient
+  // and its shared counterpart run as one launch of the persistent kernel,
+  // the shared experts' few long tiles first (so their down data gradient
+  // runs before the weight gradients)
+  GemmProblem dw_r = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f, sv->offsets, bw.dy_perm, sv->h,
+                        g->d_w_down, nullptr);
+  GemmProblem guw = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D, sv->offsets, bw.dgu,
+                       gather ? x : sv->x_perm, g->d_w_gateup, nullptr);
+  guw.rows = gather ? sv->tok : nullptr;
+  const GemmProblem dw_s = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, D, F, nullptr, dy, sv->s_h,
+                              g->d_s_down, nullptr);
+  GemmProblem guw_s = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, 1, T, 2 * F, D, nullptr, bw.s_dgu, x,
+                         g->d_s_gateup, nullptr);
+  guw_s.rows = gather ? bw.iota : nullptr;
+  const bool paired = !wg8 && F > 0 && T > 0 && gemm_big_pair_supported(dw_r, dw_s) &&
+                      gemm_big_pair_supported(guw, guw_s);
+  if (paired) {
+    s = shared_down_dgrad();
+    if (s) return s;
+  }
   // 3. down weight gradient, 4. gate/up weight gradient (token rows of
   // x_perm, or of x through tok)
-  if (wg8) {
+  if (paired) {
+    MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_gemm_big_pair(dw_r, dw_s, st));
+    if (gather) MOE_TRY(launch_iota(bw.iota, T, st));
+    MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_gemm_big_pair(guw, guw_s, st));
+  } else if (wg8) {
     MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(bw.dy_perm, nullptr, sv->offsets, (int)E, A, D, bw.pad, bw.wa, bw.wsa));
     MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(sv->h, nullptr, sv->offsets, (int)E, A, f, bw.pad, bw.wb, bw.wsb));
     MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_gemm_fp8_wgrad(E, D, f, bw.pad, bw.wa, bw.wsa, bw.wb, bw.wsb,
@@ -767,12 +810,7 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
     MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_gemm_fp8_wgrad(E, 2 * f, D, bw.pad, bw.wa, bw.wsa, bw.wb, bw.wsb,
                                                              g->d_w_gateup, st));
   } else {
-    MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, D, f,
-                                                           sv->offsets, bw.dy_perm, sv->h, g->d_w_down, nullptr),
-                                                        bw.gemm, bw.gemm_bytes, st));
-    GemmProblem guw = gp(MOE_GEMM_TN, MOE_EPI_NONE, dt, dt, dt, E, A, 2 * f, D, sv->offsets, bw.dgu,
-                         gather ? x : sv->x_perm, g->d_w_gateup, nullptr);
-    guw.rows = gather ? sv->tok : nullptr;
+    MOE_STAGE(MOE_STAGE_DOWN_WGRAD, launch_grouped_gemm(dw_r, bw.gemm, bw.gemm_bytes, st));
     MOE_STAGE(MOE_STAGE_GATE_UP_WGRAD, launch_grouped_gemm(guw, bw.gemm, bw.gemm_bytes, st));
   }
   // 5. gate/up data gradient (written over dy_perm, which is no longer needed;
@@ -790,18 +828,13 @@ static int backward_impl(const moe_desc_t* d, const moe_weights_t* w, const moe_
   }
   // 6. shared experts
   if (F > 0) {
-    if (fp8) {
-      if (!fused_q)
-        MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, launch_quantize_fp8(dy, dt, T, (int)D, bw.q_dy, bw.qs_dy, st, gf));
-      MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD,
-                launch_gemm_fp8(MOE_EPI_DSWIGLU, 1, T, F, D, nullptr, bw.q_dy, bw.qs_dy, w8->s_down_tq,
-                                w8->s_down_ts, bw.s_dgu, sv->s_preact, nullptr, st, gf));
-    } else {
-      MOE_STAGE(MOE_STAGE_SHARED_DOWN_DGRAD, launch_grouped_gemm(gp(MOE_GEMM_NN, MOE_EPI_DSWIGLU, dt, dt, dt, 1, T, D, F,
-                                     nullptr, dy, w->s_down, bw.s_dgu, sv->s_preact),
-                                  nullptr, 0, st));
+    if (!paired) {
+      s = shared_down_dgrad();
+      if (s) return s;
     }
-    if (wg8) {
+    if (paired) {
+      // the weight gradients ran with the routed ones
+    } else if (wg8) {
       MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(dy, nullptr, nullptr, 1, T, D, bw.pad_s, bw.wa, bw.wsa));
       MOE_STAGE(MOE_STAGE_FP8_QUANTIZE, quant_w(sv->s_h, nullptr, nullptr, 1, T, F, bw.pad_s, bw.wb, bw.wsb));
       MOE_STAGE(MOE_STAGE_SHARED_DOWN_WGRAD, launch_gemm_fp8_wgrad(1, D, F, bw.pad_s, bw.wa, bw.wsa, bw.wb, bw.wsb,

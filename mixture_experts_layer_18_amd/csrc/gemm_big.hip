@@ -133,8 +133,16 @@ struct Tile {
 // runs as a.nslice equal row slices of the group (whole 32-row k-steps, the
 // last slice ragged); slice s writes its fp32 sums to C[s] ([nslice, N, K]),
 // which are added in slice order afterwards.
-template <int LAYOUT, int EPI, bool F8, bool GA, int NWV, int PF = FP8_E4M3, bool SL = false>
-__global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
+// MP: two weight gradients in one launch: b_in (one group over all tokens:
+// the shared experts), whose few long tiles would leave CUs idle in a launch
+// of their own, then a_in (the routed experts).  Every workgroup first walks
+// b_in's tiles as in a launch of its own (lw, lw + W, ...); the workgroups
+// without one in its last round then take R rounds of a_in's tiles, the
+// tiles of largest groups, about one of b_in's tiles in k-steps; then every
+// workgroup walks the rest of a_in's tiles.  With GA both gather their B rows
+// (b_in's map may be the identity).
+template <int LAYOUT, int EPI, bool F8, bool GA, int NWV, int PF = FP8_E4M3, bool SL = false, bool MP = false>
+__global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in) {
   using WV = Waves<NWV>;
   constexpr int NW = WV::NW, WM = WV::WM, WN = WV::WN, WPR = WV::WPR, FI = WV::FI, FJ = WV::FJ;
   constexpr int LP = WV::LP, LQ = WV::LQ, LT = WV::LT, PAD_BYTES = WV::PAD_BYTES;
@@ -148,6 +156,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
   static_assert(!GA || LAYOUT != MOE_GEMM_NN, "gathered rows: NT or TN");
   static_assert(!GA || EPI != MOE_EPI_DSWIGLU, "gathered rows: no dSwiGLU epilogue");
   static_assert(!SL || (LAYOUT == MOE_GEMM_TN && !F8 && !GA), "row slices: bf16 weight gradient");
+  static_assert(!MP || (LAYOUT == MOE_GEMM_TN && !F8 && !SL), "paired problems: bf16 weight gradients");
   constexpr bool GN = GA && LAYOUT == MOE_GEMM_NT;  // A rows gathered, fixed per tile
   constexpr bool GT = GA && LAYOUT == MOE_GEMM_TN;  // B k-rows gathered through the ring
   constexpr int LV = LT + (GT ? 1 : 0);             // vector-memory instructions per k-step
@@ -161,9 +170,14 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: SGPR arithmetic
-  const int64_t N = a.N, K = a.K;
   const int nwg = gridDim.x, per = nwg >> 3;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int lw = xcd * per + slot;  // logical workgroup: XCD-contiguous
+
+  // One walk over the tiles of problem a.  after_b (MP): a_in's walk, which
+  // follows b_in's.
+  auto walk = [&](const Args& a, const bool after_b) __attribute__((always_inline)) {
+  const int64_t N = a.N, K = a.K;
 
   // ------------------------------------------------------------ tile table
   int total, tn_n, mt_total = 0;
@@ -172,7 +186,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     ncols = K;
     tn_n = (int)cdiv64(K, TN);
     total = (SL ? a.nslice : a.G) * (int)cdiv64(N, TM) * tn_n;
-    if (!SL && a.G > 1) {
+    if (!SL) {
       // Groups in order of decreasing row count (ties: lower index first), so
       // that the tiles of one round of the static walk reduce over similar
       // lengths: s_pref[rank] = group.  A weight-gradient tile costs its
@@ -207,7 +221,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     if (LAYOUT == MOE_GEMM_TN) {
       const int per_g = (int)cdiv64(N, TM) * tn_n;
       const int gs = L / per_g, rem = L - gs * per_g;
-      const int g = (!SL && a.G > 1) ? s_pref[gs] : gs;
+      const int g = SL ? gs : s_pref[gs];
       const int ti = rem / tn_n, tj = rem - ti * tn_n;
       t.g = __builtin_amdgcn_readfirstlane(g);
       if constexpr (SL) {
@@ -420,8 +434,46 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
 
   const int wp = wave / WPR, wq = wave % WPR;
   const int r32 = lane & 31, kh = lane >> 5;
-  int L = xcd * per + slot;
-  if (L >= total) return;
+  // this workgroup's k-th tile of the walk (false past its end)
+  int r0 = 0, R = 0;
+  if (MP && after_b) {
+    // b_in's last round left workgroups r0.. without a tile: they first take
+    // R rounds of this walk's tiles (largest groups first), the number whose
+    // k-steps come closest to one of b_in's tiles (k-steps plus about 6 for
+    // the epilogue)
+    constexpr int EPI_K = 6;
+    const int n0 = (int)(cdiv64(b_in.N, TM) * cdiv64(b_in.K, TN));
+    r0 = n0 % nwg;
+    if (r0 > 0) {
+      const int64_t hc =
+          cdiv64(group_row(b_in.offsets, 1, b_in.M_total) - group_row(b_in.offsets, 0, b_in.M_total), BK) + EPI_K;
+      const int per_g = (int)cdiv64(N, TM) * tn_n;
+      int64_t sum = 0;
+      while (R < 256) {
+        const int Lr = R * (nwg - r0);
+        if (Lr >= total) break;
+        const int64_t c = cdiv64(scratch_rows[s_pref[Lr / per_g]], BK) + EPI_K;
+        if (sum + c / 2 > hc) break;
+        sum += c;
+        ++R;
+      }
+    }
+  }
+  auto item = [&](int k, int& L) __attribute__((always_inline)) -> bool {
+    if (MP && after_b && r0 > 0) {
+      const int p1 = lw >= r0 ? R : 0;
+      if (k < p1) {
+        L = (lw - r0) + k * (nwg - r0);
+        return L < total;
+      }
+      L = R * (nwg - r0) + (k - p1) * nwg + lw;
+      return L < total;
+    }
+    L = lw + k * nwg;
+    return L < total;
+  };
+  int kk = 0, L = 0;
+  if (!item(0, L)) return;
   Tile t = tile_of(L);
   int64_t nk = (t.r_hi - t.r_lo + BKE - 1) / BKE;
   uint32_t aoff[LP];
@@ -444,8 +496,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     lds_barrier();
     // GA: the next tile's row map is loaded now, so that it has arrived by
     // the time the next tile's first stages are issued
-    const int Ln = L + nwg;
-    const bool more = Ln < total;
+    int Ln = 0;
+    const bool more = item(kk + 1, Ln);
     Tile tn = t;
     int64_t nk_n = 0;
     uint32_t aoff_n[LP];
@@ -707,6 +759,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       prefetch_next();
       if (!more) break;
       L = Ln;
+      ++kk;
       t = tn;
       nk = nk_n;
 #pragma unroll
@@ -751,6 +804,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
       prefetch_next();
       if (!more) break;
       L = Ln;
+      ++kk;
       t = tn;
       nk = nk_n;
 #pragma unroll
@@ -835,11 +889,27 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a) {
     }
     if (!more) break;
     L = Ln;
+    ++kk;
     t = tn;
     nk = nk_n;
 #pragma unroll
     for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
   }
+  };  // walk
+
+  if constexpr (MP) {
+    walk(b_in, false);
+    __syncthreads();  // the tile table is rebuilt for a_in
+    walk(a_in, true);
+  } else {
+    walk(a_in, false);
+  }
+}
+
+// p[i] = i for i < n: the identity row map
+__global__ __launch_bounds__(256) void iota_kernel(int32_t* __restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = (int32_t)i;
 }
 
 // Workgroups of the persistent grid: one per CU.
@@ -861,7 +931,14 @@ template <int LAYOUT, int EPI, bool F8 = false, bool GA = false, int NWV = kWave
           bool SL = false>
 static hipError_t run(const Args& a, hipStream_t st) {
   if (a.G == 0 || a.N == 0 || a.K == 0) return hipSuccess;
-  gemm_kernel<LAYOUT, EPI, F8, GA, NWV, PF, SL><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a);
+  gemm_kernel<LAYOUT, EPI, F8, GA, NWV, PF, SL><<<dim3((unsigned)grid_size()), dim3(64 * NWV), 0, st>>>(a, a);
+  return hipGetLastError();
+}
+// two weight gradients in one launch (b: one group, walked first)
+template <bool GA>
+static hipError_t run_pair(const Args& a, const Args& b, hipStream_t st) {
+  gemm_kernel<MOE_GEMM_TN, MOE_EPI_NONE, false, GA, kWaves, FP8_E4M3, false, true>
+      <<<dim3((unsigned)grid_size()), dim3(64 * kWaves), 0, st>>>(a, b);
   return hipGetLastError();
 }
 
@@ -925,6 +1002,49 @@ size_t gemm_big_workspace_bytes(const GemmProblem& p) {
     return 0;
   const int s = one_group_slices(p);
   return s > 1 ? (size_t)s * p.N * p.K * sizeof(float) : 0;
+}
+
+// Two weight gradients in one launch: `routed` (many groups, on this kernel
+// without row slices) and `one` (one group of bf16 rows whose operands have
+// 32-bit offsets; with a row map exactly when `routed` has one).
+bool gemm_big_pair_supported(const GemmProblem& routed, const GemmProblem& one) {
+  if (routed.layout != MOE_GEMM_TN || one.layout != MOE_GEMM_TN) return false;
+  if (routed.epilogue != MOE_EPI_NONE || one.epilogue != MOE_EPI_NONE) return false;
+  if (!gemm_big_supported(routed) || gemm_big_workspace_bytes(routed) != 0) return false;
+  if (one.G != 1 || (one.rows != nullptr) != (routed.rows != nullptr)) return false;
+  if (one.ta != MOE_BF16 || one.tb != MOE_BF16 || one.tc != MOE_BF16) return false;
+  const int64_t lim = int64_t(1) << 32;
+  return one.M_total > 0 && one.N >= 8 && one.K >= 8 && one.N % 8 == 0 && one.K % 8 == 0 &&
+         one.M_total * one.N * 2 <= lim && one.M_total * one.K * 2 <= lim;
+}
+
+static pk::Args big_args(const GemmProblem& p) {
+  pk::Args a;
+  a.G = (int)p.G;
+  a.M_total = p.M_total;
+  a.N = p.N;
+  a.K = p.K;
+  a.offsets = p.offsets;
+  a.A = (const bf16_t*)p.A;
+  a.B = (const bf16_t*)p.B;
+  a.C = (bf16_t*)p.C;
+  a.aux = (bf16_t*)p.aux;
+  a.a_scale = a.b_scale = nullptr;
+  a.rows = p.rows;
+  a.nslice = 1;
+  return a;
+}
+
+hipError_t launch_gemm_big_pair(const GemmProblem& routed, const GemmProblem& one, hipStream_t st) {
+  if (!gemm_big_pair_supported(routed, one)) return hipErrorInvalidValue;
+  const pk::Args a = big_args(routed), b = big_args(one);
+  return routed.rows ? pk::run_pair<true>(a, b, st) : pk::run_pair<false>(a, b, st);
+}
+
+hipError_t launch_iota(int32_t* p, int64_t n, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  pk::iota_kernel<<<dim3((unsigned)cdiv64(n, 256)), dim3(256), 0, st>>>(p, n);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_big(const GemmProblem& p, void* ws, size_t ws_bytes, hipStream_t st) {
