@@ -246,17 +246,29 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         if (s_pref[mid] <= tguess) lo = mid; else hi = mid;
       }
       const int g = lo;
-      // inside a group: blocks of NB column tiles x all row tiles, so the
-      // per workgroups of one XCD share the group's rows and weight columns
+      // inside a group: blocks of RB row tiles x NB column tiles (RB * NB
+      // about `per`), so that the per workgroups of one XCD in one round
+      // share RB row blocks of the group's rows and NB column blocks of its
+      // weights.  A group of at most `per` row tiles is one row block (NB =
+      // per / mt); a taller one (the shared experts: every token) takes
+      // blocks of per / 4 row tiles x 4 column tiles.
       const int mt = (g + 1 < a.G ? s_pref[g + 1] : mt_total) - s_pref[g];
       const int l = L - s_pref[g] * tn_n;
-      int NB = per / mt;
+      int RB = mt, NB = per / mt;
+      if (mt > per) {
+        NB = 4;
+        RB = per / 4;
+      }
       NB = NB < 1 ? 1 : (NB > tn_n ? tn_n : NB);
-      const int blk = l / (mt * NB);
-      const int nbw = (tn_n - blk * NB) < NB ? (tn_n - blk * NB) : NB;
-      const int rem = l - blk * mt * NB;
-      const int tm_local = rem / nbw;
-      const int tn = blk * NB + (rem - tm_local * nbw);
+      RB = RB < 1 ? 1 : RB;
+      const int rb = l / (RB * tn_n);
+      const int rbh = (mt - rb * RB) < RB ? (mt - rb * RB) : RB;
+      const int rem1 = l - rb * RB * tn_n;
+      const int cb = rem1 / (rbh * NB);
+      const int nbw = (tn_n - cb * NB) < NB ? (tn_n - cb * NB) : NB;
+      const int rem2 = rem1 - cb * rbh * NB;
+      const int tm_local = rb * RB + rem2 / nbw;
+      const int tn = cb * NB + (rem2 - (rem2 / nbw) * nbw);
       t.g = __builtin_amdgcn_readfirstlane(g);
       const int glo = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g, a.M_total));
       const int ghi = __builtin_amdgcn_readfirstlane(group_row(a.offsets, t.g + 1, a.M_total));
