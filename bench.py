@@ -816,12 +816,16 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
     ctr = measured_counters() if main_cfg else None
     gu_ctr = (ctr or {}).get("products", {}).get("gate_up (alone, after the copy)")
     fwd_tflops = (fl_gu + fl_dn) / (t_gu + t_dn) / 1e12
-    # practical HBM ceiling on this device: a 1 GiB device-to-device copy
-    # (read + write), timed with events on the same stream
+    # practical HBM ceiling on this device: a 1 GiB streaming copy with the
+    # streaming kernels' access pattern (moe_hbm_ceiling: 16-byte vectors,
+    # nontemporal), and for reference a device-to-device hipMemcpy; read +
+    # write bytes, timed with events on the same stream
     cbuf = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
     cdst = torch.empty_like(cbuf)
-    t_copy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
+    t_copy = timed_ms(lambda: M.hbm_ceiling(cbuf, cdst, stream), 10) * 1e-3
     copy_gbs = 2.0 * COPY_BYTES / t_copy / 1e9
+    t_memcpy = timed_ms(lambda: cdst.copy_(cbuf), 10) * 1e-3
+    memcpy_gbs = 2.0 * COPY_BYTES / t_memcpy / 1e9
     del cbuf, cdst
     # practical matrix-core ceiling on this device: each instruction kind
     # issued back to back on register operands (no memory traffic)
@@ -906,8 +910,10 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
         "front_end": {"stages": front, "us": front_us, "gbs": front_bytes / (front_us * 1e-6) / 1e9},
         "combine_stages_hbm": {"stages": hbm3, "gbs": hbm3_gbs, "frac": hbm3_gbs / PEAK_HBM_GBS, "us": hbm3_us,
                                "frac_of_copy": hbm3_gbs / copy_gbs},
-        "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS,
-                             "what": "1 GiB device-to-device copy (read + write), events on the same stream"},
+        "hbm_copy_ceiling": {"gbs": copy_gbs, "frac": copy_gbs / PEAK_HBM_GBS, "hipmemcpy_gbs": memcpy_gbs,
+                             "what": "1 GiB streaming copy (moe_hbm_ceiling: 16-byte vectors, nontemporal loads and "
+                                     "stores; read + write bytes), events on the same stream; hipmemcpy_gbs: the "
+                                     "same bytes through a device-to-device hipMemcpy"},
         "mfma_ceiling": {"tflops": mfma_ceiling,
                          "gate_up_frac_of_ceiling": ach / mfma_ceiling["bf16_32x32x16"],
                          "what": "moe_mfma_ceiling: 2 workgroups per CU of 8 waves issuing independent MFMAs of "

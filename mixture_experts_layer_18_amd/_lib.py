@@ -109,6 +109,7 @@ SIGNATURES = {
     "moe_grouped_gemm_fp8": (c_i32, [c_i32, c_i32, c_i64, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp, c_vp,
                                      c_vp, c_vp, c_vp]),
     "moe_mfma_ceiling": (c_i32, [c_i32, c_i64, c_vp, _P(ctypes.c_double), c_vp]),
+    "moe_hbm_ceiling": (c_i32, [c_vp, c_vp, c_i64, c_vp]),
     "moe_stage_timing_mask": (c_i32, [ctypes.c_uint32]),
     "moe_stage_timing": (c_i32, [c_i32]),
     "moe_stage_times": (c_i32, [_P(ctypes.c_double), _P(c_i64)]),

@@ -355,6 +355,15 @@ def mfma_ceiling(kind: str, iters: int, out, stream=None) -> float:
     return flop.value
 
 
+def hbm_ceiling(src, dst, stream=None):
+    """Copy src to dst (same byte size, a multiple of 16) with the streaming
+    kernels' access pattern; the caller times it."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("hbm_ceiling: src and dst sizes differ")
+    _check(L.load().moe_hbm_ceiling(_p(src), _p(dst), nbytes, _stream(stream)), "moe_hbm_ceiling")
+
+
 def stage_timing(enable: bool, stages=None):
     """Start (clearing earlier records) or stop per-stage event timing of
     moe_forward / moe_backward; `stages` (names from STAGES) limits it to

@@ -1082,6 +1082,15 @@ int moe_mfma_ceiling(int kind, int64_t iters, float* out, double* flop_per_launc
   return MOE_OK;
 }
 
+int moe_hbm_ceiling(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0 || bytes % 16 || bytes > (int64_t(1) << 40)) return MOE_ERR_INVALID;
+  if (bytes == 0) return MOE_OK;
+  if (!src || !dst) return MOE_ERR_INVALID;
+  if (!aligned16(src) || !aligned16(dst)) return MOE_ERR_ALIGN;
+  MOE_TRY(launch_stream_copy(src, dst, bytes / 16, (hipStream_t)stream));
+  return MOE_OK;
+}
+
 int moe_stage_timing_mask(uint32_t mask) {
   std::lock_guard<std::mutex> lk(g_timing_mu);
   for (const StageRec& r : g_recs) g_spare.push_back(r);

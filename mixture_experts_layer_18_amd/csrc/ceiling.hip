@@ -108,4 +108,22 @@ hipError_t launch_mfma_rate(int kind, int64_t iters, float* out, hipStream_t st)
   return hipGetLastError();
 }
 
+// Streaming copy: one 16-byte vector per thread, nontemporal load and
+// store, n vectors (the practical HBM ceiling the streaming kernels of the
+// layer are rated against).
+namespace {
+typedef uint32_t cp_u4 __attribute__((ext_vector_type(4)));
+__global__ __launch_bounds__(256) void stream_copy_kernel(const cp_u4* __restrict__ src, cp_u4* __restrict__ dst,
+                                                          int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) __builtin_nontemporal_store(__builtin_nontemporal_load(src + i), dst + i);
+}
+}  // namespace
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream_t st) {
+  if (n16 <= 0) return hipSuccess;
+  stream_copy_kernel<<<dim3((unsigned)cdiv64(n16, 256)), dim3(256), 0, st>>>((const cp_u4*)src, (cp_u4*)dst, n16);
+  return hipGetLastError();
+}
+
 }  // namespace moe

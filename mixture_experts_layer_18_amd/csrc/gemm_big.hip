@@ -88,6 +88,10 @@ struct Args {
   int nslice;            // SL: row slices of the one group (C: fp32 partials [nslice, N, K])
 };
 constexpr int RING = 8;  // GA TN: map stages held per wave
+template <bool B>
+struct Flag {
+  static constexpr bool value = B;
+};
 
 // Exclusive prefix sum over the workgroup's threads (NW waves) of one value
 // per thread; *total receives the sum.
@@ -532,6 +536,16 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       for (int jt = 0; jt < FJ; ++jt)
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[it][jt][v] = 0.0f;
+    // A wave whose outputs are all padding (the rows past a group's end in
+    // its last row tile, the columns past the end in a last column tile)
+    // runs the k-loop without fragment reads or MFMAs: the DMA issue and the
+    // barriers only.  Its accumulators stay zero and are never stored, and
+    // the other wave on its SIMD has the matrix core to itself.
+    const int colw_w = (EPI == MOE_EPI_SWIGLU) ? WN / 2 : WN;
+    const bool wact = __builtin_amdgcn_readfirstlane(
+        (int)(wp * WM < t.i_hi - t.i_lo && (int64_t)wq * colw_w < ncols - t.j0));
+    auto kloop = [&](auto act) __attribute__((always_inline)) {
+    constexpr bool ACT = decltype(act)::value;
     if constexpr (F8) {
       // Both 32-byte halves of a lane's row fragment feed one MFMA, so a
       // k-step cannot be split in reduction halves as in the bf16 loop; it is
@@ -549,23 +563,29 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       };
       constexpr int FH = FI / 2;
       v8i_t P[FH], Q[FJ];
+      if constexpr (ACT) {
 #pragma unroll
-      for (int it = 0; it < FH; ++it) P[it] = frag8(smem, wp * WM + it * 32);
+        for (int it = 0; it < FH; ++it) P[it] = frag8(smem, wp * WM + it * 32);
 #pragma unroll
-      for (int jt = 0; jt < FJ; ++jt) Q[jt] = frag8(smem + PB, wq * WN + jt * 32);
+        for (int jt = 0; jt < FJ; ++jt) Q[jt] = frag8(smem + PB, wq * WN + jt * 32);
+      }
       const int ln = opaque_i(lane);
       for (int64_t kt = 0; kt < nk; ++kt) {
         const char* sP = smem + (kt % STAGES) * SB;
         v8i_t P2[FH];
+        if constexpr (ACT) {
 #pragma unroll
-        for (int it = 0; it < FH; ++it) P2[it] = frag8(sP, wp * WM + (FH + it) * 32);
+          for (int it = 0; it < FH; ++it) P2[it] = frag8(sP, wp * WM + (FH + it) * 32);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ACT) {
 #pragma unroll
-        for (int it = 0; it < FH; ++it)
+          for (int it = 0; it < FH; ++it)
 #pragma unroll
-          for (int jt = 0; jt < FJ; ++jt)
-            acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], FP8_E4M3,
-                                                                          PF, 0, 0, 0, 0);
+            for (int jt = 0; jt < FJ; ++jt)
+              acc[it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(Q[jt], P[it], acc[it][jt], FP8_E4M3,
+                                                                            PF, 0, 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         // k-step kt+1 landed for this wave; after the barrier every wave has
         // it and none reads stage kt from LDS any more
@@ -573,47 +593,58 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         lds_barrier();
         const char* nP = smem + ((kt + 1) % STAGES) * SB;
         v8i_t Pn[FH], Qn[FJ];
+        if constexpr (ACT) {
 #pragma unroll
-        for (int jt = 0; jt < FJ; ++jt) Qn[jt] = frag8(nP + PB, wq * WN + jt * 32);
+          for (int jt = 0; jt < FJ; ++jt) Qn[jt] = frag8(nP + PB, wq * WN + jt * 32);
 #pragma unroll
-        for (int it = 0; it < FH; ++it) Pn[it] = frag8(nP, wp * WM + it * 32);
+          for (int it = 0; it < FH; ++it) Pn[it] = frag8(nP, wp * WM + it * 32);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const bool real = kt + STAGES < nk;
         static_assert(FH * FJ == LT, "one MFMA per DMA slot");
 #pragma unroll
         for (int q = 0; q < LT; ++q) {
           const int it = q / FJ, jt = q % FJ;
-          acc[FH + it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-              Q[jt], P2[it], acc[FH + it][jt], FP8_E4M3, PF, 0, 0, 0, 0);
+          if constexpr (ACT)
+            acc[FH + it][jt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                Q[jt], P2[it], acc[FH + it][jt], FP8_E4M3, PF, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, aoff);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
+        if constexpr (ACT) {
 #pragma unroll
-        for (int it = 0; it < FH; ++it) P[it] = Pn[it];
+          for (int it = 0; it < FH; ++it) P[it] = Pn[it];
 #pragma unroll
-        for (int jt = 0; jt < FJ; ++jt) Q[jt] = Qn[jt];
+          for (int jt = 0; jt < FJ; ++jt) Q[jt] = Qn[jt];
+        }
       }
     } else {
     bf16x8_t pa0[FI], qb0[FJ], pa1[FI], qb1[FJ];
+      if constexpr (ACT) {
   #pragma unroll
-      for (int it = 0; it < FI; ++it) pa0[it] = frag_p(smem, it, 0);
+        for (int it = 0; it < FI; ++it) pa0[it] = frag_p(smem, it, 0);
   #pragma unroll
-      for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(smem, jt, 0);
+        for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(smem, jt, 0);
+      }
       const int ln = opaque_i(lane);
       for (int64_t kt = 0; kt < nk; ++kt) {
         const char* sP = smem + (kt % STAGES) * SB;
+        if constexpr (ACT) {
   #pragma unroll
-        for (int it = 0; it < FI; ++it) pa1[it] = frag_p(sP, it, 1);
+          for (int it = 0; it < FI; ++it) pa1[it] = frag_p(sP, it, 1);
   #pragma unroll
-        for (int jt = 0; jt < FJ; ++jt) qb1[jt] = frag_q(sP, jt, 1);
+          for (int jt = 0; jt < FJ; ++jt) qb1[jt] = frag_q(sP, jt, 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (ACT) {
   #pragma unroll
-        for (int it = 0; it < FI; ++it)
+          for (int it = 0; it < FI; ++it)
   #pragma unroll
-          for (int jt = 0; jt < FJ; ++jt)
-            acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb0[jt], pa0[it], acc[it][jt], 0, 0, 0);
+            for (int jt = 0; jt < FJ; ++jt)
+              acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb0[jt], pa0[it], acc[it][jt], 0, 0, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         // k-step kt+1 landed for this wave (kt+2, kt+3 may be in flight); after
         // the barrier every wave has it and is done reading k-step kt
@@ -631,10 +662,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         }
         lds_barrier();
         const char* nP = smem + ((kt + 1) % STAGES) * SB;
+        if constexpr (ACT) {
   #pragma unroll
-        for (int it = 0; it < FI; ++it) pa0[it] = frag_p(nP, it, 0);
+          for (int it = 0; it < FI; ++it) pa0[it] = frag_p(nP, it, 0);
   #pragma unroll
-        for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(nP, jt, 0);
+          for (int jt = 0; jt < FJ; ++jt) qb0[jt] = frag_q(nP, jt, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         const bool real = kt + STAGES < nk;
   #pragma unroll
@@ -642,7 +675,8 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
   #pragma unroll
           for (int u = 0; u < (FI * FJ) / LT; ++u) {
             const int m = q * ((FI * FJ) / LT) + u, it = m / FJ, jt = m % FJ;
-            acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb1[jt], pa1[it], acc[it][jt], 0, 0, 0);
+            if constexpr (ACT)
+              acc[it][jt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qb1[jt], pa1[it], acc[it][jt], 0, 0, 0);
           }
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, GT ? gq : aoff);
@@ -655,6 +689,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         }
       }
     }
+    };
+    if (wact) kloop(Flag<true>{});
+    else kloop(Flag<false>{});
     // every wave is done with this tile's LDS stages: fetch the next tile's
     // first stages, then write this tile's results
     lds_barrier();

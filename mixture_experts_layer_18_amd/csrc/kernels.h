@@ -44,6 +44,7 @@ hipError_t launch_gemm_big(const GemmProblem& p, void* ws, size_t ws_bytes, hipS
 bool gemm_big_pair_supported(const GemmProblem& routed, const GemmProblem& one);
 hipError_t launch_gemm_big_pair(const GemmProblem& routed, const GemmProblem& one, hipStream_t st);
 hipError_t launch_iota(int32_t* p, int64_t n, hipStream_t st);  // p[i] = i
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, hipStream_t st);  // n16 16-byte vectors
 // fp8 (e4m3) forward products with row scales, persistent kernel
 hipError_t launch_gemm_fp8(int epilogue, int64_t G, int64_t M_total, int64_t N, int64_t K,
                            const int32_t* offsets, const uint8_t* A, const float* a_scale,

@@ -434,9 +434,16 @@ def test_fp8_layer_argument_checks(lib):
 
 def test_mfma_ceiling_argument_checks(lib):
     """The matrix-core rate aid rejects unknown kinds, bad counts and null or
-    misaligned outputs on the host."""
+    misaligned outputs on the host; the HBM copy aid, sizes that are not whole
+    16-byte vectors and null or misaligned pointers."""
     a = ctypes.c_void_p(0x10000)
     f = ctypes.c_double(0.0)
+    # the HBM counterpart: sizes in 16-byte vectors, aligned pointers
+    assert lib.moe_hbm_ceiling(a, a, 15, None) == L.MOE_ERR_INVALID
+    assert lib.moe_hbm_ceiling(a, a, -16, None) == L.MOE_ERR_INVALID
+    assert lib.moe_hbm_ceiling(None, a, 16, None) == L.MOE_ERR_INVALID
+    assert lib.moe_hbm_ceiling(ctypes.c_void_p(a.value + 8), a, 16, None) == L.MOE_ERR_ALIGN
+    assert lib.moe_hbm_ceiling(None, None, 0, None) == L.MOE_OK
     assert lib.moe_mfma_ceiling(4, 10, a, ctypes.byref(f), None) == L.MOE_ERR_INVALID
     assert lib.moe_mfma_ceiling(-1, 10, a, ctypes.byref(f), None) == L.MOE_ERR_INVALID
     assert lib.moe_mfma_ceiling(0, 0, a, ctypes.byref(f), None) == L.MOE_ERR_INVALID

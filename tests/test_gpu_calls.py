@@ -403,3 +403,15 @@ def test_forward_routing_matches_moe_route(base, kw):
                        ("offsets", saved["offsets"], offsets), ("pos", saved["pos"], pos), ("src", saved["src"], src),
                        ("tok", saved["tok"], tok)):
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), f"{cfg.name}: {name} differs"
+
+
+def test_hbm_ceiling_copies_bytes():
+    """The streaming-copy measurement aid moves every byte unchanged (a size
+    that is not a multiple of 256 vectors leaves a partial last workgroup)."""
+    print("[hbm ceiling] copy", flush=True)
+    n = (1 << 20) + 48
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device="cuda")
+    dst = torch.zeros_like(src)
+    M.hbm_ceiling(src, dst)
+    torch.cuda.synchronize()
+    assert torch.equal(src, dst)
