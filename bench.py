@@ -68,7 +68,7 @@ def parse():
 COPY_BYTES = 1 << 30
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "gate_up_gemm_moe7b_bf16_traffic.txt")
 # the routed gate/up product: forward layout, SwiGLU, bf16, rows gathered
-GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false, true, 8>"
+GATE_UP_KERNEL = "pk::gemm_kernel<0, 1, false, true, 8, 0, false, false>"
 KERNEL_SOURCES = ["mixture_experts_layer_18_amd/csrc/gemm_big.hip",
                   "mixture_experts_layer_18_amd/csrc/gemm_common.h",
                   "mixture_experts_layer_18_amd/csrc/common.h",
@@ -227,20 +227,18 @@ SIMDS, XCDS, CUS = 1024, 8, 256
 # the probe's launches, in order, named by stage (kernel symbol prefix,
 # occurrence among the probe's dispatches of that symbol)
 PROBE_STAGES = [
-    ("pk::gemm_kernel<0, 1, false, true, 8>", 1, "gate_up (in the forward)"),
-    ("pk::gemm_kernel<0, 0, false, false, 8>", 1, "down"),
-    ("pk::gemm_kernel<0, 1, false, false, 8>", 1, "shared_gate_up"),
-    ("pk::gemm_kernel<0, 0, false, false, 8>", 2, "shared_down"),
-    ("pk::gemm_kernel<0, 1, false, true, 8>", 2, "gate_up (alone, after the copy)"),
-    ("pk::gemm_kernel<1, 2, false, false, 8>", 1, "down_dgrad (dSwiGLU)"),
-    ("pk::gemm_kernel<2, 0, false, false, 8>", 1, "down_wgrad"),
-    ("pk::gemm_kernel<2, 0, false, true, 8>", 1, "gate_up_wgrad"),
-    ("pk::gemm_kernel<1, 0, false, false, 8>", 1, "gate_up_dgrad"),
-    ("pk::gemm_kernel<1, 2, false, false, 8>", 2, "shared_down_dgrad"),
-    ("mf::gemm_kernel<2, 0,", 1, "shared_down_wgrad (two-workgroup kernel)"),
-    ("mf::gemm_kernel<2, 0,", 2, "shared_gate_up_wgrad (two-workgroup kernel)"),
-    ("pk::gemm_kernel<1, 0, false, false, 8>", 2, "shared_gate_up_dgrad"),
-    ("pk::gemm_kernel<0, 1, true, false, 8>", 1, "fp8 gate_up"),
+    ("pk::gemm_kernel<0, 1, false, true, 8, 0, false, false>", 1, "gate_up (in the forward)"),
+    ("pk::gemm_kernel<0, 0, false, false, 8, 0, false, false>", 1, "down"),
+    ("pk::gemm_kernel<0, 1, false, false, 8, 0, false, false>", 1, "shared_gate_up"),
+    ("pk::gemm_kernel<0, 0, false, false, 8, 0, false, false>", 2, "shared_down"),
+    ("pk::gemm_kernel<0, 1, false, true, 8, 0, false, false>", 2, "gate_up (alone, after the copy)"),
+    ("pk::gemm_kernel<1, 2, false, false, 8, 0, false, false>", 1, "down_dgrad (dSwiGLU)"),
+    ("pk::gemm_kernel<1, 2, false, false, 8, 0, false, false>", 2, "shared_down_dgrad"),
+    ("pk::gemm_kernel<2, 0, false, false, 8, 0, false, true>", 1, "down_wgrad + shared (one launch)"),
+    ("pk::gemm_kernel<2, 0, false, true, 8, 0, false, true>", 1, "gate_up_wgrad + shared (one launch)"),
+    ("pk::gemm_kernel<1, 0, false, false, 8, 0, false, false>", 1, "gate_up_dgrad"),
+    ("pk::gemm_kernel<1, 0, false, false, 8, 0, false, false>", 2, "shared_gate_up_dgrad"),
+    ("pk::gemm_kernel<0, 1, true, false, 8, 0, false, false>", 1, "fp8 gate_up"),
 ]
 PMC_COMMAND = ("timeout -s KILL 120 rocprofv3 --pmc {counters} -d <root>/gpurun_out/pmc_{name} -o run "
                "--output-format csv -- python3 <root>/bench.py --pmc-probe")
