@@ -213,7 +213,7 @@ def _fp8_wgrad_gpu(G, offsets, a, b, b_rows=None):
     return C
 
 
-def _compare_fp8_layer(cfg, gather, grad_format="e4m3", wgrad_fp8=False):
+def _compare_fp8_layer(cfg, gather, grad_format="e4m3", wgrad_fp8=False, paired=False):
     print(f"[fp8 layer] {cfg.name} gather={gather} gradients {grad_format} fp8 weight gradients {wgrad_fp8}: inputs",
           flush=True)
     inp = synth.make_inputs(cfg, with_dy=True)
@@ -285,6 +285,13 @@ def _compare_fp8_layer(cfg, gather, grad_format="e4m3", wgrad_fp8=False):
     if F:
         if wgrad_fp8:
             dsg = _fp8_wgrad_gpu(1, None, s_dgu, x)[0]
+        elif paired:
+            # the layer ran the shared weight gradient inside the routed
+            # (gathered) launch: the same tiles, each over all rows in order,
+            # as the gathered product of one group through the identity map
+            dsg = torch.empty(2 * F, d, dtype=torch.bfloat16, device="cuda")
+            iota = torch.arange(T, dtype=torch.int32, device="cuda")
+            M.moe_grouped_gemm_gather("TN", "none", 1, T, 2 * F, d, None, s_dgu, x, dsg, iota, T)
         else:
             dsg = torch.empty(2 * F, d, dtype=torch.bfloat16, device="cuda")
             nws = M.grouped_gemm_workspace_bytes("TN", "bf16", 1, T, 2 * F, d)
@@ -332,6 +339,25 @@ def test_fp8_layer_fp8_weight_gradients_against_oracle(cfg):
     input is the GPU's after the checks above, so the weight gradients are
     compared against the oracle's fp8 products of the same codes."""
     _compare_fp8_layer(cfg, True, "e4m3", True)
+
+
+# the routed down weight gradient has 64 x 4 x 4 = 1024 tiles, so the fp8
+# backward's bf16 weight gradients run paired with the shared ones
+PAIRED = synth.CONFIG_BY_NAME["finegrained_bf16"].replace(
+    name="fp8_paired", T=2000, d=1024, E=64, k=4, f=1024, n_shared=1, f_shared=512, backward=True, seed=5)
+
+
+def test_fp8_layer_paired_weight_gradients_against_oracle():
+    """The fp8 layer whose shared weight gradients run inside the routed
+    weight-gradient launches, forward and backward compared in full."""
+    M.stage_timing(True)
+    try:
+        _compare_fp8_layer(PAIRED, True, paired=True)
+        torch.cuda.synchronize()
+        st = M.stage_times()
+    finally:
+        M.stage_timing(False)
+    assert st["down_wgrad"][1] >= 1 and st["shared_down_wgrad"][1] == 0 and st["shared_gate_up_wgrad"][1] == 0
 
 
 def test_fp8_layer_finegrained_against_oracle():

@@ -47,6 +47,31 @@ def test_backward_small_bf16():
     R.compare_full(SMALL_BF16, synth.make_inputs(SMALL_BF16), backward=True)
 
 
+# 64 experts x 4 x 4 weight-gradient tiles = 1024: the routed down weight
+# gradient runs on the persistent kernel, so each shared weight gradient
+# (16 and 8 output tiles, one round's last partial) runs in the launch of its
+# routed counterpart; 2000 tokens (a ragged last k-step of the shared
+# products) over groups of about 125 rows
+PAIRED_BF16 = synth.CONFIG_BY_NAME["moe7b_bf16"].replace(name="paired_bf16", T=2000, d=1024, E=64, k=4, f=1024,
+                                                          n_shared=1, f_shared=512)
+
+
+@pytest.mark.parametrize("gather", [False, True], ids=["permuted-copy", "gathered"])
+def test_backward_paired_shared_weight_gradients(gather):
+    import mixture_experts_layer_18_amd as M
+    print(f"[layer] paired shared weight gradients gather={gather}", flush=True)
+    M.stage_timing(True)
+    try:
+        R.compare_full(PAIRED_BF16, synth.make_inputs(PAIRED_BF16), backward=True, gather=gather)
+        torch.cuda.synchronize()
+        st = M.stage_times()
+    finally:
+        M.stage_timing(False)
+    # the shared weight gradients ran inside the routed launches
+    assert st["down_wgrad"][1] >= 1 and st["gate_up_wgrad"][1] >= 1
+    assert st["shared_down_wgrad"][1] == 0 and st["shared_gate_up_wgrad"][1] == 0
+
+
 def test_backward_small_bf16_skewed():
     cfg = SMALL_BF16.replace(name="small_skew", bias="zipf")
     print("[layer] small skew fwd+bwd", flush=True)
