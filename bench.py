@@ -724,6 +724,31 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
     step_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
     progress(f"{cfg.name}: timed {args.steps} steps, {sum(step_ms) / len(step_ms):.3f} ms per step")
     ms_step = sum(step_ms) / len(step_ms)
+    # the same step captured once in a HIP graph and replayed (each replay
+    # after the same flush, its own event pair): the step without the host's
+    # launch cost and the gaps between launches
+    graph_ms = None
+    if not args.router_terms:
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            if training:
+                M.moe_forward(desc, w, x, y, saved, wsf, cap)
+                M.moe_backward(desc, w, x, saved, dy, dx, grads, wsb, cap)
+            else:
+                M.moe_forward(desc, w, x, y, saved, wsf, cap)
+        torch.cuda.synchronize()
+        gevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for e0, e1 in gevs:
+            flush_buf.fill_(1.0)
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = sum(e0.elapsed_time(e1) for e0, e1 in gevs) / len(gevs)
+        del graph
     del flush_buf
     # every stage, over separate steps after the timed region
     M.stage_timing(True)
@@ -889,6 +914,9 @@ def run_config(args, cfg_name, cpu_tokens, pmc_probe=False):
                       "further steps with event pairs around every stage (the gate/up stage's from the timed "
                       "steps themselves)",
             "step_ms_min": min(step_ms), "step_ms_max": max(step_ms), "region_wall_s": wall,
+            "graph_replay_ms_per_step": graph_ms,
+            "graph_replay": "the same step captured once in a HIP graph (torch.cuda.CUDAGraph on a side stream) "
+                            "and replayed, each replay after the same flush inside its own event pair",
         },
         "roofline": {
             "kernel": "gate/up grouped GEMM + SwiGLU (forward, NT)",
