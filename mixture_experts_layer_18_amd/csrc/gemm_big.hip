@@ -450,6 +450,32 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
 
   const int wp = wave / WPR, wq = wave % WPR;
   const int r32 = lane & 31, kh = lane >> 5;
+  // dSwiGLU epilogue staging.  A wave's G (or U) rows of one 32-row block of
+  // its outputs form a piece of E_NI 1 KB DMA instructions (E_RPI rows of
+  // E_RBW bytes each, 16-byte chunks XOR-swizzled by row).  Piece j (0..3)
+  // of a wave sits in LDS stage slot (nk + j) % STAGES at the wave's offset:
+  // the slot that k-step nk - 4 + j frees, so the k-loop's last four steps
+  // fill pieces 0..3 (blocks 0 and 1, G then U) where they would issue pads.
+  constexpr int E_RBW = WN * 2, E_CPW = E_RBW / 16, E_RPI = 1024 / E_RBW, E_NI = 32 / E_RPI;
+  constexpr int E_WB = E_NI * 1024;  // bytes of one piece
+  static_assert(EPI != MOE_EPI_DSWIGLU || (E_NI == LT && NW * E_WB == SB && FI == 4 && WN == 64), "epilogue pieces");
+  auto e_swz = [](int r) __attribute__((always_inline)) { return E_RBW >= 256 ? (r & 15) : ((r >> 1) & 7); };
+  auto e_piece = [&](int64_t nk, int j) __attribute__((always_inline)) {
+    return (uint32_t)((nk + j) & (STAGES - 1)) * SB + (uint32_t)(wave * E_WB);
+  };
+  // instruction q of piece j holding 32-row block blk of G (j even) or U
+  auto epi_dma = [&](const Tile& t, int64_t nk, int j, int blk, int q, int ln) __attribute__((always_inline)) {
+    const int r = q * E_RPI + ln / E_CPW;
+    const int rl = (int)(t.i_hi - t.i_lo) - 1;
+    int ri = wp * WM + blk * 32 + r;
+    ri = ri < rl ? ri : rl;
+    int64_t col = t.j0 + wq * WN + (int64_t)(((ln % E_CPW) ^ e_swz(r)) * 8);
+    col = col < ncols - 8 ? col : ncols - 8;
+    const int64_t K2 = 2 * ncols;
+    const uint32_t voff = (uint32_t)(((int64_t)ri * K2 + (j & 1) * ncols + col) * 2);
+    dma16_off(a.aux + t.i_lo * K2, voff,
+              __builtin_amdgcn_readfirstlane(smem_base + e_piece(nk, j) + (uint32_t)(q * 1024)));
+  };
   // this workgroup's k-th tile of the walk (false past its end)
   int r0 = 0, R = 0;
   if (MP && after_b) {
@@ -610,6 +636,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
                 Q[jt], P2[it], acc[FH + it][jt], FP8_E4M3, PF, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, aoff);
+          else if constexpr (EPI == MOE_EPI_DSWIGLU) epi_dma(t, nk, (int)(kt + STAGES - nk), (int)(kt + STAGES - nk) >> 1, q, ln);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -680,6 +707,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
           }
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, GT ? gq : aoff);
+          else if constexpr (EPI == MOE_EPI_DSWIGLU) epi_dma(t, nk, (int)(kt + STAGES - nk), (int)(kt + STAGES - nk) >> 1, q, ln);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -731,76 +759,91 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       // scales); aux holds the forward pre-activations G | U ([M, 2W] for
       // output width W); C receives
       // dG = dH U silu'(G) | dU = dH silu(G).  Each wave brings the G and U
-      // rows of its outputs into its own 16 KB of the (now idle) LDS stages
-      // with full-row DMA, two 32-row blocks per phase, and reads them in the
+      // rows of its outputs into four 4 KB pieces of the LDS stages with
+      // full-row DMA (two 32-row blocks at a time) and reads them in the
       // accumulator layout; the next tile's first stages are fetched after.
-      constexpr int RBW = WN * 2;               // bytes of one wave-tile row of G (or U)
-      constexpr int CPW = RBW / 16;             // 16-byte chunks per row
-      constexpr int RPI = 1024 / RBW;           // rows per DMA instruction
-      constexpr int NI = 32 / RPI;              // instructions per 32-row block of G (or U)
-      constexpr int WBUF = 16384;               // LDS bytes per wave
-      constexpr int IPP = WBUF / (64 * RBW);    // 32-row blocks per phase
-      static_assert(IPP >= 1 && FI % IPP == 0 && NW * WBUF <= STAGES * SB, "epilogue staging");
-      // slot of chunk c in row r: c ^ swz(r), so that the 32 rows a read
-      // instruction touches at one chunk spread over the banks
-      auto swz = [](int r) __attribute__((always_inline)) { return RBW >= 256 ? (r & 15) : ((r >> 1) & 7); };
-      const char* wbuf = smem + wave * WBUF;
-      const uint32_t wbase = smem_base + wave * WBUF;
-      const int lrow = lane / CPW, lchunk = lane % CPW;
-      const int64_t K2 = 2 * ncols;
+      // Pieces 0..3 (blocks 0 and 1) were requested by the k-loop's last
+      // four steps; with fewer k-steps the missing ones are requested now.
+      // Block b: each lane reads its G and U values, computes dG and dU and
+      // writes them over the bytes it read; the wave then reads the block
+      // back by whole rows and stores them as full 128-byte rows (the
+      // accumulator layout would store 32-byte pieces of 32 rows, measured
+      // 3-10 % slower); then (b < 2) block b + 2 is requested into the same
+      // two pieces, its loads overlapping the stores of block b + 1.
+      const int ln = opaque_i(lane);
 #pragma unroll
-      for (int ph = 0; ph < FI / IPP; ++ph) {
-        if (ph > 0) __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the last phase's reads are done
+      for (int j = 0; j < 4; ++j)
+        if (nk + j < STAGES)
 #pragma unroll
-        for (int u = 0; u < IPP; ++u)
+          for (int q = 0; q < E_NI; ++q) epi_dma(t, nk, j, j >> 1, q, ln);
+      wait_vmcnt<0>();
 #pragma unroll
-          for (int gu = 0; gu < 2; ++gu)
+      for (int it = 0; it < FI; ++it) {
+        const int j0 = 2 * (it & 1);
+        char* Gw = smem + e_piece(nk, j0);
+        char* Uw = smem + e_piece(nk, j0 + 1);
+        const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
+        // fp8: the row's scale (padding rows, never stored, read the last row's)
+        const float sa = F8 ? a.a_scale[i < t.i_hi ? i : t.i_hi - 1] : 1.0f;
+        const int64_t K2 = 2 * ncols;
 #pragma unroll
-            for (int q = 0; q < NI; ++q) {
-              const int r = q * RPI + lrow;
-              int64_t i = t.i_lo + wp * WM + (ph * IPP + u) * 32 + r;
-              i = i < t.i_hi ? i : t.i_hi - 1;
-              int64_t col = t.j0 + wq * WN + (int64_t)((lchunk ^ swz(r)) * 8);
-              col = col < ncols - 8 ? col : ncols - 8;
-              dma16(X + i * K2 + gu * ncols + col,
-                    __builtin_amdgcn_readfirstlane(wbase + ((u * 2 + gu) * NI + q) * 1024));
+        for (int jt = 0; jt < FJ; ++jt) {
+          const int64_t c = t.j0 + wq * WN + jt * 32;
+          float dG[16], dU[16], sc[16];
+          if constexpr (F8) col_scales(c, sc);
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq) {
+            const int off = r32 * E_RBW + (((jt * 4 + gq) ^ e_swz(r32)) << 4) + kh * 8;
+            const u32x2 g2 = *reinterpret_cast<const u32x2*>(Gw + off);
+            const u32x2 u2 = *reinterpret_cast<const u32x2*>(Uw + off);
+            const float Gv[4] = {bf16_lo(g2.x), bf16_hi(g2.x), bf16_lo(g2.y), bf16_hi(g2.y)};
+            const float Uv[4] = {bf16_lo(u2.x), bf16_hi(u2.x), bf16_lo(u2.y), bf16_hi(u2.y)};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float sg = sigmoid_f(Gv[e]);
+              const float dh = F8 ? agpr_read(acc[it][jt][gq * 4 + e]) * sa * sc[gq * 4 + e]
+                                  : acc[it][jt][gq * 4 + e];
+              dG[gq * 4 + e] = dh * Uv[e] * sg * (1.0f + Gv[e] * (1.0f - sg));
+              dU[gq * 4 + e] = dh * Gv[e] * sg;
             }
-        wait_vmcnt<0>();
+          }
+          // each lane overwrites the G and U bytes it has just read
 #pragma unroll
-        for (int u = 0; u < IPP; ++u) {
-          const int it = ph * IPP + u;
-          const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
-          // fp8: the row's scale (padding rows, never stored, read the last row's)
-          const float sa = F8 ? a.a_scale[i < t.i_hi ? i : t.i_hi - 1] : 1.0f;
-          const char* Gb = wbuf + (u * 2) * NI * 1024;
-          const char* Ub = Gb + NI * 1024;
+          for (int gq = 0; gq < 4; ++gq) {
+            const int off = r32 * E_RBW + (((jt * 4 + gq) ^ e_swz(r32)) << 4) + kh * 8;
+            const u32x2 pg = {pack_bf16x2(dG[gq * 4], dG[gq * 4 + 1]), pack_bf16x2(dG[gq * 4 + 2], dG[gq * 4 + 3])};
+            const u32x2 pu = {pack_bf16x2(dU[gq * 4], dU[gq * 4 + 1]), pack_bf16x2(dU[gq * 4 + 2], dU[gq * 4 + 3])};
+            *reinterpret_cast<u32x2*>(Gw + off) = pg;
+            *reinterpret_cast<u32x2*>(Uw + off) = pu;
+          }
+        }
+        // the block's dG and dU rows leave as whole 128-byte rows: 8 lanes per row
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done
+        {
+          const int lr = lane >> 3, lc = lane & 7;
 #pragma unroll
-          for (int jt = 0; jt < FJ; ++jt) {
-            const int64_t c = t.j0 + wq * WN + jt * 32;
-            float dG[16], dU[16], sc[16];
-            if constexpr (F8) col_scales(c, sc);
-#pragma unroll
-            for (int gq = 0; gq < 4; ++gq) {
-              const int off = r32 * RBW + (((jt * 4 + gq) ^ swz(r32)) << 4) + kh * 8;
-              const u32x2 gw = *reinterpret_cast<const u32x2*>(Gb + off);
-              const u32x2 uw = *reinterpret_cast<const u32x2*>(Ub + off);
-              const float Gv[4] = {bf16_lo(gw.x), bf16_hi(gw.x), bf16_lo(gw.y), bf16_hi(gw.y)};
-              const float Uv[4] = {bf16_lo(uw.x), bf16_hi(uw.x), bf16_lo(uw.y), bf16_hi(uw.y)};
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float sg = sigmoid_f(Gv[e]);
-                const float dh = F8 ? agpr_read(acc[it][jt][gq * 4 + e]) * sa * sc[gq * 4 + e]
-                                    : acc[it][jt][gq * 4 + e];
-                dG[gq * 4 + e] = dh * Uv[e] * sg * (1.0f + Gv[e] * (1.0f - sg));
-                dU[gq * 4 + e] = dh * Gv[e] * sg;
-              }
-            }
-            if (i < t.i_hi && c < ncols) {
-              store_tile_row(C + i * K2 + c, dG, kh, ncols - c);
-              store_tile_row(C + i * K2 + ncols + c, dU, kh, ncols - c);
+          for (int q = 0; q < 32 / 8; ++q) {
+            const int r = q * 8 + lr;
+            const int off = r * E_RBW + ((lc ^ e_swz(r)) << 4);
+            const u32x4 vg = *reinterpret_cast<const u32x4*>(Gw + off);
+            const u32x4 vu = *reinterpret_cast<const u32x4*>(Uw + off);
+            const int64_t ir = t.i_lo + wp * WM + it * 32 + r;
+            const int64_t cc = t.j0 + wq * WN + lc * 8;
+            if (ir < t.i_hi && cc < ncols) {
+              *reinterpret_cast<u32x4*>(C + ir * K2 + cc) = vg;
+              *reinterpret_cast<u32x4*>(C + ir * K2 + ncols + cc) = vu;
             }
           }
         }
+        if (it < 2) {
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the pieces are read back
+#pragma unroll
+          for (int gu = 0; gu < 2; ++gu)
+#pragma unroll
+            for (int q = 0; q < E_NI; ++q) epi_dma(t, nk, j0 + gu, it + 2, q, ln);
+        }
+        // blocks 2 and 3 have landed (with the stores before them)
+        if (it == 1) wait_vmcnt<0>();
       }
       // every wave is done reading its staging area before the next tile's
       // stages overwrite it
@@ -1041,8 +1084,11 @@ bool gemm_big_supported(const GemmProblem& p) {
     if (p.G * cdiv64(p.N, 256) * cdiv64(p.K, 256) >= 4 * 256) return true;
     return p.G == 1 && p.N % 8 == 0 && p.K % 8 == 0 && one_group_slices(p) > 0;
   }
+  // (dSwiGLU: a tile's G | U rows are addressed with 32-bit offsets from
+  // its first row, 256 rows of 2K values)
   if (p.layout == MOE_GEMM_NN)
-    return (p.epilogue == MOE_EPI_NONE || p.epilogue == MOE_EPI_DSWIGLU) && p.N * p.K * 2 <= lim;
+    return (p.epilogue == MOE_EPI_NONE || (p.epilogue == MOE_EPI_DSWIGLU && p.K <= (int64_t(1) << 21))) &&
+           p.N * p.K * 2 <= lim;
   return false;
 }
 

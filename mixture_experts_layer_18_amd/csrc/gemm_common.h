@@ -38,8 +38,10 @@ MOE_DEV int xcd_remap(int bid, int nb) {
 // Store one 32-column MFMA tile row from its fp32 accumulator layout as
 // 16-byte chunks.  Lane l (kh = l/32) holds columns gq*8 + kh*4 + 0..3 of
 // groups gq = 0..3 (v[gq*4..+3]); lanes l and l+32 share the row.  For each
-// pair of groups (2p, 2p+1) the two lanes swap halves (v_permlane32_swap) so
-// that lane kh ends with the 8 consecutive columns of group 2p+kh.
+// pair of groups (2p, 2p+1), v_permlane32_swap trades lanes 32..63 of the
+// packed group-2p values with lanes 0..31 of the packed group-2p+1 values:
+// lane kh then holds the 8 consecutive columns of group 2p+kh in the pair
+// (first register: columns +0..3, second: +4..7), with no per-lane select.
 // `row` points at the tile's column 0 in the output row; columns at or past
 // `lim` (relative to that point) are not written.
 MOE_DEV void store_tile_row(bf16_t* row, const float* v, int kh, int64_t lim) {
@@ -47,18 +49,12 @@ MOE_DEV void store_tile_row(bf16_t* row, const float* v, int kh, int64_t lim) {
   for (int p = 0; p < 2; ++p) {
     const float* lo = v + 8 * p;
     const float* hi = v + 8 * p + 4;
-    const uint32_t lo0 = pack_bf16x2(lo[0], lo[1]), lo1 = pack_bf16x2(lo[2], lo[3]);
-    const uint32_t hi0 = pack_bf16x2(hi[0], hi[1]), hi1 = pack_bf16x2(hi[2], hi[3]);
-    const uint32_t s0 = kh ? lo0 : hi0, s1 = kh ? lo1 : hi1;
-    const auto r0 = __builtin_amdgcn_permlane32_swap(s0, s0, false, false);
-    const auto r1 = __builtin_amdgcn_permlane32_swap(s1, s1, false, false);
-    const uint32_t q0 = kh ? r0[0] : r0[1], q1 = kh ? r1[0] : r1[1];
+    const auto r0 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(lo[0], lo[1]), pack_bf16x2(hi[0], hi[1]), false,
+                                                     false);
+    const auto r1 = __builtin_amdgcn_permlane32_swap(pack_bf16x2(lo[2], lo[3]), pack_bf16x2(hi[2], hi[3]), false,
+                                                     false);
     u32x4 o;
-    if (kh == 0) {
-      o.x = lo0; o.y = lo1; o.z = q0; o.w = q1;
-    } else {
-      o.x = q0; o.y = q1; o.z = hi0; o.w = hi1;
-    }
+    o.x = r0[0]; o.y = r1[0]; o.z = r0[1]; o.w = r1[1];
     const int c = (2 * p + kh) * 8;
     if (c < lim) *reinterpret_cast<u32x4*>(row + c) = o;
   }

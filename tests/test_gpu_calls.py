@@ -176,6 +176,7 @@ GEMM_CASES = [
     ("bf16", 5, 40, 384, 128),
     ("f32", 4, 70, 192, 128),
     ("bf16", 3, 300, 128, 256),   # data gradient on 128 x 256 tiles
+    ("bf16", 4, 90, 64, 192),     # NN reduction of two 32-deep k-steps (dSwiGLU: G | U staged after the loop)
 ]
 
 
