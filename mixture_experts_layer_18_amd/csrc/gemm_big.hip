@@ -540,9 +540,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
 
   // STG: the results leave through LDS as whole 128-byte rows, staged in
   // the last stage slot; the next tile's last stage is requested after this
-  // tile's stores (the forward gate/up product with gathered rows, and the
-  // plain bf16 data and weight gradients; measured 5-11 % faster each)
-  constexpr bool STG = WIDE || (!F8 && !SL && !GA && EPI == MOE_EPI_NONE && LAYOUT != MOE_GEMM_NT);
+  // tile's stores (the forward gate/up product with gathered rows and every
+  // plain bf16 product; measured 2-11 % faster each)
+  constexpr bool STG = WIDE || (!F8 && !SL && EPI == MOE_EPI_NONE);
   while (true) {
     // this tile's first stages are complete (STG: all but the last, which
     // was requested last: the vector-memory counter counts loads, LDS DMAs
@@ -863,51 +863,6 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       // every wave is done reading its staging area before the next tile's
       // stages overwrite it
       lds_barrier();
-      prefetch_next();
-      if (!more) break;
-      L = Ln;
-      ++kk;
-      t = tn;
-      nk = nk_n;
-#pragma unroll
-      for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
-      continue;
-    }
-    // The plain forward product stores through LDS: each wave stages its
-    // 128 x 64 bf16 results in its own 16 KB of the idle stages (16-byte
-    // chunks XOR-swizzled by row) and then writes 8 full 128-byte rows per
-    // instruction instead of 32-byte pieces of 32 rows; the next tile's first
-    // stages are fetched after (measured 2-5 % faster on the down products;
-    // the data gradients measured slower this way and the weight gradients
-    // would spill, so they keep the direct stores).
-    constexpr bool LDS_EPI = (LAYOUT == MOE_GEMM_NT && EPI == MOE_EPI_NONE && !F8);
-    if constexpr (LDS_EPI) {
-      static_assert(WN == 64 && FJ == 2 && WM * WN * 2 == 16384 && NW * 16384 <= STAGES * SB, "staging layout");
-      char* wb = smem + wave * 16384;
-#pragma unroll
-      for (int it = 0; it < FI; ++it)
-#pragma unroll
-        for (int jt = 0; jt < FJ; ++jt) {
-          const int r = it * 32 + r32;
-#pragma unroll
-          for (int gq = 0; gq < 4; ++gq) {
-            const u32x2 pk = {pack_bf16x2(opaque(acc[it][jt][gq * 4]), opaque(acc[it][jt][gq * 4 + 1])),
-                              pack_bf16x2(opaque(acc[it][jt][gq * 4 + 2]), opaque(acc[it][jt][gq * 4 + 3]))};
-            const int cc = jt * 4 + gq;  // 16-byte chunk of the 128-byte row
-            *reinterpret_cast<u32x2*>(wb + r * 128 + ((cc ^ (r & 7)) << 4) + kh * 8) = pk;
-          }
-        }
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // this wave's LDS writes are done
-      const int lr = lane >> 3, lc = lane & 7;
-#pragma unroll
-      for (int q = 0; q < WM / 8; ++q) {
-        const int r = q * 8 + lr;
-        const u32x4 val = *reinterpret_cast<const u32x4*>(wb + r * 128 + ((lc ^ (r & 7)) << 4));
-        const int64_t i = t.i_lo + wp * WM + r;
-        const int64_t c = t.j0 + wq * WN + lc * 8;
-        if (i < t.i_hi && c < ncols) *reinterpret_cast<u32x4*>(a.C + i * ncols + c) = val;
-      }
-      lds_barrier();  // every wave is done with its staging area
       prefetch_next();
       if (!more) break;
       L = Ln;
