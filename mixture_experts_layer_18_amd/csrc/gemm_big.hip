@@ -148,10 +148,11 @@ struct Tile {
 // (b_in's map may be the identity).
 template <int LAYOUT, int EPI, bool F8, bool GA, int NWV, int PF = FP8_E4M3, bool SL = false, bool MP = false>
 __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in) {
-  // the forward gate/up product with gathered rows: 64 x 128 wave tiles (64
-  // hidden columns per wave, so that its SwiGLU results leave as whole
-  // 128-byte rows; with the staged stores below 5 % faster than 128 x 64)
-  constexpr bool WIDE = (LAYOUT == MOE_GEMM_NT && EPI == MOE_EPI_SWIGLU && !F8 && GA);
+  // the forward gate/up product with gathered rows (bf16 and fp8): 64 x 128
+  // wave tiles (64 hidden columns per wave, so that its SwiGLU results leave
+  // as whole 128-byte rows; with the staged stores below, bf16 5 % faster
+  // than 128 x 64)
+  constexpr bool WIDE = (LAYOUT == MOE_GEMM_NT && EPI == MOE_EPI_SWIGLU && GA);
   using WV = Waves<NWV, WIDE>;
   constexpr int NW = WV::NW, WM = WV::WM, WN = WV::WN, WPR = WV::WPR, FI = WV::FI, FJ = WV::FJ;
   constexpr int LP = WV::LP, LQ = WV::LQ, LT = WV::LT, PAD_BYTES = WV::PAD_BYTES;
@@ -541,8 +542,9 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
   // STG: the results leave through LDS as whole 128-byte rows, staged in
   // the last stage slot; the next tile's last stage is requested after this
   // tile's stores (the forward gate/up product with gathered rows and every
-  // plain bf16 product; measured 2-11 % faster each)
-  constexpr bool STG = WIDE || (!F8 && !SL && EPI == MOE_EPI_NONE);
+  // plain product but the one-group row slices and the fp8 weight
+  // gradients; measured 1-11 % faster each)
+  constexpr bool STG = WIDE || (!W8 && !SL && EPI == MOE_EPI_NONE);
   while (true) {
     // this tile's first stages are complete (STG: all but the last, which
     // was requested last: the vector-memory counter counts loads, LDS DMAs
@@ -768,6 +770,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         sc[gq * 4] = v.x; sc[gq * 4 + 1] = v.y; sc[gq * 4 + 2] = v.z; sc[gq * 4 + 3] = v.w;
       }
     };
+    // fp8: the scale of output row i's source (GN: a token row, per token);
+    // rows past the tile (never stored) read the last row's
+    auto row_scale = [&](int64_t i) __attribute__((always_inline)) {
+      i = i < t.i_hi ? i : t.i_hi - 1;
+      return a.a_scale[GN ? (int64_t)a.rows[i] : i];
+    };
     if constexpr (EPI == MOE_EPI_DSWIGLU) {
       // Data gradient through SwiGLU (NN bf16, or NT fp8 with the weight
       // stored transposed): the product is dH (fp8: times the row and column
@@ -912,11 +920,19 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
           for (int it = 0; it < FI; ++it) {
             const int64_t i0 = t.i_lo + wp * WM + it * 32;
             if (i0 >= t.i_hi) continue;
+            const float sa = F8 ? row_scale(i0 + r32) : 1.0f;
 #pragma unroll
             for (int jt = 0; jt < FJ; ++jt) {
               float v[16];
+              if constexpr (F8) {
+                float sc[16];
+                col_scales(c0 + jt * 32, sc);
 #pragma unroll
-              for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
+                for (int u = 0; u < 16; ++u) v[u] = agpr_read(acc[it][jt][u]) * sa * sc[u];
+              } else {
+#pragma unroll
+                for (int u = 0; u < 16; ++u) v[u] = acc[it][jt][u];
+              }
               stage(v, jt);
             }
             flush(base, ncols, i0, ncols - c0);
@@ -928,6 +944,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       for (int it = 0; it < FI && WIDE; ++it) {
         const int64_t i0 = t.i_lo + wp * WM + it * 32;
         if (i0 >= t.i_hi) continue;
+        const float sa = F8 ? row_scale(i0 + r32) : 1.0f;
         float v[16];
         if (X) {
 #pragma unroll
@@ -936,6 +953,12 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
             for (int jb = 0; jb < 2; ++jb) {
 #pragma unroll
               for (int u = 0; u < 16; ++u) v[u] = opaque(acc[it][2 * jb + gu][u]);
+              if constexpr (F8) {
+                float sc[16];
+                col_scales(gu * F + cg + jb * 32, sc);
+#pragma unroll
+                for (int u = 0; u < 16; ++u) v[u] = v[u] * sa * sc[u];
+              }
               stage(v, jb);
             }
             flush(X + gu * F + cg, N, i0, 64);
@@ -943,8 +966,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         }
 #pragma unroll
         for (int jb = 0; jb < 2; ++jb) {
+          if constexpr (F8) {
+            float sg[16], su[16];
+            col_scales(cg + jb * 32, sg);
+            col_scales(F + cg + jb * 32, su);
 #pragma unroll
-          for (int u = 0; u < 16; ++u) v[u] = silu_f(opaque(acc[it][2 * jb][u])) * opaque(acc[it][2 * jb + 1][u]);
+            for (int u = 0; u < 16; ++u)
+              v[u] = silu_f(opaque(acc[it][2 * jb][u]) * sa * sg[u]) * (opaque(acc[it][2 * jb + 1][u]) * sa * su[u]);
+          } else {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = silu_f(opaque(acc[it][2 * jb][u])) * opaque(acc[it][2 * jb + 1][u]);
+          }
           stage(v, jb);
         }
         flush(C + cg, F, i0, 64);
