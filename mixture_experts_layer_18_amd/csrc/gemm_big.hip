@@ -30,7 +30,11 @@
 //  * persistent: workgroup w on XCD w%8 walks tiles L = n*W + (w%8)*(W/8) +
 //    w/8, so the W/8 workgroups of one XCD work on neighbouring tiles (shared
 //    A rows and B columns in that XCD's L2); the first stages of the next tile
-//    are fetched before the current tile's epilogue;
+//    are fetched before the current tile's epilogue or during it;
+//  * results leave through LDS as whole 128-byte rows (staged in the last
+//    stage slot, or, for dSwiGLU, over the G | U rows just read): stores of
+//    32-byte pieces of 32 rows, the accumulator layout, stall the memory
+//    pipeline far longer per kilobyte;
 //  * DMA addresses are a wave-uniform tile base in SGPRs plus a 32-bit
 //    per-lane offset recomputed at every issue (few live registers).
 // Operands whose reduction dimension is contiguous (NT both, NN's A) sit in
@@ -461,18 +465,20 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
   // dSwiGLU epilogue staging.  A wave's G (or U) rows of one 32-row block of
   // its outputs form a piece of E_NI 1 KB DMA instructions (E_RPI rows of
   // E_RBW bytes each, 16-byte chunks XOR-swizzled by row).  Piece j (0..3)
-  // of a wave sits in LDS stage slot (nk + j) % STAGES at the wave's offset:
-  // the slot that k-step nk - 4 + j frees, so the k-loop's last four steps
-  // fill pieces 0..3 (blocks 0 and 1, G then U) where they would issue pads.
+  // of a wave sits in LDS stage slot j at the wave's offset; the k-loop's
+  // last four steps, which would issue pads, request pieces 0..3 (blocks 0
+  // and 1, G then U), each into the slot its step frees (step kt frees slot
+  // kt % 4).  Blocks 0 and 2 thus use slots 0 and 1, which the next tile's
+  // first two stages take once block 2 is done.
   constexpr int E_RBW = WN * 2, E_CPW = E_RBW / 16, E_RPI = 1024 / E_RBW, E_NI = 32 / E_RPI;
   constexpr int E_WB = E_NI * 1024;  // bytes of one piece
   static_assert(EPI != MOE_EPI_DSWIGLU || (E_NI == LT && NW * E_WB == SB && FI == 4 && WN == 64), "epilogue pieces");
   auto e_swz = [](int r) __attribute__((always_inline)) { return E_RBW >= 256 ? (r & 15) : ((r >> 1) & 7); };
-  auto e_piece = [&](int64_t nk, int j) __attribute__((always_inline)) {
-    return (uint32_t)((nk + j) & (STAGES - 1)) * SB + (uint32_t)(wave * E_WB);
+  auto e_piece = [&](int j) __attribute__((always_inline)) {
+    return (uint32_t)j * SB + (uint32_t)(wave * E_WB);
   };
   // instruction q of piece j holding 32-row block blk of G (j even) or U
-  auto epi_dma = [&](const Tile& t, int64_t nk, int j, int blk, int q, int ln) __attribute__((always_inline)) {
+  auto epi_dma = [&](const Tile& t, int j, int blk, int q, int ln) __attribute__((always_inline)) {
     const int r = q * E_RPI + ln / E_CPW;
     const int rl = (int)(t.i_hi - t.i_lo) - 1;
     int ri = wp * WM + blk * 32 + r;
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
     const int64_t K2 = 2 * ncols;
     const uint32_t voff = (uint32_t)(((int64_t)ri * K2 + (j & 1) * ncols + col) * 2);
     dma16_off(a.aux + t.i_lo * K2, voff,
-              __builtin_amdgcn_readfirstlane(smem_base + e_piece(nk, j) + (uint32_t)(q * 1024)));
+              __builtin_amdgcn_readfirstlane(smem_base + e_piece(j) + (uint32_t)(q * 1024)));
   };
   // this workgroup's k-th tile of the walk (false past its end)
   int r0 = 0, R = 0;
@@ -549,7 +555,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
     // this tile's first stages are complete (STG: all but the last, which
     // was requested last: the vector-memory counter counts loads, LDS DMAs
     // and stores together, and they complete in issue order)
+    // (dSwiGLU: all but the last two, requested after the previous tile's
+    // last block)
     if constexpr (STG) wait_vmcnt<LV>();
+    else if constexpr (EPI == MOE_EPI_DSWIGLU) wait_vmcnt<2 * LV>();
     else wait_vmcnt<0>();
     if (nk > 0) zero_tail(t, 0);
     lds_barrier();
@@ -653,7 +662,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
                 Q[jt], P2[it], acc[FH + it][jt], FP8_E4M3, PF, 0, 0, 0, 0);
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, aoff);
-          else if constexpr (EPI == MOE_EPI_DSWIGLU) epi_dma(t, nk, (int)(kt + STAGES - nk), (int)(kt + STAGES - nk) >> 1, q, ln);
+          else if constexpr (EPI == MOE_EPI_DSWIGLU) epi_dma(t, (int)(kt % STAGES), (int)(kt % STAGES) >> 1, q, ln);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -724,7 +733,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
           }
           __builtin_amdgcn_sched_barrier(0);
           if (real) issue(t, kt + STAGES, q, ln, GT ? gq : aoff);
-          else if constexpr (EPI == MOE_EPI_DSWIGLU) epi_dma(t, nk, (int)(kt + STAGES - nk), (int)(kt + STAGES - nk) >> 1, q, ln);
+          else if constexpr (EPI == MOE_EPI_DSWIGLU) epi_dma(t, (int)(kt % STAGES), (int)(kt % STAGES) >> 1, q, ln);
           else dma4_pad(Ab, pad_lds + q * 256);
           __builtin_amdgcn_sched_barrier(0);
         }
@@ -740,14 +749,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
     // every wave is done with this tile's LDS stages: fetch the next tile's
     // first stages, then write this tile's results
     lds_barrier();
-    auto prefetch_next = [&]() __attribute__((always_inline)) {
+    // the next tile's stages s0 .. s1 - 1 (s0 = 0: its tile is found first)
+    auto prefetch_next = [&](int s0, int s1) __attribute__((always_inline)) {
       if (more) {
         if constexpr (!GA) {
-          tn = tile_of(Ln);
-          nk_n = (tn.r_hi - tn.r_lo + BKE - 1) / BKE;
+          if (s0 == 0) {
+            tn = tile_of(Ln);
+            nk_n = (tn.r_hi - tn.r_lo + BKE - 1) / BKE;
+          }
         }
         const int lp = opaque_i(lane);
-        prologue(tn, nk_n, lp, aoff_n, gr_n, 0, STG ? STAGES - 1 : STAGES);
+        prologue(tn, nk_n, lp, aoff_n, gr_n, s0, s1);
       }
     };
 
@@ -792,19 +804,21 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       // back by whole rows and stores them as full 128-byte rows (the
       // accumulator layout would store 32-byte pieces of 32 rows, measured
       // 3-10 % slower); then (b < 2) block b + 2 is requested into the same
-      // two pieces, its loads overlapping the stores of block b + 1.
+      // two pieces, its loads overlapping the stores of block b + 1; after
+      // block 2 the next tile's first two stages are requested into its
+      // slots, after block 3 the other two.
       const int ln = opaque_i(lane);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (nk + j < STAGES)
+        if (j >= nk)
 #pragma unroll
-          for (int q = 0; q < E_NI; ++q) epi_dma(t, nk, j, j >> 1, q, ln);
+          for (int q = 0; q < E_NI; ++q) epi_dma(t, j, j >> 1, q, ln);
       wait_vmcnt<0>();
 #pragma unroll
       for (int it = 0; it < FI; ++it) {
         const int j0 = 2 * (it & 1);
-        char* Gw = smem + e_piece(nk, j0);
-        char* Uw = smem + e_piece(nk, j0 + 1);
+        char* Gw = smem + e_piece(j0);
+        char* Uw = smem + e_piece(j0 + 1);
         const int64_t i = t.i_lo + wp * WM + it * 32 + r32;
         // fp8: the row's scale (padding rows, never stored, read the last row's)
         const float sa = F8 ? a.a_scale[i < t.i_hi ? i : t.i_hi - 1] : 1.0f;
@@ -868,15 +882,17 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
 #pragma unroll
           for (int gu = 0; gu < 2; ++gu)
 #pragma unroll
-            for (int q = 0; q < E_NI; ++q) epi_dma(t, nk, j0 + gu, it + 2, q, ln);
+            for (int q = 0; q < E_NI; ++q) epi_dma(t, j0 + gu, it + 2, q, ln);
         }
         // blocks 2 and 3 have landed (with the stores before them)
         if (it == 1) wait_vmcnt<0>();
+        // every wave is done with slots 0 and 1 (block 2) or 2 and 3 (block
+        // 3): the next tile's stages into them
+        if (it >= 2) {
+          lds_barrier();
+          prefetch_next(it == 2 ? 0 : 2, it == 2 ? 2 : 4);
+        }
       }
-      // every wave is done reading its staging area before the next tile's
-      // stages overwrite it
-      lds_barrier();
-      prefetch_next();
       if (!more) break;
       L = Ln;
       ++kk;
@@ -886,7 +902,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       for (int i = 0; i < LP; ++i) aoff[i] = aoff_n[i];
       continue;
     }
-    prefetch_next();
+    prefetch_next(0, STG ? STAGES - 1 : STAGES);
     if constexpr (STG) {
       // Each wave stages every 32-row block of its results in its own 4 KB
       // of the last stage slot (64 columns: the plain products' 64 x 2 blocks
@@ -993,7 +1009,7 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         flush(C + cg, F, i0, 64);
       }
       lds_barrier();  // every wave is done with the last slot
-      if (more) prologue(tn, nk_n, opaque_i(lane), aoff_n, gr_n, STAGES - 1, STAGES);
+      prefetch_next(STAGES - 1, STAGES);
       if (!more) break;
       L = Ln;
       ++kk;
