@@ -515,6 +515,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
       }
     }
   }
+  // Weight gradients (tiles in order of decreasing cost): the XCDs take the
+  // slices of a round in serpentine order (XCD x slice x in even rounds,
+  // slice 7 - x in odd ones), so that no XCD always gets the dearest slice.
+  auto lw_of = [&](int round) __attribute__((always_inline)) {
+    if constexpr (LAYOUT == MOE_GEMM_TN && !SL) return ((round & 1) ? 7 - xcd : xcd) * per + slot;
+    return lw;
+  };
   auto item = [&](int k, int& L) __attribute__((always_inline)) -> bool {
     if (MP && after_b && r0 > 0) {
       const int p1 = lw >= r0 ? R : 0;
@@ -522,10 +529,10 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
         L = (lw - r0) + k * (nwg - r0);
         return L < total;
       }
-      L = R * (nwg - r0) + (k - p1) * nwg + lw;
+      L = R * (nwg - r0) + (k - p1) * nwg + lw_of(k - p1);
       return L < total;
     }
-    L = lw + k * nwg;
+    L = lw_of(k) + k * nwg;
     return L < total;
   };
   int kk = 0, L = 0;
