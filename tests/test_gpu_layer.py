@@ -54,15 +54,22 @@ def test_backward_small_bf16():
 # products) over groups of about 125 rows
 PAIRED_BF16 = synth.CONFIG_BY_NAME["moe7b_bf16"].replace(name="paired_bf16", T=2000, d=1024, E=64, k=4, f=1024,
                                                           n_shared=1, f_shared=512)
+# widths that leave partial 256-column tiles in the down products and their
+# weight gradients (f = 3.5 tiles, the shared width 2.5); 4000 tokens, so that
+# every expert's weight gradient sums enough rows for the bf16 bar (at 2000
+# tokens the smallest experts had 18 rows, and one bf16 step of their largest
+# elements reached 5.02e-2 of the RMS)
+PAIRED_RAGGED = PAIRED_BF16.replace(name="paired_ragged", T=4000, f=896, f_shared=640)
 
 
+@pytest.mark.parametrize("cfg", [PAIRED_BF16, PAIRED_RAGGED], ids=["tile-multiples", "ragged-widths"])
 @pytest.mark.parametrize("gather", [False, True], ids=["permuted-copy", "gathered"])
-def test_backward_paired_shared_weight_gradients(gather):
+def test_backward_paired_shared_weight_gradients(gather, cfg):
     import mixture_experts_layer_18_amd as M
-    print(f"[layer] paired shared weight gradients gather={gather}", flush=True)
+    print(f"[layer] paired shared weight gradients {cfg.name} gather={gather}", flush=True)
     M.stage_timing(True)
     try:
-        R.compare_full(PAIRED_BF16, synth.make_inputs(PAIRED_BF16), backward=True, gather=gather)
+        R.compare_full(cfg, synth.make_inputs(cfg), backward=True, gather=gather)
         torch.cuda.synchronize()
         st = M.stage_times()
     finally:
