@@ -1113,9 +1113,13 @@ __global__ __launch_bounds__(64 * NWV, 1) void gemm_kernel(Args a_in, Args b_in)
   };  // walk
 
   if constexpr (MP) {
-    walk(b_in, false);
-    __syncthreads();  // the tile table is rebuilt for a_in
-    walk(a_in, true);
+    // b_in's walk, then a_in's, through one copy of the walk's code (two
+    // inlined copies spilled more)
+#pragma clang loop unroll(disable)
+    for (int p = 0; p < 2; ++p) {
+      if (p == 1) __syncthreads();  // the tile table is rebuilt for a_in
+      walk(p == 0 ? b_in : a_in, p == 1);
+    }
   } else {
     walk(a_in, false);
   }
