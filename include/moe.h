@@ -291,6 +291,12 @@ int moe_combine(const moe_desc_t *desc, const void *y_perm, const float *gate,
 
 /* Whole forward pass: router GEMM (fp32) -> route -> permute -> gate/up
  * grouped GEMM with SwiGLU -> down grouped GEMM -> shared experts -> combine.
+ * This is the layer as the Handbook lays it out: section 1 "Introduction"
+ * (a router picks experts per token, the load is balanced, tokens travel to
+ * their experts) and section 2.5 "First training of MoE" (the selected
+ * experts' outputs come back and are summed by gate weight; fp32 router;
+ * grouped GEMM over the local experts); shared experts as in KempnerForge
+ * "Features / Architecture", added ungated on every token.
  *   x [T, d] (in), y [T, d] (out), saved (out, all buffers caller-allocated)
  *   ws >= moe_workspace_bytes(desc, MOE_WS_FORWARD) */
 int moe_forward(const moe_desc_t *desc, const moe_weights_t *w, const void *x, void *y,
@@ -317,7 +323,10 @@ int moe_forward_no_workspace(const moe_desc_t *desc, const moe_weights_t *w, con
 /* Whole backward pass for upstream gradient dy [T, d]: combine backward
  * (gate gradient), router backward (through the gates only; the bias gets no
  * gradient), down and gate/up data and weight gradients, shared experts,
- * unpermute-sum of the input gradient.
+ * unpermute-sum of the input gradient.  It is the exact gradient of
+ * moe_forward (the Handbook's section 2.5 layer, trained end to end there);
+ * that the bias only steers selection and takes no gradient follows the
+ * Apex-3 code page, "What's inside", row "Fine-grained MoE".
  *   x [T, d] (the forward input), saved (from moe_forward), dy [T, d] (in),
  *   dx [T, d] (out), grads (out)
  *   terms   NULL, or router training terms whose gradients are added to the
